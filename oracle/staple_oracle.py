@@ -1,0 +1,308 @@
+"""CPU oracle of the STAPLE embedding-augmented gated FFN.
+
+TEST INFRASTRUCTURE ONLY.  Nothing in the product path imports this module:
+only the tests, the smoke check and the benchmark's CPU-baseline leg do.  It
+shares no code with the HIP library and does not import it.
+
+It is a plain, slow, float64 statement of what one augmented FFN layer
+computes, together with the batch dedup, the frequency-ranked row cache and
+the table-row gradient.  Every function says which passage of the STAPLE
+pages it follows.  Where the pages leave a step open, the reading taken is
+stated next to the code.
+
+Definition of one augmented layer (positions i = 0..N-1, token IDs t_i):
+
+    g_i = W_gate x_i          a_i = W_up x_i
+    u_i = a_i + E[t_i]        h_i = silu(g_i) * u_i        y_i = W_down h_i
+
+* The up-projection is kept and the token's table row is added to it as a
+  residual path (STAPLE abstract; news synopsis "Pretrained models gain
+  sparse capacity without retraining", Synopsis and Interpretation).
+* The gate branch multiplies the memory path (same synopsis, Perspective:
+  a context-dependent gate controls how much the memory contributes).
+* Reading: the gated FFN is the SwiGLU form with SiLU on the gate and no
+  biases; the table row is indexed by the input token at the same position.
+
+Two precisions:
+
+* ``"exact"``: every intermediate is kept in float64.  The fp32 workload is
+  checked against this mode.
+* ``"bf16"``: float64 accumulation, with rounding to bf16 (nearest, ties to
+  even) exactly where the bf16 path materialises a tensor between two
+  contractions: h (operand of the down-projection), the activations g and u
+  saved for the backward pass, and du, dg (operands of the weight-gradient
+  and input-gradient contractions).  Reading: the pages fix bf16 tables and
+  weights (STAPLE Table 4 caption; Figure 4 caption) but not where
+  intermediates are rounded; these are the tensors a bf16 layer stores.
+"""
+from __future__ import annotations
+
+import math
+from typing import Optional, Sequence
+
+import numpy as np
+
+EXACT = "exact"
+BF16 = "bf16"
+
+
+# --------------------------------------------------------------------------
+# Scalar building blocks
+# --------------------------------------------------------------------------
+def bf16_round(v) -> np.ndarray:
+    """Round float64 values to the nearest bfloat16 value, ties to even.
+
+    bfloat16 keeps 8 significant bits and float32's exponent range.  The value
+    is split as m * 2^e with 0.5 <= |m| < 1, m is rounded to 8 bits with
+    round-half-even (numpy's rint), and the result is scaled back.  Below the
+    smallest normal (2^-126) the quantum is fixed at 2^-133.  Overflow past
+    the largest finite bf16 value goes to infinity.
+    """
+    v = np.asarray(v, dtype=np.float64)
+    m, e = np.frexp(v)
+    e = np.maximum(e, -125)          # subnormal range: fixed quantum 2^(-125-8)
+    q = np.rint(np.ldexp(v, 8 - e))  # value in units of the quantum 2^(e-8)
+    out = np.ldexp(q, e - 8)
+    big = np.abs(out) > 3.3895313892515355e38
+    if np.any(big):
+        out = np.where(big, np.copysign(np.inf, v), out)
+    return out
+
+
+def sigmoid(z) -> np.ndarray:
+    z = np.asarray(z, dtype=np.float64)
+    with np.errstate(over="ignore"):
+        return 1.0 / (1.0 + np.exp(-z))
+
+
+def silu(z) -> np.ndarray:
+    """SiLU(z) = z * sigmoid(z)."""
+    z = np.asarray(z, dtype=np.float64)
+    return z * sigmoid(z)
+
+
+def silu_grad(z) -> np.ndarray:
+    """d/dz [z * sigmoid(z)] = sigmoid(z) * (1 + z * (1 - sigmoid(z)))."""
+    z = np.asarray(z, dtype=np.float64)
+    s = sigmoid(z)
+    return s * (1.0 + z * (1.0 - s))
+
+
+def _maybe_round(a: np.ndarray, precision: str) -> np.ndarray:
+    if precision == BF16:
+        return bf16_round(a)
+    if precision == EXACT:
+        return a
+    raise ValueError(f"unknown precision {precision!r}")
+
+
+def _table_rows(table, ids: np.ndarray, cols: Optional[np.ndarray]) -> np.ndarray:
+    """E[t_i] for every position, restricted to the given feature columns."""
+    if cols is None:
+        return np.asarray(table[ids], dtype=np.float64)
+    return np.asarray(table[np.ix_(ids, cols)], dtype=np.float64)
+
+
+# --------------------------------------------------------------------------
+# Batch dedup (STAPLE retrieval-path table, Prefill row: the prompt tokens
+# are deduplicated once and one inverse token map serves every STAPLE layer;
+# AI Radio episode on STAPLE: only the U x d_ff active rows live on the GPU.)
+# --------------------------------------------------------------------------
+def dedup(ids: Sequence[int]):
+    """Unique IDs, inverse map, stably sorted positions and segment offsets.
+
+    Readings: unique IDs are listed in ascending order; positions sharing an
+    ID keep ascending position order; segment u of ``sorted_pos`` is
+    ``sorted_pos[seg_start[u]:seg_start[u+1]]``.
+
+    Returns (uniq int32[U], inv int32[N], sorted_pos int32[N], seg_start int32[U+1]).
+    """
+    ids = [int(t) for t in ids]
+    n = len(ids)
+    uniq = sorted(set(ids))
+    index_of = {t: k for k, t in enumerate(uniq)}
+    inv = [index_of[t] for t in ids]
+    sorted_pos = sorted(range(n), key=lambda i: (ids[i], i))
+    seg_start = [0] * (len(uniq) + 1)
+    counts = [0] * len(uniq)
+    for t in ids:
+        counts[index_of[t]] += 1
+    for k in range(len(uniq)):
+        seg_start[k + 1] = seg_start[k] + counts[k]
+    as32 = lambda a: np.asarray(a, dtype=np.int32).reshape(-1)
+    return as32(uniq), as32(inv), as32(sorted_pos), as32(seg_start)
+
+
+# --------------------------------------------------------------------------
+# Frequency-aware row cache (AI Radio episode: about 5-6% of the vocabulary
+# cached with a frequency-aware policy; STAPLE retrieval-path table, Decode
+# row: a GPU lookup probes the LFU cache.)
+# --------------------------------------------------------------------------
+def cache_build(counts: Sequence[int], capacity: int):
+    """Static top-`capacity` cache by count.
+
+    Readings: the cache is built once from a count pass (no eviction is
+    described); IDs are ranked by count, larger first, ties by smaller ID; slot
+    s holds the ID of rank s; when fewer IDs than `capacity` have non-zero
+    counts the ranking still fills every slot.
+
+    Returns (id_to_slot int32[V] with -1 for uncached IDs, slot_to_id int32[C]).
+    """
+    counts = [int(c) for c in counts]
+    vocab = len(counts)
+    if not 0 <= capacity <= vocab:
+        raise ValueError("capacity out of range")
+    ranking = sorted(range(vocab), key=lambda v: (-counts[v], v))
+    slot_to_id = ranking[:capacity]
+    id_to_slot = [-1] * vocab
+    for s, v in enumerate(slot_to_id):
+        id_to_slot[v] = s
+    return np.asarray(id_to_slot, dtype=np.int32), np.asarray(slot_to_id, dtype=np.int32)
+
+
+def cache_lookup(uniq: Sequence[int], id_to_slot: Sequence[int]):
+    """Probe the cache for each unique ID and list the misses.
+
+    Returns (code int32[U], miss_uidx int32[M]).  ``code[u]`` is the cache slot
+    of ``uniq[u]`` on a hit and ``-1 - m`` on a miss, where m is the position of
+    u in the miss list; ``miss_uidx`` lists the missing unique indices in
+    ascending order (reading: the pages do not fix an order).
+    """
+    code = []
+    miss = []
+    for u, t in enumerate(uniq):
+        s = int(id_to_slot[int(t)])
+        if s >= 0:
+            code.append(s)
+        else:
+            code.append(-1 - len(miss))
+            miss.append(u)
+    return np.asarray(code, dtype=np.int32), np.asarray(miss, dtype=np.int32)
+
+
+def assemble_rows(table, uniq: Sequence[int]) -> np.ndarray:
+    """Compact leaf block R[u] = E[uniq[u]] (AI Radio episode: the active rows,
+    materialised as an autograd leaf)."""
+    return np.asarray(table[np.asarray(uniq, dtype=np.int64)])
+
+
+# --------------------------------------------------------------------------
+# Forward
+# --------------------------------------------------------------------------
+def ffn_forward(x, w_gate, w_up, w_down, table, ids, precision: str = EXACT,
+                cols: Optional[np.ndarray] = None, with_y: bool = True) -> dict:
+    """Forward of one augmented layer.
+
+    x [N, d]; w_gate, w_up [f, d]; w_down [d, f]; table [V, f] (anything that
+    supports ``table[ids]`` and ``table[np.ix_(ids, cols)]``); ids [N].
+
+    ``cols`` restricts the feature dimension to a subset (g, u, h for those
+    columns only; y needs every column and is then not returned).
+
+    Returns g, u (pre-rounding), g_saved, u_saved (as stored for backward),
+    h, and y (when every column is present).
+    """
+    x = np.asarray(x, dtype=np.float64)
+    ids = np.asarray(ids, dtype=np.int64)
+    wg = np.asarray(w_gate, dtype=np.float64)
+    wu = np.asarray(w_up, dtype=np.float64)
+    if cols is not None:
+        wg = wg[cols]
+        wu = wu[cols]
+    g = x @ wg.T
+    a = x @ wu.T
+    u = a + _table_rows(table, ids, cols)
+    h = _maybe_round(silu(g) * u, precision)
+    out = {"g": g, "u": u, "h": h,
+           "g_saved": _maybe_round(g, precision),
+           "u_saved": _maybe_round(u, precision)}
+    if cols is None and with_y:
+        out["y"] = h @ np.asarray(w_down, dtype=np.float64).T
+    return out
+
+
+# --------------------------------------------------------------------------
+# Backward, including the table-row gradient
+# --------------------------------------------------------------------------
+def table_row_grad(du: np.ndarray, ids: Sequence[int], uniq: Sequence[int]) -> np.ndarray:
+    """dR[u] = sum of du_i over positions whose token is uniq[u].
+
+    The gradient of the compact leaf block (AI Radio episode: active rows as an
+    autograd leaf; STAPLE abstract: token-specific updates).  Reading: a plain
+    sum over occurrences, no averaging by count.
+    """
+    du = np.asarray(du, dtype=np.float64)
+    index_of = {int(t): k for k, t in enumerate(uniq)}
+    out = np.zeros((len(index_of),) + du.shape[1:], dtype=np.float64)
+    for i, t in enumerate(ids):
+        out[index_of[int(t)]] += du[i]
+    return out
+
+
+def ffn_backward(dy, x, w_gate, w_up, w_down, fwd: dict, ids, precision: str = EXACT,
+                 freeze_up: bool = False, cols: Optional[np.ndarray] = None,
+                 uniq: Optional[Sequence[int]] = None, with_dx: bool = True) -> dict:
+    """Backward of one augmented layer given the upstream gradient dy [N, d].
+
+    With ``cols`` set, ``fwd`` must come from ``ffn_forward(..., cols=cols)`` and
+    every feature-indexed result is restricted to those columns (dx needs every
+    column and is then not returned).
+
+    Returns dh, du, dg, d_rows (one row per unique ID, ascending), dw_down,
+    dw_gate, dw_up (absent when ``freeze_up``: during warmup the up-projections
+    of augmented layers are frozen, STAPLE Table 3 caption; the gradient still
+    flows through them into dx and the table rows) and dx.
+    """
+    dy = np.asarray(dy, dtype=np.float64)
+    x = np.asarray(x, dtype=np.float64)
+    wd = np.asarray(w_down, dtype=np.float64)
+    wg = np.asarray(w_gate, dtype=np.float64)
+    wu = np.asarray(w_up, dtype=np.float64)
+    if cols is not None:
+        wd = wd[:, cols]
+        wg = wg[cols]
+        wu = wu[cols]
+    g = fwd["g_saved"]
+    u = fwd["u_saved"]
+    h = fwd["h"]
+
+    dh = dy @ wd                                     # dL/dh = W_down^T dy
+    du = _maybe_round(dh * silu(g), precision)       # dL/du = dh * silu(g)
+    dg = _maybe_round(dh * u * silu_grad(g), precision)  # dL/dg = dh * u * silu'(g)
+
+    if uniq is None:
+        uniq = sorted(set(int(t) for t in ids))
+    out = {
+        "dh": dh, "du": du, "dg": dg,
+        "d_rows": table_row_grad(du, ids, uniq),    # dL/dE[t] summed over occurrences
+        "dw_down": dy.T @ h,                         # dL/dW_down = sum_i dy_i h_i^T
+        "dw_gate": dg.T @ x,                         # dL/dW_gate = sum_i dg_i x_i^T
+    }
+    if not freeze_up:
+        out["dw_up"] = du.T @ x                      # dL/dW_up = sum_i du_i x_i^T
+    if cols is None and with_dx:
+        out["dx"] = dg @ wg + du @ wu                # dL/dx = W_gate^T dg + W_up^T du
+    return out
+
+
+# --------------------------------------------------------------------------
+# Work counts used for throughput figures
+# --------------------------------------------------------------------------
+def ffn_flops(n_tokens: int, d_model: int, d_ff: int, backward: bool,
+              freeze_up: bool = False) -> int:
+    """Multiply-add FLOPs (2 per MAC) of the layer's contractions."""
+    ndf = n_tokens * d_model * d_ff
+    fwd = 6 * ndf                        # gate, up, down
+    if not backward:
+        return fwd
+    bwd = 2 * ndf + 2 * ndf + 2 * ndf + 4 * ndf   # dh, dW_down, dW_gate, dx (two terms)
+    if not freeze_up:
+        bwd += 2 * ndf                   # dW_up
+    return fwd + bwd
+
+
+def decode_layer_bytes(n_tokens: int, d_model: int, d_ff: int, n_unique: int,
+                       elem: int = 2) -> int:
+    """Bytes a decode layer must move at least: the three weight matrices once,
+    one table row per unique token, x in and y out."""
+    return (3 * d_model * d_ff + n_unique * d_ff + 2 * n_tokens * d_model) * elem
