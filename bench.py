@@ -1,0 +1,441 @@
+#!/usr/bin/env python3
+"""Throughput of the STAPLE token-indexed FFN hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W]
+
+Headline (`value`): decode tokens/s of an OLMo-2-1B-shaped decode step, batch
+64, through 12 augmented FFN layers whose 100352 x 8192 bf16 tables are all
+resident in HBM; one step runs every layer back to back (fused gate/up GEMM
+with the token-row gather in its epilogue, then the down-projection), captured
+once in a HIP graph and replayed.
+
+Also reported (`train`): tokens/s of one OLMo-2-1B-shaped training micro-batch
+(32768 Zipf tokens) through one augmented layer: dedup, compact-row gather,
+forward, backward with the fp32 table-row segment-sum and all weight and input
+gradients.
+
+Every input is synthetic and seeded (staple_synth).  Inputs are resident in
+HBM before timing starts.  The CPU oracle is timed on a bounded sample of the
+same work on the host cores (`cpu_baseline`).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "STAPLE-FFN tokens/s (decode B=64; train fwd+bwd) + HBM GB/s / MFMA % of peak"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, published
+PROFILES = os.path.join(ROOT, "profiles")
+
+
+def parse_args(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200, help="timed decode steps")
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--train-steps", type=int, default=10)
+    ap.add_argument("--train-warmup", type=int, default=3)
+    ap.add_argument("--workloads", default="decode,train")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=8.0,
+                    help="target CPU time of each oracle baseline sample")
+    ap.add_argument("--mode", default="bench", choices=["bench", "copy"],
+                    help="copy: run a plain 1 GiB device copy (counter calibration)")
+    return ap.parse_args(argv)
+
+
+def source_sha(*names) -> str:
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(ROOT, "token_indexed_ffn_amd", "csrc", n), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_from_profile(kernel_key: str, sha: str):
+    """HBM bytes per launch from the committed counter summary, if it was taken
+    on the current kernel source; otherwise None."""
+    path = os.path.join(PROFILES, "traffic.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        rec = json.load(open(path)).get(kernel_key)
+    except Exception:
+        return None
+    if not rec or rec.get("source_sha") != sha:
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def oracle_threads() -> int:
+    try:
+        from threadpoolctl import threadpool_info
+        n = [p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas"]
+        return int(max(n)) if n else 1
+    except Exception:
+        return os.cpu_count() or 1
+
+
+# ----------------------------------------------------------------------------
+# Decode: 12 layers, batch 64, full tables in HBM
+# ----------------------------------------------------------------------------
+def setup_decode(torch, st, w):
+    from staple_synth import device_normal
+    dev = torch.device("cuda:0")
+    L, n, d, f, v = w.n_layers, w.n_tokens, w.d_model, w.d_ff, w.vocab
+    ids_np = w.ids()
+    layers = []
+    for l in range(L):
+        s = w.layer_seeds(l)
+        layers.append({
+            "x": device_normal((n, d), w.x_std, s["x"], torch.bfloat16, dev),
+            "w_gate": device_normal((f, d), w.w_std, s["w_gate"], torch.bfloat16, dev),
+            "w_up": device_normal((f, d), w.w_std, s["w_up"], torch.bfloat16, dev),
+            "w_down": device_normal((d, f), w.w_std, s["w_down"], torch.bfloat16, dev),
+            "table": device_normal((v, f), w.table_std, s["table"], torch.bfloat16, dev),
+            "y": torch.empty(n, d, dtype=torch.bfloat16, device=dev),
+        })
+        torch.cuda.synchronize()
+    ids = torch.from_numpy(ids_np).to(dev)
+    h = torch.empty(n, f, dtype=torch.bfloat16, device=dev)
+    return {"layers": layers, "ids": ids, "ids_np": ids_np, "h": h}
+
+
+def decode_step(st, D):
+    ids, h = D["ids"], D["h"]
+    for lay in D["layers"]:
+        st.staple_ffn_gate_up(lay["x"], lay["w_gate"], lay["w_up"], lay["table"], ids, h)
+        st.staple_ffn_down(h, lay["w_down"], lay["y"])
+
+
+def run_decode(torch, st, w, steps, warmup):
+    import numpy as np
+    D = setup_decode(torch, st, w)
+    n, d, f = w.n_tokens, w.d_model, w.d_ff
+    n_unique = int(len(np.unique(D["ids_np"])))
+    for _ in range(3):
+        decode_step(st, D)
+    torch.cuda.synchronize()
+    if st.staple_get_device_error() != 0:
+        raise RuntimeError("device error during decode warmup")
+
+    # eager timing (launch-bound reference)
+    t0 = time.perf_counter()
+    for _ in range(10):
+        decode_step(st, D)
+    torch.cuda.synchronize()
+    eager_ms = (time.perf_counter() - t0) / 10 * 1e3
+
+    # one decode step captured as a HIP graph
+    g = torch.cuda.CUDAGraph()
+    cap = torch.cuda.Stream()
+    cap.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(cap):
+        decode_step(st, D)   # warm the capture stream
+        cap.synchronize()
+        with torch.cuda.graph(g, stream=cap):
+            decode_step(st, D)
+    torch.cuda.current_stream().wait_stream(cap)
+    torch.cuda.synchronize()
+
+    for _ in range(warmup):
+        g.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        g.replay()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    ms = elapsed / steps * 1e3
+    if st.staple_get_device_error() != 0:
+        raise RuntimeError("device error during decode timing")
+
+    # dominant kernel: the fused gate/up GEMM, one launch per layer, timed with
+    # HIP events around replays of a graph holding only those launches
+    gg = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(cap):
+        with torch.cuda.graph(gg, stream=cap):
+            for lay in D["layers"]:
+                st.staple_ffn_gate_up(lay["x"], lay["w_gate"], lay["w_up"], lay["table"],
+                                      D["ids"], D["h"])
+    torch.cuda.synchronize()
+    reps = max(20, steps // 2)
+    for _ in range(5):
+        gg.replay()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        gg.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    gu_us = e0.elapsed_time(e1) / (reps * w.n_layers) * 1e3
+
+    gu_bytes = (2 * d * f + n * d + n_unique * f + n * f) * 2      # W_gate, W_up, x, rows, h
+    down_bytes = (d * f + n * f + n * d) * 2                        # W_down, h, y
+    step_bytes = w.n_layers * (gu_bytes + down_bytes)
+    sha = source_sha("gemm.hip")
+    achieved = gu_bytes / (gu_us * 1e-6) / 1e9
+    res = {
+        "ms_per_step": ms,
+        "tokens_per_s": n / (ms * 1e-3),
+        "eager_ms_per_step": eager_ms,
+        "step_hbm_gb_s": step_bytes / (ms * 1e-3) / 1e9,
+        "step_bytes": step_bytes,
+        "n_unique": n_unique,
+        "roofline": {
+            "kernel": "gemm_kernel<bf16,GateUp> (staple_ffn_gate_up, decode)",
+            "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": achieved / HBM_PEAK_GBS,
+            "traffic": traffic_from_profile("decode_gate_up", sha),
+            "avg_launch_us": gu_us, "algorithmic_bytes_per_launch": gu_bytes,
+        },
+    }
+    return res, D
+
+
+def decode_cpu_baseline(torch, w, D, seconds):
+    """Oracle forward of the decode step on the host, layer by layer, until
+    `seconds` of CPU time have been spent in the oracle; tokens/s is scaled to
+    the whole 12-layer step."""
+    import numpy as np
+    from oracle import staple_oracle as O
+    f64 = lambda t: t.float().cpu().numpy().astype(np.float64)
+    ids = D["ids_np"]
+    uniq = np.unique(ids)
+    cache = {}
+    layer_times = []
+    l = 0
+    while sum(layer_times) < seconds and l < 4 * w.n_layers:
+        li = l % w.n_layers
+        if li not in cache:
+            if len(cache) >= 3:
+                cache.pop(next(iter(cache)))
+            lay = D["layers"][li]
+            idx = torch.from_numpy(uniq.astype(np.int64)).to(lay["table"].device)
+            cache[li] = [f64(lay[k]) for k in ("x", "w_gate", "w_up", "w_down")] + \
+                        [_Rows(uniq, f64(lay["table"][idx]))]
+        x, wg, wu, wd, table = cache[li]
+        t0 = time.perf_counter()
+        O.ffn_forward(x, wg, wu, wd, table, ids, precision=O.BF16)
+        layer_times.append(time.perf_counter() - t0)
+        l += 1
+    per_layer = float(np.mean(layer_times))
+    return {"value": w.n_tokens / (per_layer * w.n_layers), "unit": "tokens/s",
+            "cores": oracle_threads(), "kind": "oracle",
+            "sample": f"{len(layer_times)} layer forwards of the 64-token decode batch "
+                      f"(float64 numpy, bf16 rounding points), scaled to {w.n_layers} layers"}
+
+
+class _Rows:
+    """Table stand-in holding only the rows of the given sorted IDs."""
+
+    def __init__(self, ids_sorted, rows):
+        import numpy as np
+        self.ids = np.asarray(ids_sorted)
+        self.rows = rows
+
+    def __getitem__(self, key):
+        import numpy as np
+        if isinstance(key, tuple):
+            r, c = key
+            r = np.asarray(r).reshape(-1)
+            return self.rows[np.searchsorted(self.ids, r)][:, np.asarray(c).reshape(-1)]
+        return self.rows[np.searchsorted(self.ids, np.asarray(key))]
+
+
+# ----------------------------------------------------------------------------
+# Training micro-batch: one layer, fwd + bwd
+# ----------------------------------------------------------------------------
+def setup_train(torch, st, w):
+    from staple_synth import device_normal
+    dev = torch.device("cuda:0")
+    n, d, f, v = w.n_tokens, w.d_model, w.d_ff, w.vocab
+    s = w.layer_seeds(0)
+    T = {
+        "ids_np": w.ids(),
+        "x": device_normal((n, d), w.x_std, s["x"], torch.bfloat16, dev),
+        "w_gate": device_normal((f, d), w.w_std, s["w_gate"], torch.bfloat16, dev),
+        "w_up": device_normal((f, d), w.w_std, s["w_up"], torch.bfloat16, dev),
+        "w_down": device_normal((d, f), w.w_std, s["w_down"], torch.bfloat16, dev),
+        "table": device_normal((v, f), w.table_std, s["table"], torch.bfloat16, dev),
+        "dy": device_normal((n, d), w.dy_std, s["dy"], torch.bfloat16, dev),
+    }
+    T["ids"] = torch.from_numpy(T["ids_np"]).to(dev)
+    bf = dict(dtype=torch.bfloat16, device=dev)
+    f32 = dict(dtype=torch.float32, device=dev)
+    i32 = dict(dtype=torch.int32, device=dev)
+    T["dd"] = {"uniq": torch.empty(n, **i32), "inv": torch.empty(n, **i32),
+               "sorted_pos": torch.empty(n, **i32), "seg_start": torch.empty(n + 1, **i32),
+               "n_unique": torch.empty(1, **i32)}
+    T["dd_ws"] = torch.empty(max(st.lib().staple_dedup_workspace_bytes(n), 1), dtype=torch.uint8,
+                             device=dev)
+    T["rows"] = torch.empty(n, f, **bf)
+    T["fwd"] = {"y": torch.empty(n, d, **bf), "g": torch.empty(n, f, **bf),
+                "u": torch.empty(n, f, **bf), "h": torch.empty(n, f, **bf)}
+    T["bwd"] = {"d_rows": torch.empty(n, f, **f32), "dx": torch.empty(n, d, **bf),
+                "dw_gate": torch.empty(f, d, **f32), "dw_up": torch.empty(f, d, **f32),
+                "dw_down": torch.empty(d, f, **f32)}
+    T["bwd_ws"] = torch.empty(st.lib().staple_ffn_bwd_workspace_bytes(n, d, f, 1), dtype=torch.uint8,
+                              device=dev)
+    torch.cuda.synchronize()
+    return T
+
+
+def train_step(st, T, vocab, events=None):
+    dd = st.staple_dedup(T["ids"], vocab, out=T["dd"], workspace=T["dd_ws"])
+    st.staple_gather_rows(T["table"], dd["uniq"], dd["n_unique"], out=T["rows"])
+    fw = T["fwd"]
+    if events:
+        events[0].record()
+    st.staple_ffn_gate_up(T["x"], T["w_gate"], T["w_up"], T["rows"], dd["inv"], fw["h"],
+                          fw["g"], fw["u"])
+    if events:
+        events[1].record()
+    st.staple_ffn_down(fw["h"], T["w_down"], fw["y"])
+    st.staple_ffn_bwd_table_grad(T["dy"], T["x"], T["w_gate"], T["w_up"], T["w_down"], fw["g"],
+                                 fw["u"], fw["h"], dd["sorted_pos"], dd["seg_start"],
+                                 dd["n_unique"], out=T["bwd"], workspace=T["bwd_ws"])
+
+
+def run_train(torch, st, w, steps, warmup):
+    T = setup_train(torch, st, w)
+    n, d, f = w.n_tokens, w.d_model, w.d_ff
+    for _ in range(warmup):
+        train_step(st, T, w.vocab)
+    torch.cuda.synchronize()
+    if st.staple_get_device_error() != 0:
+        raise RuntimeError("device error during train warmup")
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        train_step(st, T, w.vocab)
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) / steps * 1e3
+    # dominant kernel timing: the fused gate/up GEMM, events around each launch
+    durs = []
+    for _ in range(max(3, steps // 2)):
+        ev = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+        train_step(st, T, w.vocab, events=ev)
+        torch.cuda.synchronize()
+        durs.append(ev[0].elapsed_time(ev[1]) * 1e3)
+    gu_us = sum(durs) / len(durs)
+    flops_total = 18 * n * d * f
+    gu_flops = 4 * n * d * f
+    achieved = gu_flops / (gu_us * 1e-6) / 1e12
+    return {
+        "workload": w.name, "tokens": n, "ms_per_step": ms, "tokens_per_s": n / (ms * 1e-3),
+        "step_tflops": flops_total / (ms * 1e-3) / 1e12,
+        "step_mfma_frac": flops_total / (ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
+        "n_unique": int(T["dd"]["n_unique"].item()),
+        "roofline": {
+            "kernel": "gemm_kernel<bf16,GateUp> (staple_ffn_gate_up, training batch)",
+            "bound": "mfma", "achieved": achieved, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+            "frac": achieved / BF16_PEAK_TFLOPS,
+            "traffic": traffic_from_profile("train_gate_up", source_sha("gemm.hip")),
+            "avg_launch_us": gu_us, "algorithmic_flops_per_launch": gu_flops,
+        },
+    }, T
+
+
+def train_cpu_baseline(torch, w, T, seconds):
+    """Oracle fwd + bwd of the first S tokens of the batch; tokens/s = S / time."""
+    import numpy as np
+    from oracle import staple_oracle as O
+    f64 = lambda t: t.float().cpu().numpy().astype(np.float64)
+    wg, wu, wd = (f64(T[k]) for k in ("w_gate", "w_up", "w_down"))
+    s_tokens = 64
+    done = 0
+    elapsed = 0.0
+    while elapsed < seconds and done < w.n_tokens:
+        sl = slice(done, done + s_tokens)
+        ids = T["ids_np"][sl]
+        uniq = np.unique(ids)
+        idx = torch.from_numpy(uniq.astype(np.int64)).to(T["table"].device)
+        table = _Rows(uniq, f64(T["table"][idx]))
+        x, dy = f64(T["x"][sl]), f64(T["dy"][sl])
+        t0 = time.perf_counter()
+        O.dedup(ids)
+        fw = O.ffn_forward(x, wg, wu, wd, table, ids, precision=O.BF16)
+        O.ffn_backward(dy, x, wg, wu, wd, fw, ids, precision=O.BF16)
+        elapsed += time.perf_counter() - t0
+        done += s_tokens
+    return {"value": done / elapsed, "unit": "tokens/s", "cores": oracle_threads(), "kind": "oracle",
+            "sample": f"first {done} tokens of the 32768-token batch in chunks of {s_tokens} "
+                      "(dedup + forward + backward, float64 numpy, bf16 rounding points)"}
+
+
+# ----------------------------------------------------------------------------
+def copy_probe(torch):
+    """A plain device copy of 1 GiB, five times: the reference for scaling the
+    FETCH_SIZE / WRITE_SIZE counters to bytes."""
+    a = torch.empty(1 << 29, dtype=torch.int16, device="cuda:0").fill_(1)
+    b = torch.empty_like(a)
+    torch.cuda.synchronize()
+    for _ in range(5):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_read_per_launch": a.numel() * 2,
+                      "copy_bytes_written_per_launch": b.numel() * 2}))
+
+
+def main(argv=None) -> int:
+    args = parse_args(argv)
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); "
+              "the multi-GPU path is not built.", file=sys.stderr)
+        return 2
+    import torch
+    if args.mode == "copy":
+        copy_probe(torch)
+        return 0
+    import staple_synth as S
+    import token_indexed_ffn_amd as st
+    st.lib()
+    torch.cuda.set_device(0)
+    wl = set(args.workloads.split(","))
+    out = {"metric": METRIC, "value": None, "unit": "tokens/s", "n_gpus": 1,
+           "steps": args.steps, "warmup": args.warmup, "ms_per_step": None,
+           "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+           "data": "synthetic: seeded Zipf(1.1) token IDs over vocab 100352 (fixed rank->ID "
+                   "permutation), x ~ N(0,1), weights and tables ~ N(0,0.02), bf16"}
+    w = S.OLMO1B_DECODE
+    if "decode" in wl:
+        dec, D = run_decode(torch, st, w, args.steps, args.warmup)
+        out["value"] = dec["tokens_per_s"]
+        out["ms_per_step"] = dec["ms_per_step"]
+        out["config"] = {"workload": w.name, "d_model": w.d_model, "d_ff": w.d_ff,
+                         "vocab": w.vocab, "batch": w.n_tokens, "layers": w.n_layers,
+                         "tables": "12 x 100352 x 8192 bf16, HBM-resident",
+                         "step": "12 x (staple_ffn_gate_up + staple_ffn_down), HIP graph replay"}
+        out["roofline"] = dec["roofline"]
+        out["decode"] = {k: v for k, v in dec.items() if k != "roofline"}
+        if not args.no_cpu_baseline:
+            out["cpu_baseline"] = decode_cpu_baseline(torch, w, D, args.cpu_seconds)
+        del D
+        torch.cuda.empty_cache()
+    if "train" in wl:
+        wt = S.OLMO1B_TRAIN
+        tr, T = run_train(torch, st, wt, args.train_steps, args.train_warmup)
+        if not args.no_cpu_baseline:
+            tr["cpu_baseline"] = train_cpu_baseline(torch, wt, T, args.cpu_seconds)
+        out["train"] = tr
+        if out["value"] is None:
+            out["value"] = tr["tokens_per_s"]
+            out["ms_per_step"] = tr["ms_per_step"]
+            out["roofline"] = tr["roofline"]
+            out["config"] = {"workload": wt.name}
+        del T
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,257 @@
+/*
+ * staple.h -- C ABI of libstaple, the MI355X (gfx950) hot path of the STAPLE
+ * embedding-augmented gated FFN.
+ *
+ * One augmented layer computes, for positions i = 0..N-1 with token IDs t_i:
+ *
+ *     g_i = W_gate x_i,  a_i = W_up x_i,  u_i = a_i + E[t_i],
+ *     h_i = silu(g_i) * u_i,  y_i = W_down h_i
+ *
+ * The pretrained up-projection is kept and the token-indexed table row is added
+ * to it as a residual path (STAPLE abstract; news synopsis "Pretrained models
+ * gain sparse capacity without retraining", Synopsis).  Only the rows of the
+ * tokens present in a batch are touched: the batch is deduplicated once and
+ * one inverse map serves every layer (STAPLE retrieval-path table, Prefill
+ * row); the active rows form a compact U x d_ff block whose gradient is the
+ * table-row gradient (AI Radio episode on STAPLE, paper summary).  The most
+ * frequent rows live in an HBM cache and misses come from pinned host memory
+ * (STAPLE Table 4 caption; retrieval-path table, Prefill and Decode rows).
+ *
+ * Conventions shared by every entry point:
+ *   - Pointers are DEVICE pointers owned by the caller unless marked "host".
+ *     The library never frees or retains them.
+ *   - Every call is asynchronous on `stream` (a hipStream_t; NULL = the null
+ *     stream) and returns a staple_status_t.  A non-OK status from argument
+ *     validation means nothing was enqueued and no output was written.
+ *   - No call allocates device memory.  Scratch comes from a caller-provided
+ *     workspace `ws` of `ws_bytes` bytes (256-byte aligned), sized by the
+ *     matching *_workspace_bytes query.
+ *   - Matrices are row-major.  Weights use the (out_features x in_features)
+ *     layout: w_gate, w_up are [d_ff x d_model], w_down is [d_model x d_ff].
+ *     Tables are token-major: row t is the d_ff-wide row of token t.
+ *   - Counts whose value is only known on the device (n_unique, n_miss) are
+ *     int32 device scalars; arrays they size are allocated by the caller for
+ *     the worst case.
+ *   - A token ID or row index outside its valid range found by a kernel is
+ *     not read; the kernel records it in a per-device error word instead and
+ *     the affected output is unspecified.  staple_get_device_error() reports
+ *     and clears that word.
+ */
+#ifndef STAPLE_H
+#define STAPLE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t staple_status_t;
+
+#define STAPLE_OK 0
+#define STAPLE_ERR_INVALID_ARGUMENT (-1)  /* null pointer, bad size, misalignment */
+#define STAPLE_ERR_UNSUPPORTED (-2)       /* dtype or shape the kernels do not handle */
+#define STAPLE_ERR_WORKSPACE (-3)         /* workspace smaller than the query returned */
+#define STAPLE_ERR_HIP (-4)               /* a HIP runtime call failed */
+#define STAPLE_ERR_INDEX_RANGE (-5)       /* a kernel met an out-of-range ID or index */
+#define STAPLE_ERR_HOST (-6)              /* host-side failure (thread pool, host ID check) */
+
+/* Element types.  STAPLE_BF16: bfloat16 storage, fp32 accumulation.
+ * STAPLE_F32: fp32 storage and accumulation. */
+#define STAPLE_F32 0
+#define STAPLE_BF16 1
+
+/* Human-readable text of a status code (static storage). */
+const char* staple_status_string(staple_status_t status);
+
+/* Library version string (static storage). */
+const char* staple_version(void);
+
+/* Waits for `stream`, then reads and clears the calling device's error word.
+ * Returns STAPLE_OK, or STAPLE_ERR_INDEX_RANGE if any kernel since the last
+ * call met an out-of-range ID or index. */
+staple_status_t staple_get_device_error(void* stream);
+
+/* ------------------------------------------------------------------------
+ * Batch dedup.  The batch's token IDs are deduplicated once and the inverse
+ * map is reused by every augmented layer (STAPLE retrieval-path table,
+ * Prefill row).
+ *
+ * Inputs : ids[n_tokens] int32, each in [0, vocab).
+ * Outputs: uniq[n_tokens]      distinct IDs in ascending order; first
+ *                              *n_unique entries are defined.
+ *          inv[n_tokens]       uniq[inv[i]] == ids[i].
+ *          sorted_pos[n_tokens] positions ordered by (ids[i], i) ascending.
+ *          seg_start[n_tokens+1] sorted_pos[seg_start[u] .. seg_start[u+1])
+ *                              are the positions of uniq[u]; entry *n_unique
+ *                              equals n_tokens.
+ *          n_unique            int32 device scalar, U.
+ * n_tokens may be 0 (then *n_unique = 0 and seg_start[0] = 0).
+ * vocab must be in [1, 2^31-1].  Out-of-range IDs set the device error word.
+ * The result is deterministic (no atomics decide any output).
+ * ------------------------------------------------------------------------ */
+size_t staple_dedup_workspace_bytes(int64_t n_tokens);
+staple_status_t staple_dedup(const int32_t* ids, int64_t n_tokens, int64_t vocab,
+                             int32_t* uniq, int32_t* inv, int32_t* sorted_pos,
+                             int32_t* seg_start, int32_t* n_unique,
+                             void* ws, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Frequency-aware row cache: a static cache of the most frequent rows,
+ * about 5% of the vocabulary (AI Radio episode on STAPLE: 5-6% cached,
+ * frequency-aware; STAPLE Table 4 caption: 1 GB GPU cache).  One id->slot map
+ * serves every layer; each layer has its own [capacity x d_ff] slot rows.
+ * ------------------------------------------------------------------------ */
+
+/* Count pass: counts[ids[i]] += 1 for every i (counts int64[vocab], not
+ * cleared by the call).  Out-of-range IDs set the device error word. */
+staple_status_t staple_cache_count(const int32_t* ids, int64_t n_tokens, int64_t vocab,
+                                   int64_t* counts, void* stream);
+
+/* Ranks IDs by count (larger first, ties by smaller ID) and assigns slot s to
+ * the ID of rank s for s < capacity.  When fewer IDs than `capacity` have a
+ * non-zero count the ranking still fills every slot.
+ * counts int64[vocab], each in [0, 2^31-1] (larger values set the error word).
+ * Outputs: id_to_slot int32[vocab] (slot, or -1 when not cached),
+ *          slot_to_id int32[capacity].
+ * 0 <= capacity <= vocab. */
+size_t staple_cache_build_workspace_bytes(int64_t vocab);
+staple_status_t staple_cache_build(const int64_t* counts, int64_t vocab, int64_t capacity,
+                                   int32_t* id_to_slot, int32_t* slot_to_id,
+                                   void* ws, size_t ws_bytes, void* stream);
+
+/* Copies the cached rows of one layer's table into its slot rows:
+ * slot_rows[s] = table[slot_to_id[s]] for s < capacity.  `table` is
+ * [vocab x d_ff] of `dtype`, in device memory or in pinned host memory that
+ * the device can address (hipHostMalloc). */
+staple_status_t staple_cache_fill(const void* table, int64_t vocab, int64_t d_ff, int32_t dtype,
+                                  const int32_t* slot_to_id, int64_t capacity,
+                                  void* slot_rows, void* stream);
+
+/* Probes the cache for each unique ID (STAPLE retrieval-path table: a GPU
+ * lookup probes the LFU cache) and compacts the misses in ascending order of
+ * unique index.
+ * Inputs : uniq[max_unique], n_unique (device scalar, <= max_unique),
+ *          id_to_slot int32[vocab].
+ * Outputs: code[max_unique]   slot of uniq[u] on a hit, -1-m on a miss where
+ *                             m is u's place in the miss list.
+ *          miss_uidx[max_unique] unique indices of the misses (first *n_miss).
+ *          miss_ids[max_unique]  their token IDs (first *n_miss); may be NULL.
+ *          n_miss               int32 device scalar. */
+staple_status_t staple_cache_lookup(const int32_t* uniq, const int32_t* n_unique, int64_t max_unique,
+                                    const int32_t* id_to_slot, int64_t vocab,
+                                    int32_t* code, int32_t* miss_uidx, int32_t* miss_ids,
+                                    int32_t* n_miss, void* stream);
+
+/* Miss staging (STAPLE retrieval-path table, Prefill row: only cache-miss rows
+ * come from the CPU, packed into pinned host buffers and sent with bulk
+ * asynchronous host-to-device copies).  Runs on the calling thread: packs
+ * rows host_table[host_miss_ids[m]] into host_staging (pinned,
+ * [n_miss x d_ff]) with a pool of host threads, then enqueues one
+ * hipMemcpyAsync host_staging -> dev_miss_rows on `stream` (normally a side
+ * stream; the caller records an event after it).  The caller must not reuse
+ * host_staging until that copy has completed.
+ * host_table: host [vocab x d_ff]; host_miss_ids: host int32[n_miss], each in
+ * [0, vocab) (checked on the host: STAPLE_ERR_HOST names a bad ID and nothing
+ * is copied). */
+staple_status_t staple_stage_misses(const void* host_table, int64_t vocab, int64_t d_ff,
+                                    int32_t dtype, const int32_t* host_miss_ids, int32_t n_miss,
+                                    void* host_staging, void* dev_miss_rows, void* stream);
+
+/* Compact leaf block assembly (AI Radio episode: only the active U x d_ff rows
+ * are materialised on the GPU).
+ * rows[u] = code[u] >= 0 ? cache_rows[code[u]] : miss_rows[-1-code[u]]
+ * for u < *n_unique.  cache_rows [capacity x d_ff], miss_rows [>= n_miss x d_ff]. */
+staple_status_t staple_assemble_rows(const void* cache_rows, int64_t capacity,
+                                     const void* miss_rows, int64_t max_miss,
+                                     const int32_t* code, const int32_t* n_unique,
+                                     int64_t max_unique, int64_t d_ff, int32_t dtype,
+                                     void* rows, void* stream);
+
+/* Row gather: dst[r] = src[index[r]] for r < n, where n = *n_rows when n_rows
+ * is non-NULL (a device scalar, <= max_rows) and max_rows otherwise.
+ * src [src_rows x d_ff], dst [max_rows x d_ff].  Used to build the compact
+ * block R = E[uniq] when the whole table is device-resident. */
+staple_status_t staple_gather_rows(const void* src, int64_t src_rows, const int32_t* index,
+                                   const int32_t* n_rows, int64_t max_rows, int64_t d_ff,
+                                   int32_t dtype, void* dst, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Forward of one augmented layer.
+ *   x [n_tokens x d_model] (dtype), w_gate, w_up [d_ff x d_model],
+ *   w_down [d_model x d_ff] (dtype);
+ *   rows [n_rows x d_ff] (dtype): the compact block R with row_index = inv,
+ *   or a whole device-resident table with row_index = the token IDs.
+ *   row_index int32[n_tokens], each in [0, n_rows).
+ * Outputs: y [n_tokens x d_model] of out_dtype (STAPLE_F32 or STAPLE_BF16).
+ *   save_g, save_u, save_h [n_tokens x d_ff] (dtype), each nullable: the
+ *   pre-activation g, the up branch u = W_up x + E[t] and h, for the backward.
+ * Layout requirements: d_model and d_ff multiples of 64; 16-byte aligned
+ * pointers.  n_tokens >= 0 (0 enqueues nothing).
+ * In bf16, g, u and y accumulate in fp32; h is rounded to bf16 once (the
+ * operand of the down-projection); saved g and u are rounded to bf16.
+ * ------------------------------------------------------------------------ */
+size_t staple_ffn_fwd_workspace_bytes(int64_t n_tokens, int64_t d_model, int64_t d_ff,
+                                      int32_t dtype);
+staple_status_t staple_ffn_fwd(int64_t n_tokens, int64_t d_model, int64_t d_ff,
+                               int32_t dtype, int32_t out_dtype,
+                               const void* x, const void* w_gate, const void* w_up,
+                               const void* w_down, const void* rows, int64_t n_rows,
+                               const int32_t* row_index, void* y,
+                               void* save_g, void* save_u, void* save_h,
+                               void* ws, size_t ws_bytes, void* stream);
+
+/* The two halves of staple_ffn_fwd, for callers that schedule them apart.
+ * staple_ffn_gate_up: h = silu(W_gate x) * (W_up x + rows[row_index]) into
+ *   h [n_tokens x d_ff] (dtype), with optional saves of g and u; the table
+ *   rows are gathered inside the GEMM's epilogue (STAPLE retrieval-path table:
+ *   compact-row reconstruction fused with the FFN).
+ * staple_ffn_down: y = W_down h, y of out_dtype.
+ * Same layout rules and error behaviour as staple_ffn_fwd. */
+staple_status_t staple_ffn_gate_up(int64_t n_tokens, int64_t d_model, int64_t d_ff, int32_t dtype,
+                                   const void* x, const void* w_gate, const void* w_up,
+                                   const void* rows, int64_t n_rows, const int32_t* row_index,
+                                   void* h, void* save_g, void* save_u, void* stream);
+staple_status_t staple_ffn_down(int64_t n_tokens, int64_t d_model, int64_t d_ff, int32_t dtype,
+                                int32_t out_dtype, const void* h, const void* w_down, void* y,
+                                void* stream);
+
+/* ------------------------------------------------------------------------
+ * Backward of one augmented layer with the table-row gradient.
+ *   dy [n_tokens x d_model] (dtype): upstream gradient of y.
+ *   saved_g, saved_u, saved_h: the forward's save_g/save_u/save_h (required).
+ *   sorted_pos, seg_start, n_unique: staple_dedup's outputs for this batch.
+ * Outputs (each overwritten, not accumulated):
+ *   d_rows [max_unique x d_ff] fp32: row u (< *n_unique) is the sum, over the
+ *     positions holding token uniq[u], of dL/du at that position (a plain sum,
+ *     no averaging).
+ *   dx [n_tokens x d_model] of out_dtype.
+ *   dw_gate, dw_up [d_ff x d_model] fp32; dw_down [d_model x d_ff] fp32.
+ *   freeze_up != 0: the up-projection is frozen (STAPLE Table 3 caption:
+ *     frozen during warmup); dw_up is neither computed nor written (may be
+ *     NULL) while the gradient still flows through W_up into dx and d_rows.
+ * In bf16 the backward reads bf16 g and u, forms dL/du and dL/dg in fp32 and
+ * rounds them to bf16 once; every contraction accumulates in fp32; d_rows sums
+ * the bf16 dL/du values in fp32.
+ * ------------------------------------------------------------------------ */
+size_t staple_ffn_bwd_workspace_bytes(int64_t n_tokens, int64_t d_model, int64_t d_ff,
+                                      int32_t dtype);
+staple_status_t staple_ffn_bwd_table_grad(int64_t n_tokens, int64_t d_model, int64_t d_ff,
+                                          int32_t dtype, int32_t out_dtype,
+                                          const void* dy, const void* x,
+                                          const void* w_gate, const void* w_up, const void* w_down,
+                                          const void* saved_g, const void* saved_u,
+                                          const void* saved_h,
+                                          const int32_t* sorted_pos, const int32_t* seg_start,
+                                          const int32_t* n_unique, int64_t max_unique,
+                                          float* d_rows, void* dx,
+                                          float* dw_gate, float* dw_up, float* dw_down,
+                                          int32_t freeze_up, void* ws, size_t ws_bytes,
+                                          void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* STAPLE_H */

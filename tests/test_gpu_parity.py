@@ -1,0 +1,408 @@
+"""GPU parity of the HIP path against the CPU oracle, through the C ABI.
+
+Integer outputs (dedup, inverse map, cache slots, miss lists, gathered rows)
+must match bit for bit.  Floating-point outputs must be within relative L2
+error 5e-3 and max-abs error 3e-2 of the oracle (bf16 inputs, fp32
+accumulation; the oracle runs in float64 with bf16 rounding at the points
+where the bf16 path stores bf16, and exactly for the fp32 workload).
+"""
+import sys
+
+import numpy as np
+import pytest
+
+import staple_synth as S
+from oracle import staple_oracle as O
+from tests.helpers import assert_close, assert_close_long_sum, errors, to_dev, to_np
+
+pytestmark = pytest.mark.gpu
+
+
+def _log(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def st():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import token_indexed_ffn_amd as st
+    st.lib()
+    return st
+
+
+@pytest.fixture(scope="module")
+def dev(st):
+    import torch
+    return torch.device("cuda:0")
+
+
+def _no_device_error(st):
+    assert st.staple_get_device_error() == 0
+
+
+# ---------------------------------------------------------------- dedup
+DEDUP_CASES = [
+    ("empty", 0, 10, None),
+    ("one", 1, 10, None),
+    ("decode64", 64, 100352, None),
+    ("pow2_512", 512, 4096, None),
+    ("tile_edge", 4096, 100352, None),
+    ("tile_edge_plus1", 4097, 100352, None),
+    ("ragged", 9999, 50, None),
+    ("train32k", 32768, 100352, None),
+    ("all_equal", 5000, 100352, "equal"),
+    ("all_distinct", 6000, 100352, "distinct"),
+]
+
+
+@pytest.mark.parametrize("name,n,vocab,kind", DEDUP_CASES, ids=[c[0] for c in DEDUP_CASES])
+def test_dedup_bit_exact(st, dev, name, n, vocab, kind):
+    import torch
+    _log(f"dedup case {name} n={n} vocab={vocab}")
+    if kind == "equal":
+        ids = np.full(n, 77, dtype=np.int32)
+    elif kind == "distinct":
+        ids = np.random.default_rng(3).permutation(vocab)[:n].astype(np.int32)
+    else:
+        ids = S.zipf_ids(n, vocab, 500 + n)
+    out = st.staple_dedup(torch.from_numpy(ids).to(dev), vocab)
+    torch.cuda.synchronize()
+    _no_device_error(st)
+    uniq, inv, sp, ss = O.dedup(ids)
+    u = len(uniq)
+    assert int(out["n_unique"].item()) == u
+    np.testing.assert_array_equal(to_np(out["uniq"])[:u], uniq)
+    np.testing.assert_array_equal(to_np(out["inv"])[:n], inv)
+    np.testing.assert_array_equal(to_np(out["sorted_pos"])[:n], sp)
+    np.testing.assert_array_equal(to_np(out["seg_start"])[: u + 1], ss)
+
+
+def test_dedup_flags_out_of_range_ids(st, dev):
+    import torch
+    ids = torch.tensor([3, 10, 2], dtype=torch.int32, device=dev)
+    st.staple_dedup(ids, 10)
+    assert st.staple_get_device_error() == -5
+    _no_device_error(st)  # the word was cleared
+
+
+# ---------------------------------------------------------------- cache
+@pytest.mark.parametrize("vocab,capacity,n_cal", [(4096, 205, 50_000), (100352, 5018, 1 << 20),
+                                                  (1000, 0, 5000), (1000, 1000, 5000)])
+def test_cache_count_build_lookup_bit_exact(st, dev, vocab, capacity, n_cal):
+    import torch
+    _log(f"cache vocab={vocab} capacity={capacity}")
+    cal = S.zipf_ids(n_cal, vocab, 8)
+    counts = st.staple_cache_count(torch.from_numpy(cal).to(dev), vocab)
+    ref_counts = np.bincount(cal, minlength=vocab)
+    np.testing.assert_array_equal(counts.cpu().numpy(), ref_counts)
+    id_to_slot, slot_to_id = st.staple_cache_build(counts, capacity)
+    torch.cuda.synchronize()
+    _no_device_error(st)
+    o_i2s, o_s2i = O.cache_build(ref_counts, capacity)
+    np.testing.assert_array_equal(to_np(id_to_slot), o_i2s)
+    if capacity:
+        np.testing.assert_array_equal(to_np(slot_to_id)[:capacity], o_s2i)
+
+    for n in (64, 32768):
+        ids = S.zipf_ids(n, vocab, 900 + n)
+        dd = st.staple_dedup(torch.from_numpy(ids).to(dev), vocab)
+        lk = st.staple_cache_lookup(dd["uniq"], dd["n_unique"], id_to_slot)
+        torch.cuda.synchronize()
+        _no_device_error(st)
+        uniq, _, _, _ = O.dedup(ids)
+        code, miss = O.cache_lookup(uniq, o_i2s)
+        u, m = len(uniq), len(miss)
+        assert int(lk["n_miss"].item()) == m
+        np.testing.assert_array_equal(to_np(lk["code"])[:u], code)
+        np.testing.assert_array_equal(to_np(lk["miss_uidx"])[:m], miss)
+        np.testing.assert_array_equal(to_np(lk["miss_ids"])[:m], uniq[miss])
+
+
+def test_compact_rows_hit_and_miss_paths_are_bit_identical(st, dev):
+    """R = E[uniq] bitwise, whether rows come from the HBM cache, from pinned
+    host staging, or from a device-resident table; capacity 0, 5% and full."""
+    import torch
+    vocab, f, n = 3000, 256, 2048
+    table_bits = S.normal_bf16_bits((vocab, f), 0.02, 77)
+    host_table = torch.from_numpy(table_bits.view(np.int16)).view(torch.bfloat16).pin_memory()
+    dev_table = host_table.to(dev)
+    ids = S.zipf_ids(n, vocab, 31)
+    dd = st.staple_dedup(torch.from_numpy(ids).to(dev), vocab)
+    uniq, _, _, _ = O.dedup(ids)
+    u = len(uniq)
+    expect = table_bits[uniq]
+    direct = st.staple_gather_rows(dev_table, dd["uniq"], dd["n_unique"])
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(direct[:u].cpu().view(torch.int16).numpy().view(np.uint16), expect)
+    counts = st.staple_cache_count(torch.from_numpy(S.zipf_ids(40_000, vocab, 8)).to(dev), vocab)
+    for capacity in (0, 150, vocab):
+        i2s, s2i = st.staple_cache_build(counts, capacity)
+        cache_rows = st.staple_cache_fill(host_table, s2i, capacity)   # reads pinned host memory
+        lk = st.staple_cache_lookup(dd["uniq"], dd["n_unique"], i2s)
+        torch.cuda.synchronize()
+        m = int(lk["n_miss"].item())
+        miss_ids = lk["miss_ids"][:m].cpu().contiguous()
+        staging = torch.empty(max(m, 1), f, dtype=torch.bfloat16).pin_memory()
+        miss_rows = torch.empty(max(m, 1), f, dtype=torch.bfloat16, device=dev)
+        side = torch.cuda.Stream()
+        st.staple_stage_misses(host_table, miss_ids, m, staging, miss_rows, stream=side)
+        torch.cuda.current_stream().wait_stream(side)
+        rows = st.staple_assemble_rows(cache_rows, miss_rows, lk["code"], dd["n_unique"])
+        torch.cuda.synchronize()
+        _no_device_error(st)
+        got = rows[:u].cpu().view(torch.int16).numpy().view(np.uint16)
+        np.testing.assert_array_equal(got, expect, err_msg=f"capacity {capacity}")
+
+
+# ---------------------------------------------------------------- FFN helpers
+def _run_layer(st, dev, inp, out_f32=True, freeze_up=False, backward=True, full_table=False):
+    import torch
+    dt = inp.dtype
+    tdt = torch.bfloat16 if dt == "bf16" else torch.float32
+    x, wg, wu, wd, tab, dy = (to_dev(getattr(inp, k), dt, dev)
+                              for k in ("x", "w_gate", "w_up", "w_down", "table", "dy"))
+    ids = torch.from_numpy(inp.ids).to(dev)
+    vocab = tab.shape[0]
+    dd = st.staple_dedup(ids, vocab)
+    if full_table:
+        rows, index = tab, ids
+    else:
+        rows = st.staple_gather_rows(tab, dd["uniq"], dd["n_unique"])
+        index = dd["inv"]
+    fwd = st.staple_ffn_fwd(x, wg, wu, wd, rows, index,
+                            out_dtype=torch.float32 if out_f32 else tdt, save=backward)
+    res = {"fwd": fwd, "dd": dd}
+    if backward:
+        out = None
+        if freeze_up:
+            n, f = inp.ids.shape[0], wg.shape[0]
+            d = x.shape[1]
+            out = {
+                "d_rows": torch.empty(max(n, 1), f, dtype=torch.float32, device=dev),
+                "dx": torch.empty(n, d, dtype=torch.float32 if out_f32 else tdt, device=dev),
+                "dw_gate": torch.empty(f, d, dtype=torch.float32, device=dev),
+                "dw_up": torch.full((f, d), float("nan"), dtype=torch.float32, device=dev),
+                "dw_down": torch.empty(d, f, dtype=torch.float32, device=dev),
+            }
+        res["bwd"] = st.staple_ffn_bwd_table_grad(
+            dy, x, wg, wu, wd, fwd["g"], fwd["u"], fwd["h"], dd["sorted_pos"], dd["seg_start"],
+            dd["n_unique"], freeze_up=freeze_up, out_dtype=torch.float32 if out_f32 else tdt,
+            out=out)
+    torch.cuda.synchronize()
+    _no_device_error(st)
+    return res
+
+
+def _oracle_layer(inp, precision, freeze_up=False):
+    g = {k: inp.as_f64(k) for k in ("x", "w_gate", "w_up", "w_down", "table", "dy")}
+    of = O.ffn_forward(g["x"], g["w_gate"], g["w_up"], g["w_down"], g["table"], inp.ids,
+                       precision=precision)
+    uniq, _, _, _ = O.dedup(inp.ids)
+    ob = O.ffn_backward(g["dy"], g["x"], g["w_gate"], g["w_up"], g["w_down"], of, inp.ids,
+                        precision=precision, freeze_up=freeze_up, uniq=uniq)
+    return of, ob, len(uniq)
+
+
+def _compare_layer(res, of, ob, u, name, freeze_up=False):
+    assert_close(to_np(res["fwd"]["y"]), of["y"], f"{name} y")
+    b = res["bwd"]
+    assert_close(to_np(b["dx"]), ob["dx"], f"{name} dx")
+    assert_close(to_np(b["d_rows"])[:u], ob["d_rows"], f"{name} d_rows")
+    assert_close(to_np(b["dw_gate"]), ob["dw_gate"], f"{name} dw_gate")
+    assert_close(to_np(b["dw_down"]), ob["dw_down"], f"{name} dw_down")
+    if freeze_up:
+        assert np.all(np.isnan(to_np(b["dw_up"]))), "dw_up was written while frozen"
+    else:
+        assert_close(to_np(b["dw_up"]), ob["dw_up"], f"{name} dw_up")
+
+
+# ---------------------------------------------------------------- FFN parity
+def test_tiny_fp32_layer_matches_oracle(st, dev):
+    """fp32 end to end: d_model 256, d_ff 1024, vocab 4096, 512 Zipf tokens."""
+    w = S.TINY_F32
+    _log("tiny fp32 layer")
+    inp = S.host_layer_inputs(w.n_tokens, w.d_model, w.d_ff, w.vocab, dtype="f32", seed=0)
+    res = _run_layer(st, dev, inp)
+    of, ob, u = _oracle_layer(inp, O.EXACT)
+    _compare_layer(res, of, ob, u, "tiny_f32")
+    # the table's contribution on its own (it is ~2% of y, so check it separately)
+    inp0 = S.host_layer_inputs(w.n_tokens, w.d_model, w.d_ff, w.vocab, dtype="f32", seed=0,
+                               zero_table=True)
+    res0 = _run_layer(st, dev, inp0)
+    of0, ob0, _ = _oracle_layer(inp0, O.EXACT)
+    _compare_layer(res0, of0, ob0, u, "tiny_f32_zero_table")
+    assert_close(to_np(res["fwd"]["y"]) - to_np(res0["fwd"]["y"]), of["y"] - of0["y"], "delta_y")
+
+
+@pytest.mark.parametrize("n,d,f,v,seed", [(300, 256, 512, 1000, 1), (1, 64, 128, 10, 2),
+                                          (129, 192, 320, 50, 3), (700, 128, 256, 4, 4)])
+def test_bf16_layer_matches_oracle(st, dev, n, d, f, v, seed):
+    _log(f"bf16 layer n={n} d={d} f={f} v={v}")
+    inp = S.host_layer_inputs(n, d, f, v, dtype="bf16", seed=seed)
+    res = _run_layer(st, dev, inp)
+    of, ob, u = _oracle_layer(inp, O.BF16)
+    _compare_layer(res, of, ob, u, f"bf16 n={n}")
+
+
+def test_bf16_table_contribution_and_large_table_values(st, dev):
+    """Rows with E ~ N(0,1) dominate u, so wrong rows cannot hide in tolerance."""
+    _log("bf16 strong table")
+    inp = S.host_layer_inputs(400, 128, 256, 300, dtype="bf16", seed=5, table_std=1.0)
+    res = _run_layer(st, dev, inp)
+    of, ob, u = _oracle_layer(inp, O.BF16)
+    _compare_layer(res, of, ob, u, "bf16 strong table")
+
+
+def test_zero_table_equals_dense_path_bitwise(st, dev):
+    """E = 0 reproduces the dense SwiGLU: the GPU y with a zero table equals
+    the GPU y with the table rows replaced by zeros through a full table."""
+    import torch
+    inp = S.host_layer_inputs(256, 128, 256, 64, dtype="bf16", seed=6, zero_table=True)
+    a = _run_layer(st, dev, inp, backward=False)
+    b = _run_layer(st, dev, inp, backward=False, full_table=True)
+    assert torch.equal(a["fwd"]["y"], b["fwd"]["y"])
+    of, _, _ = _oracle_layer(inp, O.BF16)
+    assert_close(to_np(a["fwd"]["y"]), of["y"], "zero-table y")
+
+
+def test_freeze_up_leaves_dw_up_untouched_and_rest_identical(st, dev):
+    import torch
+    inp = S.host_layer_inputs(333, 128, 192, 40, dtype="bf16", seed=7)
+    a = _run_layer(st, dev, inp)
+    b = _run_layer(st, dev, inp, freeze_up=True)
+    assert np.all(np.isnan(to_np(b["bwd"]["dw_up"])))
+    u = int(a["dd"]["n_unique"].item())
+    assert torch.equal(a["bwd"]["d_rows"][:u], b["bwd"]["d_rows"][:u])
+    for k in ("dx", "dw_gate", "dw_down"):
+        assert torch.equal(a["bwd"][k], b["bwd"][k]), k
+    of, ob, u = _oracle_layer(inp, O.BF16, freeze_up=True)
+    _compare_layer(b, of, ob, u, "frozen", freeze_up=True)
+
+
+def test_bf16_outputs_stored_in_bf16(st, dev):
+    inp = S.host_layer_inputs(256, 128, 256, 100, dtype="bf16", seed=8)
+    res = _run_layer(st, dev, inp, out_f32=False)
+    of, ob, u = _oracle_layer(inp, O.BF16)
+    assert_close(to_np(res["fwd"]["y"]), of["y"], "y bf16 store")
+    assert_close(to_np(res["bwd"]["dx"]), ob["dx"], "dx bf16 store")
+
+
+def test_empty_batch(st, dev):
+    import torch
+    d, f = 64, 128
+    z = torch.zeros(0, d, dtype=torch.bfloat16, device=dev)
+    w = torch.randn(f, d, device=dev).to(torch.bfloat16)
+    wd = torch.randn(d, f, device=dev).to(torch.bfloat16)
+    tab = torch.randn(10, f, device=dev).to(torch.bfloat16)
+    ids = torch.zeros(0, dtype=torch.int32, device=dev)
+    dd = st.staple_dedup(ids, 10)
+    fwd = st.staple_ffn_fwd(z, w, w, wd, tab, ids, save=True)
+    for k in ("g", "u", "h"):
+        assert fwd[k].shape == (0, f)
+    b = st.staple_ffn_bwd_table_grad(z, z, w, w, wd, fwd["g"], fwd["u"], fwd["h"],
+                                     dd["sorted_pos"], dd["seg_start"], dd["n_unique"])
+    torch.cuda.synchronize()
+    assert int(dd["n_unique"].item()) == 0
+    for k in ("dw_gate", "dw_up", "dw_down"):
+        assert torch.all(b[k] == 0), k
+
+
+# ---------------------------------------------------------------- full-size, sampled
+class RowSubset:
+    """A [vocab x f] table that stores only some rows (fetched from the device)."""
+
+    def __init__(self, ids_sorted, rows):
+        self.ids = np.asarray(ids_sorted)
+        self.rows = rows
+
+    def __getitem__(self, key):
+        if isinstance(key, tuple):
+            r, c = key
+            return self.rows[np.searchsorted(self.ids, np.asarray(r).reshape(-1))][:, np.asarray(c).reshape(-1)] \
+                .reshape(np.asarray(r).shape[0], -1)
+        return self.rows[np.searchsorted(self.ids, np.asarray(key))]
+
+
+def _device_inputs(dev, w, n_tokens, seed_base=0):
+    import torch
+    from staple_synth import device_normal
+    d, f, v = w.d_model, w.d_ff, w.vocab
+    ids = S.zipf_ids(n_tokens, v, w.ids_seed + seed_base)
+    t = {
+        "x": device_normal((n_tokens, d), 1.0, 2000 + seed_base, torch.bfloat16, dev),
+        "w_gate": device_normal((f, d), 0.02, 3000 + seed_base, torch.bfloat16, dev),
+        "w_up": device_normal((f, d), 0.02, 3001 + seed_base, torch.bfloat16, dev),
+        "w_down": device_normal((d, f), 0.02, 3002 + seed_base, torch.bfloat16, dev),
+        "table": device_normal((v, f), 0.02, 4000 + seed_base, torch.bfloat16, dev),
+        "dy": device_normal((n_tokens, d), 1.0, 5000 + seed_base, torch.bfloat16, dev),
+    }
+    return ids, t
+
+
+def test_olmo1b_train_shape_sampled(st, dev):
+    """32768 Zipf tokens, d_model 2048, d_ff 8192, vocab 100352, bf16: every
+    integer output in full; y, dx on sampled tokens and d_rows, dW on sampled
+    features, each computed by the oracle over the whole batch."""
+    import torch
+    w = S.OLMO1B_TRAIN
+    n, d, f = w.n_tokens, w.d_model, w.d_ff
+    _log("olmo1b train-shape sampled parity")
+    ids, t = _device_inputs(dev, w, n)
+    idt = torch.from_numpy(ids).to(dev)
+    dd = st.staple_dedup(idt, w.vocab)
+    rows = st.staple_gather_rows(t["table"], dd["uniq"], dd["n_unique"])
+    fwd = st.staple_ffn_fwd(t["x"], t["w_gate"], t["w_up"], t["w_down"], rows, dd["inv"],
+                            out_dtype=torch.float32, save=True)
+    bwd = st.staple_ffn_bwd_table_grad(t["dy"], t["x"], t["w_gate"], t["w_up"], t["w_down"],
+                                       fwd["g"], fwd["u"], fwd["h"], dd["sorted_pos"],
+                                       dd["seg_start"], dd["n_unique"], out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    _no_device_error(st)
+    uniq, inv, sp, ss = O.dedup(ids)
+    u = len(uniq)
+    assert int(dd["n_unique"].item()) == u
+    np.testing.assert_array_equal(to_np(dd["inv"]), inv)
+    np.testing.assert_array_equal(to_np(dd["sorted_pos"]), sp)
+    np.testing.assert_array_equal(to_np(dd["seg_start"])[: u + 1], ss)
+    f64 = lambda a: a.float().cpu().numpy().astype(np.float64)
+    table = RowSubset(uniq, f64(t["table"][torch.from_numpy(uniq.astype(np.int64)).to(dev)]))
+    x, wg, wu, wdn, dy = (f64(t[k]) for k in ("x", "w_gate", "w_up", "w_down", "dy"))
+    rng = np.random.default_rng(0)
+    rows_s = np.concatenate([[0, n - 1], rng.choice(n, 30, replace=False)])
+    cols_s = np.concatenate([[0, f - 1], rng.choice(f, 14, replace=False)])
+    # forward and dx on sampled tokens (all features)
+    of_r = O.ffn_forward(x[rows_s], wg, wu, wdn, table, ids[rows_s], precision=O.BF16)
+    assert_close(f64(fwd["y"])[rows_s], of_r["y"], "y[rows]")
+    ob_r = O.ffn_backward(dy[rows_s], x[rows_s], wg, wu, wdn, of_r, ids[rows_s], precision=O.BF16)
+    assert_close(f64(bwd["dx"])[rows_s], ob_r["dx"], "dx[rows]")
+    # table-row and weight gradients on sampled features (all tokens)
+    of_c = O.ffn_forward(x, wg, wu, wdn, table, ids, precision=O.BF16, cols=cols_s)
+    ob_c = O.ffn_backward(dy, x, wg, wu, wdn, of_c, ids, precision=O.BF16, cols=cols_s, uniq=uniq)
+    cs = torch.from_numpy(cols_s).to(dev)
+    assert_close(f64(bwd["d_rows"][:u][:, cs]), ob_c["d_rows"], "d_rows[:, cols]")
+    assert_close_long_sum(f64(bwd["dw_gate"][cs]), ob_c["dw_gate"], "dw_gate[cols]")
+    assert_close_long_sum(f64(bwd["dw_up"][cs]), ob_c["dw_up"], "dw_up[cols]")
+    assert_close_long_sum(f64(bwd["dw_down"][:, cs]), ob_c["dw_down"], "dw_down[:, cols]")
+
+
+def test_olmo1b_decode_layer_full(st, dev):
+    """Decode batch of 64 over a full 100352 x 8192 table in HBM, rows gathered
+    by token ID inside the fused epilogue; every output compared."""
+    import torch
+    w = S.OLMO1B_DECODE
+    _log("olmo1b decode layer")
+    ids, t = _device_inputs(dev, w, w.n_tokens)
+    idt = torch.from_numpy(ids).to(dev)
+    fwd = st.staple_ffn_fwd(t["x"], t["w_gate"], t["w_up"], t["w_down"], t["table"], idt,
+                            out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    _no_device_error(st)
+    f64 = lambda a: a.float().cpu().numpy().astype(np.float64)
+    uniq = np.unique(ids)
+    table = RowSubset(uniq, f64(t["table"][torch.from_numpy(uniq.astype(np.int64)).to(dev)]))
+    of = O.ffn_forward(f64(t["x"]), f64(t["w_gate"]), f64(t["w_up"]), f64(t["w_down"]), table,
+                       ids, precision=O.BF16)
+    assert_close(f64(fwd["y"]), of["y"], "decode y")

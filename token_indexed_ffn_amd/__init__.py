@@ -1,0 +1,281 @@
+"""Python binding of libstaple, the gfx950 hot path of the STAPLE
+embedding-augmented gated FFN.
+
+Each function here has the name of the C entry point it calls and does
+argument marshalling only: it checks tensor placement, allocates outputs with
+torch when the caller passes none, and forwards raw device pointers and the
+current HIP stream to the library.  Every step of the computation runs in the
+library's kernels; there is no Python or CPU fallback.
+"""
+from __future__ import annotations
+
+from typing import Optional
+
+import torch
+
+from . import _lib
+
+F32 = 0
+BF16 = 1
+
+_DT = {torch.float32: F32, torch.bfloat16: BF16}
+_TORCH_DT = {F32: torch.float32, BF16: torch.bfloat16}
+
+
+class StapleError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__(f"{what}: status {status} ({_lib.load().staple_status_string(status).decode()})")
+
+
+def lib():
+    return _lib.load()
+
+
+def _check(status: int, what: str) -> None:
+    if status != 0:
+        raise StapleError(status, what)
+
+
+def _dt(t: torch.Tensor) -> int:
+    try:
+        return _DT[t.dtype]
+    except KeyError:
+        raise TypeError(f"unsupported dtype {t.dtype}; use bfloat16 or float32") from None
+
+
+def _p(t: Optional[torch.Tensor]) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _dev(*ts) -> None:
+    for t in ts:
+        if t is not None and (not t.is_cuda or not t.is_contiguous()):
+            raise ValueError("expected contiguous device tensors")
+
+
+def _stream(stream) -> int:
+    s = torch.cuda.current_stream() if stream is None else stream
+    return s.cuda_stream
+
+
+def _ws(nbytes: int, workspace: Optional[torch.Tensor], device) -> Optional[torch.Tensor]:
+    if nbytes == 0:
+        return workspace
+    if workspace is not None:
+        if workspace.numel() * workspace.element_size() < nbytes:
+            raise ValueError(f"workspace of {nbytes} bytes required")
+        return workspace
+    return torch.empty(nbytes, dtype=torch.uint8, device=device)
+
+
+def _ws_size(w: Optional[torch.Tensor]) -> int:
+    return 0 if w is None else w.numel() * w.element_size()
+
+
+# ----------------------------------------------------------------------------
+def staple_get_device_error(stream=None) -> int:
+    """Synchronises the stream and returns (and clears) the device error status."""
+    return lib().staple_get_device_error(_stream(stream))
+
+
+def staple_dedup(ids: torch.Tensor, vocab: int, *, out: Optional[dict] = None,
+                 workspace: Optional[torch.Tensor] = None, stream=None) -> dict:
+    """Dedup of one batch: uniq, inv, sorted_pos, seg_start, n_unique (device)."""
+    _dev(ids)
+    assert ids.dtype == torch.int32
+    n = ids.numel()
+    dev = ids.device
+    if out is None:
+        out = {
+            "uniq": torch.empty(max(n, 1), dtype=torch.int32, device=dev),
+            "inv": torch.empty(max(n, 1), dtype=torch.int32, device=dev),
+            "sorted_pos": torch.empty(max(n, 1), dtype=torch.int32, device=dev),
+            "seg_start": torch.empty(n + 1, dtype=torch.int32, device=dev),
+            "n_unique": torch.empty(1, dtype=torch.int32, device=dev),
+        }
+    ws = _ws(lib().staple_dedup_workspace_bytes(n), workspace, dev)
+    _check(lib().staple_dedup(_p(ids), n, int(vocab), _p(out["uniq"]), _p(out["inv"]),
+                              _p(out["sorted_pos"]), _p(out["seg_start"]), _p(out["n_unique"]),
+                              _p(ws), _ws_size(ws), _stream(stream)), "staple_dedup")
+    return out
+
+
+def staple_cache_count(ids: torch.Tensor, vocab: int, counts: Optional[torch.Tensor] = None,
+                       stream=None) -> torch.Tensor:
+    _dev(ids, counts)
+    if counts is None:
+        counts = torch.zeros(vocab, dtype=torch.int64, device=ids.device)
+    _check(lib().staple_cache_count(_p(ids), ids.numel(), int(vocab), _p(counts), _stream(stream)),
+           "staple_cache_count")
+    return counts
+
+
+def staple_cache_build(counts: torch.Tensor, capacity: int, *, out: Optional[tuple] = None,
+                       workspace: Optional[torch.Tensor] = None, stream=None):
+    """Returns (id_to_slot int32[vocab], slot_to_id int32[capacity])."""
+    _dev(counts)
+    assert counts.dtype == torch.int64
+    vocab = counts.numel()
+    if out is None:
+        out = (torch.empty(vocab, dtype=torch.int32, device=counts.device),
+               torch.empty(max(capacity, 1), dtype=torch.int32, device=counts.device))
+    ws = _ws(lib().staple_cache_build_workspace_bytes(vocab), workspace, counts.device)
+    _check(lib().staple_cache_build(_p(counts), vocab, int(capacity), _p(out[0]), _p(out[1]),
+                                    _p(ws), _ws_size(ws), _stream(stream)), "staple_cache_build")
+    return out
+
+
+def staple_cache_fill(table: torch.Tensor, slot_to_id: torch.Tensor, capacity: int,
+                      out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """slot_rows[s] = table[slot_to_id[s]]; `table` on the device or pinned host memory."""
+    _dev(slot_to_id, out)
+    vocab, d_ff = table.shape
+    if out is None:
+        out = torch.empty(max(capacity, 1), d_ff, dtype=table.dtype, device=slot_to_id.device)
+    _check(lib().staple_cache_fill(_p(table), vocab, d_ff, _dt(table), _p(slot_to_id), int(capacity),
+                                   _p(out), _stream(stream)), "staple_cache_fill")
+    return out
+
+
+def staple_cache_lookup(uniq: torch.Tensor, n_unique: torch.Tensor, id_to_slot: torch.Tensor, *,
+                        out: Optional[dict] = None, stream=None) -> dict:
+    """code, miss_uidx, miss_ids, n_miss for the first *n_unique unique IDs."""
+    _dev(uniq, n_unique, id_to_slot)
+    mu = uniq.numel()
+    if out is None:
+        out = {k: torch.empty(max(mu, 1), dtype=torch.int32, device=uniq.device)
+               for k in ("code", "miss_uidx", "miss_ids")}
+        out["n_miss"] = torch.empty(1, dtype=torch.int32, device=uniq.device)
+    _check(lib().staple_cache_lookup(_p(uniq), _p(n_unique), mu, _p(id_to_slot), id_to_slot.numel(),
+                                     _p(out["code"]), _p(out["miss_uidx"]), _p(out.get("miss_ids")),
+                                     _p(out["n_miss"]), _stream(stream)), "staple_cache_lookup")
+    return out
+
+
+def staple_stage_misses(host_table: torch.Tensor, host_miss_ids: torch.Tensor, n_miss: int,
+                        host_staging: torch.Tensor, dev_miss_rows: torch.Tensor,
+                        stream=None) -> None:
+    """Pack host_table[host_miss_ids[:n_miss]] into pinned staging, then one async H2D copy."""
+    assert not host_table.is_cuda and not host_miss_ids.is_cuda and not host_staging.is_cuda
+    assert host_miss_ids.dtype == torch.int32 and host_table.is_contiguous()
+    vocab, d_ff = host_table.shape
+    _check(lib().staple_stage_misses(_p(host_table), vocab, d_ff, _dt(host_table), _p(host_miss_ids),
+                                     int(n_miss), _p(host_staging), _p(dev_miss_rows),
+                                     _stream(stream)), "staple_stage_misses")
+
+
+def staple_assemble_rows(cache_rows: torch.Tensor, miss_rows: torch.Tensor, code: torch.Tensor,
+                         n_unique: torch.Tensor, out: Optional[torch.Tensor] = None,
+                         stream=None) -> torch.Tensor:
+    _dev(cache_rows, miss_rows, code, n_unique, out)
+    d_ff = cache_rows.shape[1]
+    mu = code.numel()
+    if out is None:
+        out = torch.empty(mu, d_ff, dtype=cache_rows.dtype, device=code.device)
+    _check(lib().staple_assemble_rows(_p(cache_rows), cache_rows.shape[0], _p(miss_rows),
+                                      miss_rows.shape[0], _p(code), _p(n_unique), mu, d_ff,
+                                      _dt(cache_rows), _p(out), _stream(stream)),
+           "staple_assemble_rows")
+    return out
+
+
+def staple_gather_rows(src: torch.Tensor, index: torch.Tensor, n_rows: Optional[torch.Tensor] = None,
+                       out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    _dev(src, index, n_rows, out)
+    d_ff = src.shape[1]
+    mr = index.numel()
+    if out is None:
+        out = torch.empty(mr, d_ff, dtype=src.dtype, device=src.device)
+    _check(lib().staple_gather_rows(_p(src), src.shape[0], _p(index), _p(n_rows), mr, d_ff,
+                                    _dt(src), _p(out), _stream(stream)), "staple_gather_rows")
+    return out
+
+
+def staple_ffn_fwd(x: torch.Tensor, w_gate: torch.Tensor, w_up: torch.Tensor,
+                   w_down: torch.Tensor, rows: torch.Tensor, row_index: torch.Tensor, *,
+                   out_dtype: Optional[torch.dtype] = None, save: bool = False,
+                   out: Optional[dict] = None, workspace: Optional[torch.Tensor] = None,
+                   stream=None) -> dict:
+    """Forward of one augmented layer.  Returns {"y"} (+ "g", "u", "h" when save)."""
+    _dev(x, w_gate, w_up, w_down, rows, row_index)
+    n, d = x.shape
+    f = w_gate.shape[0]
+    dt = _dt(x)
+    out_dtype = out_dtype or x.dtype
+    if out is None:
+        out = {"y": torch.empty(n, d, dtype=out_dtype, device=x.device)}
+        if save:
+            for k in ("g", "u", "h"):
+                out[k] = torch.empty(n, f, dtype=x.dtype, device=x.device)
+    need = 0 if out.get("h") is not None else lib().staple_ffn_fwd_workspace_bytes(n, d, f, dt)
+    ws = _ws(need, workspace, x.device)
+    _check(lib().staple_ffn_fwd(n, d, f, dt, _DT[out["y"].dtype], _p(x), _p(w_gate), _p(w_up),
+                                _p(w_down), _p(rows), rows.shape[0], _p(row_index), _p(out["y"]),
+                                _p(out.get("g")), _p(out.get("u")), _p(out.get("h")), _p(ws),
+                                _ws_size(ws), _stream(stream)), "staple_ffn_fwd")
+    return out
+
+
+def staple_ffn_gate_up(x: torch.Tensor, w_gate: torch.Tensor, w_up: torch.Tensor,
+                       rows: torch.Tensor, row_index: torch.Tensor, h: torch.Tensor,
+                       save_g: Optional[torch.Tensor] = None, save_u: Optional[torch.Tensor] = None,
+                       stream=None) -> torch.Tensor:
+    """h = silu(x W_gate^T) * (x W_up^T + rows[row_index]) (fused gather epilogue)."""
+    _dev(x, w_gate, w_up, rows, row_index, h, save_g, save_u)
+    n, d = x.shape
+    f = w_gate.shape[0]
+    _check(lib().staple_ffn_gate_up(n, d, f, _dt(x), _p(x), _p(w_gate), _p(w_up), _p(rows),
+                                    rows.shape[0], _p(row_index), _p(h), _p(save_g), _p(save_u),
+                                    _stream(stream)), "staple_ffn_gate_up")
+    return h
+
+
+def staple_ffn_down(h: torch.Tensor, w_down: torch.Tensor, y: torch.Tensor,
+                    stream=None) -> torch.Tensor:
+    """y = h W_down^T."""
+    _dev(h, w_down, y)
+    n, f = h.shape
+    d = w_down.shape[0]
+    _check(lib().staple_ffn_down(n, d, f, _dt(h), _DT[y.dtype], _p(h), _p(w_down), _p(y),
+                                 _stream(stream)), "staple_ffn_down")
+    return y
+
+
+def staple_ffn_bwd_table_grad(dy: torch.Tensor, x: torch.Tensor, w_gate: torch.Tensor,
+                              w_up: torch.Tensor, w_down: torch.Tensor, saved_g: torch.Tensor,
+                              saved_u: torch.Tensor, saved_h: torch.Tensor,
+                              sorted_pos: torch.Tensor, seg_start: torch.Tensor,
+                              n_unique: torch.Tensor, *, max_unique: Optional[int] = None,
+                              freeze_up: bool = False, out_dtype: Optional[torch.dtype] = None,
+                              out: Optional[dict] = None, workspace: Optional[torch.Tensor] = None,
+                              stream=None) -> dict:
+    """Backward with the table-row gradient: d_rows, dx, dw_gate, dw_up, dw_down."""
+    _dev(dy, x, w_gate, w_up, w_down, saved_g, saved_u, saved_h, sorted_pos, seg_start, n_unique)
+    n, d = x.shape
+    f = w_gate.shape[0]
+    dt = _dt(x)
+    mu = n if max_unique is None else int(max_unique)
+    dev = x.device
+    if out is None:
+        out = {
+            "d_rows": torch.empty(max(mu, 1), f, dtype=torch.float32, device=dev),
+            "dx": torch.empty(n, d, dtype=out_dtype or x.dtype, device=dev),
+            "dw_gate": torch.empty(f, d, dtype=torch.float32, device=dev),
+            "dw_up": None if freeze_up else torch.empty(f, d, dtype=torch.float32, device=dev),
+            "dw_down": torch.empty(d, f, dtype=torch.float32, device=dev),
+        }
+    ws = _ws(lib().staple_ffn_bwd_workspace_bytes(n, d, f, dt), workspace, dev)
+    _check(lib().staple_ffn_bwd_table_grad(
+        n, d, f, dt, _DT[out["dx"].dtype], _p(dy), _p(x), _p(w_gate), _p(w_up), _p(w_down),
+        _p(saved_g), _p(saved_u), _p(saved_h), _p(sorted_pos), _p(seg_start), _p(n_unique), mu,
+        _p(out["d_rows"]), _p(out["dx"]), _p(out["dw_gate"]), _p(out.get("dw_up")),
+        _p(out["dw_down"]), int(bool(freeze_up)), _p(ws), _ws_size(ws), _stream(stream)),
+        "staple_ffn_bwd_table_grad")
+    return out
+
+
+def ffn_workspace_bytes(n: int, d: int, f: int, dtype: torch.dtype) -> dict:
+    return {"fwd": lib().staple_ffn_fwd_workspace_bytes(n, d, f, _DT[dtype]),
+            "bwd": lib().staple_ffn_bwd_workspace_bytes(n, d, f, _DT[dtype]),
+            "dedup": lib().staple_dedup_workspace_bytes(n)}

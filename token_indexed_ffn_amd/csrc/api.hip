@@ -1,0 +1,399 @@
+// C ABI of libstaple: argument validation, workspace sizing and dispatch to
+// the kernels.  Nothing here allocates device memory.
+#include <algorithm>
+#include <atomic>
+#include <cstring>
+#include <mutex>
+#include <thread>
+#include <vector>
+
+#include "common.h"
+
+namespace staple {
+
+// kernels (sort.hip)
+size_t dedup_workspace_bytes(int64_t n);
+hipError_t launch_dedup(const int32_t* ids, int64_t n, int64_t vocab, int32_t* uniq, int32_t* inv,
+                        int32_t* sorted_pos, int32_t* seg_start, int32_t* n_unique, void* ws,
+                        hipStream_t s, int* err);
+size_t cache_build_workspace_bytes(int64_t vocab);
+hipError_t launch_cache_build(const int64_t* counts, int64_t vocab, int64_t capacity,
+                              int32_t* id_to_slot, int32_t* slot_to_id, void* ws, hipStream_t s,
+                              int* err);
+// kernels (rows.hip)
+hipError_t launch_cache_count(const int32_t* ids, int64_t n, int64_t vocab, int64_t* counts,
+                              hipStream_t s, int* err);
+hipError_t launch_cache_lookup(const int32_t* uniq, const int32_t* n_unique, int64_t max_unique,
+                               const int32_t* id_to_slot, int64_t vocab, int32_t* code,
+                               int32_t* miss_uidx, int32_t* miss_ids, int32_t* n_miss,
+                               hipStream_t s, int* err);
+hipError_t launch_gather_rows(const void* src, int64_t src_rows, const int32_t* index,
+                              const int32_t* n_rows, int64_t max_rows, int64_t row_bytes,
+                              void* dst, hipStream_t s, int* err);
+hipError_t launch_assemble_rows(const void* cache_rows, int64_t capacity, const void* miss_rows,
+                                int64_t max_miss, const int32_t* code, const int32_t* n_unique,
+                                int64_t max_unique, int64_t row_bytes, void* rows, hipStream_t s,
+                                int* err);
+hipError_t launch_segment_sum(int dtype, const void* du, int64_t du_ld, int64_t du_col,
+                              int64_t n_tokens, int64_t d_ff, const int32_t* sorted_pos,
+                              const int32_t* seg_start, const int32_t* n_unique,
+                              int64_t max_unique, float* d_rows, hipStream_t s, int* err);
+// kernels (gemm.hip)
+template <typename T>
+hipError_t gateup_fwd(int64_t n, int64_t d, int64_t f, const void* x, const void* wg,
+                      const void* wu, const void* rows, int64_t n_rows, const int32_t* row_index,
+                      void* h, void* g_out, void* u_out, hipStream_t s, int* err);
+template <typename T>
+hipError_t down_fwd(int64_t n, int64_t d, int64_t f, const void* h, const void* wd, void* y,
+                    int out_dtype, hipStream_t s);
+template <typename T>
+hipError_t dh_act(int64_t n, int64_t d, int64_t f, const void* dy, const void* wd, const void* g,
+                  const void* u, void* dgu, hipStream_t s);
+template <typename T>
+hipError_t dx_bwd(int64_t n, int64_t d, int64_t f, const void* dgu, const void* wg,
+                  const void* wu, void* dx, int out_dtype, hipStream_t s);
+template <typename T>
+hipError_t dwdown_bwd(int64_t n, int64_t d, int64_t f, const void* dy, const void* h, float* dwd,
+                      hipStream_t s);
+template <typename T>
+hipError_t dwgu_bwd(int64_t n, int64_t d, int64_t f, const void* dgu, const void* x, float* dwg,
+                    float* dwu, bool freeze_up, hipStream_t s);
+
+// ---------------------------------------------------------------------------
+// Per-device error word
+// ---------------------------------------------------------------------------
+__device__ int g_staple_error = 0;
+
+static std::mutex g_err_mu;
+static std::vector<int*> g_err_ptr;  // indexed by device ordinal
+
+int* device_error_word() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return nullptr;
+  std::lock_guard<std::mutex> lk(g_err_mu);
+  if (static_cast<size_t>(dev) >= g_err_ptr.size()) g_err_ptr.resize(dev + 1, nullptr);
+  if (g_err_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(g_staple_error)) != hipSuccess) return nullptr;
+    g_err_ptr[dev] = static_cast<int*>(p);
+  }
+  return g_err_ptr[dev];
+}
+
+static inline int elem_bytes(int32_t dt) { return dt == STAPLE_BF16 ? 2 : 4; }
+static inline bool valid_dtype(int32_t dt) { return dt == STAPLE_BF16 || dt == STAPLE_F32; }
+static inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+static inline hipStream_t S(void* s) { return static_cast<hipStream_t>(s); }
+
+}  // namespace staple
+
+using namespace staple;
+
+#define REQUIRE(cond)                                   \
+  do {                                                  \
+    if (!(cond)) return STAPLE_ERR_INVALID_ARGUMENT;    \
+  } while (0)
+
+#define HIPCALL(expr)                                   \
+  do {                                                  \
+    if ((expr) != hipSuccess) return STAPLE_ERR_HIP;    \
+  } while (0)
+
+#define GET_ERR(var)                                    \
+  int* var = device_error_word();                       \
+  if (var == nullptr) return STAPLE_ERR_HIP
+
+extern "C" {
+
+const char* staple_status_string(staple_status_t st) {
+  switch (st) {
+    case STAPLE_OK: return "ok";
+    case STAPLE_ERR_INVALID_ARGUMENT: return "invalid argument";
+    case STAPLE_ERR_UNSUPPORTED: return "unsupported dtype or shape";
+    case STAPLE_ERR_WORKSPACE: return "workspace too small";
+    case STAPLE_ERR_HIP: return "HIP runtime error";
+    case STAPLE_ERR_INDEX_RANGE: return "out-of-range token ID or row index met on the device";
+    case STAPLE_ERR_HOST: return "host-side failure";
+    default: return "unknown status";
+  }
+}
+
+const char* staple_version(void) { return "libstaple 0.1 (gfx950)"; }
+
+staple_status_t staple_get_device_error(void* stream) {
+  GET_ERR(err);
+  int v = 0;
+  HIPCALL(hipMemcpyAsync(&v, err, sizeof(int), hipMemcpyDeviceToHost, S(stream)));
+  HIPCALL(hipStreamSynchronize(S(stream)));
+  if (v != 0) {
+    int zero = 0;
+    HIPCALL(hipMemcpyAsync(err, &zero, sizeof(int), hipMemcpyHostToDevice, S(stream)));
+    HIPCALL(hipStreamSynchronize(S(stream)));
+    return STAPLE_ERR_INDEX_RANGE;
+  }
+  return STAPLE_OK;
+}
+
+// ------------------------------------------------------------------ dedup
+size_t staple_dedup_workspace_bytes(int64_t n_tokens) {
+  return n_tokens < 0 ? 0 : dedup_workspace_bytes(n_tokens);
+}
+
+staple_status_t staple_dedup(const int32_t* ids, int64_t n, int64_t vocab, int32_t* uniq,
+                             int32_t* inv, int32_t* sorted_pos, int32_t* seg_start,
+                             int32_t* n_unique, void* ws, size_t ws_bytes, void* stream) {
+  REQUIRE(n >= 0 && n <= 0x7fffffffll && vocab >= 1 && vocab <= 0x7fffffffll);
+  REQUIRE(seg_start && n_unique);
+  REQUIRE(n == 0 || (ids && uniq && inv && sorted_pos));
+  if (ws_bytes < dedup_workspace_bytes(n)) return STAPLE_ERR_WORKSPACE;
+  REQUIRE(dedup_workspace_bytes(n) == 0 || ws != nullptr);
+  GET_ERR(err);
+  HIPCALL(launch_dedup(ids, n, vocab, uniq, inv, sorted_pos, seg_start, n_unique, ws, S(stream), err));
+  return STAPLE_OK;
+}
+
+// ------------------------------------------------------------------ cache
+staple_status_t staple_cache_count(const int32_t* ids, int64_t n, int64_t vocab, int64_t* counts,
+                                   void* stream) {
+  REQUIRE(n >= 0 && vocab >= 1 && vocab <= 0x7fffffffll && counts);
+  REQUIRE(n == 0 || ids);
+  GET_ERR(err);
+  HIPCALL(launch_cache_count(ids, n, vocab, counts, S(stream), err));
+  return STAPLE_OK;
+}
+
+size_t staple_cache_build_workspace_bytes(int64_t vocab) {
+  return vocab < 1 ? 0 : cache_build_workspace_bytes(vocab);
+}
+
+staple_status_t staple_cache_build(const int64_t* counts, int64_t vocab, int64_t capacity,
+                                   int32_t* id_to_slot, int32_t* slot_to_id, void* ws,
+                                   size_t ws_bytes, void* stream) {
+  REQUIRE(vocab >= 1 && vocab <= 0x7fffffffll && capacity >= 0 && capacity <= vocab);
+  REQUIRE(counts && id_to_slot && ws && (capacity == 0 || slot_to_id));
+  if (ws_bytes < cache_build_workspace_bytes(vocab)) return STAPLE_ERR_WORKSPACE;
+  GET_ERR(err);
+  HIPCALL(launch_cache_build(counts, vocab, capacity, id_to_slot, slot_to_id, ws, S(stream), err));
+  return STAPLE_OK;
+}
+
+staple_status_t staple_cache_fill(const void* table, int64_t vocab, int64_t d_ff, int32_t dtype,
+                                  const int32_t* slot_to_id, int64_t capacity, void* slot_rows,
+                                  void* stream) {
+  REQUIRE(valid_dtype(dtype) && vocab >= 1 && d_ff > 0 && capacity >= 0 && capacity <= vocab);
+  REQUIRE((d_ff * elem_bytes(dtype)) % 16 == 0);
+  REQUIRE(capacity == 0 || (table && slot_to_id && slot_rows));
+  REQUIRE(capacity == 0 || (aligned16(table) && aligned16(slot_rows)));
+  GET_ERR(err);
+  HIPCALL(launch_gather_rows(table, vocab, slot_to_id, nullptr, capacity, d_ff * elem_bytes(dtype),
+                             slot_rows, S(stream), err));
+  return STAPLE_OK;
+}
+
+staple_status_t staple_cache_lookup(const int32_t* uniq, const int32_t* n_unique,
+                                    int64_t max_unique, const int32_t* id_to_slot, int64_t vocab,
+                                    int32_t* code, int32_t* miss_uidx, int32_t* miss_ids,
+                                    int32_t* n_miss, void* stream) {
+  REQUIRE(max_unique >= 0 && max_unique <= 0x7fffffffll && vocab >= 1);
+  REQUIRE(n_unique && id_to_slot && n_miss);
+  REQUIRE(max_unique == 0 || (uniq && code && miss_uidx));
+  GET_ERR(err);
+  HIPCALL(launch_cache_lookup(uniq, n_unique, max_unique, id_to_slot, vocab, code, miss_uidx,
+                              miss_ids, n_miss, S(stream), err));
+  return STAPLE_OK;
+}
+
+staple_status_t staple_stage_misses(const void* host_table, int64_t vocab, int64_t d_ff,
+                                    int32_t dtype, const int32_t* host_miss_ids, int32_t n_miss,
+                                    void* host_staging, void* dev_miss_rows, void* stream) {
+  REQUIRE(valid_dtype(dtype) && vocab >= 1 && d_ff > 0 && n_miss >= 0);
+  if (n_miss == 0) return STAPLE_OK;
+  REQUIRE(host_table && host_miss_ids && host_staging && dev_miss_rows);
+  const size_t row_bytes = static_cast<size_t>(d_ff) * elem_bytes(dtype);
+  for (int32_t m = 0; m < n_miss; ++m)
+    if (host_miss_ids[m] < 0 || host_miss_ids[m] >= vocab) return STAPLE_ERR_HOST;
+  const char* src = static_cast<const char*>(host_table);
+  char* dst = static_cast<char*>(host_staging);
+  const size_t total = row_bytes * static_cast<size_t>(n_miss);
+  unsigned hw = std::max(1u, std::thread::hardware_concurrency());
+  unsigned nthreads = static_cast<unsigned>(std::min<size_t>(std::min(hw, 16u), total >> 21));
+  if (nthreads <= 1) {
+    for (int32_t m = 0; m < n_miss; ++m)
+      std::memcpy(dst + m * row_bytes, src + static_cast<size_t>(host_miss_ids[m]) * row_bytes,
+                  row_bytes);
+  } else {
+    std::vector<std::thread> pool;
+    pool.reserve(nthreads);
+    for (unsigned t = 0; t < nthreads; ++t) {
+      pool.emplace_back([=]() {
+        const int64_t lo = static_cast<int64_t>(n_miss) * t / nthreads;
+        const int64_t hi = static_cast<int64_t>(n_miss) * (t + 1) / nthreads;
+        for (int64_t m = lo; m < hi; ++m)
+          std::memcpy(dst + m * row_bytes,
+                      src + static_cast<size_t>(host_miss_ids[m]) * row_bytes, row_bytes);
+      });
+    }
+    for (auto& th : pool) th.join();
+  }
+  HIPCALL(hipMemcpyAsync(dev_miss_rows, host_staging, total, hipMemcpyHostToDevice, S(stream)));
+  return STAPLE_OK;
+}
+
+staple_status_t staple_assemble_rows(const void* cache_rows, int64_t capacity,
+                                     const void* miss_rows, int64_t max_miss, const int32_t* code,
+                                     const int32_t* n_unique, int64_t max_unique, int64_t d_ff,
+                                     int32_t dtype, void* rows, void* stream) {
+  REQUIRE(valid_dtype(dtype) && d_ff > 0 && capacity >= 0 && max_miss >= 0 && max_unique >= 0);
+  REQUIRE((d_ff * elem_bytes(dtype)) % 16 == 0);
+  REQUIRE(n_unique && (max_unique == 0 || (code && rows)));
+  REQUIRE(capacity == 0 || cache_rows);
+  REQUIRE(max_miss == 0 || miss_rows);
+  GET_ERR(err);
+  HIPCALL(launch_assemble_rows(cache_rows, capacity, miss_rows, max_miss, code, n_unique,
+                               max_unique, d_ff * elem_bytes(dtype), rows, S(stream), err));
+  return STAPLE_OK;
+}
+
+staple_status_t staple_gather_rows(const void* src, int64_t src_rows, const int32_t* index,
+                                   const int32_t* n_rows, int64_t max_rows, int64_t d_ff,
+                                   int32_t dtype, void* dst, void* stream) {
+  REQUIRE(valid_dtype(dtype) && d_ff > 0 && src_rows >= 1 && max_rows >= 0);
+  REQUIRE((d_ff * elem_bytes(dtype)) % 16 == 0);
+  REQUIRE(max_rows == 0 || (src && index && dst));
+  REQUIRE(max_rows == 0 || (aligned16(src) && aligned16(dst)));
+  GET_ERR(err);
+  HIPCALL(launch_gather_rows(src, src_rows, index, n_rows, max_rows, d_ff * elem_bytes(dtype), dst,
+                             S(stream), err));
+  return STAPLE_OK;
+}
+
+// ------------------------------------------------------------------ FFN
+static bool ffn_shape_ok(int64_t n, int64_t d, int64_t f, int32_t dtype) {
+  return n >= 0 && n <= 0x7fffffffll && d > 0 && f > 0 && d % 64 == 0 && f % 64 == 0 &&
+         d <= (1ll << 20) && f <= (1ll << 20) && valid_dtype(dtype);
+}
+
+size_t staple_ffn_fwd_workspace_bytes(int64_t n, int64_t d, int64_t f, int32_t dtype) {
+  if (!ffn_shape_ok(n, d, f, dtype)) return 0;
+  return align_up(static_cast<size_t>(n) * f * elem_bytes(dtype), 256);
+}
+
+static staple_status_t gate_up_impl(int64_t n, int64_t d, int64_t f, int32_t dtype,
+                                    const void* x, const void* w_gate, const void* w_up,
+                                    const void* rows, int64_t n_rows, const int32_t* row_index,
+                                    void* h, void* save_g, void* save_u, hipStream_t s) {
+  GET_ERR(err);
+  if (dtype == STAPLE_BF16)
+    HIPCALL(gateup_fwd<bf16_t>(n, d, f, x, w_gate, w_up, rows, n_rows, row_index, h, save_g,
+                               save_u, s, err));
+  else
+    HIPCALL(gateup_fwd<float>(n, d, f, x, w_gate, w_up, rows, n_rows, row_index, h, save_g,
+                              save_u, s, err));
+  return STAPLE_OK;
+}
+
+static staple_status_t down_impl(int64_t n, int64_t d, int64_t f, int32_t dtype, int32_t out_dtype,
+                                 const void* h, const void* w_down, void* y, hipStream_t s) {
+  if (dtype == STAPLE_BF16) HIPCALL(down_fwd<bf16_t>(n, d, f, h, w_down, y, out_dtype, s));
+  else HIPCALL(down_fwd<float>(n, d, f, h, w_down, y, out_dtype, s));
+  return STAPLE_OK;
+}
+
+staple_status_t staple_ffn_gate_up(int64_t n, int64_t d, int64_t f, int32_t dtype, const void* x,
+                                   const void* w_gate, const void* w_up, const void* rows,
+                                   int64_t n_rows, const int32_t* row_index, void* h,
+                                   void* save_g, void* save_u, void* stream) {
+  if (!ffn_shape_ok(n, d, f, dtype)) return STAPLE_ERR_UNSUPPORTED;
+  REQUIRE(w_gate && w_up && rows && n_rows >= 1);
+  REQUIRE(aligned16(w_gate) && aligned16(w_up) && aligned16(rows));
+  if (n == 0) return STAPLE_OK;
+  REQUIRE(x && row_index && h && aligned16(x) && aligned16(h));
+  REQUIRE((!save_g || aligned16(save_g)) && (!save_u || aligned16(save_u)));
+  return gate_up_impl(n, d, f, dtype, x, w_gate, w_up, rows, n_rows, row_index, h, save_g, save_u,
+                      S(stream));
+}
+
+staple_status_t staple_ffn_down(int64_t n, int64_t d, int64_t f, int32_t dtype, int32_t out_dtype,
+                                const void* h, const void* w_down, void* y, void* stream) {
+  if (!valid_dtype(out_dtype) || !ffn_shape_ok(n, d, f, dtype)) return STAPLE_ERR_UNSUPPORTED;
+  REQUIRE(w_down && aligned16(w_down));
+  if (n == 0) return STAPLE_OK;
+  REQUIRE(h && y && aligned16(h) && aligned16(y));
+  return down_impl(n, d, f, dtype, out_dtype, h, w_down, y, S(stream));
+}
+
+staple_status_t staple_ffn_fwd(int64_t n, int64_t d, int64_t f, int32_t dtype, int32_t out_dtype,
+                               const void* x, const void* w_gate, const void* w_up,
+                               const void* w_down, const void* rows, int64_t n_rows,
+                               const int32_t* row_index, void* y, void* save_g, void* save_u,
+                               void* save_h, void* ws, size_t ws_bytes, void* stream) {
+  if (!valid_dtype(dtype) || !valid_dtype(out_dtype)) return STAPLE_ERR_UNSUPPORTED;
+  if (!ffn_shape_ok(n, d, f, dtype)) return STAPLE_ERR_UNSUPPORTED;
+  REQUIRE(w_gate && w_up && w_down && rows && n_rows >= 1);
+  REQUIRE(aligned16(w_gate) && aligned16(w_up) && aligned16(w_down) && aligned16(rows));
+  if (n == 0) return STAPLE_OK;
+  REQUIRE(x && row_index && y && aligned16(x) && aligned16(y));
+  REQUIRE((!save_g || aligned16(save_g)) && (!save_u || aligned16(save_u)) &&
+          (!save_h || aligned16(save_h)));
+  void* h = save_h;
+  if (h == nullptr) {
+    if (ws_bytes < staple_ffn_fwd_workspace_bytes(n, d, f, dtype)) return STAPLE_ERR_WORKSPACE;
+    REQUIRE(ws && aligned16(ws));
+    h = ws;
+  }
+  hipStream_t s = S(stream);
+  staple_status_t st = gate_up_impl(n, d, f, dtype, x, w_gate, w_up, rows, n_rows, row_index, h,
+                                    save_g, save_u, s);
+  if (st != STAPLE_OK) return st;
+  return down_impl(n, d, f, dtype, out_dtype, h, w_down, y, s);
+}
+
+size_t staple_ffn_bwd_workspace_bytes(int64_t n, int64_t d, int64_t f, int32_t dtype) {
+  if (!ffn_shape_ok(n, d, f, dtype)) return 0;
+  return align_up(static_cast<size_t>(n) * 2 * f * elem_bytes(dtype), 256);
+}
+
+staple_status_t staple_ffn_bwd_table_grad(
+    int64_t n, int64_t d, int64_t f, int32_t dtype, int32_t out_dtype, const void* dy,
+    const void* x, const void* w_gate, const void* w_up, const void* w_down, const void* saved_g,
+    const void* saved_u, const void* saved_h, const int32_t* sorted_pos, const int32_t* seg_start,
+    const int32_t* n_unique, int64_t max_unique, float* d_rows, void* dx, float* dw_gate,
+    float* dw_up, float* dw_down, int32_t freeze_up, void* ws, size_t ws_bytes, void* stream) {
+  if (!valid_dtype(dtype) || !valid_dtype(out_dtype)) return STAPLE_ERR_UNSUPPORTED;
+  if (!ffn_shape_ok(n, d, f, dtype)) return STAPLE_ERR_UNSUPPORTED;
+  REQUIRE(w_gate && w_up && w_down && dw_gate && dw_down && (freeze_up || dw_up));
+  REQUIRE(seg_start && n_unique && max_unique >= 0 && max_unique <= n);
+  REQUIRE(aligned16(w_gate) && aligned16(w_up) && aligned16(w_down) && aligned16(dw_gate) &&
+          aligned16(dw_down) && (freeze_up || aligned16(dw_up)));
+  if (n > 0) {
+    REQUIRE(dy && x && saved_g && saved_u && saved_h && sorted_pos && d_rows && dx);
+    REQUIRE(aligned16(dy) && aligned16(x) && aligned16(saved_g) && aligned16(saved_u) &&
+            aligned16(saved_h) && aligned16(dx) && aligned16(d_rows));
+    if (ws_bytes < staple_ffn_bwd_workspace_bytes(n, d, f, dtype)) return STAPLE_ERR_WORKSPACE;
+    REQUIRE(ws && aligned16(ws));
+  }
+  GET_ERR(err);
+  hipStream_t s = S(stream);
+  void* dgu = ws;
+  const bool fz = freeze_up != 0;
+  if (dtype == STAPLE_BF16) {
+    HIPCALL(dh_act<bf16_t>(n, d, f, dy, w_down, saved_g, saved_u, dgu, s));
+    if (n > 0)
+      HIPCALL(launch_segment_sum(dtype, dgu, 2 * f, f, n, f, sorted_pos, seg_start, n_unique,
+                                 max_unique, d_rows, s, err));
+    HIPCALL(dwdown_bwd<bf16_t>(n, d, f, dy, saved_h, dw_down, s));
+    HIPCALL(dwgu_bwd<bf16_t>(n, d, f, dgu, x, dw_gate, dw_up, fz, s));
+    HIPCALL(dx_bwd<bf16_t>(n, d, f, dgu, w_gate, w_up, dx, out_dtype, s));
+  } else {
+    HIPCALL(dh_act<float>(n, d, f, dy, w_down, saved_g, saved_u, dgu, s));
+    if (n > 0)
+      HIPCALL(launch_segment_sum(dtype, dgu, 2 * f, f, n, f, sorted_pos, seg_start, n_unique,
+                                 max_unique, d_rows, s, err));
+    HIPCALL(dwdown_bwd<float>(n, d, f, dy, saved_h, dw_down, s));
+    HIPCALL(dwgu_bwd<float>(n, d, f, dgu, x, dw_gate, dw_up, fz, s));
+    HIPCALL(dx_bwd<float>(n, d, f, dgu, w_gate, w_up, dx, out_dtype, s));
+  }
+  return STAPLE_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,97 @@
+// Shared device/host helpers of libstaple (gfx950 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <stddef.h>
+
+#include "../../include/staple.h"
+
+namespace staple {
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
+typedef __attribute__((ext_vector_type(16))) float f32x16_t;
+typedef __attribute__((ext_vector_type(4))) float f32x4_t;
+typedef __attribute__((ext_vector_type(4))) uint32_t u32x4_t;
+typedef __attribute__((ext_vector_type(2))) uint32_t u32x2_t;
+
+// bfloat16 storage type (raw bits).
+struct bf16_t {
+  uint16_t bits;
+};
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) {
+  return __uint_as_float(static_cast<uint32_t>(b) << 16);
+}
+
+// float -> bfloat16, round to nearest, ties to even (finite inputs; NaN stays NaN).
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<uint16_t>((u >> 16) | 0x40u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return static_cast<uint16_t>(u >> 16);
+}
+
+// Element access for the two storage types.
+template <typename T> struct Elem;
+template <> struct Elem<float> {
+  static constexpr int kBytes = 4;
+  __device__ __forceinline__ static float load(const void* p, int64_t i) {
+    return static_cast<const float*>(p)[i];
+  }
+  __device__ __forceinline__ static void store(void* p, int64_t i, float v) {
+    static_cast<float*>(p)[i] = v;
+  }
+  // value as it would be stored (identity for fp32)
+  __device__ __forceinline__ static float quantize(float v) { return v; }
+};
+template <> struct Elem<bf16_t> {
+  static constexpr int kBytes = 2;
+  __device__ __forceinline__ static float load(const void* p, int64_t i) {
+    return bf16_to_f32(static_cast<const uint16_t*>(p)[i]);
+  }
+  __device__ __forceinline__ static void store(void* p, int64_t i, float v) {
+    static_cast<uint16_t*>(p)[i] = f32_to_bf16(v);
+  }
+  __device__ __forceinline__ static float quantize(float v) { return bf16_to_f32(f32_to_bf16(v)); }
+};
+
+__device__ __forceinline__ float sigmoidf_(float z) { return 1.0f / (1.0f + __expf(-z)); }
+
+// Kernels that meet an out-of-range ID or index OR this bit into the
+// per-device error word whose address they receive as `err`.
+constexpr int kErrIndexRange = 1;
+
+__device__ __forceinline__ void flag_index_error(int* err) { atomicOr(err, kErrIndexRange); }
+
+// Address of the calling device's error word (defined in api.hip).
+int* device_error_word();
+
+inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+// Bump allocator over a caller-provided workspace.
+struct Workspace {
+  char* base;
+  size_t size;
+  size_t used;
+  Workspace(void* b, size_t s) : base(static_cast<char*>(b)), size(s), used(0) {}
+  template <typename P> P* take(size_t bytes) {
+    size_t off = align_up(used, 256);
+    used = off + bytes;
+    return used <= size ? reinterpret_cast<P*>(base + off) : nullptr;
+  }
+};
+
+}  // namespace staple
+
+#define STAPLE_HIP_CHECK(expr)                          \
+  do {                                                  \
+    hipError_t _e = (expr);                             \
+    if (_e != hipSuccess) return STAPLE_ERR_HIP;        \
+  } while (0)
+
+#define STAPLE_LAUNCH_CHECK()                           \
+  do {                                                  \
+    hipError_t _e = hipGetLastError();                  \
+    if (_e != hipSuccess) return STAPLE_ERR_HIP;        \
+  } while (0)

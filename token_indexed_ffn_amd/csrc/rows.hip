@@ -1,0 +1,307 @@
+// Row movement kernels: cache count pass, cache probe with miss compaction,
+// row gather / compact-block assembly, and the table-row gradient
+// segment-sum.
+#include "common.h"
+
+namespace staple {
+
+// Block-wide exclusive scan (same contract as the one in sort.hip; kept local
+// to this translation unit).
+__device__ static int scan_block(int v, int* wave_tmp, int& total) {
+  const int lane = threadIdx.x & 63;
+  const int wid = threadIdx.x >> 6;
+  const int nw = blockDim.x >> 6;
+  int x = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(x, o, 64);
+    if (lane >= o) x += y;
+  }
+  if (lane == 63) wave_tmp[wid] = x;
+  __syncthreads();
+  if (wid == 0) {
+    int w = lane < nw ? wave_tmp[lane] : 0;
+#pragma unroll
+    for (int o = 1; o < 16; o <<= 1) {
+      const int y = __shfl_up(w, o, 64);
+      if (lane >= o) w += y;
+    }
+    if (lane < nw) wave_tmp[lane] = w;
+  }
+  __syncthreads();
+  const int before = wid > 0 ? wave_tmp[wid - 1] : 0;
+  total = wave_tmp[nw - 1];
+  __syncthreads();
+  return before + x - v;
+}
+
+// ---------------------------------------------------------------------------
+// Count pass over a calibration stream.
+// ---------------------------------------------------------------------------
+__global__ void count_kernel(const int32_t* ids, int64_t n, int64_t vocab,
+                             unsigned long long* counts, int* err) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (i >= n) return;
+  const int32_t t = ids[i];
+  if (t < 0 || t >= vocab) {
+    flag_index_error(err);
+    return;
+  }
+  atomicAdd(&counts[t], 1ull);
+}
+
+hipError_t launch_cache_count(const int32_t* ids, int64_t n, int64_t vocab, int64_t* counts,
+                              hipStream_t s, int* err) {
+  if (n == 0) return hipSuccess;
+  count_kernel<<<dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0, s>>>(
+      ids, n, vocab, reinterpret_cast<unsigned long long*>(counts), err);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Cache probe + stable miss compaction (one workgroup; U is at most a batch).
+// ---------------------------------------------------------------------------
+constexpr int kLookupThreads = 1024;
+
+__global__ __launch_bounds__(kLookupThreads) void lookup_kernel(
+    const int32_t* uniq, const int32_t* n_unique_p, int64_t max_unique, const int32_t* id_to_slot,
+    int64_t vocab, int32_t* code, int32_t* miss_uidx, int32_t* miss_ids, int32_t* n_miss,
+    int* err) {
+  __shared__ int wave_tmp[16];
+  int64_t nu = *n_unique_p;
+  if (nu < 0 || nu > max_unique) {
+    if (threadIdx.x == 0) flag_index_error(err);
+    nu = nu < 0 ? 0 : max_unique;
+  }
+  int carry = 0;
+  for (int64_t base = 0; base < nu; base += blockDim.x) {
+    const int64_t u = base + threadIdx.x;
+    int32_t slot = 0;
+    int32_t id = 0;
+    int miss = 0;
+    if (u < nu) {
+      id = uniq[u];
+      if (id < 0 || id >= vocab) {
+        flag_index_error(err);
+        slot = -1;
+      } else {
+        slot = id_to_slot[id];
+      }
+      miss = slot < 0;
+    }
+    int total;
+    const int before = scan_block(miss, wave_tmp, total);
+    if (u < nu) {
+      if (miss) {
+        const int m = carry + before;
+        code[u] = -1 - m;
+        miss_uidx[m] = static_cast<int32_t>(u);
+        if (miss_ids) miss_ids[m] = id;
+      } else {
+        code[u] = slot;
+      }
+    }
+    carry += total;
+  }
+  if (threadIdx.x == 0) *n_miss = carry;
+}
+
+hipError_t launch_cache_lookup(const int32_t* uniq, const int32_t* n_unique, int64_t max_unique,
+                               const int32_t* id_to_slot, int64_t vocab, int32_t* code,
+                               int32_t* miss_uidx, int32_t* miss_ids, int32_t* n_miss,
+                               hipStream_t s, int* err) {
+  lookup_kernel<<<dim3(1), dim3(kLookupThreads), 0, s>>>(uniq, n_unique, max_unique, id_to_slot,
+                                                         vocab, code, miss_uidx, miss_ids, n_miss,
+                                                         err);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Row copies.  One workgroup per destination row; 16-byte vectors.
+// ---------------------------------------------------------------------------
+constexpr int kRowThreads = 256;
+
+__device__ __forceinline__ void copy_row16(const uint4* __restrict__ src, uint4* __restrict__ dst,
+                                           int64_t vecs) {
+  for (int64_t v = threadIdx.x; v < vecs; v += kRowThreads) dst[v] = src[v];
+}
+
+// dst[r] = src[index[r]]  (r < n, n from the device scalar when given)
+__global__ __launch_bounds__(kRowThreads) void gather_rows_kernel(
+    const void* src, int64_t src_rows, const int32_t* index, const int32_t* n_rows_p,
+    int64_t row_bytes, void* dst, int* err) {
+  const int64_t r = blockIdx.x;
+  if (n_rows_p && r >= *n_rows_p) return;
+  const int32_t i = index[r];
+  if (i < 0 || i >= src_rows) {
+    if (threadIdx.x == 0) flag_index_error(err);
+    return;
+  }
+  copy_row16(reinterpret_cast<const uint4*>(static_cast<const char*>(src) + i * row_bytes),
+             reinterpret_cast<uint4*>(static_cast<char*>(dst) + r * row_bytes), row_bytes / 16);
+}
+
+hipError_t launch_gather_rows(const void* src, int64_t src_rows, const int32_t* index,
+                              const int32_t* n_rows, int64_t max_rows, int64_t row_bytes,
+                              void* dst, hipStream_t s, int* err) {
+  if (max_rows == 0) return hipSuccess;
+  gather_rows_kernel<<<dim3(static_cast<unsigned>(max_rows)), dim3(kRowThreads), 0, s>>>(
+      src, src_rows, index, n_rows, row_bytes, dst, err);
+  return hipGetLastError();
+}
+
+// rows[u] = code[u] >= 0 ? cache_rows[code[u]] : miss_rows[-1 - code[u]]
+__global__ __launch_bounds__(kRowThreads) void assemble_rows_kernel(
+    const void* cache_rows, int64_t capacity, const void* miss_rows, int64_t max_miss,
+    const int32_t* code, const int32_t* n_unique_p, int64_t row_bytes, void* rows, int* err) {
+  const int64_t u = blockIdx.x;
+  if (u >= *n_unique_p) return;
+  const int32_t c = code[u];
+  const char* src;
+  if (c >= 0) {
+    if (c >= capacity) {
+      if (threadIdx.x == 0) flag_index_error(err);
+      return;
+    }
+    src = static_cast<const char*>(cache_rows) + c * row_bytes;
+  } else {
+    const int64_t m = -1 - static_cast<int64_t>(c);
+    if (m >= max_miss) {
+      if (threadIdx.x == 0) flag_index_error(err);
+      return;
+    }
+    src = static_cast<const char*>(miss_rows) + m * row_bytes;
+  }
+  copy_row16(reinterpret_cast<const uint4*>(src),
+             reinterpret_cast<uint4*>(static_cast<char*>(rows) + u * row_bytes), row_bytes / 16);
+}
+
+hipError_t launch_assemble_rows(const void* cache_rows, int64_t capacity, const void* miss_rows,
+                                int64_t max_miss, const int32_t* code, const int32_t* n_unique,
+                                int64_t max_unique, int64_t row_bytes, void* rows, hipStream_t s,
+                                int* err) {
+  if (max_unique == 0) return hipSuccess;
+  assemble_rows_kernel<<<dim3(static_cast<unsigned>(max_unique)), dim3(kRowThreads), 0, s>>>(
+      cache_rows, capacity, miss_rows, max_miss, code, n_unique, row_bytes, rows, err);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Table-row gradient: d_rows[u, c] = sum over p in segment u of
+// du[sorted_pos[p], c], accumulated in fp32 in ascending p order per wave and
+// then over the four waves in a fixed order (deterministic).
+// du lives at column offset `du_col` of rows with stride `du_ld` (elements).
+// Each workgroup covers one segment and kSegCols columns; each lane owns 8
+// consecutive columns (one 16-byte bf16 load, or two for fp32).
+// ---------------------------------------------------------------------------
+constexpr int kSegThreads = 256;
+constexpr int kSegCols = 512;   // 64 lanes x 8 columns
+
+template <typename T>
+__device__ __forceinline__ void load8(const T* p, float (&v)[8]);
+
+template <>
+__device__ __forceinline__ void load8<bf16_t>(const bf16_t* p, float (&v)[8]) {
+  const uint4 q = *reinterpret_cast<const uint4*>(p);
+  const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    v[2 * i] = __uint_as_float(w[i] << 16);
+    v[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+  }
+}
+
+template <>
+__device__ __forceinline__ void load8<float>(const float* p, float (&v)[8]) {
+  const float4 a = *reinterpret_cast<const float4*>(p);
+  const float4 b = *reinterpret_cast<const float4*>(p + 4);
+  v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+  v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+}
+
+template <typename T>
+__global__ __launch_bounds__(kSegThreads) void segment_sum_kernel(
+    const T* __restrict__ du, int64_t du_ld, int64_t du_col, int64_t n_tokens, int64_t d_ff,
+    const int32_t* __restrict__ sorted_pos, const int32_t* __restrict__ seg_start,
+    const int32_t* __restrict__ n_unique_p, float* __restrict__ d_rows, int* err) {
+  __shared__ float part[kSegThreads / 64][kSegCols];
+  const int64_t u = blockIdx.x;
+  if (u >= *n_unique_p) return;
+  const int lane = threadIdx.x & 63;
+  const int wid = threadIdx.x >> 6;
+  const int64_t c0 = static_cast<int64_t>(blockIdx.y) * kSegCols + lane * 8;
+  const bool active = c0 < d_ff;
+  int64_t p0 = seg_start[u];
+  int64_t p1 = seg_start[u + 1];
+  if (p0 < 0 || p1 > n_tokens || p0 > p1) {
+    if (threadIdx.x == 0) flag_index_error(err);
+    p0 = p1 = 0;
+  }
+  float acc[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) acc[i] = 0.0f;
+  if (active) {
+    constexpr int kUnroll = 4;
+    int64_t p = p0 + wid;
+    for (; p + 4 * (kUnroll - 1) < p1; p += 4 * kUnroll) {
+      float v[kUnroll][8];
+#pragma unroll
+      for (int k = 0; k < kUnroll; ++k) {
+        int64_t row = sorted_pos[p + 4 * k];
+        if (row < 0 || row >= n_tokens) {
+          flag_index_error(err);
+          row = 0;
+        }
+        load8<T>(du + row * du_ld + du_col + c0, v[k]);
+      }
+#pragma unroll
+      for (int k = 0; k < kUnroll; ++k)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc[i] += v[k][i];
+    }
+    for (; p < p1; p += 4) {
+      float v[8];
+      int64_t row = sorted_pos[p];
+      if (row < 0 || row >= n_tokens) {
+        flag_index_error(err);
+        row = 0;
+      }
+      load8<T>(du + row * du_ld + du_col + c0, v);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc[i] += v[i];
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < 8; ++i) part[wid][lane * 8 + i] = acc[i];
+  __syncthreads();
+  // each thread finalises 2 of the 512 columns
+  for (int c = threadIdx.x; c < kSegCols; c += kSegThreads) {
+    const int64_t col = static_cast<int64_t>(blockIdx.y) * kSegCols + c;
+    if (col < d_ff) {
+      float s = part[0][c];
+#pragma unroll
+      for (int w = 1; w < kSegThreads / 64; ++w) s += part[w][c];
+      d_rows[u * d_ff + col] = s;
+    }
+  }
+}
+
+hipError_t launch_segment_sum(int dtype, const void* du, int64_t du_ld, int64_t du_col,
+                              int64_t n_tokens, int64_t d_ff, const int32_t* sorted_pos,
+                              const int32_t* seg_start, const int32_t* n_unique,
+                              int64_t max_unique, float* d_rows, hipStream_t s, int* err) {
+  if (max_unique == 0) return hipSuccess;
+  dim3 grid(static_cast<unsigned>(max_unique), static_cast<unsigned>((d_ff + kSegCols - 1) / kSegCols));
+  if (dtype == STAPLE_BF16) {
+    segment_sum_kernel<bf16_t><<<grid, dim3(kSegThreads), 0, s>>>(
+        static_cast<const bf16_t*>(du), du_ld, du_col, n_tokens, d_ff, sorted_pos, seg_start,
+        n_unique, d_rows, err);
+  } else {
+    segment_sum_kernel<float><<<grid, dim3(kSegThreads), 0, s>>>(
+        static_cast<const float*>(du), du_ld, du_col, n_tokens, d_ff, sorted_pos, seg_start,
+        n_unique, d_rows, err);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace staple
