@@ -107,14 +107,16 @@ def setup_decode(torch, st, w):
         torch.cuda.synchronize()
     ids = torch.from_numpy(ids_np).to(dev)
     h = torch.empty(n, f, dtype=torch.bfloat16, device=dev)
-    return {"layers": layers, "ids": ids, "ids_np": ids_np, "h": h}
+    ws = torch.empty(max(st.lib().staple_ffn_down_workspace_bytes(n, d, f, 1), 256),
+                     dtype=torch.uint8, device=dev)
+    return {"layers": layers, "ids": ids, "ids_np": ids_np, "h": h, "down_ws": ws}
 
 
 def decode_step(st, D):
     ids, h = D["ids"], D["h"]
     for lay in D["layers"]:
         st.staple_ffn_gate_up(lay["x"], lay["w_gate"], lay["w_up"], lay["table"], ids, h)
-        st.staple_ffn_down(h, lay["w_down"], lay["y"])
+        st.staple_ffn_down(h, lay["w_down"], lay["y"], workspace=D["down_ws"])
 
 
 def run_decode(torch, st, w, steps, warmup):
@@ -182,7 +184,7 @@ def run_decode(torch, st, w, steps, warmup):
     gu_bytes = (2 * d * f + n * d + n_unique * f + n * f) * 2      # W_gate, W_up, x, rows, h
     down_bytes = (d * f + n * f + n * d) * 2                        # W_down, h, y
     step_bytes = w.n_layers * (gu_bytes + down_bytes)
-    sha = source_sha("gemm.hip")
+    sha = source_sha("decode.hip")
     achieved = gu_bytes / (gu_us * 1e-6) / 1e9
     res = {
         "ms_per_step": ms,
@@ -192,7 +194,7 @@ def run_decode(torch, st, w, steps, warmup):
         "step_bytes": step_bytes,
         "n_unique": n_unique,
         "roofline": {
-            "kernel": "gemm_kernel<bf16,GateUp> (staple_ffn_gate_up, decode)",
+            "kernel": "decode_gateup_kernel (staple_ffn_gate_up, 64 tokens)",
             "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": achieved / HBM_PEAK_GBS,
             "traffic": traffic_from_profile("decode_gate_up", sha),

@@ -192,6 +192,8 @@ staple_status_t staple_gather_rows(const void* src, int64_t src_rows, const int3
  * In bf16, g, u and y accumulate in fp32; h is rounded to bf16 once (the
  * operand of the down-projection); saved g and u are rounded to bf16.
  * ------------------------------------------------------------------------ */
+/* Workspace of staple_ffn_fwd: room for h (used when save_h is NULL) plus
+ * staple_ffn_down's workspace. */
 size_t staple_ffn_fwd_workspace_bytes(int64_t n_tokens, int64_t d_model, int64_t d_ff,
                                       int32_t dtype);
 staple_status_t staple_ffn_fwd(int64_t n_tokens, int64_t d_model, int64_t d_ff,
@@ -207,15 +209,21 @@ staple_status_t staple_ffn_fwd(int64_t n_tokens, int64_t d_model, int64_t d_ff,
  *   h [n_tokens x d_ff] (dtype), with optional saves of g and u; the table
  *   rows are gathered inside the GEMM's epilogue (STAPLE retrieval-path table:
  *   compact-row reconstruction fused with the FFN).
- * staple_ffn_down: y = W_down h, y of out_dtype.
- * Same layout rules and error behaviour as staple_ffn_fwd. */
+ * staple_ffn_down: y = W_down h, y of out_dtype; its workspace holds the
+ *   fp32 partial sums of the split-K decode kernel (zero bytes when the
+ *   batch does not take that path).
+ * Same layout rules and error behaviour as staple_ffn_fwd.  Batches of at
+ * most 64 tokens in bf16 take the decode kernels (weights streamed once,
+ * split-K down-projection); larger batches and fp32 take the tiled GEMMs. */
 staple_status_t staple_ffn_gate_up(int64_t n_tokens, int64_t d_model, int64_t d_ff, int32_t dtype,
                                    const void* x, const void* w_gate, const void* w_up,
                                    const void* rows, int64_t n_rows, const int32_t* row_index,
                                    void* h, void* save_g, void* save_u, void* stream);
+size_t staple_ffn_down_workspace_bytes(int64_t n_tokens, int64_t d_model, int64_t d_ff,
+                                       int32_t dtype);
 staple_status_t staple_ffn_down(int64_t n_tokens, int64_t d_model, int64_t d_ff, int32_t dtype,
                                 int32_t out_dtype, const void* h, const void* w_down, void* y,
-                                void* stream);
+                                void* ws, size_t ws_bytes, void* stream);
 
 /* ------------------------------------------------------------------------
  * Backward of one augmented layer with the table-row gradient.

@@ -247,6 +247,36 @@ def test_bf16_layer_matches_oracle(st, dev, n, d, f, v, seed):
     _compare_layer(res, of, ob, u, f"bf16 n={n}")
 
 
+@pytest.mark.parametrize("n", [1, 17, 33, 63, 64, 65])
+def test_decode_path_boundary(st, dev, n):
+    """Batches of at most 64 bf16 tokens take the decode kernels, 65 the tiled
+    GEMMs; both give the oracle's y, h and the saved g, u."""
+    import torch
+    _log(f"decode boundary n={n}")
+    d, f, v = 256, 512, 300
+    inp = S.host_layer_inputs(n, d, f, v, dtype="bf16", seed=20 + n)
+    x, wg, wu, wd, tab = (to_dev(getattr(inp, k), "bf16", dev)
+                          for k in ("x", "w_gate", "w_up", "w_down", "table"))
+    ids = torch.from_numpy(inp.ids).to(dev)
+    fwd = st.staple_ffn_fwd(x, wg, wu, wd, tab, ids, out_dtype=torch.float32, save=True)
+    torch.cuda.synchronize()
+    _no_device_error(st)
+    g = {k: inp.as_f64(k) for k in ("x", "w_gate", "w_up", "w_down", "table")}
+    of = O.ffn_forward(g["x"], g["w_gate"], g["w_up"], g["w_down"], g["table"], inp.ids,
+                       precision=O.BF16)
+    assert_close(to_np(fwd["y"]), of["y"], f"y n={n}")
+    assert_close(to_np(fwd["h"]), of["h"], f"h n={n}")
+    assert_close(to_np(fwd["g"]), of["g_saved"], f"g n={n}")
+    assert_close(to_np(fwd["u"]), of["u_saved"], f"u n={n}")
+    # the split halves give the same bits as the fused call
+    h2 = torch.empty_like(fwd["h"])
+    st.staple_ffn_gate_up(x, wg, wu, tab, ids, h2)
+    y2 = torch.empty_like(fwd["y"])
+    st.staple_ffn_down(h2, wd, y2)
+    torch.cuda.synchronize()
+    assert torch.equal(h2, fwd["h"]) and torch.equal(y2, fwd["y"])
+
+
 def test_bf16_table_contribution_and_large_table_values(st, dev):
     """Rows with E ~ N(0,1) dominate u, so wrong rows cannot hide in tolerance."""
     _log("bf16 strong table")

@@ -208,8 +208,7 @@ def staple_ffn_fwd(x: torch.Tensor, w_gate: torch.Tensor, w_up: torch.Tensor,
         if save:
             for k in ("g", "u", "h"):
                 out[k] = torch.empty(n, f, dtype=x.dtype, device=x.device)
-    need = 0 if out.get("h") is not None else lib().staple_ffn_fwd_workspace_bytes(n, d, f, dt)
-    ws = _ws(need, workspace, x.device)
+    ws = _ws(lib().staple_ffn_fwd_workspace_bytes(n, d, f, dt), workspace, x.device)
     _check(lib().staple_ffn_fwd(n, d, f, dt, _DT[out["y"].dtype], _p(x), _p(w_gate), _p(w_up),
                                 _p(w_down), _p(rows), rows.shape[0], _p(row_index), _p(out["y"]),
                                 _p(out.get("g")), _p(out.get("u")), _p(out.get("h")), _p(ws),
@@ -232,13 +231,14 @@ def staple_ffn_gate_up(x: torch.Tensor, w_gate: torch.Tensor, w_up: torch.Tensor
 
 
 def staple_ffn_down(h: torch.Tensor, w_down: torch.Tensor, y: torch.Tensor,
-                    stream=None) -> torch.Tensor:
+                    workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
     """y = h W_down^T."""
     _dev(h, w_down, y)
     n, f = h.shape
     d = w_down.shape[0]
-    _check(lib().staple_ffn_down(n, d, f, _dt(h), _DT[y.dtype], _p(h), _p(w_down), _p(y),
-                                 _stream(stream)), "staple_ffn_down")
+    ws = _ws(lib().staple_ffn_down_workspace_bytes(n, d, f, _dt(h)), workspace, h.device)
+    _check(lib().staple_ffn_down(n, d, f, _dt(h), _DT[y.dtype], _p(h), _p(w_down), _p(y), _p(ws),
+                                 _ws_size(ws), _stream(stream)), "staple_ffn_down")
     return y
 
 

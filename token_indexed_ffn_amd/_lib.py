@@ -38,7 +38,9 @@ _SIGS = {
                                c_i64, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_sz, c_vp]),
     "staple_ffn_gate_up": (c_i32, [c_i64, c_i64, c_i64, c_i32, c_vp, c_vp, c_vp, c_vp, c_i64, c_vp,
                                    c_vp, c_vp, c_vp, c_vp]),
-    "staple_ffn_down": (c_i32, [c_i64, c_i64, c_i64, c_i32, c_i32, c_vp, c_vp, c_vp, c_vp]),
+    "staple_ffn_down_workspace_bytes": (c_sz, [c_i64, c_i64, c_i64, c_i32]),
+    "staple_ffn_down": (c_i32, [c_i64, c_i64, c_i64, c_i32, c_i32, c_vp, c_vp, c_vp, c_vp, c_sz,
+                                c_vp]),
     "staple_ffn_bwd_workspace_bytes": (c_sz, [c_i64, c_i64, c_i64, c_i32]),
     "staple_ffn_bwd_table_grad": (c_i32, [c_i64, c_i64, c_i64, c_i32, c_i32, c_vp, c_vp, c_vp,
                                           c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_i64,

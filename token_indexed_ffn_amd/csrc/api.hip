@@ -59,6 +59,16 @@ template <typename T>
 hipError_t dwgu_bwd(int64_t n, int64_t d, int64_t f, const void* dgu, const void* x, float* dwg,
                     float* dwu, bool freeze_up, hipStream_t s);
 
+// kernels (decode.hip)
+bool decode_eligible(int64_t n, int64_t d, int64_t f, int dtype);
+size_t decode_down_workspace_bytes(int64_t n, int64_t d);
+hipError_t decode_gateup(int64_t n, int64_t d, int64_t f, const void* x, const void* wg,
+                         const void* wu, const void* rows, int64_t n_rows,
+                         const int32_t* row_index, void* h, void* g_out, void* u_out,
+                         hipStream_t s, int* err);
+hipError_t decode_down(int64_t n, int64_t d, int64_t f, const void* h, const void* wd, void* y,
+                       int out_dtype, void* ws, hipStream_t s);
+
 // ---------------------------------------------------------------------------
 // Per-device error word
 // ---------------------------------------------------------------------------
@@ -273,9 +283,16 @@ static bool ffn_shape_ok(int64_t n, int64_t d, int64_t f, int32_t dtype) {
          d <= (1ll << 20) && f <= (1ll << 20) && valid_dtype(dtype);
 }
 
+size_t staple_ffn_down_workspace_bytes(int64_t n, int64_t d, int64_t f, int32_t dtype) {
+  if (!ffn_shape_ok(n, d, f, dtype)) return 0;
+  return decode_eligible(n, d, f, dtype) ? align_up(decode_down_workspace_bytes(n, d), 256) : 0;
+}
+
+// workspace of staple_ffn_fwd: [h when not saved][down partials]
 size_t staple_ffn_fwd_workspace_bytes(int64_t n, int64_t d, int64_t f, int32_t dtype) {
   if (!ffn_shape_ok(n, d, f, dtype)) return 0;
-  return align_up(static_cast<size_t>(n) * f * elem_bytes(dtype), 256);
+  return align_up(static_cast<size_t>(n) * f * elem_bytes(dtype), 256) +
+         staple_ffn_down_workspace_bytes(n, d, f, dtype);
 }
 
 static staple_status_t gate_up_impl(int64_t n, int64_t d, int64_t f, int32_t dtype,
@@ -283,7 +300,10 @@ static staple_status_t gate_up_impl(int64_t n, int64_t d, int64_t f, int32_t dty
                                     const void* rows, int64_t n_rows, const int32_t* row_index,
                                     void* h, void* save_g, void* save_u, hipStream_t s) {
   GET_ERR(err);
-  if (dtype == STAPLE_BF16)
+  if (decode_eligible(n, d, f, dtype))
+    HIPCALL(decode_gateup(n, d, f, x, w_gate, w_up, rows, n_rows, row_index, h, save_g, save_u, s,
+                          err));
+  else if (dtype == STAPLE_BF16)
     HIPCALL(gateup_fwd<bf16_t>(n, d, f, x, w_gate, w_up, rows, n_rows, row_index, h, save_g,
                                save_u, s, err));
   else
@@ -293,8 +313,10 @@ static staple_status_t gate_up_impl(int64_t n, int64_t d, int64_t f, int32_t dty
 }
 
 static staple_status_t down_impl(int64_t n, int64_t d, int64_t f, int32_t dtype, int32_t out_dtype,
-                                 const void* h, const void* w_down, void* y, hipStream_t s) {
-  if (dtype == STAPLE_BF16) HIPCALL(down_fwd<bf16_t>(n, d, f, h, w_down, y, out_dtype, s));
+                                 const void* h, const void* w_down, void* y, void* ws,
+                                 hipStream_t s) {
+  if (decode_eligible(n, d, f, dtype)) HIPCALL(decode_down(n, d, f, h, w_down, y, out_dtype, ws, s));
+  else if (dtype == STAPLE_BF16) HIPCALL(down_fwd<bf16_t>(n, d, f, h, w_down, y, out_dtype, s));
   else HIPCALL(down_fwd<float>(n, d, f, h, w_down, y, out_dtype, s));
   return STAPLE_OK;
 }
@@ -314,12 +336,16 @@ staple_status_t staple_ffn_gate_up(int64_t n, int64_t d, int64_t f, int32_t dtyp
 }
 
 staple_status_t staple_ffn_down(int64_t n, int64_t d, int64_t f, int32_t dtype, int32_t out_dtype,
-                                const void* h, const void* w_down, void* y, void* stream) {
+                                const void* h, const void* w_down, void* y, void* ws,
+                                size_t ws_bytes, void* stream) {
   if (!valid_dtype(out_dtype) || !ffn_shape_ok(n, d, f, dtype)) return STAPLE_ERR_UNSUPPORTED;
   REQUIRE(w_down && aligned16(w_down));
   if (n == 0) return STAPLE_OK;
   REQUIRE(h && y && aligned16(h) && aligned16(y));
-  return down_impl(n, d, f, dtype, out_dtype, h, w_down, y, S(stream));
+  const size_t need = staple_ffn_down_workspace_bytes(n, d, f, dtype);
+  if (ws_bytes < need) return STAPLE_ERR_WORKSPACE;
+  REQUIRE(need == 0 || (ws && aligned16(ws)));
+  return down_impl(n, d, f, dtype, out_dtype, h, w_down, y, ws, S(stream));
 }
 
 staple_status_t staple_ffn_fwd(int64_t n, int64_t d, int64_t f, int32_t dtype, int32_t out_dtype,
@@ -335,17 +361,15 @@ staple_status_t staple_ffn_fwd(int64_t n, int64_t d, int64_t f, int32_t dtype, i
   REQUIRE(x && row_index && y && aligned16(x) && aligned16(y));
   REQUIRE((!save_g || aligned16(save_g)) && (!save_u || aligned16(save_u)) &&
           (!save_h || aligned16(save_h)));
-  void* h = save_h;
-  if (h == nullptr) {
-    if (ws_bytes < staple_ffn_fwd_workspace_bytes(n, d, f, dtype)) return STAPLE_ERR_WORKSPACE;
-    REQUIRE(ws && aligned16(ws));
-    h = ws;
-  }
+  if (ws_bytes < staple_ffn_fwd_workspace_bytes(n, d, f, dtype)) return STAPLE_ERR_WORKSPACE;
+  REQUIRE(ws && aligned16(ws));
+  void* h = save_h ? save_h : ws;
+  void* down_ws = static_cast<char*>(ws) + align_up(static_cast<size_t>(n) * f * elem_bytes(dtype), 256);
   hipStream_t s = S(stream);
   staple_status_t st = gate_up_impl(n, d, f, dtype, x, w_gate, w_up, rows, n_rows, row_index, h,
                                     save_g, save_u, s);
   if (st != STAPLE_OK) return st;
-  return down_impl(n, d, f, dtype, out_dtype, h, w_down, y, s);
+  return down_impl(n, d, f, dtype, out_dtype, h, w_down, y, down_ws, s);
 }
 
 size_t staple_ffn_bwd_workspace_bytes(int64_t n, int64_t d, int64_t f, int32_t dtype) {

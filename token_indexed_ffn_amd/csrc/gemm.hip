@@ -15,7 +15,8 @@
 // half h supplies k = 8h + j to the j-th instruction, for A and B alike, so
 // the contraction covers all 16 k of the group.
 //
-// Epilogues:
+// Epilogues stage each wave's accumulators through LDS, 32 rows at a time,
+// so every global access of the epilogue is a 16-byte vector along a row:
 //   Store   - C to fp32 or bf16 (optionally split by rows into two buffers).
 //   GateUp  - the B rows interleave W_gate and W_up in 32-row groups, so one
 //             wave holds g and a = W_up x for the same (token, feature); the
@@ -70,19 +71,24 @@ struct GemmArgs {
   int* err;
 };
 
-constexpr int kGemmThreads = 256;
 constexpr int kRowBytes = 128;  // bytes of k per LDS tile row and stage
 
-__device__ __forceinline__ int swz(int row, int chunk) { return row * kRowBytes + ((chunk ^ (row & 7)) << 4); }
+// LDS tile rows are 128 bytes (8 chunks of 16 bytes).  The chunk index is
+// XORed with bits 0-2 and 3-5 of the row, so that both the MFMA fragment reads
+// (consecutive rows, one chunk) and the transposed stores of MN-major tiles
+// (rows 8 apart, one chunk) spread over the LDS banks.
+__device__ __forceinline__ int swz(int row, int chunk) {
+  return row * kRowBytes + ((chunk ^ (row & 7) ^ ((row >> 3) & 7)) << 4);
+}
 
 // ---------------------------------------------------------------------------
 // Tile loaders: global -> registers -> LDS
 // ---------------------------------------------------------------------------
-// K-major operand tile of R rows x 128 bytes.  Thread t moves 16-byte chunk
-// (t & 7) of rows (t >> 3) + 32 i.
-template <int R>
+// K-major operand tile of R rows x 128 bytes.  Thread t of NT moves 16-byte
+// chunk (t & 7) of rows (t >> 3) + (NT / 8) i.
+template <int R, int NT>
 struct KMajorTile {
-  static constexpr int kPer = R * 8 / kGemmThreads;
+  static constexpr int kPer = R * 8 / NT;
   const char* row_ptr[kPer];
   uint4 reg[kPer];
 
@@ -96,23 +102,23 @@ struct KMajorTile {
     const int c = threadIdx.x & 7;
 #pragma unroll
     for (int i = 0; i < kPer; ++i) {
-      const int r = (threadIdx.x >> 3) + 32 * i;
+      const int r = (threadIdx.x >> 3) + (NT / 8) * i;
       *reinterpret_cast<uint4*>(lds + swz(r, c)) = reg[i];
     }
   }
-  __device__ __forceinline__ static int row_of(int i) { return (threadIdx.x >> 3) + 32 * i; }
+  __device__ __forceinline__ static int row_of(int i) { return (threadIdx.x >> 3) + (NT / 8) * i; }
 };
 
 // MN-major operand tile: BK k-rows x R contiguous elements.  A unit is 4
 // consecutive k x one 16-byte vector; it is transposed in registers into
 // K-major pieces (8 bytes per row for bf16, 16 bytes for fp32).
-template <typename T, int R>
+template <typename T, int R, int NT>
 struct MNMajorTile {
   static constexpr int kVec = 16 / sizeof(T);                 // elements per 16-byte vector
   static constexpr int kBK = kRowBytes / sizeof(T);           // k per stage
   static constexpr int kChunks = R / kVec;                    // vectors per k-row
   static constexpr int kUnits = (kBK / 4) * kChunks;
-  static constexpr int kPer = (kUnits + kGemmThreads - 1) / kGemmThreads;
+  static constexpr int kPer = (kUnits + NT - 1) / NT;
   uint4 reg[kPer][4];
 
   // base(k) returns the element pointer of k-row k (already offset to the
@@ -122,7 +128,7 @@ struct MNMajorTile {
   __device__ __forceinline__ void load(int64_t k0, BaseFn base, int64_t cols) {
 #pragma unroll
     for (int i = 0; i < kPer; ++i) {
-      const int q = threadIdx.x + kGemmThreads * i;
+      const int q = threadIdx.x + NT * i;
       const int rc = q % kChunks;
       const int kq = q / kChunks;
 #pragma unroll
@@ -139,7 +145,7 @@ struct MNMajorTile {
   __device__ __forceinline__ void store(char* lds) const {
 #pragma unroll
     for (int i = 0; i < kPer; ++i) {
-      const int q = threadIdx.x + kGemmThreads * i;
+      const int q = threadIdx.x + NT * i;
       if (q >= kUnits) continue;
       const int rc = q % kChunks;
       const int kq = q / kChunks;
@@ -243,33 +249,107 @@ struct Mma<float, TM, TN> {
   }
 };
 
+// Output tile of this workgroup.  Workgroups are dispatched round-robin over
+// the 8 XCDs, each with its own L2: the linear index is first remapped so that
+// every XCD owns one contiguous range of tiles, then tiles are ordered in
+// groups of 8 M-tiles that sweep the N-tiles, so the workgroups running side
+// by side on one XCD share a few A and B panels in that XCD's L2.
+__device__ __forceinline__ void tile_coords(int64_t tiles_m, int64_t tiles_n, int64_t& mt,
+                                            int64_t& nt) {
+  const int64_t total = tiles_m * tiles_n;
+  int64_t b = blockIdx.x;
+  if (total % 8 == 0) b = (b % 8) * (total / 8) + b / 8;
+  constexpr int64_t G = 8;
+  const int64_t group = b / (G * tiles_n);
+  const int64_t first_m = group * G;
+  const int64_t gsize = (tiles_m - first_m) < G ? (tiles_m - first_m) : G;
+  const int64_t in = b - group * G * tiles_n;
+  mt = first_m + in % gsize;
+  nt = in / gsize;
+}
+
 // Row of output element r (0..15) of a 32x32 MFMA tile for this lane.
 __device__ __forceinline__ int mfma_row(int r, int lane) { return 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3); }
 
 // ---------------------------------------------------------------------------
-// The kernel
+// Epilogue staging: one wave's 32-row block of accumulators as fp32 rows of
+// WN values in LDS (row stride WN + 4 floats against bank conflicts).
 // ---------------------------------------------------------------------------
-template <typename T, int BM, int BN, bool AK, bool BK, int EPI, typename OutT>
-__global__ __launch_bounds__(kGemmThreads) void gemm_kernel(GemmArgs p) {
-  constexpr int WM = BM / 2, WN = BN / 2;   // 2 x 2 waves
+template <int TN>
+__device__ __forceinline__ void stage_rows(float* region, const f32x16_t (&acc)[TN]) {
+  constexpr int WN = TN * 32, LD = WN + 4;
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int j = 0; j < TN; ++j)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) region[mfma_row(r, lane) * LD + j * 32 + (lane & 31)] = acc[j][r];
+}
+
+__device__ __forceinline__ void read8(const float* p, float (&v)[8]) {
+  const float4 a = *reinterpret_cast<const float4*>(p);
+  const float4 b = *reinterpret_cast<const float4*>(p + 4);
+  v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w; v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+}
+
+template <typename T>
+__device__ __forceinline__ void load8g(const void* base, int64_t idx, float (&v)[8]) {
+  if constexpr (sizeof(T) == 2) {
+    const uint4 q = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(base) + idx);
+    const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[2 * i] = __uint_as_float(w[i] << 16);
+      v[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+    }
+  } else {
+    read8(static_cast<const float*>(base) + idx, v);
+  }
+}
+
+template <typename T>
+__device__ __forceinline__ void store8g(void* base, int64_t idx, const float (&v)[8]) {
+  if constexpr (sizeof(T) == 2) {
+    uint4 q;
+    q.x = static_cast<uint32_t>(f32_to_bf16(v[0])) | (static_cast<uint32_t>(f32_to_bf16(v[1])) << 16);
+    q.y = static_cast<uint32_t>(f32_to_bf16(v[2])) | (static_cast<uint32_t>(f32_to_bf16(v[3])) << 16);
+    q.z = static_cast<uint32_t>(f32_to_bf16(v[4])) | (static_cast<uint32_t>(f32_to_bf16(v[5])) << 16);
+    q.w = static_cast<uint32_t>(f32_to_bf16(v[6])) | (static_cast<uint32_t>(f32_to_bf16(v[7])) << 16);
+    *reinterpret_cast<uint4*>(static_cast<uint16_t*>(base) + idx) = q;
+  } else {
+    float* p = static_cast<float*>(base) + idx;
+    *reinterpret_cast<float4*>(p) = make_float4(v[0], v[1], v[2], v[3]);
+    *reinterpret_cast<float4*>(p + 4) = make_float4(v[4], v[5], v[6], v[7]);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// The kernel: BM x BN tile, WGM x WGN waves, 2 LDS stages of 128 bytes of k.
+// ---------------------------------------------------------------------------
+template <typename T, int BM, int BN, int WGM, int WGN, bool AK, bool BK, int EPI, typename OutT>
+__global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(GemmArgs p) {
+  constexpr int NT = 64 * WGM * WGN;
+  constexpr int WM = BM / WGM, WN = BN / WGN;
   constexpr int TM = WM / 32, TN = WN / 32;
   constexpr int kBK = kRowBytes / sizeof(T);
   static_assert(EPI != kEpiGateUp || WN % 64 == 0, "gate/up pairing needs 64-column wave tiles");
+  static_assert((32 * (WN + 4) * 4) * WGM * WGN <= 2 * (BM + BN) * kRowBytes, "epilogue staging");
 
-  __shared__ __attribute__((aligned(16))) char smem[2 * (BM + BN) * kRowBytes];
+  extern __shared__ __attribute__((aligned(16))) char smem[];   // 2 stages x (BM + BN) rows
   char* As0 = smem;
   char* Bs0 = smem + BM * kRowBytes;
   constexpr int kStage = (BM + BN) * kRowBytes;
 
-  const int64_t m0 = static_cast<int64_t>(blockIdx.x) * BM;
-  const int64_t n0 = static_cast<int64_t>(blockIdx.y) * BN;
+  int64_t mt, nt;
+  tile_coords((p.M + BM - 1) / BM, (p.N + BN - 1) / BN, mt, nt);
+  const int64_t m0 = mt * BM;
+  const int64_t n0 = nt * BN;
   const int lane = threadIdx.x & 63;
   const int wid = threadIdx.x >> 6;
-  const int wm = wid >> 1, wn = wid & 1;
+  const int wm = wid / WGN, wn = wid % WGN;
 
   // ---- operand addressing ----
-  using ATile = typename std::conditional<AK, KMajorTile<BM>, MNMajorTile<T, BM>>::type;
-  using BTile = typename std::conditional<BK, KMajorTile<BN>, MNMajorTile<T, BN>>::type;
+  using ATile = typename std::conditional<AK, KMajorTile<BM, NT>, MNMajorTile<T, BM, NT>>::type;
+  using BTile = typename std::conditional<BK, KMajorTile<BN, NT>, MNMajorTile<T, BN, NT>>::type;
   ATile at;
   BTile bt;
   if constexpr (AK) {
@@ -347,84 +427,118 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(GemmArgs p) {
     __syncthreads();
   }
 
-  // ---- epilogues ----
-  const int col_in = lane & 31;
-  if constexpr (EPI == kEpiStore) {
+  // ---- epilogue: per 32-row block, stage through this wave's LDS region ----
+  constexpr int LD = WN + 4;
+  float* region = reinterpret_cast<float*>(smem) + wid * 32 * LD;
+  constexpr int kChunks = 32 * WN / 8;          // 8-column chunks per 32-row block
 #pragma unroll
-    for (int i = 0; i < TM; ++i)
+  for (int i = 0; i < TM; ++i) {
+    stage_rows<TN>(region, acc[i]);
+    __syncthreads();
+    const int64_t mrow0 = m0 + wm * WM + i * 32;
+    if constexpr (EPI == kEpiStore) {
 #pragma unroll
-      for (int j = 0; j < TN; ++j) {
-        const int64_t n = n0 + wn * WN + j * 32 + col_in;
-        if (n >= p.N) continue;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int64_t m = m0 + wm * WM + i * 32 + mfma_row(r, lane);
-          if (m >= p.M) continue;
+      for (int q = lane; q < kChunks; q += 64) {
+        const int rr = q / (WN / 8), cc = (q % (WN / 8)) * 8;
+        const int64_t m = mrow0 + rr;
+        const int64_t n = n0 + wn * WN + cc;
+        if (m < p.M && n < p.N) {
+          float v[8];
+          read8(region + rr * LD + cc, v);
           void* cb = m < p.c_split ? p.c0 : p.c1;
           const int64_t mm = m < p.c_split ? m : m - p.c_split;
-          Elem<OutT>::store(cb, mm * p.ldc + n, acc[i][j][r]);
+          store8g<OutT>(cb, mm * p.ldc + n, v);
         }
       }
-  } else if constexpr (EPI == kEpiGateUp) {
-    const int64_t f = p.d_ff;
+    } else if constexpr (EPI == kEpiGateUp) {
+      // wave columns: pairs of [32 gate | 32 up] for the same 32 features
+      constexpr int kFeatChunks = 32 * (WN / 2) / 8;
+      const int64_t f = p.d_ff;
 #pragma unroll
-    for (int i = 0; i < TM; ++i)
-#pragma unroll
-      for (int q = 0; q < TN / 2; ++q) {
-        const int64_t feat = (n0 + wn * WN + q * 64) / 2 + col_in;
-        if (feat >= f) continue;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int64_t m = m0 + wm * WM + i * 32 + mfma_row(r, lane);
-          if (m >= p.M) continue;
+      for (int q = lane; q < kFeatChunks; q += 64) {
+        const int rr = q / (WN / 16);
+        const int fc = (q % (WN / 16)) * 8;           // feature offset within the wave's WN/2
+        const int pair = fc / 32, fin = fc % 32;
+        const int64_t m = mrow0 + rr;
+        const int64_t feat = (n0 + wn * WN) / 2 + fc;
+        if (m < p.M && feat < f) {
+          float g[8], a[8], e[8];
+          read8(region + rr * LD + pair * 64 + fin, g);
+          read8(region + rr * LD + pair * 64 + 32 + fin, a);
           const int64_t tok = p.a_rows ? static_cast<int64_t>(p.a_rows[m]) : m;
           const int64_t ri = p.row_index[tok];
-          float e = 0.0f;
-          if (ri >= 0 && ri < p.n_rows) e = Elem<T>::load(p.rows, ri * f + feat);
-          else flag_index_error(p.err);
-          const float g = acc[i][2 * q][r];
-          const float u = acc[i][2 * q + 1][r] + e;
-          const float h = g * sigmoidf_(g) * u;
+          if (ri >= 0 && ri < p.n_rows) {
+            load8g<T>(p.rows, ri * f + feat, e);
+          } else {
+            flag_index_error(p.err);
+#pragma unroll
+            for (int k = 0; k < 8; ++k) e[k] = 0.0f;
+          }
+          float u[8], h[8];
+#pragma unroll
+          for (int k = 0; k < 8; ++k) {
+            u[k] = a[k] + e[k];
+            h[k] = g[k] * sigmoidf_(g[k]) * u[k];
+          }
           const int64_t o = tok * f + feat;
-          Elem<T>::store(p.h_out, o, h);
-          if (p.g_out) Elem<T>::store(p.g_out, o, g);
-          if (p.u_out) Elem<T>::store(p.u_out, o, u);
+          store8g<T>(p.h_out, o, h);
+          if (p.g_out) store8g<T>(p.g_out, o, g);
+          if (p.u_out) store8g<T>(p.u_out, o, u);
         }
       }
-  } else {  // kEpiDhAct: C = dh (M = tokens, N = d_ff)
-    const int64_t f = p.N;
+    } else {  // kEpiDhAct: C = dh (M = tokens, N = d_ff)
+      const int64_t f = p.N;
 #pragma unroll
-    for (int i = 0; i < TM; ++i)
+      for (int q = lane; q < kChunks; q += 64) {
+        const int rr = q / (WN / 8), cc = (q % (WN / 8)) * 8;
+        const int64_t m = mrow0 + rr;
+        const int64_t n = n0 + wn * WN + cc;
+        if (m < p.M && n < f) {
+          float dh[8], g[8], u[8], dg[8], du[8];
+          read8(region + rr * LD + cc, dh);
+          load8g<T>(p.g_in, m * f + n, g);
+          load8g<T>(p.u_in, m * f + n, u);
 #pragma unroll
-      for (int j = 0; j < TN; ++j) {
-        const int64_t n = n0 + wn * WN + j * 32 + col_in;
-        if (n >= f) continue;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int64_t m = m0 + wm * WM + i * 32 + mfma_row(r, lane);
-          if (m >= p.M) continue;
-          const float dh = acc[i][j][r];
-          const float g = Elem<T>::load(p.g_in, m * f + n);
-          const float u = Elem<T>::load(p.u_in, m * f + n);
-          const float s = sigmoidf_(g);
-          const float du = dh * g * s;
-          const float dg = dh * u * s * (1.0f + g * (1.0f - s));
-          Elem<T>::store(p.dgu_out, m * 2 * f + n, dg);
-          Elem<T>::store(p.dgu_out, m * 2 * f + f + n, du);
+          for (int k = 0; k < 8; ++k) {
+            const float s = sigmoidf_(g[k]);
+            du[k] = dh[k] * g[k] * s;
+            dg[k] = dh[k] * u[k] * s * (1.0f + g[k] * (1.0f - s));
+          }
+          store8g<T>(p.dgu_out, m * 2 * f + n, dg);
+          store8g<T>(p.dgu_out, m * 2 * f + f + n, du);
         }
       }
+    }
+    __syncthreads();
   }
 }
 
 // ---------------------------------------------------------------------------
 // Host launchers
 // ---------------------------------------------------------------------------
-template <typename T, int BM, int BN, bool AK, bool BK, int EPI, typename OutT>
+template <typename T, int BM, int BN, int WGM, int WGN, bool AK, bool BK, int EPI, typename OutT>
+static hipError_t run_tile(const GemmArgs& a, hipStream_t s) {
+  constexpr size_t kSmem = 2 * (BM + BN) * kRowBytes;
+  auto kern = &gemm_kernel<T, BM, BN, WGM, WGN, AK, BK, EPI, OutT>;
+  static const hipError_t attr = hipFuncSetAttribute(
+      reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
+      static_cast<int>(kSmem));
+  if (attr != hipSuccess) return attr;
+  const int64_t tiles = ((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN);
+  kern<<<dim3(static_cast<unsigned>(tiles)), dim3(64 * WGM * WGN), kSmem, s>>>(a);
+  return hipGetLastError();
+}
+
+// 256x256 tiles on 8 waves (128x64 per wave) for large bf16 problems,
+// 128x128 tiles on 4 waves otherwise.
+template <typename T, bool AK, bool BK, int EPI, typename OutT>
 static hipError_t run(const GemmArgs& a, hipStream_t s) {
   if (a.M <= 0 || a.N <= 0) return hipSuccess;
-  dim3 grid(static_cast<unsigned>((a.M + BM - 1) / BM), static_cast<unsigned>((a.N + BN - 1) / BN));
-  gemm_kernel<T, BM, BN, AK, BK, EPI, OutT><<<grid, dim3(kGemmThreads), 0, s>>>(a);
-  return hipGetLastError();
+  if constexpr (sizeof(T) == 2) {
+    if (a.M >= 256 && a.N >= 256 && ((a.M + 255) / 256) * ((a.N + 255) / 256) >= 128)
+      return run_tile<T, 256, 256, 2, 4, AK, BK, EPI, OutT>(a, s);
+  }
+  return run_tile<T, 128, 128, 2, 2, AK, BK, EPI, OutT>(a, s);
 }
 
 template <typename T>
@@ -445,7 +559,7 @@ hipError_t gateup_fwd(int64_t n, int64_t d, int64_t f, const void* x, const void
   a.b0 = wg; a.b1 = wu; a.ldb = d;
   a.rows = rows; a.row_index = row_index; a.n_rows = n_rows; a.d_ff = f;
   a.h_out = h; a.g_out = g_out; a.u_out = u_out; a.err = err;
-  return run<T, 128, 128, true, true, kEpiGateUp, T>(a, s);
+  return run<T, true, true, kEpiGateUp, T>(a, s);
 }
 
 // y = h W_down^T
@@ -457,8 +571,8 @@ hipError_t down_fwd(int64_t n, int64_t d, int64_t f, const void* h, const void* 
   a.a0 = h; a.lda = f;
   a.b0 = wd; a.ldb = f;
   a.c0 = y; a.ldc = d;
-  if (out_dtype == STAPLE_F32) return run<T, 128, 128, true, true, kEpiStore, float>(a, s);
-  return run<T, 128, 128, true, true, kEpiStore, bf16_t>(a, s);
+  if (out_dtype == STAPLE_F32) return run<T, true, true, kEpiStore, float>(a, s);
+  return run<T, true, true, kEpiStore, bf16_t>(a, s);
 }
 
 // dh = dy W_down; dgu[:, :f] = dg, dgu[:, f:] = du
@@ -470,7 +584,7 @@ hipError_t dh_act(int64_t n, int64_t d, int64_t f, const void* dy, const void* w
   a.a0 = dy; a.lda = d;
   a.b0 = wd; a.ldb = f;          // B(k=j, n) = W_down[j, n]
   a.g_in = g; a.u_in = u; a.dgu_out = dgu;
-  return run<T, 128, 128, true, false, kEpiDhAct, T>(a, s);
+  return run<T, true, false, kEpiDhAct, T>(a, s);
 }
 
 // dx = dg W_gate + du W_up  (K = 2f over the concatenated [dg | du])
@@ -482,8 +596,8 @@ hipError_t dx_bwd(int64_t n, int64_t d, int64_t f, const void* dgu, const void* 
   a.a0 = dgu; a.lda = 2 * f;
   a.b0 = wg; a.b1 = wu; a.ldb = d; a.b_split = f;
   a.c0 = dx; a.ldc = d;
-  if (out_dtype == STAPLE_F32) return run<T, 128, 128, true, false, kEpiStore, float>(a, s);
-  return run<T, 128, 128, true, false, kEpiStore, bf16_t>(a, s);
+  if (out_dtype == STAPLE_F32) return run<T, true, false, kEpiStore, float>(a, s);
+  return run<T, true, false, kEpiStore, bf16_t>(a, s);
 }
 
 // dw_down = dy^T h   (M = d, N = f, K = tokens)
@@ -495,7 +609,7 @@ hipError_t dwdown_bwd(int64_t n, int64_t d, int64_t f, const void* dy, const voi
   a.a0 = dy; a.lda = d;
   a.b0 = h; a.ldb = f;
   a.c0 = dwd; a.ldc = f;
-  return run<T, 128, 128, false, false, kEpiStore, float>(a, s);
+  return run<T, false, false, kEpiStore, float>(a, s);
 }
 
 // [dw_gate; dw_up] = [dg | du]^T x   (M = 2f, or f when the up-projection is frozen)
@@ -507,7 +621,7 @@ hipError_t dwgu_bwd(int64_t n, int64_t d, int64_t f, const void* dgu, const void
   a.a0 = dgu; a.lda = 2 * f;
   a.b0 = x; a.ldb = d;
   a.c0 = dwg; a.c1 = dwu; a.ldc = d; a.c_split = f;
-  return run<T, 128, 128, false, false, kEpiStore, float>(a, s);
+  return run<T, false, false, kEpiStore, float>(a, s);
 }
 
 #define STAPLE_INST(T)                                                                          \
