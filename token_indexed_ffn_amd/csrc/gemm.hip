@@ -90,20 +90,22 @@ template <int R, int NT>
 struct KMajorTile {
   static constexpr int kPer = R * 8 / NT;
   const char* row_ptr[kPer];
-  uint4 reg[kPer];
+  uint4 reg[2][kPer];
 
+  template <int S>
   __device__ __forceinline__ void load(int64_t k_byte) {
     const int c = threadIdx.x & 7;
 #pragma unroll
     for (int i = 0; i < kPer; ++i)
-      reg[i] = *reinterpret_cast<const uint4*>(row_ptr[i] + k_byte + c * 16);
+      reg[S][i] = *reinterpret_cast<const uint4*>(row_ptr[i] + k_byte + c * 16);
   }
+  template <int S>
   __device__ __forceinline__ void store(char* lds) const {
     const int c = threadIdx.x & 7;
 #pragma unroll
     for (int i = 0; i < kPer; ++i) {
       const int r = (threadIdx.x >> 3) + (NT / 8) * i;
-      *reinterpret_cast<uint4*>(lds + swz(r, c)) = reg[i];
+      *reinterpret_cast<uint4*>(lds + swz(r, c)) = reg[S][i];
     }
   }
   __device__ __forceinline__ static int row_of(int i) { return (threadIdx.x >> 3) + (NT / 8) * i; }
@@ -119,12 +121,12 @@ struct MNMajorTile {
   static constexpr int kChunks = R / kVec;                    // vectors per k-row
   static constexpr int kUnits = (kBK / 4) * kChunks;
   static constexpr int kPer = (kUnits + NT - 1) / NT;
-  uint4 reg[kPer][4];
+  uint4 reg[2][kPer][4];
 
   // base(k) returns the element pointer of k-row k (already offset to the
   // tile's first column) or nullptr when the row lies outside the operand;
   // `cols` is the number of valid columns in the tile.
-  template <typename BaseFn>
+  template <int S, typename BaseFn>
   __device__ __forceinline__ void load(int64_t k0, BaseFn base, int64_t cols) {
 #pragma unroll
     for (int i = 0; i < kPer; ++i) {
@@ -135,13 +137,14 @@ struct MNMajorTile {
       for (int kk = 0; kk < 4; ++kk) {
         const T* rowp = (q < kUnits) ? base(k0 + kq * 4 + kk) : nullptr;
         if (rowp != nullptr && static_cast<int64_t>(rc) * kVec < cols)
-          reg[i][kk] = *reinterpret_cast<const uint4*>(rowp + rc * kVec);
+          reg[S][i][kk] = *reinterpret_cast<const uint4*>(rowp + rc * kVec);
         else
-          reg[i][kk] = make_uint4(0, 0, 0, 0);
+          reg[S][i][kk] = make_uint4(0, 0, 0, 0);
       }
     }
   }
 
+  template <int S>
   __device__ __forceinline__ void store(char* lds) const {
 #pragma unroll
     for (int i = 0; i < kPer; ++i) {
@@ -149,11 +152,11 @@ struct MNMajorTile {
       if (q >= kUnits) continue;
       const int rc = q % kChunks;
       const int kq = q / kChunks;
+      const uint32_t* v0 = reinterpret_cast<const uint32_t*>(&reg[S][i][0]);
+      const uint32_t* v1 = reinterpret_cast<const uint32_t*>(&reg[S][i][1]);
+      const uint32_t* v2 = reinterpret_cast<const uint32_t*>(&reg[S][i][2]);
+      const uint32_t* v3 = reinterpret_cast<const uint32_t*>(&reg[S][i][3]);
       if constexpr (sizeof(T) == 2) {
-        const uint32_t* v0 = reinterpret_cast<const uint32_t*>(&reg[i][0]);
-        const uint32_t* v1 = reinterpret_cast<const uint32_t*>(&reg[i][1]);
-        const uint32_t* v2 = reinterpret_cast<const uint32_t*>(&reg[i][2]);
-        const uint32_t* v3 = reinterpret_cast<const uint32_t*>(&reg[i][3]);
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           // elements 2j (low halves) and 2j+1 (high halves) of the four k-rows
@@ -163,15 +166,10 @@ struct MNMajorTile {
           hi.x = (v0[j] >> 16) | (v1[j] & 0xffff0000u);
           hi.y = (v2[j] >> 16) | (v3[j] & 0xffff0000u);
           const int r0 = rc * 8 + 2 * j;
-          const int r1 = r0 + 1;
           *reinterpret_cast<uint2*>(lds + swz(r0, kq >> 1) + (kq & 1) * 8) = lo;
-          *reinterpret_cast<uint2*>(lds + swz(r1, kq >> 1) + (kq & 1) * 8) = hi;
+          *reinterpret_cast<uint2*>(lds + swz(r0 + 1, kq >> 1) + (kq & 1) * 8) = hi;
         }
       } else {
-        const uint32_t* v0 = reinterpret_cast<const uint32_t*>(&reg[i][0]);
-        const uint32_t* v1 = reinterpret_cast<const uint32_t*>(&reg[i][1]);
-        const uint32_t* v2 = reinterpret_cast<const uint32_t*>(&reg[i][2]);
-        const uint32_t* v3 = reinterpret_cast<const uint32_t*>(&reg[i][3]);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const uint4 w = make_uint4(v0[e], v1[e], v2[e], v3[e]);
@@ -325,7 +323,8 @@ __device__ __forceinline__ void store8g(void* base, int64_t idx, const float (&v
 // ---------------------------------------------------------------------------
 // The kernel: BM x BN tile, WGM x WGN waves, 2 LDS stages of 128 bytes of k.
 // ---------------------------------------------------------------------------
-template <typename T, int BM, int BN, int WGM, int WGN, bool AK, bool BK, int EPI, typename OutT>
+template <typename T, int BM, int BN, int WGM, int WGN, int NSLOT, bool AK, bool BK, int EPI,
+          typename OutT>
 __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(GemmArgs p) {
   constexpr int NT = 64 * WGM * WGN;
   constexpr int WM = BM / WGM, WN = BN / WGN;
@@ -391,14 +390,6 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(GemmArgs p) {
                                : static_cast<const T*>(p.b1) + (k - p.b_split) * p.ldb;
     return b + n0;
   };
-  auto load_tiles = [&](int64_t kt) {
-    const int64_t k0 = kt * kBK;
-    if constexpr (AK) at.load(k0 * static_cast<int64_t>(sizeof(T)));
-    else at.load(k0, a_base, a_cols);
-    if constexpr (BK) bt.load(k0 * static_cast<int64_t>(sizeof(T)));
-    else bt.load(k0, b_base, b_cols);
-  };
-
   f32x16_t acc[TM][TN];
 #pragma unroll
   for (int i = 0; i < TM; ++i)
@@ -407,24 +398,63 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(GemmArgs p) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
-  const int64_t nk = (p.K + kBK - 1) / kBK;
-  load_tiles(0);
-  at.store(As0);
-  bt.store(Bs0);
-  __syncthreads();
-  for (int64_t kt = 0; kt < nk; ++kt) {
-    const int cur = static_cast<int>(kt & 1);
-    if (kt + 1 < nk) load_tiles(kt + 1);
-    const char* As = As0 + cur * kStage;
-    const char* Bs = Bs0 + cur * kStage;
+  auto load_tiles = [&](auto slot, int64_t kt) {
+    constexpr int S = decltype(slot)::value;
+    const int64_t k0 = kt * kBK;
+    if constexpr (AK) at.template load<S>(k0 * static_cast<int64_t>(sizeof(T)));
+    else at.template load<S>(k0, a_base, a_cols);
+    if constexpr (BK) bt.template load<S>(k0 * static_cast<int64_t>(sizeof(T)));
+    else bt.template load<S>(k0, b_base, b_cols);
+  };
+  auto store_tiles = [&](auto slot, int buf) {
+    constexpr int S = decltype(slot)::value;
+    at.template store<S>(As0 + buf * kStage);
+    bt.template store<S>(Bs0 + buf * kStage);
+  };
+  auto compute = [&](int buf) {
+    const char* As = As0 + buf * kStage;
+    const char* Bs = Bs0 + buf * kStage;
 #pragma unroll
     for (int kg = 0; kg < Mma<T, TM, TN>::kGroups; ++kg)
       Mma<T, TM, TN>::step(As, Bs, wm * WM, wn * WN, kg, acc);
-    if (kt + 1 < nk) {
-      at.store(As0 + (cur ^ 1) * kStage);
-      bt.store(Bs0 + (cur ^ 1) * kStage);
-    }
+  };
+  using S0 = std::integral_constant<int, 0>;
+  using S1 = std::integral_constant<int, 1>;
+
+  const int64_t nk = (p.K + kBK - 1) / kBK;
+  if constexpr (NSLOT == 2) {
+    // Two register slots keep the global loads two stages ahead of the MFMAs:
+    // while stage kt is multiplied out of one LDS buffer, stage kt+1 waits in
+    // registers for the other buffer and stage kt+2 is in flight.  Loads past
+    // the last stage re-read it (clamped) so the loop has no conditional loads.
+    auto clampk = [&](int64_t k) { return k < nk ? k : nk - 1; };
+    load_tiles(S0{}, 0);
+    load_tiles(S1{}, clampk(1));
+    store_tiles(S0{}, 0);
     __syncthreads();
+    for (int64_t kt = 0; kt < nk; kt += 2) {
+      load_tiles(S0{}, clampk(kt + 2));
+      compute(0);
+      store_tiles(S1{}, 1);
+      __syncthreads();
+      if (kt + 1 >= nk) break;
+      load_tiles(S1{}, clampk(kt + 3));
+      compute(1);
+      store_tiles(S0{}, 0);
+      __syncthreads();
+    }
+  } else {
+    // One register slot: stage kt+1 is loaded while stage kt is multiplied.
+    load_tiles(S0{}, 0);
+    store_tiles(S0{}, 0);
+    __syncthreads();
+    for (int64_t kt = 0; kt < nk; ++kt) {
+      const int cur = static_cast<int>(kt & 1);
+      if (kt + 1 < nk) load_tiles(S0{}, kt + 1);
+      compute(cur);
+      if (kt + 1 < nk) store_tiles(S0{}, cur ^ 1);
+      __syncthreads();
+    }
   }
 
   // ---- epilogue: per 32-row block, stage through this wave's LDS region ----
@@ -516,10 +546,11 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(GemmArgs p) {
 // ---------------------------------------------------------------------------
 // Host launchers
 // ---------------------------------------------------------------------------
-template <typename T, int BM, int BN, int WGM, int WGN, bool AK, bool BK, int EPI, typename OutT>
+template <typename T, int BM, int BN, int WGM, int WGN, int NSLOT, bool AK, bool BK, int EPI,
+          typename OutT>
 static hipError_t run_tile(const GemmArgs& a, hipStream_t s) {
   constexpr size_t kSmem = 2 * (BM + BN) * kRowBytes;
-  auto kern = &gemm_kernel<T, BM, BN, WGM, WGN, AK, BK, EPI, OutT>;
+  auto kern = &gemm_kernel<T, BM, BN, WGM, WGN, NSLOT, AK, BK, EPI, OutT>;
   static const hipError_t attr = hipFuncSetAttribute(
       reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
       static_cast<int>(kSmem));
@@ -529,16 +560,22 @@ static hipError_t run_tile(const GemmArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-// 256x256 tiles on 8 waves (128x64 per wave) for large bf16 problems,
-// 128x128 tiles on 4 waves otherwise.
+// Shape of the large-problem tile: 0 = 256x256 on 8 waves (128x64 per wave),
+// one register slot; 1 = 256x256 on 4 waves (128x128 per wave), two slots.
+static int g_big_tile = 0;
+void gemm_set_big_tile(int v) { g_big_tile = v; }
+
+// 256x256 tiles for large bf16 problems, 128x128 tiles on 4 waves otherwise.
 template <typename T, bool AK, bool BK, int EPI, typename OutT>
 static hipError_t run(const GemmArgs& a, hipStream_t s) {
   if (a.M <= 0 || a.N <= 0) return hipSuccess;
   if constexpr (sizeof(T) == 2) {
-    if (a.M >= 256 && a.N >= 256 && ((a.M + 255) / 256) * ((a.N + 255) / 256) >= 128)
-      return run_tile<T, 256, 256, 2, 4, AK, BK, EPI, OutT>(a, s);
+    if (a.M >= 256 && a.N >= 256 && ((a.M + 255) / 256) * ((a.N + 255) / 256) >= 128) {
+      if (g_big_tile == 0) return run_tile<T, 256, 256, 2, 4, 1, AK, BK, EPI, OutT>(a, s);
+      return run_tile<T, 256, 256, 2, 2, 2, AK, BK, EPI, OutT>(a, s);
+    }
   }
-  return run_tile<T, 128, 128, 2, 2, AK, BK, EPI, OutT>(a, s);
+  return run_tile<T, 128, 128, 2, 2, 1, AK, BK, EPI, OutT>(a, s);
 }
 
 template <typename T>
