@@ -374,6 +374,173 @@ def train_cpu_baseline(torch, w, T, seconds):
                       "(dedup + forward + backward, float64 numpy, bf16 rounding points)"}
 
 
+
+# ----------------------------------------------------------------------------
+# Host-offloaded tables with the HBM row cache (decode batch and training batch)
+# ----------------------------------------------------------------------------
+def setup_offload(torch, st, w, n_layers):
+    """Pinned host tables (one per layer), the calibration-ranked HBM cache and
+    per-layer cached rows."""
+    import numpy as np
+    import staple_synth as S
+    from staple_synth import device_normal
+    dev = torch.device("cuda:0")
+    v, f = w.vocab, w.d_ff
+    counts = torch.from_numpy(S.calibration_counts(v)).to(dev)
+    cap = w.cache_capacity
+    id_to_slot, slot_to_id = st.staple_cache_build(counts, cap)
+    tables, cache_rows = [], []
+    for l in range(n_layers):
+        dtab = device_normal((v, f), w.table_std, w.layer_seeds(l)["table"], torch.bfloat16, dev)
+        htab = torch.empty((v, f), dtype=torch.bfloat16, pin_memory=True)
+        htab.copy_(dtab)
+        del dtab
+        tables.append(htab)
+        cache_rows.append(st.staple_cache_fill(htab, slot_to_id, cap))
+    torch.cuda.synchronize()
+    return {"id_to_slot": id_to_slot, "slot_to_id": slot_to_id, "tables": tables,
+            "cache_rows": cache_rows}
+
+
+def _miss_list_to_host(torch, lk, host_buf):
+    """Copies n_miss and the miss IDs to pinned host memory (one sync)."""
+    n = torch.empty(1, dtype=torch.int32, pin_memory=True)
+    n.copy_(lk["n_miss"], non_blocking=True)
+    host_buf[: lk["miss_ids"].numel()].copy_(lk["miss_ids"], non_blocking=True)
+    torch.cuda.current_stream().synchronize()
+    return int(n.item())
+
+
+def run_offload_decode(torch, st, w, steps, warmup):
+    from staple_synth import device_normal
+    dev = torch.device("cuda:0")
+    n, d, f, v, L = w.n_tokens, w.d_model, w.d_ff, w.vocab, w.n_layers
+    O = setup_offload(torch, st, w, L)
+    ids = torch.from_numpy(w.ids()).to(dev)
+    layers = []
+    for l in range(L):
+        s = w.layer_seeds(l)
+        layers.append({k: device_normal(shape, std, s[k], torch.bfloat16, dev) for k, shape, std in (
+            ("x", (n, d), w.x_std), ("w_gate", (f, d), w.w_std), ("w_up", (f, d), w.w_std),
+            ("w_down", (d, f), w.w_std))})
+        layers[-1]["y"] = torch.empty(n, d, dtype=torch.bfloat16, device=dev)
+    i32 = dict(dtype=torch.int32, device=dev)
+    dd_out = {"uniq": torch.empty(n, **i32), "inv": torch.empty(n, **i32),
+              "sorted_pos": torch.empty(n, **i32), "seg_start": torch.empty(n + 1, **i32),
+              "n_unique": torch.empty(1, **i32)}
+    lk_out = {k: torch.empty(n, **i32) for k in ("code", "miss_uidx", "miss_ids")}
+    lk_out["n_miss"] = torch.empty(1, **i32)
+    miss_host = torch.empty(n, dtype=torch.int32, pin_memory=True)
+    staging = [torch.empty(n, f, dtype=torch.bfloat16, pin_memory=True) for _ in range(L)]
+    dev_miss = [torch.empty(n, f, dtype=torch.bfloat16, device=dev) for _ in range(L)]
+    R = torch.empty(n, f, dtype=torch.bfloat16, device=dev)
+    h = torch.empty(n, f, dtype=torch.bfloat16, device=dev)
+    ws = torch.empty(max(st.lib().staple_ffn_down_workspace_bytes(n, d, f, 1), 256), dtype=torch.uint8,
+                     device=dev)
+    side = torch.cuda.Stream()
+    events = [torch.cuda.Event() for _ in range(L)]
+    main = torch.cuda.current_stream()
+
+    def step():
+        dd = st.staple_dedup(ids, v, out=dd_out)
+        lk = st.staple_cache_lookup(dd["uniq"], dd["n_unique"], O["id_to_slot"], out=lk_out)
+        m = _miss_list_to_host(torch, lk, miss_host)
+        for l, lay in enumerate(layers):
+            st.staple_stage_misses(O["tables"][l], miss_host, m, staging[l], dev_miss[l], stream=side)
+            events[l].record(side)
+            main.wait_event(events[l])
+            st.staple_assemble_rows(O["cache_rows"][l], dev_miss[l], lk["code"], dd["n_unique"], out=R)
+            st.staple_ffn_gate_up(lay["x"], lay["w_gate"], lay["w_up"], R, dd["inv"], h)
+            st.staple_ffn_down(h, lay["w_down"], lay["y"], workspace=ws)
+        return m
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    if st.staple_get_device_error() != 0:
+        raise RuntimeError("device error in offload decode")
+    misses = []
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        misses.append(step())
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) / steps * 1e3
+    n_unique = int(dd_out["n_unique"].item())
+    m = misses[-1]
+    return {"workload": w.name, "ms_per_step": ms, "tokens_per_s": n / (ms * 1e-3),
+            "n_unique": n_unique, "misses_per_layer": m, "cache_capacity": w.cache_capacity,
+            "token_hit_rate": None, "pcie_bytes_per_step": m * f * 2 * L,
+            "note": "eager step: dedup + cache probe once, one host sync for the miss list, "
+                    "per layer host pack + H2D on a side stream, cache/miss row assembly, "
+                    "gate/up, down"}
+
+
+def run_offload_train(torch, st, w, steps, warmup):
+    import numpy as np
+    from staple_synth import device_normal
+    dev = torch.device("cuda:0")
+    n, d, f, v = w.n_tokens, w.d_model, w.d_ff, w.vocab
+    O = setup_offload(torch, st, w, 1)
+    T = setup_train(torch, st, w)
+    i32 = dict(dtype=torch.int32, device=dev)
+    lk_out = {k: torch.empty(n, **i32) for k in ("code", "miss_uidx", "miss_ids")}
+    lk_out["n_miss"] = torch.empty(1, **i32)
+    miss_host = torch.empty(n, dtype=torch.int32, pin_memory=True)
+    staging = torch.empty(n, f, dtype=torch.bfloat16, pin_memory=True)
+    dev_miss = torch.empty(n, f, dtype=torch.bfloat16, device=dev)
+    side = torch.cuda.Stream()
+    main = torch.cuda.current_stream()
+    ev_copy0, ev_copy1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev_ready = torch.cuda.Event()
+    stats = {"pack_s": 0.0, "copy_ms": 0.0}
+
+    def step(measure=False):
+        dd = st.staple_dedup(T["ids"], v, out=T["dd"], workspace=T["dd_ws"])
+        lk = st.staple_cache_lookup(dd["uniq"], dd["n_unique"], O["id_to_slot"], out=lk_out)
+        m = _miss_list_to_host(torch, lk, miss_host)
+        side.wait_stream(main)
+        t0 = time.perf_counter()
+        with torch.cuda.stream(side):
+            ev_copy0.record(side)
+        st.staple_stage_misses(O["tables"][0], miss_host, m, staging, dev_miss, stream=side)
+        with torch.cuda.stream(side):
+            ev_copy1.record(side)
+        stats["pack_s"] += time.perf_counter() - t0
+        ev_ready.record(side)
+        main.wait_event(ev_ready)
+        st.staple_assemble_rows(O["cache_rows"][0], dev_miss, lk["code"], dd["n_unique"], out=T["rows"])
+        fw = T["fwd"]
+        st.staple_ffn_gate_up(T["x"], T["w_gate"], T["w_up"], T["rows"], dd["inv"], fw["h"], fw["g"], fw["u"])
+        st.staple_ffn_down(fw["h"], T["w_down"], fw["y"])
+        st.staple_ffn_bwd_table_grad(T["dy"], T["x"], T["w_gate"], T["w_up"], T["w_down"], fw["g"],
+                                     fw["u"], fw["h"], dd["sorted_pos"], dd["seg_start"],
+                                     dd["n_unique"], out=T["bwd"], workspace=T["bwd_ws"])
+        return m
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    if st.staple_get_device_error() != 0:
+        raise RuntimeError("device error in offload train")
+    stats["pack_s"] = 0.0
+    copy_ms = []
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        m = step()
+        ev_copy1.synchronize()
+        copy_ms.append(ev_copy0.elapsed_time(ev_copy1))
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) / steps * 1e3
+    copy = float(np.median(copy_ms))
+    return {"workload": w.name, "ms_per_step": ms, "tokens_per_s": n / (ms * 1e-3),
+            "n_unique": int(T["dd"]["n_unique"].item()), "miss_rows": m,
+            "cache_capacity": w.cache_capacity,
+            "host_pack_ms": stats["pack_s"] / steps * 1e3,
+            "h2d_ms": copy, "h2d_gb_s": m * f * 2 / (copy * 1e-3) / 1e9,
+            "note": "eager step: dedup + cache probe, one host sync for the miss list, host "
+                    "pack + H2D of the miss rows on a side stream (the main stream waits for "
+                    "it before assembling R: the copy is not yet hidden), forward, backward"}
+
 # ----------------------------------------------------------------------------
 def copy_probe(torch):
     """A plain device copy of 1 GiB, five times: the reference for scaling the
@@ -435,6 +602,25 @@ def main(argv=None) -> int:
             out["roofline"] = tr["roofline"]
             out["config"] = {"workload": wt.name}
         del T
+        torch.cuda.empty_cache()
+    if "decode7b" in wl:
+        w7 = S.OLMO7B_DECODE
+        dec7, D7 = run_decode(torch, st, w7, max(20, args.steps // 2), args.warmup)
+        out["decode_7b"] = dict(dec7, workload=w7.name)
+        del D7
+        torch.cuda.empty_cache()
+    if "train7b" in wl:
+        w7 = S.OLMO7B_TRAIN
+        tr7, T7 = run_train(torch, st, w7, args.train_steps, args.train_warmup)
+        out["train_7b"] = tr7
+        del T7
+        torch.cuda.empty_cache()
+    if "offload" in wl:
+        out["offload_decode"] = run_offload_decode(torch, st, S.OLMO1B_OFFLOAD, 20, 3)
+        torch.cuda.empty_cache()
+        out["offload_train"] = run_offload_train(torch, st, S.OLMO1B_OFFLOAD_TRAIN,
+                                                 args.train_steps, args.train_warmup)
+        torch.cuda.empty_cache()
     print(json.dumps(out), flush=True)
     return 0
 

@@ -182,13 +182,26 @@ OLMO1B_OFFLOAD = Workload(
           "count pass) cached in HBM; decode batch 64 and a 32768-token "
           "training batch")
 
-OLMO7B = Workload(
+OLMO7B_TRAIN = Workload(
     name="olmo2_7b_train_16k", d_model=4096, d_ff=11008, vocab=100352,
-    n_tokens=16384, n_layers=16, ids_seed=1004,
-    notes="7B-shaped layers; first 16 of 32 FFN layers augmented; training "
-          "batch 16384 on one layer and a decode batch of 64 over 16 layers")
+    n_tokens=16384, n_layers=1, ids_seed=1004,
+    notes="7B-shaped layer (the first 16 of 32 FFN layers are augmented): "
+          "training batch of 16384 tokens, forward and backward")
 
-WORKLOADS = {w.name: w for w in (TINY_F32, OLMO1B_DECODE, OLMO1B_TRAIN, OLMO1B_OFFLOAD, OLMO7B)}
+OLMO7B_DECODE = Workload(
+    name="olmo2_7b_decode_b64_16L", d_model=4096, d_ff=11008, vocab=100352,
+    n_tokens=64, n_layers=16, ids_seed=1005,
+    notes="7B-shaped decode step: 16 augmented layers, each with its own "
+          "100352x11008 bf16 table in HBM; forward only")
+
+OLMO1B_OFFLOAD_TRAIN = Workload(
+    name="olmo2_1b_offload_cache5_train_32k", d_model=2048, d_ff=8192, vocab=100352,
+    n_tokens=8 * 4096, n_layers=1, cache_fraction=0.05, ids_seed=1006,
+    notes="training batch of 32768 tokens through one layer whose table is in "
+          "pinned host memory with the top-5% rows cached in HBM")
+
+WORKLOADS = {w.name: w for w in (TINY_F32, OLMO1B_DECODE, OLMO1B_TRAIN, OLMO1B_OFFLOAD,
+                                 OLMO1B_OFFLOAD_TRAIN, OLMO7B_TRAIN, OLMO7B_DECODE)}
 
 
 @dataclass
