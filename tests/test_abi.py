@@ -50,7 +50,9 @@ def test_workspace_queries(lib):
     assert lib.staple_dedup_workspace_bytes(64) == 0
     assert lib.staple_dedup_workspace_bytes(32768) == 32768 * 8
     assert lib.staple_dedup_workspace_bytes(4097) == 8192 * 8
-    assert lib.staple_ffn_bwd_workspace_bytes(100, 64, 128, 1) == ((100 * 256 * 2 + 255) // 256) * 256
+    dgu = ((100 * 256 * 2 + 255) // 256) * 256          # [dg | du] in bf16
+    partials = 2 * ((100 + 31) // 32) * 128 * 4            # segment-sum chunk partials
+    assert lib.staple_ffn_bwd_workspace_bytes(100, 64, 128, 1) == dgu + partials
     assert lib.staple_ffn_fwd_workspace_bytes(100, 64, 100, 1) == 0   # d_ff not a multiple of 64
     assert lib.staple_cache_build_workspace_bytes(100352) == 131072 * 8
 

@@ -34,10 +34,11 @@ hipError_t launch_assemble_rows(const void* cache_rows, int64_t capacity, const 
                                 int64_t max_miss, const int32_t* code, const int32_t* n_unique,
                                 int64_t max_unique, int64_t row_bytes, void* rows, hipStream_t s,
                                 int* err);
+size_t segment_sum_workspace_bytes(int64_t n_tokens, int64_t d_ff);
 hipError_t launch_segment_sum(int dtype, const void* du, int64_t du_ld, int64_t du_col,
                               int64_t n_tokens, int64_t d_ff, const int32_t* sorted_pos,
                               const int32_t* seg_start, const int32_t* n_unique,
-                              int64_t max_unique, float* d_rows, hipStream_t s, int* err);
+                              int64_t max_unique, float* d_rows, void* ws, hipStream_t s, int* err);
 // kernels (gemm.hip)
 template <typename T>
 hipError_t gateup_fwd(int64_t n, int64_t d, int64_t f, const void* x, const void* wg,
@@ -372,9 +373,14 @@ staple_status_t staple_ffn_fwd(int64_t n, int64_t d, int64_t f, int32_t dtype, i
   return down_impl(n, d, f, dtype, out_dtype, h, w_down, y, down_ws, s);
 }
 
+// workspace of the backward: [dg | du] (n x 2f) then the segment-sum partials
+static size_t bwd_dgu_bytes(int64_t n, int64_t f, int32_t dtype) {
+  return align_up(static_cast<size_t>(n) * 2 * f * elem_bytes(dtype), 256);
+}
+
 size_t staple_ffn_bwd_workspace_bytes(int64_t n, int64_t d, int64_t f, int32_t dtype) {
   if (!ffn_shape_ok(n, d, f, dtype)) return 0;
-  return align_up(static_cast<size_t>(n) * 2 * f * elem_bytes(dtype), 256);
+  return bwd_dgu_bytes(n, f, dtype) + align_up(segment_sum_workspace_bytes(n, f), 256);
 }
 
 staple_status_t staple_ffn_bwd_table_grad(
@@ -399,12 +405,13 @@ staple_status_t staple_ffn_bwd_table_grad(
   GET_ERR(err);
   hipStream_t s = S(stream);
   void* dgu = ws;
+  void* seg_ws = n > 0 ? static_cast<char*>(ws) + bwd_dgu_bytes(n, f, dtype) : nullptr;
   const bool fz = freeze_up != 0;
   if (dtype == STAPLE_BF16) {
     HIPCALL(dh_act<bf16_t>(n, d, f, dy, w_down, saved_g, saved_u, dgu, s));
     if (n > 0)
       HIPCALL(launch_segment_sum(dtype, dgu, 2 * f, f, n, f, sorted_pos, seg_start, n_unique,
-                                 max_unique, d_rows, s, err));
+                                 max_unique, d_rows, seg_ws, s, err));
     HIPCALL(dwdown_bwd<bf16_t>(n, d, f, dy, saved_h, dw_down, s));
     HIPCALL(dwgu_bwd<bf16_t>(n, d, f, dgu, x, dw_gate, dw_up, fz, s));
     HIPCALL(dx_bwd<bf16_t>(n, d, f, dgu, w_gate, w_up, dx, out_dtype, s));
@@ -412,7 +419,7 @@ staple_status_t staple_ffn_bwd_table_grad(
     HIPCALL(dh_act<float>(n, d, f, dy, w_down, saved_g, saved_u, dgu, s));
     if (n > 0)
       HIPCALL(launch_segment_sum(dtype, dgu, 2 * f, f, n, f, sorted_pos, seg_start, n_unique,
-                                 max_unique, d_rows, s, err));
+                                 max_unique, d_rows, seg_ws, s, err));
     HIPCALL(dwdown_bwd<float>(n, d, f, dy, saved_h, dw_down, s));
     HIPCALL(dwgu_bwd<float>(n, d, f, dgu, x, dw_gate, dw_up, fz, s));
     HIPCALL(dx_bwd<float>(n, d, f, dgu, w_gate, w_up, dx, out_dtype, s));

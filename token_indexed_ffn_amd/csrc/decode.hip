@@ -295,6 +295,8 @@ __global__ __launch_bounds__(64 * WAVES) void decode_down_partial_kernel(
   }
 }
 
+
+
 template <typename OutT>
 __global__ void decode_down_reduce_kernel(int64_t count, int ksplit, const float* __restrict__ partial,
                                           OutT* __restrict__ y) {

@@ -73,6 +73,9 @@ struct GemmArgs {
 
 constexpr int kRowBytes = 128;  // bytes of k per LDS tile row and stage
 
+typedef __attribute__((address_space(3))) char lds_char;
+typedef __attribute__((address_space(3))) void lds_void;
+
 // LDS tile rows are 128 bytes (8 chunks of 16 bytes).  The chunk index is
 // XORed with bits 0-2 and 3-5 of the row, so that both the MFMA fragment reads
 // (consecutive rows, one chunk) and the transposed stores of MN-major tiles
@@ -88,27 +91,34 @@ __device__ __forceinline__ int swz(int row, int chunk) {
 // chunk (t & 7) of rows (t >> 3) + (NT / 8) i.
 template <int R, int NT>
 struct KMajorTile {
+  // Direct global -> LDS loads: the i-th 16-byte load instruction of wave w
+  // fills LDS rows [8 (i NW + w), 8 (i NW + w) + 8) of the tile (1 KB, lane l
+  // at byte 16 l), so lane l fetches row 8 (i NW + w) + l / 8 and, for the
+  // swizzled position (l % 8), the logical chunk (l % 8) ^ swizzle(row).
+  static constexpr int kNW = NT / 64;
   static constexpr int kPer = R * 8 / NT;
   const char* row_ptr[kPer];
-  uint4 reg[2][kPer];
+  int chunk_byte[kPer];
 
-  template <int S>
-  __device__ __forceinline__ void load(int64_t k_byte) {
-    const int c = threadIdx.x & 7;
-#pragma unroll
-    for (int i = 0; i < kPer; ++i)
-      reg[S][i] = *reinterpret_cast<const uint4*>(row_ptr[i] + k_byte + c * 16);
+  __device__ __forceinline__ static int row_of(int i) {
+    return 8 * (i * kNW + (threadIdx.x >> 6)) + ((threadIdx.x & 63) >> 3);
   }
-  template <int S>
-  __device__ __forceinline__ void store(char* lds) const {
-    const int c = threadIdx.x & 7;
+  __device__ __forceinline__ void init_chunks() {
 #pragma unroll
     for (int i = 0; i < kPer; ++i) {
-      const int r = (threadIdx.x >> 3) + (NT / 8) * i;
-      *reinterpret_cast<uint4*>(lds + swz(r, c)) = reg[S][i];
+      const int row = row_of(i);
+      const int phys = threadIdx.x & 7;
+      chunk_byte[i] = (phys ^ (row & 7) ^ ((row >> 3) & 7)) << 4;
     }
   }
-  __device__ __forceinline__ static int row_of(int i) { return (threadIdx.x >> 3) + (NT / 8) * i; }
+  // `lds` is the tile's LDS buffer (local address space).
+  __device__ __forceinline__ void load(int64_t k_byte, lds_char* lds) const {
+    const int w = threadIdx.x >> 6;
+#pragma unroll
+    for (int i = 0; i < kPer; ++i)
+      __builtin_amdgcn_global_load_lds(static_cast<const void*>(row_ptr[i] + k_byte + chunk_byte[i]),
+                                       static_cast<lds_void*>(lds + (i * kNW + w) * 1024), 16, 0, 0);
+  }
 };
 
 // MN-major operand tile: BK k-rows x R contiguous elements.  A unit is 4
@@ -323,8 +333,7 @@ __device__ __forceinline__ void store8g(void* base, int64_t idx, const float (&v
 // ---------------------------------------------------------------------------
 // The kernel: BM x BN tile, WGM x WGN waves, 2 LDS stages of 128 bytes of k.
 // ---------------------------------------------------------------------------
-template <typename T, int BM, int BN, int WGM, int WGN, int NSLOT, bool AK, bool BK, int EPI,
-          typename OutT>
+template <typename T, int BM, int BN, int WGM, int WGN, bool AK, bool BK, int EPI, typename OutT>
 __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(GemmArgs p) {
   constexpr int NT = 64 * WGM * WGN;
   constexpr int WM = BM / WGM, WN = BN / WGN;
@@ -334,6 +343,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(GemmArgs p) {
   static_assert((32 * (WN + 4) * 4) * WGM * WGN <= 2 * (BM + BN) * kRowBytes, "epilogue staging");
 
   extern __shared__ __attribute__((aligned(16))) char smem[];   // 2 stages x (BM + BN) rows
+  char* smem_lds = smem;
   char* As0 = smem;
   char* Bs0 = smem + BM * kRowBytes;
   constexpr int kStage = (BM + BN) * kRowBytes;
@@ -359,6 +369,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(GemmArgs p) {
       const int64_t row = p.a_rows ? static_cast<int64_t>(p.a_rows[m]) : m;
       at.row_ptr[i] = static_cast<const char*>(p.a0) + row * p.lda * sizeof(T);
     }
+    at.init_chunks();
   }
   if constexpr (BK) {
 #pragma unroll
@@ -375,6 +386,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(GemmArgs p) {
       }
       bt.row_ptr[i] = base;
     }
+    bt.init_chunks();
   }
   const int64_t a_cols = p.M - m0;  // valid m in this tile (MN-major A)
   const int64_t b_cols = p.N - n0;  // valid n in this tile (MN-major B)
@@ -390,6 +402,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(GemmArgs p) {
                                : static_cast<const T*>(p.b1) + (k - p.b_split) * p.ldb;
     return b + n0;
   };
+
   f32x16_t acc[TM][TN];
 #pragma unroll
   for (int i = 0; i < TM; ++i)
@@ -398,18 +411,20 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(GemmArgs p) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
-  auto load_tiles = [&](auto slot, int64_t kt) {
-    constexpr int S = decltype(slot)::value;
+  // K-major operands go straight from global memory into the LDS buffer of
+  // the next stage; MN-major operands pass through registers (for the
+  // transpose) and are written after the current stage's MFMAs.
+  lds_char* lds = (lds_char*)(smem_lds);   // address-space cast of the dynamic LDS block
+  auto issue_loads = [&](int64_t kt, int buf) {
     const int64_t k0 = kt * kBK;
-    if constexpr (AK) at.template load<S>(k0 * static_cast<int64_t>(sizeof(T)));
-    else at.template load<S>(k0, a_base, a_cols);
-    if constexpr (BK) bt.template load<S>(k0 * static_cast<int64_t>(sizeof(T)));
-    else bt.template load<S>(k0, b_base, b_cols);
+    if constexpr (AK) at.load(k0 * static_cast<int64_t>(sizeof(T)), lds + buf * kStage);
+    else at.template load<0>(k0, a_base, a_cols);
+    if constexpr (BK) bt.load(k0 * static_cast<int64_t>(sizeof(T)), lds + buf * kStage + BM * kRowBytes);
+    else bt.template load<0>(k0, b_base, b_cols);
   };
-  auto store_tiles = [&](auto slot, int buf) {
-    constexpr int S = decltype(slot)::value;
-    at.template store<S>(As0 + buf * kStage);
-    bt.template store<S>(Bs0 + buf * kStage);
+  auto store_regs = [&](int buf) {
+    if constexpr (!AK) at.template store<0>(As0 + buf * kStage);
+    if constexpr (!BK) bt.template store<0>(Bs0 + buf * kStage);
   };
   auto compute = [&](int buf) {
     const char* As = As0 + buf * kStage;
@@ -418,43 +433,19 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(GemmArgs p) {
     for (int kg = 0; kg < Mma<T, TM, TN>::kGroups; ++kg)
       Mma<T, TM, TN>::step(As, Bs, wm * WM, wn * WN, kg, acc);
   };
-  using S0 = std::integral_constant<int, 0>;
-  using S1 = std::integral_constant<int, 1>;
 
   const int64_t nk = (p.K + kBK - 1) / kBK;
-  if constexpr (NSLOT == 2) {
-    // Two register slots keep the global loads two stages ahead of the MFMAs:
-    // while stage kt is multiplied out of one LDS buffer, stage kt+1 waits in
-    // registers for the other buffer and stage kt+2 is in flight.  Loads past
-    // the last stage re-read it (clamped) so the loop has no conditional loads.
-    auto clampk = [&](int64_t k) { return k < nk ? k : nk - 1; };
-    load_tiles(S0{}, 0);
-    load_tiles(S1{}, clampk(1));
-    store_tiles(S0{}, 0);
+  issue_loads(0, 0);
+  store_regs(0);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  for (int64_t kt = 0; kt < nk; ++kt) {
+    const int cur = static_cast<int>(kt & 1);
+    if (kt + 1 < nk) issue_loads(kt + 1, cur ^ 1);
+    compute(cur);
+    if (kt + 1 < nk) store_regs(cur ^ 1);
+    __builtin_amdgcn_s_waitcnt(0);   // this thread's direct-to-LDS loads have landed
     __syncthreads();
-    for (int64_t kt = 0; kt < nk; kt += 2) {
-      load_tiles(S0{}, clampk(kt + 2));
-      compute(0);
-      store_tiles(S1{}, 1);
-      __syncthreads();
-      if (kt + 1 >= nk) break;
-      load_tiles(S1{}, clampk(kt + 3));
-      compute(1);
-      store_tiles(S0{}, 0);
-      __syncthreads();
-    }
-  } else {
-    // One register slot: stage kt+1 is loaded while stage kt is multiplied.
-    load_tiles(S0{}, 0);
-    store_tiles(S0{}, 0);
-    __syncthreads();
-    for (int64_t kt = 0; kt < nk; ++kt) {
-      const int cur = static_cast<int>(kt & 1);
-      if (kt + 1 < nk) load_tiles(S0{}, kt + 1);
-      compute(cur);
-      if (kt + 1 < nk) store_tiles(S0{}, cur ^ 1);
-      __syncthreads();
-    }
   }
 
   // ---- epilogue: per 32-row block, stage through this wave's LDS region ----
@@ -546,11 +537,10 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(GemmArgs p) {
 // ---------------------------------------------------------------------------
 // Host launchers
 // ---------------------------------------------------------------------------
-template <typename T, int BM, int BN, int WGM, int WGN, int NSLOT, bool AK, bool BK, int EPI,
-          typename OutT>
+template <typename T, int BM, int BN, int WGM, int WGN, bool AK, bool BK, int EPI, typename OutT>
 static hipError_t run_tile(const GemmArgs& a, hipStream_t s) {
   constexpr size_t kSmem = 2 * (BM + BN) * kRowBytes;
-  auto kern = &gemm_kernel<T, BM, BN, WGM, WGN, NSLOT, AK, BK, EPI, OutT>;
+  auto kern = &gemm_kernel<T, BM, BN, WGM, WGN, AK, BK, EPI, OutT>;
   static const hipError_t attr = hipFuncSetAttribute(
       reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
       static_cast<int>(kSmem));
@@ -560,22 +550,15 @@ static hipError_t run_tile(const GemmArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-// Shape of the large-problem tile: 0 = 256x256 on 8 waves (128x64 per wave),
-// one register slot; 1 = 256x256 on 4 waves (128x128 per wave), two slots.
-static int g_big_tile = 0;
-void gemm_set_big_tile(int v) { g_big_tile = v; }
-
 // 256x256 tiles for large bf16 problems, 128x128 tiles on 4 waves otherwise.
 template <typename T, bool AK, bool BK, int EPI, typename OutT>
 static hipError_t run(const GemmArgs& a, hipStream_t s) {
   if (a.M <= 0 || a.N <= 0) return hipSuccess;
   if constexpr (sizeof(T) == 2) {
-    if (a.M >= 256 && a.N >= 256 && ((a.M + 255) / 256) * ((a.N + 255) / 256) >= 128) {
-      if (g_big_tile == 0) return run_tile<T, 256, 256, 2, 4, 1, AK, BK, EPI, OutT>(a, s);
-      return run_tile<T, 256, 256, 2, 2, 2, AK, BK, EPI, OutT>(a, s);
-    }
+    if (a.M >= 256 && a.N >= 256 && ((a.M + 255) / 256) * ((a.N + 255) / 256) >= 128)
+      return run_tile<T, 256, 256, 2, 4, AK, BK, EPI, OutT>(a, s);
   }
-  return run_tile<T, 128, 128, 2, 2, 1, AK, BK, EPI, OutT>(a, s);
+  return run_tile<T, 128, 128, 2, 2, AK, BK, EPI, OutT>(a, s);
 }
 
 template <typename T>

@@ -187,14 +187,23 @@ hipError_t launch_assemble_rows(const void* cache_rows, int64_t capacity, const 
 }
 
 // ---------------------------------------------------------------------------
-// Table-row gradient: d_rows[u, c] = sum over p in segment u of
-// du[sorted_pos[p], c], accumulated in fp32 in ascending p order per wave and
-// then over the four waves in a fixed order (deterministic).
-// du lives at column offset `du_col` of rows with stride `du_ld` (elements).
-// Each workgroup covers one segment and kSegCols columns; each lane owns 8
-// consecutive columns (one 16-byte bf16 load, or two for fp32).
+// Table-row gradient: d_rows[u, c] = sum over sorted positions p of segment u
+// of du[sorted_pos[p], c], accumulated in fp32.
+//
+// Token frequencies are Zipf-skewed (one ID can hold ~13% of a batch), so the
+// work is split over fixed chunks of kSegChunk sorted positions rather than
+// over segments.  Pass 1: one wave per (chunk, 512 columns) walks its
+// positions in order; a segment that starts and ends inside the chunk is
+// written to d_rows directly; the run of a segment that began in an earlier
+// chunk goes to first[chunk], the run of a segment that continues into the
+// next chunk goes to last[chunk].  Pass 2: each segment spanning chunks
+// c0 < c1 sums last[c0] + first[c0+1] + ... + first[c1] in that order (done
+// by the wave of chunk c0).
+// Every sum has a fixed order, so the result is deterministic.
+// du lives at column offset du_col of rows with stride du_ld (elements);
+// each lane owns 8 consecutive columns (one 16-byte bf16 load, two for fp32).
 // ---------------------------------------------------------------------------
-constexpr int kSegThreads = 256;
+constexpr int kSegChunk = 32;
 constexpr int kSegCols = 512;   // 64 lanes x 8 columns
 
 template <typename T>
@@ -219,88 +228,119 @@ __device__ __forceinline__ void load8<float>(const float* p, float (&v)[8]) {
   v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
 }
 
+__device__ __forceinline__ void store8f(float* p, const float (&v)[8]) {
+  *reinterpret_cast<float4*>(p) = make_float4(v[0], v[1], v[2], v[3]);
+  *reinterpret_cast<float4*>(p + 4) = make_float4(v[4], v[5], v[6], v[7]);
+}
+
 template <typename T>
-__global__ __launch_bounds__(kSegThreads) void segment_sum_kernel(
+__global__ __launch_bounds__(64) void segsum_chunk_kernel(
     const T* __restrict__ du, int64_t du_ld, int64_t du_col, int64_t n_tokens, int64_t d_ff,
     const int32_t* __restrict__ sorted_pos, const int32_t* __restrict__ seg_start,
-    const int32_t* __restrict__ n_unique_p, float* __restrict__ d_rows, int* err) {
-  __shared__ float part[kSegThreads / 64][kSegCols];
-  const int64_t u = blockIdx.x;
-  if (u >= *n_unique_p) return;
-  const int lane = threadIdx.x & 63;
-  const int wid = threadIdx.x >> 6;
-  const int64_t c0 = static_cast<int64_t>(blockIdx.y) * kSegCols + lane * 8;
-  const bool active = c0 < d_ff;
-  int64_t p0 = seg_start[u];
-  int64_t p1 = seg_start[u + 1];
-  if (p0 < 0 || p1 > n_tokens || p0 > p1) {
-    if (threadIdx.x == 0) flag_index_error(err);
-    p0 = p1 = 0;
+    const int32_t* __restrict__ n_unique_p, float* __restrict__ d_rows, float* __restrict__ first,
+    float* __restrict__ last, int* err) {
+  const int lane = threadIdx.x;
+  const int64_t c = blockIdx.x;
+  const int64_t col = static_cast<int64_t>(blockIdx.y) * kSegCols + lane * 8;
+  const int64_t p0 = c * kSegChunk;
+  const int64_t p1 = min(p0 + kSegChunk, n_tokens);
+  const int64_t nu = *n_unique_p;
+  if (col >= d_ff || nu <= 0) return;
+  // segment holding p0: largest s with seg_start[s] <= p0
+  int64_t lo = 0, hi = nu - 1;
+  while (lo < hi) {
+    const int64_t mid = (lo + hi + 1) >> 1;
+    if (seg_start[mid] <= p0) lo = mid; else hi = mid - 1;
   }
+  int64_t sg = lo;
+  int64_t s_begin = seg_start[sg], s_end = seg_start[sg + 1];
   float acc[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) acc[i] = 0.0f;
-  if (active) {
-    constexpr int kUnroll = 4;
-    int64_t p = p0 + wid;
-    for (; p + 4 * (kUnroll - 1) < p1; p += 4 * kUnroll) {
-      float v[kUnroll][8];
-#pragma unroll
-      for (int k = 0; k < kUnroll; ++k) {
-        int64_t row = sorted_pos[p + 4 * k];
-        if (row < 0 || row >= n_tokens) {
-          flag_index_error(err);
-          row = 0;
-        }
-        load8<T>(du + row * du_ld + du_col + c0, v[k]);
-      }
-#pragma unroll
-      for (int k = 0; k < kUnroll; ++k)
-#pragma unroll
-        for (int i = 0; i < 8; ++i) acc[i] += v[k][i];
+  for (int64_t p = p0; p < p1; ++p) {
+    int64_t row = sorted_pos[p];
+    if (row < 0 || row >= n_tokens) {
+      flag_index_error(err);
+      row = 0;
     }
-    for (; p < p1; p += 4) {
-      float v[8];
-      int64_t row = sorted_pos[p];
-      if (row < 0 || row >= n_tokens) {
-        flag_index_error(err);
-        row = 0;
-      }
-      load8<T>(du + row * du_ld + du_col + c0, v);
+    float v[8];
+    load8<T>(du + row * du_ld + du_col + col, v);
 #pragma unroll
-      for (int i = 0; i < 8; ++i) acc[i] += v[i];
+    for (int i = 0; i < 8; ++i) acc[i] += v[i];
+    const bool seg_ends = (p + 1 == s_end);
+    if (seg_ends || p + 1 == p1) {
+      float* dst;
+      if (s_begin >= p0 && s_end <= p1) dst = d_rows + sg * d_ff + col;   // whole segment here
+      else if (s_begin < p0) dst = first + c * d_ff + col;                // began in an earlier chunk
+      else dst = last + c * d_ff + col;                                   // continues past p1
+      store8f(dst, acc);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc[i] = 0.0f;
+      if (seg_ends && sg + 1 < nu) {
+        ++sg;
+        s_begin = s_end;
+        s_end = seg_start[sg + 1];
+      }
     }
   }
-#pragma unroll
-  for (int i = 0; i < 8; ++i) part[wid][lane * 8 + i] = acc[i];
-  __syncthreads();
-  // each thread finalises 2 of the 512 columns
-  for (int c = threadIdx.x; c < kSegCols; c += kSegThreads) {
-    const int64_t col = static_cast<int64_t>(blockIdx.y) * kSegCols + c;
-    if (col < d_ff) {
-      float s = part[0][c];
-#pragma unroll
-      for (int w = 1; w < kSegThreads / 64; ++w) s += part[w][c];
-      d_rows[u * d_ff + col] = s;
-    }
+}
+
+// One wave per (chunk, 512 columns): the chunk whose last run starts a
+// segment that continues past it owns that segment's final sum.
+__global__ __launch_bounds__(64) void segsum_fixup_kernel(
+    int64_t n_tokens, int64_t d_ff, const int32_t* __restrict__ seg_start,
+    const int32_t* __restrict__ n_unique_p, const float* __restrict__ first,
+    const float* __restrict__ last, float* __restrict__ d_rows) {
+  const int64_t c0 = blockIdx.x;
+  const int64_t col = static_cast<int64_t>(blockIdx.y) * kSegCols + threadIdx.x * 8;
+  const int64_t nu = *n_unique_p;
+  if (col >= d_ff || nu <= 0) return;
+  const int64_t p0 = c0 * kSegChunk;
+  const int64_t p1 = min(p0 + kSegChunk, n_tokens);
+  // segment holding position p1 - 1
+  int64_t lo = 0, hi = nu - 1;
+  while (lo < hi) {
+    const int64_t mid = (lo + hi + 1) >> 1;
+    if (seg_start[mid] <= p1 - 1) lo = mid; else hi = mid - 1;
   }
+  const int64_t b = seg_start[lo], e = seg_start[lo + 1];
+  if (b < p0 || e <= p1) return;   // not a segment that starts here and continues
+  const int64_t c1 = (e - 1) / kSegChunk;
+  float acc[8];
+  load8<float>(last + c0 * d_ff + col, acc);
+  for (int64_t c = c0 + 1; c <= c1; ++c) {
+    float v[8];
+    load8<float>(first + c * d_ff + col, v);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[i] += v[i];
+  }
+  store8f(d_rows + lo * d_ff + col, acc);
+}
+
+size_t segment_sum_workspace_bytes(int64_t n_tokens, int64_t d_ff) {
+  const int64_t chunks = (n_tokens + kSegChunk - 1) / kSegChunk;
+  return static_cast<size_t>(2 * chunks * d_ff) * sizeof(float);
 }
 
 hipError_t launch_segment_sum(int dtype, const void* du, int64_t du_ld, int64_t du_col,
                               int64_t n_tokens, int64_t d_ff, const int32_t* sorted_pos,
                               const int32_t* seg_start, const int32_t* n_unique,
-                              int64_t max_unique, float* d_rows, hipStream_t s, int* err) {
-  if (max_unique == 0) return hipSuccess;
-  dim3 grid(static_cast<unsigned>(max_unique), static_cast<unsigned>((d_ff + kSegCols - 1) / kSegCols));
-  if (dtype == STAPLE_BF16) {
-    segment_sum_kernel<bf16_t><<<grid, dim3(kSegThreads), 0, s>>>(
+                              int64_t max_unique, float* d_rows, void* ws, hipStream_t s, int* err) {
+  if (max_unique == 0 || n_tokens == 0) return hipSuccess;
+  const int64_t chunks = (n_tokens + kSegChunk - 1) / kSegChunk;
+  float* first = static_cast<float*>(ws);
+  float* last = first + chunks * d_ff;
+  const unsigned cb = static_cast<unsigned>((d_ff + kSegCols - 1) / kSegCols);
+  if (dtype == STAPLE_BF16)
+    segsum_chunk_kernel<bf16_t><<<dim3(static_cast<unsigned>(chunks), cb), dim3(64), 0, s>>>(
         static_cast<const bf16_t*>(du), du_ld, du_col, n_tokens, d_ff, sorted_pos, seg_start,
-        n_unique, d_rows, err);
-  } else {
-    segment_sum_kernel<float><<<grid, dim3(kSegThreads), 0, s>>>(
+        n_unique, d_rows, first, last, err);
+  else
+    segsum_chunk_kernel<float><<<dim3(static_cast<unsigned>(chunks), cb), dim3(64), 0, s>>>(
         static_cast<const float*>(du), du_ld, du_col, n_tokens, d_ff, sorted_pos, seg_start,
-        n_unique, d_rows, err);
-  }
+        n_unique, d_rows, first, last, err);
+  segsum_fixup_kernel<<<dim3(static_cast<unsigned>(chunks), cb), dim3(64), 0, s>>>(
+      n_tokens, d_ff, seg_start, n_unique, first, last, d_rows);
   return hipGetLastError();
 }
 
