@@ -15,6 +15,11 @@ typedef __attribute__((ext_vector_type(4))) float f32x4_t;
 typedef __attribute__((ext_vector_type(4))) uint32_t u32x4_t;
 typedef __attribute__((ext_vector_type(2))) uint32_t u32x2_t;
 
+// Pointers into LDS (local address space), e.g. for loads straight from
+// global memory into LDS.
+typedef __attribute__((address_space(3))) char lds_char;
+typedef __attribute__((address_space(3))) void lds_void;
+
 // bfloat16 storage type (raw bits).
 struct bf16_t {
   uint16_t bits;

@@ -3,14 +3,17 @@
 //
 // Both kernels put the weight matrix on the MFMA's A side (16-row blocks of
 // v_mfma_f32_16x16x32_bf16) and the tokens on the B side (four 16-token
-// tiles).  A 64-wide "macro step" of k is 128 bytes of every row; lane
-// (r, q) = (lane % 16, lane / 16) loads its bytes [16q, 16q+16) and
-// [64+16q, 64+16q+16), so each load instruction reads 64 contiguous bytes of
-// 16 rows, and the j-th MFMA of the step takes the j-th load of every lane.
-// A and B use the same k order, so the contraction is unchanged.  Two steps
-// of loads are kept in flight per wave.
+// tiles).  A 64-wide "macro step" of k is 128 bytes of every row; for the
+// weights, lane (r, q) = (lane % 16, lane / 16) loads its bytes [16q, 16q+16)
+// and [64+16q, 64+16q+16) straight into registers, so each load instruction
+// reads 64 contiguous bytes of 16 rows, and the j-th MFMA of the step takes
+// the j-th load of every lane.  The activation, which every workgroup reads,
+// is loaded as whole cache lines and put into the same fragment pattern
+// through LDS (half the cache-line requests of the fragment pattern).  A and
+// B use the same k order, so the contraction is unchanged.  Two steps of
+// loads are kept in flight per wave.
 //
-// Gate/up: one workgroup per 32 features; its eight waves split d_model and
+// Gate/up: one workgroup per 32 features; its four waves split d_model and
 // their partial sums meet in LDS, after which the epilogue gathers each
 // token's table row, forms u = W_up x + E[t] and h = silu(W_gate x) * u
 // (STAPLE abstract: the up-projection is retained and the embedding added as
@@ -20,7 +23,7 @@
 // Down: d_model is too narrow to fill 256 CUs with whole-K tiles, so the K
 // range (d_ff) is split over several workgroups per output block (8 per 64
 // outputs by default); each writes an fp32 partial and a second small kernel
-// sums the partials in a fixed order (deterministic) and stores y.
+// sums the partials in split order (deterministic) and stores y.
 #include "common.h"
 
 namespace staple {
@@ -59,52 +62,6 @@ __device__ __forceinline__ void mma_step(const Frag2 (&a)[NA], const Frag2 (&b)[
             as_bf16x8(a[i].v[j]), as_bf16x8(b[k].v[j]), acc[i * NB + k], 0, 0, 0);
 }
 
-// Streams macro steps [s0, s1) of NA weight row-blocks (16 rows each) and NB
-// token tiles (16 tokens each) through NS register slots: the loads of NS
-// steps are in flight while one step's MFMAs run.  The loop body has no
-// branch: refills past s1 re-read the last step (in cache) and the weight
-// fragments of steps past s1 are zeroed with a mask, so every path keeps the
-// same loads in flight and each MFMA group waits only for its own (oldest)
-// slot.  With PIPE, scheduling barriers keep each refill where it is written;
-// otherwise the compiler sinks the loads next to their use.
-template <int NA, int NB, bool PIPE, int NS = 2>
-__device__ __forceinline__ void stream_k(const char* const (&pa)[NA], const char* const (&pb)[NB],
-                                         int64_t s0, int64_t s1, f32x4_t (&acc)[NA * NB]) {
-  const int64_t ngroups = (s1 - s0 + NS - 1) / NS;
-  if (ngroups <= 0) return;
-  auto off = [&](int64_t s) -> int64_t { return (s < s1 ? s : s1 - 1) * 128; };
-  Frag2 a[NS][NA], b[NS][NB];
-#pragma unroll
-  for (int j = 0; j < NS; ++j) {
-#pragma unroll
-    for (int i = 0; i < NA; ++i) load_step(a[j][i], pa[i], off(s0 + j));
-#pragma unroll
-    for (int k = 0; k < NB; ++k) load_step(b[j][k], pb[k], off(s0 + j));
-  }
-  for (int64_t it = 0; it < ngroups; ++it) {
-#pragma unroll
-    for (int j = 0; j < NS; ++j) {
-      const int64_t s = s0 + it * NS + j;
-      if constexpr (PIPE) __builtin_amdgcn_sched_barrier(0);
-      const uint32_t keep = (s < s1) ? 0xffffffffu : 0u;
-#pragma unroll
-      for (int i = 0; i < NA; ++i)
-#pragma unroll
-        for (int jj = 0; jj < 2; ++jj) {
-          a[j][i].v[jj].x &= keep; a[j][i].v[jj].y &= keep;
-          a[j][i].v[jj].z &= keep; a[j][i].v[jj].w &= keep;
-        }
-      mma_step<NA, NB>(a[j], b[j], acc);
-      if constexpr (PIPE) __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int i = 0; i < NA; ++i) load_step(a[j][i], pa[i], off(s + NS));
-#pragma unroll
-      for (int k = 0; k < NB; ++k) load_step(b[j][k], pb[k], off(s + NS));
-    }
-  }
-  if constexpr (PIPE) __builtin_amdgcn_sched_barrier(0);
-}
-
 // Position in the LDS partials of output (row-block a, token tile b, row
 // rr in 0..15, token column cc in 0..15) for `wave`, with NT = NA * NB tiles.
 template <int NT>
@@ -132,62 +89,159 @@ __device__ __forceinline__ void add_partials(const float* part, int slot, f32x4_
     for (int i = 0; i < 4; ++i) acc[t][i] += part[((slot * NT + t) * 4 + i) * 64 + lane];
 }
 
-template <int WAVES, bool PIPE, int NS>
-__global__ __launch_bounds__(64 * WAVES) void decode_gateup_kernel(
+typedef __attribute__((address_space(3))) u32x4_t lds_u32x4;
+
+// The activation block of one macro step in LDS: 64 tokens x 128 bytes, token
+// t's 16-byte chunk c at t * 128 + ((c ^ ((t >> 1) & 7)) << 4).  It is loaded
+// from global memory with eight 1 KB instructions that each cover 8 whole
+// tokens x 128 bytes (full cache lines, lane l: token 8i + l / 8, chunk
+// l % 8), written to the wave's LDS block and read back in the Frag2 pattern;
+// the XOR keeps every 16-lane group of both the writes and the reads on
+// distinct banks.
+constexpr int kXBlock = 64 * 128;
+
+__device__ __forceinline__ int xblock_at(int t, int c) { return t * 128 + ((c ^ ((t >> 1) & 7)) << 4); }
+
+// Streams macro steps [s0, s1) of NA weight row-blocks (16 rows each, pa[i]
+// the lane's bytes at step 0) and the activation of NB token tiles through NS
+// register slots: the loads of NS steps are in flight while one step's MFMAs
+// run.  The activation is loaded as full cache lines (px[i]: the 16 bytes of
+// the lane's i-th load at step 0) and rearranged into MFMA fragments through
+// the wave's own LDS block (kXBlock bytes at `xlds`).  Scheduling barriers
+// keep each refill where it is written (otherwise the compiler sinks the
+// loads next to their use); steps past s1 in the last group read the last
+// step again and their weights are masked to zero, and the last group issues
+// no refills.  `after_prologue` runs once the first NS steps are in flight.
+template <int NA, int NB, int NS, typename Hook>
+__device__ __forceinline__ void stream_k_xline(const char* const (&pa)[NA], const char* const (&px)[8],
+                                               lds_char* xlds, int64_t s0, int64_t s1,
+                                               f32x4_t (&acc)[NA * NB], Hook&& after_prologue) {
+  const int lane = threadIdx.x & 63;
+  const int r = lane & 15, q = lane >> 4;
+  const int64_t ngroups = (s1 - s0 + NS - 1) / NS;
+  if (ngroups <= 0) {
+    after_prologue();
+    return;
+  }
+  auto off = [&](int64_t s) -> int64_t { return (s < s1 ? s : s1 - 1) * 128; };
+  Frag2 a[NS][NA];
+  uint4 xv[NS][8];
+  int wofs[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) wofs[i] = xblock_at(8 * i + (lane >> 3), lane & 7);
+  auto issue = [&](int j, int64_t s) {
+#pragma unroll
+    for (int i = 0; i < NA; ++i) load_step(a[j][i], pa[i], off(s));
+#pragma unroll
+    for (int i = 0; i < 8; ++i) xv[j][i] = *reinterpret_cast<const uint4*>(px[i] + off(s));
+  };
+  auto consume = [&](int j, int64_t s) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      *reinterpret_cast<lds_u32x4*>(xlds + wofs[i]) = __builtin_bit_cast(u32x4_t, xv[j][i]);
+    Frag2 b[NB];
+#pragma unroll
+    for (int k = 0; k < NB; ++k) {
+      const int t = 16 * k + r;
+      b[k].v[0] = __builtin_bit_cast(uint4, *reinterpret_cast<const lds_u32x4*>(xlds + xblock_at(t, q)));
+      b[k].v[1] = __builtin_bit_cast(uint4, *reinterpret_cast<const lds_u32x4*>(xlds + xblock_at(t, q + 4)));
+    }
+    const uint32_t keep = (s < s1) ? 0xffffffffu : 0u;
+#pragma unroll
+    for (int i = 0; i < NA; ++i)
+#pragma unroll
+      for (int jj = 0; jj < 2; ++jj) {
+        a[j][i].v[jj].x &= keep; a[j][i].v[jj].y &= keep;
+        a[j][i].v[jj].z &= keep; a[j][i].v[jj].w &= keep;
+      }
+    mma_step<NA, NB>(a[j], b, acc);
+  };
+#pragma unroll
+  for (int j = 0; j < NS; ++j) issue(j, s0 + j);
+  after_prologue();
+  for (int64_t it = 0; it + 1 < ngroups; ++it) {
+#pragma unroll
+    for (int j = 0; j < NS; ++j) {
+      const int64_t s = s0 + it * NS + j;
+      __builtin_amdgcn_sched_barrier(0);
+      consume(j, s);
+      __builtin_amdgcn_sched_barrier(0);
+      issue(j, s + NS);
+    }
+  }
+  // last group: nothing more to load
+  const int64_t sl = s0 + (ngroups - 1) * NS;
+#pragma unroll
+  for (int j = 0; j < NS; ++j) {
+    __builtin_amdgcn_sched_barrier(0);
+    consume(j, sl + j);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+// Gate/up for at most 64 tokens: one workgroup (4 waves) per 32 features,
+// the waves split d_model, and the wave partial sums are folded in LDS after
+// the stream; the epilogue gathers each token's table row, forms
+// u = W_up x + E[t] and h = silu(W_gate x) * u and stores h (and g, u when
+// asked) with 16-byte vectors.
+template <int NS>
+__global__ __launch_bounds__(256) void decode_gateup_kernel(
     int n, int64_t d, int64_t f, const uint16_t* __restrict__ x, const uint16_t* __restrict__ wg,
     const uint16_t* __restrict__ wu, const uint16_t* __restrict__ rows, int64_t n_rows,
     const int32_t* __restrict__ row_index, uint16_t* __restrict__ h, uint16_t* __restrict__ g_out,
     uint16_t* __restrict__ u_out, int* err) {
-  constexpr int NA = 4, NB = 4, NT = NA * NB;   // A: gate rows 0-15, 16-31, up rows 0-15, 16-31
-  __shared__ float part[4 * NT * 4 * 64];       // 4 slots, 64 KB
+  constexpr int WAVES = 4, NA = 4, NB = 4, NT = NA * NB;
+  constexpr int kRing = NT * 4 * 64 * 4;            // bytes of LDS per wave (partials)
+  static_assert(kRing >= kXBlock, "activation block fits");
+  __shared__ __attribute__((aligned(16))) char smem[WAVES * kRing];
+  lds_char* lds = (lds_char*)(smem);
   const int lane = threadIdx.x & 63;
   const int wid = threadIdx.x >> 6;
   const int r = lane & 15, q = lane >> 4;
   const int64_t f0 = static_cast<int64_t>(blockIdx.x) * 32;
   const int64_t T = d / 64;
-  // workgroups on one XCD run side by side; rotating which K slice each wave
-  // takes spreads their simultaneous reads of x over different L2 lines
   const int slice = (wid + static_cast<int>(blockIdx.x >> 3)) % WAVES;
   const int64_t s0 = T * slice / WAVES, s1 = T * (slice + 1) / WAVES;
   const char* pa[NA] = {reinterpret_cast<const char*>(wg + (f0 + r) * d) + q * 16,
                         reinterpret_cast<const char*>(wg + (f0 + 16 + r) * d) + q * 16,
                         reinterpret_cast<const char*>(wu + (f0 + r) * d) + q * 16,
                         reinterpret_cast<const char*>(wu + (f0 + 16 + r) * d) + q * 16};
-  const char* pb[NB];
+  const char* px[8];
 #pragma unroll
-  for (int k = 0; k < NB; ++k)
-    pb[k] = reinterpret_cast<const char*>(x + static_cast<int64_t>(min(16 * k + r, n - 1)) * d) + q * 16;
+  for (int i = 0; i < 8; ++i) {
+    const int t = min(8 * i + (lane >> 3), n - 1);
+    px[i] = reinterpret_cast<const char*>(x + static_cast<int64_t>(t) * d) + (lane & 7) * 16;
+  }
 
-  // the epilogue's table row is fetched first, so its latency hides under the stream
+  // epilogue thread -> (token et, 8 consecutive features); its table row is
+  // fetched (branch-free, from a valid address) once the first steps are in
+  // flight
   const int et = threadIdx.x >> 2;
   const int efq = (threadIdx.x & 3) * 8;
-  uint4 erow = make_uint4(0, 0, 0, 0);
-  bool erow_ok = true;
-  if (threadIdx.x < 256 && et < n) {
-    const int64_t ri = row_index[et];
-    erow_ok = ri >= 0 && ri < n_rows;
-    if (erow_ok) erow = *reinterpret_cast<const uint4*>(rows + ri * f + f0 + efq);
-  }
+  bool erow_ok;
+  uint4 erow;
 
   f32x4_t acc[NT];
 #pragma unroll
   for (int t = 0; t < NT; ++t)
 #pragma unroll
     for (int i = 0; i < 4; ++i) acc[t][i] = 0.0f;
-  stream_k<NA, NB, PIPE, NS>(pa, pb, s0, s1, acc);
+  stream_k_xline<NA, NB, NS>(pa, px, lds + wid * kRing, s0, s1, acc, [&]() {
+    const int64_t ri = row_index[min(et, n - 1)];
+    erow_ok = ri >= 0 && ri < n_rows;
+    const uint16_t* esrc = erow_ok ? rows + ri * f + f0 + efq : x;
+    erow = *reinterpret_cast<const uint4*>(esrc);
+  });
 
-  if constexpr (WAVES == 8) {
-    // fold waves 4..7 into waves 0..3, then waves 0..3 publish their sums
-    if (wid >= 4) store_partials<NT>(part, wid - 4, acc);
-    __syncthreads();
-    if (wid < 4) add_partials<NT>(part, wid, acc);
-    __syncthreads();
-  }
-  if (wid < 4) store_partials<NT>(part, wid, acc);
+  // each wave parks its sums in its own LDS block
+  float* part = reinterpret_cast<float*>(smem);
+  constexpr int kRingF = kRing / 4;
+#pragma unroll
+  for (int t = 0; t < NT; ++t)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) part[wid * kRingF + (t * 4 + i) * 64 + lane] = acc[t][i];
   __syncthreads();
 
-  // epilogue: thread -> (token t, 8 consecutive features)
-  if (threadIdx.x >= 256) return;
   const int t = et;
   const int fq = efq;
   if (t >= n) return;
@@ -197,11 +251,13 @@ __global__ __launch_bounds__(64 * WAVES) void decode_gateup_kernel(
     const int fr = fq + e;
     const int tile_g = (fr >> 4) * NB + (t >> 4);
     const int tile_u = (2 + (fr >> 4)) * NB + (t >> 4);
+    const int rr = fr & 15, cc = t & 15;
+    const int at = cc + 16 * (rr >> 2), reg = rr & 3;
     float g = 0.0f, a = 0.0f;
 #pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      g += part[part_at<NT>(w, tile_g, fr & 15, t & 15)];
-      a += part[part_at<NT>(w, tile_u, fr & 15, t & 15)];
+    for (int w = 0; w < WAVES; ++w) {
+      g += part[w * kRingF + (tile_g * 4 + reg) * 64 + at];
+      a += part[w * kRingF + (tile_u * 4 + reg) * 64 + at];
     }
     gv[e] = g;
     av[e] = a;
@@ -241,13 +297,17 @@ __global__ __launch_bounds__(64 * WAVES) void decode_gateup_kernel(
 }
 
 // Partial y over one K split: partial[ks][t][n0 + c] (fp32) for the 16*NA
-// outputs n0.. of this workgroup and split ks of KS.
+// outputs n0.. of this workgroup and split ks of KS.  (Summing the splits in
+// the last workgroup to finish, behind an arrival counter, measured slower on
+// MI355X than the separate reduction kernel: publishing the partials across
+// XCDs costs an L2 writeback or uncached accesses per workgroup.)
 template <int WAVES, int NS, int NA, int KS>
 __global__ __launch_bounds__(64 * WAVES) void decode_down_partial_kernel(
     int n, int64_t d, int64_t f, const uint16_t* __restrict__ h, const uint16_t* __restrict__ wd,
     float* __restrict__ partial) {
   constexpr int NB = 4, NT = NA * NB, F = 16 * NA, FPT = F / 4;
-  __shared__ float part[WAVES * NT * 4 * 64];
+  static_assert(NT * 4 * 64 * 4 >= kXBlock, "activation block fits in the wave's partials");
+  __shared__ __attribute__((aligned(16))) float part[WAVES * NT * 4 * 64];
   const int lane = threadIdx.x & 63;
   const int wid = threadIdx.x >> 6;
   const int r = lane & 15, q = lane >> 4;
@@ -260,42 +320,43 @@ __global__ __launch_bounds__(64 * WAVES) void decode_down_partial_kernel(
 #pragma unroll
   for (int i = 0; i < NA; ++i)
     pa[i] = reinterpret_cast<const char*>(wd + (n0 + 16 * i + r) * f) + q * 16;
-  const char* pb[NB];
+  const char* px[8];
 #pragma unroll
-  for (int k = 0; k < NB; ++k)
-    pb[k] = reinterpret_cast<const char*>(h + static_cast<int64_t>(min(16 * k + r, n - 1)) * f) + q * 16;
+  for (int i = 0; i < 8; ++i) {
+    const int t = min(8 * i + (lane >> 3), n - 1);
+    px[i] = reinterpret_cast<const char*>(h + static_cast<int64_t>(t) * f) + (lane & 7) * 16;
+  }
 
   f32x4_t acc[NT];
 #pragma unroll
   for (int t = 0; t < NT; ++t)
 #pragma unroll
     for (int i = 0; i < 4; ++i) acc[t][i] = 0.0f;
-  stream_k<NA, NB, true, NS>(pa, pb, s0, s1, acc);
+  lds_char* xlds = (lds_char*)(reinterpret_cast<char*>(part) + wid * NT * 4 * 64 * 4);
+  stream_k_xline<NA, NB, NS>(pa, px, xlds, s0, s1, acc, []() {});
 
   store_partials<NT>(part, wid, acc);
   __syncthreads();
-  if (threadIdx.x >= 256) return;
   const int t = threadIdx.x >> 2;
   const int fq = (threadIdx.x & 3) * FPT;
-  if (t >= n) return;
-  float* dst = partial + (static_cast<int64_t>(ks) * n + t) * d + n0 + fq;
+  if (threadIdx.x < 256 && t < n) {
+    float* dst = partial + (static_cast<int64_t>(ks) * n + t) * d + n0 + fq;
 #pragma unroll
-  for (int e0 = 0; e0 < FPT; e0 += 4) {
-    float out[4];
+    for (int e0 = 0; e0 < FPT; e0 += 4) {
+      float out[4];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int fr = fq + e0 + e;
-      const int tile = (fr >> 4) * NB + (t >> 4);
-      float sum = 0.0f;
+      for (int e = 0; e < 4; ++e) {
+        const int fr = fq + e0 + e;
+        const int tile = (fr >> 4) * NB + (t >> 4);
+        float sum = 0.0f;
 #pragma unroll
-      for (int w = 0; w < WAVES; ++w) sum += part[part_at<NT>(w, tile, fr & 15, t & 15)];
-      out[e] = sum;
+        for (int w = 0; w < WAVES; ++w) sum += part[part_at<NT>(w, tile, fr & 15, t & 15)];
+        out[e] = sum;
+      }
+      *reinterpret_cast<float4*>(dst + e0) = make_float4(out[0], out[1], out[2], out[3]);
     }
-    *reinterpret_cast<float4*>(dst + e0) = make_float4(out[0], out[1], out[2], out[3]);
   }
 }
-
-
 
 template <typename OutT>
 __global__ void decode_down_reduce_kernel(int64_t count, int ksplit, const float* __restrict__ partial,
@@ -326,10 +387,9 @@ size_t decode_down_workspace_bytes(int64_t n, int64_t d) {
   return static_cast<size_t>(kDownSplitMax) * n * d * sizeof(float);
 }
 
-// Launch shapes (waves per workgroup, explicit two-step load pipeline) of the
-// two decode kernels.
+// Launch shapes of the two decode kernels.
 struct DecodeConfig {
-  int gu_slots;   // register slots of the gate/up kernel (2..4), 4 waves, explicit pipeline
+  int gu_slots;   // steps in flight per wave in the gate/up kernel (2 or 3)
   int dn_shape;   // down kernel shape: 1 (32 outputs, 4 splits), 2 (64, 8), 3 (64, 4), 4 (128, 8)
 };
 // Measured best on MI355X for d_model 2048 / d_ff 8192, batch 64.
@@ -337,32 +397,26 @@ static DecodeConfig g_decode_cfg = {2, 2};
 
 void decode_set_config(int gu_slots, int dn_shape) { g_decode_cfg = {gu_slots, dn_shape}; }
 
-template <int W, bool P, int NS>
-static void launch_gu(int64_t n, int64_t d, int64_t f, const void* x, const void* wg,
-                      const void* wu, const void* rows, int64_t n_rows, const int32_t* row_index,
-                      void* h, void* g_out, void* u_out, hipStream_t s, int* err) {
-  decode_gateup_kernel<W, P, NS><<<dim3(static_cast<unsigned>(f / 32)), dim3(64 * W), 0, s>>>(
-      static_cast<int>(n), d, f, static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(wg),
-      static_cast<const uint16_t*>(wu), static_cast<const uint16_t*>(rows), n_rows, row_index,
-      static_cast<uint16_t*>(h), static_cast<uint16_t*>(g_out), static_cast<uint16_t*>(u_out), err);
-}
-
 hipError_t decode_gateup(int64_t n, int64_t d, int64_t f, const void* x, const void* wg,
                          const void* wu, const void* rows, int64_t n_rows,
                          const int32_t* row_index, void* h, void* g_out, void* u_out,
                          hipStream_t s, int* err) {
-  const int ns = g_decode_cfg.gu_slots;
-  if (ns == 4) launch_gu<4, true, 4>(n, d, f, x, wg, wu, rows, n_rows, row_index, h, g_out, u_out, s, err);
-  else if (ns == 3) launch_gu<4, true, 3>(n, d, f, x, wg, wu, rows, n_rows, row_index, h, g_out, u_out, s, err);
-  else launch_gu<4, true, 2>(n, d, f, x, wg, wu, rows, n_rows, row_index, h, g_out, u_out, s, err);
+  auto go = [&](auto kern) {
+    kern<<<dim3(static_cast<unsigned>(f / 32)), dim3(256), 0, s>>>(
+        static_cast<int>(n), d, f, static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(wg),
+        static_cast<const uint16_t*>(wu), static_cast<const uint16_t*>(rows), n_rows, row_index,
+        static_cast<uint16_t*>(h), static_cast<uint16_t*>(g_out), static_cast<uint16_t*>(u_out), err);
+  };
+  if (g_decode_cfg.gu_slots >= 3) go(decode_gateup_kernel<3>);
+  else go(decode_gateup_kernel<2>);
   return hipGetLastError();
 }
 
-template <int NS, int NA, int KS>
+template <int NA, int KS>
 static void launch_dn(int64_t n, int64_t d, int64_t f, const void* h, const void* wd, float* partial,
                       hipStream_t s) {
-  decode_down_partial_kernel<4, NS, NA, KS><<<dim3(static_cast<unsigned>(d / (16 * NA)), KS),
-                                              dim3(256), 0, s>>>(
+  decode_down_partial_kernel<4, 2, NA, KS><<<dim3(static_cast<unsigned>(d / (16 * NA)), KS),
+                                             dim3(256), 0, s>>>(
       static_cast<int>(n), d, f, static_cast<const uint16_t*>(h), static_cast<const uint16_t*>(wd),
       partial);
 }
@@ -370,12 +424,12 @@ static void launch_dn(int64_t n, int64_t d, int64_t f, const void* h, const void
 hipError_t decode_down(int64_t n, int64_t d, int64_t f, const void* h, const void* wd, void* y,
                        int out_dtype, void* ws, hipStream_t s) {
   float* partial = static_cast<float*>(ws);
-  int ks = 4;
+  int ks = 8;
   switch (g_decode_cfg.dn_shape) {
-    case 1: launch_dn<2, 2, 4>(n, d, f, h, wd, partial, s); ks = 4; break;
-    case 2: launch_dn<2, 4, 8>(n, d, f, h, wd, partial, s); ks = 8; break;
-    case 3: launch_dn<2, 4, 4>(n, d, f, h, wd, partial, s); ks = 4; break;
-    default: launch_dn<2, 8, 8>(n, d, f, h, wd, partial, s); ks = 8; break;
+    case 1: launch_dn<2, 4>(n, d, f, h, wd, partial, s); ks = 4; break;
+    case 3: launch_dn<4, 4>(n, d, f, h, wd, partial, s); ks = 4; break;
+    case 4: launch_dn<8, 8>(n, d, f, h, wd, partial, s); ks = 8; break;
+    default: launch_dn<4, 8>(n, d, f, h, wd, partial, s); ks = 8; break;
   }
   const int64_t count = n * d;
   const unsigned blocks = static_cast<unsigned>((count / 4 + 255) / 256);

@@ -73,9 +73,6 @@ struct GemmArgs {
 
 constexpr int kRowBytes = 128;  // bytes of k per LDS tile row and stage
 
-typedef __attribute__((address_space(3))) char lds_char;
-typedef __attribute__((address_space(3))) void lds_void;
-
 // LDS tile rows are 128 bytes (8 chunks of 16 bytes).  The chunk index is
 // XORed with bits 0-2 and 3-5 of the row, so that both the MFMA fragment reads
 // (consecutive rows, one chunk) and the transposed stores of MN-major tiles
@@ -190,29 +187,120 @@ struct MNMajorTile {
   }
 };
 
+// bf16 MN-major operand tile loaded straight into LDS without a transpose:
+// LDS keeps the operand's own layout, [64 k-rows][R elements], in 32-byte
+// chunks whose index is XORed with swz_mn(k); the MFMA fragments are then read
+// with the transposing LDS load (ds_read_b64_tr_b16).  The i-th load
+// instruction of wave w fills 1 KB = 1024 / (2 R) k-rows; lane l covers 16
+// bytes of it.  k-rows past K read a zero page so they add nothing.
+__device__ const uint4 g_gemm_zero_page[1] = {};
+
+__device__ __forceinline__ int swz_mn(int k) { return ((k & 3) << 1) | ((k >> 3) & 1); }
+
+template <int R, int NT>
+struct MNDirectTile {
+  static constexpr int kNW = NT / 64;
+  static constexpr int kRB = R * 2;                 // bytes per k-row
+  static constexpr int kRowsPerInst = 1024 / kRB;   // k-rows per 1 KB instruction
+  static constexpr int kPer = 64 / kRowsPerInst / kNW;
+  static_assert(kPer * kRowsPerInst * kNW == 64, "tile shape");
+  int krow[kPer];        // k-row (0..63) this lane fills with instruction i
+  int elem[kPer];        // element offset along the row (logical, 8 elements)
+
+  __device__ __forceinline__ void init() {
+    const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      const int byte = (i * kNW + w) * 1024 + l * 16;   // LDS byte in the tile
+      const int k = byte / kRB;
+      const int in_row = byte % kRB;
+      const int phys32 = in_row >> 5, half = (in_row >> 4) & 1;
+      const int c32 = phys32 ^ swz_mn(k);
+      krow[i] = k;
+      elem[i] = c32 * 16 + half * 8;
+    }
+  }
+  // base(k) returns the element pointer of global k-row k offset to the tile's
+  // first column, or nullptr past the end of K; `cols` is the number of valid
+  // columns in the tile (a multiple of 8, so a 16-byte piece is all in or out).
+  template <typename BaseFn>
+  __device__ __forceinline__ void load(int64_t k0, BaseFn base, int64_t cols, lds_char* lds) const {
+    const int w = threadIdx.x >> 6;
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      const uint16_t* rowp = base(k0 + krow[i]);
+      const void* src = (rowp != nullptr && elem[i] < cols)
+                            ? static_cast<const void*>(rowp + elem[i])
+                            : static_cast<const void*>(g_gemm_zero_page);
+      __builtin_amdgcn_global_load_lds(src, static_cast<lds_void*>(lds + (i * kNW + w) * 1024), 16, 0, 0);
+    }
+  }
+};
+
+typedef short v4s_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4s_t lds_v4s;
+
+// 8 bf16 of k (kg*16 + 8*octet .. +7) for column `col` of an MN-major LDS tile
+// with row bytes RB, read by the 16-lane group of this lane (lane & 15 = i16):
+// two transposing reads, each giving 4 consecutive k of column col0 + i16.
+template <int RB>
+__device__ __forceinline__ bf16x8_t read_tr_frag(const lds_char* tile, int kbase, int col0) {
+  const int i16 = threadIdx.x & 15;
+  bf16x8_t out;
+  v4s_t lo, hi;
+  {
+    const int k = kbase + (i16 >> 2), c = col0 + 4 * (i16 & 3);
+    const lds_char* p = tile + k * RB + (((c >> 4) ^ swz_mn(k)) << 5) + (c & 15) * 2;
+    lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)p);
+  }
+  {
+    const int k = kbase + 4 + (i16 >> 2), c = col0 + 4 * (i16 & 3);
+    const lds_char* p = tile + k * RB + (((c >> 4) ^ swz_mn(k)) << 5) + (c & 15) * 2;
+    hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)p);
+  }
+  typedef short v8s_t __attribute__((ext_vector_type(8)));
+  const v8s_t v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  out = __builtin_bit_cast(bf16x8_t, v);
+  return out;
+}
+
 // ---------------------------------------------------------------------------
 // MFMA step over one 16-wide k group
 // ---------------------------------------------------------------------------
-template <typename T, int TM, int TN>
+template <typename T, int TM, int TN, bool AK, bool BK, int BM, int BN>
 struct Mma;
 
-template <int TM, int TN>
-struct Mma<bf16_t, TM, TN> {
+typedef __attribute__((address_space(3))) bf16x8_t lds_bf16x8;
+
+// bf16: K-major tiles are read with one 16-byte LDS read per fragment,
+// MN-major tiles (kept in the operand's own layout) with two transposing reads.
+template <int TM, int TN, bool AK, bool BK, int BM, int BN>
+struct Mma<bf16_t, TM, TN, AK, BK, BM, BN> {
   static constexpr int kGroups = 4;  // 64 bf16 of k per stage
-  __device__ __forceinline__ static void step(const char* As, const char* Bs, int a_row0, int b_row0,
-                                              int kg, f32x16_t (&acc)[TM][TN]) {
+  __device__ __forceinline__ static void step(const lds_char* As, const lds_char* Bs, int a_row0,
+                                              int b_row0, int kg, f32x16_t (&acc)[TM][TN]) {
     const int lane = threadIdx.x & 63;
     const int chunk = kg * 2 + (lane >> 5);
+    const int kbase = kg * 16 + 8 * (lane >> 5);
+    const int half16 = 16 * ((lane >> 4) & 1);
     bf16x8_t a[TM], b[TN];
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
-      const int r = a_row0 + i * 32 + (lane & 31);
-      a[i] = *reinterpret_cast<const bf16x8_t*>(As + swz(r, chunk));
+      if constexpr (AK) {
+        const int r = a_row0 + i * 32 + (lane & 31);
+        a[i] = *reinterpret_cast<const lds_bf16x8*>(As + swz(r, chunk));
+      } else {
+        a[i] = read_tr_frag<BM * 2>(As, kbase, a_row0 + i * 32 + half16);
+      }
     }
 #pragma unroll
     for (int j = 0; j < TN; ++j) {
-      const int r = b_row0 + j * 32 + (lane & 31);
-      b[j] = *reinterpret_cast<const bf16x8_t*>(Bs + swz(r, chunk));
+      if constexpr (BK) {
+        const int r = b_row0 + j * 32 + (lane & 31);
+        b[j] = *reinterpret_cast<const lds_bf16x8*>(Bs + swz(r, chunk));
+      } else {
+        b[j] = read_tr_frag<BN * 2>(Bs, kbase, b_row0 + j * 32 + half16);
+      }
     }
 #pragma unroll
     for (int i = 0; i < TM; ++i)
@@ -222,25 +310,27 @@ struct Mma<bf16_t, TM, TN> {
   }
 };
 
-template <int TM, int TN>
-struct Mma<float, TM, TN> {
+template <int TM, int TN, bool AK, bool BK, int BM, int BN>
+struct Mma<float, TM, TN, AK, BK, BM, BN> {
   static constexpr int kGroups = 2;  // 32 fp32 of k per stage
-  __device__ __forceinline__ static void step(const char* As, const char* Bs, int a_row0, int b_row0,
-                                              int kg, f32x16_t (&acc)[TM][TN]) {
+  __device__ __forceinline__ static void step(const lds_char* As, const lds_char* Bs, int a_row0,
+                                              int b_row0, int kg, f32x16_t (&acc)[TM][TN]) {
     const int lane = threadIdx.x & 63;
     const int chunk = kg * 4 + (lane >> 5) * 2;
+    const char* Ag = (const char*)As;
+    const char* Bg = (const char*)Bs;
     float4 a[TM][2], b[TN][2];
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
       const int r = a_row0 + i * 32 + (lane & 31);
-      a[i][0] = *reinterpret_cast<const float4*>(As + swz(r, chunk));
-      a[i][1] = *reinterpret_cast<const float4*>(As + swz(r, chunk + 1));
+      a[i][0] = *reinterpret_cast<const float4*>(Ag + swz(r, chunk));
+      a[i][1] = *reinterpret_cast<const float4*>(Ag + swz(r, chunk + 1));
     }
 #pragma unroll
     for (int j = 0; j < TN; ++j) {
       const int r = b_row0 + j * 32 + (lane & 31);
-      b[j][0] = *reinterpret_cast<const float4*>(Bs + swz(r, chunk));
-      b[j][1] = *reinterpret_cast<const float4*>(Bs + swz(r, chunk + 1));
+      b[j][0] = *reinterpret_cast<const float4*>(Bg + swz(r, chunk));
+      b[j][1] = *reinterpret_cast<const float4*>(Bg + swz(r, chunk + 1));
     }
 #pragma unroll
     for (int i = 0; i < TM; ++i)
@@ -357,8 +447,13 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(GemmArgs p) {
   const int wm = wid / WGN, wn = wid % WGN;
 
   // ---- operand addressing ----
-  using ATile = typename std::conditional<AK, KMajorTile<BM, NT>, MNMajorTile<T, BM, NT>>::type;
-  using BTile = typename std::conditional<BK, KMajorTile<BN, NT>, MNMajorTile<T, BN, NT>>::type;
+  // bf16 MN-major operands load straight into LDS (transposed on the read);
+  // fp32 MN-major operands are transposed in registers.
+  constexpr bool kMNDirect = sizeof(T) == 2;
+  using AMN = typename std::conditional<kMNDirect, MNDirectTile<BM, NT>, MNMajorTile<T, BM, NT>>::type;
+  using BMN = typename std::conditional<kMNDirect, MNDirectTile<BN, NT>, MNMajorTile<T, BN, NT>>::type;
+  using ATile = typename std::conditional<AK, KMajorTile<BM, NT>, AMN>::type;
+  using BTile = typename std::conditional<BK, KMajorTile<BN, NT>, BMN>::type;
   ATile at;
   BTile bt;
   if constexpr (AK) {
@@ -388,6 +483,8 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(GemmArgs p) {
     }
     bt.init_chunks();
   }
+  if constexpr (!AK && kMNDirect) at.init();
+  if constexpr (!BK && kMNDirect) bt.init();
   const int64_t a_cols = p.M - m0;  // valid m in this tile (MN-major A)
   const int64_t b_cols = p.N - n0;  // valid n in this tile (MN-major B)
   auto a_base = [&](int64_t k) -> const T* {
@@ -411,27 +508,33 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(GemmArgs p) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
-  // K-major operands go straight from global memory into the LDS buffer of
-  // the next stage; MN-major operands pass through registers (for the
+  // Operands go straight from global memory into the LDS buffer of the next
+  // stage, except fp32 MN-major ones, which pass through registers (for the
   // transpose) and are written after the current stage's MFMAs.
   lds_char* lds = (lds_char*)(smem_lds);   // address-space cast of the dynamic LDS block
+  auto a_base16 = [&](int64_t k) { return reinterpret_cast<const uint16_t*>(a_base(k)); };
+  auto b_base16 = [&](int64_t k) { return reinterpret_cast<const uint16_t*>(b_base(k)); };
   auto issue_loads = [&](int64_t kt, int buf) {
     const int64_t k0 = kt * kBK;
-    if constexpr (AK) at.load(k0 * static_cast<int64_t>(sizeof(T)), lds + buf * kStage);
+    lds_char* la = lds + buf * kStage;
+    lds_char* lb = la + BM * kRowBytes;
+    if constexpr (AK) at.load(k0 * static_cast<int64_t>(sizeof(T)), la);
+    else if constexpr (kMNDirect) at.load(k0, a_base16, a_cols, la);
     else at.template load<0>(k0, a_base, a_cols);
-    if constexpr (BK) bt.load(k0 * static_cast<int64_t>(sizeof(T)), lds + buf * kStage + BM * kRowBytes);
+    if constexpr (BK) bt.load(k0 * static_cast<int64_t>(sizeof(T)), lb);
+    else if constexpr (kMNDirect) bt.load(k0, b_base16, b_cols, lb);
     else bt.template load<0>(k0, b_base, b_cols);
   };
   auto store_regs = [&](int buf) {
-    if constexpr (!AK) at.template store<0>(As0 + buf * kStage);
-    if constexpr (!BK) bt.template store<0>(Bs0 + buf * kStage);
+    if constexpr (!AK && !kMNDirect) at.template store<0>(As0 + buf * kStage);
+    if constexpr (!BK && !kMNDirect) bt.template store<0>(Bs0 + buf * kStage);
   };
+  using MmaT = Mma<T, TM, TN, AK, BK, BM, BN>;
   auto compute = [&](int buf) {
-    const char* As = As0 + buf * kStage;
-    const char* Bs = Bs0 + buf * kStage;
+    const lds_char* As = lds + buf * kStage;
+    const lds_char* Bs = As + BM * kRowBytes;
 #pragma unroll
-    for (int kg = 0; kg < Mma<T, TM, TN>::kGroups; ++kg)
-      Mma<T, TM, TN>::step(As, Bs, wm * WM, wn * WN, kg, acc);
+    for (int kg = 0; kg < MmaT::kGroups; ++kg) MmaT::step(As, Bs, wm * WM, wn * WN, kg, acc);
   };
 
   const int64_t nk = (p.K + kBK - 1) / kBK;
