@@ -73,39 +73,50 @@ struct GemmArgs {
 
 constexpr int kRowBytes = 128;  // bytes of k per LDS tile row and stage
 
-// LDS tile rows are 128 bytes (8 chunks of 16 bytes).  The chunk index is
-// XORed with bits 0-2 and 3-5 of the row, so that both the MFMA fragment reads
-// (consecutive rows, one chunk) and the transposed stores of MN-major tiles
-// (rows 8 apart, one chunk) spread over the LDS banks.
+// K-major LDS tile rows hold RB bytes of k: 128 (8 chunks of 16 bytes) or 64
+// (4 chunks).  The chunk index is XORed with a function of the row so that the
+// MFMA fragment reads (consecutive rows, one chunk) spread over the LDS banks:
+// with 128-byte rows, bits 0-2 and 3-5 of the row (which also spreads the
+// transposed stores of register-staged MN-major tiles, rows 8 apart); with
+// 64-byte rows, bits 2-3 (four rows share a 256-byte bank window).
+template <int RB>
+__device__ __forceinline__ int row_swizzle(int row) {
+  if constexpr (RB == 128) return (row & 7) ^ ((row >> 3) & 7);
+  else return (row >> 2) & 3;
+}
+template <int RB = kRowBytes>
 __device__ __forceinline__ int swz(int row, int chunk) {
-  return row * kRowBytes + ((chunk ^ (row & 7) ^ ((row >> 3) & 7)) << 4);
+  return row * RB + ((chunk ^ row_swizzle<RB>(row)) << 4);
 }
 
 // ---------------------------------------------------------------------------
 // Tile loaders: global -> registers -> LDS
 // ---------------------------------------------------------------------------
-// K-major operand tile of R rows x 128 bytes.  Thread t of NT moves 16-byte
-// chunk (t & 7) of rows (t >> 3) + (NT / 8) i.
-template <int R, int NT>
+// K-major operand tile of R rows x RB bytes of k.
+template <int R, int NT, int RB>
 struct KMajorTile {
   // Direct global -> LDS loads: the i-th 16-byte load instruction of wave w
-  // fills LDS rows [8 (i NW + w), 8 (i NW + w) + 8) of the tile (1 KB, lane l
-  // at byte 16 l), so lane l fetches row 8 (i NW + w) + l / 8 and, for the
-  // swizzled position (l % 8), the logical chunk (l % 8) ^ swizzle(row).
+  // fills the 1 KB of LDS rows [RPI (i NW + w), RPI (i NW + w) + RPI) of the
+  // tile (RPI = 1024 / RB rows; lane l at byte 16 l), so lane l fetches row
+  // RPI (i NW + w) + l / LPR (LPR = RB / 16 lanes per row) and, for the
+  // swizzled position (l % LPR), the logical chunk (l % LPR) ^ swizzle(row).
   static constexpr int kNW = NT / 64;
-  static constexpr int kPer = R * 8 / NT;
+  static constexpr int kLPR = RB / 16;
+  static constexpr int kRPI = 1024 / RB;
+  static constexpr int kPer = R / (kRPI * kNW);
+  static_assert(kPer * kRPI * kNW == R, "tile shape");
   const char* row_ptr[kPer];
   int chunk_byte[kPer];
 
   __device__ __forceinline__ static int row_of(int i) {
-    return 8 * (i * kNW + (threadIdx.x >> 6)) + ((threadIdx.x & 63) >> 3);
+    return kRPI * (i * kNW + (threadIdx.x >> 6)) + (threadIdx.x & 63) / kLPR;
   }
   __device__ __forceinline__ void init_chunks() {
 #pragma unroll
     for (int i = 0; i < kPer; ++i) {
       const int row = row_of(i);
-      const int phys = threadIdx.x & 7;
-      chunk_byte[i] = (phys ^ (row & 7) ^ ((row >> 3) & 7)) << 4;
+      const int phys = threadIdx.x % kLPR;
+      chunk_byte[i] = (phys ^ row_swizzle<RB>(row)) << 4;
     }
   }
   // `lds` is the tile's LDS buffer (local address space).
@@ -188,7 +199,7 @@ struct MNMajorTile {
 };
 
 // bf16 MN-major operand tile loaded straight into LDS without a transpose:
-// LDS keeps the operand's own layout, [64 k-rows][R elements], in 32-byte
+// LDS keeps the operand's own layout, [KR k-rows][R elements], in 32-byte
 // chunks whose index is XORed with swz_mn(k); the MFMA fragments are then read
 // with the transposing LDS load (ds_read_b64_tr_b16).  The i-th load
 // instruction of wave w fills 1 KB = 1024 / (2 R) k-rows; lane l covers 16
@@ -197,14 +208,14 @@ __device__ const uint4 g_gemm_zero_page[1] = {};
 
 __device__ __forceinline__ int swz_mn(int k) { return ((k & 3) << 1) | ((k >> 3) & 1); }
 
-template <int R, int NT>
+template <int R, int NT, int KR>
 struct MNDirectTile {
   static constexpr int kNW = NT / 64;
   static constexpr int kRB = R * 2;                 // bytes per k-row
   static constexpr int kRowsPerInst = 1024 / kRB;   // k-rows per 1 KB instruction
-  static constexpr int kPer = 64 / kRowsPerInst / kNW;
-  static_assert(kPer * kRowsPerInst * kNW == 64, "tile shape");
-  int krow[kPer];        // k-row (0..63) this lane fills with instruction i
+  static constexpr int kPer = KR / kRowsPerInst / kNW;
+  static_assert(kPer * kRowsPerInst * kNW == KR, "tile shape");
+  int krow[kPer];        // k-row (0..KR-1) this lane fills with instruction i
   int elem[kPer];        // element offset along the row (logical, 8 elements)
 
   __device__ __forceinline__ void init() {
@@ -267,51 +278,69 @@ __device__ __forceinline__ bf16x8_t read_tr_frag(const lds_char* tile, int kbase
 // ---------------------------------------------------------------------------
 // MFMA step over one 16-wide k group
 // ---------------------------------------------------------------------------
-template <typename T, int TM, int TN, bool AK, bool BK, int BM, int BN>
+template <typename T, int TM, int TN, bool AK, bool BK, int BM, int BN, int RB>
 struct Mma;
 
 typedef __attribute__((address_space(3))) bf16x8_t lds_bf16x8;
 
 // bf16: K-major tiles are read with one 16-byte LDS read per fragment,
 // MN-major tiles (kept in the operand's own layout) with two transposing reads.
-template <int TM, int TN, bool AK, bool BK, int BM, int BN>
-struct Mma<bf16_t, TM, TN, AK, BK, BM, BN> {
-  static constexpr int kGroups = 4;  // 64 bf16 of k per stage
-  __device__ __forceinline__ static void step(const lds_char* As, const lds_char* Bs, int a_row0,
-                                              int b_row0, int kg, f32x16_t (&acc)[TM][TN]) {
+template <int TM, int TN, bool AK, bool BK, int BM, int BN, int RB>
+struct Mma<bf16_t, TM, TN, AK, BK, BM, BN, RB> {
+  static constexpr int kGroups = RB / 32;  // 16 bf16 of k per group
+  struct Frags {
+    bf16x8_t a[TM], b[TN];
+  };
+  __device__ __forceinline__ static void read(const lds_char* As, const lds_char* Bs, int a_row0,
+                                              int b_row0, int kg, Frags& fr) {
     const int lane = threadIdx.x & 63;
     const int chunk = kg * 2 + (lane >> 5);
     const int kbase = kg * 16 + 8 * (lane >> 5);
     const int half16 = 16 * ((lane >> 4) & 1);
-    bf16x8_t a[TM], b[TN];
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
       if constexpr (AK) {
         const int r = a_row0 + i * 32 + (lane & 31);
-        a[i] = *reinterpret_cast<const lds_bf16x8*>(As + swz(r, chunk));
+        fr.a[i] = *reinterpret_cast<const lds_bf16x8*>(As + swz<RB>(r, chunk));
       } else {
-        a[i] = read_tr_frag<BM * 2>(As, kbase, a_row0 + i * 32 + half16);
+        fr.a[i] = read_tr_frag<BM * 2>(As, kbase, a_row0 + i * 32 + half16);
       }
     }
 #pragma unroll
     for (int j = 0; j < TN; ++j) {
       if constexpr (BK) {
         const int r = b_row0 + j * 32 + (lane & 31);
-        b[j] = *reinterpret_cast<const lds_bf16x8*>(Bs + swz(r, chunk));
+        fr.b[j] = *reinterpret_cast<const lds_bf16x8*>(Bs + swz<RB>(r, chunk));
       } else {
-        b[j] = read_tr_frag<BN * 2>(Bs, kbase, b_row0 + j * 32 + half16);
+        fr.b[j] = read_tr_frag<BN * 2>(Bs, kbase, b_row0 + j * 32 + half16);
       }
     }
+  }
+  __device__ __forceinline__ static void mma(const Frags& fr, f32x16_t (&acc)[TM][TN]) {
 #pragma unroll
     for (int i = 0; i < TM; ++i)
 #pragma unroll
       for (int j = 0; j < TN; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr.a[i], fr.b[j], acc[i][j], 0, 0, 0);
+  }
+  // One stage: the fragments of group kg + 1 are read while group kg's MFMAs run.
+  __device__ __forceinline__ static void stage(const lds_char* As, const lds_char* Bs, int a_row0,
+                                               int b_row0, f32x16_t (&acc)[TM][TN]) {
+    Frags fr[2];
+    read(As, Bs, a_row0, b_row0, 0, fr[0]);
+#pragma unroll
+    for (int kg = 0; kg < kGroups; ++kg) {
+      if (kg + 1 < kGroups) read(As, Bs, a_row0, b_row0, kg + 1, fr[(kg + 1) & 1]);
+      __builtin_amdgcn_sched_barrier(0);   // keep the reads ahead of the MFMAs
+      mma(fr[kg & 1], acc);
+      __builtin_amdgcn_sched_barrier(0);
+    }
   }
 };
 
-template <int TM, int TN, bool AK, bool BK, int BM, int BN>
-struct Mma<float, TM, TN, AK, BK, BM, BN> {
+template <int TM, int TN, bool AK, bool BK, int BM, int BN, int RB>
+struct Mma<float, TM, TN, AK, BK, BM, BN, RB> {
+  static_assert(RB == kRowBytes, "fp32 tiles use 128-byte rows");
   static constexpr int kGroups = 2;  // 32 fp32 of k per stage
   __device__ __forceinline__ static void step(const lds_char* As, const lds_char* Bs, int a_row0,
                                               int b_row0, int kg, f32x16_t (&acc)[TM][TN]) {
@@ -344,6 +373,11 @@ struct Mma<float, TM, TN, AK, BK, BM, BN> {
         for (int e = 0; e < 8; ++e)
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(av[e], bv[e], acc[i][j], 0, 0, 0);
       }
+  }
+  __device__ __forceinline__ static void stage(const lds_char* As, const lds_char* Bs, int a_row0,
+                                               int b_row0, f32x16_t (&acc)[TM][TN]) {
+#pragma unroll
+    for (int kg = 0; kg < kGroups; ++kg) step(As, Bs, a_row0, b_row0, kg, acc);
   }
 };
 
@@ -421,22 +455,23 @@ __device__ __forceinline__ void store8g(void* base, int64_t idx, const float (&v
 }
 
 // ---------------------------------------------------------------------------
-// The kernel: BM x BN tile, WGM x WGN waves, 2 LDS stages of 128 bytes of k.
+// The kernel: BM x BN tile, WGM x WGN waves, NS LDS stages of RB bytes of k.
 // ---------------------------------------------------------------------------
-template <typename T, int BM, int BN, int WGM, int WGN, bool AK, bool BK, int EPI, typename OutT>
+template <typename T, int BM, int BN, int WGM, int WGN, bool AK, bool BK, int EPI, typename OutT,
+          int RB, int NS>
 __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(GemmArgs p) {
   constexpr int NT = 64 * WGM * WGN;
   constexpr int WM = BM / WGM, WN = BN / WGN;
   constexpr int TM = WM / 32, TN = WN / 32;
-  constexpr int kBK = kRowBytes / sizeof(T);
+  constexpr int kBK = RB / sizeof(T);
   static_assert(EPI != kEpiGateUp || WN % 64 == 0, "gate/up pairing needs 64-column wave tiles");
-  static_assert((32 * (WN + 4) * 4) * WGM * WGN <= 2 * (BM + BN) * kRowBytes, "epilogue staging");
+  static_assert((32 * (WN + 4) * 4) * WGM * WGN <= NS * (BM + BN) * RB, "epilogue staging");
 
-  extern __shared__ __attribute__((aligned(16))) char smem[];   // 2 stages x (BM + BN) rows
+  extern __shared__ __attribute__((aligned(16))) char smem[];   // NS stages x (BM + BN) rows
   char* smem_lds = smem;
   char* As0 = smem;
-  char* Bs0 = smem + BM * kRowBytes;
-  constexpr int kStage = (BM + BN) * kRowBytes;
+  char* Bs0 = smem + BM * RB;
+  constexpr int kStage = (BM + BN) * RB;
 
   int64_t mt, nt;
   tile_coords((p.M + BM - 1) / BM, (p.N + BN - 1) / BN, mt, nt);
@@ -450,10 +485,12 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(GemmArgs p) {
   // bf16 MN-major operands load straight into LDS (transposed on the read);
   // fp32 MN-major operands are transposed in registers.
   constexpr bool kMNDirect = sizeof(T) == 2;
-  using AMN = typename std::conditional<kMNDirect, MNDirectTile<BM, NT>, MNMajorTile<T, BM, NT>>::type;
-  using BMN = typename std::conditional<kMNDirect, MNDirectTile<BN, NT>, MNMajorTile<T, BN, NT>>::type;
-  using ATile = typename std::conditional<AK, KMajorTile<BM, NT>, AMN>::type;
-  using BTile = typename std::conditional<BK, KMajorTile<BN, NT>, BMN>::type;
+  static_assert(kMNDirect || (RB == kRowBytes && NS == 2),
+                "fp32 MN-major tiles pass through registers: 128-byte rows, two stages");
+  using AMN = typename std::conditional<kMNDirect, MNDirectTile<BM, NT, kBK>, MNMajorTile<T, BM, NT>>::type;
+  using BMN = typename std::conditional<kMNDirect, MNDirectTile<BN, NT, kBK>, MNMajorTile<T, BN, NT>>::type;
+  using ATile = typename std::conditional<AK, KMajorTile<BM, NT, RB>, AMN>::type;
+  using BTile = typename std::conditional<BK, KMajorTile<BN, NT, RB>, BMN>::type;
   ATile at;
   BTile bt;
   if constexpr (AK) {
@@ -508,16 +545,17 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(GemmArgs p) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
-  // Operands go straight from global memory into the LDS buffer of the next
-  // stage, except fp32 MN-major ones, which pass through registers (for the
-  // transpose) and are written after the current stage's MFMAs.
+  // Operands go straight from global memory into the LDS buffer of a later
+  // stage (NS - 1 stages ahead), except fp32 MN-major ones, which pass through
+  // registers (for the transpose) and are written after the current stage's
+  // MFMAs (NS = 2).
   lds_char* lds = (lds_char*)(smem_lds);   // address-space cast of the dynamic LDS block
   auto a_base16 = [&](int64_t k) { return reinterpret_cast<const uint16_t*>(a_base(k)); };
   auto b_base16 = [&](int64_t k) { return reinterpret_cast<const uint16_t*>(b_base(k)); };
   auto issue_loads = [&](int64_t kt, int buf) {
     const int64_t k0 = kt * kBK;
     lds_char* la = lds + buf * kStage;
-    lds_char* lb = la + BM * kRowBytes;
+    lds_char* lb = la + BM * RB;
     if constexpr (AK) at.load(k0 * static_cast<int64_t>(sizeof(T)), la);
     else if constexpr (kMNDirect) at.load(k0, a_base16, a_cols, la);
     else at.template load<0>(k0, a_base, a_cols);
@@ -529,27 +567,41 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(GemmArgs p) {
     if constexpr (!AK && !kMNDirect) at.template store<0>(As0 + buf * kStage);
     if constexpr (!BK && !kMNDirect) bt.template store<0>(Bs0 + buf * kStage);
   };
-  using MmaT = Mma<T, TM, TN, AK, BK, BM, BN>;
+  using MmaT = Mma<T, TM, TN, AK, BK, BM, BN, RB>;
   auto compute = [&](int buf) {
     const lds_char* As = lds + buf * kStage;
-    const lds_char* Bs = As + BM * kRowBytes;
-#pragma unroll
-    for (int kg = 0; kg < MmaT::kGroups; ++kg) MmaT::step(As, Bs, wm * WM, wn * WN, kg, acc);
+    const lds_char* Bs = As + BM * RB;
+    MmaT::stage(As, Bs, wm * WM, wn * WN, acc);
   };
 
+  // Pipeline: stage kt is computed while stages kt+1 .. kt+NS-1 are in
+  // flight.  Every stage issues the same number of load instructions per
+  // thread (kLoads), so "stage kt has landed" is a vmcnt of kLoads times the
+  // number of younger stages; the barrier after it also tells every wave that
+  // the buffer about to be refilled has been read by all.
+  constexpr int kLoads = (AK || kMNDirect ? ATile::kPer : 0) + (BK || kMNDirect ? BTile::kPer : 0);
   const int64_t nk = (p.K + kBK - 1) / kBK;
-  issue_loads(0, 0);
-  store_regs(0);
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-  for (int64_t kt = 0; kt < nk; ++kt) {
-    const int cur = static_cast<int>(kt & 1);
-    if (kt + 1 < nk) issue_loads(kt + 1, cur ^ 1);
-    compute(cur);
-    if (kt + 1 < nk) store_regs(cur ^ 1);
-    __builtin_amdgcn_s_waitcnt(0);   // this thread's direct-to-LDS loads have landed
-    __syncthreads();
+#pragma unroll
+  for (int st = 0; st < NS - 1; ++st) {
+    if (st < nk) {
+      issue_loads(st, st);
+      store_regs(st);
+    }
   }
+  for (int64_t kt = 0; kt < nk; ++kt) {
+    const int64_t younger = (nk - 1 - kt) < (NS - 2) ? (nk - 1 - kt) : (NS - 2);
+    static_assert(NS >= 2 && NS <= 5 && (NS - 2) * kLoads < 64, "stages");
+    if (younger >= 3) wait_vmcnt<(NS >= 5 ? 3 * kLoads : 0)>();
+    else if (younger == 2) wait_vmcnt<(NS >= 4 ? 2 * kLoads : 0)>();
+    else if (younger == 1) wait_vmcnt<(NS >= 3 ? kLoads : 0)>();
+    else wait_vmcnt<0>();
+    if constexpr (kMNDirect) lds_barrier();
+    else __syncthreads();   // register-staged tiles were written with ds_write
+    if (kt + NS - 1 < nk) issue_loads(kt + NS - 1, static_cast<int>((kt + NS - 1) % NS));
+    compute(static_cast<int>(kt % NS));
+    if (kt + NS - 1 < nk) store_regs(static_cast<int>((kt + NS - 1) % NS));
+  }
+  __syncthreads();   // the epilogue reuses the stage buffers
 
   // ---- epilogue: per 32-row block, stage through this wave's LDS region ----
   constexpr int LD = WN + 4;
@@ -575,58 +627,91 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(GemmArgs p) {
         }
       }
     } else if constexpr (EPI == kEpiGateUp) {
-      // wave columns: pairs of [32 gate | 32 up] for the same 32 features
+      // wave columns: pairs of [32 gate | 32 up] for the same 32 features.
+      // The table rows are fetched for all of this lane's chunks first (their
+      // loads overlap), then h, g, u are formed and stored.
       constexpr int kFeatChunks = 32 * (WN / 2) / 8;
+      constexpr int kPerLane = (kFeatChunks + 63) / 64;
       const int64_t f = p.d_ff;
+      int64_t ri[kPerLane], tokq[kPerLane];
+      float e[kPerLane][8];
 #pragma unroll
-      for (int q = lane; q < kFeatChunks; q += 64) {
+      for (int c = 0; c < kPerLane; ++c) {
+        const int q = lane + 64 * c;
+        const int rr = q / (WN / 16);
+        const int64_t m = mrow0 + rr;
+        const int64_t mm = m < p.M ? m : p.M - 1;
+        tokq[c] = p.a_rows ? static_cast<int64_t>(p.a_rows[mm]) : mm;
+        ri[c] = p.row_index[tokq[c]];
+      }
+#pragma unroll
+      for (int c = 0; c < kPerLane; ++c) {
+        const int q = lane + 64 * c;
+        const int fc = (q % (WN / 16)) * 8;
+        const int64_t feat = (n0 + wn * WN) / 2 + fc;
+        const bool ok = ri[c] >= 0 && ri[c] < p.n_rows && feat < f;
+        load8g<T>(p.rows, ok ? ri[c] * f + feat : 0, e[c]);
+      }
+#pragma unroll
+      for (int c = 0; c < kPerLane; ++c) {
+        const int q = lane + 64 * c;
+        if (q >= kFeatChunks) continue;
         const int rr = q / (WN / 16);
         const int fc = (q % (WN / 16)) * 8;           // feature offset within the wave's WN/2
         const int pair = fc / 32, fin = fc % 32;
         const int64_t m = mrow0 + rr;
         const int64_t feat = (n0 + wn * WN) / 2 + fc;
         if (m < p.M && feat < f) {
-          float g[8], a[8], e[8];
+          float g[8], a[8];
           read8(region + rr * LD + pair * 64 + fin, g);
           read8(region + rr * LD + pair * 64 + 32 + fin, a);
-          const int64_t tok = p.a_rows ? static_cast<int64_t>(p.a_rows[m]) : m;
-          const int64_t ri = p.row_index[tok];
-          if (ri >= 0 && ri < p.n_rows) {
-            load8g<T>(p.rows, ri * f + feat, e);
-          } else {
+          if (!(ri[c] >= 0 && ri[c] < p.n_rows)) {
             flag_index_error(p.err);
 #pragma unroll
-            for (int k = 0; k < 8; ++k) e[k] = 0.0f;
+            for (int k = 0; k < 8; ++k) e[c][k] = 0.0f;
           }
           float u[8], h[8];
 #pragma unroll
           for (int k = 0; k < 8; ++k) {
-            u[k] = a[k] + e[k];
+            u[k] = a[k] + e[c][k];
             h[k] = g[k] * sigmoidf_(g[k]) * u[k];
           }
-          const int64_t o = tok * f + feat;
+          const int64_t o = tokq[c] * f + feat;
           store8g<T>(p.h_out, o, h);
           if (p.g_out) store8g<T>(p.g_out, o, g);
           if (p.u_out) store8g<T>(p.u_out, o, u);
         }
       }
     } else {  // kEpiDhAct: C = dh (M = tokens, N = d_ff)
+      // g and u of all of this lane's chunks are loaded first, then dg, du
+      // are formed and stored
       const int64_t f = p.N;
+      constexpr int kPerLane = (kChunks + 63) / 64;
+      float gv[kPerLane][8], uv[kPerLane][8];
 #pragma unroll
-      for (int q = lane; q < kChunks; q += 64) {
+      for (int c = 0; c < kPerLane; ++c) {
+        const int q = lane + 64 * c;
         const int rr = q / (WN / 8), cc = (q % (WN / 8)) * 8;
         const int64_t m = mrow0 + rr;
         const int64_t n = n0 + wn * WN + cc;
-        if (m < p.M && n < f) {
-          float dh[8], g[8], u[8], dg[8], du[8];
+        const bool ok = q < kChunks && m < p.M && n < f;
+        load8g<T>(p.g_in, ok ? m * f + n : 0, gv[c]);
+        load8g<T>(p.u_in, ok ? m * f + n : 0, uv[c]);
+      }
+#pragma unroll
+      for (int c = 0; c < kPerLane; ++c) {
+        const int q = lane + 64 * c;
+        const int rr = q / (WN / 8), cc = (q % (WN / 8)) * 8;
+        const int64_t m = mrow0 + rr;
+        const int64_t n = n0 + wn * WN + cc;
+        if (q < kChunks && m < p.M && n < f) {
+          float dh[8], dg[8], du[8];
           read8(region + rr * LD + cc, dh);
-          load8g<T>(p.g_in, m * f + n, g);
-          load8g<T>(p.u_in, m * f + n, u);
 #pragma unroll
           for (int k = 0; k < 8; ++k) {
-            const float s = sigmoidf_(g[k]);
-            du[k] = dh[k] * g[k] * s;
-            dg[k] = dh[k] * u[k] * s * (1.0f + g[k] * (1.0f - s));
+            const float s = sigmoidf_(gv[c][k]);
+            du[k] = dh[k] * gv[c][k] * s;
+            dg[k] = dh[k] * uv[c][k] * s * (1.0f + gv[c][k] * (1.0f - s));
           }
           store8g<T>(p.dgu_out, m * 2 * f + n, dg);
           store8g<T>(p.dgu_out, m * 2 * f + f + n, du);
@@ -640,10 +725,11 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(GemmArgs p) {
 // ---------------------------------------------------------------------------
 // Host launchers
 // ---------------------------------------------------------------------------
-template <typename T, int BM, int BN, int WGM, int WGN, bool AK, bool BK, int EPI, typename OutT>
+template <typename T, int BM, int BN, int WGM, int WGN, bool AK, bool BK, int EPI, typename OutT,
+          int RB, int NS>
 static hipError_t run_tile(const GemmArgs& a, hipStream_t s) {
-  constexpr size_t kSmem = 2 * (BM + BN) * kRowBytes;
-  auto kern = &gemm_kernel<T, BM, BN, WGM, WGN, AK, BK, EPI, OutT>;
+  constexpr size_t kSmem = static_cast<size_t>(NS) * (BM + BN) * RB;
+  auto kern = &gemm_kernel<T, BM, BN, WGM, WGN, AK, BK, EPI, OutT, RB, NS>;
   static const hipError_t attr = hipFuncSetAttribute(
       reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
       static_cast<int>(kSmem));
@@ -658,10 +744,15 @@ template <typename T, bool AK, bool BK, int EPI, typename OutT>
 static hipError_t run(const GemmArgs& a, hipStream_t s) {
   if (a.M <= 0 || a.N <= 0) return hipSuccess;
   if constexpr (sizeof(T) == 2) {
+    // (2x2 waves of 128x128, with half the LDS reads per MFMA, measured
+    // slower: one wave per SIMD hides too little latency)
+    // (Four or five 32 KB stages of 64-byte rows, which keep three or four
+    // stages of loads in flight, measured no faster: the kernels are not
+    // waiting on global-load latency.)
     if (a.M >= 256 && a.N >= 256 && ((a.M + 255) / 256) * ((a.N + 255) / 256) >= 128)
-      return run_tile<T, 256, 256, 2, 4, AK, BK, EPI, OutT>(a, s);
+      return run_tile<T, 256, 256, 2, 4, AK, BK, EPI, OutT, kRowBytes, 2>(a, s);
   }
-  return run_tile<T, 128, 128, 2, 2, AK, BK, EPI, OutT>(a, s);
+  return run_tile<T, 128, 128, 2, 2, AK, BK, EPI, OutT, kRowBytes, 2>(a, s);
 }
 
 template <typename T>
