@@ -190,7 +190,7 @@ def run_decode(torch, st, w, steps, warmup):
     gu_bytes = (2 * d * f + n * d + n_unique * f + n * f) * 2      # W_gate, W_up, x, rows, h
     down_bytes = (d * f + n * f + n * d) * 2                        # W_down, h, y
     step_bytes = w.n_layers * (gu_bytes + down_bytes)
-    sha = source_sha("decode.hip")
+    sha = source_sha("decode.hip", "common.h")
     achieved = gu_bytes / (gu_us * 1e-6) / 1e9
     res = {
         "ms_per_step": ms,
@@ -349,7 +349,7 @@ def run_train(torch, st, w, steps, warmup):
             "kernel": "gemm_kernel<bf16,GateUp> (staple_ffn_gate_up, training batch)",
             "bound": "mfma", "achieved": achieved, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
             "frac": achieved / BF16_PEAK_TFLOPS,
-            "traffic": traffic_from_profile("train_gate_up", source_sha("gemm.hip")),
+            "traffic": traffic_from_profile("train_gate_up", source_sha("gemm.hip", "common.h")),
             "avg_launch_us": gu_us, "algorithmic_flops_per_launch": gu_flops,
         },
     }, T

@@ -10,11 +10,11 @@
 // the j-th load of every lane.  The activation, which every workgroup reads,
 // is loaded as whole cache lines and put into the same fragment pattern
 // through LDS (half the cache-line requests of the fragment pattern).  A and
-// B use the same k order, so the contraction is unchanged.  Two steps of
-// loads are kept in flight per wave.
+// B use the same k order, so the contraction is unchanged.
 //
-// Gate/up: one workgroup per 32 features; its four waves split d_model and
-// their partial sums meet in LDS, after which the epilogue gathers each
+// Gate/up: one workgroup per 32 features; each of its four waves owns the
+// gate and up rows of 8 features over all of d_model, the activation of each
+// step is shared by the waves through LDS, and the epilogue gathers each
 // token's table row, forms u = W_up x + E[t] and h = silu(W_gate x) * u
 // (STAPLE abstract: the up-projection is retained and the embedding added as
 // a residual path; retrieval-path table: row reconstruction fused with the
@@ -179,90 +179,141 @@ __device__ __forceinline__ void stream_k_xline(const char* const (&pa)[NA], cons
   __builtin_amdgcn_sched_barrier(0);
 }
 
-// Gate/up for at most 64 tokens: one workgroup (4 waves) per 32 features,
-// the waves split d_model, and the wave partial sums are folded in LDS after
-// the stream; the epilogue gathers each token's table row, forms
-// u = W_up x + E[t] and h = silu(W_gate x) * u and stores h (and g, u when
-// asked) with 16-byte vectors.
-template <int NS>
-__global__ __launch_bounds__(256) void decode_gateup_kernel(
+// Gate/up for at most 64 tokens, features split over the waves: one
+// workgroup (4 waves) per 32 features; wave w owns gate and up rows of
+// features 8w .. 8w+7 (one 16-row MFMA block: 8 gate rows, then 8 up rows)
+// over the whole of d_model, so no partial sums cross waves.  The activation
+// of SPB macro steps (64 tokens x 128 bytes each) is loaded once per
+// workgroup as whole cache lines (two 1 KB loads per wave and step), written
+// to one of two LDS slots and read by all four waves; one barrier per SPB
+// steps hands a slot over.  Weights and activations are loaded WD steps ahead
+// (8 + 8 registers per step): loads complete in issue order, so waiting for
+// a step's activation also waits for every weight load issued before it.
+template <int WD, int SPB>
+__global__ __launch_bounds__(256) void decode_gateup_fs_kernel(
     int n, int64_t d, int64_t f, const uint16_t* __restrict__ x, const uint16_t* __restrict__ wg,
     const uint16_t* __restrict__ wu, const uint16_t* __restrict__ rows, int64_t n_rows,
     const int32_t* __restrict__ row_index, uint16_t* __restrict__ h, uint16_t* __restrict__ g_out,
     uint16_t* __restrict__ u_out, int* err) {
-  constexpr int WAVES = 4, NA = 4, NB = 4, NT = NA * NB;
-  constexpr int kRing = NT * 4 * 64 * 4;            // bytes of LDS per wave (partials)
-  static_assert(kRing >= kXBlock, "activation block fits");
-  __shared__ __attribute__((aligned(16))) char smem[WAVES * kRing];
-  lds_char* lds = (lds_char*)(smem);
+  constexpr int NB = 4;
+  constexpr int XS = WD / SPB;                          // slots of activation registers (super-steps)
+  constexpr int U = XS % 2 == 0 ? XS : 2 * XS;          // unrolled super-steps (even: LDS slot parity)
+  static_assert(WD % SPB == 0 && XS >= 1, "prefetch depth in whole super-steps");
+  constexpr int kSlot = SPB * kXBlock;
+  constexpr int kEpiLd = 65;                            // floats per staged row
+  __shared__ __attribute__((aligned(16))) char xs[2 * kSlot];
+  __shared__ float stage[4][16 * kEpiLd];
+  lds_char* xl = (lds_char*)(xs);
   const int lane = threadIdx.x & 63;
   const int wid = threadIdx.x >> 6;
   const int r = lane & 15, q = lane >> 4;
-  const int64_t f0 = static_cast<int64_t>(blockIdx.x) * 32;
+  const int64_t f0 = static_cast<int64_t>(blockIdx.x) * 32 + 8 * wid;   // this wave's features
   const int64_t T = d / 64;
-  const int slice = (wid + static_cast<int>(blockIdx.x >> 3)) % WAVES;
-  const int64_t s0 = T * slice / WAVES, s1 = T * (slice + 1) / WAVES;
-  const char* pa[NA] = {reinterpret_cast<const char*>(wg + (f0 + r) * d) + q * 16,
-                        reinterpret_cast<const char*>(wg + (f0 + 16 + r) * d) + q * 16,
-                        reinterpret_cast<const char*>(wu + (f0 + r) * d) + q * 16,
-                        reinterpret_cast<const char*>(wu + (f0 + 16 + r) * d) + q * 16};
-  const char* px[8];
+  const char* pa = reinterpret_cast<const char*>(r < 8 ? wg + (f0 + r) * d : wu + (f0 + r - 8) * d) + q * 16;
+  // activation loads of this wave: tokens 16 wid + l / 8 and 16 wid + 8 + l / 8, chunk l % 8
+  const char* px[2];
+  int wofs[2];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int t = min(8 * i + (lane >> 3), n - 1);
-    px[i] = reinterpret_cast<const char*>(x + static_cast<int64_t>(t) * d) + (lane & 7) * 16;
+  for (int i = 0; i < 2; ++i) {
+    const int tt = 16 * wid + 8 * i + (lane >> 3);
+    px[i] = reinterpret_cast<const char*>(x + static_cast<int64_t>(min(tt, n - 1)) * d) + (lane & 7) * 16;
+    wofs[i] = xblock_at(tt, lane & 7);
   }
+  auto off = [&](int64_t s) -> int64_t { return (s < T ? s : T - 1) * 128; };
 
-  // epilogue thread -> (token et, 8 consecutive features); its table row is
-  // fetched (branch-free, from a valid address) once the first steps are in
-  // flight
-  const int et = threadIdx.x >> 2;
-  const int efq = (threadIdx.x & 3) * 8;
-  bool erow_ok;
-  uint4 erow;
+  Frag2 a[WD];
+  uint4 xv[XS][SPB][2];
+  f32x4_t acc[NB];
+#pragma unroll
+  for (int k = 0; k < NB; ++k)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc[k][i] = 0.0f;
+  auto load_x = [&](uint4 (&dst)[SPB][2], int64_t super) {
+#pragma unroll
+    for (int sb = 0; sb < SPB; ++sb)
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+        dst[sb][i] = *reinterpret_cast<const uint4*>(px[i] + off(super * SPB + sb));
+  };
+  auto store_x = [&](lds_char* slot, const uint4 (&src)[SPB][2]) {
+#pragma unroll
+    for (int sb = 0; sb < SPB; ++sb)
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+        *reinterpret_cast<lds_u32x4*>(slot + sb * kXBlock + wofs[i]) = __builtin_bit_cast(u32x4_t, src[sb][i]);
+  };
 
-  f32x4_t acc[NT];
+  // super-step 0 goes to slot 0 now; super-steps 1 .. XS wait in xv[S % XS]
+  uint4 x0[SPB][2];
+  load_x(x0, 0);
 #pragma unroll
-  for (int t = 0; t < NT; ++t)
+  for (int j = 0; j < WD; ++j) load_step(a[j], pa, off(j));
 #pragma unroll
-    for (int i = 0; i < 4; ++i) acc[t][i] = 0.0f;
-  stream_k_xline<NA, NB, NS>(pa, px, lds + wid * kRing, s0, s1, acc, [&]() {
-    const int64_t ri = row_index[min(et, n - 1)];
-    erow_ok = ri >= 0 && ri < n_rows;
-    const uint16_t* esrc = erow_ok ? rows + ri * f + f0 + efq : x;
-    erow = *reinterpret_cast<const uint4*>(esrc);
-  });
-
-  // each wave parks its sums in its own LDS block
-  float* part = reinterpret_cast<float*>(smem);
-  constexpr int kRingF = kRing / 4;
-#pragma unroll
-  for (int t = 0; t < NT; ++t)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) part[wid * kRingF + (t * 4 + i) * 64 + lane] = acc[t][i];
+  for (int j = 1; j <= XS; ++j) load_x(xv[j % XS], j);
+  // the epilogue's table row (lane = token, this wave's 8 features)
+  const int64_t ri = row_index[min(lane, n - 1)];
+  const bool erow_ok = ri >= 0 && ri < n_rows;
+  const uint4 erow = *reinterpret_cast<const uint4*>(erow_ok ? rows + ri * f + f0 : x);
+  store_x(xl, x0);
   __syncthreads();
 
-  const int t = et;
-  const int fq = efq;
+  const int64_t nsuper = (T + SPB - 1) / SPB;
+  const int64_t ngroups = (nsuper + U - 1) / U;
+  for (int64_t it = 0; it < ngroups; ++it) {
+#pragma unroll
+    for (int j = 0; j < U; ++j) {
+      const int64_t S = it * U + j;
+      __builtin_amdgcn_sched_barrier(0);
+      store_x(xl + ((j + 1) & 1) * kSlot, xv[(j + 1) % XS]);   // super-step S+1
+      const lds_char* cur = xl + (j & 1) * kSlot;
+#pragma unroll
+      for (int sb = 0; sb < SPB; ++sb) {
+        const int64_t s = S * SPB + sb;
+        const int wi = (j * SPB + sb) % WD;
+        Frag2 b[NB];
+#pragma unroll
+        for (int k = 0; k < NB; ++k) {
+          const int t = 16 * k + r;
+          b[k].v[0] = __builtin_bit_cast(uint4, *reinterpret_cast<const lds_u32x4*>(cur + sb * kXBlock + xblock_at(t, q)));
+          b[k].v[1] = __builtin_bit_cast(uint4, *reinterpret_cast<const lds_u32x4*>(cur + sb * kXBlock + xblock_at(t, q + 4)));
+        }
+        const uint32_t keep = (s < T) ? 0xffffffffu : 0u;
+#pragma unroll
+        for (int jj = 0; jj < 2; ++jj) {
+          a[wi].v[jj].x &= keep; a[wi].v[jj].y &= keep;
+          a[wi].v[jj].z &= keep; a[wi].v[jj].w &= keep;
+        }
+        const Frag2 aa[1] = {a[wi]};
+        mma_step<1, NB>(aa, b, acc);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int sb = 0; sb < SPB; ++sb) {
+        const int64_t s = S * SPB + sb;
+        load_step(a[(j * SPB + sb) % WD], pa, off(s + WD));
+      }
+      load_x(xv[(j + 1) % XS], S + 1 + XS);
+      lds_barrier();
+    }
+  }
+  __builtin_amdgcn_sched_barrier(0);
+
+  // epilogue: rows 0-7 (gate) and 8-15 (up) of this wave's block, staged so
+  // that lane t holds its token's 8 gate and 8 up sums
+  float* st = stage[wid];
+#pragma unroll
+  for (int k = 0; k < NB; ++k)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) st[(4 * q + i) * kEpiLd + 16 * k + r] = acc[k][i];
+  __builtin_amdgcn_s_waitcnt(0xF | (3 << 14) | (7 << 4));   // lgkmcnt(0): own stores visible to own reads
+  const int t = lane;
   if (t >= n) return;
-  float gv[8], av[8];
+  float gv[8], uv[8], hv[8], ev[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
-    const int fr = fq + e;
-    const int tile_g = (fr >> 4) * NB + (t >> 4);
-    const int tile_u = (2 + (fr >> 4)) * NB + (t >> 4);
-    const int rr = fr & 15, cc = t & 15;
-    const int at = cc + 16 * (rr >> 2), reg = rr & 3;
-    float g = 0.0f, a = 0.0f;
-#pragma unroll
-    for (int w = 0; w < WAVES; ++w) {
-      g += part[w * kRingF + (tile_g * 4 + reg) * 64 + at];
-      a += part[w * kRingF + (tile_u * 4 + reg) * 64 + at];
-    }
-    gv[e] = g;
-    av[e] = a;
+    gv[e] = st[e * kEpiLd + t];
+    uv[e] = st[(8 + e) * kEpiLd + t];
   }
-  float ev[8];
   if (erow_ok) {
     const uint32_t wds[4] = {erow.x, erow.y, erow.z, erow.w};
 #pragma unroll
@@ -275,25 +326,23 @@ __global__ __launch_bounds__(256) void decode_gateup_kernel(
 #pragma unroll
     for (int i = 0; i < 8; ++i) ev[i] = 0.0f;
   }
-  uint32_t ph[4], pg[4], pu[4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    float hv[2], uv[2];
-#pragma unroll
-    for (int k = 0; k < 2; ++k) {
-      const int e = 2 * i + k;
-      uv[k] = av[e] + ev[e];
-      hv[k] = gv[e] * sigmoidf_(gv[e]) * uv[k];
-    }
-    ph[i] = static_cast<uint32_t>(f32_to_bf16(hv[0])) | (static_cast<uint32_t>(f32_to_bf16(hv[1])) << 16);
-    pg[i] = static_cast<uint32_t>(f32_to_bf16(gv[2 * i])) |
-            (static_cast<uint32_t>(f32_to_bf16(gv[2 * i + 1])) << 16);
-    pu[i] = static_cast<uint32_t>(f32_to_bf16(uv[0])) | (static_cast<uint32_t>(f32_to_bf16(uv[1])) << 16);
+  for (int e = 0; e < 8; ++e) {
+    uv[e] += ev[e];
+    hv[e] = gv[e] * sigmoidf_(gv[e]) * uv[e];
   }
-  const int64_t o = static_cast<int64_t>(t) * f + f0 + fq;
-  *reinterpret_cast<uint4*>(h + o) = make_uint4(ph[0], ph[1], ph[2], ph[3]);
-  if (g_out) *reinterpret_cast<uint4*>(g_out + o) = make_uint4(pg[0], pg[1], pg[2], pg[3]);
-  if (u_out) *reinterpret_cast<uint4*>(u_out + o) = make_uint4(pu[0], pu[1], pu[2], pu[3]);
+  auto pack = [](const float (&v)[8]) {
+    uint4 o;
+    o.x = static_cast<uint32_t>(f32_to_bf16(v[0])) | (static_cast<uint32_t>(f32_to_bf16(v[1])) << 16);
+    o.y = static_cast<uint32_t>(f32_to_bf16(v[2])) | (static_cast<uint32_t>(f32_to_bf16(v[3])) << 16);
+    o.z = static_cast<uint32_t>(f32_to_bf16(v[4])) | (static_cast<uint32_t>(f32_to_bf16(v[5])) << 16);
+    o.w = static_cast<uint32_t>(f32_to_bf16(v[6])) | (static_cast<uint32_t>(f32_to_bf16(v[7])) << 16);
+    return o;
+  };
+  const int64_t o = static_cast<int64_t>(t) * f + f0;
+  *reinterpret_cast<uint4*>(h + o) = pack(hv);
+  if (g_out) *reinterpret_cast<uint4*>(g_out + o) = pack(gv);
+  if (u_out) *reinterpret_cast<uint4*>(u_out + o) = pack(uv);
 }
 
 // Partial y over one K split: partial[ks][t][n0 + c] (fp32) for the 16*NA
@@ -388,14 +437,15 @@ size_t decode_down_workspace_bytes(int64_t n, int64_t d) {
 }
 
 // Launch shapes of the two decode kernels.
+// (gate/up: deeper prefetch, 2 or 4 steps per barrier and the earlier
+// d_model split over the waves with a partial-sum fold all measured slower.)
 struct DecodeConfig {
-  int gu_slots;   // steps in flight per wave in the gate/up kernel (2 or 3)
   int dn_shape;   // down kernel shape: 1 (32 outputs, 4 splits), 2 (64, 8), 3 (64, 4), 4 (128, 8)
 };
 // Measured best on MI355X for d_model 2048 / d_ff 8192, batch 64.
-static DecodeConfig g_decode_cfg = {2, 2};
+static DecodeConfig g_decode_cfg = {2};
 
-void decode_set_config(int gu_slots, int dn_shape) { g_decode_cfg = {gu_slots, dn_shape}; }
+void decode_set_config(int dn_shape) { g_decode_cfg = {dn_shape}; }
 
 hipError_t decode_gateup(int64_t n, int64_t d, int64_t f, const void* x, const void* wg,
                          const void* wu, const void* rows, int64_t n_rows,
@@ -407,8 +457,7 @@ hipError_t decode_gateup(int64_t n, int64_t d, int64_t f, const void* x, const v
         static_cast<const uint16_t*>(wu), static_cast<const uint16_t*>(rows), n_rows, row_index,
         static_cast<uint16_t*>(h), static_cast<uint16_t*>(g_out), static_cast<uint16_t*>(u_out), err);
   };
-  if (g_decode_cfg.gu_slots >= 3) go(decode_gateup_kernel<3>);
-  else go(decode_gateup_kernel<2>);
+  go(decode_gateup_fs_kernel<4, 1>);
   return hipGetLastError();
 }
 
