@@ -75,33 +75,42 @@ constexpr int kXBlock = 64 * 128;
 __device__ __forceinline__ int xblock_at(int t, int c) { return t * 128 + ((c ^ ((t >> 1) & 7)) << 4); }
 
 // One wave's 16 weight rows (pa: the lane's bytes at step 0) times the
-// activation of at most 64 tokens over macro steps [s0, s1), with the four
-// waves of the workgroup streaming the same steps: the activation of each
-// step (64 tokens x 128 bytes, act[t]: token t's row) is loaded once per
-// workgroup as whole cache lines (two 1 KB loads per wave: tokens
-// 16 wid + l / 8 and 16 wid + 8 + l / 8, chunk l % 8), written to one of two
-// LDS slots (`xl`, 2 x kXBlock bytes) and read by all four waves; one barrier
-// per step hands a slot over.  Weights and activations are loaded WD steps
-// ahead (8 + 8 registers per step): loads complete in issue order, so waiting
-// for a step's activation also waits for every weight load issued before it.
-// `after_prologue` runs once the first steps are in flight.
-template <int WD, typename Hook>
+// activation of at most 64 tokens over macro steps [s0, s1).  The workgroup
+// has 4 KH waves: waves w and w + 4 k (k < KH) stream the same 16 rows over
+// KH parts of the K range (part k = wid / 4), and the four waves of one part
+// share its activation: each step's block (64 tokens x 128 bytes, act[t]:
+// token t's row) is loaded once per part as whole cache lines (two 1 KB loads
+// per wave: tokens 16 (wid % 4) + l / 8 and 16 (wid % 4) + 8 + l / 8, chunk
+// l % 8), written to one of two LDS slots (`xl`, 2 x KH x kXBlock bytes) and
+// read by the part's four waves; one barrier per step hands a slot over.
+// Every wave runs the same number of steps, `len_max` (waves with fewer read
+// their last step again with zeroed weights), so the barriers match.
+// Weights and activations are loaded WD steps ahead (8 + 8 registers per
+// step): loads complete in issue order, so waiting for a step's activation
+// also waits for every weight load issued before it.  `after_prologue` runs
+// once the first steps are in flight.
+template <int WD, int KH, typename Hook>
 __device__ __forceinline__ void stream_shared_act(const char* pa, const uint16_t* act, int64_t act_ld,
                                                   int n, lds_char* xl, int64_t s0, int64_t s1,
-                                                  f32x4_t (&acc)[4], Hook&& after_prologue) {
+                                                  int64_t len_max, f32x4_t (&acc)[4],
+                                                  Hook&& after_prologue) {
   constexpr int NB = 4;
   constexpr int U = WD % 2 == 0 ? WD : 2 * WD;          // unrolled steps (even: LDS slot parity)
+  constexpr int kSlot = KH * kXBlock;
   const int lane = threadIdx.x & 63;
   const int wid = threadIdx.x >> 6;
+  const int grp = wid & 3, part = wid >> 2;
   const int r = lane & 15, q = lane >> 4;
   const char* px[2];
   int wofs[2];
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
-    const int tt = 16 * wid + 8 * i + (lane >> 3);
+    const int tt = 16 * grp + 8 * i + (lane >> 3);
     px[i] = reinterpret_cast<const char*>(act + static_cast<int64_t>(min(tt, n - 1)) * act_ld) + (lane & 7) * 16;
-    wofs[i] = xblock_at(tt, lane & 7);
+    wofs[i] = part * kXBlock + xblock_at(tt, lane & 7);
   }
+  // steps past s1 (or an empty range) re-read a valid step: s1 - 1, or s0 - 1
+  // (the previous part's last step) when the range is empty
   auto off = [&](int64_t s) -> int64_t { return (s < s1 ? s : s1 - 1) * 128; };
   auto load_x = [&](uint4 (&dst)[2], int64_t s) {
 #pragma unroll
@@ -116,7 +125,7 @@ __device__ __forceinline__ void stream_shared_act(const char* pa, const uint16_t
   for (int k = 0; k < NB; ++k)
 #pragma unroll
     for (int i = 0; i < 4; ++i) acc[k][i] = 0.0f;
-  if (s1 <= s0) {
+  if (len_max <= 0) {   // uniform over the workgroup
     after_prologue();
     return;
   }
@@ -133,14 +142,14 @@ __device__ __forceinline__ void stream_shared_act(const char* pa, const uint16_t
   store_x(xl, x0);
   __syncthreads();
 
-  const int64_t ngroups = (s1 - s0 + U - 1) / U;
+  const int64_t ngroups = (len_max + U - 1) / U;
   for (int64_t it = 0; it < ngroups; ++it) {
 #pragma unroll
     for (int j = 0; j < U; ++j) {
       const int64_t s = s0 + it * U + j;
       __builtin_amdgcn_sched_barrier(0);
-      store_x(xl + ((j + 1) & 1) * kXBlock, xv[(j + 1) % WD]);   // step s+1
-      const lds_char* cur = xl + (j & 1) * kXBlock;
+      store_x(xl + ((j + 1) & 1) * kSlot, xv[(j + 1) % WD]);   // step s+1
+      const lds_char* cur = xl + (j & 1) * kSlot + part * kXBlock;
       Frag2 b[NB];
 #pragma unroll
       for (int k = 0; k < NB; ++k) {
@@ -169,49 +178,73 @@ __device__ __forceinline__ void stream_shared_act(const char* pa, const uint16_t
 // Stages one wave's 16-row x 64-token MFMA result so that lane t can read
 // row e of its token at st[e * kStageLd + t].
 constexpr int kStageLd = 65;
+template <bool ADD = false>
 __device__ __forceinline__ void stage_wave_rows(float* st, const f32x4_t (&acc)[4]) {
   const int lane = threadIdx.x & 63;
   const int r = lane & 15, q = lane >> 4;
 #pragma unroll
   for (int k = 0; k < 4; ++k)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) st[(4 * q + i) * kStageLd + 16 * k + r] = acc[k][i];
+    for (int i = 0; i < 4; ++i) {
+      float& e = st[(4 * q + i) * kStageLd + 16 * k + r];
+      if constexpr (ADD) e += acc[k][i];
+      else e = acc[k][i];
+    }
+}
+
+// Folds the KH parts of a workgroup's K range: the part-k waves (k >= 1) add
+// their sums into the staged rows of their row group in part order; on return
+// stage[wid % 4] holds the full sums and only part-0 waves go on.
+template <int KH>
+__device__ __forceinline__ bool fold_parts(float (*stage)[16 * kStageLd], const f32x4_t (&acc)[4]) {
+  const int wid = threadIdx.x >> 6;
+  const int grp = wid & 3, part = wid >> 2;
+  if (part == 0) stage_wave_rows(stage[grp], acc);
+#pragma unroll
+  for (int k = 1; k < KH; ++k) {
+    __syncthreads();
+    if (part == k) stage_wave_rows<true>(stage[grp], acc);
+  }
+  if constexpr (KH > 1) __syncthreads();
+  return part == 0;
 }
 
 // Gate/up for at most 64 tokens, features split over the waves: one
-// workgroup (4 waves) per 32 features; wave w owns the gate and up rows of
-// features 8w .. 8w+7 (one 16-row MFMA block: 8 gate rows, then 8 up rows)
-// over all of d_model, so no partial sums cross waves.
-template <int WD>
-__global__ __launch_bounds__(256) void decode_gateup_kernel(
+// workgroup (4 KH waves) per 32 features; wave w owns the gate and up rows of
+// features 8 (w % 4) .. +8 (one 16-row MFMA block: 8 gate rows, then 8 up
+// rows) over part w / 4 of d_model, and the KH parts are folded in LDS.
+template <int WD, int KH>
+__global__ __launch_bounds__(256 * KH) void decode_gateup_kernel(
     int n, int64_t d, int64_t f, const uint16_t* __restrict__ x, const uint16_t* __restrict__ wg,
     const uint16_t* __restrict__ wu, const uint16_t* __restrict__ rows, int64_t n_rows,
     const int32_t* __restrict__ row_index, uint16_t* __restrict__ h, uint16_t* __restrict__ g_out,
     uint16_t* __restrict__ u_out, int* err) {
-  __shared__ __attribute__((aligned(16))) char xs[2 * kXBlock];
+  __shared__ __attribute__((aligned(16))) char xs[2 * KH * kXBlock];
   __shared__ float stage[4][16 * kStageLd];
   const int lane = threadIdx.x & 63;
   const int wid = threadIdx.x >> 6;
+  const int grp = wid & 3, part = wid >> 2;
   const int r = lane & 15, q = lane >> 4;
-  const int64_t f0 = static_cast<int64_t>(blockIdx.x) * 32 + 8 * wid;   // this wave's features
+  const int64_t f0 = static_cast<int64_t>(blockIdx.x) * 32 + 8 * grp;   // this wave's features
   const char* pa = reinterpret_cast<const char*>(r < 8 ? wg + (f0 + r) * d : wu + (f0 + r - 8) * d) + q * 16;
+  const int64_t T = d / 64, len = (T + KH - 1) / KH;
+  const int64_t s0 = part * len < T ? part * len : T, s1 = s0 + len < T ? s0 + len : T;
   f32x4_t acc[4];
   // the epilogue's table row (lane = token, this wave's 8 features), fetched
   // once the stream is under way
   int64_t ri;
   bool erow_ok;
   uint4 erow;
-  stream_shared_act<WD>(pa, x, d, n, (lds_char*)(xs), 0, d / 64, acc, [&]() {
+  stream_shared_act<WD, KH>(pa, x, d, n, (lds_char*)(xs), s0, s1, len, acc, [&]() {
     ri = row_index[min(lane, n - 1)];
     erow_ok = ri >= 0 && ri < n_rows;
     erow = *reinterpret_cast<const uint4*>(erow_ok ? rows + ri * f + f0 : x);
   });
 
-  // epilogue: rows 0-7 (gate) and 8-15 (up) of this wave's block, staged so
-  // that lane t holds its token's 8 gate and 8 up sums (the wave reads back
-  // only what it wrote itself, so no barrier is needed)
-  float* st = stage[wid];
-  stage_wave_rows(st, acc);
+  // epilogue: rows 0-7 (gate) and 8-15 (up) of the row group's block, staged
+  // so that lane t holds its token's 8 gate and 8 up sums
+  if (!fold_parts<KH>(stage, acc)) return;
+  const float* st = stage[grp];
   const int t = lane;
   if (t >= n) return;
   float gv[8], uv[8], hv[8], ev[8];
@@ -251,28 +284,33 @@ __global__ __launch_bounds__(256) void decode_gateup_kernel(
   if (u_out) *reinterpret_cast<uint4*>(u_out + o) = pack(uv);
 }
 
-// Down projection for at most 64 tokens, d_ff split KS ways: workgroup
-// (output block b of 64, split ks) with wave w owning outputs 64 b + 16 w ..
-// +16 over the split's steps; writes partial[ks][t][n] in fp32.
-template <int WD, int KS>
-__global__ __launch_bounds__(256) void decode_down_kernel(int n, int64_t d, int64_t f,
-                                                             const uint16_t* __restrict__ h,
-                                                             const uint16_t* __restrict__ wd,
-                                                             float* __restrict__ partial) {
-  __shared__ __attribute__((aligned(16))) char xs[2 * kXBlock];
+// Down projection for at most 64 tokens, d_ff split KS ways over workgroups
+// and KH ways inside one: workgroup (output block b of 64, split ks) with
+// wave w owning outputs 64 b + 16 (w % 4) .. +16 over part w / 4 of the
+// split's steps; writes partial[ks][t][n] in fp32.
+template <int WD, int KS, int KH>
+__global__ __launch_bounds__(256 * KH) void decode_down_kernel(int n, int64_t d, int64_t f,
+                                                               const uint16_t* __restrict__ h,
+                                                               const uint16_t* __restrict__ wd,
+                                                               float* __restrict__ partial) {
+  __shared__ __attribute__((aligned(16))) char xs[2 * KH * kXBlock];
   __shared__ float stage[4][16 * kStageLd];
   const int lane = threadIdx.x & 63;
   const int wid = threadIdx.x >> 6;
+  const int grp = wid & 3, part = wid >> 2;
   const int r = lane & 15, q = lane >> 4;
-  const int64_t n0 = static_cast<int64_t>(blockIdx.x) * 64 + 16 * wid;
+  const int64_t n0 = static_cast<int64_t>(blockIdx.x) * 64 + 16 * grp;
   const int ks = blockIdx.y;
   const int64_t T = f / 64;
-  const int64_t s0 = T * ks / KS, s1 = T * (ks + 1) / KS;
+  const int64_t k0 = T * ks / KS, k1 = T * (ks + 1) / KS;
+  const int64_t len = (k1 - k0 + KH - 1) / KH;
+  const int64_t s0 = k0 + part * len < k1 ? k0 + part * len : k1;
+  const int64_t s1 = s0 + len < k1 ? s0 + len : k1;
   const char* pa = reinterpret_cast<const char*>(wd + (n0 + r) * f) + q * 16;
   f32x4_t acc[4];
-  stream_shared_act<WD>(pa, h, f, n, (lds_char*)(xs), s0, s1, acc, []() {});
-  float* st = stage[wid];
-  stage_wave_rows(st, acc);
+  stream_shared_act<WD, KH>(pa, h, f, n, (lds_char*)(xs), s0, s1, len, acc, []() {});
+  if (!fold_parts<KH>(stage, acc)) return;
+  const float* st = stage[grp];
   const int t = lane;
   if (t >= n) return;
   float* dst = partial + (static_cast<int64_t>(ks) * n + t) * d + n0;
@@ -314,30 +352,36 @@ size_t decode_down_workspace_bytes(int64_t n, int64_t d) {
 
 // Launch shapes of the two decode kernels.
 // Launch shapes (measured on MI355X for d_model 2048 / d_ff 8192, batch 64):
-// four steps in flight per wave, d_ff split 8 ways in the down projection.
+// four steps in flight per wave; gate/up on 8 waves (d_model in two parts),
+// down on 4 waves with d_ff split 8 ways over workgroups.
 // Deeper prefetch, 2 or 4 steps per barrier, 4 splits, and the earlier
 // layouts that split d_model (or d_ff) over the waves of a workgroup and
 // folded their partial sums in LDS all measured slower.
 constexpr int kDecodeAhead = 4;
 constexpr int kDownSplit = 8;
+constexpr int kGateUpParts = 2;   // d_model split in two inside a gate/up workgroup (8 waves)
+constexpr int kDownParts = 1;
 static_assert(kDownSplit <= kDownSplitMax, "down partials fit the workspace");
 
 hipError_t decode_gateup(int64_t n, int64_t d, int64_t f, const void* x, const void* wg,
                          const void* wu, const void* rows, int64_t n_rows,
                          const int32_t* row_index, void* h, void* g_out, void* u_out,
                          hipStream_t s, int* err) {
-  decode_gateup_kernel<kDecodeAhead><<<dim3(static_cast<unsigned>(f / 32)), dim3(256), 0, s>>>(
-      static_cast<int>(n), d, f, static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(wg),
-      static_cast<const uint16_t*>(wu), static_cast<const uint16_t*>(rows), n_rows, row_index,
-      static_cast<uint16_t*>(h), static_cast<uint16_t*>(g_out), static_cast<uint16_t*>(u_out), err);
+  auto go = [&](auto kern, int threads) {
+    kern<<<dim3(static_cast<unsigned>(f / 32)), dim3(threads), 0, s>>>(
+        static_cast<int>(n), d, f, static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(wg),
+        static_cast<const uint16_t*>(wu), static_cast<const uint16_t*>(rows), n_rows, row_index,
+        static_cast<uint16_t*>(h), static_cast<uint16_t*>(g_out), static_cast<uint16_t*>(u_out), err);
+  };
+  go(decode_gateup_kernel<kDecodeAhead, kGateUpParts>, 256 * kGateUpParts);
   return hipGetLastError();
 }
 
 hipError_t decode_down(int64_t n, int64_t d, int64_t f, const void* h, const void* wd, void* y,
                        int out_dtype, void* ws, hipStream_t s) {
   float* partial = static_cast<float*>(ws);
-  decode_down_kernel<kDecodeAhead, kDownSplit>
-      <<<dim3(static_cast<unsigned>(d / 64), kDownSplit), dim3(256), 0, s>>>(
+  decode_down_kernel<kDecodeAhead, kDownSplit, kDownParts>
+      <<<dim3(static_cast<unsigned>(d / 64), kDownSplit), dim3(256 * kDownParts), 0, s>>>(
           static_cast<int>(n), d, f, static_cast<const uint16_t*>(h), static_cast<const uint16_t*>(wd),
           partial);
   const int64_t count = n * d;
