@@ -62,8 +62,9 @@ def source_sha(*names) -> str:
 
 
 def traffic_from_profile(kernel_key: str, sha: str):
-    """HBM bytes per launch from the committed counter summary, if it was taken
-    on the current kernel source; otherwise None."""
+    """HBM bytes per launch of one kernel on one workload ("kernel/workload")
+    from the committed counter summary, if it was taken on the current kernel
+    source; otherwise None."""
     path = os.path.join(PROFILES, "traffic.json")
     if not os.path.exists(path):
         return None
@@ -205,7 +206,7 @@ def run_decode(torch, st, w, steps, warmup):
             "kernel": "decode_gateup_kernel (staple_ffn_gate_up, 64 tokens)",
             "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": achieved / HBM_PEAK_GBS,
-            "traffic": traffic_from_profile("decode_gate_up", sha),
+            "traffic": traffic_from_profile(f"decode_gate_up/{w.name}", sha),
             "avg_launch_us": gu_us, "algorithmic_bytes_per_launch": gu_bytes,
         },
     }
@@ -349,7 +350,8 @@ def run_train(torch, st, w, steps, warmup):
             "kernel": "gemm_kernel<bf16,GateUp> (staple_ffn_gate_up, training batch)",
             "bound": "mfma", "achieved": achieved, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
             "frac": achieved / BF16_PEAK_TFLOPS,
-            "traffic": traffic_from_profile("train_gate_up", source_sha("gemm.hip", "common.h")),
+            "traffic": traffic_from_profile(f"train_gate_up/{w.name}",
+                                            source_sha("gemm.hip", "common.h")),
             "avg_launch_us": gu_us, "algorithmic_flops_per_launch": gu_flops,
         },
     }, T
