@@ -454,13 +454,22 @@ def run_offload_decode(torch, st, w, steps, warmup):
         dd = st.staple_dedup(ids, v, out=dd_out)
         lk = st.staple_cache_lookup(dd["uniq"], dd["n_unique"], O["id_to_slot"], out=lk_out)
         m = _miss_list_to_host(torch, lk, miss_host)
-        for l, lay in enumerate(layers):
+        # layer l+1's miss rows are packed on the host and sent on the side
+        # stream right after layer l's FFN is queued, so both overlap it
+        side.wait_stream(main)
+
+        def stage(l):
             st.staple_stage_misses(O["tables"][l], miss_host, m, staging[l], dev_miss[l], stream=side)
             events[l].record(side)
+
+        stage(0)
+        for l, lay in enumerate(layers):
             main.wait_event(events[l])
             st.staple_assemble_rows(O["cache_rows"][l], dev_miss[l], lk["code"], dd["n_unique"], out=R)
             st.staple_ffn_fwd(lay["x"], lay["w_gate"], lay["w_up"], lay["w_down"], R, dd["inv"],
                               out={"y": lay["y"]}, workspace=ws)
+            if l + 1 < L:
+                stage(l + 1)
         return m
 
     for _ in range(warmup):
@@ -480,8 +489,9 @@ def run_offload_decode(torch, st, w, steps, warmup):
             "n_unique": n_unique, "misses_per_layer": m, "cache_capacity": w.cache_capacity,
             "token_hit_rate": None, "pcie_bytes_per_step": m * f * 2 * L,
             "note": "eager step: dedup + cache probe once, one host sync for the miss list, "
-                    "per layer host pack + H2D on a side stream, cache/miss row assembly, "
-                    "gate/up, down"}
+                    "per layer: wait for its H2D, cache/miss row assembly, gate/up, down, then "
+                    "the next layer's host pack + H2D on a side stream (overlapping this "
+                    "layer's FFN)"}
 
 
 def run_offload_train(torch, st, w, steps, warmup):
@@ -495,18 +505,25 @@ def run_offload_train(torch, st, w, steps, warmup):
     lk_out = {k: torch.empty(n, **i32) for k in ("code", "miss_uidx", "miss_ids")}
     lk_out["n_miss"] = torch.empty(1, **i32)
     miss_host = torch.empty(n, dtype=torch.int32, pin_memory=True)
+    counts_host = torch.empty(2, dtype=torch.int32, pin_memory=True)
+    sp_out = {k: torch.empty(n, **i32) for k in ("hit_pos", "miss_pos", "tok_row")}
+    sp_out["counts"] = torch.empty(2, **i32)
     staging = torch.empty(n, f, dtype=torch.bfloat16, pin_memory=True)
     dev_miss = torch.empty(n, f, dtype=torch.bfloat16, device=dev)
     side = torch.cuda.Stream()
     main = torch.cuda.current_stream()
     ev_copy0, ev_copy1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     ev_ready = torch.cuda.Event()
-    stats = {"pack_s": 0.0, "copy_ms": 0.0}
+    stats = {"pack_s": 0.0, "copy_ms": 0.0, "hit_tokens": 0}
 
     def step(measure=False):
         dd = st.staple_dedup(T["ids"], v, out=T["dd"], workspace=T["dd_ws"])
         lk = st.staple_cache_lookup(dd["uniq"], dd["n_unique"], O["id_to_slot"], out=lk_out)
-        m = _miss_list_to_host(torch, lk, miss_host)
+        sp = st.staple_split_tokens(dd["inv"], lk["code"], dd["n_unique"], out=sp_out)
+        counts_host.copy_(sp["counts"], non_blocking=True)
+        m = _miss_list_to_host(torch, lk, miss_host)        # one host sync for both
+        n_hit, n_miss_tok = int(counts_host[0]), int(counts_host[1])
+        stats["hit_tokens"] = n_hit
         side.wait_stream(main)
         t0 = time.perf_counter()
         with torch.cuda.stream(side):
@@ -516,10 +533,13 @@ def run_offload_train(torch, st, w, steps, warmup):
             ev_copy1.record(side)
         stats["pack_s"] += time.perf_counter() - t0
         ev_ready.record(side)
-        main.wait_event(ev_ready)
-        st.staple_assemble_rows(O["cache_rows"][0], dev_miss, lk["code"], dd["n_unique"], out=T["rows"])
         fw = T["fwd"]
-        st.staple_ffn_gate_up(T["x"], T["w_gate"], T["w_up"], T["rows"], dd["inv"], fw["h"], fw["g"], fw["u"])
+        # the tokens whose rows are cached run while the miss rows are in flight
+        st.staple_ffn_gate_up_tokens(sp["hit_pos"], n_hit, T["x"], T["w_gate"], T["w_up"],
+                                     O["cache_rows"][0], sp["tok_row"], fw["h"], fw["g"], fw["u"])
+        main.wait_event(ev_ready)
+        st.staple_ffn_gate_up_tokens(sp["miss_pos"], n_miss_tok, T["x"], T["w_gate"], T["w_up"],
+                                     dev_miss, sp["tok_row"], fw["h"], fw["g"], fw["u"])
         st.staple_ffn_down(fw["h"], T["w_down"], fw["y"])
         st.staple_ffn_bwd_table_grad(T["dy"], T["x"], T["w_gate"], T["w_up"], T["w_down"], fw["g"],
                                      fw["u"], fw["h"], dd["sorted_pos"], dd["seg_start"],
@@ -546,9 +566,12 @@ def run_offload_train(torch, st, w, steps, warmup):
             "cache_capacity": w.cache_capacity,
             "host_pack_ms": stats["pack_s"] / steps * 1e3,
             "h2d_ms": copy, "h2d_gb_s": m * f * 2 / (copy * 1e-3) / 1e9,
-            "note": "eager step: dedup + cache probe, one host sync for the miss list, host "
-                    "pack + H2D of the miss rows on a side stream (the main stream waits for "
-                    "it before assembling R: the copy is not yet hidden), forward, backward"}
+            "token_hit_rate": stats["hit_tokens"] / n,
+            "note": "eager step: dedup + cache probe + token split, one host sync for the miss "
+                    "list and the split counts, host pack + H2D of the miss rows on a side "
+                    "stream while the gate/up GEMM of the cached tokens runs (rows read from "
+                    "the cache slots), then the missed tokens' gate/up (rows from the staged "
+                    "misses), down, backward"}
 
 # ----------------------------------------------------------------------------
 def copy_probe(torch):

@@ -144,6 +144,24 @@ staple_status_t staple_cache_lookup(const int32_t* uniq, const int32_t* n_unique
                                     int32_t* code, int32_t* miss_uidx, int32_t* miss_ids,
                                     int32_t* n_miss, void* stream);
 
+/* Splits the batch's token positions by cache outcome, for a gate/up that
+ * runs the cached tokens while the miss rows are in flight.
+ * Inputs : inv int32[n_tokens] (token -> unique index, from staple_dedup),
+ *          code int32[max_unique] and n_unique (from staple_cache_lookup).
+ * Outputs: hit_pos  int32[n_tokens]: positions of tokens whose row is cached,
+ *                   ascending (first counts[0]);
+ *          miss_pos int32[n_tokens]: positions of the other tokens, ascending
+ *                   (first counts[1]);
+ *          tok_row  int32[n_tokens]: each token's row in its source block,
+ *                   the cache slot for a hit, the miss index for a miss;
+ *          counts   int32[2] device: {hits, misses}.
+ * A token whose inv entry is outside [0, n_unique) sets the device error
+ * word and is listed with the hits with tok_row -1.  max_unique <= n_tokens. */
+staple_status_t staple_split_tokens(const int32_t* inv, int64_t n_tokens, const int32_t* code,
+                                   const int32_t* n_unique, int64_t max_unique, int32_t* hit_pos,
+                                   int32_t* miss_pos, int32_t* tok_row, int32_t* counts,
+                                   void* stream);
+
 /* Miss staging (STAPLE retrieval-path table, Prefill row: only cache-miss rows
  * come from the CPU, packed into pinned host buffers and sent with bulk
  * asynchronous host-to-device copies).  Runs on the calling thread: packs
@@ -219,6 +237,24 @@ staple_status_t staple_ffn_gate_up(int64_t n_tokens, int64_t d_model, int64_t d_
                                    const void* x, const void* w_gate, const void* w_up,
                                    const void* rows, int64_t n_rows, const int32_t* row_index,
                                    void* h, void* save_g, void* save_u, void* stream);
+
+/* Gate/up over a subset of the batch's tokens, so that the tokens whose
+ * table rows are cached can run while the miss rows are still being copied
+ * from host memory (STAPLE retrieval-path table: misses staged on a side
+ * stream, overlapped with the FFN).  Computes the rows token_pos[0 .. n_sel)
+ * of h (and g, u) exactly as staple_ffn_gate_up computes them for the whole
+ * batch; x, h, g, u are [n_tokens x ...] and row_index is indexed by token
+ * position, so the two halves of a split batch can read their table rows from
+ * different blocks (cache slots, staged misses).
+ * token_pos: device int32[n_sel]; an entry outside [0, n_tokens) sets the
+ * device error word and that token is neither read nor written. */
+staple_status_t staple_ffn_gate_up_tokens(int64_t n_sel, const int32_t* token_pos,
+                                          int64_t n_tokens, int64_t d_model, int64_t d_ff,
+                                          int32_t dtype, const void* x, const void* w_gate,
+                                          const void* w_up, const void* rows, int64_t n_rows,
+                                          const int32_t* row_index, void* h, void* save_g,
+                                          void* save_u, void* stream);
+
 size_t staple_ffn_down_workspace_bytes(int64_t n_tokens, int64_t d_model, int64_t d_ff,
                                        int32_t dtype);
 staple_status_t staple_ffn_down(int64_t n_tokens, int64_t d_model, int64_t d_ff, int32_t dtype,

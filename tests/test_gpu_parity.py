@@ -157,6 +157,79 @@ def test_compact_rows_hit_and_miss_paths_are_bit_identical(st, dev):
         np.testing.assert_array_equal(got, expect, err_msg=f"capacity {capacity}")
 
 
+# ---------------------------------------------------- cache-split gate/up
+@pytest.mark.parametrize("n,d,f,dtype,capacity", [
+    (1000, 256, 512, "bf16", 0), (1000, 256, 512, "bf16", 120), (1000, 256, 512, "bf16", 2000),
+    (64, 256, 512, "bf16", 60), (20, 128, 256, "bf16", 2000), (37, 128, 256, "bf16", 0),
+    (300, 128, 256, "f32", 90)])
+def test_split_gate_up_matches_whole_batch_bitwise(st, dev, n, d, f, dtype, capacity):
+    """The cached tokens' gate/up (rows from the cache slots) and the missed
+    tokens' gate/up (rows from the staged misses) together give the bits of
+    one gate/up over the whole batch with the assembled rows E[uniq]; the
+    split lists are the oracle's dedup and cache probe, token by token."""
+    import torch
+    vocab = 2000
+    _log(f"split gate/up n={n} d={d} f={f} {dtype} capacity={capacity}")
+    inp = S.host_layer_inputs(n, d, f, vocab, dtype=dtype, seed=60 + n + capacity)
+    x, wg, wu, tab = (to_dev(getattr(inp, k), dtype, dev) for k in ("x", "w_gate", "w_up", "table"))
+    ids = torch.from_numpy(inp.ids).to(dev)
+    dd = st.staple_dedup(ids, vocab)
+    counts = st.staple_cache_count(torch.from_numpy(S.zipf_ids(20_000, vocab, 8)).to(dev), vocab)
+    i2s, s2i = st.staple_cache_build(counts, capacity)
+    cache_rows = st.staple_cache_fill(tab, s2i, capacity)
+    lk = st.staple_cache_lookup(dd["uniq"], dd["n_unique"], i2s)
+    sp = st.staple_split_tokens(dd["inv"], lk["code"], dd["n_unique"])
+    torch.cuda.synchronize()
+    m = int(lk["n_miss"].item())
+    miss_rows = st.staple_gather_rows(tab, lk["miss_ids"], lk["n_miss"])
+    # oracle's view of the split
+    uniq, inv, _, _ = O.dedup(inp.ids)
+    i2s_np = i2s.cpu().numpy()
+    code, _ = O.cache_lookup(uniq, i2s_np)
+    tcode = np.asarray(code)[np.asarray(inv)]
+    hit_pos = np.nonzero(tcode >= 0)[0]
+    miss_pos = np.nonzero(tcode < 0)[0]
+    n_hit, n_miss = (int(v) for v in sp["counts"].cpu().numpy())
+    assert (n_hit, n_miss) == (len(hit_pos), len(miss_pos))
+    np.testing.assert_array_equal(sp["hit_pos"][:n_hit].cpu().numpy(), hit_pos)
+    np.testing.assert_array_equal(sp["miss_pos"][:n_miss].cpu().numpy(), miss_pos)
+    np.testing.assert_array_equal(sp["tok_row"][:n].cpu().numpy(),
+                                  np.where(tcode >= 0, tcode, -1 - tcode))
+    # whole batch with the assembled rows
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    rows = st.staple_gather_rows(tab, dd["uniq"], dd["n_unique"])
+    ref = {k: torch.empty(n, f, dtype=tdt, device=dev) for k in ("h", "g", "u")}
+    st.staple_ffn_gate_up(x, wg, wu, rows, dd["inv"], ref["h"], ref["g"], ref["u"])
+    # split: cached tokens first, then the misses
+    got = {k: torch.full((n, f), float("nan"), dtype=tdt, device=dev) for k in ("h", "g", "u")}
+    crow = cache_rows if capacity > 0 else torch.zeros(1, f, dtype=tdt, device=dev)
+    st.staple_ffn_gate_up_tokens(sp["hit_pos"], n_hit, x, wg, wu, crow, sp["tok_row"], got["h"],
+                                 got["g"], got["u"])
+    st.staple_ffn_gate_up_tokens(sp["miss_pos"], n_miss, x, wg, wu, miss_rows, sp["tok_row"],
+                                 got["h"], got["g"], got["u"])
+    torch.cuda.synchronize()
+    _no_device_error(st)
+    for k in ("h", "g", "u"):
+        assert torch.equal(got[k], ref[k]), f"{k} differs"
+
+
+def test_gate_up_tokens_out_of_range_position_is_flagged(st, dev):
+    """A token position outside the batch sets the device error word and
+    writes nothing (host-side range is not checked for device lists)."""
+    import torch
+    n, d, f, vocab = 100, 128, 256, 50
+    inp = S.host_layer_inputs(n, d, f, vocab, dtype="bf16", seed=5)
+    x, wg, wu, tab = (to_dev(getattr(inp, k), "bf16", dev) for k in ("x", "w_gate", "w_up", "table"))
+    ids = torch.from_numpy(inp.ids).to(dev)
+    for n_sel in (3, 80):     # decode kernel, tiled GEMM
+        pos = torch.tensor([0, n + 5, 2] + list(range(3, n_sel)), dtype=torch.int32, device=dev)[:n_sel]
+        h = torch.zeros(n, f, dtype=torch.bfloat16, device=dev)
+        st.staple_ffn_gate_up_tokens(pos, n_sel, x, wg, wu, tab, ids, h)
+        torch.cuda.synchronize()
+        assert st.staple_get_device_error() != 0      # reading it also clears it
+        assert torch.count_nonzero(h[n_sel:]) == 0 and torch.count_nonzero(h[1]) == 0
+
+
 # ---------------------------------------------------------------- FFN helpers
 def _run_layer(st, dev, inp, out_f32=True, freeze_up=False, backward=True, full_table=False):
     import torch

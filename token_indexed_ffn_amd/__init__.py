@@ -153,6 +153,22 @@ def staple_cache_lookup(uniq: torch.Tensor, n_unique: torch.Tensor, id_to_slot: 
     return out
 
 
+def staple_split_tokens(inv: torch.Tensor, code: torch.Tensor, n_unique: torch.Tensor, *,
+                        out: Optional[dict] = None, stream=None) -> dict:
+    """hit_pos, miss_pos, tok_row and counts {hits, misses} of the batch's tokens."""
+    _dev(inv, code, n_unique)
+    n = inv.numel()
+    max_unique = min(code.numel(), n)
+    if out is None:
+        out = {k: torch.empty(max(n, 1), dtype=torch.int32, device=inv.device)
+               for k in ("hit_pos", "miss_pos", "tok_row")}
+        out["counts"] = torch.empty(2, dtype=torch.int32, device=inv.device)
+    _check(lib().staple_split_tokens(_p(inv), n, _p(code), _p(n_unique), max_unique,
+                                     _p(out["hit_pos"]), _p(out["miss_pos"]), _p(out["tok_row"]),
+                                     _p(out["counts"]), _stream(stream)), "staple_split_tokens")
+    return out
+
+
 def staple_stage_misses(host_table: torch.Tensor, host_miss_ids: torch.Tensor, n_miss: int,
                         host_staging: torch.Tensor, dev_miss_rows: torch.Tensor,
                         stream=None) -> None:
@@ -227,6 +243,22 @@ def staple_ffn_gate_up(x: torch.Tensor, w_gate: torch.Tensor, w_up: torch.Tensor
     _check(lib().staple_ffn_gate_up(n, d, f, _dt(x), _p(x), _p(w_gate), _p(w_up), _p(rows),
                                     rows.shape[0], _p(row_index), _p(h), _p(save_g), _p(save_u),
                                     _stream(stream)), "staple_ffn_gate_up")
+    return h
+
+
+def staple_ffn_gate_up_tokens(token_pos: torch.Tensor, n_sel: int, x: torch.Tensor,
+                              w_gate: torch.Tensor, w_up: torch.Tensor, rows: torch.Tensor,
+                              row_index: torch.Tensor, h: torch.Tensor,
+                              save_g: Optional[torch.Tensor] = None,
+                              save_u: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """staple_ffn_gate_up for the tokens token_pos[:n_sel] only (rows of x, h, g, u)."""
+    _dev(token_pos, x, w_gate, w_up, rows, row_index, h, save_g, save_u)
+    n, d = x.shape
+    f = w_gate.shape[0]
+    _check(lib().staple_ffn_gate_up_tokens(int(n_sel), _p(token_pos), n, d, f, _dt(x), _p(x),
+                                           _p(w_gate), _p(w_up), _p(rows), rows.shape[0],
+                                           _p(row_index), _p(h), _p(save_g), _p(save_u),
+                                           _stream(stream)), "staple_ffn_gate_up_tokens")
     return h
 
 

@@ -29,6 +29,7 @@ _SIGS = {
     "staple_cache_build": (c_i32, [c_vp, c_i64, c_i64, c_vp, c_vp, c_vp, c_sz, c_vp]),
     "staple_cache_fill": (c_i32, [c_vp, c_i64, c_i64, c_i32, c_vp, c_i64, c_vp, c_vp]),
     "staple_cache_lookup": (c_i32, [c_vp, c_vp, c_i64, c_vp, c_i64, c_vp, c_vp, c_vp, c_vp, c_vp]),
+    "staple_split_tokens": (c_i32, [c_vp, c_i64, c_vp, c_vp, c_i64, c_vp, c_vp, c_vp, c_vp, c_vp]),
     "staple_stage_misses": (c_i32, [c_vp, c_i64, c_i64, c_i32, c_vp, c_i32, c_vp, c_vp, c_vp]),
     "staple_assemble_rows": (c_i32, [c_vp, c_i64, c_vp, c_i64, c_vp, c_vp, c_i64, c_i64, c_i32,
                                      c_vp, c_vp]),
@@ -38,6 +39,8 @@ _SIGS = {
                                c_i64, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_sz, c_vp]),
     "staple_ffn_gate_up": (c_i32, [c_i64, c_i64, c_i64, c_i32, c_vp, c_vp, c_vp, c_vp, c_i64, c_vp,
                                    c_vp, c_vp, c_vp, c_vp]),
+    "staple_ffn_gate_up_tokens": (c_i32, [c_i64, c_vp, c_i64, c_i64, c_i64, c_i32, c_vp, c_vp, c_vp,
+                                          c_vp, c_i64, c_vp, c_vp, c_vp, c_vp, c_vp]),
     "staple_ffn_down_workspace_bytes": (c_sz, [c_i64, c_i64, c_i64, c_i32]),
     "staple_ffn_down": (c_i32, [c_i64, c_i64, c_i64, c_i32, c_i32, c_vp, c_vp, c_vp, c_vp, c_sz,
                                 c_vp]),

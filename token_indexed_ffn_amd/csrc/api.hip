@@ -23,6 +23,10 @@ hipError_t launch_cache_build(const int64_t* counts, int64_t vocab, int64_t capa
 // kernels (rows.hip)
 hipError_t launch_cache_count(const int32_t* ids, int64_t n, int64_t vocab, int64_t* counts,
                               hipStream_t s, int* err);
+hipError_t launch_split_tokens(const int32_t* inv, int64_t n, const int32_t* code,
+                               const int32_t* n_unique, int64_t max_unique, int32_t* hit_pos,
+                               int32_t* miss_pos, int32_t* tok_row, int32_t* counts, hipStream_t s,
+                               int* err);
 hipError_t launch_cache_lookup(const int32_t* uniq, const int32_t* n_unique, int64_t max_unique,
                                const int32_t* id_to_slot, int64_t vocab, int32_t* code,
                                int32_t* miss_uidx, int32_t* miss_ids, int32_t* n_miss,
@@ -41,9 +45,10 @@ hipError_t launch_segment_sum(int dtype, const void* du, int64_t du_ld, int64_t 
                               int64_t max_unique, float* d_rows, void* ws, hipStream_t s, int* err);
 // kernels (gemm.hip)
 template <typename T>
-hipError_t gateup_fwd(int64_t n, int64_t d, int64_t f, const void* x, const void* wg,
-                      const void* wu, const void* rows, int64_t n_rows, const int32_t* row_index,
-                      void* h, void* g_out, void* u_out, hipStream_t s, int* err);
+hipError_t gateup_fwd(int64_t n_sel, const int32_t* pos, int64_t n_tokens, int64_t d, int64_t f,
+                      const void* x, const void* wg, const void* wu, const void* rows,
+                      int64_t n_rows, const int32_t* row_index, void* h, void* g_out, void* u_out,
+                      hipStream_t s, int* err);
 template <typename T>
 hipError_t down_fwd(int64_t n, int64_t d, int64_t f, const void* h, const void* wd, void* y,
                     int out_dtype, hipStream_t s);
@@ -63,10 +68,10 @@ hipError_t dwgu_bwd(int64_t n, int64_t d, int64_t f, const void* dgu, const void
 // kernels (decode.hip)
 bool decode_eligible(int64_t n, int64_t d, int64_t f, int dtype);
 size_t decode_down_workspace_bytes(int64_t n, int64_t d);
-hipError_t decode_gateup(int64_t n, int64_t d, int64_t f, const void* x, const void* wg,
-                         const void* wu, const void* rows, int64_t n_rows,
-                         const int32_t* row_index, void* h, void* g_out, void* u_out,
-                         hipStream_t s, int* err);
+hipError_t decode_gateup(int64_t n, const int32_t* pos, int64_t n_tokens, int64_t d, int64_t f,
+                         const void* x, const void* wg, const void* wu, const void* rows,
+                         int64_t n_rows, const int32_t* row_index, void* h, void* g_out,
+                         void* u_out, hipStream_t s, int* err);
 hipError_t decode_down(int64_t n, int64_t d, int64_t f, const void* h, const void* wd, void* y,
                        int out_dtype, void* ws, hipStream_t s);
 
@@ -214,6 +219,19 @@ staple_status_t staple_cache_lookup(const int32_t* uniq, const int32_t* n_unique
   return STAPLE_OK;
 }
 
+staple_status_t staple_split_tokens(const int32_t* inv, int64_t n_tokens, const int32_t* code,
+                                   const int32_t* n_unique, int64_t max_unique, int32_t* hit_pos,
+                                   int32_t* miss_pos, int32_t* tok_row, int32_t* counts,
+                                   void* stream) {
+  REQUIRE(n_tokens >= 0 && n_tokens <= 0x7fffffffll && max_unique >= 0 && max_unique <= n_tokens);
+  REQUIRE(n_unique && counts);
+  REQUIRE(n_tokens == 0 || (inv && code && hit_pos && miss_pos && tok_row));
+  GET_ERR(err);
+  HIPCALL(launch_split_tokens(inv, n_tokens, code, n_unique, max_unique, hit_pos, miss_pos, tok_row,
+                              counts, S(stream), err));
+  return STAPLE_OK;
+}
+
 staple_status_t staple_stage_misses(const void* host_table, int64_t vocab, int64_t d_ff,
                                     int32_t dtype, const int32_t* host_miss_ids, int32_t n_miss,
                                     void* host_staging, void* dev_miss_rows, void* stream) {
@@ -296,20 +314,21 @@ size_t staple_ffn_fwd_workspace_bytes(int64_t n, int64_t d, int64_t f, int32_t d
          staple_ffn_down_workspace_bytes(n, d, f, dtype);
 }
 
-static staple_status_t gate_up_impl(int64_t n, int64_t d, int64_t f, int32_t dtype,
-                                    const void* x, const void* w_gate, const void* w_up,
-                                    const void* rows, int64_t n_rows, const int32_t* row_index,
-                                    void* h, void* save_g, void* save_u, hipStream_t s) {
+static staple_status_t gate_up_impl(int64_t n_sel, const int32_t* pos, int64_t n_tokens,
+                                    int64_t d, int64_t f, int32_t dtype, const void* x,
+                                    const void* w_gate, const void* w_up, const void* rows,
+                                    int64_t n_rows, const int32_t* row_index, void* h,
+                                    void* save_g, void* save_u, hipStream_t s) {
   GET_ERR(err);
-  if (decode_eligible(n, d, f, dtype))
-    HIPCALL(decode_gateup(n, d, f, x, w_gate, w_up, rows, n_rows, row_index, h, save_g, save_u, s,
-                          err));
+  if (decode_eligible(n_sel, d, f, dtype))
+    HIPCALL(decode_gateup(n_sel, pos, n_tokens, d, f, x, w_gate, w_up, rows, n_rows, row_index, h,
+                          save_g, save_u, s, err));
   else if (dtype == STAPLE_BF16)
-    HIPCALL(gateup_fwd<bf16_t>(n, d, f, x, w_gate, w_up, rows, n_rows, row_index, h, save_g,
-                               save_u, s, err));
+    HIPCALL(gateup_fwd<bf16_t>(n_sel, pos, n_tokens, d, f, x, w_gate, w_up, rows, n_rows,
+                               row_index, h, save_g, save_u, s, err));
   else
-    HIPCALL(gateup_fwd<float>(n, d, f, x, w_gate, w_up, rows, n_rows, row_index, h, save_g,
-                              save_u, s, err));
+    HIPCALL(gateup_fwd<float>(n_sel, pos, n_tokens, d, f, x, w_gate, w_up, rows, n_rows, row_index,
+                              h, save_g, save_u, s, err));
   return STAPLE_OK;
 }
 
@@ -332,8 +351,24 @@ staple_status_t staple_ffn_gate_up(int64_t n, int64_t d, int64_t f, int32_t dtyp
   if (n == 0) return STAPLE_OK;
   REQUIRE(x && row_index && h && aligned16(x) && aligned16(h));
   REQUIRE((!save_g || aligned16(save_g)) && (!save_u || aligned16(save_u)));
-  return gate_up_impl(n, d, f, dtype, x, w_gate, w_up, rows, n_rows, row_index, h, save_g, save_u,
-                      S(stream));
+  return gate_up_impl(n, nullptr, n, d, f, dtype, x, w_gate, w_up, rows, n_rows, row_index, h,
+                      save_g, save_u, S(stream));
+}
+
+staple_status_t staple_ffn_gate_up_tokens(int64_t n_sel, const int32_t* token_pos, int64_t n_tokens,
+                                          int64_t d, int64_t f, int32_t dtype, const void* x,
+                                          const void* w_gate, const void* w_up, const void* rows,
+                                          int64_t n_rows, const int32_t* row_index, void* h,
+                                          void* save_g, void* save_u, void* stream) {
+  if (!ffn_shape_ok(n_tokens, d, f, dtype)) return STAPLE_ERR_UNSUPPORTED;
+  REQUIRE(n_sel >= 0 && n_sel <= n_tokens);
+  REQUIRE(w_gate && w_up && rows && n_rows >= 1);
+  REQUIRE(aligned16(w_gate) && aligned16(w_up) && aligned16(rows));
+  if (n_sel == 0) return STAPLE_OK;
+  REQUIRE(token_pos && x && row_index && h && aligned16(x) && aligned16(h));
+  REQUIRE((!save_g || aligned16(save_g)) && (!save_u || aligned16(save_u)));
+  return gate_up_impl(n_sel, token_pos, n_tokens, d, f, dtype, x, w_gate, w_up, rows, n_rows,
+                      row_index, h, save_g, save_u, S(stream));
 }
 
 staple_status_t staple_ffn_down(int64_t n, int64_t d, int64_t f, int32_t dtype, int32_t out_dtype,
@@ -367,8 +402,8 @@ staple_status_t staple_ffn_fwd(int64_t n, int64_t d, int64_t f, int32_t dtype, i
   void* h = save_h ? save_h : ws;
   void* down_ws = static_cast<char*>(ws) + align_up(static_cast<size_t>(n) * f * elem_bytes(dtype), 256);
   hipStream_t s = S(stream);
-  staple_status_t st = gate_up_impl(n, d, f, dtype, x, w_gate, w_up, rows, n_rows, row_index, h,
-                                    save_g, save_u, s);
+  staple_status_t st = gate_up_impl(n, nullptr, n, d, f, dtype, x, w_gate, w_up, rows, n_rows,
+                                    row_index, h, save_g, save_u, s);
   if (st != STAPLE_OK) return st;
   return down_impl(n, d, f, dtype, out_dtype, h, w_down, y, down_ws, s);
 }

@@ -81,18 +81,19 @@ __device__ __forceinline__ int xblock_at(int t, int c) { return t * 128 + ((c ^ 
 // share its activation: each step's block (64 tokens x 128 bytes, act[t]:
 // token t's row) is loaded once per part as whole cache lines (two 1 KB loads
 // per wave: tokens 16 (wid % 4) + l / 8 and 16 (wid % 4) + 8 + l / 8, chunk
-// l % 8), written to one of two LDS slots (`xl`, 2 x KH x kXBlock bytes) and
-// read by the part's four waves; one barrier per step hands a slot over.
+// l % 8; act_row(t) gives the row of act that holds token t), written to one
+// of two LDS slots (`xl`, 2 x KH x kXBlock bytes) and read by the part's four
+// waves; one barrier per step hands a slot over.
 // Every wave runs the same number of steps, `len_max` (waves with fewer read
 // their last step again with zeroed weights), so the barriers match.
 // Weights and activations are loaded WD steps ahead (8 + 8 registers per
 // step): loads complete in issue order, so waiting for a step's activation
 // also waits for every weight load issued before it.  `after_prologue` runs
 // once the first steps are in flight.
-template <int WD, int KH, typename Hook>
+template <int WD, int KH, typename RowFn, typename Hook>
 __device__ __forceinline__ void stream_shared_act(const char* pa, const uint16_t* act, int64_t act_ld,
-                                                  int n, lds_char* xl, int64_t s0, int64_t s1,
-                                                  int64_t len_max, f32x4_t (&acc)[4],
+                                                  RowFn act_row, int n, lds_char* xl, int64_t s0,
+                                                  int64_t s1, int64_t len_max, f32x4_t (&acc)[4],
                                                   Hook&& after_prologue) {
   constexpr int NB = 4;
   constexpr int U = WD % 2 == 0 ? WD : 2 * WD;          // unrolled steps (even: LDS slot parity)
@@ -106,7 +107,7 @@ __device__ __forceinline__ void stream_shared_act(const char* pa, const uint16_t
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
     const int tt = 16 * grp + 8 * i + (lane >> 3);
-    px[i] = reinterpret_cast<const char*>(act + static_cast<int64_t>(min(tt, n - 1)) * act_ld) + (lane & 7) * 16;
+    px[i] = reinterpret_cast<const char*>(act + act_row(min(tt, n - 1)) * act_ld) + (lane & 7) * 16;
     wofs[i] = part * kXBlock + xblock_at(tt, lane & 7);
   }
   // steps past s1 (or an empty range) re-read a valid step: s1 - 1, or s0 - 1
@@ -213,9 +214,13 @@ __device__ __forceinline__ bool fold_parts(float (*stage)[16 * kStageLd], const 
 // workgroup (4 KH waves) per 32 features; wave w owns the gate and up rows of
 // features 8 (w % 4) .. +8 (one 16-row MFMA block: 8 gate rows, then 8 up
 // rows) over part w / 4 of d_model, and the KH parts are folded in LDS.
+// With `pos`, the n tokens of the launch are pos[0 .. n) of the n_tokens rows
+// of x, h, g, u and row_index (out-of-range positions set the error word and
+// are neither read nor written).
 template <int WD, int KH>
 __global__ __launch_bounds__(256 * KH) void decode_gateup_kernel(
-    int n, int64_t d, int64_t f, const uint16_t* __restrict__ x, const uint16_t* __restrict__ wg,
+    int n, const int32_t* __restrict__ pos, int64_t n_tokens, int64_t d, int64_t f,
+    const uint16_t* __restrict__ x, const uint16_t* __restrict__ wg,
     const uint16_t* __restrict__ wu, const uint16_t* __restrict__ rows, int64_t n_rows,
     const int32_t* __restrict__ row_index, uint16_t* __restrict__ h, uint16_t* __restrict__ g_out,
     uint16_t* __restrict__ u_out, int* err) {
@@ -232,11 +237,22 @@ __global__ __launch_bounds__(256 * KH) void decode_gateup_kernel(
   f32x4_t acc[4];
   // the epilogue's table row (lane = token, this wave's 8 features), fetched
   // once the stream is under way
+  // token position of launch token t (-1 when out of range)
+  auto tok_of = [&](int t) -> int64_t {
+    if (!pos) return t;
+    const int64_t p = pos[t];
+    return p >= 0 && p < n_tokens ? p : -1;
+  };
+  auto act_row = [&](int t) -> int64_t {
+    const int64_t p = tok_of(t);
+    return p < 0 ? 0 : p;
+  };
+  const int64_t tok = tok_of(min(lane, n - 1));
   int64_t ri;
   bool erow_ok;
   uint4 erow;
-  stream_shared_act<WD, KH>(pa, x, d, n, (lds_char*)(xs), s0, s1, len, acc, [&]() {
-    ri = row_index[min(lane, n - 1)];
+  stream_shared_act<WD, KH>(pa, x, d, act_row, n, (lds_char*)(xs), s0, s1, len, acc, [&]() {
+    ri = row_index[tok < 0 ? 0 : tok];
     erow_ok = ri >= 0 && ri < n_rows;
     erow = *reinterpret_cast<const uint4*>(erow_ok ? rows + ri * f + f0 : x);
   });
@@ -247,6 +263,10 @@ __global__ __launch_bounds__(256 * KH) void decode_gateup_kernel(
   const float* st = stage[grp];
   const int t = lane;
   if (t >= n) return;
+  if (tok < 0) {
+    flag_index_error(err);
+    return;
+  }
   float gv[8], uv[8], hv[8], ev[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
@@ -278,7 +298,7 @@ __global__ __launch_bounds__(256 * KH) void decode_gateup_kernel(
     o.w = static_cast<uint32_t>(f32_to_bf16(v[6])) | (static_cast<uint32_t>(f32_to_bf16(v[7])) << 16);
     return o;
   };
-  const int64_t o = static_cast<int64_t>(t) * f + f0;
+  const int64_t o = tok * f + f0;
   *reinterpret_cast<uint4*>(h + o) = pack(hv);
   if (g_out) *reinterpret_cast<uint4*>(g_out + o) = pack(gv);
   if (u_out) *reinterpret_cast<uint4*>(u_out + o) = pack(uv);
@@ -308,7 +328,8 @@ __global__ __launch_bounds__(256 * KH) void decode_down_kernel(int n, int64_t d,
   const int64_t s1 = s0 + len < k1 ? s0 + len : k1;
   const char* pa = reinterpret_cast<const char*>(wd + (n0 + r) * f) + q * 16;
   f32x4_t acc[4];
-  stream_shared_act<WD, KH>(pa, h, f, n, (lds_char*)(xs), s0, s1, len, acc, []() {});
+  stream_shared_act<WD, KH>(pa, h, f, [](int t) -> int64_t { return t; }, n, (lds_char*)(xs), s0,
+                            s1, len, acc, []() {});
   if (!fold_parts<KH>(stage, acc)) return;
   const float* st = stage[grp];
   const int t = lane;
@@ -363,13 +384,14 @@ constexpr int kGateUpParts = 2;   // d_model split in two inside a gate/up workg
 constexpr int kDownParts = 1;
 static_assert(kDownSplit <= kDownSplitMax, "down partials fit the workspace");
 
-hipError_t decode_gateup(int64_t n, int64_t d, int64_t f, const void* x, const void* wg,
-                         const void* wu, const void* rows, int64_t n_rows,
-                         const int32_t* row_index, void* h, void* g_out, void* u_out,
-                         hipStream_t s, int* err) {
+hipError_t decode_gateup(int64_t n, const int32_t* pos, int64_t n_tokens, int64_t d, int64_t f,
+                         const void* x, const void* wg, const void* wu, const void* rows,
+                         int64_t n_rows, const int32_t* row_index, void* h, void* g_out,
+                         void* u_out, hipStream_t s, int* err) {
   auto go = [&](auto kern, int threads) {
     kern<<<dim3(static_cast<unsigned>(f / 32)), dim3(threads), 0, s>>>(
-        static_cast<int>(n), d, f, static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(wg),
+        static_cast<int>(n), pos, n_tokens, d, f, static_cast<const uint16_t*>(x),
+        static_cast<const uint16_t*>(wg),
         static_cast<const uint16_t*>(wu), static_cast<const uint16_t*>(rows), n_rows, row_index,
         static_cast<uint16_t*>(h), static_cast<uint16_t*>(g_out), static_cast<uint16_t*>(u_out), err);
   };

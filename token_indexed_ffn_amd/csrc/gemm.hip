@@ -36,13 +36,16 @@ enum EpiKind { kEpiStore = 0, kEpiGateUp = 1, kEpiDhAct = 2 };
 
 struct GemmArgs {
   int64_t M, N, K;
-  // A operand.  K-major: A(m,k) = a0[row(m) * lda + k], row(m) = a_rows ? a_rows[m] : m.
+  // A operand.  K-major: A(m,k) = a0[row(m) * lda + k], row(m) = a_rows ? a_rows[m] : m
+  // (a_rows entries outside [0, a_rows_bound) set the error word; row 0 is read
+  // instead and the gate/up epilogue stores nothing for them).
   // MN-major: A(m,k) = (k < a_split ? a0 + k*lda : a1 + (k-a_split)*lda)[m].
   const void* a0;
   const void* a1;
   int64_t lda;
   int64_t a_split;
   const int32_t* a_rows;
+  int64_t a_rows_bound;
   // B operand.  K-major: B(k,n) = (n < b_split ? b0 + n*ldb : b1 + (n-b_split)*ldb)[k].
   // MN-major: B(k,n) = (k < b_split ? b0 + k*ldb : b1 + (k-b_split)*ldb)[n].
   // GateUp: K-major with n in 64-row groups: rows 0-31 of a group are W_gate
@@ -498,7 +501,14 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(GemmArgs p) {
     for (int i = 0; i < ATile::kPer; ++i) {
       int64_t m = m0 + ATile::row_of(i);
       if (m > p.M - 1) m = p.M - 1;
-      const int64_t row = p.a_rows ? static_cast<int64_t>(p.a_rows[m]) : m;
+      int64_t row = m;
+      if (p.a_rows) {
+        row = p.a_rows[m];
+        if (row < 0 || row >= p.a_rows_bound) {
+          flag_index_error(p.err);
+          row = 0;
+        }
+      }
       at.row_ptr[i] = static_cast<const char*>(p.a0) + row * p.lda * sizeof(T);
     }
     at.init_chunks();
@@ -642,7 +652,8 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(GemmArgs p) {
         const int64_t m = mrow0 + rr;
         const int64_t mm = m < p.M ? m : p.M - 1;
         tokq[c] = p.a_rows ? static_cast<int64_t>(p.a_rows[mm]) : mm;
-        ri[c] = p.row_index[tokq[c]];
+        if (tokq[c] < 0 || tokq[c] >= p.a_rows_bound) tokq[c] = -1;   // flagged in the prologue
+        ri[c] = p.row_index[tokq[c] < 0 ? 0 : tokq[c]];
       }
 #pragma unroll
       for (int c = 0; c < kPerLane; ++c) {
@@ -661,7 +672,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(GemmArgs p) {
         const int pair = fc / 32, fin = fc % 32;
         const int64_t m = mrow0 + rr;
         const int64_t feat = (n0 + wn * WN) / 2 + fc;
-        if (m < p.M && feat < f) {
+        if (m < p.M && feat < f && tokq[c] >= 0) {
           float g[8], a[8];
           read8(region + rr * LD + pair * 64 + fin, g);
           read8(region + rr * LD + pair * 64 + 32 + fin, a);
@@ -763,13 +774,17 @@ static GemmArgs blank() {
 }
 
 // h = silu(x W_gate^T) * (x W_up^T + rows[row_index]); optional saves of g, u.
+// With `pos`, only the n_sel tokens pos[0 .. n_sel) of the n_tokens are
+// computed (their rows of x, h, g, u; row_index stays indexed by token).
 template <typename T>
-hipError_t gateup_fwd(int64_t n, int64_t d, int64_t f, const void* x, const void* wg,
-                      const void* wu, const void* rows, int64_t n_rows, const int32_t* row_index,
-                      void* h, void* g_out, void* u_out, hipStream_t s, int* err) {
+hipError_t gateup_fwd(int64_t n_sel, const int32_t* pos, int64_t n_tokens, int64_t d, int64_t f,
+                      const void* x, const void* wg, const void* wu, const void* rows,
+                      int64_t n_rows, const int32_t* row_index, void* h, void* g_out, void* u_out,
+                      hipStream_t s, int* err) {
   GemmArgs a = blank<T>();
-  a.M = n; a.N = 2 * f; a.K = d;
+  a.M = n_sel; a.N = 2 * f; a.K = d;
   a.a0 = x; a.lda = d;
+  a.a_rows = pos; a.a_rows_bound = n_tokens;
   a.b0 = wg; a.b1 = wu; a.ldb = d;
   a.rows = rows; a.row_index = row_index; a.n_rows = n_rows; a.d_ff = f;
   a.h_out = h; a.g_out = g_out; a.u_out = u_out; a.err = err;
@@ -839,9 +854,9 @@ hipError_t dwgu_bwd(int64_t n, int64_t d, int64_t f, const void* dgu, const void
 }
 
 #define STAPLE_INST(T)                                                                          \
-  template hipError_t gateup_fwd<T>(int64_t, int64_t, int64_t, const void*, const void*,       \
-                                    const void*, const void*, int64_t, const int32_t*, void*,   \
-                                    void*, void*, hipStream_t, int*);                           \
+  template hipError_t gateup_fwd<T>(int64_t, const int32_t*, int64_t, int64_t, int64_t,        \
+                                    const void*, const void*, const void*, const void*, int64_t,\
+                                    const int32_t*, void*, void*, void*, hipStream_t, int*);     \
   template hipError_t down_fwd<T>(int64_t, int64_t, int64_t, const void*, const void*, void*,  \
                                   int, hipStream_t);                                            \
   template hipError_t dh_act<T>(int64_t, int64_t, int64_t, const void*, const void*,           \

@@ -117,6 +117,65 @@ hipError_t launch_cache_lookup(const int32_t* uniq, const int32_t* n_unique, int
 }
 
 // ---------------------------------------------------------------------------
+// Token split by cache outcome (one workgroup, stable): the token positions
+// whose row is cached and those whose row was a miss, each in ascending
+// order, and every token's row in its source (cache slot or miss index).
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(kLookupThreads) void split_tokens_kernel(
+    const int32_t* inv, int64_t n, const int32_t* code, const int32_t* n_unique_p,
+    int64_t max_unique, int32_t* hit_pos, int32_t* miss_pos, int32_t* tok_row, int32_t* counts,
+    int* err) {
+  __shared__ int wave_tmp[16];
+  int64_t nu = *n_unique_p;
+  if (nu < 0 || nu > max_unique) {
+    if (threadIdx.x == 0) flag_index_error(err);
+    nu = nu < 0 ? 0 : max_unique;
+  }
+  int hits = 0, misses = 0;
+  for (int64_t base = 0; base < n; base += blockDim.x) {
+    const int64_t t = base + threadIdx.x;
+    int hit = 0, miss = 0;
+    int32_t row = -1;
+    if (t < n) {
+      const int32_t u = inv[t];
+      if (u < 0 || u >= nu) {
+        flag_index_error(err);   // kept with the hits, row -1: the gate/up epilogue flags it again
+        hit = 1;
+      } else {
+        const int32_t c = code[u];
+        hit = c >= 0;
+        miss = !hit;
+        row = hit ? c : -1 - c;
+      }
+    }
+    int total_hit, total_miss;
+    const int bh = scan_block(hit, wave_tmp, total_hit);
+    const int bm = scan_block(miss, wave_tmp, total_miss);
+    if (t < n) {
+      tok_row[t] = row;
+      if (hit) hit_pos[hits + bh] = static_cast<int32_t>(t);
+      if (miss) miss_pos[misses + bm] = static_cast<int32_t>(t);
+    }
+    hits += total_hit;
+    misses += total_miss;
+  }
+  if (threadIdx.x == 0) {
+    counts[0] = hits;
+    counts[1] = misses;
+  }
+}
+
+hipError_t launch_split_tokens(const int32_t* inv, int64_t n, const int32_t* code,
+                               const int32_t* n_unique, int64_t max_unique, int32_t* hit_pos,
+                               int32_t* miss_pos, int32_t* tok_row, int32_t* counts, hipStream_t s,
+                               int* err) {
+  split_tokens_kernel<<<dim3(1), dim3(kLookupThreads), 0, s>>>(inv, n, code, n_unique, max_unique,
+                                                               hit_pos, miss_pos, tok_row, counts,
+                                                               err);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
 // Row copies.  One workgroup per destination row; 16-byte vectors.
 // ---------------------------------------------------------------------------
 constexpr int kRowThreads = 256;
