@@ -124,7 +124,8 @@ staple_status_t staple_cache_build(const int64_t* counts, int64_t vocab, int64_t
 /* Copies the cached rows of one layer's table into its slot rows:
  * slot_rows[s] = table[slot_to_id[s]] for s < capacity.  `table` is
  * [vocab x d_ff] of `dtype`, in device memory or in pinned host memory that
- * the device can address (hipHostMalloc). */
+ * the device can address (hipHostMalloc); pageable host memory for `table` or
+ * `slot_rows` is rejected with STAPLE_ERR_INVALID_ARGUMENT before any launch. */
 staple_status_t staple_cache_fill(const void* table, int64_t vocab, int64_t d_ff, int32_t dtype,
                                   const int32_t* slot_to_id, int64_t capacity,
                                   void* slot_rows, void* stream);
@@ -189,8 +190,13 @@ staple_status_t staple_assemble_rows(const void* cache_rows, int64_t capacity,
 
 /* Row gather: dst[r] = src[index[r]] for r < n, where n = *n_rows when n_rows
  * is non-NULL (a device scalar, <= max_rows) and max_rows otherwise.
- * src [src_rows x d_ff], dst [max_rows x d_ff].  Used to build the compact
- * block R = E[uniq] when the whole table is device-resident. */
+ * src [src_rows x d_ff] in device memory or in pinned host memory that the
+ * device can address (hipHostMalloc), dst [max_rows x d_ff] (device memory
+ * or pinned host memory); pageable host memory for either is rejected with
+ * STAPLE_ERR_INVALID_ARGUMENT before any launch.  Builds the
+ * compact block R = E[uniq] when the whole table is device-resident, and
+ * reads miss rows straight from a pinned host table (one workgroup per row,
+ * whole-row reads over PCIe, no host round trip for the miss list). */
 staple_status_t staple_gather_rows(const void* src, int64_t src_rows, const int32_t* index,
                                    const int32_t* n_rows, int64_t max_rows, int64_t d_ff,
                                    int32_t dtype, void* dst, void* stream);

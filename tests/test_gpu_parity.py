@@ -123,7 +123,8 @@ def test_cache_count_build_lookup_bit_exact(st, dev, vocab, capacity, n_cal):
 
 def test_compact_rows_hit_and_miss_paths_are_bit_identical(st, dev):
     """R = E[uniq] bitwise, whether rows come from the HBM cache, from pinned
-    host staging, or from a device-resident table; capacity 0, 5% and full."""
+    host staging, from a kernel reading the pinned host table, or from a
+    device-resident table; capacity 0, 5% and full."""
     import torch
     vocab, f, n = 3000, 256, 2048
     table_bits = S.normal_bf16_bits((vocab, f), 0.02, 77)
@@ -151,10 +152,38 @@ def test_compact_rows_hit_and_miss_paths_are_bit_identical(st, dev):
         st.staple_stage_misses(host_table, miss_ids, m, staging, miss_rows, stream=side)
         torch.cuda.current_stream().wait_stream(side)
         rows = st.staple_assemble_rows(cache_rows, miss_rows, lk["code"], dd["n_unique"])
+        # misses read by a kernel straight from the pinned host table
+        direct_miss = st.staple_gather_rows(host_table, lk["miss_ids"], lk["n_miss"])
+        rows2 = st.staple_assemble_rows(cache_rows, direct_miss, lk["code"], dd["n_unique"])
         torch.cuda.synchronize()
         _no_device_error(st)
         got = rows[:u].cpu().view(torch.int16).numpy().view(np.uint16)
         np.testing.assert_array_equal(got, expect, err_msg=f"capacity {capacity}")
+        got2 = rows2[:u].cpu().view(torch.int16).numpy().view(np.uint16)
+        np.testing.assert_array_equal(got2, expect, err_msg=f"capacity {capacity}, direct misses")
+
+
+def test_row_copies_refuse_pageable_host_memory(st, dev):
+    """A pageable host buffer handed to a row copy (source or destination) is
+    refused on the host with STAPLE_ERR_INVALID_ARGUMENT; nothing is launched."""
+    import torch
+    f = 256
+    src = torch.zeros(8, f, dtype=torch.bfloat16, device=dev)
+    idx = torch.arange(4, dtype=torch.int32, device=dev)
+    pageable = torch.zeros(4, f, dtype=torch.bfloat16)
+    lib = st.lib()
+    rc = lib.staple_gather_rows(src.data_ptr(), 8, idx.data_ptr(), None, 4, f, 1,
+                                pageable.data_ptr(), None)
+    assert rc == -1
+    rc = lib.staple_gather_rows(pageable.data_ptr(), 4, idx.data_ptr(), None, 4, f, 1,
+                                src.data_ptr(), None)
+    assert rc == -1
+    slot_to_id = torch.arange(4, dtype=torch.int32, device=dev)
+    rc = lib.staple_cache_fill(pageable.data_ptr(), 4, f, 1, slot_to_id.data_ptr(), 4,
+                               src.data_ptr(), None)
+    assert rc == -1
+    torch.cuda.synchronize()
+    _no_device_error(st)
 
 
 # ---------------------------------------------------- cache-split gate/up

@@ -198,11 +198,14 @@ def staple_assemble_rows(cache_rows: torch.Tensor, miss_rows: torch.Tensor, code
 
 def staple_gather_rows(src: torch.Tensor, index: torch.Tensor, n_rows: Optional[torch.Tensor] = None,
                        out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
-    _dev(src, index, n_rows, out)
+    """dst[r] = src[index[r]]; `src` on the device or in pinned host memory."""
+    if not (src.is_cuda or src.is_pinned()) or not src.is_contiguous():
+        raise ValueError("src must be a contiguous device or pinned host tensor")
+    _dev(index, n_rows, out)
     d_ff = src.shape[1]
     mr = index.numel()
     if out is None:
-        out = torch.empty(mr, d_ff, dtype=src.dtype, device=src.device)
+        out = torch.empty(mr, d_ff, dtype=src.dtype, device=index.device)
     _check(lib().staple_gather_rows(_p(src), src.shape[0], _p(index), _p(n_rows), mr, d_ff,
                                     _dt(src), _p(out), _stream(stream)), "staple_gather_rows")
     return out

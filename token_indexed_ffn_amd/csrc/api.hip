@@ -99,6 +99,19 @@ int* device_error_word() {
 static inline int elem_bytes(int32_t dt) { return dt == STAPLE_BF16 ? 2 : 4; }
 static inline bool valid_dtype(int32_t dt) { return dt == STAPLE_BF16 || dt == STAPLE_F32; }
 static inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// True when kernels can address `p`: device memory, or pinned (registered or
+// hipHostMalloc'd) host memory.  Pageable host memory is refused on the host
+// instead of faulting in a kernel.  A failed query leaves no error behind.
+static bool device_addressable(const void* p) {
+  hipPointerAttribute_t attr{};
+  if (hipPointerGetAttributes(&attr, p) != hipSuccess) {
+    (void)hipGetLastError();
+    return false;
+  }
+  return attr.type == hipMemoryTypeDevice || attr.type == hipMemoryTypeHost ||
+         attr.type == hipMemoryTypeManaged;
+}
 static inline hipStream_t S(void* s) { return static_cast<hipStream_t>(s); }
 
 }  // namespace staple
@@ -200,6 +213,7 @@ staple_status_t staple_cache_fill(const void* table, int64_t vocab, int64_t d_ff
   REQUIRE((d_ff * elem_bytes(dtype)) % 16 == 0);
   REQUIRE(capacity == 0 || (table && slot_to_id && slot_rows));
   REQUIRE(capacity == 0 || (aligned16(table) && aligned16(slot_rows)));
+  REQUIRE(capacity == 0 || (device_addressable(table) && device_addressable(slot_rows)));
   GET_ERR(err);
   HIPCALL(launch_gather_rows(table, vocab, slot_to_id, nullptr, capacity, d_ff * elem_bytes(dtype),
                              slot_rows, S(stream), err));
@@ -290,6 +304,7 @@ staple_status_t staple_gather_rows(const void* src, int64_t src_rows, const int3
   REQUIRE((d_ff * elem_bytes(dtype)) % 16 == 0);
   REQUIRE(max_rows == 0 || (src && index && dst));
   REQUIRE(max_rows == 0 || (aligned16(src) && aligned16(dst)));
+  REQUIRE(max_rows == 0 || (device_addressable(src) && device_addressable(dst)));
   GET_ERR(err);
   HIPCALL(launch_gather_rows(src, src_rows, index, n_rows, max_rows, d_ff * elem_bytes(dtype), dst,
                              S(stream), err));
