@@ -473,27 +473,16 @@ def run_offload_decode(torch, st, w, steps, warmup):
         return m
 
     def step_direct():
-        # no host round trip: a kernel reads each layer's miss rows straight
-        # from the pinned host table (staple_gather_rows with the device miss
-        # list and count), on the side stream one layer ahead
+        # no host round trip: before each layer a kernel reads that layer's
+        # miss rows straight from the pinned host table (staple_gather_rows
+        # with the device miss list and count), in stream order
         dd = st.staple_dedup(ids, v, out=dd_out)
         lk = st.staple_cache_lookup(dd["uniq"], dd["n_unique"], O["id_to_slot"], out=lk_out)
-        side.wait_stream(main)
-
-        def fetch(l):
-            with torch.cuda.stream(side):
-                st.staple_gather_rows(O["tables"][l], lk["miss_ids"], lk["n_miss"], out=dev_miss[l],
-                                      stream=side)
-                events[l].record(side)
-
-        fetch(0)
         for l, lay in enumerate(layers):
-            main.wait_event(events[l])
+            st.staple_gather_rows(O["tables"][l], lk["miss_ids"], lk["n_miss"], out=dev_miss[l])
             st.staple_assemble_rows(O["cache_rows"][l], dev_miss[l], lk["code"], dd["n_unique"], out=R)
             st.staple_ffn_fwd(lay["x"], lay["w_gate"], lay["w_up"], lay["w_down"], R, dd["inv"],
                               out={"y": lay["y"]}, workspace=ws)
-            if l + 1 < L:
-                fetch(l + 1)
         return None
 
     def timed(step):
@@ -520,9 +509,9 @@ def run_offload_decode(torch, st, w, steps, warmup):
             "pcie_bytes_per_step": m * f * 2 * L,
             "note": "eager steps, dedup + cache probe once per step. direct: per layer a kernel "
                     "gathers the miss rows from the pinned host table over PCIe (device miss "
-                    "list, no host sync) on a side stream one layer ahead, then row assembly, "
-                    "gate/up, down. staged: one host sync for the miss list, host pack + H2D "
-                    "copy per layer on the side stream one layer ahead"}
+                    "list, no host sync, one stream), then row assembly, gate/up, down. staged: "
+                    "one host sync for the miss list, host pack + H2D copy per layer on a side "
+                    "stream one layer ahead"}
 
 
 def run_offload_train(torch, st, w, steps, warmup):

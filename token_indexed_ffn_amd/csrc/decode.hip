@@ -373,12 +373,14 @@ size_t decode_down_workspace_bytes(int64_t n, int64_t d) {
 
 // Launch shapes of the two decode kernels.
 // Launch shapes (measured on MI355X for d_model 2048 / d_ff 8192, batch 64):
-// four steps in flight per wave; gate/up on 8 waves (d_model in two parts),
-// down on 4 waves with d_ff split 8 ways over workgroups.
+// gate/up on 8 waves (d_model in two parts) with two steps in flight per
+// wave, down on 4 waves with four steps in flight and d_ff split 8 ways over
+// workgroups.
 // Deeper prefetch, 2 or 4 steps per barrier, 4 splits, and the earlier
 // layouts that split d_model (or d_ff) over the waves of a workgroup and
 // folded their partial sums in LDS all measured slower.
-constexpr int kDecodeAhead = 4;
+constexpr int kGateUpAhead = 2;   // steps in flight per wave
+constexpr int kDownAhead = 4;
 constexpr int kDownSplit = 8;
 constexpr int kGateUpParts = 2;   // d_model split in two inside a gate/up workgroup (8 waves)
 constexpr int kDownParts = 1;
@@ -395,14 +397,14 @@ hipError_t decode_gateup(int64_t n, const int32_t* pos, int64_t n_tokens, int64_
         static_cast<const uint16_t*>(wu), static_cast<const uint16_t*>(rows), n_rows, row_index,
         static_cast<uint16_t*>(h), static_cast<uint16_t*>(g_out), static_cast<uint16_t*>(u_out), err);
   };
-  go(decode_gateup_kernel<kDecodeAhead, kGateUpParts>, 256 * kGateUpParts);
+  go(decode_gateup_kernel<kGateUpAhead, kGateUpParts>, 256 * kGateUpParts);
   return hipGetLastError();
 }
 
 hipError_t decode_down(int64_t n, int64_t d, int64_t f, const void* h, const void* wd, void* y,
                        int out_dtype, void* ws, hipStream_t s) {
   float* partial = static_cast<float*>(ws);
-  decode_down_kernel<kDecodeAhead, kDownSplit, kDownParts>
+  decode_down_kernel<kDownAhead, kDownSplit, kDownParts>
       <<<dim3(static_cast<unsigned>(d / 64), kDownSplit), dim3(256 * kDownParts), 0, s>>>(
           static_cast<int>(n), d, f, static_cast<const uint16_t*>(h), static_cast<const uint16_t*>(wd),
           partial);

@@ -760,6 +760,8 @@ static hipError_t run(const GemmArgs& a, hipStream_t s) {
     // (Four or five 32 KB stages of 64-byte rows, which keep three or four
     // stages of loads in flight, measured no faster: the kernels are not
     // waiting on global-load latency.)
+    // (256x128 or 128x256 tiles on 4 waves, two workgroups per CU with
+    // three 64-byte-row stages, measured slower on every training GEMM.)
     if (a.M >= 256 && a.N >= 256 && ((a.M + 255) / 256) * ((a.N + 255) / 256) >= 128)
       return run_tile<T, 256, 256, 2, 4, AK, BK, EPI, OutT, kRowBytes, 2>(a, s);
   }
