@@ -188,6 +188,22 @@ staple_status_t staple_assemble_rows(const void* cache_rows, int64_t capacity,
                                      int64_t max_unique, int64_t d_ff, int32_t dtype,
                                      void* rows, void* stream);
 
+/* Compact block assembly with the misses read straight from the table:
+ * rows[u] = code[u] >= 0 ? cache_rows[code[u]] : table[uniq[u]] for
+ * u < *n_unique, one workgroup per row.  `table` [vocab x d_ff] is in device
+ * memory or in pinned host memory that the device can address (hipHostMalloc):
+ * with a host table the misses cross PCIe inside the kernel, with no host
+ * round trip for the miss list (STAPLE retrieval-path table, decode: misses
+ * read from host memory).  uniq, code, n_unique as from staple_dedup and
+ * staple_cache_lookup; pageable host memory for `table` or `rows` is rejected
+ * with STAPLE_ERR_INVALID_ARGUMENT before any launch. */
+staple_status_t staple_assemble_rows_from_table(const void* cache_rows, int64_t capacity,
+                                                const void* table, int64_t vocab,
+                                                const int32_t* uniq, const int32_t* code,
+                                                const int32_t* n_unique, int64_t max_unique,
+                                                int64_t d_ff, int32_t dtype, void* rows,
+                                                void* stream);
+
 /* Row gather: dst[r] = src[index[r]] for r < n, where n = *n_rows when n_rows
  * is non-NULL (a device scalar, <= max_rows) and max_rows otherwise.
  * src [src_rows x d_ff] in device memory or in pinned host memory that the

@@ -152,15 +152,20 @@ def test_compact_rows_hit_and_miss_paths_are_bit_identical(st, dev):
         st.staple_stage_misses(host_table, miss_ids, m, staging, miss_rows, stream=side)
         torch.cuda.current_stream().wait_stream(side)
         rows = st.staple_assemble_rows(cache_rows, miss_rows, lk["code"], dd["n_unique"])
-        # misses read by a kernel straight from the pinned host table
+        # misses read by a kernel straight from the pinned host table, either
+        # gathered first or read inside the assembly; and from the device table
         direct_miss = st.staple_gather_rows(host_table, lk["miss_ids"], lk["n_miss"])
         rows2 = st.staple_assemble_rows(cache_rows, direct_miss, lk["code"], dd["n_unique"])
+        rows3 = st.staple_assemble_rows_from_table(cache_rows, host_table, dd["uniq"], lk["code"],
+                                                   dd["n_unique"], capacity=capacity)
+        rows4 = st.staple_assemble_rows_from_table(cache_rows, dev_table, dd["uniq"], lk["code"],
+                                                   dd["n_unique"], capacity=capacity)
         torch.cuda.synchronize()
         _no_device_error(st)
-        got = rows[:u].cpu().view(torch.int16).numpy().view(np.uint16)
-        np.testing.assert_array_equal(got, expect, err_msg=f"capacity {capacity}")
-        got2 = rows2[:u].cpu().view(torch.int16).numpy().view(np.uint16)
-        np.testing.assert_array_equal(got2, expect, err_msg=f"capacity {capacity}, direct misses")
+        for name, r in (("staged", rows), ("gathered from host", rows2),
+                        ("assembled from host table", rows3), ("assembled from device table", rows4)):
+            got = r[:u].cpu().view(torch.int16).numpy().view(np.uint16)
+            np.testing.assert_array_equal(got, expect, err_msg=f"capacity {capacity}, {name}")
 
 
 def test_row_copies_refuse_pageable_host_memory(st, dev):

@@ -196,6 +196,27 @@ def staple_assemble_rows(cache_rows: torch.Tensor, miss_rows: torch.Tensor, code
     return out
 
 
+def staple_assemble_rows_from_table(cache_rows: torch.Tensor, table: torch.Tensor,
+                                    uniq: torch.Tensor, code: torch.Tensor,
+                                    n_unique: torch.Tensor, out: Optional[torch.Tensor] = None,
+                                    capacity: Optional[int] = None, stream=None) -> torch.Tensor:
+    """R[u] = cache_rows[code[u]] on a hit, table[uniq[u]] on a miss (`table` on the device
+    or in pinned host memory)."""
+    if not (table.is_cuda or table.is_pinned()) or not table.is_contiguous():
+        raise ValueError("table must be a contiguous device or pinned host tensor")
+    _dev(cache_rows, uniq, code, n_unique, out)
+    vocab, d_ff = table.shape
+    mu = uniq.numel()
+    cap = cache_rows.shape[0] if capacity is None else capacity
+    if out is None:
+        out = torch.empty(max(mu, 1), d_ff, dtype=table.dtype, device=uniq.device)
+    _check(lib().staple_assemble_rows_from_table(_p(cache_rows), cap, _p(table), vocab, _p(uniq),
+                                                 _p(code), _p(n_unique), mu, d_ff, _dt(table),
+                                                 _p(out), _stream(stream)),
+           "staple_assemble_rows_from_table")
+    return out
+
+
 def staple_gather_rows(src: torch.Tensor, index: torch.Tensor, n_rows: Optional[torch.Tensor] = None,
                        out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
     """dst[r] = src[index[r]]; `src` on the device or in pinned host memory."""

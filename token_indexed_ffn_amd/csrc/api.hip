@@ -38,6 +38,10 @@ hipError_t launch_assemble_rows(const void* cache_rows, int64_t capacity, const 
                                 int64_t max_miss, const int32_t* code, const int32_t* n_unique,
                                 int64_t max_unique, int64_t row_bytes, void* rows, hipStream_t s,
                                 int* err);
+hipError_t launch_assemble_rows_table(const void* cache_rows, int64_t capacity, const void* table,
+                                      int64_t vocab, const int32_t* uniq, const int32_t* code,
+                                      const int32_t* n_unique, int64_t max_unique,
+                                      int64_t row_bytes, void* rows, hipStream_t s, int* err);
 size_t segment_sum_workspace_bytes(int64_t n_tokens, int64_t d_ff);
 hipError_t launch_segment_sum(int dtype, const void* du, int64_t du_ld, int64_t du_col,
                               int64_t n_tokens, int64_t d_ff, const int32_t* sorted_pos,
@@ -294,6 +298,25 @@ staple_status_t staple_assemble_rows(const void* cache_rows, int64_t capacity,
   GET_ERR(err);
   HIPCALL(launch_assemble_rows(cache_rows, capacity, miss_rows, max_miss, code, n_unique,
                                max_unique, d_ff * elem_bytes(dtype), rows, S(stream), err));
+  return STAPLE_OK;
+}
+
+staple_status_t staple_assemble_rows_from_table(const void* cache_rows, int64_t capacity,
+                                                const void* table, int64_t vocab,
+                                                const int32_t* uniq, const int32_t* code,
+                                                const int32_t* n_unique, int64_t max_unique,
+                                                int64_t d_ff, int32_t dtype, void* rows,
+                                                void* stream) {
+  REQUIRE(valid_dtype(dtype) && d_ff > 0 && capacity >= 0 && vocab >= 1 && max_unique >= 0);
+  REQUIRE((d_ff * elem_bytes(dtype)) % 16 == 0);
+  REQUIRE(n_unique && table && (max_unique == 0 || (uniq && code && rows)));
+  REQUIRE(capacity == 0 || cache_rows);
+  REQUIRE(aligned16(table) && (capacity == 0 || aligned16(cache_rows)) &&
+          (max_unique == 0 || aligned16(rows)));
+  REQUIRE(device_addressable(table) && (max_unique == 0 || device_addressable(rows)));
+  GET_ERR(err);
+  HIPCALL(launch_assemble_rows_table(cache_rows, capacity, table, vocab, uniq, code, n_unique,
+                                     max_unique, d_ff * elem_bytes(dtype), rows, S(stream), err));
   return STAPLE_OK;
 }
 

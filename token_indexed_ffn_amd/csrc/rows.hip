@@ -245,6 +245,45 @@ hipError_t launch_assemble_rows(const void* cache_rows, int64_t capacity, const 
   return hipGetLastError();
 }
 
+// rows[u] = code[u] >= 0 ? cache_rows[code[u]] : table[uniq[u]]: hits from the
+// HBM cache, misses read straight from the table (device memory or pinned
+// host memory read over PCIe, one whole row per workgroup).
+__global__ __launch_bounds__(kRowThreads) void assemble_rows_table_kernel(
+    const void* cache_rows, int64_t capacity, const void* table, int64_t vocab,
+    const int32_t* uniq, const int32_t* code, const int32_t* n_unique_p, int64_t row_bytes,
+    void* rows, int* err) {
+  const int64_t u = blockIdx.x;
+  if (u >= *n_unique_p) return;
+  const int32_t c = code[u];
+  const char* src;
+  if (c >= 0) {
+    if (c >= capacity) {
+      if (threadIdx.x == 0) flag_index_error(err);
+      return;
+    }
+    src = static_cast<const char*>(cache_rows) + c * row_bytes;
+  } else {
+    const int32_t id = uniq[u];
+    if (id < 0 || id >= vocab) {
+      if (threadIdx.x == 0) flag_index_error(err);
+      return;
+    }
+    src = static_cast<const char*>(table) + id * row_bytes;
+  }
+  copy_row16(reinterpret_cast<const uint4*>(src),
+             reinterpret_cast<uint4*>(static_cast<char*>(rows) + u * row_bytes), row_bytes / 16);
+}
+
+hipError_t launch_assemble_rows_table(const void* cache_rows, int64_t capacity, const void* table,
+                                      int64_t vocab, const int32_t* uniq, const int32_t* code,
+                                      const int32_t* n_unique, int64_t max_unique,
+                                      int64_t row_bytes, void* rows, hipStream_t s, int* err) {
+  if (max_unique == 0) return hipSuccess;
+  assemble_rows_table_kernel<<<dim3(static_cast<unsigned>(max_unique)), dim3(kRowThreads), 0, s>>>(
+      cache_rows, capacity, table, vocab, uniq, code, n_unique, row_bytes, rows, err);
+  return hipGetLastError();
+}
+
 // ---------------------------------------------------------------------------
 // Table-row gradient: d_rows[u, c] = sum over sorted positions p of segment u
 // of du[sorted_pos[p], c], accumulated in fp32.
