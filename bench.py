@@ -105,6 +105,10 @@ def setup_decode(torch, st, w):
             "table": device_normal((v, f), w.table_std, s["table"], torch.bfloat16, dev),
             "y": torch.empty(n, d, dtype=torch.bfloat16, device=dev),
         })
+        lay = layers[-1]
+        # the serving layout: packed once when the weights are loaded
+        lay["pgu"], lay["pd"] = st.staple_decode_pack_weights(lay["w_gate"], lay["w_up"],
+                                                              lay["w_down"], d_model=d, d_ff=f)
         torch.cuda.synchronize()
     ids = torch.from_numpy(ids_np).to(dev)
     h = torch.empty(n, f, dtype=torch.bfloat16, device=dev)
@@ -114,6 +118,14 @@ def setup_decode(torch, st, w):
 
 
 def decode_step(st, D):
+    ids = D["ids"]
+    for lay in D["layers"]:
+        st.staple_ffn_fwd_packed(lay["x"], lay["pgu"], lay["pd"], lay["table"], ids,
+                                 d_ff=lay["w_gate"].shape[0], out={"y": lay["y"]},
+                                 workspace=D["fwd_ws"])
+
+
+def decode_step_row_major(st, D):
     ids = D["ids"]
     for lay in D["layers"]:
         st.staple_ffn_fwd(lay["x"], lay["w_gate"], lay["w_up"], lay["w_down"], lay["table"], ids,
@@ -140,6 +152,16 @@ def run_decode(torch, st, w, steps, warmup):
         decode_step(st, D)
     torch.cuda.synchronize()
     eager_ms = (time.perf_counter() - t0) / steps * 1e3
+
+    # the same step on the row-major weights, for comparison
+    for _ in range(warmup):
+        decode_step_row_major(st, D)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        decode_step_row_major(st, D)
+    torch.cuda.synchronize()
+    row_major_ms = (time.perf_counter() - t0) / steps * 1e3
 
     # one decode step captured as a HIP graph
     g = torch.cuda.CUDAGraph()
@@ -174,8 +196,7 @@ def run_decode(torch, st, w, steps, warmup):
     with torch.cuda.stream(cap):
         with torch.cuda.graph(gg, stream=cap):
             for lay in D["layers"]:
-                st.staple_ffn_gate_up(lay["x"], lay["w_gate"], lay["w_up"], lay["table"],
-                                      D["ids"], D["h"])
+                st.staple_ffn_gate_up_packed(lay["x"], lay["pgu"], lay["table"], D["ids"], D["h"])
     torch.cuda.synchronize()
     reps = max(20, steps // 2)
     for _ in range(5):
@@ -199,11 +220,13 @@ def run_decode(torch, st, w, steps, warmup):
         "launch": launch,
         "graph_ms_per_step": graph_ms,
         "eager_ms_per_step": eager_ms,
+        "row_major_eager_ms_per_step": row_major_ms,
+        "weights": "packed decode layout (staple_decode_pack_weights, once at load)",
         "step_hbm_gb_s": step_bytes / (ms * 1e-3) / 1e9,
         "step_bytes": step_bytes,
         "n_unique": n_unique,
         "roofline": {
-            "kernel": "decode_gateup_kernel (staple_ffn_gate_up, 64 tokens)",
+            "kernel": "decode_gateup_kernel (staple_ffn_gate_up_packed, 64 tokens)",
             "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": achieved / HBM_PEAK_GBS,
             "traffic": traffic_from_profile(f"decode_gate_up/{w.name}", sha),
@@ -434,6 +457,10 @@ def run_offload_decode(torch, st, w, steps, warmup):
             ("x", (n, d), w.x_std), ("w_gate", (f, d), w.w_std), ("w_up", (f, d), w.w_std),
             ("w_down", (d, f), w.w_std))})
         layers[-1]["y"] = torch.empty(n, d, dtype=torch.bfloat16, device=dev)
+        lay = layers[-1]
+        lay["pgu"], lay["pd"] = st.staple_decode_pack_weights(lay["w_gate"], lay["w_up"],
+                                                              lay["w_down"], d_model=d, d_ff=f)
+        del lay["w_gate"], lay["w_up"], lay["w_down"]
     i32 = dict(dtype=torch.int32, device=dev)
     dd_out = {"uniq": torch.empty(n, **i32), "inv": torch.empty(n, **i32),
               "sorted_pos": torch.empty(n, **i32), "seg_start": torch.empty(n + 1, **i32),
@@ -466,8 +493,8 @@ def run_offload_decode(torch, st, w, steps, warmup):
         for l, lay in enumerate(layers):
             main.wait_event(events[l])
             st.staple_assemble_rows(O["cache_rows"][l], dev_miss[l], lk["code"], dd["n_unique"], out=R)
-            st.staple_ffn_fwd(lay["x"], lay["w_gate"], lay["w_up"], lay["w_down"], R, dd["inv"],
-                              out={"y": lay["y"]}, workspace=ws)
+            st.staple_ffn_fwd_packed(lay["x"], lay["pgu"], lay["pd"], R, dd["inv"], d_ff=f,
+                                     out={"y": lay["y"]}, workspace=ws)
             if l + 1 < L:
                 stage(l + 1)
         return m
@@ -482,8 +509,8 @@ def run_offload_decode(torch, st, w, steps, warmup):
             st.staple_assemble_rows_from_table(O["cache_rows"][l], O["tables"][l], dd["uniq"],
                                                lk["code"], dd["n_unique"], out=R,
                                                capacity=w.cache_capacity)
-            st.staple_ffn_fwd(lay["x"], lay["w_gate"], lay["w_up"], lay["w_down"], R, dd["inv"],
-                              out={"y": lay["y"]}, workspace=ws)
+            st.staple_ffn_fwd_packed(lay["x"], lay["pgu"], lay["pd"], R, dd["inv"], d_ff=f,
+                                     out={"y": lay["y"]}, workspace=ws)
         return None
 
     def timed(step):
@@ -657,7 +684,7 @@ def main(argv=None) -> int:
         out["config"] = {"workload": w.name, "d_model": w.d_model, "d_ff": w.d_ff,
                          "vocab": w.vocab, "batch": w.n_tokens, "layers": w.n_layers,
                          "tables": "12 x 100352 x 8192 bf16, HBM-resident",
-                         "step": "12 x staple_ffn_fwd (gate/up kernel + down kernel), "
+                         "step": "12 x staple_ffn_fwd_packed (gate/up kernel, down kernel, split-K sum), "
                                  + dec["launch"]}
         out["roofline"] = dec["roofline"]
         out["decode"] = {k: v for k, v in dec.items() if k != "roofline"}

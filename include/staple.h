@@ -284,6 +284,61 @@ staple_status_t staple_ffn_down(int64_t n_tokens, int64_t d_model, int64_t d_ff,
                                 void* ws, size_t ws_bytes, void* stream);
 
 /* ------------------------------------------------------------------------
+ * Decode with packed weights.  The forward of a serving step (at most 64
+ * tokens) streams every weight byte once per step, so its speed is the HBM
+ * read rate of the weight stream; the row-major matrices make each load
+ * instruction read 64-byte pieces of 16 rows a row apart.  A packed copy,
+ * made once when the weights are loaded, stores the bytes in the order the
+ * decode kernels read them (STAPLE's layer, abstract: the same
+ * y = W_down (silu(W_gate x) * (W_up x + E[t])) as staple_ffn_fwd).
+ *
+ * staple_decode_pack_weights: bf16 only.  Either output may be NULL (then
+ *   its source may be NULL too).
+ *   w_gate, w_up [d_ff x d_model], w_down [d_model x d_ff] row-major bf16.
+ *   packed_gate_up: 2 * d_ff * d_model bf16 elements (the size of w_gate and
+ *     w_up together); packed_down: d_model * d_ff elements.  Both are owned
+ *     by the caller, device memory, 16-byte aligned, and must not overlap
+ *     the sources.
+ *   Format (a private layout: produce it only with this call): an operand of
+ *   R rows x K columns is cut into K/64 steps of R/16 row blocks; bytes
+ *   ((s * R/16 + b) * 2 + j) * 1024 + 16 * l .. +16 hold bytes
+ *   128 s + 64 j + 16 (l / 16) .. +16 of row l % 16 of block b.  A gate/up
+ *   block b holds rows 8b .. 8b+7 of w_gate (block rows 0-7) and of w_up
+ *   (block rows 8-15); a down block b holds rows 16b .. 16b+15 of w_down.
+ *   d_model and d_ff multiples of 64.
+ * staple_ffn_fwd_packed: staple_ffn_fwd for 1 <= n_tokens <= 64 in bf16
+ *   (n_tokens == 0 enqueues nothing) reading the packed weights; same
+ *   arguments otherwise, same workspace (staple_ffn_fwd_workspace_bytes),
+ *   same outputs bit for bit as staple_ffn_fwd on the unpacked weights.
+ *   Larger batches or fp32 return STAPLE_ERR_UNSUPPORTED.
+ * staple_ffn_gate_up_packed, staple_ffn_down_packed: its two halves, as
+ *   staple_ffn_gate_up and staple_ffn_down are those of staple_ffn_fwd (same
+ *   arguments with the packed operand in place of the row-major ones, same
+ *   workspace for the down half, same bits), with the same limits as
+ *   staple_ffn_fwd_packed.
+ * ------------------------------------------------------------------------ */
+staple_status_t staple_decode_pack_weights(int64_t d_model, int64_t d_ff, int32_t dtype,
+                                           const void* w_gate, const void* w_up,
+                                           const void* w_down, void* packed_gate_up,
+                                           void* packed_down, void* stream);
+staple_status_t staple_ffn_gate_up_packed(int64_t n_tokens, int64_t d_model, int64_t d_ff,
+                                          int32_t dtype, const void* x,
+                                          const void* packed_gate_up, const void* rows,
+                                          int64_t n_rows, const int32_t* row_index, void* h,
+                                          void* save_g, void* save_u, void* stream);
+staple_status_t staple_ffn_down_packed(int64_t n_tokens, int64_t d_model, int64_t d_ff,
+                                       int32_t dtype, int32_t out_dtype, const void* h,
+                                       const void* packed_down, void* y, void* ws,
+                                       size_t ws_bytes, void* stream);
+staple_status_t staple_ffn_fwd_packed(int64_t n_tokens, int64_t d_model, int64_t d_ff,
+                                      int32_t dtype, int32_t out_dtype, const void* x,
+                                      const void* packed_gate_up, const void* packed_down,
+                                      const void* rows, int64_t n_rows,
+                                      const int32_t* row_index, void* y, void* save_g,
+                                      void* save_u, void* save_h, void* ws, size_t ws_bytes,
+                                      void* stream);
+
+/* ------------------------------------------------------------------------
  * Backward of one augmented layer with the table-row gradient.
  *   dy [n_tokens x d_model] (dtype): upstream gradient of y.
  *   saved_g, saved_u, saved_h: the forward's save_g/save_u/save_h (required).

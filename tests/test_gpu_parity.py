@@ -384,6 +384,93 @@ def test_decode_path_boundary(st, dev, n):
     assert torch.equal(h2, fwd["h"]) and torch.equal(y2, fwd["y"])
 
 
+def _packed_expected(a, b, rows_per_block_from_a):
+    """The documented packed order: steps of 64 columns, row blocks of 16 rows
+    (8 of a then 8 of b, or 16 of a), two 32-column halves, 64 lanes = (q, r)
+    with lane q * 16 + r holding columns 8 q .. 8 q + 8 of the half, row r."""
+    k = a.shape[1]
+    if rows_per_block_from_a == 8:
+        m = np.concatenate([a.reshape(-1, 8, k), b.reshape(-1, 8, k)], axis=1)
+    else:
+        m = a.reshape(-1, 16, k)
+    rb = m.shape[0]
+    m = m.reshape(rb, 16, k // 64, 2, 4, 8)          # (b, r, s, j, q, e)
+    return m.transpose(2, 0, 3, 4, 1, 5).reshape(-1)  # (s, b, j, q, r, e)
+
+
+@pytest.mark.parametrize("d,f", [(64, 64), (192, 320), (256, 512)])
+def test_decode_pack_is_the_documented_permutation(st, dev, d, f):
+    """Packing moves bytes only: every bf16 bit pattern lands where the
+    documented layout says (compared as raw 16-bit words)."""
+    import torch
+    _log(f"decode pack d={d} f={f}")
+    rng = np.random.default_rng(d + f)
+    raw = {k: rng.integers(-32768, 32768, size=sh, dtype=np.int16)
+           for k, sh in (("wg", (f, d)), ("wu", (f, d)), ("wd", (d, f)))}
+    t = {k: torch.from_numpy(v).to(dev).view(torch.bfloat16) for k, v in raw.items()}
+    pgu, pd = st.staple_decode_pack_weights(t["wg"], t["wu"], t["wd"], d_model=d, d_ff=f)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(pgu.view(torch.int16).cpu().numpy(),
+                                  _packed_expected(raw["wg"], raw["wu"], 8))
+    np.testing.assert_array_equal(pd.view(torch.int16).cpu().numpy(),
+                                  _packed_expected(raw["wd"], None, 16))
+
+
+@pytest.mark.parametrize("n,d,f", [(1, 256, 512), (17, 192, 320), (64, 256, 512), (33, 64, 64)])
+def test_ffn_fwd_packed_matches_oracle_and_row_major_bitwise(st, dev, n, d, f):
+    """The decode forward on packed weights gives the oracle's y, h, g, u and
+    the same bits as staple_ffn_fwd on the row-major weights."""
+    import torch
+    _log(f"packed decode n={n} d={d} f={f}")
+    inp = S.host_layer_inputs(n, d, f, 300, dtype="bf16", seed=40 + n)
+    x, wg, wu, wd, tab = (to_dev(getattr(inp, k), "bf16", dev)
+                          for k in ("x", "w_gate", "w_up", "w_down", "table"))
+    ids = torch.from_numpy(inp.ids).to(dev)
+    pgu, pd = st.staple_decode_pack_weights(wg, wu, wd, d_model=d, d_ff=f)
+    ref = st.staple_ffn_fwd(x, wg, wu, wd, tab, ids, out_dtype=torch.float32, save=True)
+    got = st.staple_ffn_fwd_packed(x, pgu, pd, tab, ids, d_ff=f, out_dtype=torch.float32, save=True)
+    got16 = st.staple_ffn_fwd_packed(x, pgu, pd, tab, ids, d_ff=f)
+    ref16 = st.staple_ffn_fwd(x, wg, wu, wd, tab, ids)
+    torch.cuda.synchronize()
+    _no_device_error(st)
+    for k in ("y", "h", "g", "u"):
+        assert torch.equal(got[k], ref[k]), k
+    assert torch.equal(got16["y"], ref16["y"])
+    # the two halves give the same bits as the fused call
+    h2 = torch.empty_like(got["h"])
+    st.staple_ffn_gate_up_packed(x, pgu, tab, ids, h2)
+    y2 = torch.empty_like(got["y"])
+    st.staple_ffn_down_packed(h2, pd, y2)
+    torch.cuda.synchronize()
+    assert torch.equal(h2, got["h"]) and torch.equal(y2, got["y"])
+    g = {k: inp.as_f64(k) for k in ("x", "w_gate", "w_up", "w_down", "table")}
+    of = O.ffn_forward(g["x"], g["w_gate"], g["w_up"], g["w_down"], g["table"], inp.ids,
+                       precision=O.BF16)
+    assert_close(to_np(got["y"]), of["y"], f"packed y n={n}")
+    assert_close(to_np(got["h"]), of["h"], f"packed h n={n}")
+    assert_close(to_np(got["u"]), of["u_saved"], f"packed u n={n}")
+
+
+def test_ffn_fwd_packed_refuses_what_it_does_not_cover(st, dev):
+    """More than 64 tokens or fp32 is refused; an empty batch is a no-op."""
+    import torch
+    d, f = 64, 64
+    wg = torch.zeros(f, d, dtype=torch.bfloat16, device=dev)
+    pgu, pd = st.staple_decode_pack_weights(wg, wg, wg.t().contiguous(), d_model=d, d_ff=f)
+    tab = torch.zeros(4, f, dtype=torch.bfloat16, device=dev)
+    for n in (65, 128):
+        x = torch.zeros(n, d, dtype=torch.bfloat16, device=dev)
+        ids = torch.zeros(n, dtype=torch.int32, device=dev)
+        with pytest.raises(RuntimeError, match="UNSUPPORTED|unsupported"):
+            st.staple_ffn_fwd_packed(x, pgu, pd, tab, ids, d_ff=f)
+    x0 = torch.zeros(0, d, dtype=torch.bfloat16, device=dev)
+    out = st.staple_ffn_fwd_packed(x0, pgu, pd, tab, torch.zeros(0, dtype=torch.int32, device=dev),
+                                   d_ff=f)
+    assert out["y"].shape == (0, d)
+    with pytest.raises(RuntimeError, match="UNSUPPORTED|unsupported"):
+        st.staple_decode_pack_weights(wg.float(), wg.float(), wg.float(), d_model=d, d_ff=f)
+
+
 def test_bf16_table_contribution_and_large_table_values(st, dev):
     """Rows with E ~ N(0,1) dominate u, so wrong rows cannot hide in tolerance."""
     _log("bf16 strong table")
@@ -543,3 +630,11 @@ def test_olmo1b_decode_layer_full(st, dev):
     of = O.ffn_forward(f64(t["x"]), f64(t["w_gate"]), f64(t["w_up"]), f64(t["w_down"]), table,
                        ids, precision=O.BF16)
     assert_close(f64(fwd["y"]), of["y"], "decode y")
+    # the packed weights (the serving layout) give the same bits
+    pgu, pd = st.staple_decode_pack_weights(t["w_gate"], t["w_up"], t["w_down"], d_model=w.d_model,
+                                            d_ff=w.d_ff)
+    got = st.staple_ffn_fwd_packed(t["x"], pgu, pd, t["table"], idt, d_ff=w.d_ff,
+                                   out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    _no_device_error(st)
+    assert torch.equal(got["y"], fwd["y"])

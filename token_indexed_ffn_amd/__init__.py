@@ -256,6 +256,77 @@ def staple_ffn_fwd(x: torch.Tensor, w_gate: torch.Tensor, w_up: torch.Tensor,
     return out
 
 
+def staple_decode_pack_weights(w_gate: Optional[torch.Tensor], w_up: Optional[torch.Tensor],
+                               w_down: Optional[torch.Tensor], *, d_model: int, d_ff: int,
+                               stream=None) -> tuple:
+    """Packed copies of (w_gate, w_up) and of w_down in the decode kernels' read order
+    (bf16).  Returns (packed_gate_up, packed_down); an entry is None when its sources are."""
+    _dev(w_gate, w_up, w_down)
+    ref = next(t for t in (w_gate, w_up, w_down) if t is not None)
+    pgu = pd = None
+    if w_gate is not None or w_up is not None:
+        pgu = torch.empty(2 * d_ff * d_model, dtype=ref.dtype, device=ref.device)
+    if w_down is not None:
+        pd = torch.empty(d_model * d_ff, dtype=ref.dtype, device=ref.device)
+    _check(lib().staple_decode_pack_weights(d_model, d_ff, _dt(ref), _p(w_gate), _p(w_up),
+                                            _p(w_down), _p(pgu), _p(pd), _stream(stream)),
+           "staple_decode_pack_weights")
+    return pgu, pd
+
+
+def staple_ffn_fwd_packed(x: torch.Tensor, packed_gate_up: torch.Tensor,
+                          packed_down: torch.Tensor, rows: torch.Tensor, row_index: torch.Tensor,
+                          *, d_ff: int, out_dtype: Optional[torch.dtype] = None,
+                          save: bool = False, out: Optional[dict] = None,
+                          workspace: Optional[torch.Tensor] = None, stream=None) -> dict:
+    """staple_ffn_fwd for a decode batch (<= 64 tokens) on packed weights."""
+    _dev(x, packed_gate_up, packed_down, rows, row_index)
+    n, d = x.shape
+    f = d_ff
+    dt = _dt(x)
+    out_dtype = out_dtype or x.dtype
+    if out is None:
+        out = {"y": torch.empty(n, d, dtype=out_dtype, device=x.device)}
+        if save:
+            for k in ("g", "u", "h"):
+                out[k] = torch.empty(n, f, dtype=x.dtype, device=x.device)
+    ws = _ws(lib().staple_ffn_fwd_workspace_bytes(n, d, f, dt), workspace, x.device)
+    _check(lib().staple_ffn_fwd_packed(n, d, f, dt, _DT[out["y"].dtype], _p(x), _p(packed_gate_up),
+                                       _p(packed_down), _p(rows), rows.shape[0], _p(row_index),
+                                       _p(out["y"]), _p(out.get("g")), _p(out.get("u")),
+                                       _p(out.get("h")), _p(ws), _ws_size(ws), _stream(stream)),
+           "staple_ffn_fwd_packed")
+    return out
+
+
+def staple_ffn_gate_up_packed(x: torch.Tensor, packed_gate_up: torch.Tensor, rows: torch.Tensor,
+                              row_index: torch.Tensor, h: torch.Tensor,
+                              save_g: Optional[torch.Tensor] = None,
+                              save_u: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """staple_ffn_gate_up for a decode batch on the packed gate/up weights."""
+    _dev(x, packed_gate_up, rows, row_index, h, save_g, save_u)
+    n, d = x.shape
+    f = h.shape[1]
+    _check(lib().staple_ffn_gate_up_packed(n, d, f, _dt(x), _p(x), _p(packed_gate_up), _p(rows),
+                                           rows.shape[0], _p(row_index), _p(h), _p(save_g),
+                                           _p(save_u), _stream(stream)),
+           "staple_ffn_gate_up_packed")
+    return h
+
+
+def staple_ffn_down_packed(h: torch.Tensor, packed_down: torch.Tensor, y: torch.Tensor,
+                           workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """staple_ffn_down for a decode batch on the packed down weights."""
+    _dev(h, packed_down, y)
+    n, f = h.shape
+    d = y.shape[1]
+    ws = _ws(lib().staple_ffn_down_workspace_bytes(n, d, f, _dt(h)), workspace, h.device)
+    _check(lib().staple_ffn_down_packed(n, d, f, _dt(h), _DT[y.dtype], _p(h), _p(packed_down),
+                                        _p(y), _p(ws), _ws_size(ws), _stream(stream)),
+           "staple_ffn_down_packed")
+    return y
+
+
 def staple_ffn_gate_up(x: torch.Tensor, w_gate: torch.Tensor, w_up: torch.Tensor,
                        rows: torch.Tensor, row_index: torch.Tensor, h: torch.Tensor,
                        save_g: Optional[torch.Tensor] = None, save_u: Optional[torch.Tensor] = None,

@@ -46,6 +46,13 @@ _SIGS = {
     "staple_ffn_down_workspace_bytes": (c_sz, [c_i64, c_i64, c_i64, c_i32]),
     "staple_ffn_down": (c_i32, [c_i64, c_i64, c_i64, c_i32, c_i32, c_vp, c_vp, c_vp, c_vp, c_sz,
                                 c_vp]),
+    "staple_decode_pack_weights": (c_i32, [c_i64, c_i64, c_i32, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp]),
+    "staple_ffn_gate_up_packed": (c_i32, [c_i64, c_i64, c_i64, c_i32, c_vp, c_vp, c_vp, c_i64,
+                                          c_vp, c_vp, c_vp, c_vp, c_vp]),
+    "staple_ffn_down_packed": (c_i32, [c_i64, c_i64, c_i64, c_i32, c_i32, c_vp, c_vp, c_vp, c_vp,
+                                       c_sz, c_vp]),
+    "staple_ffn_fwd_packed": (c_i32, [c_i64, c_i64, c_i64, c_i32, c_i32, c_vp, c_vp, c_vp, c_vp,
+                                      c_i64, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_sz, c_vp]),
     "staple_ffn_bwd_workspace_bytes": (c_sz, [c_i64, c_i64, c_i64, c_i32]),
     "staple_ffn_bwd_table_grad": (c_i32, [c_i64, c_i64, c_i64, c_i32, c_i32, c_vp, c_vp, c_vp,
                                           c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_i64,

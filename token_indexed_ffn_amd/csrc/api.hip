@@ -75,9 +75,11 @@ size_t decode_down_workspace_bytes(int64_t n, int64_t d);
 hipError_t decode_gateup(int64_t n, const int32_t* pos, int64_t n_tokens, int64_t d, int64_t f,
                          const void* x, const void* wg, const void* wu, const void* rows,
                          int64_t n_rows, const int32_t* row_index, void* h, void* g_out,
-                         void* u_out, hipStream_t s, int* err);
+                         void* u_out, hipStream_t s, int* err, bool packed);
 hipError_t decode_down(int64_t n, int64_t d, int64_t f, const void* h, const void* wd, void* y,
-                       int out_dtype, void* ws, hipStream_t s);
+                       int out_dtype, void* ws, hipStream_t s, bool packed);
+hipError_t decode_pack(int64_t d, int64_t f, const void* wg, const void* wu, const void* wd,
+                       void* packed_gu, void* packed_down, hipStream_t s);
 
 // ---------------------------------------------------------------------------
 // Per-device error word
@@ -360,7 +362,7 @@ static staple_status_t gate_up_impl(int64_t n_sel, const int32_t* pos, int64_t n
   GET_ERR(err);
   if (decode_eligible(n_sel, d, f, dtype))
     HIPCALL(decode_gateup(n_sel, pos, n_tokens, d, f, x, w_gate, w_up, rows, n_rows, row_index, h,
-                          save_g, save_u, s, err));
+                          save_g, save_u, s, err, false));
   else if (dtype == STAPLE_BF16)
     HIPCALL(gateup_fwd<bf16_t>(n_sel, pos, n_tokens, d, f, x, w_gate, w_up, rows, n_rows,
                                row_index, h, save_g, save_u, s, err));
@@ -373,7 +375,7 @@ static staple_status_t gate_up_impl(int64_t n_sel, const int32_t* pos, int64_t n
 static staple_status_t down_impl(int64_t n, int64_t d, int64_t f, int32_t dtype, int32_t out_dtype,
                                  const void* h, const void* w_down, void* y, void* ws,
                                  hipStream_t s) {
-  if (decode_eligible(n, d, f, dtype)) HIPCALL(decode_down(n, d, f, h, w_down, y, out_dtype, ws, s));
+  if (decode_eligible(n, d, f, dtype)) HIPCALL(decode_down(n, d, f, h, w_down, y, out_dtype, ws, s, false));
   else if (dtype == STAPLE_BF16) HIPCALL(down_fwd<bf16_t>(n, d, f, h, w_down, y, out_dtype, s));
   else HIPCALL(down_fwd<float>(n, d, f, h, w_down, y, out_dtype, s));
   return STAPLE_OK;
@@ -444,6 +446,79 @@ staple_status_t staple_ffn_fwd(int64_t n, int64_t d, int64_t f, int32_t dtype, i
                                     row_index, h, save_g, save_u, s);
   if (st != STAPLE_OK) return st;
   return down_impl(n, d, f, dtype, out_dtype, h, w_down, y, down_ws, s);
+}
+
+staple_status_t staple_decode_pack_weights(int64_t d, int64_t f, int32_t dtype, const void* w_gate,
+                                           const void* w_up, const void* w_down,
+                                           void* packed_gate_up, void* packed_down, void* stream) {
+  if (dtype != STAPLE_BF16 || !ffn_shape_ok(1, d, f, dtype)) return STAPLE_ERR_UNSUPPORTED;
+  REQUIRE(packed_gate_up || packed_down);
+  REQUIRE(!packed_gate_up || (w_gate && w_up && aligned16(w_gate) && aligned16(w_up) &&
+                              aligned16(packed_gate_up)));
+  REQUIRE(!packed_down || (w_down && aligned16(w_down) && aligned16(packed_down)));
+  HIPCALL(decode_pack(d, f, w_gate, w_up, w_down, packed_gate_up, packed_down, S(stream)));
+  return STAPLE_OK;
+}
+
+staple_status_t staple_ffn_gate_up_packed(int64_t n, int64_t d, int64_t f, int32_t dtype,
+                                          const void* x, const void* packed_gate_up,
+                                          const void* rows, int64_t n_rows,
+                                          const int32_t* row_index, void* h, void* save_g,
+                                          void* save_u, void* stream) {
+  if (dtype != STAPLE_BF16 || !ffn_shape_ok(n, d, f, dtype)) return STAPLE_ERR_UNSUPPORTED;
+  if (n > 0 && !decode_eligible(n, d, f, dtype)) return STAPLE_ERR_UNSUPPORTED;
+  REQUIRE(packed_gate_up && rows && n_rows >= 1);
+  REQUIRE(aligned16(packed_gate_up) && aligned16(rows));
+  if (n == 0) return STAPLE_OK;
+  REQUIRE(x && row_index && h && aligned16(x) && aligned16(h));
+  REQUIRE((!save_g || aligned16(save_g)) && (!save_u || aligned16(save_u)));
+  GET_ERR(err);
+  HIPCALL(decode_gateup(n, nullptr, n, d, f, x, packed_gate_up, nullptr, rows, n_rows, row_index, h,
+                        save_g, save_u, S(stream), err, true));
+  return STAPLE_OK;
+}
+
+staple_status_t staple_ffn_down_packed(int64_t n, int64_t d, int64_t f, int32_t dtype,
+                                       int32_t out_dtype, const void* h, const void* packed_down,
+                                       void* y, void* ws, size_t ws_bytes, void* stream) {
+  if (dtype != STAPLE_BF16 || !valid_dtype(out_dtype) || !ffn_shape_ok(n, d, f, dtype))
+    return STAPLE_ERR_UNSUPPORTED;
+  if (n > 0 && !decode_eligible(n, d, f, dtype)) return STAPLE_ERR_UNSUPPORTED;
+  REQUIRE(packed_down && aligned16(packed_down));
+  if (n == 0) return STAPLE_OK;
+  REQUIRE(h && y && aligned16(h) && aligned16(y));
+  if (ws_bytes < staple_ffn_down_workspace_bytes(n, d, f, dtype)) return STAPLE_ERR_WORKSPACE;
+  REQUIRE(ws && aligned16(ws));
+  HIPCALL(decode_down(n, d, f, h, packed_down, y, out_dtype, ws, S(stream), true));
+  return STAPLE_OK;
+}
+
+staple_status_t staple_ffn_fwd_packed(int64_t n, int64_t d, int64_t f, int32_t dtype,
+                                      int32_t out_dtype, const void* x,
+                                      const void* packed_gate_up, const void* packed_down,
+                                      const void* rows, int64_t n_rows,
+                                      const int32_t* row_index, void* y, void* save_g,
+                                      void* save_u, void* save_h, void* ws, size_t ws_bytes,
+                                      void* stream) {
+  if (dtype != STAPLE_BF16 || !valid_dtype(out_dtype)) return STAPLE_ERR_UNSUPPORTED;
+  if (!ffn_shape_ok(n, d, f, dtype)) return STAPLE_ERR_UNSUPPORTED;
+  if (n > 0 && !decode_eligible(n, d, f, dtype)) return STAPLE_ERR_UNSUPPORTED;
+  REQUIRE(packed_gate_up && packed_down && rows && n_rows >= 1);
+  REQUIRE(aligned16(packed_gate_up) && aligned16(packed_down) && aligned16(rows));
+  if (n == 0) return STAPLE_OK;
+  REQUIRE(x && row_index && y && aligned16(x) && aligned16(y));
+  REQUIRE((!save_g || aligned16(save_g)) && (!save_u || aligned16(save_u)) &&
+          (!save_h || aligned16(save_h)));
+  if (ws_bytes < staple_ffn_fwd_workspace_bytes(n, d, f, dtype)) return STAPLE_ERR_WORKSPACE;
+  REQUIRE(ws && aligned16(ws));
+  void* h = save_h ? save_h : ws;
+  void* down_ws = static_cast<char*>(ws) + align_up(static_cast<size_t>(n) * f * elem_bytes(dtype), 256);
+  hipStream_t s = S(stream);
+  GET_ERR(err);
+  HIPCALL(decode_gateup(n, nullptr, n, d, f, x, packed_gate_up, nullptr, rows, n_rows, row_index, h,
+                        save_g, save_u, s, err, true));
+  HIPCALL(decode_down(n, d, f, h, packed_down, y, out_dtype, down_ws, s, true));
+  return STAPLE_OK;
 }
 
 // workspace of the backward: [dg | du] (n x 2f) then the segment-sum partials

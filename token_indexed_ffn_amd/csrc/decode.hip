@@ -38,11 +38,6 @@ struct Frag2 {
   uint4 v[2];
 };
 
-__device__ __forceinline__ void load_step(Frag2& f, const char* p, int64_t off) {
-  f.v[0] = *reinterpret_cast<const uint4*>(p + off);
-  f.v[1] = *reinterpret_cast<const uint4*>(p + off + 64);
-}
-
 __device__ __forceinline__ bf16x8_t as_bf16x8(const uint4& u) {
   return __builtin_bit_cast(bf16x8_t, u);
 }
@@ -90,11 +85,13 @@ __device__ __forceinline__ int xblock_at(int t, int c) { return t * 128 + ((c ^ 
 // step): loads complete in issue order, so waiting for a step's activation
 // also waits for every weight load issued before it.  `after_prologue` runs
 // once the first steps are in flight.
-template <int WD, int KH, typename RowFn, typename Hook>
-__device__ __forceinline__ void stream_shared_act(const char* pa, const uint16_t* act, int64_t act_ld,
-                                                  RowFn act_row, int n, lds_char* xl, int64_t s0,
-                                                  int64_t s1, int64_t len_max, f32x4_t (&acc)[4],
-                                                  Hook&& after_prologue) {
+// The weight bytes of step s are at pa + s * wstep and pa + s * wstep + JOFF
+// (row-major rows: wstep 128, JOFF 64; packed fragments: JOFF 1024).
+template <int WD, int KH, int JOFF, typename RowFn, typename Hook>
+__device__ __forceinline__ void stream_shared_act(const char* pa, int64_t wstep, const uint16_t* act,
+                                                  int64_t act_ld, RowFn act_row, int n, lds_char* xl,
+                                                  int64_t s0, int64_t s1, int64_t len_max,
+                                                  f32x4_t (&acc)[4], Hook&& after_prologue) {
   constexpr int NB = 4;
   constexpr int U = WD % 2 == 0 ? WD : 2 * WD;          // unrolled steps (even: LDS slot parity)
   constexpr int kSlot = KH * kXBlock;
@@ -112,10 +109,15 @@ __device__ __forceinline__ void stream_shared_act(const char* pa, const uint16_t
   }
   // steps past s1 (or an empty range) re-read a valid step: s1 - 1, or s0 - 1
   // (the previous part's last step) when the range is empty
-  auto off = [&](int64_t s) -> int64_t { return (s < s1 ? s : s1 - 1) * 128; };
+  auto clamp = [&](int64_t s) -> int64_t { return s < s1 ? s : s1 - 1; };
+  auto load_w = [&](Frag2& fr, int64_t s) {
+    const char* p = pa + clamp(s) * wstep;
+    fr.v[0] = *reinterpret_cast<const uint4*>(p);
+    fr.v[1] = *reinterpret_cast<const uint4*>(p + JOFF);
+  };
   auto load_x = [&](uint4 (&dst)[2], int64_t s) {
 #pragma unroll
-    for (int i = 0; i < 2; ++i) dst[i] = *reinterpret_cast<const uint4*>(px[i] + off(s));
+    for (int i = 0; i < 2; ++i) dst[i] = *reinterpret_cast<const uint4*>(px[i] + clamp(s) * 128);
   };
   auto store_x = [&](lds_char* slot, const uint4 (&src)[2]) {
 #pragma unroll
@@ -136,7 +138,7 @@ __device__ __forceinline__ void stream_shared_act(const char* pa, const uint16_t
   uint4 xv[WD][2], x0[2];
   load_x(x0, s0);
 #pragma unroll
-  for (int j = 0; j < WD; ++j) load_step(a[j], pa, off(s0 + j));
+  for (int j = 0; j < WD; ++j) load_w(a[j], s0 + j);
 #pragma unroll
   for (int j = 1; j <= WD; ++j) load_x(xv[j % WD], s0 + j);
   after_prologue();
@@ -168,7 +170,7 @@ __device__ __forceinline__ void stream_shared_act(const char* pa, const uint16_t
       const Frag2 aa[1] = {a[wi]};
       mma_step<1, NB>(aa, b, acc);
       __builtin_amdgcn_sched_barrier(0);
-      load_step(a[wi], pa, off(s + WD));
+      load_w(a[wi], s + WD);
       load_x(xv[(j + 1) % WD], s + 1 + WD);
       lds_barrier();
     }
@@ -217,7 +219,7 @@ __device__ __forceinline__ bool fold_parts(float (*stage)[16 * kStageLd], const 
 // With `pos`, the n tokens of the launch are pos[0 .. n) of the n_tokens rows
 // of x, h, g, u and row_index (out-of-range positions set the error word and
 // are neither read nor written).
-template <int WD, int KH>
+template <int WD, int KH, bool PACKED>
 __global__ __launch_bounds__(256 * KH) void decode_gateup_kernel(
     int n, const int32_t* __restrict__ pos, int64_t n_tokens, int64_t d, int64_t f,
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ wg,
@@ -231,7 +233,11 @@ __global__ __launch_bounds__(256 * KH) void decode_gateup_kernel(
   const int grp = wid & 3, part = wid >> 2;
   const int r = lane & 15, q = lane >> 4;
   const int64_t f0 = static_cast<int64_t>(blockIdx.x) * 32 + 8 * grp;   // this wave's features
-  const char* pa = reinterpret_cast<const char*>(r < 8 ? wg + (f0 + r) * d : wu + (f0 + r - 8) * d) + q * 16;
+  // PACKED: wg is the packed gate/up block (row block = 8 features)
+  const char* pa =
+      PACKED ? reinterpret_cast<const char*>(wg) + (static_cast<int64_t>(blockIdx.x) * 4 + grp) * 2048 + lane * 16
+             : reinterpret_cast<const char*>(r < 8 ? wg + (f0 + r) * d : wu + (f0 + r - 8) * d) + q * 16;
+  const int64_t wstep = PACKED ? (f / 8) * 2048 : 128;
   const int64_t T = d / 64, len = (T + KH - 1) / KH;
   const int64_t s0 = part * len < T ? part * len : T, s1 = s0 + len < T ? s0 + len : T;
   f32x4_t acc[4];
@@ -251,7 +257,8 @@ __global__ __launch_bounds__(256 * KH) void decode_gateup_kernel(
   int64_t ri;
   bool erow_ok;
   uint4 erow;
-  stream_shared_act<WD, KH>(pa, x, d, act_row, n, (lds_char*)(xs), s0, s1, len, acc, [&]() {
+  stream_shared_act<WD, KH, PACKED ? 1024 : 64>(pa, wstep, x, d, act_row, n, (lds_char*)(xs), s0, s1,
+                                                 len, acc, [&]() {
     ri = row_index[tok < 0 ? 0 : tok];
     erow_ok = ri >= 0 && ri < n_rows;
     erow = *reinterpret_cast<const uint4*>(erow_ok ? rows + ri * f + f0 : x);
@@ -308,7 +315,7 @@ __global__ __launch_bounds__(256 * KH) void decode_gateup_kernel(
 // and KH ways inside one: workgroup (output block b of 64, split ks) with
 // wave w owning outputs 64 b + 16 (w % 4) .. +16 over part w / 4 of the
 // split's steps; writes partial[ks][t][n] in fp32.
-template <int WD, int KS, int KH>
+template <int WD, int KS, int KH, bool PACKED>
 __global__ __launch_bounds__(256 * KH) void decode_down_kernel(int n, int64_t d, int64_t f,
                                                                const uint16_t* __restrict__ h,
                                                                const uint16_t* __restrict__ wd,
@@ -326,10 +333,14 @@ __global__ __launch_bounds__(256 * KH) void decode_down_kernel(int n, int64_t d,
   const int64_t len = (k1 - k0 + KH - 1) / KH;
   const int64_t s0 = k0 + part * len < k1 ? k0 + part * len : k1;
   const int64_t s1 = s0 + len < k1 ? s0 + len : k1;
-  const char* pa = reinterpret_cast<const char*>(wd + (n0 + r) * f) + q * 16;
+  // PACKED: wd is the packed down block (row block = 16 outputs)
+  const char* pa =
+      PACKED ? reinterpret_cast<const char*>(wd) + (static_cast<int64_t>(blockIdx.x) * 4 + grp) * 2048 + lane * 16
+             : reinterpret_cast<const char*>(wd + (n0 + r) * f) + q * 16;
+  const int64_t wstep = PACKED ? (d / 16) * 2048 : 128;
   f32x4_t acc[4];
-  stream_shared_act<WD, KH>(pa, h, f, [](int t) -> int64_t { return t; }, n, (lds_char*)(xs), s0,
-                            s1, len, acc, []() {});
+  stream_shared_act<WD, KH, PACKED ? 1024 : 64>(pa, wstep, h, f, [](int t) -> int64_t { return t; }, n,
+                                                 (lds_char*)(xs), s0, s1, len, acc, []() {});
   if (!fold_parts<KH>(stage, acc)) return;
   const float* st = stage[grp];
   const int t = lane;
@@ -363,6 +374,27 @@ __global__ void decode_down_reduce_kernel(int64_t count, int ksplit, const float
   }
 }
 
+// Packed weights for the decode kernels: a [R x K] bf16 operand becomes
+// K/64 steps of R/16 row blocks, each block two 1 KB loads of 64 lanes x 16
+// bytes in the Frag2 pattern: byte ((s * R/16 + rb) * 2 + j) * 1024 + 16 lane
+// holds bytes [128 s + 64 j + 16 (lane / 16), +16) of block row lane % 16.
+// A gate/up row block is features 8 rb .. 8 rb + 8: its rows 0-7 are those
+// rows of W_gate and rows 8-15 those of W_up; a down row block is rows
+// 16 rb .. 16 rb + 16 of W_down.  Step-major order over all row blocks puts
+// what the whole grid reads at one step side by side in HBM, and every load
+// instruction of the decode kernels reads 1 KB of contiguous memory.
+__global__ void decode_pack_kernel(int64_t total, int64_t rb_count, int64_t k, bool gate_up,
+                                   const uint16_t* __restrict__ a, const uint16_t* __restrict__ b,
+                                   uint4* __restrict__ out) {
+  const int64_t c = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (c >= total) return;
+  const int lane = static_cast<int>(c & 63), j = static_cast<int>((c >> 6) & 1);
+  const int64_t blk = c >> 7, rb = blk % rb_count, s = blk / rb_count;
+  const int r = lane & 15, q = lane >> 4;
+  const uint16_t* row = gate_up ? (r < 8 ? a + (8 * rb + r) * k : b + (8 * rb + r - 8) * k) : a + (16 * rb + r) * k;
+  out[c] = *reinterpret_cast<const uint4*>(row + s * 64 + j * 32 + q * 8);
+}
+
 bool decode_eligible(int64_t n, int64_t d, int64_t f, int dtype) {
   return dtype == STAPLE_BF16 && n >= 1 && n <= kDecMaxTokens && d % 64 == 0 && f % 64 == 0;
 }
@@ -386,10 +418,23 @@ constexpr int kGateUpParts = 2;   // d_model split in two inside a gate/up workg
 constexpr int kDownParts = 1;
 static_assert(kDownSplit <= kDownSplitMax, "down partials fit the workspace");
 
+hipError_t decode_pack(int64_t d, int64_t f, const void* wg, const void* wu, const void* wd,
+                       void* packed_gu, void* packed_down, hipStream_t s) {
+  auto go = [&](int64_t rbs, int64_t k, bool gu, const void* a, const void* b, void* out) {
+    const int64_t total = rbs * (k / 64) * 128;
+    decode_pack_kernel<<<dim3(static_cast<unsigned>((total + 255) / 256)), dim3(256), 0, s>>>(
+        total, rbs, k, gu, static_cast<const uint16_t*>(a), static_cast<const uint16_t*>(b),
+        static_cast<uint4*>(out));
+  };
+  if (packed_gu) go(f / 8, d, true, wg, wu, packed_gu);
+  if (packed_down) go(d / 16, f, false, wd, nullptr, packed_down);
+  return hipGetLastError();
+}
+
 hipError_t decode_gateup(int64_t n, const int32_t* pos, int64_t n_tokens, int64_t d, int64_t f,
                          const void* x, const void* wg, const void* wu, const void* rows,
                          int64_t n_rows, const int32_t* row_index, void* h, void* g_out,
-                         void* u_out, hipStream_t s, int* err) {
+                         void* u_out, hipStream_t s, int* err, bool packed) {
   auto go = [&](auto kern, int threads) {
     kern<<<dim3(static_cast<unsigned>(f / 32)), dim3(threads), 0, s>>>(
         static_cast<int>(n), pos, n_tokens, d, f, static_cast<const uint16_t*>(x),
@@ -397,17 +442,21 @@ hipError_t decode_gateup(int64_t n, const int32_t* pos, int64_t n_tokens, int64_
         static_cast<const uint16_t*>(wu), static_cast<const uint16_t*>(rows), n_rows, row_index,
         static_cast<uint16_t*>(h), static_cast<uint16_t*>(g_out), static_cast<uint16_t*>(u_out), err);
   };
-  go(decode_gateup_kernel<kGateUpAhead, kGateUpParts>, 256 * kGateUpParts);
+  if (packed) go(decode_gateup_kernel<kGateUpAhead, kGateUpParts, true>, 256 * kGateUpParts);
+  else go(decode_gateup_kernel<kGateUpAhead, kGateUpParts, false>, 256 * kGateUpParts);
   return hipGetLastError();
 }
 
 hipError_t decode_down(int64_t n, int64_t d, int64_t f, const void* h, const void* wd, void* y,
-                       int out_dtype, void* ws, hipStream_t s) {
+                       int out_dtype, void* ws, hipStream_t s, bool packed) {
   float* partial = static_cast<float*>(ws);
-  decode_down_kernel<kDownAhead, kDownSplit, kDownParts>
-      <<<dim3(static_cast<unsigned>(d / 64), kDownSplit), dim3(256 * kDownParts), 0, s>>>(
-          static_cast<int>(n), d, f, static_cast<const uint16_t*>(h), static_cast<const uint16_t*>(wd),
-          partial);
+  auto go = [&](auto kern) {
+    kern<<<dim3(static_cast<unsigned>(d / 64), kDownSplit), dim3(256 * kDownParts), 0, s>>>(
+        static_cast<int>(n), d, f, static_cast<const uint16_t*>(h), static_cast<const uint16_t*>(wd),
+        partial);
+  };
+  if (packed) go(decode_down_kernel<kDownAhead, kDownSplit, kDownParts, true>);
+  else go(decode_down_kernel<kDownAhead, kDownSplit, kDownParts, false>);
   const int64_t count = n * d;
   const unsigned blocks = static_cast<unsigned>((count / 4 + 255) / 256);
   if (out_dtype == STAPLE_F32)
