@@ -3,27 +3,30 @@
 //
 // Both kernels put the weight matrix on the MFMA's A side (16-row blocks of
 // v_mfma_f32_16x16x32_bf16) and the tokens on the B side (four 16-token
-// tiles).  A 64-wide "macro step" of k is 128 bytes of every row; for the
-// weights, lane (r, q) = (lane % 16, lane / 16) loads its bytes [16q, 16q+16)
-// and [64+16q, 64+16q+16) straight into registers, so each load instruction
-// reads 64 contiguous bytes of 16 rows, and the j-th MFMA of the step takes
-// the j-th load of every lane.  The activation, which every workgroup reads,
-// is loaded as whole cache lines and put into the same fragment pattern
-// through LDS (half the cache-line requests of the fragment pattern).  A and
-// B use the same k order, so the contraction is unchanged.
+// tiles).  A 64-wide "macro step" of k is 128 bytes of every row; lane
+// (r, q) = (lane % 16, lane / 16) holds bytes [16q, 16q+16) and
+// [64+16q, 64+16q+16) of row r, and the j-th MFMA of the step takes the j-th
+// of them.  Weights come either row-major (each load instruction reads 64
+// contiguous bytes of 16 rows) or packed in exactly this order (each load
+// instruction reads 1 KB of contiguous memory; see decode_pack_kernel).  The
+// activation, which every workgroup reads, is loaded by dedicated loader waves
+// as whole cache lines straight into LDS and read back in the fragment
+// pattern, so the compute waves' load queue holds weights only.  A and B use
+// the same k order, so the contraction is unchanged.
 //
-// Gate/up: one workgroup per 32 features; each of its four waves owns the
-// gate and up rows of 8 features over all of d_model, the activation of each
-// step is shared by the waves through LDS, and the epilogue gathers each
-// token's table row, forms u = W_up x + E[t] and h = silu(W_gate x) * u
-// (STAPLE abstract: the up-projection is retained and the embedding added as
-// a residual path; retrieval-path table: row reconstruction fused with the
-// FFN) and stores h with 16-byte vectors.
+// Gate/up: one workgroup per 32 features; each compute wave owns the gate and
+// up rows of 8 features over a part of d_model, the parts are folded in LDS,
+// and the epilogue gathers each token's table row, forms u = W_up x + E[t]
+// and h = silu(W_gate x) * u (STAPLE abstract: the up-projection is retained
+// and the embedding added as a residual path; retrieval-path table: row
+// reconstruction fused with the FFN) and stores h with 16-byte vectors.
 //
 // Down: d_model is too narrow to fill 256 CUs with whole-K tiles, so the K
-// range (d_ff) is split over several workgroups per output block (8 per 64
-// outputs by default); each writes an fp32 partial and a second small kernel
-// sums the partials in split order (deterministic) and stores y.
+// range (d_ff) is split over several workgroups per output block; each writes
+// an fp32 partial and a second small kernel sums the partials in split order
+// (deterministic) and stores y.
+#include <type_traits>
+
 #include "common.h"
 
 namespace staple {
@@ -60,99 +63,116 @@ __device__ __forceinline__ void mma_step(const Frag2 (&a)[NA], const Frag2 (&b)[
 typedef __attribute__((address_space(3))) u32x4_t lds_u32x4;
 
 // The activation block of one macro step in LDS: 64 tokens x 128 bytes, token
-// t's 16-byte chunk c at t * 128 + ((c ^ ((t >> 1) & 7)) << 4).  It is loaded
-// from global memory with eight 1 KB instructions that each cover 8 whole
-// tokens x 128 bytes (full cache lines), written to LDS and read back in the
-// Frag2 pattern; the XOR keeps every 16-lane group of both the writes and the
-// reads on distinct banks.
+// t's 16-byte chunk c at t * 128 + ((c ^ ((t >> 1) & 7)) << 4); the XOR keeps
+// every 16-lane group of the Frag2-pattern reads on distinct banks.  It is
+// loaded straight from global memory into LDS by eight 1 KB instructions,
+// load i covering tokens 8i .. 8i+7 as whole cache lines: lane l writes LDS
+// bytes 1024 i + 16 l, i.e. token 8i + l / 8 at position l % 8, so it fetches
+// the chunk that position holds, (l % 8) ^ ((t >> 1) & 7).
 constexpr int kXBlock = 64 * 128;
 
 __device__ __forceinline__ int xblock_at(int t, int c) { return t * 128 + ((c ^ ((t >> 1) & 7)) << 4); }
 
-// One wave's 16 weight rows (pa: the lane's bytes at step 0) times the
-// activation of at most 64 tokens over macro steps [s0, s1).  The workgroup
-// has 4 KH waves: waves w and w + 4 k (k < KH) stream the same 16 rows over
-// KH parts of the K range (part k = wid / 4), and the four waves of one part
-// share its activation: each step's block (64 tokens x 128 bytes, act[t]:
-// token t's row) is loaded once per part as whole cache lines (two 1 KB loads
-// per wave: tokens 16 (wid % 4) + l / 8 and 16 (wid % 4) + 8 + l / 8, chunk
-// l % 8; act_row(t) gives the row of act that holds token t), written to one
-// of two LDS slots (`xl`, 2 x KH x kXBlock bytes) and read by the part's four
-// waves; one barrier per step hands a slot over.
-// Every wave runs the same number of steps, `len_max` (waves with fewer read
-// their last step again with zeroed weights), so the barriers match.
-// Weights and activations are loaded WD steps ahead (8 + 8 registers per
-// step): loads complete in issue order, so waiting for a step's activation
-// also waits for every weight load issued before it.  `after_prologue` runs
-// once the first steps are in flight.
-// The weight bytes of step s are at pa + s * wstep and pa + s * wstep + JOFF
-// (row-major rows: wstep 128, JOFF 64; packed fragments: JOFF 1024).
-template <int WD, int KH, int JOFF, typename RowFn, typename Hook>
-__device__ __forceinline__ void stream_shared_act(const char* pa, int64_t wstep, const uint16_t* act,
-                                                  int64_t act_ld, RowFn act_row, int n, lds_char* xl,
-                                                  int64_t s0, int64_t s1, int64_t len_max,
-                                                  f32x4_t (&acc)[4], Hook&& after_prologue) {
-  constexpr int NB = 4;
-  constexpr int U = WD % 2 == 0 ? WD : 2 * WD;          // unrolled steps (even: LDS slot parity)
+// Activation ring: A steps in flight, one more slot than that (A + 1 slots)
+// so the slot a load lands in was read two barriers earlier.
+
+// Roles in a decode workgroup of 5 KH waves: waves 0 .. 4 KH - 1 compute
+// (row group w % 4, K part w / 4); wave 4 KH + p loads part p's activation.
+struct WaveRole {
+  bool loader;
+  int grp, part;
+};
+template <int KH>
+__device__ __forceinline__ WaveRole wave_role() {
+  const int wid = threadIdx.x >> 6;
+  if (wid >= 4 * KH) return {true, 0, wid - 4 * KH};
+  return {false, wid & 3, wid >> 2};
+}
+
+// One compute wave's 16 weight rows (pa: the lane's bytes at step 0; step s
+// at pa + s * wstep and pa + s * wstep + JOFF: row-major rows have wstep 128
+// and JOFF 64, packed fragments JOFF 1024) times the activation of at most 64
+// tokens (act[act_row(t)]: token t's row) over macro steps [s0, s1) of its K
+// part; acc[k] is token tile k.
+//
+// The four compute waves of a part share the part's activation, which its
+// loader wave brings into a ring of A + 1 LDS slots (kXBlock per part) with
+// global-to-LDS loads A steps ahead, waiting on its own load counter only.  Compute waves issue only weight loads (WD steps ahead, 8
+// registers per step), so a weight wait never waits behind activation loads
+// and the reverse.  One barrier per step: before barrier i the loader's step
+// i + 1 has landed, and its next load targets the slot read at step i - 1.
+// Every wave runs the same number of steps, `len_max` (steps past s1 re-read
+// the last valid step with zeroed weights), so the barriers match.
+// `after_prologue` runs on compute waves once their first loads are issued.
+template <int WD, int A, int KH, int JOFF, typename RowFn, typename Hook>
+__device__ __forceinline__ void stream_act_ring(WaveRole role, const char* pa, int64_t wstep,
+                                                const uint16_t* act, int64_t act_ld, RowFn act_row,
+                                                int n, lds_char* xl, int64_t s0, int64_t s1,
+                                                int64_t len_max, f32x4_t (&acc)[4],
+                                                Hook&& after_prologue) {
+  constexpr int NB = 4, NS = A + 1;
+  constexpr int U = NS % WD == 0 ? NS : NS * WD;   // unrolled steps: static slot and register indices
   constexpr int kSlot = KH * kXBlock;
   const int lane = threadIdx.x & 63;
-  const int wid = threadIdx.x >> 6;
-  const int grp = wid & 3, part = wid >> 2;
-  const int r = lane & 15, q = lane >> 4;
-  const char* px[2];
-  int wofs[2];
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int tt = 16 * grp + 8 * i + (lane >> 3);
-    px[i] = reinterpret_cast<const char*>(act + act_row(min(tt, n - 1)) * act_ld) + (lane & 7) * 16;
-    wofs[i] = part * kXBlock + xblock_at(tt, lane & 7);
-  }
-  // steps past s1 (or an empty range) re-read a valid step: s1 - 1, or s0 - 1
-  // (the previous part's last step) when the range is empty
   auto clamp = [&](int64_t s) -> int64_t { return s < s1 ? s : s1 - 1; };
-  auto load_w = [&](Frag2& fr, int64_t s) {
-    const char* p = pa + clamp(s) * wstep;
-    fr.v[0] = *reinterpret_cast<const uint4*>(p);
-    fr.v[1] = *reinterpret_cast<const uint4*>(p + JOFF);
-  };
-  auto load_x = [&](uint4 (&dst)[2], int64_t s) {
-#pragma unroll
-    for (int i = 0; i < 2; ++i) dst[i] = *reinterpret_cast<const uint4*>(px[i] + clamp(s) * 128);
-  };
-  auto store_x = [&](lds_char* slot, const uint4 (&src)[2]) {
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-      *reinterpret_cast<lds_u32x4*>(slot + wofs[i]) = __builtin_bit_cast(u32x4_t, src[i]);
-  };
 #pragma unroll
   for (int k = 0; k < NB; ++k)
 #pragma unroll
     for (int i = 0; i < 4; ++i) acc[k][i] = 0.0f;
   if (len_max <= 0) {   // uniform over the workgroup
-    after_prologue();
+    if (!role.loader) after_prologue();
+    return;
+  }
+  const int64_t ngroups = (len_max + U - 1) / U;
+
+  if (role.loader) {
+    const char* px[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int t = 8 * i + (lane >> 3);
+      const int chunk = (lane & 7) ^ ((t >> 1) & 7);
+      px[i] = reinterpret_cast<const char*>(act + act_row(min(t, n - 1)) * act_ld) + chunk * 16;
+    }
+    lds_char* base = xl + role.part * kXBlock;
+    auto issue = [&](int64_t s, int slot) {
+      const int64_t o = clamp(s) * 128;
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        __builtin_amdgcn_global_load_lds(static_cast<const void*>(px[i] + o),
+                                         static_cast<lds_void*>(base + slot * kSlot + i * 1024), 16, 0, 0);
+    };
+#pragma unroll
+    for (int j = 0; j < A; ++j) issue(s0 + j, j);
+    wait_vmcnt<8 * (A - 1)>();
+    lds_barrier();
+    for (int64_t it = 0; it < ngroups; ++it) {
+#pragma unroll
+      for (int j = 0; j < U; ++j) {
+        issue(s0 + it * U + j + A, (j + A) % NS);
+        wait_vmcnt<8 * (A - 1)>();
+        lds_barrier();
+      }
+    }
     return;
   }
 
-  // step s0 goes to slot 0 now; steps s0+1 .. s0+WD wait in xv[(s - s0) % WD]
+  const int r = lane & 15, q = lane >> 4;
+  auto load_w = [&](Frag2& fr, int64_t s) {
+    const char* p = pa + clamp(s) * wstep;
+    fr.v[0] = *reinterpret_cast<const uint4*>(p);
+    fr.v[1] = *reinterpret_cast<const uint4*>(p + JOFF);
+  };
   Frag2 a[WD];
-  uint4 xv[WD][2], x0[2];
-  load_x(x0, s0);
 #pragma unroll
   for (int j = 0; j < WD; ++j) load_w(a[j], s0 + j);
-#pragma unroll
-  for (int j = 1; j <= WD; ++j) load_x(xv[j % WD], s0 + j);
   after_prologue();
-  store_x(xl, x0);
-  __syncthreads();
-
-  const int64_t ngroups = (len_max + U - 1) / U;
+  lds_barrier();
   for (int64_t it = 0; it < ngroups; ++it) {
 #pragma unroll
     for (int j = 0; j < U; ++j) {
       const int64_t s = s0 + it * U + j;
       __builtin_amdgcn_sched_barrier(0);
-      store_x(xl + ((j + 1) & 1) * kSlot, xv[(j + 1) % WD]);   // step s+1
-      const lds_char* cur = xl + (j & 1) * kSlot + part * kXBlock;
+      const lds_char* cur = xl + (j % NS) * kSlot + role.part * kXBlock;
       Frag2 b[NB];
 #pragma unroll
       for (int k = 0; k < NB; ++k) {
@@ -171,7 +191,6 @@ __device__ __forceinline__ void stream_shared_act(const char* pa, int64_t wstep,
       mma_step<1, NB>(aa, b, acc);
       __builtin_amdgcn_sched_barrier(0);
       load_w(a[wi], s + WD);
-      load_x(xv[(j + 1) % WD], s + 1 + WD);
       lds_barrier();
     }
   }
@@ -195,42 +214,43 @@ __device__ __forceinline__ void stage_wave_rows(float* st, const f32x4_t (&acc)[
     }
 }
 
-// Folds the KH parts of a workgroup's K range: the part-k waves (k >= 1) add
-// their sums into the staged rows of their row group in part order; on return
-// stage[wid % 4] holds the full sums and only part-0 waves go on.
+// Folds the KH parts of a workgroup's K range: the part-k compute waves
+// (k >= 1) add their sums into the staged rows of their row group in part
+// order; loader waves only join the barriers.  On return stage[grp] holds the
+// full sums and only part-0 compute waves go on.
 template <int KH>
-__device__ __forceinline__ bool fold_parts(float (*stage)[16 * kStageLd], const f32x4_t (&acc)[4]) {
-  const int wid = threadIdx.x >> 6;
-  const int grp = wid & 3, part = wid >> 2;
-  if (part == 0) stage_wave_rows(stage[grp], acc);
+__device__ __forceinline__ bool fold_parts(WaveRole role, float (*stage)[16 * kStageLd],
+                                           const f32x4_t (&acc)[4]) {
+  if (!role.loader && role.part == 0) stage_wave_rows(stage[role.grp], acc);
 #pragma unroll
   for (int k = 1; k < KH; ++k) {
     __syncthreads();
-    if (part == k) stage_wave_rows<true>(stage[grp], acc);
+    if (!role.loader && role.part == k) stage_wave_rows<true>(stage[role.grp], acc);
   }
   if constexpr (KH > 1) __syncthreads();
-  return part == 0;
+  return !role.loader && role.part == 0;
 }
 
 // Gate/up for at most 64 tokens, features split over the waves: one
-// workgroup (4 KH waves) per 32 features; wave w owns the gate and up rows of
-// features 8 (w % 4) .. +8 (one 16-row MFMA block: 8 gate rows, then 8 up
-// rows) over part w / 4 of d_model, and the KH parts are folded in LDS.
+// workgroup (4 KH compute waves and KH activation loaders) per 32 features;
+// compute wave w owns the gate and up rows of features 8 (w % 4) .. +8 (one
+// 16-row MFMA block: 8 gate rows, then 8 up rows) over part w / 4 of d_model,
+// and the KH parts are folded in LDS.
 // With `pos`, the n tokens of the launch are pos[0 .. n) of the n_tokens rows
 // of x, h, g, u and row_index (out-of-range positions set the error word and
 // are neither read nor written).
-template <int WD, int KH, bool PACKED>
-__global__ __launch_bounds__(256 * KH) void decode_gateup_kernel(
+template <int WD, int A, int KH, bool PACKED>
+__global__ __launch_bounds__(320 * KH) void decode_gateup_kernel(
     int n, const int32_t* __restrict__ pos, int64_t n_tokens, int64_t d, int64_t f,
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ wg,
     const uint16_t* __restrict__ wu, const uint16_t* __restrict__ rows, int64_t n_rows,
     const int32_t* __restrict__ row_index, uint16_t* __restrict__ h, uint16_t* __restrict__ g_out,
     uint16_t* __restrict__ u_out, int* err) {
-  __shared__ __attribute__((aligned(16))) char xs[2 * KH * kXBlock];
+  __shared__ __attribute__((aligned(16))) char xs[(A + 1) * KH * kXBlock];
   __shared__ float stage[4][16 * kStageLd];
   const int lane = threadIdx.x & 63;
-  const int wid = threadIdx.x >> 6;
-  const int grp = wid & 3, part = wid >> 2;
+  const WaveRole role = wave_role<KH>();
+  const int grp = role.grp, part = role.part;
   const int r = lane & 15, q = lane >> 4;
   const int64_t f0 = static_cast<int64_t>(blockIdx.x) * 32 + 8 * grp;   // this wave's features
   // PACKED: wg is the packed gate/up block (row block = 8 features)
@@ -257,8 +277,8 @@ __global__ __launch_bounds__(256 * KH) void decode_gateup_kernel(
   int64_t ri;
   bool erow_ok;
   uint4 erow;
-  stream_shared_act<WD, KH, PACKED ? 1024 : 64>(pa, wstep, x, d, act_row, n, (lds_char*)(xs), s0, s1,
-                                                 len, acc, [&]() {
+  stream_act_ring<WD, A, KH, PACKED ? 1024 : 64>(role, pa, wstep, x, d, act_row, n, (lds_char*)(xs), s0,
+                                               s1, len, acc, [&]() {
     ri = row_index[tok < 0 ? 0 : tok];
     erow_ok = ri >= 0 && ri < n_rows;
     erow = *reinterpret_cast<const uint4*>(erow_ok ? rows + ri * f + f0 : x);
@@ -266,7 +286,7 @@ __global__ __launch_bounds__(256 * KH) void decode_gateup_kernel(
 
   // epilogue: rows 0-7 (gate) and 8-15 (up) of the row group's block, staged
   // so that lane t holds its token's 8 gate and 8 up sums
-  if (!fold_parts<KH>(stage, acc)) return;
+  if (!fold_parts<KH>(role, stage, acc)) return;
   const float* st = stage[grp];
   const int t = lane;
   if (t >= n) return;
@@ -313,18 +333,19 @@ __global__ __launch_bounds__(256 * KH) void decode_gateup_kernel(
 
 // Down projection for at most 64 tokens, d_ff split KS ways over workgroups
 // and KH ways inside one: workgroup (output block b of 64, split ks) with
-// wave w owning outputs 64 b + 16 (w % 4) .. +16 over part w / 4 of the
-// split's steps; writes partial[ks][t][n] in fp32.
-template <int WD, int KS, int KH, bool PACKED>
-__global__ __launch_bounds__(256 * KH) void decode_down_kernel(int n, int64_t d, int64_t f,
+// compute wave w owning outputs 64 b + 16 (w % 4) .. +16 over part w / 4 of
+// the split's steps (plus KH activation loaders); writes partial[ks][t][n] in
+// fp32.
+template <int WD, int A, int KS, int KH, bool PACKED>
+__global__ __launch_bounds__(320 * KH) void decode_down_kernel(int n, int64_t d, int64_t f,
                                                                const uint16_t* __restrict__ h,
                                                                const uint16_t* __restrict__ wd,
                                                                float* __restrict__ partial) {
-  __shared__ __attribute__((aligned(16))) char xs[2 * KH * kXBlock];
+  __shared__ __attribute__((aligned(16))) char xs[(A + 1) * KH * kXBlock];
   __shared__ float stage[4][16 * kStageLd];
   const int lane = threadIdx.x & 63;
-  const int wid = threadIdx.x >> 6;
-  const int grp = wid & 3, part = wid >> 2;
+  const WaveRole role = wave_role<KH>();
+  const int grp = role.grp, part = role.part;
   const int r = lane & 15, q = lane >> 4;
   const int64_t n0 = static_cast<int64_t>(blockIdx.x) * 64 + 16 * grp;
   const int ks = blockIdx.y;
@@ -339,9 +360,9 @@ __global__ __launch_bounds__(256 * KH) void decode_down_kernel(int n, int64_t d,
              : reinterpret_cast<const char*>(wd + (n0 + r) * f) + q * 16;
   const int64_t wstep = PACKED ? (d / 16) * 2048 : 128;
   f32x4_t acc[4];
-  stream_shared_act<WD, KH, PACKED ? 1024 : 64>(pa, wstep, h, f, [](int t) -> int64_t { return t; }, n,
-                                                 (lds_char*)(xs), s0, s1, len, acc, []() {});
-  if (!fold_parts<KH>(stage, acc)) return;
+  stream_act_ring<WD, A, KH, PACKED ? 1024 : 64>(role, pa, wstep, h, f, [](int t) -> int64_t { return t; },
+                                               n, (lds_char*)(xs), s0, s1, len, acc, []() {});
+  if (!fold_parts<KH>(role, stage, acc)) return;
   const float* st = stage[grp];
   const int t = lane;
   if (t >= n) return;
@@ -403,20 +424,25 @@ size_t decode_down_workspace_bytes(int64_t n, int64_t d) {
   return static_cast<size_t>(kDownSplitMax) * n * d * sizeof(float);
 }
 
-// Launch shapes of the two decode kernels.
-// Launch shapes (measured on MI355X for d_model 2048 / d_ff 8192, batch 64):
-// gate/up on 8 waves (d_model in two parts) with two steps in flight per
-// wave, down on 4 waves with four steps in flight and d_ff split 8 ways over
-// workgroups.
-// Deeper prefetch, 2 or 4 steps per barrier, 4 splits, and the earlier
-// layouts that split d_model (or d_ff) over the waves of a workgroup and
-// folded their partial sums in LDS all measured slower.
-constexpr int kGateUpAhead = 2;   // steps in flight per wave
-constexpr int kDownAhead = 4;
-constexpr int kDownSplit = 8;
-constexpr int kGateUpParts = 2;   // d_model split in two inside a gate/up workgroup (8 waves)
-constexpr int kDownParts = 1;
-static_assert(kDownSplit <= kDownSplitMax, "down partials fit the workspace");
+// Launch shapes of the two decode kernels (measured on MI355X, batch 64,
+// d_model 2048 / d_ff 8192 and 4096 / 11008): gate/up on 8 waves (d_model in
+// two parts) with two steps in flight per wave; down on 4 waves with four
+// steps in flight and d_ff split over about one workgroup per CU (8 ways for
+// 32 output blocks, 4 for 64, 2 from 128 on).
+// Deeper prefetch, 2 or 4 steps per barrier, other split counts, and the
+// earlier layouts that split d_model (or d_ff) over the waves of a workgroup
+// and folded their partial sums in LDS all measured slower.
+constexpr int kGateUpAhead = 2;      // weight steps in flight per compute wave
+constexpr int kGateUpActAhead = 3;   // activation steps in flight per loader wave
+constexpr int kGateUpParts = 2;      // d_model split in two inside a gate/up workgroup
+constexpr int kDownAhead = 2;
+constexpr int kDownActAhead = 3;
+constexpr int kDownParts = 2;
+
+int decode_down_splits(int64_t d) {
+  const int64_t blocks = d / 64;
+  return blocks <= 32 ? 8 : blocks <= 64 ? 4 : 2;
+}
 
 hipError_t decode_pack(int64_t d, int64_t f, const void* wg, const void* wu, const void* wd,
                        void* packed_gu, void* packed_down, hipStream_t s) {
@@ -442,28 +468,34 @@ hipError_t decode_gateup(int64_t n, const int32_t* pos, int64_t n_tokens, int64_
         static_cast<const uint16_t*>(wu), static_cast<const uint16_t*>(rows), n_rows, row_index,
         static_cast<uint16_t*>(h), static_cast<uint16_t*>(g_out), static_cast<uint16_t*>(u_out), err);
   };
-  if (packed) go(decode_gateup_kernel<kGateUpAhead, kGateUpParts, true>, 256 * kGateUpParts);
-  else go(decode_gateup_kernel<kGateUpAhead, kGateUpParts, false>, 256 * kGateUpParts);
+  if (packed) go(decode_gateup_kernel<kGateUpAhead, kGateUpActAhead, kGateUpParts, true>, 320 * kGateUpParts);
+  else go(decode_gateup_kernel<kGateUpAhead, kGateUpActAhead, kGateUpParts, false>, 320 * kGateUpParts);
   return hipGetLastError();
 }
 
 hipError_t decode_down(int64_t n, int64_t d, int64_t f, const void* h, const void* wd, void* y,
                        int out_dtype, void* ws, hipStream_t s, bool packed) {
   float* partial = static_cast<float*>(ws);
+  const int ks = decode_down_splits(d);
   auto go = [&](auto kern) {
-    kern<<<dim3(static_cast<unsigned>(d / 64), kDownSplit), dim3(256 * kDownParts), 0, s>>>(
+    kern<<<dim3(static_cast<unsigned>(d / 64), ks), dim3(320 * kDownParts), 0, s>>>(
         static_cast<int>(n), d, f, static_cast<const uint16_t*>(h), static_cast<const uint16_t*>(wd),
         partial);
   };
-  if (packed) go(decode_down_kernel<kDownAhead, kDownSplit, kDownParts, true>);
-  else go(decode_down_kernel<kDownAhead, kDownSplit, kDownParts, false>);
+  auto pick = [&](auto packed_tag) {
+    constexpr bool P = decltype(packed_tag)::value;
+    if (ks == 8) go(decode_down_kernel<kDownAhead, kDownActAhead, 8, kDownParts, P>);
+    else if (ks == 4) go(decode_down_kernel<kDownAhead, kDownActAhead, 4, kDownParts, P>);
+    else go(decode_down_kernel<kDownAhead, kDownActAhead, 2, kDownParts, P>);
+  };
+  if (packed) pick(std::true_type{});
+  else pick(std::false_type{});
   const int64_t count = n * d;
   const unsigned blocks = static_cast<unsigned>((count / 4 + 255) / 256);
   if (out_dtype == STAPLE_F32)
-    decode_down_reduce_kernel<float><<<blocks, 256, 0, s>>>(count, kDownSplit, partial,
-                                                            static_cast<float*>(y));
+    decode_down_reduce_kernel<float><<<blocks, 256, 0, s>>>(count, ks, partial, static_cast<float*>(y));
   else
-    decode_down_reduce_kernel<uint16_t><<<blocks, 256, 0, s>>>(count, kDownSplit, partial,
+    decode_down_reduce_kernel<uint16_t><<<blocks, 256, 0, s>>>(count, ks, partial,
                                                                static_cast<uint16_t*>(y));
   return hipGetLastError();
 }
