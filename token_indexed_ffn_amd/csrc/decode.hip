@@ -347,8 +347,12 @@ __global__ __launch_bounds__(320 * KH) void decode_down_kernel(int n, int64_t d,
   const WaveRole role = wave_role<KH>();
   const int grp = role.grp, part = role.part;
   const int r = lane & 15, q = lane >> 4;
-  const int64_t n0 = static_cast<int64_t>(blockIdx.x) * 64 + 16 * grp;
-  const int ks = blockIdx.y;
+  // workgroup id -> (split, output block) split-minor: consecutive ids go to
+  // different XCDs, so each XCD's workgroups share few d_ff slices of h and
+  // fetch only those into their L2
+  const int ks = static_cast<int>(blockIdx.x % KS);
+  const int64_t blk = blockIdx.x / KS;
+  const int64_t n0 = blk * 64 + 16 * grp;
   const int64_t T = f / 64;
   const int64_t k0 = T * ks / KS, k1 = T * (ks + 1) / KS;
   const int64_t len = (k1 - k0 + KH - 1) / KH;
@@ -356,7 +360,7 @@ __global__ __launch_bounds__(320 * KH) void decode_down_kernel(int n, int64_t d,
   const int64_t s1 = s0 + len < k1 ? s0 + len : k1;
   // PACKED: wd is the packed down block (row block = 16 outputs)
   const char* pa =
-      PACKED ? reinterpret_cast<const char*>(wd) + (static_cast<int64_t>(blockIdx.x) * 4 + grp) * 2048 + lane * 16
+      PACKED ? reinterpret_cast<const char*>(wd) + (blk * 4 + grp) * 2048 + lane * 16
              : reinterpret_cast<const char*>(wd + (n0 + r) * f) + q * 16;
   const int64_t wstep = PACKED ? (d / 16) * 2048 : 128;
   f32x4_t acc[4];
@@ -478,7 +482,7 @@ hipError_t decode_down(int64_t n, int64_t d, int64_t f, const void* h, const voi
   float* partial = static_cast<float*>(ws);
   const int ks = decode_down_splits(d);
   auto go = [&](auto kern) {
-    kern<<<dim3(static_cast<unsigned>(d / 64), ks), dim3(320 * kDownParts), 0, s>>>(
+    kern<<<dim3(static_cast<unsigned>(d / 64 * ks)), dim3(320 * kDownParts), 0, s>>>(
         static_cast<int>(n), d, f, static_cast<const uint16_t*>(h), static_cast<const uint16_t*>(wd),
         partial);
   };
