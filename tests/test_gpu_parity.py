@@ -195,7 +195,7 @@ def test_row_copies_refuse_pageable_host_memory(st, dev):
 @pytest.mark.parametrize("n,d,f,dtype,capacity", [
     (1000, 256, 512, "bf16", 0), (1000, 256, 512, "bf16", 120), (1000, 256, 512, "bf16", 2000),
     (64, 256, 512, "bf16", 60), (20, 128, 256, "bf16", 2000), (37, 128, 256, "bf16", 0),
-    (300, 128, 256, "f32", 90)])
+    (300, 128, 256, "f32", 90), (48, 64, 11008, "bf16", 300)])
 def test_split_gate_up_matches_whole_batch_bitwise(st, dev, n, d, f, dtype, capacity):
     """The cached tokens' gate/up (rows from the cache slots) and the missed
     tokens' gate/up (rows from the staged misses) together give the bits of
@@ -416,10 +416,13 @@ def test_decode_pack_is_the_documented_permutation(st, dev, d, f):
                                   _packed_expected(raw["wd"], None, 16))
 
 
-@pytest.mark.parametrize("n,d,f", [(1, 256, 512), (17, 192, 320), (64, 256, 512), (33, 64, 64)])
+@pytest.mark.parametrize("n,d,f", [(1, 256, 512), (17, 192, 320), (64, 256, 512), (33, 64, 64),
+                                   (64, 128, 11008), (17, 64, 11008)])
 def test_ffn_fwd_packed_matches_oracle_and_row_major_bitwise(st, dev, n, d, f):
     """The decode forward on packed weights gives the oracle's y, h, g, u and
-    the same bits as staple_ffn_fwd on the row-major weights."""
+    the same bits as staple_ffn_fwd on the row-major weights.  d_ff 11008 has
+    more 8-feature groups than four per CU, so gate/up runs six groups per
+    workgroup with a partly empty last workgroup."""
     import torch
     _log(f"packed decode n={n} d={d} f={f}")
     inp = S.host_layer_inputs(n, d, f, 300, dtype="bf16", seed=40 + n)

@@ -25,6 +25,7 @@
 // range (d_ff) is split over several workgroups per output block; each writes
 // an fp32 partial and a second small kernel sums the partials in split order
 // (deterministic) and stores y.
+#include <atomic>
 #include <type_traits>
 
 #include "common.h"
@@ -76,17 +77,18 @@ __device__ __forceinline__ int xblock_at(int t, int c) { return t * 128 + ((c ^ 
 // Activation ring: A steps in flight, one more slot than that (A + 1 slots)
 // so the slot a load lands in was read two barriers earlier.
 
-// Roles in a decode workgroup of 5 KH waves: waves 0 .. 4 KH - 1 compute
-// (row group w % 4, K part w / 4); wave 4 KH + p loads part p's activation.
+// Roles in a decode workgroup of (G + 1) KH waves: waves 0 .. G KH - 1
+// compute (row group w % G, K part w / G); wave G KH + p loads part p's
+// activation.
 struct WaveRole {
   bool loader;
   int grp, part;
 };
-template <int KH>
+template <int G, int KH>
 __device__ __forceinline__ WaveRole wave_role() {
   const int wid = threadIdx.x >> 6;
-  if (wid >= 4 * KH) return {true, 0, wid - 4 * KH};
-  return {false, wid & 3, wid >> 2};
+  if (wid >= G * KH) return {true, 0, wid - G * KH};
+  return {false, wid % G, wid / G};
 }
 
 // One compute wave's 16 weight rows (pa: the lane's bytes at step 0; step s
@@ -102,10 +104,12 @@ __device__ __forceinline__ WaveRole wave_role() {
 // and the reverse.  One barrier per step: before barrier i the loader's step
 // i + 1 has landed, and its next load targets the slot read at step i - 1.
 // Every wave runs the same number of steps, `len_max` (steps past s1 re-read
-// the last valid step with zeroed weights), so the barriers match.
+// the last valid step with zeroed weights), so the barriers match; a compute
+// wave with `active` false (a row group past the end of the matrix, pa still
+// pointing at valid memory) runs them with zeroed weights too.
 // `after_prologue` runs on compute waves once their first loads are issued.
 template <int WD, int A, int KH, int JOFF, typename RowFn, typename Hook>
-__device__ __forceinline__ void stream_act_ring(WaveRole role, const char* pa, int64_t wstep,
+__device__ __forceinline__ void stream_act_ring(WaveRole role, bool active, const char* pa, int64_t wstep,
                                                 const uint16_t* act, int64_t act_ld, RowFn act_row,
                                                 int n, lds_char* xl, int64_t s0, int64_t s1,
                                                 int64_t len_max, f32x4_t (&acc)[4],
@@ -181,7 +185,7 @@ __device__ __forceinline__ void stream_act_ring(WaveRole role, const char* pa, i
         b[k].v[1] = __builtin_bit_cast(uint4, *reinterpret_cast<const lds_u32x4*>(cur + xblock_at(t, q + 4)));
       }
       const int wi = j % WD;
-      const uint32_t keep = (s < s1) ? 0xffffffffu : 0u;
+      const uint32_t keep = (active && s < s1) ? 0xffffffffu : 0u;
 #pragma unroll
       for (int jj = 0; jj < 2; ++jj) {
         a[wi].v[jj].x &= keep; a[wi].v[jj].y &= keep;
@@ -217,7 +221,8 @@ __device__ __forceinline__ void stage_wave_rows(float* st, const f32x4_t (&acc)[
 // Folds the KH parts of a workgroup's K range: the part-k compute waves
 // (k >= 1) add their sums into the staged rows of their row group in part
 // order; loader waves only join the barriers.  On return stage[grp] holds the
-// full sums and only part-0 compute waves go on.
+// full sums and only part-0 compute waves go on.  (stage: one 16-row block
+// per row group.)
 template <int KH>
 __device__ __forceinline__ bool fold_parts(WaveRole role, float (*stage)[16 * kStageLd],
                                            const f32x4_t (&acc)[4]) {
@@ -232,37 +237,40 @@ __device__ __forceinline__ bool fold_parts(WaveRole role, float (*stage)[16 * kS
 }
 
 // Gate/up for at most 64 tokens, features split over the waves: one
-// workgroup (4 KH compute waves and KH activation loaders) per 32 features;
-// compute wave w owns the gate and up rows of features 8 (w % 4) .. +8 (one
-// 16-row MFMA block: 8 gate rows, then 8 up rows) over part w / 4 of d_model,
-// and the KH parts are folded in LDS.
+// workgroup (G KH compute waves and KH activation loaders) per 8 G features;
+// compute wave w owns the gate and up rows of features 8 (w % G) .. +8 of the
+// workgroup (one 16-row MFMA block: 8 gate rows, then 8 up rows) over part
+// w / G of d_model, and the KH parts are folded in LDS.  Row groups past f
+// (in the last workgroup when f / 8 is not a multiple of G) stream nothing
+// and store nothing.
 // With `pos`, the n tokens of the launch are pos[0 .. n) of the n_tokens rows
 // of x, h, g, u and row_index (out-of-range positions set the error word and
 // are neither read nor written).
-template <int WD, int A, int KH, bool PACKED>
-__global__ __launch_bounds__(320 * KH) void decode_gateup_kernel(
+template <int WD, int A, int G, int KH, bool PACKED>
+__global__ __launch_bounds__(64 * (G + 1) * KH) void decode_gateup_kernel(
     int n, const int32_t* __restrict__ pos, int64_t n_tokens, int64_t d, int64_t f,
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ wg,
     const uint16_t* __restrict__ wu, const uint16_t* __restrict__ rows, int64_t n_rows,
     const int32_t* __restrict__ row_index, uint16_t* __restrict__ h, uint16_t* __restrict__ g_out,
     uint16_t* __restrict__ u_out, int* err) {
   __shared__ __attribute__((aligned(16))) char xs[(A + 1) * KH * kXBlock];
-  __shared__ float stage[4][16 * kStageLd];
+  __shared__ float stage[G][16 * kStageLd];
   const int lane = threadIdx.x & 63;
-  const WaveRole role = wave_role<KH>();
+  const WaveRole role = wave_role<G, KH>();
   const int grp = role.grp, part = role.part;
   const int r = lane & 15, q = lane >> 4;
-  const int64_t f0 = static_cast<int64_t>(blockIdx.x) * 32 + 8 * grp;   // this wave's features
+  const int64_t rb = static_cast<int64_t>(blockIdx.x) * G + grp;   // this wave's row group
+  const bool active = rb < f / 8;
+  const int64_t rbc = active ? rb : 0;                              // valid memory for the rest
+  const int64_t f0 = rbc * 8;                                       // this wave's features
   // PACKED: wg is the packed gate/up block (row block = 8 features)
   const char* pa =
-      PACKED ? reinterpret_cast<const char*>(wg) + (static_cast<int64_t>(blockIdx.x) * 4 + grp) * 2048 + lane * 16
+      PACKED ? reinterpret_cast<const char*>(wg) + rbc * 2048 + lane * 16
              : reinterpret_cast<const char*>(r < 8 ? wg + (f0 + r) * d : wu + (f0 + r - 8) * d) + q * 16;
   const int64_t wstep = PACKED ? (f / 8) * 2048 : 128;
   const int64_t T = d / 64, len = (T + KH - 1) / KH;
   const int64_t s0 = part * len < T ? part * len : T, s1 = s0 + len < T ? s0 + len : T;
   f32x4_t acc[4];
-  // the epilogue's table row (lane = token, this wave's 8 features), fetched
-  // once the stream is under way
   // token position of launch token t (-1 when out of range)
   auto tok_of = [&](int t) -> int64_t {
     if (!pos) return t;
@@ -274,11 +282,13 @@ __global__ __launch_bounds__(320 * KH) void decode_gateup_kernel(
     return p < 0 ? 0 : p;
   };
   const int64_t tok = tok_of(min(lane, n - 1));
+  // the epilogue's table row (lane = token, this wave's 8 features), fetched
+  // once the stream is under way
   int64_t ri;
   bool erow_ok;
   uint4 erow;
-  stream_act_ring<WD, A, KH, PACKED ? 1024 : 64>(role, pa, wstep, x, d, act_row, n, (lds_char*)(xs), s0,
-                                               s1, len, acc, [&]() {
+  stream_act_ring<WD, A, KH, PACKED ? 1024 : 64>(role, active, pa, wstep, x, d, act_row, n,
+                                                  (lds_char*)(xs), s0, s1, len, acc, [&]() {
     ri = row_index[tok < 0 ? 0 : tok];
     erow_ok = ri >= 0 && ri < n_rows;
     erow = *reinterpret_cast<const uint4*>(erow_ok ? rows + ri * f + f0 : x);
@@ -286,7 +296,7 @@ __global__ __launch_bounds__(320 * KH) void decode_gateup_kernel(
 
   // epilogue: rows 0-7 (gate) and 8-15 (up) of the row group's block, staged
   // so that lane t holds its token's 8 gate and 8 up sums
-  if (!fold_parts<KH>(role, stage, acc)) return;
+  if (!fold_parts<KH>(role, stage, acc) || !active) return;
   const float* st = stage[grp];
   const int t = lane;
   if (t >= n) return;
@@ -344,7 +354,7 @@ __global__ __launch_bounds__(320 * KH) void decode_down_kernel(int n, int64_t d,
   __shared__ __attribute__((aligned(16))) char xs[(A + 1) * KH * kXBlock];
   __shared__ float stage[4][16 * kStageLd];
   const int lane = threadIdx.x & 63;
-  const WaveRole role = wave_role<KH>();
+  const WaveRole role = wave_role<4, KH>();
   const int grp = role.grp, part = role.part;
   const int r = lane & 15, q = lane >> 4;
   // workgroup id -> (split, output block) split-minor: consecutive ids go to
@@ -364,7 +374,7 @@ __global__ __launch_bounds__(320 * KH) void decode_down_kernel(int n, int64_t d,
              : reinterpret_cast<const char*>(wd + (n0 + r) * f) + q * 16;
   const int64_t wstep = PACKED ? (d / 16) * 2048 : 128;
   f32x4_t acc[4];
-  stream_act_ring<WD, A, KH, PACKED ? 1024 : 64>(role, pa, wstep, h, f, [](int t) -> int64_t { return t; },
+  stream_act_ring<WD, A, KH, PACKED ? 1024 : 64>(role, true, pa, wstep, h, f, [](int t) -> int64_t { return t; },
                                                n, (lds_char*)(xs), s0, s1, len, acc, []() {});
   if (!fold_parts<KH>(role, stage, acc)) return;
   const float* st = stage[grp];
@@ -438,7 +448,7 @@ size_t decode_down_workspace_bytes(int64_t n, int64_t d) {
 // and folded their partial sums in LDS all measured slower.
 constexpr int kGateUpAhead = 2;      // weight steps in flight per compute wave
 constexpr int kGateUpActAhead = 3;   // activation steps in flight per loader wave
-constexpr int kGateUpParts = 2;      // d_model split in two inside a gate/up workgroup
+constexpr int kGateUpParts = 2;      // d_model split in two inside a 4-group gate/up workgroup
 constexpr int kDownAhead = 2;
 constexpr int kDownActAhead = 3;
 constexpr int kDownParts = 2;
@@ -461,19 +471,46 @@ hipError_t decode_pack(int64_t d, int64_t f, const void* wg, const void* wu, con
   return hipGetLastError();
 }
 
+// Compute units of the current device, looked up once per device.
+static int device_cus() {
+  constexpr int kMaxDevices = 64;
+  static std::atomic<int> cache[kMaxDevices];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 256;
+  int v = cache[dev].load(std::memory_order_relaxed);
+  if (v <= 0) {
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0)
+      v = 256;
+    cache[dev].store(v, std::memory_order_relaxed);
+  }
+  return v;
+}
+
 hipError_t decode_gateup(int64_t n, const int32_t* pos, int64_t n_tokens, int64_t d, int64_t f,
                          const void* x, const void* wg, const void* wu, const void* rows,
                          int64_t n_rows, const int32_t* row_index, void* h, void* g_out,
                          void* u_out, hipStream_t s, int* err, bool packed) {
+  // 4 row groups (32 features) per workgroup, on two K parts, while that fits
+  // one workgroup per CU; else 6 row groups on one part (d_ff 11008: 230
+  // workgroups of 7 waves instead of 344 of 10 on 256 CUs whose LDS holds one
+  // 10-wave workgroup each: 32 us instead of 44 per launch at d_model 4096)
+  const int64_t groups = f / 8;
+  const bool wide = groups > 4LL * device_cus();
+  const unsigned grid = static_cast<unsigned>(wide ? (groups + 5) / 6 : groups / 4);
   auto go = [&](auto kern, int threads) {
-    kern<<<dim3(static_cast<unsigned>(f / 32)), dim3(threads), 0, s>>>(
+    kern<<<dim3(grid), dim3(threads), 0, s>>>(
         static_cast<int>(n), pos, n_tokens, d, f, static_cast<const uint16_t*>(x),
         static_cast<const uint16_t*>(wg),
         static_cast<const uint16_t*>(wu), static_cast<const uint16_t*>(rows), n_rows, row_index,
         static_cast<uint16_t*>(h), static_cast<uint16_t*>(g_out), static_cast<uint16_t*>(u_out), err);
   };
-  if (packed) go(decode_gateup_kernel<kGateUpAhead, kGateUpActAhead, kGateUpParts, true>, 320 * kGateUpParts);
-  else go(decode_gateup_kernel<kGateUpAhead, kGateUpActAhead, kGateUpParts, false>, 320 * kGateUpParts);
+  auto pick = [&](auto packed_tag) {
+    constexpr bool P = decltype(packed_tag)::value;
+    if (wide) go(decode_gateup_kernel<kGateUpAhead, kGateUpActAhead, 6, 1, P>, 64 * 7);
+    else go(decode_gateup_kernel<kGateUpAhead, kGateUpActAhead, 4, kGateUpParts, P>, 64 * 5 * kGateUpParts);
+  };
+  if (packed) pick(std::true_type{});
+  else pick(std::false_type{});
   return hipGetLastError();
 }
 
