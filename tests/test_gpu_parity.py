@@ -168,6 +168,37 @@ def test_compact_rows_hit_and_miss_paths_are_bit_identical(st, dev):
             np.testing.assert_array_equal(got, expect, err_msg=f"capacity {capacity}, {name}")
 
 
+@pytest.mark.parametrize("f", [8192, 9000])
+def test_wide_row_copies_from_host_and_device(st, dev, f):
+    """Rows of 16 KB and more (the copy loop's four-deep unrolled part plus a
+    remainder) gathered and assembled from a pinned host table (a capped,
+    grid-striding launch) and from a device table, bit for bit."""
+    import torch
+    vocab, n = 700, 300
+    bits = S.normal_bf16_bits((vocab, f), 0.02, 5 + f)
+    host_table = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).pin_memory()
+    dev_table = host_table.to(dev)
+    rng = np.random.default_rng(f)
+    index = rng.integers(0, vocab, size=n).astype(np.int32)
+    idx = torch.from_numpy(index).to(dev)
+    cnt = torch.tensor([n - 7], dtype=torch.int32, device=dev)
+    a = st.staple_gather_rows(host_table, idx, cnt)
+    b = st.staple_gather_rows(dev_table, idx, cnt)
+    code = torch.from_numpy(np.where(np.arange(n) % 3 == 0, np.arange(n) % 50, -1).astype(np.int32)).to(dev)
+    cache_rows = dev_table[:50].contiguous()
+    c = st.staple_assemble_rows_from_table(cache_rows, host_table, idx, code, cnt)
+    torch.cuda.synchronize()
+    _no_device_error(st)
+    m = n - 7
+    want = bits[index[:m]]
+    for name, r in (("host gather", a), ("device gather", b)):
+        np.testing.assert_array_equal(r[:m].cpu().view(torch.int16).numpy().view(np.uint16), want,
+                                      err_msg=name)
+    cpu_code = code.cpu().numpy()[:m]
+    want_c = np.where((cpu_code >= 0)[:, None], bits[np.maximum(cpu_code, 0)], want)
+    np.testing.assert_array_equal(c[:m].cpu().view(torch.int16).numpy().view(np.uint16), want_c)
+
+
 def test_row_copies_refuse_pageable_host_memory(st, dev):
     """A pageable host buffer handed to a row copy (source or destination) is
     refused on the host with STAPLE_ERR_INVALID_ARGUMENT; nothing is launched."""

@@ -33,7 +33,7 @@ hipError_t launch_cache_lookup(const int32_t* uniq, const int32_t* n_unique, int
                                hipStream_t s, int* err);
 hipError_t launch_gather_rows(const void* src, int64_t src_rows, const int32_t* index,
                               const int32_t* n_rows, int64_t max_rows, int64_t row_bytes,
-                              void* dst, hipStream_t s, int* err);
+                              void* dst, hipStream_t s, int* err, unsigned max_workgroups);
 hipError_t launch_assemble_rows(const void* cache_rows, int64_t capacity, const void* miss_rows,
                                 int64_t max_miss, const int32_t* code, const int32_t* n_unique,
                                 int64_t max_unique, int64_t row_bytes, void* rows, hipStream_t s,
@@ -41,7 +41,8 @@ hipError_t launch_assemble_rows(const void* cache_rows, int64_t capacity, const 
 hipError_t launch_assemble_rows_table(const void* cache_rows, int64_t capacity, const void* table,
                                       int64_t vocab, const int32_t* uniq, const int32_t* code,
                                       const int32_t* n_unique, int64_t max_unique,
-                                      int64_t row_bytes, void* rows, hipStream_t s, int* err);
+                                      int64_t row_bytes, void* rows, hipStream_t s, int* err,
+                                      unsigned max_workgroups);
 size_t segment_sum_workspace_bytes(int64_t n_tokens, int64_t d_ff);
 hipError_t launch_segment_sum(int dtype, const void* du, int64_t du_ld, int64_t du_col,
                               int64_t n_tokens, int64_t d_ff, const int32_t* sorted_pos,
@@ -118,6 +119,20 @@ static bool device_addressable(const void* p) {
   return attr.type == hipMemoryTypeDevice || attr.type == hipMemoryTypeHost ||
          attr.type == hipMemoryTypeManaged;
 }
+// Pinned host memory (a row copy from it reads over PCIe).
+static bool host_memory(const void* p) {
+  hipPointerAttribute_t attr{};
+  if (hipPointerGetAttributes(&attr, p) != hipSuccess) {
+    (void)hipGetLastError();
+    return false;
+  }
+  return attr.type == hipMemoryTypeHost;
+}
+// Workgroups of a row copy that reads host memory: enough loads in flight for
+// PCIe (64 x 16 KB), few enough to leave room beside a concurrent kernel.
+constexpr unsigned kHostCopyWorkgroups = 64;
+static unsigned copy_workgroups(const void* src) { return host_memory(src) ? kHostCopyWorkgroups : 0; }
+
 static inline hipStream_t S(void* s) { return static_cast<hipStream_t>(s); }
 
 }  // namespace staple
@@ -222,7 +237,7 @@ staple_status_t staple_cache_fill(const void* table, int64_t vocab, int64_t d_ff
   REQUIRE(capacity == 0 || (device_addressable(table) && device_addressable(slot_rows)));
   GET_ERR(err);
   HIPCALL(launch_gather_rows(table, vocab, slot_to_id, nullptr, capacity, d_ff * elem_bytes(dtype),
-                             slot_rows, S(stream), err));
+                             slot_rows, S(stream), err, copy_workgroups(table)));
   return STAPLE_OK;
 }
 
@@ -318,7 +333,8 @@ staple_status_t staple_assemble_rows_from_table(const void* cache_rows, int64_t 
   REQUIRE(device_addressable(table) && (max_unique == 0 || device_addressable(rows)));
   GET_ERR(err);
   HIPCALL(launch_assemble_rows_table(cache_rows, capacity, table, vocab, uniq, code, n_unique,
-                                     max_unique, d_ff * elem_bytes(dtype), rows, S(stream), err));
+                                     max_unique, d_ff * elem_bytes(dtype), rows, S(stream), err,
+                                     copy_workgroups(table)));
   return STAPLE_OK;
 }
 
@@ -332,7 +348,8 @@ staple_status_t staple_gather_rows(const void* src, int64_t src_rows, const int3
   REQUIRE(max_rows == 0 || (device_addressable(src) && device_addressable(dst)));
   GET_ERR(err);
   HIPCALL(launch_gather_rows(src, src_rows, index, n_rows, max_rows, d_ff * elem_bytes(dtype), dst,
-                             S(stream), err));
+                             S(stream), err,
+                             copy_workgroups(src)));
   return STAPLE_OK;
 }
 

@@ -180,32 +180,52 @@ hipError_t launch_split_tokens(const int32_t* inv, int64_t n, const int32_t* cod
 // ---------------------------------------------------------------------------
 constexpr int kRowThreads = 256;
 
+// Four 16-byte loads in flight per thread before the stores (a row read over
+// PCIe from pinned host memory has a long latency).
 __device__ __forceinline__ void copy_row16(const uint4* __restrict__ src, uint4* __restrict__ dst,
                                            int64_t vecs) {
-  for (int64_t v = threadIdx.x; v < vecs; v += kRowThreads) dst[v] = src[v];
+  int64_t v = threadIdx.x;
+  for (; v + 3 * kRowThreads < vecs; v += 4 * kRowThreads) {
+    uint4 t[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) t[j] = src[v + j * kRowThreads];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) dst[v + j * kRowThreads] = t[j];
+  }
+  for (; v < vecs; v += kRowThreads) dst[v] = src[v];
 }
+
+// Row copies run one workgroup per row (grid-stride over rows when the grid
+// is capped).  Copies whose source is host memory cap the grid so that their
+// long-latency workgroups occupy one slot on a few CUs and a concurrent
+// kernel (the gate/up GEMM the copy overlaps) still fits beside them.
 
 // dst[r] = src[index[r]]  (r < n, n from the device scalar when given)
 __global__ __launch_bounds__(kRowThreads) void gather_rows_kernel(
     const void* src, int64_t src_rows, const int32_t* index, const int32_t* n_rows_p,
-    int64_t row_bytes, void* dst, int* err) {
-  const int64_t r = blockIdx.x;
-  if (n_rows_p && r >= *n_rows_p) return;
-  const int32_t i = index[r];
-  if (i < 0 || i >= src_rows) {
-    if (threadIdx.x == 0) flag_index_error(err);
-    return;
+    int64_t max_rows, int64_t row_bytes, void* dst, int* err) {
+  const int64_t n = n_rows_p ? min(static_cast<int64_t>(*n_rows_p), max_rows) : max_rows;
+  for (int64_t r = blockIdx.x; r < n; r += gridDim.x) {
+    const int32_t i = index[r];
+    if (i < 0 || i >= src_rows) {
+      if (threadIdx.x == 0) flag_index_error(err);
+      continue;
+    }
+    copy_row16(reinterpret_cast<const uint4*>(static_cast<const char*>(src) + i * row_bytes),
+               reinterpret_cast<uint4*>(static_cast<char*>(dst) + r * row_bytes), row_bytes / 16);
   }
-  copy_row16(reinterpret_cast<const uint4*>(static_cast<const char*>(src) + i * row_bytes),
-             reinterpret_cast<uint4*>(static_cast<char*>(dst) + r * row_bytes), row_bytes / 16);
+}
+
+static unsigned row_grid(int64_t rows, unsigned max_workgroups) {
+  return static_cast<unsigned>(max_workgroups > 0 && rows > max_workgroups ? max_workgroups : rows);
 }
 
 hipError_t launch_gather_rows(const void* src, int64_t src_rows, const int32_t* index,
                               const int32_t* n_rows, int64_t max_rows, int64_t row_bytes,
-                              void* dst, hipStream_t s, int* err) {
+                              void* dst, hipStream_t s, int* err, unsigned max_workgroups) {
   if (max_rows == 0) return hipSuccess;
-  gather_rows_kernel<<<dim3(static_cast<unsigned>(max_rows)), dim3(kRowThreads), 0, s>>>(
-      src, src_rows, index, n_rows, row_bytes, dst, err);
+  gather_rows_kernel<<<dim3(row_grid(max_rows, max_workgroups)), dim3(kRowThreads), 0, s>>>(
+      src, src_rows, index, n_rows, max_rows, row_bytes, dst, err);
   return hipGetLastError();
 }
 
@@ -250,37 +270,39 @@ hipError_t launch_assemble_rows(const void* cache_rows, int64_t capacity, const 
 // host memory read over PCIe, one whole row per workgroup).
 __global__ __launch_bounds__(kRowThreads) void assemble_rows_table_kernel(
     const void* cache_rows, int64_t capacity, const void* table, int64_t vocab,
-    const int32_t* uniq, const int32_t* code, const int32_t* n_unique_p, int64_t row_bytes,
-    void* rows, int* err) {
-  const int64_t u = blockIdx.x;
-  if (u >= *n_unique_p) return;
-  const int32_t c = code[u];
-  const char* src;
-  if (c >= 0) {
-    if (c >= capacity) {
-      if (threadIdx.x == 0) flag_index_error(err);
-      return;
+    const int32_t* uniq, const int32_t* code, const int32_t* n_unique_p, int64_t max_unique,
+    int64_t row_bytes, void* rows, int* err) {
+  const int64_t n = min(static_cast<int64_t>(*n_unique_p), max_unique);
+  for (int64_t u = blockIdx.x; u < n; u += gridDim.x) {
+    const int32_t c = code[u];
+    const char* src;
+    if (c >= 0) {
+      if (c >= capacity) {
+        if (threadIdx.x == 0) flag_index_error(err);
+        continue;
+      }
+      src = static_cast<const char*>(cache_rows) + c * row_bytes;
+    } else {
+      const int32_t id = uniq[u];
+      if (id < 0 || id >= vocab) {
+        if (threadIdx.x == 0) flag_index_error(err);
+        continue;
+      }
+      src = static_cast<const char*>(table) + id * row_bytes;
     }
-    src = static_cast<const char*>(cache_rows) + c * row_bytes;
-  } else {
-    const int32_t id = uniq[u];
-    if (id < 0 || id >= vocab) {
-      if (threadIdx.x == 0) flag_index_error(err);
-      return;
-    }
-    src = static_cast<const char*>(table) + id * row_bytes;
+    copy_row16(reinterpret_cast<const uint4*>(src),
+               reinterpret_cast<uint4*>(static_cast<char*>(rows) + u * row_bytes), row_bytes / 16);
   }
-  copy_row16(reinterpret_cast<const uint4*>(src),
-             reinterpret_cast<uint4*>(static_cast<char*>(rows) + u * row_bytes), row_bytes / 16);
 }
 
 hipError_t launch_assemble_rows_table(const void* cache_rows, int64_t capacity, const void* table,
                                       int64_t vocab, const int32_t* uniq, const int32_t* code,
                                       const int32_t* n_unique, int64_t max_unique,
-                                      int64_t row_bytes, void* rows, hipStream_t s, int* err) {
+                                      int64_t row_bytes, void* rows, hipStream_t s, int* err,
+                                      unsigned max_workgroups) {
   if (max_unique == 0) return hipSuccess;
-  assemble_rows_table_kernel<<<dim3(static_cast<unsigned>(max_unique)), dim3(kRowThreads), 0, s>>>(
-      cache_rows, capacity, table, vocab, uniq, code, n_unique, row_bytes, rows, err);
+  assemble_rows_table_kernel<<<dim3(row_grid(max_unique, max_workgroups)), dim3(kRowThreads), 0, s>>>(
+      cache_rows, capacity, table, vocab, uniq, code, n_unique, max_unique, row_bytes, rows, err);
   return hipGetLastError();
 }
 
