@@ -342,19 +342,20 @@ __global__ __launch_bounds__(64 * (G + 1) * KH) void decode_gateup_kernel(
 }
 
 // Down projection for at most 64 tokens, d_ff split KS ways over workgroups
-// and KH ways inside one: workgroup (output block b of 64, split ks) with
-// compute wave w owning outputs 64 b + 16 (w % 4) .. +16 over part w / 4 of
+// and KH ways inside one: workgroup (output block b of 16 G, split ks) with
+// compute wave w owning outputs 16 G b + 16 (w % G) .. +16 over part w / G of
 // the split's steps (plus KH activation loaders); writes partial[ks][t][n] in
-// fp32.
-template <int WD, int A, int KS, int KH, bool PACKED>
-__global__ __launch_bounds__(320 * KH) void decode_down_kernel(int n, int64_t d, int64_t f,
-                                                               const uint16_t* __restrict__ h,
-                                                               const uint16_t* __restrict__ wd,
-                                                               float* __restrict__ partial) {
+// fp32.  Row groups past d_model (in the last block when d / 16 is not a
+// multiple of G) stream nothing and write nothing.
+template <int WD, int A, int G, int KS, int KH, bool PACKED>
+__global__ __launch_bounds__(64 * (G + 1) * KH) void decode_down_kernel(int n, int64_t d, int64_t f,
+                                                                       const uint16_t* __restrict__ h,
+                                                                       const uint16_t* __restrict__ wd,
+                                                                       float* __restrict__ partial) {
   __shared__ __attribute__((aligned(16))) char xs[(A + 1) * KH * kXBlock];
-  __shared__ float stage[4][16 * kStageLd];
+  __shared__ float stage[G][16 * kStageLd];
   const int lane = threadIdx.x & 63;
-  const WaveRole role = wave_role<4, KH>();
+  const WaveRole role = wave_role<G, KH>();
   const int grp = role.grp, part = role.part;
   const int r = lane & 15, q = lane >> 4;
   // workgroup id -> (split, output block) split-minor: consecutive ids go to
@@ -362,7 +363,10 @@ __global__ __launch_bounds__(320 * KH) void decode_down_kernel(int n, int64_t d,
   // fetch only those into their L2
   const int ks = static_cast<int>(blockIdx.x % KS);
   const int64_t blk = blockIdx.x / KS;
-  const int64_t n0 = blk * 64 + 16 * grp;
+  const int64_t rb = blk * G + grp;           // this wave's 16-output row group
+  const bool active = rb < d / 16;
+  const int64_t rbc = active ? rb : 0;        // valid memory for the rest
+  const int64_t n0 = rbc * 16;
   const int64_t T = f / 64;
   const int64_t k0 = T * ks / KS, k1 = T * (ks + 1) / KS;
   const int64_t len = (k1 - k0 + KH - 1) / KH;
@@ -370,13 +374,14 @@ __global__ __launch_bounds__(320 * KH) void decode_down_kernel(int n, int64_t d,
   const int64_t s1 = s0 + len < k1 ? s0 + len : k1;
   // PACKED: wd is the packed down block (row block = 16 outputs)
   const char* pa =
-      PACKED ? reinterpret_cast<const char*>(wd) + (blk * 4 + grp) * 2048 + lane * 16
+      PACKED ? reinterpret_cast<const char*>(wd) + rbc * 2048 + lane * 16
              : reinterpret_cast<const char*>(wd + (n0 + r) * f) + q * 16;
   const int64_t wstep = PACKED ? (d / 16) * 2048 : 128;
   f32x4_t acc[4];
-  stream_act_ring<WD, A, KH, PACKED ? 1024 : 64>(role, true, pa, wstep, h, f, [](int t) -> int64_t { return t; },
-                                               n, (lds_char*)(xs), s0, s1, len, acc, []() {});
-  if (!fold_parts<KH>(role, stage, acc)) return;
+  stream_act_ring<WD, A, KH, PACKED ? 1024 : 64>(role, active, pa, wstep, h, f,
+                                                  [](int t) -> int64_t { return t; }, n,
+                                                  (lds_char*)(xs), s0, s1, len, acc, []() {});
+  if (!fold_parts<KH>(role, stage, acc) || !active) return;
   const float* st = stage[grp];
   const int t = lane;
   if (t >= n) return;
@@ -525,9 +530,9 @@ hipError_t decode_down(int64_t n, int64_t d, int64_t f, const void* h, const voi
   };
   auto pick = [&](auto packed_tag) {
     constexpr bool P = decltype(packed_tag)::value;
-    if (ks == 8) go(decode_down_kernel<kDownAhead, kDownActAhead, 8, kDownParts, P>);
-    else if (ks == 4) go(decode_down_kernel<kDownAhead, kDownActAhead, 4, kDownParts, P>);
-    else go(decode_down_kernel<kDownAhead, kDownActAhead, 2, kDownParts, P>);
+    if (ks == 8) go(decode_down_kernel<kDownAhead, kDownActAhead, 4, 8, kDownParts, P>);
+    else if (ks == 4) go(decode_down_kernel<kDownAhead, kDownActAhead, 4, 4, kDownParts, P>);
+    else go(decode_down_kernel<kDownAhead, kDownActAhead, 4, 2, kDownParts, P>);
   };
   if (packed) pick(std::true_type{});
   else pick(std::false_type{});
