@@ -286,6 +286,51 @@ def ffn_backward(dy, x, w_gate, w_up, w_down, fwd: dict, ids, precision: str = E
 
 
 # --------------------------------------------------------------------------
+# Optimizer step on the touched table rows
+# --------------------------------------------------------------------------
+ADAMW_DEFAULTS = dict(beta1=0.9, beta2=0.999, eps=1e-8)
+
+
+def adamw_rows(table, m, v, rows: Sequence[int], grad, lr: float, weight_decay: float,
+               step: int, beta1: float = 0.9, beta2: float = 0.999,
+               eps: float = 1e-8):
+    """One AdamW step applied to the listed rows of a table and its moments.
+
+    The tables are trained with AdamW, their moments kept in fp32 beside the
+    bf16 table (Figure 4 caption: bf16 tables and fp32 AdamW moments in host
+    DRAM; Table 3: peak learning rate and weight decay of the table group).
+    For each listed row r with gradient g (decoupled weight decay, bias
+    correction with the global step t):
+
+        p <- p (1 - lr wd)
+        m <- beta1 m + (1 - beta1) g          v <- beta2 v + (1 - beta2) g^2
+        p <- p - lr / (1 - beta1^t) * m / (sqrt(v) / sqrt(1 - beta2^t) + eps)
+
+    Readings: the pages give neither the betas nor epsilon, so they default
+    to (0.9, 0.999) and 1e-8; rows outside `rows` are not touched at all,
+    neither the parameters nor the moments (a row absent from the batch has
+    no gradient, and decaying every row of a 100352-row table in host memory
+    at every step is not what an offloaded sparse update does); the step
+    count is global, as in a sparse Adam over an embedding.
+    Returns new float64 arrays (table, m, v); the inputs are not modified.
+    """
+    p = np.array(table, dtype=np.float64, copy=True)
+    m = np.array(m, dtype=np.float64, copy=True)
+    v = np.array(v, dtype=np.float64, copy=True)
+    g = np.asarray(grad, dtype=np.float64)
+    rows = np.asarray(rows, dtype=np.int64)
+    assert len(np.unique(rows)) == len(rows), "rows must be distinct"
+    bc1 = 1.0 - beta1 ** step
+    bc2 = 1.0 - beta2 ** step
+    for k, r in enumerate(rows):
+        p[r] *= 1.0 - lr * weight_decay
+        m[r] = beta1 * m[r] + (1.0 - beta1) * g[k]
+        v[r] = beta2 * v[r] + (1.0 - beta2) * g[k] * g[k]
+        p[r] -= lr / bc1 * m[r] / (np.sqrt(v[r]) / math.sqrt(bc2) + eps)
+    return p, m, v
+
+
+# --------------------------------------------------------------------------
 # Work counts used for throughput figures
 # --------------------------------------------------------------------------
 def ffn_flops(n_tokens: int, d_model: int, d_ff: int, backward: bool,

@@ -389,3 +389,90 @@ def test_page_figures_fix_the_1b_workload_shapes():
         got = round(computed[ent["name"]], ent["printed_decimals"])
         assert got == pytest.approx(ent["value"]), (ent["name"], computed[ent["name"]])
     assert S.OLMO1B_OFFLOAD.cache_capacity == 5018
+
+
+# ---------------------------------------------------------------- AdamW on rows
+def _adamw_case(seed, vocab=9, f=6, n_rows=4):
+    rng = np.random.default_rng(seed)
+    table = rng.normal(0, 0.5, (vocab, f))
+    rows = rng.choice(vocab, n_rows, replace=False)
+    grad = rng.normal(0, 1.0, (n_rows, f))
+    return table, rows, grad
+
+
+def test_adamw_first_step_closed_form():
+    """From zero moments, step 1: m = (1-b1) g, v = (1-b2) g^2, and the bias
+    corrections turn the update into lr * g / (|g| + eps) after the decay."""
+    table, rows, grad = _adamw_case(0)
+    lr, wd, b1, b2, eps = 3e-4, 1e-4, 0.9, 0.999, 1e-8
+    p, m, v = O.adamw_rows(table, np.zeros_like(table), np.zeros_like(table), rows, grad,
+                           lr=lr, weight_decay=wd, step=1, beta1=b1, beta2=b2, eps=eps)
+    want_p = table.copy()
+    want_p[rows] = table[rows] * (1 - lr * wd) - lr * grad / (np.abs(grad) + eps)
+    np.testing.assert_allclose(p, want_p, rtol=0, atol=1e-15)
+    np.testing.assert_allclose(m[rows], (1 - b1) * grad, rtol=1e-15)
+    np.testing.assert_allclose(v[rows], (1 - b2) * grad ** 2, rtol=1e-15)
+
+
+def test_adamw_zero_gradient_row_only_decays():
+    table, rows, grad = _adamw_case(1)
+    grad[:] = 0.0
+    p, m, v = O.adamw_rows(table, np.zeros_like(table), np.zeros_like(table), rows, grad,
+                           lr=1e-2, weight_decay=0.5, step=1)
+    np.testing.assert_array_equal(p[rows], table[rows] * (1 - 1e-2 * 0.5))
+    assert not m.any() and not v.any()
+
+
+def test_adamw_untouched_rows_are_bit_identical():
+    table, rows, grad = _adamw_case(2)
+    m0 = np.random.default_rng(3).normal(0, 0.1, table.shape)
+    v0 = np.abs(np.random.default_rng(4).normal(0, 0.1, table.shape))
+    p, m, v = O.adamw_rows(table, m0, v0, rows, grad, lr=1e-3, weight_decay=1e-4, step=7)
+    other = np.setdiff1d(np.arange(table.shape[0]), rows)
+    np.testing.assert_array_equal(p[other], table[other])
+    np.testing.assert_array_equal(m[other], m0[other])
+    np.testing.assert_array_equal(v[other], v0[other])
+
+
+def test_adamw_all_rows_touched_matches_torch_adamw():
+    """With every row in every step the update is torch.optim.AdamW's (float64)."""
+    rng = np.random.default_rng(5)
+    vocab, f = 7, 5
+    table = rng.normal(0, 0.5, (vocab, f))
+    lr, wd, b1, b2, eps = 4e-4, 1e-4, 0.9, 0.999, 1e-8
+    w = torch.nn.Parameter(torch.tensor(table, dtype=torch.float64))
+    opt = torch.optim.AdamW([w], lr=lr, betas=(b1, b2), eps=eps, weight_decay=wd)
+    p, m, v = table.copy(), np.zeros_like(table), np.zeros_like(table)
+    for step in range(1, 4):
+        g = rng.normal(0, 1.0, (vocab, f))
+        w.grad = torch.tensor(g, dtype=torch.float64)
+        opt.step()
+        p, m, v = O.adamw_rows(p, m, v, np.arange(vocab), g, lr=lr, weight_decay=wd,
+                               step=step, beta1=b1, beta2=b2, eps=eps)
+    np.testing.assert_allclose(p, w.detach().numpy(), rtol=1e-13, atol=1e-15)
+    st = opt.state[w]
+    np.testing.assert_allclose(m, st["exp_avg"].numpy(), rtol=1e-13)
+    np.testing.assert_allclose(v, st["exp_avg_sq"].numpy(), rtol=1e-13)
+
+
+def test_adamw_sparse_rows_match_torch_sparse_adam():
+    """Rows absent from a step keep their moments and parameters, and the bias
+    correction counts global steps: torch.optim.SparseAdam's semantics (no
+    weight decay there; it adds eps before the bias correction, so eps is
+    made negligible and the comparison is to 1e-9)."""
+    rng = np.random.default_rng(6)
+    vocab, f = 10, 4
+    table = rng.normal(0, 0.5, (vocab, f))
+    lr, b1, b2, eps = 1e-2, 0.9, 0.999, 1e-30
+    w = torch.nn.Parameter(torch.tensor(table, dtype=torch.float64))
+    opt = torch.optim.SparseAdam([w], lr=lr, betas=(b1, b2), eps=eps)
+    p, m, v = table.copy(), np.zeros_like(table), np.zeros_like(table)
+    for step, rows in enumerate(([0, 3, 7], [3, 5], [0, 1, 3, 9], [5, 7]), start=1):
+        rows = np.array(rows)
+        g = rng.normal(0, 1.0, (len(rows), f))
+        w.grad = torch.sparse_coo_tensor(torch.tensor(rows)[None], torch.tensor(g), (vocab, f))
+        opt.step()
+        p, m, v = O.adamw_rows(p, m, v, rows, g, lr=lr, weight_decay=0.0, step=step,
+                               beta1=b1, beta2=b2, eps=eps)
+    np.testing.assert_allclose(p, w.detach().numpy(), rtol=1e-9, atol=1e-12)
+    np.testing.assert_array_equal(p[[2, 4, 6, 8]], table[[2, 4, 6, 8]])
