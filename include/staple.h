@@ -339,6 +339,53 @@ staple_status_t staple_ffn_fwd_packed(int64_t n_tokens, int64_t d_model, int64_t
                                       void* stream);
 
 /* ------------------------------------------------------------------------
+ * AdamW step on the table rows a batch touched.  The tables are trained with
+ * AdamW with fp32 moments beside the bf16 table (STAPLE Figure 4 caption:
+ * bf16 tables and fp32 AdamW moments in host DRAM; Table 3: peak learning
+ * rate and weight decay of the table group).  For each listed row r with
+ * gradient g (one row of d_rows, e.g. staple_ffn_bwd_table_grad's output,
+ * paired with staple_dedup's uniq), in fp32:
+ *   p = p (1 - lr wd);  m = b1 m + (1 - b1) g;  v = b2 v + (1 - b2) g^2;
+ *   p = p - lr / (1 - b1^step) * m / (sqrt(v) / sqrt(1 - b2^step) + eps)
+ * and p is stored in the table's dtype (bf16: round to nearest even).
+ * Rows not listed keep their parameters and moments; `step` (>= 1) is the
+ * global step count used for the bias corrections.  The pages give no betas
+ * or epsilon; callers pass them (0.9, 0.999, 1e-8 are the usual defaults).
+ *
+ * staple_adamw_rows: device pointers.  table [vocab x d_ff] (dtype), m, v
+ *   [vocab x d_ff] fp32, grad [max_rows x d_ff] fp32 (row k is the gradient
+ *   of table row rows[k]); rows int32[max_rows], distinct; n_rows a device
+ *   scalar (NULL: all max_rows).  d_ff a multiple of 8; 16-byte aligned
+ *   pointers.  A row outside [0, vocab) sets the device error word and is
+ *   skipped.  Asynchronous on `stream`.
+ * staple_adamw_rows_host: the same update on host memory with host threads
+ *   (n_threads <= 0: up to 16), synchronous; rows and grad are host arrays of
+ *   n_rows entries; a row outside [0, vocab) returns STAPLE_ERR_HOST before
+ *   anything is written.  The offloaded layout: the table and its moments in
+ *   host memory, the gradient rows copied from the device first.
+ * staple_cache_refresh: after an update of the host table, copies every
+ *   updated row that is cached (code[u] >= 0, as from staple_cache_lookup)
+ *   back into its cache slot: cache_rows[code[u]] = table[uniq[u]] for
+ *   u < *n_unique.  table: device or pinned host memory; cache_rows
+ *   [capacity x d_ff] device.  Out-of-range codes or IDs set the device error
+ *   word.
+ * ------------------------------------------------------------------------ */
+staple_status_t staple_adamw_rows(void* table, float* m, float* v, int64_t vocab, int64_t d_ff,
+                                  int32_t dtype, const int32_t* rows, const int32_t* n_rows,
+                                  int64_t max_rows, const float* grad, float lr, float beta1,
+                                  float beta2, float eps, float weight_decay, int64_t step,
+                                  void* stream);
+staple_status_t staple_adamw_rows_host(void* table, float* m, float* v, int64_t vocab, int64_t d_ff,
+                                       int32_t dtype, const int32_t* rows, int64_t n_rows,
+                                       const float* grad, float lr, float beta1, float beta2,
+                                       float eps, float weight_decay, int64_t step,
+                                       int32_t n_threads);
+staple_status_t staple_cache_refresh(const void* table, int64_t vocab, int64_t d_ff, int32_t dtype,
+                                     const int32_t* uniq, const int32_t* code,
+                                     const int32_t* n_unique, int64_t max_unique, void* cache_rows,
+                                     int64_t capacity, void* stream);
+
+/* ------------------------------------------------------------------------
  * Backward of one augmented layer with the table-row gradient.
  *   dy [n_tokens x d_model] (dtype): upstream gradient of y.
  *   saved_g, saved_u, saved_h: the forward's save_g/save_u/save_h (required).

@@ -672,3 +672,103 @@ def test_olmo1b_decode_layer_full(st, dev):
     torch.cuda.synchronize()
     _no_device_error(st)
     assert torch.equal(got["y"], fwd["y"])
+
+
+# ---------------------------------------------------------------- AdamW on table rows
+def _bf16_ulp(x):
+    e = np.floor(np.log2(np.maximum(np.abs(x), 1e-30)))
+    return 2.0 ** (e - 7)
+
+
+@pytest.mark.parametrize("dtype,f", [("bf16", 8192), ("f32", 64), ("bf16", 11008)])
+def test_device_adamw_rows_match_oracle(st, dev, dtype, f):
+    """Three lazy steps of the device update (rows from staple_dedup's uniq,
+    count from its device scalar) against the oracle's AdamW, with the oracle
+    rounded to bf16 where the table stores bf16; untouched rows bit-identical."""
+    import torch
+    _log(f"device adamw {dtype} f={f}")
+    rng = np.random.default_rng(21 + f)
+    vocab = 300
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    table = torch.tensor(rng.normal(0, 0.02, (vocab, f)), dtype=tdt, device=dev)
+    m = torch.zeros(vocab, f, dtype=torch.float32, device=dev)
+    v = torch.zeros(vocab, f, dtype=torch.float32, device=dev)
+    ref_p, ref_m, ref_v = table.double().cpu().numpy(), np.zeros((vocab, f)), np.zeros((vocab, f))
+    f32 = lambda x: float(np.float32(x))
+    ohp = dict(lr=f32(3e-4), weight_decay=f32(1e-4), beta1=f32(0.9), beta2=f32(0.999), eps=f32(1e-8))
+    for step, n_tok in enumerate((200, 64, 500), start=1):
+        ids = S.zipf_ids(n_tok, vocab, 90 + step)
+        dd = st.staple_dedup(torch.from_numpy(ids).to(dev), vocab)
+        torch.cuda.synchronize()
+        u = int(dd["n_unique"].item())
+        uniq = dd["uniq"][:u].cpu().numpy()
+        grad = torch.tensor(rng.normal(0, 1.0, (n_tok, f)), dtype=torch.float32, device=dev)
+        before = table.clone()
+        st.staple_adamw_rows(table, m, v, dd["uniq"], grad, n_rows=dd["n_unique"], lr=3e-4,
+                             weight_decay=1e-4, step=step)
+        torch.cuda.synchronize()
+        _no_device_error(st)
+        ref_p, ref_m, ref_v = O.adamw_rows(ref_p, ref_m, ref_v, uniq,
+                                           grad[:u].double().cpu().numpy(), step=step, **ohp)
+        if dtype == "bf16":
+            ref_p = O.bf16_round(ref_p)
+        other = torch.from_numpy(np.setdiff1d(np.arange(vocab), uniq)).to(dev)
+        assert torch.equal(table[other], before[other]), "untouched rows changed"
+        got = table.double().cpu().numpy()
+        if dtype == "f32":
+            np.testing.assert_allclose(got, ref_p, rtol=2e-6, atol=1e-9)
+        else:
+            bad = np.abs(got - ref_p) > _bf16_ulp(ref_p) * 1.01
+            assert not bad.any(), f"{bad.sum()} parameters beyond one bf16 ulp"
+            # a one-ulp rounding flip must not carry into the next step's check
+            ref_p = got.copy()
+        np.testing.assert_allclose(m.double().cpu().numpy(), ref_m, rtol=2e-6, atol=2e-7)
+        np.testing.assert_allclose(v.double().cpu().numpy(), ref_v, rtol=2e-6, atol=1e-8)
+
+
+def test_device_adamw_flags_rows_outside_the_table(st, dev):
+    import torch
+    table = torch.zeros(16, 64, dtype=torch.bfloat16, device=dev)
+    m = torch.zeros(16, 64, device=dev)
+    v = torch.zeros(16, 64, device=dev)
+    rows = torch.tensor([3, 16, 5], dtype=torch.int32, device=dev)
+    grad = torch.ones(3, 64, device=dev)
+    st.staple_adamw_rows(table, m, v, rows, grad, lr=1e-2, weight_decay=0.0, step=1)
+    torch.cuda.synchronize()
+    assert st.staple_get_device_error() != 0
+    assert m[3].abs().sum() > 0 and m[5].abs().sum() > 0
+    assert torch.count_nonzero(m[torch.tensor([0, 1, 2, 4, 6, 15], device=dev)]) == 0
+
+
+def test_cache_refresh_after_host_update(st, dev):
+    """Host AdamW on a pinned table, then the cached copies of the updated rows
+    are refreshed: every cache slot equals its table row again, bit for bit,
+    and slots of rows not in the batch are untouched."""
+    import torch
+    vocab, f, cap = 3000, 256, 150
+    bits = S.normal_bf16_bits((vocab, f), 0.02, 55)
+    host = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).pin_memory()
+    m = torch.zeros(vocab, f)
+    v = torch.zeros(vocab, f)
+    counts = st.staple_cache_count(torch.from_numpy(S.zipf_ids(40_000, vocab, 8)).to(dev), vocab)
+    i2s, s2i = st.staple_cache_build(counts, cap)
+    cache_rows = st.staple_cache_fill(host, s2i, cap)
+    ids = S.zipf_ids(1024, vocab, 56)
+    dd = st.staple_dedup(torch.from_numpy(ids).to(dev), vocab)
+    lk = st.staple_cache_lookup(dd["uniq"], dd["n_unique"], i2s)
+    torch.cuda.synchronize()
+    u = int(dd["n_unique"].item())
+    grad = torch.randn(u, f, generator=torch.Generator().manual_seed(3))
+    st.staple_adamw_rows_host(host, m, v, dd["uniq"][:u].cpu().contiguous(), grad, lr=1e-2,
+                              weight_decay=0.0, step=1)
+    stale = cache_rows.clone()
+    st.staple_cache_refresh(host, dd["uniq"], lk["code"], dd["n_unique"], cache_rows)
+    torch.cuda.synchronize()
+    _no_device_error(st)
+    slot_ids = s2i.cpu().numpy()
+    want = host[torch.from_numpy(slot_ids.astype(np.int64))].to(dev)
+    assert torch.equal(cache_rows, want)
+    touched = np.isin(slot_ids, dd["uniq"][:u].cpu().numpy())
+    assert touched.any() and (~touched).any()
+    keep = torch.from_numpy(np.nonzero(~touched)[0]).to(dev)
+    assert torch.equal(cache_rows[keep], stale[keep])

@@ -1,0 +1,77 @@
+"""The host AdamW update of touched table rows (plain host code in
+libstaple.so, no GPU needed) against the oracle's AdamW step."""
+import numpy as np
+import pytest
+
+from oracle import staple_oracle as O
+
+
+def _lib():
+    st = pytest.importorskip("token_indexed_ffn_amd")
+    try:
+        st.lib()
+    except RuntimeError as e:                      # library not built
+        pytest.skip(str(e))
+    return st
+
+
+def _bf16_ulp(x):
+    e = np.floor(np.log2(np.maximum(np.abs(x), 1e-30)))
+    return 2.0 ** (e - 7)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_host_adamw_rows_match_oracle_over_lazy_steps(dtype):
+    import torch
+    st = _lib()
+    rng = np.random.default_rng(11)
+    vocab, f = 40, 24
+    p0 = rng.normal(0, 0.05, (vocab, f))
+    tdt = torch.float32 if dtype == "f32" else torch.bfloat16
+    table = torch.tensor(p0, dtype=tdt)
+    m = torch.zeros(vocab, f, dtype=torch.float32)
+    v = torch.zeros(vocab, f, dtype=torch.float32)
+    ref_p = table.double().numpy()
+    ref_m, ref_v = np.zeros((vocab, f)), np.zeros((vocab, f))
+    hp = dict(lr=4e-4, weight_decay=1e-4)
+    # the library takes its hyperparameters as float32: give the oracle the same values
+    f32 = lambda x: float(np.float32(x))
+    ohp = dict(lr=f32(4e-4), weight_decay=f32(1e-4), beta1=f32(0.9), beta2=f32(0.999), eps=f32(1e-8))
+    for step, n in enumerate((13, 7, 21), start=1):
+        rows = np.sort(rng.choice(vocab, n, replace=False)).astype(np.int32)
+        grad = rng.normal(0, 1.0, (n, f)).astype(np.float32)
+        before = table.clone()
+        st.staple_adamw_rows_host(table, m, v, torch.from_numpy(rows), torch.from_numpy(grad),
+                                  step=step, **hp)
+        ref_p, ref_m, ref_v = O.adamw_rows(ref_p, ref_m, ref_v, rows, grad.astype(np.float64),
+                                           step=step, **ohp)
+        if dtype == "bf16":
+            ref_p = O.bf16_round(ref_p)            # the table is stored in bf16 after each step
+        other = np.setdiff1d(np.arange(vocab), rows)
+        assert torch.equal(table[other], before[other]), "untouched rows changed"
+        got = table.double().numpy()
+        if dtype == "f32":
+            np.testing.assert_allclose(got, ref_p, rtol=2e-6, atol=1e-9)
+        else:
+            assert np.all(np.abs(got - ref_p) <= _bf16_ulp(ref_p) * 1.01), "beyond one bf16 ulp"
+            ref_p = got.copy()      # a one-ulp rounding flip must not carry into the next step
+        # fp32 rounding of the terms (|(1-b1) g| <= ~0.5, |(1-b2) g^2| <= ~0.02):
+        # a few float32 ulps of the terms, also where the new moment cancels
+        np.testing.assert_allclose(m.double().numpy(), ref_m, rtol=2e-6, atol=2e-7)
+        np.testing.assert_allclose(v.double().numpy(), ref_v, rtol=2e-6, atol=1e-8)
+
+
+def test_host_adamw_refuses_rows_outside_the_table():
+    import torch
+    st = _lib()
+    table = torch.zeros(8, 16, dtype=torch.bfloat16)
+    m, v = torch.zeros(8, 16), torch.zeros(8, 16)
+    grad = torch.ones(2, 16)
+    before = table.clone()
+    with pytest.raises(RuntimeError):
+        st.staple_adamw_rows_host(table, m, v, torch.tensor([1, 8], dtype=torch.int32), grad,
+                                  lr=1e-3, weight_decay=0.0, step=1)
+    assert torch.equal(table, before) and not m.any()
+    with pytest.raises(RuntimeError):       # step 0 has no bias correction
+        st.staple_adamw_rows_host(table, m, v, torch.tensor([1, 2], dtype=torch.int32), grad,
+                                  lr=1e-3, weight_decay=0.0, step=0)

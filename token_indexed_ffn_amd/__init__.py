@@ -369,6 +369,46 @@ def staple_ffn_down(h: torch.Tensor, w_down: torch.Tensor, y: torch.Tensor,
     return y
 
 
+def staple_adamw_rows(table: torch.Tensor, m: torch.Tensor, v: torch.Tensor, rows: torch.Tensor,
+                      grad: torch.Tensor, *, lr: float, weight_decay: float, step: int,
+                      n_rows: Optional[torch.Tensor] = None, beta1: float = 0.9,
+                      beta2: float = 0.999, eps: float = 1e-8, stream=None) -> None:
+    """AdamW on table rows rows[:n] (device tensors; n from the device scalar when given)."""
+    _dev(table, m, v, rows, grad, n_rows)
+    vocab, d_ff = table.shape
+    _check(lib().staple_adamw_rows(_p(table), _p(m), _p(v), vocab, d_ff, _dt(table), _p(rows),
+                                   _p(n_rows), rows.numel(), _p(grad), lr, beta1, beta2, eps,
+                                   weight_decay, step, _stream(stream)), "staple_adamw_rows")
+
+
+def staple_adamw_rows_host(table: torch.Tensor, m: torch.Tensor, v: torch.Tensor,
+                           rows: torch.Tensor, grad: torch.Tensor, *, lr: float,
+                           weight_decay: float, step: int, beta1: float = 0.9,
+                           beta2: float = 0.999, eps: float = 1e-8, n_threads: int = 0) -> None:
+    """The same update on host tensors with host threads (synchronous)."""
+    for t in (table, m, v, rows, grad):
+        if t.is_cuda or not t.is_contiguous():
+            raise ValueError("expected contiguous host tensors")
+    if m.dtype != torch.float32 or v.dtype != torch.float32 or grad.dtype != torch.float32:
+        raise TypeError("moments and gradients are float32")
+    vocab, d_ff = table.shape
+    _check(lib().staple_adamw_rows_host(_p(table), _p(m), _p(v), vocab, d_ff, _dt(table), _p(rows),
+                                        rows.numel(), _p(grad), lr, beta1, beta2, eps,
+                                        weight_decay, step, n_threads), "staple_adamw_rows_host")
+
+
+def staple_cache_refresh(table: torch.Tensor, uniq: torch.Tensor, code: torch.Tensor,
+                         n_unique: torch.Tensor, cache_rows: torch.Tensor, stream=None) -> None:
+    """cache_rows[code[u]] = table[uniq[u]] for the cached rows among uniq[:n_unique]."""
+    if not (table.is_cuda or table.is_pinned()) or not table.is_contiguous():
+        raise ValueError("table must be a contiguous device or pinned host tensor")
+    _dev(uniq, code, n_unique, cache_rows)
+    vocab, d_ff = table.shape
+    _check(lib().staple_cache_refresh(_p(table), vocab, d_ff, _dt(table), _p(uniq), _p(code),
+                                      _p(n_unique), uniq.numel(), _p(cache_rows),
+                                      cache_rows.shape[0], _stream(stream)), "staple_cache_refresh")
+
+
 def staple_ffn_bwd_table_grad(dy: torch.Tensor, x: torch.Tensor, w_gate: torch.Tensor,
                               w_up: torch.Tensor, w_down: torch.Tensor, saved_g: torch.Tensor,
                               saved_u: torch.Tensor, saved_h: torch.Tensor,

@@ -16,6 +16,7 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libstaple.so")
 
 c_i32, c_i64, c_sz, c_vp = ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t, ctypes.c_void_p
+c_f32 = ctypes.c_float
 
 # name -> (restype, argtypes)
 _SIGS = {
@@ -53,6 +54,12 @@ _SIGS = {
                                        c_sz, c_vp]),
     "staple_ffn_fwd_packed": (c_i32, [c_i64, c_i64, c_i64, c_i32, c_i32, c_vp, c_vp, c_vp, c_vp,
                                       c_i64, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_sz, c_vp]),
+    "staple_adamw_rows": (c_i32, [c_vp, c_vp, c_vp, c_i64, c_i64, c_i32, c_vp, c_vp, c_i64, c_vp,
+                                  c_f32, c_f32, c_f32, c_f32, c_f32, c_i64, c_vp]),
+    "staple_adamw_rows_host": (c_i32, [c_vp, c_vp, c_vp, c_i64, c_i64, c_i32, c_vp, c_i64, c_vp,
+                                       c_f32, c_f32, c_f32, c_f32, c_f32, c_i64, c_i32]),
+    "staple_cache_refresh": (c_i32, [c_vp, c_i64, c_i64, c_i32, c_vp, c_vp, c_vp, c_i64, c_vp, c_i64,
+                                     c_vp]),
     "staple_ffn_bwd_workspace_bytes": (c_sz, [c_i64, c_i64, c_i64, c_i32]),
     "staple_ffn_bwd_table_grad": (c_i32, [c_i64, c_i64, c_i64, c_i32, c_i32, c_vp, c_vp, c_vp,
                                           c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_i64,

@@ -4,6 +4,7 @@
 #include <atomic>
 #include <cstring>
 #include <mutex>
+#include <cmath>
 #include <thread>
 #include <vector>
 
@@ -81,6 +82,19 @@ hipError_t decode_down(int64_t n, int64_t d, int64_t f, const void* h, const voi
                        int out_dtype, void* ws, hipStream_t s, bool packed);
 hipError_t decode_pack(int64_t d, int64_t f, const void* wg, const void* wu, const void* wd,
                        void* packed_gu, void* packed_down, hipStream_t s);
+
+// kernels (optim.hip)
+AdamWConsts adamw_consts(float lr, float beta1, float beta2, float eps, float weight_decay,
+                         int64_t step);
+hipError_t launch_adamw_rows(void* table, int dtype, float* m, float* v, int64_t vocab, int64_t d_ff,
+                             const int32_t* rows, const int32_t* n_rows, int64_t max_rows,
+                             const float* grad, const AdamWConsts& c, hipStream_t s, int* err);
+void host_adamw_rows(void* table, int dtype, float* m, float* v, int64_t d_ff, const int32_t* rows,
+                     int64_t n_rows, const float* grad, const AdamWConsts& c, int n_threads);
+hipError_t launch_cache_refresh(const void* table, int64_t vocab, const int32_t* uniq,
+                                const int32_t* code, const int32_t* n_unique, int64_t max_unique,
+                                int64_t row_bytes, void* cache_rows, int64_t capacity, hipStream_t s,
+                                int* err, unsigned max_workgroups);
 
 // ---------------------------------------------------------------------------
 // Per-device error word
@@ -535,6 +549,66 @@ staple_status_t staple_ffn_fwd_packed(int64_t n, int64_t d, int64_t f, int32_t d
   HIPCALL(decode_gateup(n, nullptr, n, d, f, x, packed_gate_up, nullptr, rows, n_rows, row_index, h,
                         save_g, save_u, s, err, true));
   HIPCALL(decode_down(n, d, f, h, packed_down, y, out_dtype, down_ws, s, true));
+  return STAPLE_OK;
+}
+
+// ------------------------------------------------------------------ AdamW
+static bool adamw_hparams_ok(float lr, float beta1, float beta2, float eps, float weight_decay,
+                             int64_t step) {
+  return step >= 1 && std::isfinite(lr) && lr >= 0.0f && beta1 >= 0.0f && beta1 < 1.0f &&
+         beta2 >= 0.0f && beta2 < 1.0f && std::isfinite(eps) && eps >= 0.0f &&
+         std::isfinite(weight_decay) && weight_decay >= 0.0f;
+}
+
+staple_status_t staple_adamw_rows(void* table, float* m, float* v, int64_t vocab, int64_t d_ff,
+                                  int32_t dtype, const int32_t* rows, const int32_t* n_rows,
+                                  int64_t max_rows, const float* grad, float lr, float beta1,
+                                  float beta2, float eps, float weight_decay, int64_t step,
+                                  void* stream) {
+  REQUIRE(valid_dtype(dtype) && vocab >= 1 && d_ff > 0 && d_ff % 8 == 0 && max_rows >= 0);
+  REQUIRE(adamw_hparams_ok(lr, beta1, beta2, eps, weight_decay, step));
+  if (max_rows == 0) return STAPLE_OK;
+  REQUIRE(table && m && v && rows && grad);
+  REQUIRE(aligned16(table) && aligned16(m) && aligned16(v) && aligned16(grad));
+  GET_ERR(err);
+  const AdamWConsts c = adamw_consts(lr, beta1, beta2, eps, weight_decay, step);
+  HIPCALL(launch_adamw_rows(table, dtype, m, v, vocab, d_ff, rows, n_rows, max_rows, grad, c,
+                            S(stream), err));
+  return STAPLE_OK;
+}
+
+staple_status_t staple_adamw_rows_host(void* table, float* m, float* v, int64_t vocab, int64_t d_ff,
+                                       int32_t dtype, const int32_t* rows, int64_t n_rows,
+                                       const float* grad, float lr, float beta1, float beta2,
+                                       float eps, float weight_decay, int64_t step,
+                                       int32_t n_threads) {
+  REQUIRE(valid_dtype(dtype) && vocab >= 1 && d_ff > 0 && n_rows >= 0);
+  REQUIRE(adamw_hparams_ok(lr, beta1, beta2, eps, weight_decay, step));
+  if (n_rows == 0) return STAPLE_OK;
+  REQUIRE(table && m && v && rows && grad);
+  for (int64_t k = 0; k < n_rows; ++k)
+    if (rows[k] < 0 || rows[k] >= vocab) return STAPLE_ERR_HOST;
+  const int hw = static_cast<int>(std::max(1u, std::thread::hardware_concurrency()));
+  const int nt = n_threads > 0 ? n_threads : std::min(hw, 16);
+  const AdamWConsts c = adamw_consts(lr, beta1, beta2, eps, weight_decay, step);
+  host_adamw_rows(table, dtype, m, v, d_ff, rows, n_rows, grad, c, nt);
+  return STAPLE_OK;
+}
+
+staple_status_t staple_cache_refresh(const void* table, int64_t vocab, int64_t d_ff, int32_t dtype,
+                                     const int32_t* uniq, const int32_t* code,
+                                     const int32_t* n_unique, int64_t max_unique, void* cache_rows,
+                                     int64_t capacity, void* stream) {
+  REQUIRE(valid_dtype(dtype) && vocab >= 1 && d_ff > 0 && capacity >= 0 && max_unique >= 0);
+  REQUIRE((d_ff * elem_bytes(dtype)) % 16 == 0);
+  if (max_unique == 0 || capacity == 0) return STAPLE_OK;
+  REQUIRE(table && uniq && code && n_unique && cache_rows);
+  REQUIRE(aligned16(table) && aligned16(cache_rows));
+  REQUIRE(device_addressable(table) && device_addressable(cache_rows));
+  GET_ERR(err);
+  HIPCALL(launch_cache_refresh(table, vocab, uniq, code, n_unique, max_unique,
+                               d_ff * elem_bytes(dtype), cache_rows, capacity, S(stream), err,
+                               copy_workgroups(table)));
   return STAPLE_OK;
 }
 

@@ -114,6 +114,14 @@ struct Workspace {
     if (_e != hipSuccess) return STAPLE_ERR_HIP;        \
   } while (0)
 
+// Constants of one AdamW step (optim.hip): decay = 1 - lr wd,
+// step_size = lr / (1 - beta1^t), inv_sqrt_bc2 = 1 / sqrt(1 - beta2^t).
+namespace staple {
+struct AdamWConsts {
+  float decay, beta1, one_m_beta1, beta2, one_m_beta2, step_size, inv_sqrt_bc2, eps;
+};
+}  // namespace staple
+
 #define STAPLE_LAUNCH_CHECK()                           \
   do {                                                  \
     hipError_t _e = hipGetLastError();                  \

@@ -1,0 +1,225 @@
+// AdamW step on the touched rows of a token-indexed table, on the device and
+// on the host, and the refresh of cached copies of updated rows.
+//
+// The tables are trained with AdamW and their moments kept in fp32 beside
+// the bf16 table, in host memory in the offloaded design (STAPLE Figure 4
+// caption: bf16 tables and fp32 AdamW moments in host DRAM; Table 3: peak
+// learning rate and weight decay of the table group).  Only the rows of the
+// batch's unique IDs are updated: a row absent from the batch keeps its
+// parameters and moments, and the bias correction uses the global step.
+//
+// Per element, in fp32 (decay = 1 - lr wd, step_size = lr / (1 - beta1^t),
+// inv_sqrt_bc2 = 1 / sqrt(1 - beta2^t), the last two formed once in double):
+//
+//   p = p decay;  m = beta1 m + (1 - beta1) g;  v = beta2 v + (1 - beta2) g g
+//   p = p - step_size m / (sqrt(v) inv_sqrt_bc2 + eps)
+//
+// and p is stored back in the table's type (bf16 rounded to nearest even).
+#include <algorithm>
+#include <cmath>
+#include <cstring>
+#include <thread>
+#include <vector>
+
+#include "common.h"
+
+namespace staple {
+
+AdamWConsts adamw_consts(float lr, float beta1, float beta2, float eps, float weight_decay,
+                         int64_t step) {
+  const double bc1 = 1.0 - std::pow(static_cast<double>(beta1), static_cast<double>(step));
+  const double bc2 = 1.0 - std::pow(static_cast<double>(beta2), static_cast<double>(step));
+  AdamWConsts c;
+  c.decay = static_cast<float>(1.0 - static_cast<double>(lr) * weight_decay);
+  c.beta1 = beta1;
+  c.one_m_beta1 = static_cast<float>(1.0 - beta1);
+  c.beta2 = beta2;
+  c.one_m_beta2 = static_cast<float>(1.0 - beta2);
+  c.step_size = static_cast<float>(lr / bc1);
+  c.inv_sqrt_bc2 = static_cast<float>(1.0 / std::sqrt(bc2));
+  c.eps = eps;
+  return c;
+}
+
+__host__ __device__ __forceinline__ void adamw_element(float& p, float& m, float& v, float g,
+                                                       const AdamWConsts& c) {
+  p = p * c.decay;
+  m = c.beta1 * m + c.one_m_beta1 * g;
+  v = c.beta2 * v + c.one_m_beta2 * (g * g);
+  p = p - c.step_size * m / (std::sqrt(v) * c.inv_sqrt_bc2 + c.eps);
+}
+
+// ---------------------------------------------------------------------------
+// Device: one workgroup per listed row (grid-stride over rows), each thread
+// 8 consecutive elements per pass (16-byte bf16 / 32-byte fp32 accesses).
+// ---------------------------------------------------------------------------
+constexpr int kAdamThreads = 256;
+
+template <typename PT>
+__global__ __launch_bounds__(kAdamThreads) void adamw_rows_kernel(
+    PT* __restrict__ table, float* __restrict__ m, float* __restrict__ v, int64_t vocab,
+    int64_t d_ff, const int32_t* __restrict__ rows, const int32_t* __restrict__ n_rows_p,
+    int64_t max_rows, const float* __restrict__ grad, AdamWConsts c, int* err) {
+  const int64_t n = n_rows_p ? min(static_cast<int64_t>(*n_rows_p), max_rows) : max_rows;
+  for (int64_t k = blockIdx.x; k < n; k += gridDim.x) {
+    const int32_t r = rows[k];
+    if (r < 0 || r >= vocab) {
+      if (threadIdx.x == 0) flag_index_error(err);
+      continue;
+    }
+    const int64_t base = static_cast<int64_t>(r) * d_ff;
+    for (int64_t e = static_cast<int64_t>(threadIdx.x) * 8; e < d_ff; e += kAdamThreads * 8) {
+      float pv[8], mv[8], vv[8], gv[8];
+      const float4* mp = reinterpret_cast<const float4*>(m + base + e);
+      const float4* vp = reinterpret_cast<const float4*>(v + base + e);
+      const float4* gp = reinterpret_cast<const float4*>(grad + k * d_ff + e);
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const float4 a = mp[h], b = vp[h], q = gp[h];
+        mv[4 * h] = a.x; mv[4 * h + 1] = a.y; mv[4 * h + 2] = a.z; mv[4 * h + 3] = a.w;
+        vv[4 * h] = b.x; vv[4 * h + 1] = b.y; vv[4 * h + 2] = b.z; vv[4 * h + 3] = b.w;
+        gv[4 * h] = q.x; gv[4 * h + 1] = q.y; gv[4 * h + 2] = q.z; gv[4 * h + 3] = q.w;
+      }
+      if constexpr (sizeof(PT) == 2) {
+        const uint4 raw = *reinterpret_cast<const uint4*>(table + base + e);
+        const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          pv[2 * i] = __uint_as_float(w[i] << 16);
+          pv[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+        }
+      } else {
+        const float4* pp = reinterpret_cast<const float4*>(table + base + e);
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const float4 a = pp[h];
+          pv[4 * h] = a.x; pv[4 * h + 1] = a.y; pv[4 * h + 2] = a.z; pv[4 * h + 3] = a.w;
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < 8; ++i) adamw_element(pv[i], mv[i], vv[i], gv[i], c);
+      float4* mo = reinterpret_cast<float4*>(m + base + e);
+      float4* vo = reinterpret_cast<float4*>(v + base + e);
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        mo[h] = make_float4(mv[4 * h], mv[4 * h + 1], mv[4 * h + 2], mv[4 * h + 3]);
+        vo[h] = make_float4(vv[4 * h], vv[4 * h + 1], vv[4 * h + 2], vv[4 * h + 3]);
+      }
+      if constexpr (sizeof(PT) == 2) {
+        uint4 o;
+        o.x = f32_to_bf16(pv[0]) | (static_cast<uint32_t>(f32_to_bf16(pv[1])) << 16);
+        o.y = f32_to_bf16(pv[2]) | (static_cast<uint32_t>(f32_to_bf16(pv[3])) << 16);
+        o.z = f32_to_bf16(pv[4]) | (static_cast<uint32_t>(f32_to_bf16(pv[5])) << 16);
+        o.w = f32_to_bf16(pv[6]) | (static_cast<uint32_t>(f32_to_bf16(pv[7])) << 16);
+        *reinterpret_cast<uint4*>(table + base + e) = o;
+      } else {
+        float4* po = reinterpret_cast<float4*>(table + base + e);
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+          po[h] = make_float4(pv[4 * h], pv[4 * h + 1], pv[4 * h + 2], pv[4 * h + 3]);
+      }
+    }
+  }
+}
+
+hipError_t launch_adamw_rows(void* table, int dtype, float* m, float* v, int64_t vocab, int64_t d_ff,
+                             const int32_t* rows, const int32_t* n_rows, int64_t max_rows,
+                             const float* grad, const AdamWConsts& c, hipStream_t s, int* err) {
+  if (max_rows == 0) return hipSuccess;
+  const unsigned grid = static_cast<unsigned>(std::min<int64_t>(max_rows, 65535));
+  if (dtype == STAPLE_BF16)
+    adamw_rows_kernel<uint16_t><<<grid, kAdamThreads, 0, s>>>(static_cast<uint16_t*>(table), m, v, vocab,
+                                                              d_ff, rows, n_rows, max_rows, grad, c, err);
+  else
+    adamw_rows_kernel<float><<<grid, kAdamThreads, 0, s>>>(static_cast<float*>(table), m, v, vocab, d_ff,
+                                                           rows, n_rows, max_rows, grad, c, err);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Host: the same update with host threads over rows (bf16 stored with
+// round-to-nearest-even, NaN kept quiet).
+// ---------------------------------------------------------------------------
+static inline float host_bf16_to_f32(uint16_t b) {
+  const uint32_t u = static_cast<uint32_t>(b) << 16;
+  float f;
+  std::memcpy(&f, &u, 4);
+  return f;
+}
+static inline uint16_t host_f32_to_bf16(float f) {
+  uint32_t u;
+  std::memcpy(&u, &f, 4);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<uint16_t>((u >> 16) | 0x40);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return static_cast<uint16_t>(u >> 16);
+}
+
+void host_adamw_rows(void* table, int dtype, float* m, float* v, int64_t d_ff, const int32_t* rows,
+                     int64_t n_rows, const float* grad, const AdamWConsts& c, int n_threads) {
+  auto do_rows = [&](int64_t lo, int64_t hi) {
+    for (int64_t k = lo; k < hi; ++k) {
+      const int64_t base = static_cast<int64_t>(rows[k]) * d_ff;
+      float* mr = m + base;
+      float* vr = v + base;
+      const float* gr = grad + k * d_ff;
+      if (dtype == STAPLE_BF16) {
+        uint16_t* pr = static_cast<uint16_t*>(table) + base;
+        for (int64_t e = 0; e < d_ff; ++e) {
+          float p = host_bf16_to_f32(pr[e]);
+          adamw_element(p, mr[e], vr[e], gr[e], c);
+          pr[e] = host_f32_to_bf16(p);
+        }
+      } else {
+        float* pr = static_cast<float*>(table) + base;
+        for (int64_t e = 0; e < d_ff; ++e) adamw_element(pr[e], mr[e], vr[e], gr[e], c);
+      }
+    }
+  };
+  const int64_t nt = std::max<int64_t>(1, std::min<int64_t>(n_threads, n_rows));
+  if (nt <= 1) {
+    do_rows(0, n_rows);
+    return;
+  }
+  std::vector<std::thread> pool;
+  pool.reserve(static_cast<size_t>(nt));
+  for (int64_t t = 0; t < nt; ++t)
+    pool.emplace_back(do_rows, n_rows * t / nt, n_rows * (t + 1) / nt);
+  for (auto& th : pool) th.join();
+}
+
+// ---------------------------------------------------------------------------
+// Cache refresh: cache_rows[code[u]] = table[uniq[u]] for every u < n with
+// code[u] >= 0 (the cached rows among those just updated).
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void cache_refresh_kernel(
+    const void* __restrict__ table, int64_t vocab, const int32_t* __restrict__ uniq,
+    const int32_t* __restrict__ code, const int32_t* __restrict__ n_unique_p, int64_t max_unique,
+    int64_t row_bytes, void* __restrict__ cache_rows, int64_t capacity, int* err) {
+  const int64_t n = min(static_cast<int64_t>(*n_unique_p), max_unique);
+  for (int64_t u = blockIdx.x; u < n; u += gridDim.x) {
+    const int32_t c = code[u];
+    if (c < 0) continue;
+    const int32_t id = uniq[u];
+    if (c >= capacity || id < 0 || id >= vocab) {
+      if (threadIdx.x == 0) flag_index_error(err);
+      continue;
+    }
+    const uint4* src = reinterpret_cast<const uint4*>(static_cast<const char*>(table) + id * row_bytes);
+    uint4* dst = reinterpret_cast<uint4*>(static_cast<char*>(cache_rows) + c * row_bytes);
+    for (int64_t i = threadIdx.x; i < row_bytes / 16; i += 256) dst[i] = src[i];
+  }
+}
+
+hipError_t launch_cache_refresh(const void* table, int64_t vocab, const int32_t* uniq,
+                                const int32_t* code, const int32_t* n_unique, int64_t max_unique,
+                                int64_t row_bytes, void* cache_rows, int64_t capacity, hipStream_t s,
+                                int* err, unsigned max_workgroups) {
+  if (max_unique == 0) return hipSuccess;
+  const unsigned grid = static_cast<unsigned>(
+      max_workgroups > 0 && max_unique > max_workgroups ? max_workgroups : std::min<int64_t>(max_unique, 65535));
+  cache_refresh_kernel<<<grid, 256, 0, s>>>(table, vocab, uniq, code, n_unique, max_unique, row_bytes,
+                                            cache_rows, capacity, err);
+  return hipGetLastError();
+}
+
+}  // namespace staple
