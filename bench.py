@@ -364,6 +364,7 @@ def run_train(torch, st, w, steps, warmup):
     flops_total = 18 * n * d * f
     gu_flops = 4 * n * d * f
     achieved = gu_flops / (gu_us * 1e-6) / 1e12
+    adamw = run_device_adamw(torch, st, T, w, reps=max(5, steps))
     return {
         "workload": w.name, "tokens": n, "ms_per_step": ms, "tokens_per_s": n / (ms * 1e-3),
         "step_tflops": flops_total / (ms * 1e-3) / 1e12,
@@ -377,7 +378,38 @@ def run_train(torch, st, w, steps, warmup):
                                             source_sha("gemm.hip", "common.h")),
             "avg_launch_us": gu_us, "algorithmic_flops_per_launch": gu_flops,
         },
+        "adamw_table_rows": adamw,
     }, T
+
+
+def run_device_adamw(torch, st, T, w, reps):
+    """AdamW on the batch's unique table rows, table and fp32 moments in HBM,
+    gradients from the step's d_rows; events around the launches."""
+    dev = T["table"].device
+    vocab, f = T["table"].shape
+    m = torch.zeros(vocab, f, dtype=torch.float32, device=dev)
+    v = torch.zeros(vocab, f, dtype=torch.float32, device=dev)
+    dd, g = T["dd"], T["bwd"]["d_rows"]
+    kw = dict(lr=3e-4, weight_decay=1e-4, n_rows=dd["n_unique"])
+    st.staple_adamw_rows(T["table"], m, v, dd["uniq"], g, step=1, **kw)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(reps):
+        st.staple_adamw_rows(T["table"], m, v, dd["uniq"], g, step=2 + i, **kw)
+    e1.record()
+    torch.cuda.synchronize()
+    if st.staple_get_device_error() != 0:
+        raise RuntimeError("device error in AdamW")
+    us = e0.elapsed_time(e1) / reps * 1e3
+    u = int(dd["n_unique"].item())
+    nbytes = u * f * (2 * 2 + 2 * 4 + 2 * 4 + 4)     # param, m, v read + written, gradient read
+    del m, v
+    torch.cuda.empty_cache()
+    return {"rows": u, "us_per_step": us, "hbm_gb_s": nbytes / (us * 1e-6) / 1e9,
+            "algorithmic_bytes": nbytes, "frac_of_hbm_peak": nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS,
+            "note": "staple_adamw_rows over the batch's unique rows (bf16 table, fp32 moments in "
+                    "HBM): 24 bytes moved per element"}
 
 
 def train_cpu_baseline(torch, w, T, seconds):
@@ -619,6 +651,7 @@ def run_offload_train(torch, st, w, steps, warmup):
                 stats["pack_s"] / steps * 1e3, m)
 
     res = {k: timed(k) for k in ("staged", "direct", "resident")}
+    host_adamw = run_host_adamw(torch, st, O, T, lk_out)
     mode = min(("staged", "direct"), key=lambda k: res[k][0])
     ms, _, _, m = res[mode]
     ms_res = res["resident"][0]
@@ -626,6 +659,7 @@ def run_offload_train(torch, st, w, steps, warmup):
            "method": mode, "n_unique": int(T["dd"]["n_unique"].item()), "miss_rows": m,
            "cache_capacity": w.cache_capacity, "token_hit_rate": stats["hit_tokens"] / n,
            "resident_ms_per_step": ms_res, "pcie_bytes_per_step": m * f * 2}
+    out["adamw_host"] = host_adamw
     for k in ("staged", "direct"):
         ms_k, copy_k, pack_k, _ = res[k]
         out[k] = {"ms_per_step": ms_k, "copy_ms": copy_k, "host_pack_ms": pack_k,
@@ -640,6 +674,48 @@ def run_offload_train(torch, st, w, steps, warmup):
                    "resident: the same step with the miss rows already in HBM, for the hidden "
                    "fraction = 1 - (t - t_resident) / (host pack + copy time)")
     return out
+
+
+def run_host_adamw(torch, st, O, T, lk, reps=3):
+    """The pages' optimizer placement for offloaded tables: the table and its
+    fp32 moments in host memory; after the backward the batch's row gradients
+    come to the host over PCIe, host threads update the rows, and the cached
+    copies of the updated rows are refreshed from the host table."""
+    import numpy as np
+    table = O["tables"][0]
+    vocab, f = table.shape
+    dd = T["dd"]
+    u = int(dd["n_unique"].item())
+    m = torch.zeros(vocab, f, dtype=torch.float32)
+    v = torch.zeros(vocab, f, dtype=torch.float32)
+    grad_h = torch.empty(u, f, dtype=torch.float32, pin_memory=True)
+    uniq_h = dd["uniq"][:u].cpu().contiguous()
+    t_copy, t_upd, t_ref = [], [], []
+    for i in range(reps):
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        grad_h.copy_(T["bwd"]["d_rows"][:u], non_blocking=True)
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        st.staple_adamw_rows_host(table, m, v, uniq_h, grad_h, lr=3e-4, weight_decay=1e-4,
+                                  step=i + 1)
+        t2 = time.perf_counter()
+        st.staple_cache_refresh(table, dd["uniq"], lk["code"], dd["n_unique"], O["cache_rows"][0])
+        torch.cuda.synchronize()
+        t3 = time.perf_counter()
+        t_copy.append(t1 - t0)
+        t_upd.append(t2 - t1)
+        t_ref.append(t3 - t2)
+    if st.staple_get_device_error() != 0:
+        raise RuntimeError("device error in the cache refresh")
+    upd = float(np.median(t_upd))
+    nbytes = u * f * (2 * 2 + 2 * 4 + 2 * 4 + 4)
+    return {"rows": u, "grad_d2h_ms": float(np.median(t_copy)) * 1e3, "update_ms": upd * 1e3,
+            "cache_refresh_ms": float(np.median(t_ref)) * 1e3,
+            "host_gb_s": nbytes / upd / 1e9, "threads": min(16, os.cpu_count() or 1),
+            "note": "staple_adamw_rows_host over the batch's unique rows (bf16 table, fp32 "
+                    "moments in host memory), after a D2H copy of the fp32 row gradients; then "
+                    "staple_cache_refresh of the cached rows among them"}
 
 
 # ----------------------------------------------------------------------------
