@@ -201,17 +201,22 @@ def ffn_forward(x, w_gate, w_up, w_down, table, ids, precision: str = EXACT,
 
     Returns g, u (pre-rounding), g_saved, u_saved (as stored for backward),
     h, and y (when every column is present).
+
+    ``w_up=None`` is the STEM layer the pages compare against: the
+    up-projection is replaced by the token's table row, u = E[t] (STAPLE
+    abstract: STEM replaces the FFN up-projections with token-indexed
+    embeddings, STAPLE keeps them and adds the embeddings as a residual).
     """
     x = np.asarray(x, dtype=np.float64)
     ids = np.asarray(ids, dtype=np.int64)
     wg = np.asarray(w_gate, dtype=np.float64)
-    wu = np.asarray(w_up, dtype=np.float64)
+    wu = None if w_up is None else np.asarray(w_up, dtype=np.float64)
     if cols is not None:
         wg = wg[cols]
-        wu = wu[cols]
+        wu = None if wu is None else wu[cols]
     g = x @ wg.T
-    a = x @ wu.T
-    u = a + _table_rows(table, ids, cols)
+    rows = _table_rows(table, ids, cols)
+    u = rows if wu is None else x @ wu.T + rows
     h = _maybe_round(silu(g) * u, precision)
     out = {"g": g, "u": u, "h": h,
            "g_saved": _maybe_round(g, precision),
@@ -252,16 +257,19 @@ def ffn_backward(dy, x, w_gate, w_up, w_down, fwd: dict, ids, precision: str = E
     dw_gate, dw_up (absent when ``freeze_up``: during warmup the up-projections
     of augmented layers are frozen, STAPLE Table 3 caption; the gradient still
     flows through them into dx and the table rows) and dx.
+
+    ``w_up=None`` (STEM, see ffn_forward): there is no dw_up and dx has no
+    up-projection term.
     """
     dy = np.asarray(dy, dtype=np.float64)
     x = np.asarray(x, dtype=np.float64)
     wd = np.asarray(w_down, dtype=np.float64)
     wg = np.asarray(w_gate, dtype=np.float64)
-    wu = np.asarray(w_up, dtype=np.float64)
+    wu = None if w_up is None else np.asarray(w_up, dtype=np.float64)
     if cols is not None:
         wd = wd[:, cols]
         wg = wg[cols]
-        wu = wu[cols]
+        wu = None if wu is None else wu[cols]
     g = fwd["g_saved"]
     u = fwd["u_saved"]
     h = fwd["h"]
@@ -278,10 +286,12 @@ def ffn_backward(dy, x, w_gate, w_up, w_down, fwd: dict, ids, precision: str = E
         "dw_down": dy.T @ h,                         # dL/dW_down = sum_i dy_i h_i^T
         "dw_gate": dg.T @ x,                         # dL/dW_gate = sum_i dg_i x_i^T
     }
-    if not freeze_up:
+    if not freeze_up and wu is not None:
         out["dw_up"] = du.T @ x                      # dL/dW_up = sum_i du_i x_i^T
     if cols is None and with_dx:
-        out["dx"] = dg @ wg + du @ wu                # dL/dx = W_gate^T dg + W_up^T du
+        out["dx"] = dg @ wg                          # dL/dx = W_gate^T dg (+ W_up^T du)
+        if wu is not None:
+            out["dx"] = out["dx"] + du @ wu
     return out
 
 

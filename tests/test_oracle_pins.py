@@ -476,3 +476,41 @@ def test_adamw_sparse_rows_match_torch_sparse_adam():
                                beta1=b1, beta2=b2, eps=eps)
     np.testing.assert_allclose(p, w.detach().numpy(), rtol=1e-9, atol=1e-12)
     np.testing.assert_array_equal(p[[2, 4, 6, 8]], table[[2, 4, 6, 8]])
+
+
+# ---------------------------------------------------------------- STEM variant
+def test_stem_is_staple_with_a_zero_up_projection():
+    """STEM (up-projection replaced by the table row) equals the STAPLE layer
+    with W_up = 0 in every output but dW_up, bit for bit in float64."""
+    rng = np.random.default_rng(31)
+    x, wg, wu, wd, e, ids, dy = _rand_layer(rng, 40, 16, 24, 9)
+    zero = np.zeros_like(wu)
+    for prec in (O.EXACT, O.BF16):
+        fs = O.ffn_forward(x, wg, None, wd, e, ids, precision=prec)
+        fz = O.ffn_forward(x, wg, zero, wd, e, ids, precision=prec)
+        for k in ("g", "u", "h", "y", "g_saved", "u_saved"):
+            np.testing.assert_array_equal(fs[k], fz[k], err_msg=k)
+        bs = O.ffn_backward(dy, x, wg, None, wd, fs, ids, precision=prec)
+        bz = O.ffn_backward(dy, x, wg, zero, wd, fz, ids, precision=prec)
+        assert "dw_up" not in bs
+        for k in ("dh", "du", "dg", "d_rows", "dw_down", "dw_gate", "dx"):
+            np.testing.assert_array_equal(bs[k], bz[k], err_msg=k)
+
+
+def test_stem_matches_torch_autograd():
+    """y = W_down (silu(W_gate x) * E[t]) and its gradients, by autograd."""
+    rng = np.random.default_rng(32)
+    n, d, f, v = 33, 12, 20, 7
+    x, wg, _, wd, e, ids, dy = _rand_layer(rng, n, d, f, v)
+    t = lambda a: torch.tensor(a, dtype=torch.float64, requires_grad=True)
+    xt, wgt, wdt, et = t(x), t(wg), t(wd), t(e)
+    y = F.linear(F.silu(F.linear(xt, wgt)) * et[torch.tensor(ids)], wdt)
+    y.backward(torch.tensor(dy, dtype=torch.float64))
+    fs = O.ffn_forward(x, wg, None, wd, e, ids)
+    bs = O.ffn_backward(dy, x, wg, None, wd, fs, ids)
+    uniq = np.unique(ids)
+    np.testing.assert_allclose(fs["y"], y.detach().numpy(), rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(bs["dx"], xt.grad.numpy(), rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(bs["dw_gate"], wgt.grad.numpy(), rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(bs["dw_down"], wdt.grad.numpy(), rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(bs["d_rows"], et.grad.numpy()[uniq], rtol=1e-12, atol=1e-12)
