@@ -17,6 +17,14 @@
  * frequent rows live in an HBM cache and misses come from pinned host memory
  * (STAPLE Table 4 caption; retrieval-path table, Prefill and Decode rows).
  *
+ * The forward and backward calls also run the STEM layer, the replacement
+ * design STAPLE is compared against (STAPLE abstract; Table 1 and Table 4,
+ * STEM rows): it has no up-projection and the table row takes its place,
+ *
+ *     u_i = E[t_i],  h_i = silu(W_gate x_i) * u_i,  y_i = W_down h_i,
+ *
+ * selected by passing w_up = NULL (row-major weights) or up_proj = 0 (packed).
+ *
  * Conventions shared by every entry point:
  *   - Pointers are DEVICE pointers owned by the caller unless marked "host".
  *     The library never frees or retains them.
@@ -220,13 +228,15 @@ staple_status_t staple_gather_rows(const void* src, int64_t src_rows, const int3
 /* ------------------------------------------------------------------------
  * Forward of one augmented layer.
  *   x [n_tokens x d_model] (dtype), w_gate, w_up [d_ff x d_model],
- *   w_down [d_model x d_ff] (dtype);
+ *   w_down [d_model x d_ff] (dtype); w_up NULL selects the STEM layer
+ *   (u = rows[row_index], the gate GEMM alone);
  *   rows [n_rows x d_ff] (dtype): the compact block R with row_index = inv,
  *   or a whole device-resident table with row_index = the token IDs.
  *   row_index int32[n_tokens], each in [0, n_rows).
  * Outputs: y [n_tokens x d_model] of out_dtype (STAPLE_F32 or STAPLE_BF16).
  *   save_g, save_u, save_h [n_tokens x d_ff] (dtype), each nullable: the
- *   pre-activation g, the up branch u = W_up x + E[t] and h, for the backward.
+ *   pre-activation g, the up branch u = W_up x + E[t] (STEM: u = E[t]) and h,
+ *   for the backward.
  * Layout requirements: d_model and d_ff multiples of 64; 16-byte aligned
  * pointers.  n_tokens >= 0 (0 enqueues nothing).
  * In bf16, g, u and y accumulate in fp32; h is rounded to bf16 once (the
@@ -294,22 +304,27 @@ staple_status_t staple_ffn_down(int64_t n_tokens, int64_t d_model, int64_t d_ff,
  *
  * staple_decode_pack_weights: bf16 only.  Either output may be NULL (then
  *   its source may be NULL too).
- *   w_gate, w_up [d_ff x d_model], w_down [d_model x d_ff] row-major bf16.
+ *   w_gate, w_up [d_ff x d_model], w_down [d_model x d_ff] row-major bf16;
+ *   w_up NULL packs the STEM layer's gate-only operand.
  *   packed_gate_up: 2 * d_ff * d_model bf16 elements (the size of w_gate and
- *     w_up together); packed_down: d_model * d_ff elements.  Both are owned
- *     by the caller, device memory, 16-byte aligned, and must not overlap
- *     the sources.
+ *     w_up together; d_ff * d_model for the gate-only operand); packed_down:
+ *     d_model * d_ff elements.  Both are owned by the caller, device memory,
+ *     16-byte aligned, and must not overlap the sources.
  *   Format (a private layout: produce it only with this call): an operand of
  *   R rows x K columns is cut into K/64 steps of R/16 row blocks; bytes
  *   ((s * R/16 + b) * 2 + j) * 1024 + 16 * l .. +16 hold bytes
  *   128 s + 64 j + 16 (l / 16) .. +16 of row l % 16 of block b.  A gate/up
  *   block b holds rows 8b .. 8b+7 of w_gate (block rows 0-7) and of w_up
- *   (block rows 8-15); a down block b holds rows 16b .. 16b+15 of w_down.
+ *   (block rows 8-15); a gate-only block b rows 16b .. 16b+15 of w_gate; a
+ *   down block b rows 16b .. 16b+15 of w_down.
  *   d_model and d_ff multiples of 64.
  * staple_ffn_fwd_packed: staple_ffn_fwd for 1 <= n_tokens <= 64 in bf16
  *   (n_tokens == 0 enqueues nothing) reading the packed weights; same
  *   arguments otherwise, same workspace (staple_ffn_fwd_workspace_bytes),
  *   same outputs bit for bit as staple_ffn_fwd on the unpacked weights.
+ *   up_proj: nonzero when packed_gate_up was packed with w_up (the STAPLE
+ *   layer), 0 when it is the gate-only operand (the STEM layer, as
+ *   staple_ffn_fwd with w_up = NULL); a mismatch reads the wrong layout.
  *   Larger batches or fp32 return STAPLE_ERR_UNSUPPORTED.
  * staple_ffn_gate_up_packed, staple_ffn_down_packed: its two halves, as
  *   staple_ffn_gate_up and staple_ffn_down are those of staple_ffn_fwd (same
@@ -323,8 +338,9 @@ staple_status_t staple_decode_pack_weights(int64_t d_model, int64_t d_ff, int32_
                                            void* packed_down, void* stream);
 staple_status_t staple_ffn_gate_up_packed(int64_t n_tokens, int64_t d_model, int64_t d_ff,
                                           int32_t dtype, const void* x,
-                                          const void* packed_gate_up, const void* rows,
-                                          int64_t n_rows, const int32_t* row_index, void* h,
+                                          const void* packed_gate_up, int32_t up_proj,
+                                          const void* rows, int64_t n_rows,
+                                          const int32_t* row_index, void* h,
                                           void* save_g, void* save_u, void* stream);
 staple_status_t staple_ffn_down_packed(int64_t n_tokens, int64_t d_model, int64_t d_ff,
                                        int32_t dtype, int32_t out_dtype, const void* h,
@@ -332,8 +348,8 @@ staple_status_t staple_ffn_down_packed(int64_t n_tokens, int64_t d_model, int64_
                                        size_t ws_bytes, void* stream);
 staple_status_t staple_ffn_fwd_packed(int64_t n_tokens, int64_t d_model, int64_t d_ff,
                                       int32_t dtype, int32_t out_dtype, const void* x,
-                                      const void* packed_gate_up, const void* packed_down,
-                                      const void* rows, int64_t n_rows,
+                                      const void* packed_gate_up, int32_t up_proj,
+                                      const void* packed_down, const void* rows, int64_t n_rows,
                                       const int32_t* row_index, void* y, void* save_g,
                                       void* save_u, void* save_h, void* ws, size_t ws_bytes,
                                       void* stream);
@@ -399,6 +415,8 @@ staple_status_t staple_cache_refresh(const void* table, int64_t vocab, int64_t d
  *   freeze_up != 0: the up-projection is frozen (STAPLE Table 3 caption:
  *     frozen during warmup); dw_up is neither computed nor written (may be
  *     NULL) while the gradient still flows through W_up into dx and d_rows.
+ *   w_up NULL: the STEM layer (saved_u = E[t] from its forward); dx = dL/dg
+ *     W_gate, d_rows as above, dw_up neither computed nor written.
  * In bf16 the backward reads bf16 g and u, forms dL/du and dL/dg in fp32 and
  * rounds them to bf16 once; every contraction accumulates in fp32; d_rows sums
  * the bf16 dL/du values in fp32.

@@ -772,3 +772,132 @@ def test_cache_refresh_after_host_update(st, dev):
     assert touched.any() and (~touched).any()
     keep = torch.from_numpy(np.nonzero(~touched)[0]).to(dev)
     assert torch.equal(cache_rows[keep], stale[keep])
+
+
+# ---------------------------------------------------------------- STEM layer (w_up None)
+def _run_stem(st, dev, inp, out_f32=True):
+    import torch
+    dt = inp.dtype
+    x, wg, wd, tab, dy = (to_dev(getattr(inp, k), dt, dev)
+                          for k in ("x", "w_gate", "w_down", "table", "dy"))
+    ids = torch.from_numpy(inp.ids).to(dev)
+    dd = st.staple_dedup(ids, tab.shape[0])
+    rows = st.staple_gather_rows(tab, dd["uniq"], dd["n_unique"])
+    odt = torch.float32 if out_f32 else x.dtype
+    fwd = st.staple_ffn_fwd(x, wg, None, wd, rows, dd["inv"], out_dtype=odt, save=True)
+    n, d = x.shape
+    f = wg.shape[0]
+    out = {
+        "d_rows": torch.empty(max(n, 1), f, dtype=torch.float32, device=dev),
+        "dx": torch.empty(n, d, dtype=odt, device=dev),
+        "dw_gate": torch.empty(f, d, dtype=torch.float32, device=dev),
+        "dw_up": torch.full((f, d), float("nan"), dtype=torch.float32, device=dev),
+        "dw_down": torch.empty(d, f, dtype=torch.float32, device=dev),
+    }
+    bwd = st.staple_ffn_bwd_table_grad(dy, x, wg, None, wd, fwd["g"], fwd["u"], fwd["h"],
+                                       dd["sorted_pos"], dd["seg_start"], dd["n_unique"],
+                                       out_dtype=odt, out=out)
+    torch.cuda.synchronize()
+    _no_device_error(st)
+    return fwd, bwd
+
+
+@pytest.mark.parametrize("dtype,n,d,f,v,seed", [
+    ("f32", 300, 256, 512, 1000, 60),     # tiled GEMMs, exact fp32 oracle
+    ("bf16", 300, 256, 512, 1000, 61),    # tiled GEMMs
+    ("bf16", 129, 192, 320, 50, 62),      # ragged tiles, repeated tokens
+    ("bf16", 17, 256, 512, 300, 63),      # decode gate kernel (row-major weights)
+    ("bf16", 64, 64, 64, 10, 64),         # decode, one row group per workgroup pair
+    ("bf16", 1, 64, 128, 10, 65),
+])
+def test_stem_layer_matches_oracle(st, dev, dtype, n, d, f, v, seed):
+    """The STEM layer (no up-projection, u = E[t]): forward y, h, g, u and the
+    backward dx, d_rows, dw_gate, dw_down against the oracle with w_up None;
+    dw_up is not written."""
+    _log(f"stem layer {dtype} n={n} d={d} f={f}")
+    inp = S.host_layer_inputs(n, d, f, v, dtype=dtype, seed=seed, table_std=1.0)
+    fwd, bwd = _run_stem(st, dev, inp)
+    prec = O.EXACT if dtype == "f32" else O.BF16
+    g = {k: inp.as_f64(k) for k in ("x", "w_gate", "w_down", "table", "dy")}
+    of = O.ffn_forward(g["x"], g["w_gate"], None, g["w_down"], g["table"], inp.ids, precision=prec)
+    uniq, _, _, _ = O.dedup(inp.ids)
+    ob = O.ffn_backward(g["dy"], g["x"], g["w_gate"], None, g["w_down"], of, inp.ids,
+                        precision=prec, uniq=uniq)
+    name = f"stem {dtype} n={n}"
+    assert_close(to_np(fwd["y"]), of["y"], f"{name} y")
+    assert_close(to_np(fwd["h"]), of["h"], f"{name} h")
+    assert_close(to_np(fwd["g"]), of["g_saved"], f"{name} g")
+    np.testing.assert_array_equal(to_np(fwd["u"]), of["u_saved"])   # u is the table row itself
+    assert_close(to_np(bwd["dx"]), ob["dx"], f"{name} dx")
+    assert_close(to_np(bwd["d_rows"])[:len(uniq)], ob["d_rows"], f"{name} d_rows")
+    assert_close(to_np(bwd["dw_gate"]), ob["dw_gate"], f"{name} dw_gate")
+    assert_close(to_np(bwd["dw_down"]), ob["dw_down"], f"{name} dw_down")
+    assert "dw_up" not in ob
+    assert np.all(np.isnan(to_np(bwd["dw_up"]))), "dw_up was written for the STEM layer"
+
+
+@pytest.mark.parametrize("n", [40, 300])
+def test_stem_split_gate_matches_whole_batch_bitwise(st, dev, n):
+    """The gate-only kernels over two token subsets (the cached / staged-miss
+    split) give the whole batch's h, g, u bit for bit (40 tokens: decode
+    kernel; 300: tiled GEMM)."""
+    import torch
+    _log(f"stem split n={n}")
+    d, f = 128, 320
+    inp = S.host_layer_inputs(n, d, f, 200, dtype="bf16", seed=70 + n, table_std=1.0)
+    x, wg, tab = (to_dev(getattr(inp, k), "bf16", dev) for k in ("x", "w_gate", "table"))
+    ids = torch.from_numpy(inp.ids).to(dev)
+    out = {k: torch.zeros(n, f, dtype=torch.bfloat16, device=dev) for k in ("h", "g", "u")}
+    st.staple_ffn_gate_up(x, wg, None, tab, ids, out["h"], out["g"], out["u"])
+    perm = torch.from_numpy(np.random.default_rng(n).permutation(n).astype(np.int32)).to(dev)
+    k = n // 3
+    part = {kk: torch.zeros(n, f, dtype=torch.bfloat16, device=dev) for kk in ("h", "g", "u")}
+    for sel in (perm[:k], perm[k:]):
+        st.staple_ffn_gate_up_tokens(sel, sel.numel(), x, wg, None, tab, ids, part["h"],
+                                     part["g"], part["u"])
+    torch.cuda.synchronize()
+    _no_device_error(st)
+    for kk in ("h", "g", "u"):
+        assert torch.equal(part[kk], out[kk]), kk
+
+
+@pytest.mark.parametrize("d,f", [(64, 64), (192, 320)])
+def test_stem_decode_pack_is_the_documented_permutation(st, dev, d, f):
+    """Packing without w_up writes W_gate alone in 16-row blocks."""
+    import torch
+    rng = np.random.default_rng(d * f)
+    raw = rng.integers(-32768, 32768, size=(f, d), dtype=np.int16)
+    wg = torch.from_numpy(raw).to(dev).view(torch.bfloat16)
+    pgu, pd = st.staple_decode_pack_weights(wg, None, None, d_model=d, d_ff=f)
+    torch.cuda.synchronize()
+    assert pd is None and pgu.numel() == f * d
+    np.testing.assert_array_equal(pgu.view(torch.int16).cpu().numpy(), _packed_expected(raw, None, 16))
+
+
+@pytest.mark.parametrize("n,d,f", [(17, 256, 512), (64, 64, 64), (1, 64, 8192), (64, 64, 11008),
+                                   (33, 64, 16384), (17, 64, 16448)])
+def test_stem_packed_matches_oracle_and_row_major_bitwise(st, dev, n, d, f):
+    """The STEM decode forward on gate-only packed weights gives the same bits
+    as the row-major call and the oracle's y, h.  The d_ff values cover every
+    workgroup shape: 2 row groups per workgroup (64, 8192), 3 (11008), 4
+    (16384) and 6 with a partly empty last workgroup (16448)."""
+    import torch
+    _log(f"stem packed n={n} d={d} f={f}")
+    inp = S.host_layer_inputs(n, d, f, 300, dtype="bf16", seed=80 + n, table_std=1.0)
+    x, wg, wd, tab = (to_dev(getattr(inp, k), "bf16", dev) for k in ("x", "w_gate", "w_down", "table"))
+    ids = torch.from_numpy(inp.ids).to(dev)
+    pgu, pd = st.staple_decode_pack_weights(wg, None, wd, d_model=d, d_ff=f)
+    ref = st.staple_ffn_fwd(x, wg, None, wd, tab, ids, out_dtype=torch.float32, save=True)
+    got = st.staple_ffn_fwd_packed(x, pgu, pd, tab, ids, d_ff=f, out_dtype=torch.float32, save=True)
+    h2 = torch.empty_like(got["h"])
+    st.staple_ffn_gate_up_packed(x, pgu, tab, ids, h2)
+    torch.cuda.synchronize()
+    _no_device_error(st)
+    for k in ("y", "h", "g", "u"):
+        assert torch.equal(got[k], ref[k]), k
+    assert torch.equal(h2, got["h"])
+    g = {k: inp.as_f64(k) for k in ("x", "w_gate", "w_down", "table")}
+    of = O.ffn_forward(g["x"], g["w_gate"], None, g["w_down"], g["table"], inp.ids, precision=O.BF16)
+    assert_close(to_np(got["y"]), of["y"], f"stem packed y n={n} f={f}")
+    assert_close(to_np(got["h"]), of["h"], f"stem packed h n={n} f={f}")
+    np.testing.assert_array_equal(to_np(got["u"]), of["u_saved"])

@@ -232,12 +232,13 @@ def staple_gather_rows(src: torch.Tensor, index: torch.Tensor, n_rows: Optional[
     return out
 
 
-def staple_ffn_fwd(x: torch.Tensor, w_gate: torch.Tensor, w_up: torch.Tensor,
+def staple_ffn_fwd(x: torch.Tensor, w_gate: torch.Tensor, w_up: Optional[torch.Tensor],
                    w_down: torch.Tensor, rows: torch.Tensor, row_index: torch.Tensor, *,
                    out_dtype: Optional[torch.dtype] = None, save: bool = False,
                    out: Optional[dict] = None, workspace: Optional[torch.Tensor] = None,
                    stream=None) -> dict:
-    """Forward of one augmented layer.  Returns {"y"} (+ "g", "u", "h" when save)."""
+    """Forward of one augmented layer (w_up None: the STEM layer, u = rows[row_index]).
+    Returns {"y"} (+ "g", "u", "h" when save)."""
     _dev(x, w_gate, w_up, w_down, rows, row_index)
     n, d = x.shape
     f = w_gate.shape[0]
@@ -260,12 +261,15 @@ def staple_decode_pack_weights(w_gate: Optional[torch.Tensor], w_up: Optional[to
                                w_down: Optional[torch.Tensor], *, d_model: int, d_ff: int,
                                stream=None) -> tuple:
     """Packed copies of (w_gate, w_up) and of w_down in the decode kernels' read order
-    (bf16).  Returns (packed_gate_up, packed_down); an entry is None when its sources are."""
+    (bf16).  Returns (packed_gate_up, packed_down); packed_gate_up is None without w_gate
+    and the gate-only (STEM) operand, d_ff * d_model elements, when w_up is None;
+    packed_down is None without w_down."""
     _dev(w_gate, w_up, w_down)
     ref = next(t for t in (w_gate, w_up, w_down) if t is not None)
     pgu = pd = None
-    if w_gate is not None or w_up is not None:
-        pgu = torch.empty(2 * d_ff * d_model, dtype=ref.dtype, device=ref.device)
+    if w_gate is not None:
+        pgu = torch.empty((1 if w_up is None else 2) * d_ff * d_model, dtype=ref.dtype,
+                          device=ref.device)
     if w_down is not None:
         pd = torch.empty(d_model * d_ff, dtype=ref.dtype, device=ref.device)
     _check(lib().staple_decode_pack_weights(d_model, d_ff, _dt(ref), _p(w_gate), _p(w_up),
@@ -274,15 +278,26 @@ def staple_decode_pack_weights(w_gate: Optional[torch.Tensor], w_up: Optional[to
     return pgu, pd
 
 
+def _up_proj(packed_gate_up: torch.Tensor, d: int, f: int) -> int:
+    """1 for a packed STAPLE gate/up operand (2 f d elements), 0 for a gate-only one (f d)."""
+    if packed_gate_up.numel() == 2 * f * d:
+        return 1
+    if packed_gate_up.numel() == f * d:
+        return 0
+    raise ValueError("packed_gate_up has neither the gate/up nor the gate-only size")
+
+
 def staple_ffn_fwd_packed(x: torch.Tensor, packed_gate_up: torch.Tensor,
                           packed_down: torch.Tensor, rows: torch.Tensor, row_index: torch.Tensor,
                           *, d_ff: int, out_dtype: Optional[torch.dtype] = None,
                           save: bool = False, out: Optional[dict] = None,
                           workspace: Optional[torch.Tensor] = None, stream=None) -> dict:
-    """staple_ffn_fwd for a decode batch (<= 64 tokens) on packed weights."""
+    """staple_ffn_fwd for a decode batch (<= 64 tokens) on packed weights (a gate-only
+    packed operand runs the STEM layer)."""
     _dev(x, packed_gate_up, packed_down, rows, row_index)
     n, d = x.shape
     f = d_ff
+    up = _up_proj(packed_gate_up, d, f)
     dt = _dt(x)
     out_dtype = out_dtype or x.dtype
     if out is None:
@@ -292,7 +307,7 @@ def staple_ffn_fwd_packed(x: torch.Tensor, packed_gate_up: torch.Tensor,
                 out[k] = torch.empty(n, f, dtype=x.dtype, device=x.device)
     ws = _ws(lib().staple_ffn_fwd_workspace_bytes(n, d, f, dt), workspace, x.device)
     _check(lib().staple_ffn_fwd_packed(n, d, f, dt, _DT[out["y"].dtype], _p(x), _p(packed_gate_up),
-                                       _p(packed_down), _p(rows), rows.shape[0], _p(row_index),
+                                       up, _p(packed_down), _p(rows), rows.shape[0], _p(row_index),
                                        _p(out["y"]), _p(out.get("g")), _p(out.get("u")),
                                        _p(out.get("h")), _p(ws), _ws_size(ws), _stream(stream)),
            "staple_ffn_fwd_packed")
@@ -307,7 +322,8 @@ def staple_ffn_gate_up_packed(x: torch.Tensor, packed_gate_up: torch.Tensor, row
     _dev(x, packed_gate_up, rows, row_index, h, save_g, save_u)
     n, d = x.shape
     f = h.shape[1]
-    _check(lib().staple_ffn_gate_up_packed(n, d, f, _dt(x), _p(x), _p(packed_gate_up), _p(rows),
+    _check(lib().staple_ffn_gate_up_packed(n, d, f, _dt(x), _p(x), _p(packed_gate_up),
+                                           _up_proj(packed_gate_up, d, f), _p(rows),
                                            rows.shape[0], _p(row_index), _p(h), _p(save_g),
                                            _p(save_u), _stream(stream)),
            "staple_ffn_gate_up_packed")
@@ -327,11 +343,12 @@ def staple_ffn_down_packed(h: torch.Tensor, packed_down: torch.Tensor, y: torch.
     return y
 
 
-def staple_ffn_gate_up(x: torch.Tensor, w_gate: torch.Tensor, w_up: torch.Tensor,
+def staple_ffn_gate_up(x: torch.Tensor, w_gate: torch.Tensor, w_up: Optional[torch.Tensor],
                        rows: torch.Tensor, row_index: torch.Tensor, h: torch.Tensor,
                        save_g: Optional[torch.Tensor] = None, save_u: Optional[torch.Tensor] = None,
                        stream=None) -> torch.Tensor:
-    """h = silu(x W_gate^T) * (x W_up^T + rows[row_index]) (fused gather epilogue)."""
+    """h = silu(x W_gate^T) * (x W_up^T + rows[row_index]) (fused gather epilogue);
+    w_up None: h = silu(x W_gate^T) * rows[row_index] (the STEM layer)."""
     _dev(x, w_gate, w_up, rows, row_index, h, save_g, save_u)
     n, d = x.shape
     f = w_gate.shape[0]
@@ -342,8 +359,8 @@ def staple_ffn_gate_up(x: torch.Tensor, w_gate: torch.Tensor, w_up: torch.Tensor
 
 
 def staple_ffn_gate_up_tokens(token_pos: torch.Tensor, n_sel: int, x: torch.Tensor,
-                              w_gate: torch.Tensor, w_up: torch.Tensor, rows: torch.Tensor,
-                              row_index: torch.Tensor, h: torch.Tensor,
+                              w_gate: torch.Tensor, w_up: Optional[torch.Tensor],
+                              rows: torch.Tensor, row_index: torch.Tensor, h: torch.Tensor,
                               save_g: Optional[torch.Tensor] = None,
                               save_u: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
     """staple_ffn_gate_up for the tokens token_pos[:n_sel] only (rows of x, h, g, u)."""
@@ -410,14 +427,16 @@ def staple_cache_refresh(table: torch.Tensor, uniq: torch.Tensor, code: torch.Te
 
 
 def staple_ffn_bwd_table_grad(dy: torch.Tensor, x: torch.Tensor, w_gate: torch.Tensor,
-                              w_up: torch.Tensor, w_down: torch.Tensor, saved_g: torch.Tensor,
+                              w_up: Optional[torch.Tensor], w_down: torch.Tensor,
+                              saved_g: torch.Tensor,
                               saved_u: torch.Tensor, saved_h: torch.Tensor,
                               sorted_pos: torch.Tensor, seg_start: torch.Tensor,
                               n_unique: torch.Tensor, *, max_unique: Optional[int] = None,
                               freeze_up: bool = False, out_dtype: Optional[torch.dtype] = None,
                               out: Optional[dict] = None, workspace: Optional[torch.Tensor] = None,
                               stream=None) -> dict:
-    """Backward with the table-row gradient: d_rows, dx, dw_gate, dw_up, dw_down."""
+    """Backward with the table-row gradient: d_rows, dx, dw_gate, dw_up, dw_down
+    (w_up None: the STEM layer, no dw_up)."""
     _dev(dy, x, w_gate, w_up, w_down, saved_g, saved_u, saved_h, sorted_pos, seg_start, n_unique)
     n, d = x.shape
     f = w_gate.shape[0]
@@ -429,7 +448,8 @@ def staple_ffn_bwd_table_grad(dy: torch.Tensor, x: torch.Tensor, w_gate: torch.T
             "d_rows": torch.empty(max(mu, 1), f, dtype=torch.float32, device=dev),
             "dx": torch.empty(n, d, dtype=out_dtype or x.dtype, device=dev),
             "dw_gate": torch.empty(f, d, dtype=torch.float32, device=dev),
-            "dw_up": None if freeze_up else torch.empty(f, d, dtype=torch.float32, device=dev),
+            "dw_up": None if freeze_up or w_up is None
+            else torch.empty(f, d, dtype=torch.float32, device=dev),
             "dw_down": torch.empty(d, f, dtype=torch.float32, device=dev),
         }
     ws = _ws(lib().staple_ffn_bwd_workspace_bytes(n, d, f, dt), workspace, dev)

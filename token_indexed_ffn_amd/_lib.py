@@ -48,12 +48,13 @@ _SIGS = {
     "staple_ffn_down": (c_i32, [c_i64, c_i64, c_i64, c_i32, c_i32, c_vp, c_vp, c_vp, c_vp, c_sz,
                                 c_vp]),
     "staple_decode_pack_weights": (c_i32, [c_i64, c_i64, c_i32, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp]),
-    "staple_ffn_gate_up_packed": (c_i32, [c_i64, c_i64, c_i64, c_i32, c_vp, c_vp, c_vp, c_i64,
-                                          c_vp, c_vp, c_vp, c_vp, c_vp]),
+    "staple_ffn_gate_up_packed": (c_i32, [c_i64, c_i64, c_i64, c_i32, c_vp, c_vp, c_i32, c_vp,
+                                          c_i64, c_vp, c_vp, c_vp, c_vp, c_vp]),
     "staple_ffn_down_packed": (c_i32, [c_i64, c_i64, c_i64, c_i32, c_i32, c_vp, c_vp, c_vp, c_vp,
                                        c_sz, c_vp]),
-    "staple_ffn_fwd_packed": (c_i32, [c_i64, c_i64, c_i64, c_i32, c_i32, c_vp, c_vp, c_vp, c_vp,
-                                      c_i64, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_sz, c_vp]),
+    "staple_ffn_fwd_packed": (c_i32, [c_i64, c_i64, c_i64, c_i32, c_i32, c_vp, c_vp, c_i32, c_vp,
+                                      c_vp, c_i64, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_sz,
+                                      c_vp]),
     "staple_adamw_rows": (c_i32, [c_vp, c_vp, c_vp, c_i64, c_i64, c_i32, c_vp, c_vp, c_i64, c_vp,
                                   c_f32, c_f32, c_f32, c_f32, c_f32, c_i64, c_vp]),
     "staple_adamw_rows_host": (c_i32, [c_vp, c_vp, c_vp, c_i64, c_i64, c_i32, c_vp, c_i64, c_vp,

@@ -77,7 +77,7 @@ size_t decode_down_workspace_bytes(int64_t n, int64_t d);
 hipError_t decode_gateup(int64_t n, const int32_t* pos, int64_t n_tokens, int64_t d, int64_t f,
                          const void* x, const void* wg, const void* wu, const void* rows,
                          int64_t n_rows, const int32_t* row_index, void* h, void* g_out,
-                         void* u_out, hipStream_t s, int* err, bool packed);
+                         void* u_out, hipStream_t s, int* err, bool packed, bool up);
 hipError_t decode_down(int64_t n, int64_t d, int64_t f, const void* h, const void* wd, void* y,
                        int out_dtype, void* ws, hipStream_t s, bool packed);
 hipError_t decode_pack(int64_t d, int64_t f, const void* wg, const void* wu, const void* wd,
@@ -393,7 +393,7 @@ static staple_status_t gate_up_impl(int64_t n_sel, const int32_t* pos, int64_t n
   GET_ERR(err);
   if (decode_eligible(n_sel, d, f, dtype))
     HIPCALL(decode_gateup(n_sel, pos, n_tokens, d, f, x, w_gate, w_up, rows, n_rows, row_index, h,
-                          save_g, save_u, s, err, false));
+                          save_g, save_u, s, err, false, w_up != nullptr));
   else if (dtype == STAPLE_BF16)
     HIPCALL(gateup_fwd<bf16_t>(n_sel, pos, n_tokens, d, f, x, w_gate, w_up, rows, n_rows,
                                row_index, h, save_g, save_u, s, err));
@@ -417,8 +417,8 @@ staple_status_t staple_ffn_gate_up(int64_t n, int64_t d, int64_t f, int32_t dtyp
                                    int64_t n_rows, const int32_t* row_index, void* h,
                                    void* save_g, void* save_u, void* stream) {
   if (!ffn_shape_ok(n, d, f, dtype)) return STAPLE_ERR_UNSUPPORTED;
-  REQUIRE(w_gate && w_up && rows && n_rows >= 1);
-  REQUIRE(aligned16(w_gate) && aligned16(w_up) && aligned16(rows));
+  REQUIRE(w_gate && rows && n_rows >= 1);
+  REQUIRE(aligned16(w_gate) && (!w_up || aligned16(w_up)) && aligned16(rows));
   if (n == 0) return STAPLE_OK;
   REQUIRE(x && row_index && h && aligned16(x) && aligned16(h));
   REQUIRE((!save_g || aligned16(save_g)) && (!save_u || aligned16(save_u)));
@@ -433,8 +433,8 @@ staple_status_t staple_ffn_gate_up_tokens(int64_t n_sel, const int32_t* token_po
                                           void* save_g, void* save_u, void* stream) {
   if (!ffn_shape_ok(n_tokens, d, f, dtype)) return STAPLE_ERR_UNSUPPORTED;
   REQUIRE(n_sel >= 0 && n_sel <= n_tokens);
-  REQUIRE(w_gate && w_up && rows && n_rows >= 1);
-  REQUIRE(aligned16(w_gate) && aligned16(w_up) && aligned16(rows));
+  REQUIRE(w_gate && rows && n_rows >= 1);
+  REQUIRE(aligned16(w_gate) && (!w_up || aligned16(w_up)) && aligned16(rows));
   if (n_sel == 0) return STAPLE_OK;
   REQUIRE(token_pos && x && row_index && h && aligned16(x) && aligned16(h));
   REQUIRE((!save_g || aligned16(save_g)) && (!save_u || aligned16(save_u)));
@@ -462,8 +462,8 @@ staple_status_t staple_ffn_fwd(int64_t n, int64_t d, int64_t f, int32_t dtype, i
                                void* save_h, void* ws, size_t ws_bytes, void* stream) {
   if (!valid_dtype(dtype) || !valid_dtype(out_dtype)) return STAPLE_ERR_UNSUPPORTED;
   if (!ffn_shape_ok(n, d, f, dtype)) return STAPLE_ERR_UNSUPPORTED;
-  REQUIRE(w_gate && w_up && w_down && rows && n_rows >= 1);
-  REQUIRE(aligned16(w_gate) && aligned16(w_up) && aligned16(w_down) && aligned16(rows));
+  REQUIRE(w_gate && w_down && rows && n_rows >= 1);
+  REQUIRE(aligned16(w_gate) && (!w_up || aligned16(w_up)) && aligned16(w_down) && aligned16(rows));
   if (n == 0) return STAPLE_OK;
   REQUIRE(x && row_index && y && aligned16(x) && aligned16(y));
   REQUIRE((!save_g || aligned16(save_g)) && (!save_u || aligned16(save_u)) &&
@@ -484,7 +484,7 @@ staple_status_t staple_decode_pack_weights(int64_t d, int64_t f, int32_t dtype, 
                                            void* packed_gate_up, void* packed_down, void* stream) {
   if (dtype != STAPLE_BF16 || !ffn_shape_ok(1, d, f, dtype)) return STAPLE_ERR_UNSUPPORTED;
   REQUIRE(packed_gate_up || packed_down);
-  REQUIRE(!packed_gate_up || (w_gate && w_up && aligned16(w_gate) && aligned16(w_up) &&
+  REQUIRE(!packed_gate_up || (w_gate && aligned16(w_gate) && (!w_up || aligned16(w_up)) &&
                               aligned16(packed_gate_up)));
   REQUIRE(!packed_down || (w_down && aligned16(w_down) && aligned16(packed_down)));
   HIPCALL(decode_pack(d, f, w_gate, w_up, w_down, packed_gate_up, packed_down, S(stream)));
@@ -493,7 +493,7 @@ staple_status_t staple_decode_pack_weights(int64_t d, int64_t f, int32_t dtype, 
 
 staple_status_t staple_ffn_gate_up_packed(int64_t n, int64_t d, int64_t f, int32_t dtype,
                                           const void* x, const void* packed_gate_up,
-                                          const void* rows, int64_t n_rows,
+                                          int32_t up_proj, const void* rows, int64_t n_rows,
                                           const int32_t* row_index, void* h, void* save_g,
                                           void* save_u, void* stream) {
   if (dtype != STAPLE_BF16 || !ffn_shape_ok(n, d, f, dtype)) return STAPLE_ERR_UNSUPPORTED;
@@ -505,7 +505,7 @@ staple_status_t staple_ffn_gate_up_packed(int64_t n, int64_t d, int64_t f, int32
   REQUIRE((!save_g || aligned16(save_g)) && (!save_u || aligned16(save_u)));
   GET_ERR(err);
   HIPCALL(decode_gateup(n, nullptr, n, d, f, x, packed_gate_up, nullptr, rows, n_rows, row_index, h,
-                        save_g, save_u, S(stream), err, true));
+                        save_g, save_u, S(stream), err, true, up_proj != 0));
   return STAPLE_OK;
 }
 
@@ -526,8 +526,8 @@ staple_status_t staple_ffn_down_packed(int64_t n, int64_t d, int64_t f, int32_t 
 
 staple_status_t staple_ffn_fwd_packed(int64_t n, int64_t d, int64_t f, int32_t dtype,
                                       int32_t out_dtype, const void* x,
-                                      const void* packed_gate_up, const void* packed_down,
-                                      const void* rows, int64_t n_rows,
+                                      const void* packed_gate_up, int32_t up_proj,
+                                      const void* packed_down, const void* rows, int64_t n_rows,
                                       const int32_t* row_index, void* y, void* save_g,
                                       void* save_u, void* save_h, void* ws, size_t ws_bytes,
                                       void* stream) {
@@ -547,7 +547,7 @@ staple_status_t staple_ffn_fwd_packed(int64_t n, int64_t d, int64_t f, int32_t d
   hipStream_t s = S(stream);
   GET_ERR(err);
   HIPCALL(decode_gateup(n, nullptr, n, d, f, x, packed_gate_up, nullptr, rows, n_rows, row_index, h,
-                        save_g, save_u, s, err, true));
+                        save_g, save_u, s, err, true, up_proj != 0));
   HIPCALL(decode_down(n, d, f, h, packed_down, y, out_dtype, down_ws, s, true));
   return STAPLE_OK;
 }
@@ -630,10 +630,12 @@ staple_status_t staple_ffn_bwd_table_grad(
     float* dw_up, float* dw_down, int32_t freeze_up, void* ws, size_t ws_bytes, void* stream) {
   if (!valid_dtype(dtype) || !valid_dtype(out_dtype)) return STAPLE_ERR_UNSUPPORTED;
   if (!ffn_shape_ok(n, d, f, dtype)) return STAPLE_ERR_UNSUPPORTED;
-  REQUIRE(w_gate && w_up && w_down && dw_gate && dw_down && (freeze_up || dw_up));
+  // w_up null: the STEM layer (no up-projection, so no dw_up either)
+  const bool fz = freeze_up != 0 || !w_up;
+  REQUIRE(w_gate && w_down && dw_gate && dw_down && (fz || dw_up));
   REQUIRE(seg_start && n_unique && max_unique >= 0 && max_unique <= n);
-  REQUIRE(aligned16(w_gate) && aligned16(w_up) && aligned16(w_down) && aligned16(dw_gate) &&
-          aligned16(dw_down) && (freeze_up || aligned16(dw_up)));
+  REQUIRE(aligned16(w_gate) && (!w_up || aligned16(w_up)) && aligned16(w_down) &&
+          aligned16(dw_gate) && aligned16(dw_down) && (fz || aligned16(dw_up)));
   if (n > 0) {
     REQUIRE(dy && x && saved_g && saved_u && saved_h && sorted_pos && d_rows && dx);
     REQUIRE(aligned16(dy) && aligned16(x) && aligned16(saved_g) && aligned16(saved_u) &&
@@ -645,7 +647,6 @@ staple_status_t staple_ffn_bwd_table_grad(
   hipStream_t s = S(stream);
   void* dgu = ws;
   void* seg_ws = n > 0 ? static_cast<char*>(ws) + bwd_dgu_bytes(n, f, dtype) : nullptr;
-  const bool fz = freeze_up != 0;
   if (dtype == STAPLE_BF16) {
     HIPCALL(dh_act<bf16_t>(n, d, f, dy, w_down, saved_g, saved_u, dgu, s));
     if (n > 0)

@@ -20,6 +20,9 @@
 // and h = silu(W_gate x) * u (STAPLE abstract: the up-projection is retained
 // and the embedding added as a residual path; retrieval-path table: row
 // reconstruction fused with the FFN) and stores h with 16-byte vectors.
+// The STEM layer, which has no up-projection (the table row replaces it,
+// STAPLE abstract and Table 4's STEM row), runs the same kernel on W_gate
+// alone: a wave owns the gate rows of 16 features and u = E[t].
 //
 // Down: d_model is too narrow to fill 256 CUs with whole-K tiles, so the K
 // range (d_ff) is split over several workgroups per output block; each writes
@@ -237,16 +240,18 @@ __device__ __forceinline__ bool fold_parts(WaveRole role, float (*stage)[16 * kS
 }
 
 // Gate/up for at most 64 tokens, features split over the waves: one
-// workgroup (G KH compute waves and KH activation loaders) per 8 G features;
-// compute wave w owns the gate and up rows of features 8 (w % G) .. +8 of the
-// workgroup (one 16-row MFMA block: 8 gate rows, then 8 up rows) over part
-// w / G of d_model, and the KH parts are folded in LDS.  Row groups past f
-// (in the last workgroup when f / 8 is not a multiple of G) stream nothing
-// and store nothing.
+// workgroup (G KH compute waves and KH activation loaders) per FG G features;
+// compute wave w owns one 16-row MFMA block over part w / G of d_model, and
+// the KH parts are folded in LDS.  With UP (the STAPLE layer, FG = 8) the
+// block is the gate rows then the up rows of features 8 (w % G) .. +8 of the
+// workgroup; without (the STEM layer, FG = 16) it is the gate rows of
+// features 16 (w % G) .. +16 and u is the table row.  Row groups past f (in
+// the last workgroup when f / FG is not a multiple of G) stream nothing and
+// store nothing.
 // With `pos`, the n tokens of the launch are pos[0 .. n) of the n_tokens rows
 // of x, h, g, u and row_index (out-of-range positions set the error word and
 // are neither read nor written).
-template <int WD, int A, int G, int KH, bool PACKED>
+template <int WD, int A, int G, int KH, bool PACKED, bool UP>
 __global__ __launch_bounds__(64 * (G + 1) * KH) void decode_gateup_kernel(
     int n, const int32_t* __restrict__ pos, int64_t n_tokens, int64_t d, int64_t f,
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ wg,
@@ -259,15 +264,16 @@ __global__ __launch_bounds__(64 * (G + 1) * KH) void decode_gateup_kernel(
   const WaveRole role = wave_role<G, KH>();
   const int grp = role.grp, part = role.part;
   const int r = lane & 15, q = lane >> 4;
+  constexpr int FG = UP ? 8 : 16;                                   // features per row group
   const int64_t rb = static_cast<int64_t>(blockIdx.x) * G + grp;   // this wave's row group
-  const bool active = rb < f / 8;
+  const bool active = rb < f / FG;
   const int64_t rbc = active ? rb : 0;                              // valid memory for the rest
-  const int64_t f0 = rbc * 8;                                       // this wave's features
-  // PACKED: wg is the packed gate/up block (row block = 8 features)
-  const char* pa =
-      PACKED ? reinterpret_cast<const char*>(wg) + rbc * 2048 + lane * 16
-             : reinterpret_cast<const char*>(r < 8 ? wg + (f0 + r) * d : wu + (f0 + r - 8) * d) + q * 16;
-  const int64_t wstep = PACKED ? (f / 8) * 2048 : 128;
+  const int64_t f0 = rbc * FG;                                      // this wave's features
+  // PACKED: wg is the packed gate/up (or gate) block of this row group
+  const uint16_t* wrow = !UP ? wg + (f0 + r) * d : r < 8 ? wg + (f0 + r) * d : wu + (f0 + r - 8) * d;
+  const char* pa = PACKED ? reinterpret_cast<const char*>(wg) + rbc * 2048 + lane * 16
+                          : reinterpret_cast<const char*>(wrow) + q * 16;
+  const int64_t wstep = PACKED ? (f / FG) * 2048 : 128;
   const int64_t T = d / 64, len = (T + KH - 1) / KH;
   const int64_t s0 = part * len < T ? part * len : T, s1 = s0 + len < T ? s0 + len : T;
   f32x4_t acc[4];
@@ -286,16 +292,18 @@ __global__ __launch_bounds__(64 * (G + 1) * KH) void decode_gateup_kernel(
   // once the stream is under way
   int64_t ri;
   bool erow_ok;
-  uint4 erow;
+  uint4 erow[FG / 8];
   stream_act_ring<WD, A, KH, PACKED ? 1024 : 64>(role, active, pa, wstep, x, d, act_row, n,
                                                   (lds_char*)(xs), s0, s1, len, acc, [&]() {
     ri = row_index[tok < 0 ? 0 : tok];
     erow_ok = ri >= 0 && ri < n_rows;
-    erow = *reinterpret_cast<const uint4*>(erow_ok ? rows + ri * f + f0 : x);
+#pragma unroll
+    for (int c = 0; c < FG / 8; ++c)
+      erow[c] = *reinterpret_cast<const uint4*>(erow_ok ? rows + ri * f + f0 + 8 * c : x);
   });
 
-  // epilogue: rows 0-7 (gate) and 8-15 (up) of the row group's block, staged
-  // so that lane t holds its token's 8 gate and 8 up sums
+  // epilogue: the row group's block staged so that lane t holds its token's
+  // 16 sums (UP: 8 gate then 8 up; STEM: 16 gate)
   if (!fold_parts<KH>(role, stage, acc) || !active) return;
   const float* st = stage[grp];
   const int t = lane;
@@ -304,30 +312,29 @@ __global__ __launch_bounds__(64 * (G + 1) * KH) void decode_gateup_kernel(
     flag_index_error(err);
     return;
   }
-  float gv[8], uv[8], hv[8], ev[8];
-#pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    gv[e] = st[e * kStageLd + t];
-    uv[e] = st[(8 + e) * kStageLd + t];
-  }
+  float gv[FG], uv[FG], hv[FG], ev[FG];
   if (erow_ok) {
-    const uint32_t wds[4] = {erow.x, erow.y, erow.z, erow.w};
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      ev[2 * i] = __uint_as_float(wds[i] << 16);
-      ev[2 * i + 1] = __uint_as_float(wds[i] & 0xffff0000u);
+    for (int c = 0; c < FG / 8; ++c) {
+      const uint32_t wds[4] = {erow[c].x, erow[c].y, erow[c].z, erow[c].w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        ev[8 * c + 2 * i] = __uint_as_float(wds[i] << 16);
+        ev[8 * c + 2 * i + 1] = __uint_as_float(wds[i] & 0xffff0000u);
+      }
     }
   } else {
     flag_index_error(err);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) ev[i] = 0.0f;
+    for (int i = 0; i < FG; ++i) ev[i] = 0.0f;
   }
 #pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    uv[e] += ev[e];
+  for (int e = 0; e < FG; ++e) {
+    gv[e] = st[e * kStageLd + t];
+    uv[e] = UP ? st[(8 + e) * kStageLd + t] + ev[e] : ev[e];
     hv[e] = gv[e] * sigmoidf_(gv[e]) * uv[e];
   }
-  auto pack = [](const float (&v)[8]) {
+  auto pack = [](const float* v) {
     uint4 o;
     o.x = static_cast<uint32_t>(f32_to_bf16(v[0])) | (static_cast<uint32_t>(f32_to_bf16(v[1])) << 16);
     o.y = static_cast<uint32_t>(f32_to_bf16(v[2])) | (static_cast<uint32_t>(f32_to_bf16(v[3])) << 16);
@@ -336,9 +343,12 @@ __global__ __launch_bounds__(64 * (G + 1) * KH) void decode_gateup_kernel(
     return o;
   };
   const int64_t o = tok * f + f0;
-  *reinterpret_cast<uint4*>(h + o) = pack(hv);
-  if (g_out) *reinterpret_cast<uint4*>(g_out + o) = pack(gv);
-  if (u_out) *reinterpret_cast<uint4*>(u_out + o) = pack(uv);
+#pragma unroll
+  for (int c = 0; c < FG / 8; ++c) {
+    *reinterpret_cast<uint4*>(h + o + 8 * c) = pack(hv + 8 * c);
+    if (g_out) *reinterpret_cast<uint4*>(g_out + o + 8 * c) = pack(gv + 8 * c);
+    if (u_out) *reinterpret_cast<uint4*>(u_out + o + 8 * c) = pack(uv + 8 * c);
+  }
 }
 
 // Down projection for at most 64 tokens, d_ff split KS ways over workgroups
@@ -420,7 +430,8 @@ __global__ void decode_down_reduce_kernel(int64_t count, int ksplit, const float
 // holds bytes [128 s + 64 j + 16 (lane / 16), +16) of block row lane % 16.
 // A gate/up row block is features 8 rb .. 8 rb + 8: its rows 0-7 are those
 // rows of W_gate and rows 8-15 those of W_up; a down row block is rows
-// 16 rb .. 16 rb + 16 of W_down.  Step-major order over all row blocks puts
+// 16 rb .. 16 rb + 16 of W_down, and a gate-only block (the STEM layer) rows
+// 16 rb .. 16 rb + 16 of W_gate.  Step-major order over all row blocks puts
 // what the whole grid reads at one step side by side in HBM, and every load
 // instruction of the decode kernels reads 1 KB of contiguous memory.
 __global__ void decode_pack_kernel(int64_t total, int64_t rb_count, int64_t k, bool gate_up,
@@ -471,7 +482,10 @@ hipError_t decode_pack(int64_t d, int64_t f, const void* wg, const void* wu, con
         total, rbs, k, gu, static_cast<const uint16_t*>(a), static_cast<const uint16_t*>(b),
         static_cast<uint4*>(out));
   };
-  if (packed_gu) go(f / 8, d, true, wg, wu, packed_gu);
+  if (packed_gu) {
+    if (wu) go(f / 8, d, true, wg, wu, packed_gu);
+    else go(f / 16, d, false, wg, nullptr, packed_gu);   // gate-only blocks
+  }
   if (packed_down) go(d / 16, f, false, wd, nullptr, packed_down);
   return hipGetLastError();
 }
@@ -491,17 +505,26 @@ static int device_cus() {
   return v;
 }
 
+// `up`: the weights hold W_up (the STAPLE layer; row-major: wu, packed: the
+// interleaved blocks) or not (the STEM layer: W_gate alone, u = E[t]).
 hipError_t decode_gateup(int64_t n, const int32_t* pos, int64_t n_tokens, int64_t d, int64_t f,
                          const void* x, const void* wg, const void* wu, const void* rows,
                          int64_t n_rows, const int32_t* row_index, void* h, void* g_out,
-                         void* u_out, hipStream_t s, int* err, bool packed) {
-  // 4 row groups (32 features) per workgroup, on two K parts, while that fits
-  // one workgroup per CU; else 6 row groups on one part (d_ff 11008: 230
-  // workgroups of 7 waves instead of 344 of 10 on 256 CUs whose LDS holds one
-  // 10-wave workgroup each: 32 us instead of 44 per launch at d_model 4096)
-  const int64_t groups = f / 8;
-  const bool wide = groups > 4LL * device_cus();
-  const unsigned grid = static_cast<unsigned>(wide ? (groups + 5) / 6 : groups / 4);
+                         void* u_out, hipStream_t s, int* err, bool packed, bool up) {
+  // STAPLE: 4 row groups (32 features) per workgroup, on two K parts, while
+  // that fits one workgroup per CU; else 6 row groups on one part (d_ff
+  // 11008: 230 workgroups of 7 waves instead of 344 of 10 on 256 CUs whose
+  // LDS holds one 10-wave workgroup each: 32 us instead of 44 per launch at
+  // d_model 4096).
+  // STEM (16-feature row groups, half the bytes per feature): as many row
+  // groups per workgroup as make about one workgroup per CU, 2, 3 or 4 on two
+  // K parts, else 6 on one.
+  const int64_t groups = up ? f / 8 : f / 16;
+  const int64_t cus = device_cus();
+  const bool wide = groups > 4 * cus;
+  const int per = up ? (wide ? 6 : 4)
+                     : (groups <= 2 * cus ? 2 : groups <= 3 * cus ? 3 : wide ? 6 : 4);
+  const unsigned grid = static_cast<unsigned>((groups + per - 1) / per);
   auto go = [&](auto kern, int threads) {
     kern<<<dim3(grid), dim3(threads), 0, s>>>(
         static_cast<int>(n), pos, n_tokens, d, f, static_cast<const uint16_t*>(x),
@@ -509,13 +532,20 @@ hipError_t decode_gateup(int64_t n, const int32_t* pos, int64_t n_tokens, int64_
         static_cast<const uint16_t*>(wu), static_cast<const uint16_t*>(rows), n_rows, row_index,
         static_cast<uint16_t*>(h), static_cast<uint16_t*>(g_out), static_cast<uint16_t*>(u_out), err);
   };
-  auto pick = [&](auto packed_tag) {
-    constexpr bool P = decltype(packed_tag)::value;
-    if (wide) go(decode_gateup_kernel<kGateUpAhead, kGateUpActAhead, 6, 1, P>, 64 * 7);
-    else go(decode_gateup_kernel<kGateUpAhead, kGateUpActAhead, 4, kGateUpParts, P>, 64 * 5 * kGateUpParts);
+  auto pick = [&](auto packed_tag, auto up_tag) {
+    constexpr bool P = decltype(packed_tag)::value, U = decltype(up_tag)::value;
+    constexpr int WD = kGateUpAhead, A = kGateUpActAhead, KH = kGateUpParts;
+    if (per == 6) go(decode_gateup_kernel<WD, A, 6, 1, P, U>, 64 * 7);
+    else if (per == 4) go(decode_gateup_kernel<WD, A, 4, KH, P, U>, 64 * 5 * KH);
+    else if constexpr (!U) {
+      if (per == 3) go(decode_gateup_kernel<WD, A, 3, KH, P, U>, 64 * 4 * KH);
+      else go(decode_gateup_kernel<WD, A, 2, KH, P, U>, 64 * 3 * KH);
+    }
   };
-  if (packed) pick(std::true_type{});
-  else pick(std::false_type{});
+  if (packed && up) pick(std::true_type{}, std::true_type{});
+  else if (packed) pick(std::true_type{}, std::false_type{});
+  else if (up) pick(std::false_type{}, std::true_type{});
+  else pick(std::false_type{}, std::false_type{});
   return hipGetLastError();
 }
 

@@ -24,6 +24,10 @@
 //             h = silu(g) * u (STAPLE abstract: the up-projection is kept and
 //             the embedding added as a residual path) and stores h (and g, u
 //             for the backward when requested).
+//   GateStem- C is g = W_gate x alone (the STEM layer, which has no
+//             up-projection: the token's table row takes its place, STAPLE
+//             abstract and Table 1); the epilogue reads the table row e and
+//             stores h = silu(g) * e (and g, u = e when requested).
 //   DhAct   - C is dh = dy W_down; the epilogue reads saved g, u and writes
 //             dg = dh * u * silu'(g) and du = dh * silu(g) side by side.
 #include <type_traits>
@@ -32,7 +36,7 @@
 
 namespace staple {
 
-enum EpiKind { kEpiStore = 0, kEpiGateUp = 1, kEpiDhAct = 2 };
+enum EpiKind { kEpiStore = 0, kEpiGateUp = 1, kEpiDhAct = 2, kEpiGateStem = 3 };
 
 struct GemmArgs {
   int64_t M, N, K;
@@ -59,7 +63,7 @@ struct GemmArgs {
   void* c1;
   int64_t ldc;
   int64_t c_split;
-  // GateUp
+  // GateUp, GateStem (GateStem: B is W_gate alone, N = d_ff)
   const void* rows;
   const int32_t* row_index;
   int64_t n_rows;
@@ -693,6 +697,51 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(GemmArgs p) {
           if (p.u_out) store8g<T>(p.u_out, o, u);
         }
       }
+    } else if constexpr (EPI == kEpiGateStem) {
+      // C = g (M = tokens, N = d_ff).  The table rows of all of this lane's
+      // chunks are fetched first, then h, g, u are formed and stored.
+      const int64_t f = p.d_ff;
+      constexpr int kPerLane = (kChunks + 63) / 64;
+      int64_t ri[kPerLane], tokq[kPerLane];
+      float e[kPerLane][8];
+#pragma unroll
+      for (int c = 0; c < kPerLane; ++c) {
+        const int q = lane + 64 * c;
+        const int64_t m = mrow0 + q / (WN / 8);
+        const int64_t mm = m < p.M ? m : p.M - 1;
+        tokq[c] = p.a_rows ? static_cast<int64_t>(p.a_rows[mm]) : mm;
+        if (tokq[c] < 0 || tokq[c] >= p.a_rows_bound) tokq[c] = -1;   // flagged in the prologue
+        ri[c] = p.row_index[tokq[c] < 0 ? 0 : tokq[c]];
+      }
+#pragma unroll
+      for (int c = 0; c < kPerLane; ++c) {
+        const int q = lane + 64 * c;
+        const int64_t n = n0 + wn * WN + (q % (WN / 8)) * 8;
+        const bool ok = q < kChunks && ri[c] >= 0 && ri[c] < p.n_rows && n < f;
+        load8g<T>(p.rows, ok ? ri[c] * f + n : 0, e[c]);
+      }
+#pragma unroll
+      for (int c = 0; c < kPerLane; ++c) {
+        const int q = lane + 64 * c;
+        const int rr = q / (WN / 8), cc = (q % (WN / 8)) * 8;
+        const int64_t m = mrow0 + rr;
+        const int64_t n = n0 + wn * WN + cc;
+        if (q < kChunks && m < p.M && n < f && tokq[c] >= 0) {
+          float g[8], h[8];
+          read8(region + rr * LD + cc, g);
+          if (!(ri[c] >= 0 && ri[c] < p.n_rows)) {
+            flag_index_error(p.err);
+#pragma unroll
+            for (int k = 0; k < 8; ++k) e[c][k] = 0.0f;
+          }
+#pragma unroll
+          for (int k = 0; k < 8; ++k) h[k] = g[k] * sigmoidf_(g[k]) * e[c][k];
+          const int64_t o = tokq[c] * f + n;
+          store8g<T>(p.h_out, o, h);
+          if (p.g_out) store8g<T>(p.g_out, o, g);
+          if (p.u_out) store8g<T>(p.u_out, o, e[c]);
+        }
+      }
     } else {  // kEpiDhAct: C = dh (M = tokens, N = d_ff)
       // g and u of all of this lane's chunks are loaded first, then dg, du
       // are formed and stored
@@ -776,8 +825,9 @@ static GemmArgs blank() {
 }
 
 // h = silu(x W_gate^T) * (x W_up^T + rows[row_index]); optional saves of g, u.
-// With `pos`, only the n_sel tokens pos[0 .. n_sel) of the n_tokens are
-// computed (their rows of x, h, g, u; row_index stays indexed by token).
+// With wu null (the STEM layer) u = rows[row_index] and the GEMM is W_gate's
+// alone.  With `pos`, only the n_sel tokens pos[0 .. n_sel) of the n_tokens
+// are computed (their rows of x, h, g, u; row_index stays indexed by token).
 template <typename T>
 hipError_t gateup_fwd(int64_t n_sel, const int32_t* pos, int64_t n_tokens, int64_t d, int64_t f,
                       const void* x, const void* wg, const void* wu, const void* rows,
@@ -790,6 +840,10 @@ hipError_t gateup_fwd(int64_t n_sel, const int32_t* pos, int64_t n_tokens, int64
   a.b0 = wg; a.b1 = wu; a.ldb = d;
   a.rows = rows; a.row_index = row_index; a.n_rows = n_rows; a.d_ff = f;
   a.h_out = h; a.g_out = g_out; a.u_out = u_out; a.err = err;
+  if (!wu) {
+    a.N = f;
+    return run<T, true, true, kEpiGateStem, T>(a, s);
+  }
   return run<T, true, true, kEpiGateUp, T>(a, s);
 }
 
@@ -818,12 +872,13 @@ hipError_t dh_act(int64_t n, int64_t d, int64_t f, const void* dy, const void* w
   return run<T, true, false, kEpiDhAct, T>(a, s);
 }
 
-// dx = dg W_gate + du W_up  (K = 2f over the concatenated [dg | du])
+// dx = dg W_gate + du W_up  (K = 2f over the concatenated [dg | du]); with wu
+// null (STEM) dx = dg W_gate (K = f, the dg half of each row)
 template <typename T>
 hipError_t dx_bwd(int64_t n, int64_t d, int64_t f, const void* dgu, const void* wg,
                   const void* wu, void* dx, int out_dtype, hipStream_t s) {
   GemmArgs a = blank<T>();
-  a.M = n; a.N = d; a.K = 2 * f;
+  a.M = n; a.N = d; a.K = wu ? 2 * f : f;
   a.a0 = dgu; a.lda = 2 * f;
   a.b0 = wg; a.b1 = wu; a.ldb = d; a.b_split = f;
   a.c0 = dx; a.ldc = d;
