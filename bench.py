@@ -44,7 +44,7 @@ def parse_args(argv=None):
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--train-steps", type=int, default=10)
     ap.add_argument("--train-warmup", type=int, default=3)
-    ap.add_argument("--workloads", default="decode,train")
+    ap.add_argument("--workloads", default="decode,train,stem")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=8.0,
                     help="target CPU time of each oracle baseline sample")
@@ -89,7 +89,8 @@ def oracle_threads() -> int:
 # ----------------------------------------------------------------------------
 # Decode: 12 layers, batch 64, full tables in HBM
 # ----------------------------------------------------------------------------
-def setup_decode(torch, st, w):
+def setup_decode(torch, st, w, stem=False):
+    """stem: the STEM layer (no up-projection, u = E[t]) instead of STAPLE's."""
     from staple_synth import device_normal
     dev = torch.device("cuda:0")
     L, n, d, f, v = w.n_layers, w.n_tokens, w.d_model, w.d_ff, w.vocab
@@ -100,7 +101,7 @@ def setup_decode(torch, st, w):
         layers.append({
             "x": device_normal((n, d), w.x_std, s["x"], torch.bfloat16, dev),
             "w_gate": device_normal((f, d), w.w_std, s["w_gate"], torch.bfloat16, dev),
-            "w_up": device_normal((f, d), w.w_std, s["w_up"], torch.bfloat16, dev),
+            "w_up": None if stem else device_normal((f, d), w.w_std, s["w_up"], torch.bfloat16, dev),
             "w_down": device_normal((d, f), w.w_std, s["w_down"], torch.bfloat16, dev),
             "table": device_normal((v, f), w.table_std, s["table"], torch.bfloat16, dev),
             "y": torch.empty(n, d, dtype=torch.bfloat16, device=dev),
@@ -132,9 +133,9 @@ def decode_step_row_major(st, D):
                           out={"y": lay["y"]}, workspace=D["fwd_ws"])
 
 
-def run_decode(torch, st, w, steps, warmup):
+def run_decode(torch, st, w, steps, warmup, stem=False):
     import numpy as np
-    D = setup_decode(torch, st, w)
+    D = setup_decode(torch, st, w, stem)
     n, d, f = w.n_tokens, w.d_model, w.d_ff
     n_unique = int(len(np.unique(D["ids_np"])))
     for _ in range(3):
@@ -209,7 +210,8 @@ def run_decode(torch, st, w, steps, warmup):
     torch.cuda.synchronize()
     gu_us = e0.elapsed_time(e1) / (reps * w.n_layers) * 1e3
 
-    gu_bytes = (2 * d * f + n * d + n_unique * f + n * f) * 2      # W_gate, W_up, x, rows, h
+    n_w = 1 if stem else 2
+    gu_bytes = (n_w * d * f + n * d + n_unique * f + n * f) * 2    # W_gate (+ W_up), x, rows, h
     down_bytes = (d * f + n * f + n * d) * 2                        # W_down, h, y
     step_bytes = w.n_layers * (gu_bytes + down_bytes)
     sha = source_sha("decode.hip", "common.h")
@@ -226,10 +228,11 @@ def run_decode(torch, st, w, steps, warmup):
         "step_bytes": step_bytes,
         "n_unique": n_unique,
         "roofline": {
-            "kernel": "decode_gateup_kernel (staple_ffn_gate_up_packed, 64 tokens)",
+            "kernel": "decode_gateup_kernel (staple_ffn_gate_up_packed, 64 tokens"
+                      + (", STEM gate-only)" if stem else ")"),
             "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": achieved / HBM_PEAK_GBS,
-            "traffic": traffic_from_profile(f"decode_gate_up/{w.name}", sha),
+            "traffic": None if stem else traffic_from_profile(f"decode_gate_up/{w.name}", sha),
             "avg_launch_us": gu_us, "algorithmic_bytes_per_launch": gu_bytes,
         },
     }
@@ -289,7 +292,8 @@ class _Rows:
 # ----------------------------------------------------------------------------
 # Training micro-batch: one layer, fwd + bwd
 # ----------------------------------------------------------------------------
-def setup_train(torch, st, w):
+def setup_train(torch, st, w, stem=False):
+    """stem: the STEM layer (no up-projection, u = E[t]) instead of STAPLE's."""
     from staple_synth import device_normal
     dev = torch.device("cuda:0")
     n, d, f, v = w.n_tokens, w.d_model, w.d_ff, w.vocab
@@ -298,7 +302,7 @@ def setup_train(torch, st, w):
         "ids_np": w.ids(),
         "x": device_normal((n, d), w.x_std, s["x"], torch.bfloat16, dev),
         "w_gate": device_normal((f, d), w.w_std, s["w_gate"], torch.bfloat16, dev),
-        "w_up": device_normal((f, d), w.w_std, s["w_up"], torch.bfloat16, dev),
+        "w_up": None if stem else device_normal((f, d), w.w_std, s["w_up"], torch.bfloat16, dev),
         "w_down": device_normal((d, f), w.w_std, s["w_down"], torch.bfloat16, dev),
         "table": device_normal((v, f), w.table_std, s["table"], torch.bfloat16, dev),
         "dy": device_normal((n, d), w.dy_std, s["dy"], torch.bfloat16, dev),
@@ -316,7 +320,8 @@ def setup_train(torch, st, w):
     T["fwd"] = {"y": torch.empty(n, d, **bf), "g": torch.empty(n, f, **bf),
                 "u": torch.empty(n, f, **bf), "h": torch.empty(n, f, **bf)}
     T["bwd"] = {"d_rows": torch.empty(n, f, **f32), "dx": torch.empty(n, d, **bf),
-                "dw_gate": torch.empty(f, d, **f32), "dw_up": torch.empty(f, d, **f32),
+                "dw_gate": torch.empty(f, d, **f32),
+                "dw_up": None if stem else torch.empty(f, d, **f32),
                 "dw_down": torch.empty(d, f, **f32)}
     T["bwd_ws"] = torch.empty(st.lib().staple_ffn_bwd_workspace_bytes(n, d, f, 1), dtype=torch.uint8,
                               device=dev)
@@ -340,8 +345,8 @@ def train_step(st, T, vocab, events=None):
                                  dd["n_unique"], out=T["bwd"], workspace=T["bwd_ws"])
 
 
-def run_train(torch, st, w, steps, warmup):
-    T = setup_train(torch, st, w)
+def run_train(torch, st, w, steps, warmup, stem=False):
+    T = setup_train(torch, st, w, stem)
     n, d, f = w.n_tokens, w.d_model, w.d_ff
     for _ in range(warmup):
         train_step(st, T, w.vocab)
@@ -361,24 +366,27 @@ def run_train(torch, st, w, steps, warmup):
         torch.cuda.synchronize()
         durs.append(ev[0].elapsed_time(ev[1]) * 1e3)
     gu_us = sum(durs) / len(durs)
-    flops_total = 18 * n * d * f
-    gu_flops = 4 * n * d * f
+    # STAPLE: gate/up 4ndf + down 2ndf forward, twice that backward; STEM has
+    # no up-projection: gate 2ndf + down 2ndf forward, twice that backward
+    flops_total = (12 if stem else 18) * n * d * f
+    gu_flops = (2 if stem else 4) * n * d * f
     achieved = gu_flops / (gu_us * 1e-6) / 1e12
-    adamw = run_device_adamw(torch, st, T, w, reps=max(5, steps))
+    adamw = None if stem else run_device_adamw(torch, st, T, w, reps=max(5, steps))
     return {
         "workload": w.name, "tokens": n, "ms_per_step": ms, "tokens_per_s": n / (ms * 1e-3),
         "step_tflops": flops_total / (ms * 1e-3) / 1e12,
         "step_mfma_frac": flops_total / (ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
         "n_unique": int(T["dd"]["n_unique"].item()),
         "roofline": {
-            "kernel": "gemm_kernel<bf16,GateUp> (staple_ffn_gate_up, training batch)",
+            "kernel": ("gemm_kernel<bf16,GateStem> (staple_ffn_gate_up, w_up NULL, training batch)"
+                       if stem else "gemm_kernel<bf16,GateUp> (staple_ffn_gate_up, training batch)"),
             "bound": "mfma", "achieved": achieved, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
             "frac": achieved / BF16_PEAK_TFLOPS,
-            "traffic": traffic_from_profile(f"train_gate_up/{w.name}",
-                                            source_sha("gemm.hip", "common.h")),
+            "traffic": None if stem else traffic_from_profile(f"train_gate_up/{w.name}",
+                                                              source_sha("gemm.hip", "common.h")),
             "avg_launch_us": gu_us, "algorithmic_flops_per_launch": gu_flops,
         },
-        "adamw_table_rows": adamw,
+        **({"adamw_table_rows": adamw} if adamw else {}),
     }, T
 
 
@@ -792,6 +800,17 @@ def main(argv=None) -> int:
         tr7, T7 = run_train(torch, st, w7, args.train_steps, args.train_warmup)
         out["train_7b"] = tr7
         del T7
+        torch.cuda.empty_cache()
+    if "stem" in wl:
+        # the STEM layer STAPLE is compared against (no up-projection), same workloads
+        dec_s, D_s = run_decode(torch, st, w, args.steps, args.warmup, stem=True)
+        out["decode_stem"] = dict(dec_s, workload=w.name + "_stem")
+        del D_s
+        torch.cuda.empty_cache()
+        tr_s, T_s = run_train(torch, st, S.OLMO1B_TRAIN, args.train_steps, args.train_warmup,
+                              stem=True)
+        out["train_stem"] = dict(tr_s, workload=S.OLMO1B_TRAIN.name + "_stem")
+        del T_s
         torch.cuda.empty_cache()
     if "offload" in wl:
         out["offload_decode"] = run_offload_decode(torch, st, S.OLMO1B_OFFLOAD, 20, 3)
