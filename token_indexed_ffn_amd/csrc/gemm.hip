@@ -79,6 +79,20 @@ struct GemmArgs {
 };
 
 constexpr int kRowBytes = 128;  // bytes of k per LDS tile row and stage
+typedef __attribute__((address_space(3))) u32x4_t lds_u32x4_t;
+
+// One 16-byte-per-lane global -> LDS load (global_load_lds_dwordx4: lane l
+// writes LDS bytes [dst + 16 l, +16), dst wave-uniform, passed in M0).  It is
+// issued from inline asm so that the compiler does not count it among the
+// LDS-counter events: with such a load in flight it would otherwise wait for
+// every outstanding LDS read (lgkmcnt(0)) before each MFMA group instead of
+// only the ones the group needs.  The asm has no register outputs (the data
+// goes to LDS); its completion is waited for by hand (vmcnt) before the
+// barrier that publishes the stage, as for the builtin form.
+__device__ __forceinline__ void dma16(const void* src, lds_void* dst) {
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(reinterpret_cast<uintptr_t>(dst)));
+  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "{m0}"(m0) : "memory");
+}
 
 // K-major LDS tile rows hold RB bytes of k: 128 (8 chunks of 16 bytes) or 64
 // (4 chunks).  The chunk index is XORed with a function of the row so that the
@@ -131,8 +145,19 @@ struct KMajorTile {
     const int w = threadIdx.x >> 6;
 #pragma unroll
     for (int i = 0; i < kPer; ++i)
-      __builtin_amdgcn_global_load_lds(static_cast<const void*>(row_ptr[i] + k_byte + chunk_byte[i]),
-                                       static_cast<lds_void*>(lds + (i * kNW + w) * 1024), 16, 0, 0);
+      dma16(static_cast<const void*>(row_ptr[i] + k_byte + chunk_byte[i]),
+            static_cast<lds_void*>(lds + (i * kNW + w) * 1024));
+  }
+  // Register-staged form of the same loads: load_regs fetches the 16-byte
+  // pieces into reg[], store_piece(i) writes piece i where load() would have.
+  u32x4_t reg[kPer];
+  __device__ __forceinline__ void load_regs(int64_t k_byte) {
+#pragma unroll
+    for (int i = 0; i < kPer; ++i)
+      reg[i] = *reinterpret_cast<const u32x4_t*>(row_ptr[i] + k_byte + chunk_byte[i]);
+  }
+  __device__ __forceinline__ void store_piece(lds_char* lds, int i) const {
+    *reinterpret_cast<lds_u32x4_t*>(lds + (i * kNW + (threadIdx.x >> 6)) * 1024 + (threadIdx.x & 63) * 16) = reg[i];
   }
 };
 
@@ -242,16 +267,27 @@ struct MNDirectTile {
   // first column, or nullptr past the end of K; `cols` is the number of valid
   // columns in the tile (a multiple of 8, so a 16-byte piece is all in or out).
   template <typename BaseFn>
+  __device__ __forceinline__ const void* src(int64_t k0, BaseFn base, int64_t cols, int i) const {
+    const uint16_t* rowp = base(k0 + krow[i]);
+    return (rowp != nullptr && elem[i] < cols) ? static_cast<const void*>(rowp + elem[i])
+                                               : static_cast<const void*>(g_gemm_zero_page);
+  }
+  template <typename BaseFn>
   __device__ __forceinline__ void load(int64_t k0, BaseFn base, int64_t cols, lds_char* lds) const {
     const int w = threadIdx.x >> 6;
 #pragma unroll
-    for (int i = 0; i < kPer; ++i) {
-      const uint16_t* rowp = base(k0 + krow[i]);
-      const void* src = (rowp != nullptr && elem[i] < cols)
-                            ? static_cast<const void*>(rowp + elem[i])
-                            : static_cast<const void*>(g_gemm_zero_page);
-      __builtin_amdgcn_global_load_lds(src, static_cast<lds_void*>(lds + (i * kNW + w) * 1024), 16, 0, 0);
-    }
+    for (int i = 0; i < kPer; ++i)
+      dma16(src(k0, base, cols, i), static_cast<lds_void*>(lds + (i * kNW + w) * 1024));
+  }
+  // Register-staged form (see KMajorTile).
+  u32x4_t reg[kPer];
+  template <typename BaseFn>
+  __device__ __forceinline__ void load_regs(int64_t k0, BaseFn base, int64_t cols) {
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) reg[i] = *reinterpret_cast<const u32x4_t*>(src(k0, base, cols, i));
+  }
+  __device__ __forceinline__ void store_piece(lds_char* lds, int i) const {
+    *reinterpret_cast<lds_u32x4_t*>(lds + (i * kNW + (threadIdx.x >> 6)) * 1024 + (threadIdx.x & 63) * 16) = reg[i];
   }
 };
 
@@ -298,29 +334,62 @@ struct Mma<bf16_t, TM, TN, AK, BK, BM, BN, RB> {
   struct Frags {
     bf16x8_t a[TM], b[TN];
   };
-  __device__ __forceinline__ static void read(const lds_char* As, const lds_char* Bs, int a_row0,
-                                              int b_row0, int kg, Frags& fr) {
+  // Fragment piece q of group kg: q < TM is A fragment q, else B fragment q - TM.
+  __device__ __forceinline__ static void read_piece(const lds_char* As, const lds_char* Bs,
+                                                    int a_row0, int b_row0, int kg, int q,
+                                                    Frags& fr) {
     const int lane = threadIdx.x & 63;
     const int chunk = kg * 2 + (lane >> 5);
     const int kbase = kg * 16 + 8 * (lane >> 5);
     const int half16 = 16 * ((lane >> 4) & 1);
-#pragma unroll
-    for (int i = 0; i < TM; ++i) {
+    if (q < TM) {
+      const int i = q;
       if constexpr (AK) {
         const int r = a_row0 + i * 32 + (lane & 31);
         fr.a[i] = *reinterpret_cast<const lds_bf16x8*>(As + swz<RB>(r, chunk));
       } else {
         fr.a[i] = read_tr_frag<BM * 2>(As, kbase, a_row0 + i * 32 + half16);
       }
-    }
-#pragma unroll
-    for (int j = 0; j < TN; ++j) {
+    } else {
+      const int j = q - TM;
       if constexpr (BK) {
         const int r = b_row0 + j * 32 + (lane & 31);
         fr.b[j] = *reinterpret_cast<const lds_bf16x8*>(Bs + swz<RB>(r, chunk));
       } else {
         fr.b[j] = read_tr_frag<BN * 2>(Bs, kbase, b_row0 + j * 32 + half16);
       }
+    }
+  }
+  __device__ __forceinline__ static void read(const lds_char* As, const lds_char* Bs, int a_row0,
+                                              int b_row0, int kg, Frags& fr) {
+#pragma unroll
+    for (int q = 0; q < TM + TN; ++q) read_piece(As, Bs, a_row0, b_row0, kg, q, fr);
+  }
+  // The MFMAs of one group, after(m) called after MFMA m (in this order).
+  template <typename AfterFn>
+  __device__ __forceinline__ static void mma_each(const Frags& fr, f32x16_t (&acc)[TM][TN],
+                                                  AfterFn after) {
+#pragma unroll
+    for (int m = 0; m < TM * TN; ++m) {
+      const int i = m / TN, j = m % TN;
+      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr.a[i], fr.b[j], acc[i][j], 0, 0, 0);
+      after(m);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+  // The MFMAs of one group with the TM + TN fragment reads of the next group
+  // issued one after each of the first TM + TN MFMAs, in this order (each
+  // next-group MFMA then finds its fragments read several MFMAs earlier).
+  template <typename ReadFn>
+  __device__ __forceinline__ static void mma_interleaved(const Frags& fr, f32x16_t (&acc)[TM][TN],
+                                                         ReadFn read_next) {
+    static_assert(TM + TN <= TM * TN, "reads spread over the MFMAs");
+#pragma unroll
+    for (int m = 0; m < TM * TN; ++m) {
+      const int i = m / TN, j = m % TN;
+      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr.a[i], fr.b[j], acc[i][j], 0, 0, 0);
+      if (m < TM + TN) read_next(m);
+      __builtin_amdgcn_sched_barrier(0);
     }
   }
   __device__ __forceinline__ static void mma(const Frags& fr, f32x16_t (&acc)[TM][TN]) {
@@ -463,9 +532,13 @@ __device__ __forceinline__ void store8g(void* base, int64_t idx, const float (&v
 
 // ---------------------------------------------------------------------------
 // The kernel: BM x BN tile, WGM x WGN waves, NS LDS stages of RB bytes of k.
+// PIPE 0: operands loaded straight into LDS NS - 1 stages ahead, one barrier
+// per stage at its start, fragments read one group ahead within the stage.
+// PIPE 2 (bf16): operands staged through registers, fragment reads one group
+// ahead across stage boundaries and interleaved with the MFMAs (see the loop).
 // ---------------------------------------------------------------------------
 template <typename T, int BM, int BN, int WGM, int WGN, bool AK, bool BK, int EPI, typename OutT,
-          int RB, int NS>
+          int RB, int NS, int PIPE = 0>
 __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(GemmArgs p) {
   constexpr int NT = 64 * WGM * WGN;
   constexpr int WM = BM / WGM, WN = BN / WGN;
@@ -595,6 +668,64 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(GemmArgs p) {
   // the buffer about to be refilled has been read by all.
   constexpr int kLoads = (AK || kMNDirect ? ATile::kPer : 0) + (BK || kMNDirect ? BTile::kPer : 0);
   const int64_t nk = (p.K + kBK - 1) / kBK;
+  if constexpr (PIPE == 2) {
+    // Register-staged pipeline, two LDS stages of 64 k (four groups).  In
+    // stage s: groups 0-2 read the next group's fragments during their
+    // MFMAs; group 2 also writes stage s + 1 (in registers since stage s - 1)
+    // into the other LDS buffer, one 16-byte piece per MFMA; barrier B_{s+1}
+    // (this wave's LDS writes and reads done, then s_barrier) publishes it;
+    // group 3 reads stage s + 1's first group and issues the global loads of
+    // stage s + 2 into the registers.  The other buffer held stage s - 1,
+    // whose last reads came before B_s.  Past the end of K the writes go to
+    // the idle buffer and the loads re-read the last stage, so every stage
+    // runs the same instruction sequence.
+    static_assert(kMNDirect && RB == 128 && NS == 2 && ATile::kPer + BTile::kPer <= TM * TN,
+                  "register-staged pipeline");
+    constexpr int NA = ATile::kPer, NP = ATile::kPer + BTile::kPer;
+    using Fr = typename MmaT::Frags;
+    Fr fr[2];
+    const int a_row0 = wm * WM, b_row0 = wn * WN;
+    auto load_regs = [&](int64_t kt) {
+      const int64_t k0 = kt * kBK;
+      if constexpr (AK) at.load_regs(k0 * static_cast<int64_t>(sizeof(T)));
+      else at.load_regs(k0, a_base16, a_cols);
+      if constexpr (BK) bt.load_regs(k0 * static_cast<int64_t>(sizeof(T)));
+      else bt.load_regs(k0, b_base16, b_cols);
+    };
+    auto store_piece = [&](int buf, int q) {
+      lds_char* la = lds + buf * kStage;
+      if (q < NA) at.store_piece(la, q);
+      else bt.store_piece(la + BM * RB, q - NA);
+    };
+    if (nk > 0) {
+      load_regs(0);
+#pragma unroll
+      for (int q = 0; q < NP; ++q) store_piece(0, q);
+      load_regs(nk > 1 ? 1 : 0);
+      lds_barrier();                                        // B_0
+      MmaT::read(lds, lds + BM * RB, a_row0, b_row0, 0, fr[0]);
+    }
+    for (int64_t st = 0; st < nk; ++st) {
+      const int cur = static_cast<int>(st & 1);
+      const lds_char* As = lds + cur * kStage;
+      const lds_char* Bs = As + BM * RB;
+      MmaT::mma_interleaved(fr[0], acc, [&](int q) { MmaT::read_piece(As, Bs, a_row0, b_row0, 1, q, fr[1]); });
+      MmaT::mma_interleaved(fr[1], acc, [&](int q) { MmaT::read_piece(As, Bs, a_row0, b_row0, 2, q, fr[0]); });
+      MmaT::mma_each(fr[0], acc, [&](int m) {
+        if (m < TM + TN) MmaT::read_piece(As, Bs, a_row0, b_row0, 3, m, fr[1]);
+        if (m < NP) store_piece(cur ^ 1, m);
+      });
+      lds_barrier();                                        // B_{st+1}
+      const bool more = st + 1 < nk;
+      const lds_char* An = more ? lds + (cur ^ 1) * kStage : As;
+      const lds_char* Bn = An + BM * RB;
+      const int64_t next = st + 2 < nk ? st + 2 : nk - 1;
+      MmaT::mma_each(fr[1], acc, [&](int m) {
+        if (m < TM + TN) MmaT::read_piece(An, Bn, a_row0, b_row0, 0, m, fr[0]);
+        if (m == TM + TN) load_regs(next);
+      });
+    }
+  } else {
 #pragma unroll
   for (int st = 0; st < NS - 1; ++st) {
     if (st < nk) {
@@ -614,6 +745,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(GemmArgs p) {
     if (kt + NS - 1 < nk) issue_loads(kt + NS - 1, static_cast<int>((kt + NS - 1) % NS));
     compute(static_cast<int>(kt % NS));
     if (kt + NS - 1 < nk) store_regs(static_cast<int>((kt + NS - 1) % NS));
+  }
   }
   __syncthreads();   // the epilogue reuses the stage buffers
 
@@ -786,10 +918,10 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(GemmArgs p) {
 // Host launchers
 // ---------------------------------------------------------------------------
 template <typename T, int BM, int BN, int WGM, int WGN, bool AK, bool BK, int EPI, typename OutT,
-          int RB, int NS>
+          int RB, int NS, int PIPE = 0>
 static hipError_t run_tile(const GemmArgs& a, hipStream_t s) {
   constexpr size_t kSmem = static_cast<size_t>(NS) * (BM + BN) * RB;
-  auto kern = &gemm_kernel<T, BM, BN, WGM, WGN, AK, BK, EPI, OutT, RB, NS>;
+  auto kern = &gemm_kernel<T, BM, BN, WGM, WGN, AK, BK, EPI, OutT, RB, NS, PIPE>;
   static const hipError_t attr = hipFuncSetAttribute(
       reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
       static_cast<int>(kSmem));
@@ -804,15 +936,14 @@ template <typename T, bool AK, bool BK, int EPI, typename OutT>
 static hipError_t run(const GemmArgs& a, hipStream_t s) {
   if (a.M <= 0 || a.N <= 0) return hipSuccess;
   if constexpr (sizeof(T) == 2) {
-    // (2x2 waves of 128x128, with half the LDS reads per MFMA, measured
-    // slower: one wave per SIMD hides too little latency)
-    // (Four or five 32 KB stages of 64-byte rows, which keep three or four
-    // stages of loads in flight, measured no faster: the kernels are not
-    // waiting on global-load latency.)
-    // (256x128 or 128x256 tiles on 4 waves, two workgroups per CU with
-    // three 64-byte-row stages, measured slower on every training GEMM.)
+    // Register-staged 8-wave pipeline: 1-3 points of MFMA peak above the
+    // direct-to-LDS one on five of the six training GEMMs (level on dx).
+    // Measured slower: 2x2 waves of 128x128 (half the LDS reads per MFMA)
+    // with either pipeline, three to five 32 KB stages (loads three or four
+    // stages ahead: the kernels are not waiting on global-load latency), and
+    // 256x128 or 128x256 tiles on 4 waves with two workgroups per CU.
     if (a.M >= 256 && a.N >= 256 && ((a.M + 255) / 256) * ((a.N + 255) / 256) >= 128)
-      return run_tile<T, 256, 256, 2, 4, AK, BK, EPI, OutT, kRowBytes, 2>(a, s);
+      return run_tile<T, 256, 256, 2, 4, AK, BK, EPI, OutT, kRowBytes, 2, 2>(a, s);
   }
   return run_tile<T, 128, 128, 2, 2, AK, BK, EPI, OutT, kRowBytes, 2>(a, s);
 }
