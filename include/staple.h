@@ -355,6 +355,56 @@ staple_status_t staple_ffn_fwd_packed(int64_t n_tokens, int64_t d_model, int64_t
                                       void* stream);
 
 /* ------------------------------------------------------------------------
+ * One decode step over a stack of layers whose tables live in pinned host
+ * memory with the most frequent rows cached in HBM (STAPLE retrieval-path
+ * table, Decode row: one dedup and cache probe per step, then the layers;
+ * Table 4 caption: the 1 GB cache of frequent rows).  Enqueues on `stream`:
+ *   1. staple_dedup of ids (the batch's n tokens) and staple_cache_lookup
+ *      against id_to_slot;
+ *   2. every layer's compact rows R_l = layers[l].rows (hits from
+ *      layers[l].cache_rows, misses read straight from layers[l].table, as
+ *      staple_assemble_rows_from_table), one launch for up to 32 layers, so
+ *      the host reads of all layers' misses are in flight together;
+ *   3. each layer's decode forward (staple_ffn_fwd_packed with rows = R_l,
+ *      row_index = inv).
+ * The whole step is one native call: issuing it costs one call per step
+ * instead of several per layer.
+ *
+ *   layers: host array of n_layers descriptors:
+ *     x [n x d_model] bf16; packed_gate_up, packed_down from
+ *     staple_decode_pack_weights (up_proj as for staple_ffn_fwd_packed);
+ *     cache_rows [capacity x d_ff] bf16 device (slot s = the row of the ID
+ *     with slot s in id_to_slot, e.g. from staple_cache_fill); table
+ *     [vocab x d_ff] bf16, pinned host (hipHostMalloc) or device; rows
+ *     [n x d_ff] bf16 device, one per layer (it holds R_l after the step);
+ *     y [n x d_model] of out_dtype.
+ *   1 <= n <= 64, d_model and d_ff multiples of 64 (else UNSUPPORTED).
+ *   uniq, inv, sorted_pos [n], seg_start [n + 1], n_unique [1]: staple_dedup's
+ *     outputs; code, miss_uidx [n], n_miss [1]: staple_cache_lookup's.
+ *   ws: staple_decode_step_workspace_bytes(n, d_model, d_ff) bytes.
+ * Same outputs bit for bit as the separate calls.  Argument errors return
+ * before anything is enqueued; the device error word reports IDs or slots
+ * out of range.
+ * ------------------------------------------------------------------------ */
+typedef struct staple_decode_layer {
+  const void* x;
+  const void* packed_gate_up;
+  const void* packed_down;
+  const void* cache_rows;
+  const void* table;
+  void* rows;
+  void* y;
+} staple_decode_layer_t;
+
+size_t staple_decode_step_workspace_bytes(int64_t n_tokens, int64_t d_model, int64_t d_ff);
+staple_status_t staple_decode_step_cached(
+    int64_t n_layers, const staple_decode_layer_t* layers, int64_t n_tokens, int64_t d_model,
+    int64_t d_ff, int32_t up_proj, int32_t out_dtype, const int32_t* ids, int64_t vocab,
+    const int32_t* id_to_slot, int64_t capacity, int32_t* uniq, int32_t* inv,
+    int32_t* sorted_pos, int32_t* seg_start, int32_t* n_unique, int32_t* code,
+    int32_t* miss_uidx, int32_t* n_miss, void* ws, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
  * AdamW step on the table rows a batch touched.  The tables are trained with
  * AdamW with fp32 moments beside the bf16 table (STAPLE Figure 4 caption:
  * bf16 tables and fp32 AdamW moments in host DRAM; Table 3: peak learning

@@ -901,3 +901,91 @@ def test_stem_packed_matches_oracle_and_row_major_bitwise(st, dev, n, d, f):
     assert_close(to_np(got["y"]), of["y"], f"stem packed y n={n} f={f}")
     assert_close(to_np(got["h"]), of["h"], f"stem packed h n={n} f={f}")
     np.testing.assert_array_equal(to_np(got["u"]), of["u_saved"])
+
+
+# ---------------------------------------------------------------- native decode step driver
+@pytest.mark.parametrize("stem", [False, True])
+def test_decode_step_driver_matches_per_layer_calls(st, dev, stem):
+    """staple_decode_step_cached (dedup, cache probe, every layer's rows from
+    the HBM cache or the pinned host table in one launch, the packed FFNs)
+    gives each layer's y and rows bit for bit as the separate calls over
+    several steps, and y matches the oracle on the full table."""
+    import torch
+    L, n, d, f, vocab, cap = 3, 33, 128, 256, 500, 40
+    _log(f"decode step driver stem={stem}")
+    counts = st.staple_cache_count(torch.from_numpy(S.zipf_ids(20_000, vocab, 3)).to(dev), vocab)
+    i2s, s2i = st.staple_cache_build(counts, cap)
+    layers, ref = [], []
+    for l in range(L):
+        inp = S.host_layer_inputs(n, d, f, vocab, dtype="bf16", seed=90 + l, table_std=0.5)
+        x, wg, wu, wd = (to_dev(getattr(inp, k), "bf16", dev) for k in ("x", "w_gate", "w_up", "w_down"))
+        host_table = torch.from_numpy(inp.table.view(np.int16)).view(torch.bfloat16).pin_memory()
+        pgu, pd = st.staple_decode_pack_weights(wg, None if stem else wu, wd, d_model=d, d_ff=f)
+        layers.append({"x": x, "packed_gate_up": pgu, "packed_down": pd,
+                       "cache_rows": st.staple_cache_fill(host_table, s2i, cap), "table": host_table,
+                       "rows": torch.zeros(n, f, dtype=torch.bfloat16, device=dev),
+                       "y": torch.zeros(n, d, dtype=torch.float32, device=dev)})
+        ref.append(inp)
+    stack = st.DecodeStack(layers, d_model=d, d_ff=f, n_tokens=n)
+    i32 = dict(dtype=torch.int32, device=dev)
+    dd = {"uniq": torch.empty(n, **i32), "inv": torch.empty(n, **i32),
+          "sorted_pos": torch.empty(n, **i32), "seg_start": torch.empty(n + 1, **i32),
+          "n_unique": torch.empty(1, **i32)}
+    lk = {"code": torch.empty(n, **i32), "miss_uidx": torch.empty(n, **i32),
+          "n_miss": torch.empty(1, **i32)}
+    ws = torch.empty(st.decode_step_workspace_bytes(n, d, f), dtype=torch.uint8, device=dev)
+    for step in range(3):
+        ids_np = S.zipf_ids(n, vocab, 500 + step)
+        ids = torch.from_numpy(ids_np).to(dev)
+        d2 = st.staple_dedup(ids, vocab)
+        l2 = st.staple_cache_lookup(d2["uniq"], d2["n_unique"], i2s)
+        want = []
+        for lay in layers:
+            r = st.staple_assemble_rows_from_table(lay["cache_rows"], lay["table"], d2["uniq"],
+                                                   l2["code"], d2["n_unique"], capacity=cap)
+            y = st.staple_ffn_fwd_packed(lay["x"], lay["packed_gate_up"], lay["packed_down"], r,
+                                         d2["inv"], d_ff=f, out_dtype=torch.float32)["y"]
+            want.append((r, y))
+        for lay in layers:
+            lay["y"].zero_()
+            lay["rows"].zero_()
+        st.staple_decode_step_cached(stack, ids, i2s, cap, dedup_out=dd, lookup_out=lk, workspace=ws)
+        torch.cuda.synchronize()
+        _no_device_error(st)
+        u = int(d2["n_unique"].item())
+        assert int(dd["n_unique"].item()) == u
+        assert torch.equal(dd["inv"], d2["inv"]) and torch.equal(lk["code"][:u], l2["code"][:u])
+        for l, lay in enumerate(layers):
+            assert torch.equal(lay["y"], want[l][1]), (step, l)
+            assert torch.equal(lay["rows"][:u], want[l][0][:u]), (step, l)
+            g = {k: ref[l].as_f64(k) for k in ("x", "w_gate", "w_up", "w_down", "table")}
+            of = O.ffn_forward(g["x"], g["w_gate"], None if stem else g["w_up"], g["w_down"],
+                               g["table"], ids_np, precision=O.BF16)
+            assert_close(to_np(lay["y"]), of["y"], f"driver y layer {l} step {step}")
+
+
+def test_decode_step_driver_refuses_bad_arguments(st, dev):
+    """Batches past 64 tokens and a layer without a table are refused before
+    anything is enqueued."""
+    import ctypes
+    import torch
+    d, f, vocab = 64, 64, 10
+    t = lambda *sh, **kw: torch.zeros(*sh, dtype=kw.get("dtype", torch.bfloat16), device=dev)
+    host_table = torch.zeros(vocab, f, dtype=torch.bfloat16).pin_memory()
+    lay = {"x": t(64, d), "packed_gate_up": t(2 * f * d), "packed_down": t(f * d),
+           "cache_rows": t(1, f), "table": host_table, "rows": t(64, f), "y": t(64, d)}
+    stack = st.DecodeStack([lay], d_model=d, d_ff=f, n_tokens=64)
+    i32 = dict(dtype=torch.int32)
+    dd = {k: t(66, **i32) for k in ("uniq", "inv", "sorted_pos", "seg_start", "n_unique")}
+    lk = {k: t(66, **i32) for k in ("code", "miss_uidx", "n_miss")}
+    ws = t(1 << 20, dtype=torch.uint8)
+    i2s = torch.full((vocab,), -1, dtype=torch.int32, device=dev)
+    with pytest.raises(RuntimeError, match="UNSUPPORTED|unsupported"):
+        st.staple_decode_step_cached(stack, t(65, **i32), i2s, 0, dedup_out=dd, lookup_out=lk,
+                                     workspace=ws)
+    stack.desc[0].table = None      # a layer without its table
+    with pytest.raises(RuntimeError, match="INVALID|invalid"):
+        st.staple_decode_step_cached(stack, t(64, **i32), i2s, 0, dedup_out=dd, lookup_out=lk,
+                                     workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(dd["n_unique"]) == 0 and torch.count_nonzero(lay["y"]) == 0

@@ -11,6 +11,8 @@ from __future__ import annotations
 
 from typing import Optional
 
+import ctypes
+
 import torch
 
 from . import _lib
@@ -384,6 +386,51 @@ def staple_ffn_down(h: torch.Tensor, w_down: torch.Tensor, y: torch.Tensor,
     _check(lib().staple_ffn_down(n, d, f, _dt(h), _DT[y.dtype], _p(h), _p(w_down), _p(y), _p(ws),
                                  _ws_size(ws), _stream(stream)), "staple_ffn_down")
     return y
+
+
+class _DecodeLayer(ctypes.Structure):
+    _fields_ = [(k, ctypes.c_void_p) for k in
+                ("x", "packed_gate_up", "packed_down", "cache_rows", "table", "rows", "y")]
+
+
+class DecodeStack:
+    """The per-layer tensors of staple_decode_step_cached, marshalled once
+    (the descriptor array is rebuilt only when this object is)."""
+
+    def __init__(self, layers: list, *, d_model: int, d_ff: int, n_tokens: int):
+        keys = ("x", "packed_gate_up", "packed_down", "cache_rows", "table", "rows", "y")
+        self.layers = [{k: lay[k] for k in keys} for lay in layers]   # keeps the tensors alive
+        for lay in self.layers:
+            _dev(lay["x"], lay["packed_gate_up"], lay["packed_down"], lay["cache_rows"],
+                 lay["rows"], lay["y"])
+            if not (lay["table"].is_cuda or lay["table"].is_pinned()):
+                raise ValueError("table must be a device or pinned host tensor")
+        self.n_layers = len(layers)
+        self.d_model, self.d_ff, self.n_tokens = d_model, d_ff, n_tokens
+        self.up_proj = _up_proj(self.layers[0]["packed_gate_up"], d_model, d_ff)
+        self.out_dtype = _DT[self.layers[0]["y"].dtype]
+        self.desc = (_DecodeLayer * self.n_layers)(
+            *[_DecodeLayer(*[_p(lay[k]) for k in keys]) for lay in self.layers])
+
+
+def staple_decode_step_cached(stack: DecodeStack, ids: torch.Tensor, id_to_slot: torch.Tensor,
+                              capacity: int, *, dedup_out: dict, lookup_out: dict,
+                              workspace: torch.Tensor, stream=None) -> None:
+    """One decode step over the stack: dedup + cache probe, every layer's rows (one
+    launch), each layer's packed FFN."""
+    n = ids.numel()
+    vocab = id_to_slot.numel()
+    dd, lk = dedup_out, lookup_out
+    _check(lib().staple_decode_step_cached(
+        stack.n_layers, ctypes.cast(stack.desc, ctypes.c_void_p), n, stack.d_model, stack.d_ff,
+        stack.up_proj, stack.out_dtype, _p(ids), vocab, _p(id_to_slot), int(capacity),
+        _p(dd["uniq"]), _p(dd["inv"]), _p(dd["sorted_pos"]), _p(dd["seg_start"]),
+        _p(dd["n_unique"]), _p(lk["code"]), _p(lk["miss_uidx"]), _p(lk["n_miss"]), _p(workspace),
+        _ws_size(workspace), _stream(stream)), "staple_decode_step_cached")
+
+
+def decode_step_workspace_bytes(n: int, d: int, f: int) -> int:
+    return lib().staple_decode_step_workspace_bytes(n, d, f)
 
 
 def staple_adamw_rows(table: torch.Tensor, m: torch.Tensor, v: torch.Tensor, rows: torch.Tensor,

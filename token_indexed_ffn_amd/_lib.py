@@ -55,6 +55,10 @@ _SIGS = {
     "staple_ffn_fwd_packed": (c_i32, [c_i64, c_i64, c_i64, c_i32, c_i32, c_vp, c_vp, c_i32, c_vp,
                                       c_vp, c_i64, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_sz,
                                       c_vp]),
+    "staple_decode_step_workspace_bytes": (c_sz, [c_i64, c_i64, c_i64]),
+    "staple_decode_step_cached": (c_i32, [c_i64, c_vp, c_i64, c_i64, c_i64, c_i32, c_i32, c_vp,
+                                          c_i64, c_vp, c_i64, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp,
+                                          c_vp, c_vp, c_vp, c_sz, c_vp]),
     "staple_adamw_rows": (c_i32, [c_vp, c_vp, c_vp, c_i64, c_i64, c_i32, c_vp, c_vp, c_i64, c_vp,
                                   c_f32, c_f32, c_f32, c_f32, c_f32, c_i64, c_vp]),
     "staple_adamw_rows_host": (c_i32, [c_vp, c_vp, c_vp, c_i64, c_i64, c_i32, c_vp, c_i64, c_vp,

@@ -44,6 +44,10 @@ hipError_t launch_assemble_rows_table(const void* cache_rows, int64_t capacity, 
                                       const int32_t* n_unique, int64_t max_unique,
                                       int64_t row_bytes, void* rows, hipStream_t s, int* err,
                                       unsigned max_workgroups);
+hipError_t launch_assemble_rows_layers(const LayerRowSources& src, int n_layers, int64_t capacity,
+                                       int64_t vocab, const int32_t* uniq, const int32_t* code,
+                                       const int32_t* n_unique, int64_t max_unique,
+                                       int64_t row_bytes, hipStream_t s, int* err);
 size_t segment_sum_workspace_bytes(int64_t n_tokens, int64_t d_ff);
 hipError_t launch_segment_sum(int dtype, const void* du, int64_t du_ld, int64_t du_col,
                               int64_t n_tokens, int64_t d_ff, const int32_t* sorted_pos,
@@ -549,6 +553,68 @@ staple_status_t staple_ffn_fwd_packed(int64_t n, int64_t d, int64_t f, int32_t d
   HIPCALL(decode_gateup(n, nullptr, n, d, f, x, packed_gate_up, nullptr, rows, n_rows, row_index, h,
                         save_g, save_u, s, err, true, up_proj != 0));
   HIPCALL(decode_down(n, d, f, h, packed_down, y, out_dtype, down_ws, s, true));
+  return STAPLE_OK;
+}
+
+// ------------------------------------------------------------------ decode step driver
+size_t staple_decode_step_workspace_bytes(int64_t n, int64_t d, int64_t f) {
+  if (!decode_eligible(n, d, f, STAPLE_BF16) || !ffn_shape_ok(n, d, f, STAPLE_BF16)) return 0;
+  return align_up(dedup_workspace_bytes(n), 256) + staple_ffn_fwd_workspace_bytes(n, d, f, STAPLE_BF16);
+}
+
+staple_status_t staple_decode_step_cached(
+    int64_t n_layers, const staple_decode_layer_t* layers, int64_t n, int64_t d, int64_t f,
+    int32_t up_proj, int32_t out_dtype, const int32_t* ids, int64_t vocab,
+    const int32_t* id_to_slot, int64_t capacity, int32_t* uniq, int32_t* inv, int32_t* sorted_pos,
+    int32_t* seg_start, int32_t* n_unique, int32_t* code, int32_t* miss_uidx, int32_t* n_miss,
+    void* ws, size_t ws_bytes, void* stream) {
+  if (!valid_dtype(out_dtype) || !ffn_shape_ok(n, d, f, STAPLE_BF16) ||
+      !decode_eligible(n, d, f, STAPLE_BF16))
+    return STAPLE_ERR_UNSUPPORTED;
+  REQUIRE(n_layers >= 1 && n_layers <= 4096 && layers);
+  REQUIRE(vocab >= 1 && vocab <= 0x7fffffffll && capacity >= 0);
+  REQUIRE(ids && id_to_slot && uniq && inv && sorted_pos && seg_start && n_unique && code &&
+          miss_uidx && n_miss);
+  const size_t need = staple_decode_step_workspace_bytes(n, d, f);
+  if (ws_bytes < need) return STAPLE_ERR_WORKSPACE;
+  REQUIRE(ws && aligned16(ws));
+  for (int64_t l = 0; l < n_layers; ++l) {
+    const staple_decode_layer_t& L = layers[l];
+    REQUIRE(L.x && L.packed_gate_up && L.packed_down && L.table && L.rows && L.y);
+    REQUIRE(capacity == 0 || L.cache_rows);
+    REQUIRE(aligned16(L.x) && aligned16(L.packed_gate_up) && aligned16(L.packed_down) &&
+            aligned16(L.table) && aligned16(L.rows) && aligned16(L.y) &&
+            (capacity == 0 || aligned16(L.cache_rows)));
+    REQUIRE(device_addressable(L.table));
+  }
+  GET_ERR(err);
+  hipStream_t s = S(stream);
+  void* dedup_ws = ws;
+  void* fwd_ws = static_cast<char*>(ws) + align_up(dedup_workspace_bytes(n), 256);
+  void* h = fwd_ws;
+  void* down_ws = static_cast<char*>(fwd_ws) + align_up(static_cast<size_t>(n) * f * 2, 256);
+  HIPCALL(launch_dedup(ids, n, vocab, uniq, inv, sorted_pos, seg_start, n_unique, dedup_ws, s, err));
+  HIPCALL(launch_cache_lookup(uniq, n_unique, n, id_to_slot, vocab, code, miss_uidx, nullptr, n_miss,
+                              s, err));
+  // every layer's rows in one launch per slice of layers: the misses of all
+  // layers are read from host memory together
+  for (int64_t l0 = 0; l0 < n_layers; l0 += kMaxAssembleLayers) {
+    const int cnt = static_cast<int>(std::min<int64_t>(kMaxAssembleLayers, n_layers - l0));
+    LayerRowSources src{};
+    for (int i = 0; i < cnt; ++i) {
+      src.cache_rows[i] = layers[l0 + i].cache_rows;
+      src.table[i] = layers[l0 + i].table;
+      src.rows[i] = layers[l0 + i].rows;
+    }
+    HIPCALL(launch_assemble_rows_layers(src, cnt, capacity, vocab, uniq, code, n_unique, n, f * 2, s,
+                                        err));
+  }
+  for (int64_t l = 0; l < n_layers; ++l) {
+    const staple_decode_layer_t& L = layers[l];
+    HIPCALL(decode_gateup(n, nullptr, n, d, f, L.x, L.packed_gate_up, nullptr, L.rows, n, inv, h,
+                          nullptr, nullptr, s, err, true, up_proj != 0));
+    HIPCALL(decode_down(n, d, f, h, L.packed_down, L.y, out_dtype, down_ws, s, true));
+  }
   return STAPLE_OK;
 }
 

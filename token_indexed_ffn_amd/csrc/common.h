@@ -120,6 +120,16 @@ namespace staple {
 struct AdamWConsts {
   float decay, beta1, one_m_beta1, beta2, one_m_beta2, step_size, inv_sqrt_bc2, eps;
 };
+
+// Per-layer row sources of a multi-layer row assembly (passed by value as a
+// kernel argument; a longer stack is assembled in slices of this many layers).
+constexpr int kMaxAssembleLayers = 32;
+constexpr unsigned kLayerRowWorkgroups = 512;
+struct LayerRowSources {
+  const void* cache_rows[kMaxAssembleLayers];
+  const void* table[kMaxAssembleLayers];
+  void* rows[kMaxAssembleLayers];
+};
 }  // namespace staple
 
 #define STAPLE_LAUNCH_CHECK()                           \

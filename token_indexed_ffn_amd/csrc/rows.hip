@@ -306,6 +306,54 @@ hipError_t launch_assemble_rows_table(const void* cache_rows, int64_t capacity, 
   return hipGetLastError();
 }
 
+// The same assembly for several layers at once (the tables of a layer stack
+// share one cache map): work item k = (layer k / max_unique, unique row
+// k % max_unique), one row per workgroup, so the PCIe reads of every layer's
+// misses are in flight together.
+__global__ __launch_bounds__(kRowThreads) void assemble_rows_layers_kernel(
+    LayerRowSources src, int n_layers, int64_t capacity, int64_t vocab, const int32_t* uniq,
+    const int32_t* code, const int32_t* n_unique_p, int64_t max_unique, int64_t row_bytes,
+    int* err) {
+  const int64_t n = min(static_cast<int64_t>(*n_unique_p), max_unique);
+  const int64_t total = static_cast<int64_t>(n_layers) * max_unique;
+  for (int64_t k = blockIdx.x; k < total; k += gridDim.x) {
+    const int l = static_cast<int>(k / max_unique);
+    const int64_t u = k - static_cast<int64_t>(l) * max_unique;
+    if (u >= n) continue;
+    const int32_t c = code[u];
+    const char* from;
+    if (c >= 0) {
+      if (c >= capacity) {
+        if (threadIdx.x == 0) flag_index_error(err);
+        continue;
+      }
+      from = static_cast<const char*>(src.cache_rows[l]) + c * row_bytes;
+    } else {
+      const int32_t id = uniq[u];
+      if (id < 0 || id >= vocab) {
+        if (threadIdx.x == 0) flag_index_error(err);
+        continue;
+      }
+      from = static_cast<const char*>(src.table[l]) + id * row_bytes;
+    }
+    copy_row16(reinterpret_cast<const uint4*>(from),
+               reinterpret_cast<uint4*>(static_cast<char*>(src.rows[l]) + u * row_bytes),
+               row_bytes / 16);
+  }
+}
+
+hipError_t launch_assemble_rows_layers(const LayerRowSources& src, int n_layers, int64_t capacity,
+                                       int64_t vocab, const int32_t* uniq, const int32_t* code,
+                                       const int32_t* n_unique, int64_t max_unique,
+                                       int64_t row_bytes, hipStream_t s, int* err) {
+  if (max_unique == 0 || n_layers == 0) return hipSuccess;
+  assemble_rows_layers_kernel<<<dim3(row_grid(n_layers * max_unique, kLayerRowWorkgroups)),
+                                dim3(kRowThreads), 0, s>>>(src, n_layers, capacity, vocab, uniq,
+                                                            code, n_unique, max_unique, row_bytes,
+                                                            err);
+  return hipGetLastError();
+}
+
 // ---------------------------------------------------------------------------
 // Table-row gradient: d_rows[u, c] = sum over sorted positions p of segment u
 // of du[sorted_pos[p], c], accumulated in fp32.

@@ -248,6 +248,54 @@ __global__ __launch_bounds__(kSortThreads) void dedup_small_kernel(
              wave_tmp);
 }
 
+// Whole dedup of at most 64 positions (a decode batch) in one wave: lane i
+// holds key i, the bitonic network runs on registers with lane exchanges,
+// and the segment starts come from a ballot, so there is no LDS and no
+// barrier.  Same outputs as the workgroup kernels.
+__device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int mask) {
+  const uint32_t lo = static_cast<uint32_t>(__shfl_xor(static_cast<int>(v & 0xffffffffu), mask, 64));
+  const uint32_t hi = static_cast<uint32_t>(__shfl_xor(static_cast<int>(v >> 32), mask, 64));
+  return (static_cast<uint64_t>(hi) << 32) | lo;
+}
+
+__global__ __launch_bounds__(64) void dedup_wave_kernel(const int32_t* ids, int64_t n, int64_t vocab,
+                                                        int32_t* uniq, int32_t* inv,
+                                                        int32_t* sorted_pos, int32_t* seg_start,
+                                                        int32_t* n_unique, int* err) {
+  const int lane = threadIdx.x;
+  uint64_t key = dedup_key(ids, lane, n, vocab, err);
+#pragma unroll
+  for (int k = 2; k <= 64; k <<= 1) {
+#pragma unroll
+    for (int j = k >> 1; j >= 1; j >>= 1) {
+      const uint64_t other = shfl_xor_u64(key, j);
+      const bool asc = (lane & k) == 0;       // k = 64: the whole wave ascending
+      const bool lower = (lane & j) == 0;
+      key = (lower == asc) ? (key < other ? key : other) : (key < other ? other : key);
+    }
+  }
+  const bool valid = lane < n;
+  const int32_t id = static_cast<int32_t>(key >> 32);
+  const int32_t prev = __shfl_up(id, 1, 64);
+  const bool first = valid && (lane == 0 || prev != id);
+  const uint64_t starts = __ballot(first);
+  const int seg = __popcll(starts & ((2ull << lane) - 1)) - 1;   // segment of this position
+  if (valid) {
+    const int32_t pos = static_cast<int32_t>(key & 0xffffffffu);
+    if (first) {
+      uniq[seg] = id;
+      seg_start[seg] = lane;
+    }
+    sorted_pos[lane] = pos;
+    inv[pos] = seg;
+  }
+  if (lane == 0) {
+    const int total = __popcll(starts);
+    *n_unique = total;
+    seg_start[total] = static_cast<int32_t>(n);
+  }
+}
+
 size_t dedup_workspace_bytes(int64_t n) {
   if (n <= kTile) return 0;
   return static_cast<size_t>(next_pow2(n)) * sizeof(uint64_t);
@@ -256,6 +304,11 @@ size_t dedup_workspace_bytes(int64_t n) {
 hipError_t launch_dedup(const int32_t* ids, int64_t n, int64_t vocab, int32_t* uniq, int32_t* inv,
                         int32_t* sorted_pos, int32_t* seg_start, int32_t* n_unique, void* ws,
                         hipStream_t s, int* err) {
+  if (n <= 64) {
+    dedup_wave_kernel<<<dim3(1), dim3(64), 0, s>>>(ids, n, vocab, uniq, inv, sorted_pos, seg_start,
+                                                   n_unique, err);
+    return hipGetLastError();
+  }
   if (n <= kTile) {
     const int64_t padded = n <= 1 ? 1 : next_pow2(n);
     dedup_small_kernel<<<dim3(1), dim3(kSortThreads), 0, s>>>(ids, n, padded, vocab, uniq, inv,
