@@ -126,8 +126,7 @@ struct KMajorTile {
   static constexpr int kRPI = 1024 / RB;
   static constexpr int kPer = R / (kRPI * kNW);
   static_assert(kPer * kRPI * kNW == R, "tile shape");
-  const char* row_ptr[kPer];
-  int chunk_byte[kPer];
+  const char* row_ptr[kPer];   // row start, then (init_chunks) plus the lane's chunk offset
 
   __device__ __forceinline__ static int row_of(int i) {
     return kRPI * (i * kNW + (threadIdx.x >> 6)) + (threadIdx.x & 63) / kLPR;
@@ -137,7 +136,7 @@ struct KMajorTile {
     for (int i = 0; i < kPer; ++i) {
       const int row = row_of(i);
       const int phys = threadIdx.x % kLPR;
-      chunk_byte[i] = (phys ^ row_swizzle<RB>(row)) << 4;
+      row_ptr[i] += (phys ^ row_swizzle<RB>(row)) << 4;
     }
   }
   // `lds` is the tile's LDS buffer (local address space).
@@ -145,7 +144,7 @@ struct KMajorTile {
     const int w = threadIdx.x >> 6;
 #pragma unroll
     for (int i = 0; i < kPer; ++i)
-      dma16(static_cast<const void*>(row_ptr[i] + k_byte + chunk_byte[i]),
+      dma16(static_cast<const void*>(row_ptr[i] + k_byte),
             static_cast<lds_void*>(lds + (i * kNW + w) * 1024));
   }
   // Register-staged form of the same loads: load_regs fetches the 16-byte
@@ -153,8 +152,7 @@ struct KMajorTile {
   u32x4_t reg[kPer];
   __device__ __forceinline__ void load_regs(int64_t k_byte) {
 #pragma unroll
-    for (int i = 0; i < kPer; ++i)
-      reg[i] = *reinterpret_cast<const u32x4_t*>(row_ptr[i] + k_byte + chunk_byte[i]);
+    for (int i = 0; i < kPer; ++i) reg[i] = *reinterpret_cast<const u32x4_t*>(row_ptr[i] + k_byte);
   }
   __device__ __forceinline__ void store_piece(lds_char* lds, int i) const {
     *reinterpret_cast<lds_u32x4_t*>(lds + (i * kNW + (threadIdx.x >> 6)) * 1024 + (threadIdx.x & 63) * 16) = reg[i];
