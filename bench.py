@@ -5,14 +5,19 @@
 
 Headline (`value`): decode tokens/s of an OLMo-2-1B-shaped decode step, batch
 64, through 12 augmented FFN layers whose 100352 x 8192 bf16 tables are all
-resident in HBM; one step runs every layer back to back (fused gate/up GEMM
-with the token-row gather in its epilogue, then the down-projection), captured
-once in a HIP graph and replayed.
+resident in HBM; one step runs every layer back to back (the packed decode
+gate/up kernel with the token-row gather in its epilogue, then the split-K
+down-projection and its sum), timed both as eager launches and as replays of
+one HIP graph; the faster is reported.
 
-Also reported (`train`): tokens/s of one OLMo-2-1B-shaped training micro-batch
-(32768 Zipf tokens) through one augmented layer: dedup, compact-row gather,
+Also reported: `train`, tokens/s of one OLMo-2-1B-shaped training micro-batch
+(32768 Zipf tokens) through one augmented layer (dedup, compact-row gather,
 forward, backward with the fp32 table-row segment-sum and all weight and input
-gradients.
+gradients, then AdamW on the touched table rows); `decode_stem`, `train_stem`,
+the same two workloads for the STEM layer (no up-projection).  With
+`--workloads`: `decode7b`, `train7b` (OLMo-2-7B shapes) and `offload` (tables in
+pinned host memory with a 5% HBM cache of the most frequent rows, decode and
+training, PCIe-inclusive).
 
 Every input is synthetic and seeded (staple_synth).  Inputs are resident in
 HBM before timing starts.  The CPU oracle is timed on a bounded sample of the

@@ -14,8 +14,9 @@
 // pattern, so the compute waves' load queue holds weights only.  A and B use
 // the same k order, so the contraction is unchanged.
 //
-// Gate/up: one workgroup per 32 features; each compute wave owns the gate and
-// up rows of 8 features over a part of d_model, the parts are folded in LDS,
+// Gate/up: one workgroup per 4 groups of 8 features (6 groups when d_ff has
+// more than four groups per CU); each compute wave owns the gate and up rows
+// of one group over a part of d_model, the parts are folded in LDS,
 // and the epilogue gathers each token's table row, forms u = W_up x + E[t]
 // and h = silu(W_gate x) * u (STAPLE abstract: the up-projection is retained
 // and the embedding added as a residual path; retrieval-path table: row

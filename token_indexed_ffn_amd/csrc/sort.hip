@@ -11,7 +11,9 @@
 // Dedup (STAPLE retrieval-path table, Prefill row: dedup once, one inverse
 // token map for every layer): key = (id << 32) | position.  After the sort,
 // a single-workgroup scan marks the first key of each ID run and writes the
-// unique IDs, segment offsets, sorted positions and the inverse map.
+// unique IDs, segment offsets, sorted positions and the inverse map.  A
+// decode batch (at most 64 positions) is sorted and scanned by one wave in
+// registers.
 //
 // Cache ranking (AI Radio episode on STAPLE: frequency-aware cache of about 5%
 // of the vocabulary): key = ((2^31-1 - count) << 32) | id, so ascending key
