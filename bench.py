@@ -347,7 +347,8 @@ def train_step(st, T, vocab, events=None):
     st.staple_ffn_down(fw["h"], T["w_down"], fw["y"])
     st.staple_ffn_bwd_table_grad(T["dy"], T["x"], T["w_gate"], T["w_up"], T["w_down"], fw["g"],
                                  fw["u"], fw["h"], dd["sorted_pos"], dd["seg_start"],
-                                 dd["n_unique"], out=T["bwd"], workspace=T["bwd_ws"])
+                                 dd["n_unique"], inv=dd["inv"], out=T["bwd"],
+                                 workspace=T["bwd_ws"])
 
 
 def run_train(torch, st, w, steps, warmup, stem=False):
@@ -665,7 +666,8 @@ def run_offload_train(torch, st, w, steps, warmup):
         st.staple_ffn_down(fw["h"], T["w_down"], fw["y"])
         st.staple_ffn_bwd_table_grad(T["dy"], T["x"], T["w_gate"], T["w_up"], T["w_down"], fw["g"],
                                      fw["u"], fw["h"], dd["sorted_pos"], dd["seg_start"],
-                                     dd["n_unique"], out=T["bwd"], workspace=T["bwd_ws"])
+                                     dd["n_unique"], inv=dd["inv"], out=T["bwd"],
+                                     workspace=T["bwd_ws"])
         return m
 
     def timed(mode):

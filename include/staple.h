@@ -455,7 +455,7 @@ staple_status_t staple_cache_refresh(const void* table, int64_t vocab, int64_t d
  * Backward of one augmented layer with the table-row gradient.
  *   dy [n_tokens x d_model] (dtype): upstream gradient of y.
  *   saved_g, saved_u, saved_h: the forward's save_g/save_u/save_h (required).
- *   sorted_pos, seg_start, n_unique: staple_dedup's outputs for this batch.
+ *   sorted_pos, inv, seg_start, n_unique: staple_dedup's outputs for this batch.
  * Outputs (each overwritten, not accumulated):
  *   d_rows [max_unique x d_ff] fp32: row u (< *n_unique) is the sum, over the
  *     positions holding token uniq[u], of dL/du at that position (a plain sum,
@@ -479,7 +479,8 @@ staple_status_t staple_ffn_bwd_table_grad(int64_t n_tokens, int64_t d_model, int
                                           const void* w_gate, const void* w_up, const void* w_down,
                                           const void* saved_g, const void* saved_u,
                                           const void* saved_h,
-                                          const int32_t* sorted_pos, const int32_t* seg_start,
+                                          const int32_t* sorted_pos, const int32_t* inv,
+                                          const int32_t* seg_start,
                                           const int32_t* n_unique, int64_t max_unique,
                                           float* d_rows, void* dx,
                                           float* dw_gate, float* dw_up, float* dw_down,

@@ -327,7 +327,8 @@ def _run_layer(st, dev, inp, out_f32=True, freeze_up=False, backward=True, full_
             }
         res["bwd"] = st.staple_ffn_bwd_table_grad(
             dy, x, wg, wu, wd, fwd["g"], fwd["u"], fwd["h"], dd["sorted_pos"], dd["seg_start"],
-            dd["n_unique"], freeze_up=freeze_up, out_dtype=torch.float32 if out_f32 else tdt,
+            dd["n_unique"], inv=dd["inv"], freeze_up=freeze_up,
+            out_dtype=torch.float32 if out_f32 else tdt,
             out=out)
     torch.cuda.synchronize()
     _no_device_error(st)
@@ -561,7 +562,8 @@ def test_empty_batch(st, dev):
     for k in ("g", "u", "h"):
         assert fwd[k].shape == (0, f)
     b = st.staple_ffn_bwd_table_grad(z, z, w, w, wd, fwd["g"], fwd["u"], fwd["h"],
-                                     dd["sorted_pos"], dd["seg_start"], dd["n_unique"])
+                                     dd["sorted_pos"], dd["seg_start"], dd["n_unique"],
+                                     inv=dd["inv"])
     torch.cuda.synchronize()
     assert int(dd["n_unique"].item()) == 0
     for k in ("dw_gate", "dw_up", "dw_down"):
@@ -616,7 +618,8 @@ def test_olmo1b_train_shape_sampled(st, dev):
                             out_dtype=torch.float32, save=True)
     bwd = st.staple_ffn_bwd_table_grad(t["dy"], t["x"], t["w_gate"], t["w_up"], t["w_down"],
                                        fwd["g"], fwd["u"], fwd["h"], dd["sorted_pos"],
-                                       dd["seg_start"], dd["n_unique"], out_dtype=torch.float32)
+                                       dd["seg_start"], dd["n_unique"], inv=dd["inv"],
+                                       out_dtype=torch.float32)
     torch.cuda.synchronize()
     _no_device_error(st)
     uniq, inv, sp, ss = O.dedup(ids)
@@ -796,7 +799,7 @@ def _run_stem(st, dev, inp, out_f32=True):
     }
     bwd = st.staple_ffn_bwd_table_grad(dy, x, wg, None, wd, fwd["g"], fwd["u"], fwd["h"],
                                        dd["sorted_pos"], dd["seg_start"], dd["n_unique"],
-                                       out_dtype=odt, out=out)
+                                       inv=dd["inv"], out_dtype=odt, out=out)
     torch.cuda.synchronize()
     _no_device_error(st)
     return fwd, bwd

@@ -478,13 +478,16 @@ def staple_ffn_bwd_table_grad(dy: torch.Tensor, x: torch.Tensor, w_gate: torch.T
                               saved_g: torch.Tensor,
                               saved_u: torch.Tensor, saved_h: torch.Tensor,
                               sorted_pos: torch.Tensor, seg_start: torch.Tensor,
-                              n_unique: torch.Tensor, *, max_unique: Optional[int] = None,
+                              n_unique: torch.Tensor, *, inv: torch.Tensor,
+                              max_unique: Optional[int] = None,
                               freeze_up: bool = False, out_dtype: Optional[torch.dtype] = None,
                               out: Optional[dict] = None, workspace: Optional[torch.Tensor] = None,
                               stream=None) -> dict:
     """Backward with the table-row gradient: d_rows, dx, dw_gate, dw_up, dw_down
-    (w_up None: the STEM layer, no dw_up)."""
-    _dev(dy, x, w_gate, w_up, w_down, saved_g, saved_u, saved_h, sorted_pos, seg_start, n_unique)
+    (w_up None: the STEM layer, no dw_up).  sorted_pos, inv, seg_start, n_unique are
+    staple_dedup's outputs for the batch."""
+    _dev(dy, x, w_gate, w_up, w_down, saved_g, saved_u, saved_h, sorted_pos, inv, seg_start,
+         n_unique)
     n, d = x.shape
     f = w_gate.shape[0]
     dt = _dt(x)
@@ -502,7 +505,8 @@ def staple_ffn_bwd_table_grad(dy: torch.Tensor, x: torch.Tensor, w_gate: torch.T
     ws = _ws(lib().staple_ffn_bwd_workspace_bytes(n, d, f, dt), workspace, dev)
     _check(lib().staple_ffn_bwd_table_grad(
         n, d, f, dt, _DT[out["dx"].dtype], _p(dy), _p(x), _p(w_gate), _p(w_up), _p(w_down),
-        _p(saved_g), _p(saved_u), _p(saved_h), _p(sorted_pos), _p(seg_start), _p(n_unique), mu,
+        _p(saved_g), _p(saved_u), _p(saved_h), _p(sorted_pos), _p(inv), _p(seg_start),
+        _p(n_unique), mu,
         _p(out["d_rows"]), _p(out["dx"]), _p(out["dw_gate"]), _p(out.get("dw_up")),
         _p(out["dw_down"]), int(bool(freeze_up)), _p(ws), _ws_size(ws), _stream(stream)),
         "staple_ffn_bwd_table_grad")

@@ -67,8 +67,9 @@ _SIGS = {
                                      c_vp]),
     "staple_ffn_bwd_workspace_bytes": (c_sz, [c_i64, c_i64, c_i64, c_i32]),
     "staple_ffn_bwd_table_grad": (c_i32, [c_i64, c_i64, c_i64, c_i32, c_i32, c_vp, c_vp, c_vp,
-                                          c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_i64,
-                                          c_vp, c_vp, c_vp, c_vp, c_vp, c_i32, c_vp, c_sz, c_vp]),
+                                          c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp,
+                                          c_i64, c_vp, c_vp, c_vp, c_vp, c_vp, c_i32, c_vp, c_sz,
+                                          c_vp]),
 }
 
 EXPORTED = tuple(_SIGS)

@@ -51,7 +51,8 @@ hipError_t launch_assemble_rows_layers(const LayerRowSources& src, int n_layers,
 size_t segment_sum_workspace_bytes(int64_t n_tokens, int64_t d_ff);
 hipError_t launch_segment_sum(int dtype, const void* du, int64_t du_ld, int64_t du_col,
                               int64_t n_tokens, int64_t d_ff, const int32_t* sorted_pos,
-                              const int32_t* seg_start, const int32_t* n_unique,
+                              const int32_t* inv, const int32_t* seg_start,
+                              const int32_t* n_unique,
                               int64_t max_unique, float* d_rows, void* ws, hipStream_t s, int* err);
 // kernels (gemm.hip)
 template <typename T>
@@ -691,7 +692,8 @@ size_t staple_ffn_bwd_workspace_bytes(int64_t n, int64_t d, int64_t f, int32_t d
 staple_status_t staple_ffn_bwd_table_grad(
     int64_t n, int64_t d, int64_t f, int32_t dtype, int32_t out_dtype, const void* dy,
     const void* x, const void* w_gate, const void* w_up, const void* w_down, const void* saved_g,
-    const void* saved_u, const void* saved_h, const int32_t* sorted_pos, const int32_t* seg_start,
+    const void* saved_u, const void* saved_h, const int32_t* sorted_pos, const int32_t* inv,
+    const int32_t* seg_start,
     const int32_t* n_unique, int64_t max_unique, float* d_rows, void* dx, float* dw_gate,
     float* dw_up, float* dw_down, int32_t freeze_up, void* ws, size_t ws_bytes, void* stream) {
   if (!valid_dtype(dtype) || !valid_dtype(out_dtype)) return STAPLE_ERR_UNSUPPORTED;
@@ -703,7 +705,7 @@ staple_status_t staple_ffn_bwd_table_grad(
   REQUIRE(aligned16(w_gate) && (!w_up || aligned16(w_up)) && aligned16(w_down) &&
           aligned16(dw_gate) && aligned16(dw_down) && (fz || aligned16(dw_up)));
   if (n > 0) {
-    REQUIRE(dy && x && saved_g && saved_u && saved_h && sorted_pos && d_rows && dx);
+    REQUIRE(dy && x && saved_g && saved_u && saved_h && sorted_pos && inv && d_rows && dx);
     REQUIRE(aligned16(dy) && aligned16(x) && aligned16(saved_g) && aligned16(saved_u) &&
             aligned16(saved_h) && aligned16(dx) && aligned16(d_rows));
     if (ws_bytes < staple_ffn_bwd_workspace_bytes(n, d, f, dtype)) return STAPLE_ERR_WORKSPACE;
@@ -716,7 +718,7 @@ staple_status_t staple_ffn_bwd_table_grad(
   if (dtype == STAPLE_BF16) {
     HIPCALL(dh_act<bf16_t>(n, d, f, dy, w_down, saved_g, saved_u, dgu, s));
     if (n > 0)
-      HIPCALL(launch_segment_sum(dtype, dgu, 2 * f, f, n, f, sorted_pos, seg_start, n_unique,
+      HIPCALL(launch_segment_sum(dtype, dgu, 2 * f, f, n, f, sorted_pos, inv, seg_start, n_unique,
                                  max_unique, d_rows, seg_ws, s, err));
     HIPCALL(dwdown_bwd<bf16_t>(n, d, f, dy, saved_h, dw_down, s));
     HIPCALL(dwgu_bwd<bf16_t>(n, d, f, dgu, x, dw_gate, dw_up, fz, s));
@@ -724,7 +726,7 @@ staple_status_t staple_ffn_bwd_table_grad(
   } else {
     HIPCALL(dh_act<float>(n, d, f, dy, w_down, saved_g, saved_u, dgu, s));
     if (n > 0)
-      HIPCALL(launch_segment_sum(dtype, dgu, 2 * f, f, n, f, sorted_pos, seg_start, n_unique,
+      HIPCALL(launch_segment_sum(dtype, dgu, 2 * f, f, n, f, sorted_pos, inv, seg_start, n_unique,
                                  max_unique, d_rows, seg_ws, s, err));
     HIPCALL(dwdown_bwd<float>(n, d, f, dy, saved_h, dw_down, s));
     HIPCALL(dwgu_bwd<float>(n, d, f, dgu, x, dw_gate, dw_up, fz, s));

@@ -55,12 +55,78 @@ __host__ __device__ __forceinline__ void adamw_element(float& p, float& m, float
 // ---------------------------------------------------------------------------
 constexpr int kAdamThreads = 256;
 
+// One 8-element piece of a row: parameters, moments and gradient in fp32.
+struct AdamPiece {
+  float p[8], m[8], v[8], g[8];
+};
+
+template <typename PT>
+__device__ __forceinline__ void adam_load(const PT* table, const float* m, const float* v,
+                                          const float* grad, int64_t pe, int64_t ge, AdamPiece& x) {
+  const float4* mp = reinterpret_cast<const float4*>(m + pe);
+  const float4* vp = reinterpret_cast<const float4*>(v + pe);
+  const float4* gp = reinterpret_cast<const float4*>(grad + ge);
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const float4 a = mp[h], b = vp[h], q = gp[h];
+    x.m[4 * h] = a.x; x.m[4 * h + 1] = a.y; x.m[4 * h + 2] = a.z; x.m[4 * h + 3] = a.w;
+    x.v[4 * h] = b.x; x.v[4 * h + 1] = b.y; x.v[4 * h + 2] = b.z; x.v[4 * h + 3] = b.w;
+    x.g[4 * h] = q.x; x.g[4 * h + 1] = q.y; x.g[4 * h + 2] = q.z; x.g[4 * h + 3] = q.w;
+  }
+  if constexpr (sizeof(PT) == 2) {
+    const uint4 raw = *reinterpret_cast<const uint4*>(table + pe);
+    const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      x.p[2 * i] = __uint_as_float(w[i] << 16);
+      x.p[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+    }
+  } else {
+    const float4* pp = reinterpret_cast<const float4*>(table + pe);
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const float4 a = pp[h];
+      x.p[4 * h] = a.x; x.p[4 * h + 1] = a.y; x.p[4 * h + 2] = a.z; x.p[4 * h + 3] = a.w;
+    }
+  }
+}
+
+template <typename PT>
+__device__ __forceinline__ void adam_update_store(PT* table, float* m, float* v, int64_t pe,
+                                                  AdamPiece& x, const AdamWConsts& c) {
+#pragma unroll
+  for (int i = 0; i < 8; ++i) adamw_element(x.p[i], x.m[i], x.v[i], x.g[i], c);
+  float4* mo = reinterpret_cast<float4*>(m + pe);
+  float4* vo = reinterpret_cast<float4*>(v + pe);
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    mo[h] = make_float4(x.m[4 * h], x.m[4 * h + 1], x.m[4 * h + 2], x.m[4 * h + 3]);
+    vo[h] = make_float4(x.v[4 * h], x.v[4 * h + 1], x.v[4 * h + 2], x.v[4 * h + 3]);
+  }
+  if constexpr (sizeof(PT) == 2) {
+    uint4 o;
+    o.x = f32_to_bf16(x.p[0]) | (static_cast<uint32_t>(f32_to_bf16(x.p[1])) << 16);
+    o.y = f32_to_bf16(x.p[2]) | (static_cast<uint32_t>(f32_to_bf16(x.p[3])) << 16);
+    o.z = f32_to_bf16(x.p[4]) | (static_cast<uint32_t>(f32_to_bf16(x.p[5])) << 16);
+    o.w = f32_to_bf16(x.p[6]) | (static_cast<uint32_t>(f32_to_bf16(x.p[7])) << 16);
+    *reinterpret_cast<uint4*>(table + pe) = o;
+  } else {
+    float4* po = reinterpret_cast<float4*>(table + pe);
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+      po[h] = make_float4(x.p[4 * h], x.p[4 * h + 1], x.p[4 * h + 2], x.p[4 * h + 3]);
+  }
+}
+
+// Two pieces per thread are loaded before either is updated, so each thread
+// keeps twice the loads in flight.
 template <typename PT>
 __global__ __launch_bounds__(kAdamThreads) void adamw_rows_kernel(
     PT* __restrict__ table, float* __restrict__ m, float* __restrict__ v, int64_t vocab,
     int64_t d_ff, const int32_t* __restrict__ rows, const int32_t* __restrict__ n_rows_p,
     int64_t max_rows, const float* __restrict__ grad, AdamWConsts c, int* err) {
   const int64_t n = n_rows_p ? min(static_cast<int64_t>(*n_rows_p), max_rows) : max_rows;
+  constexpr int64_t kPass = kAdamThreads * 8;
   for (int64_t k = blockIdx.x; k < n; k += gridDim.x) {
     const int32_t r = rows[k];
     if (r < 0 || r >= vocab) {
@@ -68,56 +134,14 @@ __global__ __launch_bounds__(kAdamThreads) void adamw_rows_kernel(
       continue;
     }
     const int64_t base = static_cast<int64_t>(r) * d_ff;
-    for (int64_t e = static_cast<int64_t>(threadIdx.x) * 8; e < d_ff; e += kAdamThreads * 8) {
-      float pv[8], mv[8], vv[8], gv[8];
-      const float4* mp = reinterpret_cast<const float4*>(m + base + e);
-      const float4* vp = reinterpret_cast<const float4*>(v + base + e);
-      const float4* gp = reinterpret_cast<const float4*>(grad + k * d_ff + e);
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const float4 a = mp[h], b = vp[h], q = gp[h];
-        mv[4 * h] = a.x; mv[4 * h + 1] = a.y; mv[4 * h + 2] = a.z; mv[4 * h + 3] = a.w;
-        vv[4 * h] = b.x; vv[4 * h + 1] = b.y; vv[4 * h + 2] = b.z; vv[4 * h + 3] = b.w;
-        gv[4 * h] = q.x; gv[4 * h + 1] = q.y; gv[4 * h + 2] = q.z; gv[4 * h + 3] = q.w;
-      }
-      if constexpr (sizeof(PT) == 2) {
-        const uint4 raw = *reinterpret_cast<const uint4*>(table + base + e);
-        const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          pv[2 * i] = __uint_as_float(w[i] << 16);
-          pv[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
-        }
-      } else {
-        const float4* pp = reinterpret_cast<const float4*>(table + base + e);
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          const float4 a = pp[h];
-          pv[4 * h] = a.x; pv[4 * h + 1] = a.y; pv[4 * h + 2] = a.z; pv[4 * h + 3] = a.w;
-        }
-      }
-#pragma unroll
-      for (int i = 0; i < 8; ++i) adamw_element(pv[i], mv[i], vv[i], gv[i], c);
-      float4* mo = reinterpret_cast<float4*>(m + base + e);
-      float4* vo = reinterpret_cast<float4*>(v + base + e);
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        mo[h] = make_float4(mv[4 * h], mv[4 * h + 1], mv[4 * h + 2], mv[4 * h + 3]);
-        vo[h] = make_float4(vv[4 * h], vv[4 * h + 1], vv[4 * h + 2], vv[4 * h + 3]);
-      }
-      if constexpr (sizeof(PT) == 2) {
-        uint4 o;
-        o.x = f32_to_bf16(pv[0]) | (static_cast<uint32_t>(f32_to_bf16(pv[1])) << 16);
-        o.y = f32_to_bf16(pv[2]) | (static_cast<uint32_t>(f32_to_bf16(pv[3])) << 16);
-        o.z = f32_to_bf16(pv[4]) | (static_cast<uint32_t>(f32_to_bf16(pv[5])) << 16);
-        o.w = f32_to_bf16(pv[6]) | (static_cast<uint32_t>(f32_to_bf16(pv[7])) << 16);
-        *reinterpret_cast<uint4*>(table + base + e) = o;
-      } else {
-        float4* po = reinterpret_cast<float4*>(table + base + e);
-#pragma unroll
-        for (int h = 0; h < 2; ++h)
-          po[h] = make_float4(pv[4 * h], pv[4 * h + 1], pv[4 * h + 2], pv[4 * h + 3]);
-      }
+    const int64_t gbase = k * d_ff;
+    for (int64_t e = static_cast<int64_t>(threadIdx.x) * 8; e < d_ff; e += 2 * kPass) {
+      const bool two = e + kPass < d_ff;
+      AdamPiece a, b;
+      adam_load(table, m, v, grad, base + e, gbase + e, a);
+      if (two) adam_load(table, m, v, grad, base + e + kPass, gbase + e + kPass, b);
+      adam_update_store(table, m, v, base + e, a, c);
+      if (two) adam_update_store(table, m, v, base + e + kPass, b, c);
     }
   }
 }

@@ -360,7 +360,9 @@ hipError_t launch_assemble_rows_layers(const LayerRowSources& src, int n_layers,
 //
 // Token frequencies are Zipf-skewed (one ID can hold ~13% of a batch), so the
 // work is split over fixed chunks of kSegChunk sorted positions rather than
-// over segments.  Pass 1: one wave per (chunk, 512 columns) walks its
+// over segments (one wave per (chunk, 512 columns), four waves of
+// neighbouring column blocks per workgroup, the column blocks of a chunk
+// dispatched together so its du rows are read whole within a short time).  Pass 1: each wave walks its
 // positions in order; a segment that starts and ends inside the chunk is
 // written to d_rows directly; the run of a segment that began in an earlier
 // chunk goes to first[chunk], the run of a segment that continues into the
@@ -373,6 +375,9 @@ hipError_t launch_assemble_rows_layers(const LayerRowSources& src, int n_layers,
 // ---------------------------------------------------------------------------
 constexpr int kSegChunk = 32;
 constexpr int kSegCols = 512;   // 64 lanes x 8 columns
+constexpr int kSegAhead = 8;    // du rows in flight per lane (chunk pass)
+constexpr int kFixAhead = 8;    // partials in flight per lane (fixup pass)
+constexpr int kSegWaves = 4;    // column blocks per workgroup (one wave each)
 
 template <typename T>
 __device__ __forceinline__ void load8(const T* p, float (&v)[8]);
@@ -401,53 +406,90 @@ __device__ __forceinline__ void store8f(float* p, const float (&v)[8]) {
   *reinterpret_cast<float4*>(p + 4) = make_float4(v[4], v[5], v[6], v[7]);
 }
 
+// Segment of sorted position p: the inverse map of its token (two loads; an
+// out-of-range entry sets the error word and counts as segment 0).
+__device__ __forceinline__ int64_t segment_of(int64_t p, int64_t n_tokens, int64_t nu,
+                                              const int32_t* sorted_pos, const int32_t* inv,
+                                              int* err) {
+  const int32_t t = sorted_pos[p];
+  if (t < 0 || t >= n_tokens) {
+    flag_index_error(err);
+    return 0;
+  }
+  const int32_t s = inv[t];
+  if (s < 0 || s >= nu) {
+    flag_index_error(err);
+    return 0;
+  }
+  return s;
+}
+
 template <typename T>
-__global__ __launch_bounds__(64) void segsum_chunk_kernel(
+__global__ __launch_bounds__(64 * kSegWaves) void segsum_chunk_kernel(
     const T* __restrict__ du, int64_t du_ld, int64_t du_col, int64_t n_tokens, int64_t d_ff,
-    const int32_t* __restrict__ sorted_pos, const int32_t* __restrict__ seg_start,
-    const int32_t* __restrict__ n_unique_p, float* __restrict__ d_rows, float* __restrict__ first,
-    float* __restrict__ last, int* err) {
-  const int lane = threadIdx.x;
-  const int64_t c = blockIdx.x;
-  const int64_t col = static_cast<int64_t>(blockIdx.y) * kSegCols + lane * 8;
+    const int32_t* __restrict__ sorted_pos, const int32_t* __restrict__ inv,
+    const int32_t* __restrict__ seg_start, const int32_t* __restrict__ n_unique_p,
+    float* __restrict__ d_rows, float* __restrict__ first, float* __restrict__ last, int* err) {
+  const int lane = threadIdx.x & 63;
+  const int64_t c = blockIdx.y;
+  const int64_t col = (static_cast<int64_t>(blockIdx.x) * kSegWaves + (threadIdx.x >> 6)) * kSegCols +
+                      lane * 8;
   const int64_t p0 = c * kSegChunk;
   const int64_t p1 = min(p0 + kSegChunk, n_tokens);
   const int64_t nu = *n_unique_p;
-  if (col >= d_ff || nu <= 0) return;
-  // segment holding p0: largest s with seg_start[s] <= p0
-  int64_t lo = 0, hi = nu - 1;
-  while (lo < hi) {
-    const int64_t mid = (lo + hi + 1) >> 1;
-    if (seg_start[mid] <= p0) lo = mid; else hi = mid - 1;
-  }
-  int64_t sg = lo;
+  // whole waves past d_ff leave; inside a wave every lane stays for the row
+  // exchange and only lanes with col < d_ff load and store
+  if (col - lane * 8 >= d_ff || nu <= 0) return;
+  const bool col_ok = col < d_ff;
+  const int64_t lcol = col_ok ? col : 0;
+  int64_t sg = segment_of(p0, n_tokens, nu, sorted_pos, inv, err);
   int64_t s_begin = seg_start[sg], s_end = seg_start[sg + 1];
   float acc[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) acc[i] = 0.0f;
-  for (int64_t p = p0; p < p1; ++p) {
-    int64_t row = sorted_pos[p];
-    if (row < 0 || row >= n_tokens) {
-      flag_index_error(err);
-      row = 0;
+  // the chunk's rows: lane i holds the row of position p0 + i % 32
+  static_assert(kSegChunk <= 64, "one position per lane");
+  int32_t my_row = 0;
+  {
+    const int64_t p = p0 + (lane % kSegChunk);
+    if (p < p1) {
+      my_row = sorted_pos[p];
+      if (my_row < 0 || my_row >= n_tokens) {
+        flag_index_error(err);
+        my_row = 0;
+      }
     }
-    float v[8];
-    load8<T>(du + row * du_ld + du_col + col, v);
+  }
+  // positions in groups of kSegAhead: the group's rows are loaded together,
+  // then added in position order (the order of the sums does not change)
+  for (int64_t pb = p0; pb < p1; pb += kSegAhead) {
+    float v[kSegAhead][8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) acc[i] += v[i];
-    const bool seg_ends = (p + 1 == s_end);
-    if (seg_ends || p + 1 == p1) {
-      float* dst;
-      if (s_begin >= p0 && s_end <= p1) dst = d_rows + sg * d_ff + col;   // whole segment here
-      else if (s_begin < p0) dst = first + c * d_ff + col;                // began in an earlier chunk
-      else dst = last + c * d_ff + col;                                   // continues past p1
-      store8f(dst, acc);
+    for (int j = 0; j < kSegAhead; ++j) {
+      const int64_t p = pb + j < p1 ? pb + j : p1 - 1;
+      const int64_t row = __shfl(my_row, static_cast<int>(p - p0), 64);
+      load8<T>(du + row * du_ld + du_col + lcol, v[j]);
+    }
 #pragma unroll
-      for (int i = 0; i < 8; ++i) acc[i] = 0.0f;
-      if (seg_ends && sg + 1 < nu) {
-        ++sg;
-        s_begin = s_end;
-        s_end = seg_start[sg + 1];
+    for (int j = 0; j < kSegAhead; ++j) {
+      const int64_t p = pb + j;
+      if (p >= p1) break;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc[i] += v[j][i];
+      const bool seg_ends = (p + 1 == s_end);
+      if (seg_ends || p + 1 == p1) {
+        float* dst;
+        if (s_begin >= p0 && s_end <= p1) dst = d_rows + sg * d_ff + col;   // whole segment here
+        else if (s_begin < p0) dst = first + c * d_ff + col;                // began in an earlier chunk
+        else dst = last + c * d_ff + col;                                   // continues past p1
+        if (col_ok) store8f(dst, acc);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc[i] = 0.0f;
+        if (seg_ends && sg + 1 < nu) {
+          ++sg;
+          s_begin = s_end;
+          s_end = seg_start[sg + 1];
+        }
       }
     }
   }
@@ -455,32 +497,39 @@ __global__ __launch_bounds__(64) void segsum_chunk_kernel(
 
 // One wave per (chunk, 512 columns): the chunk whose last run starts a
 // segment that continues past it owns that segment's final sum.
-__global__ __launch_bounds__(64) void segsum_fixup_kernel(
-    int64_t n_tokens, int64_t d_ff, const int32_t* __restrict__ seg_start,
+__global__ __launch_bounds__(64 * kSegWaves) void segsum_fixup_kernel(
+    int64_t n_tokens, int64_t d_ff, const int32_t* __restrict__ sorted_pos,
+    const int32_t* __restrict__ inv, const int32_t* __restrict__ seg_start,
     const int32_t* __restrict__ n_unique_p, const float* __restrict__ first,
-    const float* __restrict__ last, float* __restrict__ d_rows) {
-  const int64_t c0 = blockIdx.x;
-  const int64_t col = static_cast<int64_t>(blockIdx.y) * kSegCols + threadIdx.x * 8;
+    const float* __restrict__ last, float* __restrict__ d_rows, int* err) {
+  const int64_t c0 = blockIdx.y;
+  const int64_t col = (static_cast<int64_t>(blockIdx.x) * kSegWaves + (threadIdx.x >> 6)) * kSegCols +
+                      (threadIdx.x & 63) * 8;
   const int64_t nu = *n_unique_p;
   if (col >= d_ff || nu <= 0) return;
   const int64_t p0 = c0 * kSegChunk;
   const int64_t p1 = min(p0 + kSegChunk, n_tokens);
-  // segment holding position p1 - 1
-  int64_t lo = 0, hi = nu - 1;
-  while (lo < hi) {
-    const int64_t mid = (lo + hi + 1) >> 1;
-    if (seg_start[mid] <= p1 - 1) lo = mid; else hi = mid - 1;
-  }
+  const int64_t lo = segment_of(p1 - 1, n_tokens, nu, sorted_pos, inv, err);
   const int64_t b = seg_start[lo], e = seg_start[lo + 1];
   if (b < p0 || e <= p1) return;   // not a segment that starts here and continues
   const int64_t c1 = (e - 1) / kSegChunk;
   float acc[8];
   load8<float>(last + c0 * d_ff + col, acc);
-  for (int64_t c = c0 + 1; c <= c1; ++c) {
-    float v[8];
-    load8<float>(first + c * d_ff + col, v);
+  // kFixAhead partials loaded together, added in chunk order
+  for (int64_t cb = c0 + 1; cb <= c1; cb += kFixAhead) {
+    float v[kFixAhead][8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) acc[i] += v[i];
+    for (int j = 0; j < kFixAhead; ++j) {
+      const int64_t c = cb + j <= c1 ? cb + j : c1;
+      load8<float>(first + c * d_ff + col, v[j]);
+    }
+#pragma unroll
+    for (int j = 0; j < kFixAhead; ++j) {
+      if (cb + j <= c1) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc[i] += v[j][i];
+      }
+    }
   }
   store8f(d_rows + lo * d_ff + col, acc);
 }
@@ -492,23 +541,24 @@ size_t segment_sum_workspace_bytes(int64_t n_tokens, int64_t d_ff) {
 
 hipError_t launch_segment_sum(int dtype, const void* du, int64_t du_ld, int64_t du_col,
                               int64_t n_tokens, int64_t d_ff, const int32_t* sorted_pos,
-                              const int32_t* seg_start, const int32_t* n_unique,
+                              const int32_t* inv, const int32_t* seg_start,
+                              const int32_t* n_unique,
                               int64_t max_unique, float* d_rows, void* ws, hipStream_t s, int* err) {
   if (max_unique == 0 || n_tokens == 0) return hipSuccess;
   const int64_t chunks = (n_tokens + kSegChunk - 1) / kSegChunk;
   float* first = static_cast<float*>(ws);
   float* last = first + chunks * d_ff;
-  const unsigned cb = static_cast<unsigned>((d_ff + kSegCols - 1) / kSegCols);
+  const unsigned cb = static_cast<unsigned>((d_ff + kSegCols * kSegWaves - 1) / (kSegCols * kSegWaves));
   if (dtype == STAPLE_BF16)
-    segsum_chunk_kernel<bf16_t><<<dim3(static_cast<unsigned>(chunks), cb), dim3(64), 0, s>>>(
-        static_cast<const bf16_t*>(du), du_ld, du_col, n_tokens, d_ff, sorted_pos, seg_start,
+    segsum_chunk_kernel<bf16_t><<<dim3(cb, static_cast<unsigned>(chunks)), dim3(64 * kSegWaves), 0, s>>>(
+        static_cast<const bf16_t*>(du), du_ld, du_col, n_tokens, d_ff, sorted_pos, inv, seg_start,
         n_unique, d_rows, first, last, err);
   else
-    segsum_chunk_kernel<float><<<dim3(static_cast<unsigned>(chunks), cb), dim3(64), 0, s>>>(
-        static_cast<const float*>(du), du_ld, du_col, n_tokens, d_ff, sorted_pos, seg_start,
+    segsum_chunk_kernel<float><<<dim3(cb, static_cast<unsigned>(chunks)), dim3(64 * kSegWaves), 0, s>>>(
+        static_cast<const float*>(du), du_ld, du_col, n_tokens, d_ff, sorted_pos, inv, seg_start,
         n_unique, d_rows, first, last, err);
-  segsum_fixup_kernel<<<dim3(static_cast<unsigned>(chunks), cb), dim3(64), 0, s>>>(
-      n_tokens, d_ff, seg_start, n_unique, first, last, d_rows);
+  segsum_fixup_kernel<<<dim3(cb, static_cast<unsigned>(chunks)), dim3(64 * kSegWaves), 0, s>>>(
+      n_tokens, d_ff, sorted_pos, inv, seg_start, n_unique, first, last, d_rows, err);
   return hipGetLastError();
 }
 
