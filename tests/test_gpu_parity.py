@@ -602,14 +602,16 @@ def _device_inputs(dev, w, n_tokens, seed_base=0):
     return ids, t
 
 
-def test_olmo1b_train_shape_sampled(st, dev):
-    """32768 Zipf tokens, d_model 2048, d_ff 8192, vocab 100352, bf16: every
+@pytest.mark.parametrize("wname", ["olmo1b", "olmo7b"])
+def test_olmo_train_shape_sampled(st, dev, wname):
+    """The training batch at full size, bf16 (1B: 32768 Zipf tokens, d_model
+    2048, d_ff 8192; 7B: 16384 tokens, 4096, 11008; vocab 100352): every
     integer output in full; y, dx on sampled tokens and d_rows, dW on sampled
     features, each computed by the oracle over the whole batch."""
     import torch
-    w = S.OLMO1B_TRAIN
+    w = {"olmo1b": S.OLMO1B_TRAIN, "olmo7b": S.OLMO7B_TRAIN}[wname]
     n, d, f = w.n_tokens, w.d_model, w.d_ff
-    _log("olmo1b train-shape sampled parity")
+    _log(f"{wname} train-shape sampled parity")
     ids, t = _device_inputs(dev, w, n)
     idt = torch.from_numpy(ids).to(dev)
     dd = st.staple_dedup(idt, w.vocab)
@@ -649,12 +651,15 @@ def test_olmo1b_train_shape_sampled(st, dev):
     assert_close_long_sum(f64(bwd["dw_down"][:, cs]), ob_c["dw_down"], "dw_down[:, cols]")
 
 
-def test_olmo1b_decode_layer_full(st, dev):
-    """Decode batch of 64 over a full 100352 x 8192 table in HBM, rows gathered
-    by token ID inside the fused epilogue; every output compared."""
+@pytest.mark.parametrize("wname", ["olmo1b", "olmo7b"])
+def test_olmo_decode_layer_full(st, dev, wname):
+    """Decode batch of 64 over a full 100352 x d_ff table in HBM (1B: d_model
+    2048, d_ff 8192; 7B: 4096, 11008), rows gathered by token ID inside the
+    fused epilogue; every output compared, and the packed serving layout gives
+    the same bits."""
     import torch
-    w = S.OLMO1B_DECODE
-    _log("olmo1b decode layer")
+    w = {"olmo1b": S.OLMO1B_DECODE, "olmo7b": S.OLMO7B_DECODE}[wname]
+    _log(f"{wname} decode layer")
     ids, t = _device_inputs(dev, w, w.n_tokens)
     idt = torch.from_numpy(ids).to(dev)
     fwd = st.staple_ffn_fwd(t["x"], t["w_gate"], t["w_up"], t["w_down"], t["table"], idt,
