@@ -48,12 +48,19 @@ __device__ __forceinline__ float bf16_to_f32(uint16_t b) {
   return __uint_as_float(static_cast<uint32_t>(b) << 16);
 }
 
-// float -> bfloat16, round to nearest, ties to even (finite inputs; NaN stays NaN).
+// Two floats -> two bfloat16 (lo in bits 0-15), rounded to nearest with ties
+// to even (NaN stays NaN), by gfx950's packed conversion (one
+// v_cvt_pk_bf16_f32 per pair instead of an integer rounding sequence per
+// element).
+typedef float cvt_f32x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 cvt_bf16x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  const cvt_f32x2_t v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, cvt_bf16x2_t));
+}
+
 __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<uint16_t>((u >> 16) | 0x40u);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return static_cast<uint16_t>(u >> 16);
+  return static_cast<uint16_t>(pack_bf16x2(f, 0.0f));
 }
 
 // Element access for the two storage types.
@@ -80,7 +87,9 @@ template <> struct Elem<bf16_t> {
   __device__ __forceinline__ static float quantize(float v) { return bf16_to_f32(f32_to_bf16(v)); }
 };
 
-__device__ __forceinline__ float sigmoidf_(float z) { return 1.0f / (1.0f + __expf(-z)); }
+// 1 / (1 + e^-z) with the hardware exponential and reciprocal (v_rcp_f32,
+// about 1 ulp) rather than an IEEE division.
+__device__ __forceinline__ float sigmoidf_(float z) { return __builtin_amdgcn_rcpf(1.0f + __expf(-z)); }
 
 // Kernels that meet an out-of-range ID or index OR this bit into the
 // per-device error word whose address they receive as `err`.

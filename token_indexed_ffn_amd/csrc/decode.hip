@@ -337,10 +337,10 @@ __global__ __launch_bounds__(64 * (G + 1) * KH) void decode_gateup_kernel(
   }
   auto pack = [](const float* v) {
     uint4 o;
-    o.x = static_cast<uint32_t>(f32_to_bf16(v[0])) | (static_cast<uint32_t>(f32_to_bf16(v[1])) << 16);
-    o.y = static_cast<uint32_t>(f32_to_bf16(v[2])) | (static_cast<uint32_t>(f32_to_bf16(v[3])) << 16);
-    o.z = static_cast<uint32_t>(f32_to_bf16(v[4])) | (static_cast<uint32_t>(f32_to_bf16(v[5])) << 16);
-    o.w = static_cast<uint32_t>(f32_to_bf16(v[6])) | (static_cast<uint32_t>(f32_to_bf16(v[7])) << 16);
+    o.x = pack_bf16x2(v[0], v[1]);
+    o.y = pack_bf16x2(v[2], v[3]);
+    o.z = pack_bf16x2(v[4], v[5]);
+    o.w = pack_bf16x2(v[6], v[7]);
     return o;
   };
   const int64_t o = tok * f + f0;
@@ -419,8 +419,8 @@ __global__ void decode_down_reduce_kernel(int64_t count, int ksplit, const float
     *reinterpret_cast<float4*>(reinterpret_cast<float*>(y) + i) = s;
   } else {
     uint2 o;
-    o.x = static_cast<uint32_t>(f32_to_bf16(s.x)) | (static_cast<uint32_t>(f32_to_bf16(s.y)) << 16);
-    o.y = static_cast<uint32_t>(f32_to_bf16(s.z)) | (static_cast<uint32_t>(f32_to_bf16(s.w)) << 16);
+    o.x = pack_bf16x2(s.x, s.y);
+    o.y = pack_bf16x2(s.z, s.w);
     *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(y) + i) = o;
   }
 }

@@ -516,10 +516,10 @@ template <typename T>
 __device__ __forceinline__ void store8g(void* base, int64_t idx, const float (&v)[8]) {
   if constexpr (sizeof(T) == 2) {
     uint4 q;
-    q.x = static_cast<uint32_t>(f32_to_bf16(v[0])) | (static_cast<uint32_t>(f32_to_bf16(v[1])) << 16);
-    q.y = static_cast<uint32_t>(f32_to_bf16(v[2])) | (static_cast<uint32_t>(f32_to_bf16(v[3])) << 16);
-    q.z = static_cast<uint32_t>(f32_to_bf16(v[4])) | (static_cast<uint32_t>(f32_to_bf16(v[5])) << 16);
-    q.w = static_cast<uint32_t>(f32_to_bf16(v[6])) | (static_cast<uint32_t>(f32_to_bf16(v[7])) << 16);
+    q.x = pack_bf16x2(v[0], v[1]);
+    q.y = pack_bf16x2(v[2], v[3]);
+    q.z = pack_bf16x2(v[4], v[5]);
+    q.w = pack_bf16x2(v[6], v[7]);
     *reinterpret_cast<uint4*>(static_cast<uint16_t*>(base) + idx) = q;
   } else {
     float* p = static_cast<float*>(base) + idx;

@@ -105,10 +105,10 @@ __device__ __forceinline__ void adam_update_store(PT* table, float* m, float* v,
   }
   if constexpr (sizeof(PT) == 2) {
     uint4 o;
-    o.x = f32_to_bf16(x.p[0]) | (static_cast<uint32_t>(f32_to_bf16(x.p[1])) << 16);
-    o.y = f32_to_bf16(x.p[2]) | (static_cast<uint32_t>(f32_to_bf16(x.p[3])) << 16);
-    o.z = f32_to_bf16(x.p[4]) | (static_cast<uint32_t>(f32_to_bf16(x.p[5])) << 16);
-    o.w = f32_to_bf16(x.p[6]) | (static_cast<uint32_t>(f32_to_bf16(x.p[7])) << 16);
+    o.x = pack_bf16x2(x.p[0], x.p[1]);
+    o.y = pack_bf16x2(x.p[2], x.p[3]);
+    o.z = pack_bf16x2(x.p[4], x.p[5]);
+    o.w = pack_bf16x2(x.p[6], x.p[7]);
     *reinterpret_cast<uint4*>(table + pe) = o;
   } else {
     float4* po = reinterpret_cast<float4*>(table + pe);
