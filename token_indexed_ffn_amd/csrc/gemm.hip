@@ -497,6 +497,38 @@ __device__ __forceinline__ void read8(const float* p, float (&v)[8]) {
   v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w; v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
 }
 
+// Eight elements of T kept as loaded (bf16: one 16-byte vector), so that a
+// load can be issued well before its values are used.
+template <typename T>
+struct Raw8 {
+  uint4 q[sizeof(T) / 2];
+};
+
+template <typename T>
+__device__ __forceinline__ Raw8<T> raw_load8(const void* base, int64_t idx) {
+  Raw8<T> r;
+  const uint4* src = reinterpret_cast<const uint4*>(static_cast<const T*>(base) + idx);
+#pragma unroll
+  for (int i = 0; i < static_cast<int>(sizeof(T) / 2); ++i) r.q[i] = src[i];
+  return r;
+}
+
+template <typename T>
+__device__ __forceinline__ void raw_unpack8(const Raw8<T>& r, float (&v)[8]) {
+  if constexpr (sizeof(T) == 2) {
+    const uint32_t w[4] = {r.q[0].x, r.q[0].y, r.q[0].z, r.q[0].w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[2 * i] = __uint_as_float(w[i] << 16);
+      v[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+    }
+  } else {
+    const uint32_t w[8] = {r.q[0].x, r.q[0].y, r.q[0].z, r.q[0].w, r.q[1].x, r.q[1].y, r.q[1].z, r.q[1].w};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = __uint_as_float(w[i]);
+  }
+}
+
 template <typename T>
 __device__ __forceinline__ void load8g(const void* base, int64_t idx, float (&v)[8]) {
   if constexpr (sizeof(T) == 2) {
@@ -622,6 +654,41 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(GemmArgs p) {
     return b + n0;
   };
 
+  // Gate epilogues: the token and table-row index of every row of the tile
+  // are loaded here and kept in LDS past the stage buffers ([BM] tokens,
+  // then [BM] row indices; -1 for a token outside the batch), so that the
+  // epilogue can issue all of its table-row gathers at once.  They are
+  // written to LDS after the first stage's loads are issued, whose wait
+  // covers them.
+  constexpr bool kGate = EPI == kEpiGateUp || EPI == kEpiGateStem;
+  int* idx_lds = reinterpret_cast<int*>(smem + NS * kStage);
+  constexpr int kIdxPer = (BM + NT - 1) / NT;
+  int pro_tok[kGate ? kIdxPer : 1], pro_ri[kGate ? kIdxPer : 1];
+  if constexpr (kGate) {
+#pragma unroll
+    for (int j = 0; j < kIdxPer; ++j) {
+      const int t = static_cast<int>(threadIdx.x) + j * NT;
+      int64_t m = m0 + t;
+      if (m > p.M - 1) m = p.M - 1;
+      int64_t tok = p.a_rows ? static_cast<int64_t>(p.a_rows[m]) : m;
+      if (tok < 0 || tok >= p.a_rows_bound) tok = -1;   // flagged with the A operand's rows
+      pro_tok[j] = static_cast<int>(tok);
+      pro_ri[j] = tok < 0 ? -1 : p.row_index[tok];
+    }
+  }
+  auto stash_idx = [&]() {
+    if constexpr (kGate) {
+#pragma unroll
+      for (int j = 0; j < kIdxPer; ++j) {
+        const int t = static_cast<int>(threadIdx.x) + j * NT;
+        if (t < BM) {
+          idx_lds[t] = pro_tok[j];
+          idx_lds[BM + t] = pro_ri[j];
+        }
+      }
+    }
+  };
+
   f32x16_t acc[TM][TN];
 #pragma unroll
   for (int i = 0; i < TM; ++i)
@@ -697,11 +764,14 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(GemmArgs p) {
     };
     if (nk > 0) {
       load_regs(0);
+      stash_idx();
 #pragma unroll
       for (int q = 0; q < NP; ++q) store_piece(0, q);
       load_regs(nk > 1 ? 1 : 0);
       lds_barrier();                                        // B_0
       MmaT::read(lds, lds + BM * RB, a_row0, b_row0, 0, fr[0]);
+    } else {
+      stash_idx();
     }
     for (int64_t st = 0; st < nk; ++st) {
       const int cur = static_cast<int>(st & 1);
@@ -731,6 +801,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(GemmArgs p) {
       store_regs(st);
     }
   }
+  stash_idx();
   for (int64_t kt = 0; kt < nk; ++kt) {
     const int64_t younger = (nk - 1 - kt) < (NS - 2) ? (nk - 1 - kt) : (NS - 2);
     static_assert(NS >= 2 && NS <= 5 && (NS - 2) * kLoads < 64, "stages");
@@ -751,6 +822,29 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(GemmArgs p) {
   constexpr int LD = WN + 4;
   float* region = reinterpret_cast<float*>(smem) + wid * 32 * LD;
   constexpr int kChunks = 32 * WN / 8;          // 8-column chunks per 32-row block
+  // Gate epilogues: chunk q = lane + 64 c of block i is row q / kCpr of the
+  // block and 8 features from (q % kCpr) 8 of the wave's features (gate/up:
+  // wave columns are pairs of [32 gate | 32 up] for the same 32 features).
+  // Every block's table rows are fetched before the first block is formed:
+  // one gather latency per tile instead of two dependent ones per block.
+  constexpr int kCpr = EPI == kEpiGateUp ? WN / 16 : WN / 8;
+  constexpr int kGateChunks = 32 * kCpr;
+  constexpr int kGatePer = (kGateChunks + 63) / 64;
+  const int64_t wave_feat0 = EPI == kEpiGateUp ? (n0 + wn * WN) / 2 : n0 + wn * WN;
+  Raw8<T> epre[kGate ? TM : 1][kGate ? kGatePer : 1];
+  if constexpr (kGate) {
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int c = 0; c < kGatePer; ++c) {
+        const int q = lane + 64 * c;
+        const int row = wm * WM + i * 32 + q / kCpr;
+        const int64_t feat = wave_feat0 + (q % kCpr) * 8;
+        const int64_t ri = idx_lds[BM + row];
+        const bool ok = q < kGateChunks && ri >= 0 && ri < p.n_rows && feat < p.d_ff;
+        epre[i][c] = raw_load8<T>(p.rows, ok ? ri * p.d_ff + feat : 0);
+      }
+  }
 #pragma unroll
   for (int i = 0; i < TM; ++i) {
     stage_rows<TN>(region, acc[i]);
@@ -771,105 +865,68 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(GemmArgs p) {
         }
       }
     } else if constexpr (EPI == kEpiGateUp) {
-      // wave columns: pairs of [32 gate | 32 up] for the same 32 features.
-      // The table rows are fetched for all of this lane's chunks first (their
-      // loads overlap), then h, g, u are formed and stored.
-      constexpr int kFeatChunks = 32 * (WN / 2) / 8;
-      constexpr int kPerLane = (kFeatChunks + 63) / 64;
+      // h, g, u from the staged [gate | up] pairs and the prefetched rows
       const int64_t f = p.d_ff;
-      int64_t ri[kPerLane], tokq[kPerLane];
-      float e[kPerLane][8];
 #pragma unroll
-      for (int c = 0; c < kPerLane; ++c) {
+      for (int c = 0; c < kGatePer; ++c) {
         const int q = lane + 64 * c;
-        const int rr = q / (WN / 16);
-        const int64_t m = mrow0 + rr;
-        const int64_t mm = m < p.M ? m : p.M - 1;
-        tokq[c] = p.a_rows ? static_cast<int64_t>(p.a_rows[mm]) : mm;
-        if (tokq[c] < 0 || tokq[c] >= p.a_rows_bound) tokq[c] = -1;   // flagged in the prologue
-        ri[c] = p.row_index[tokq[c] < 0 ? 0 : tokq[c]];
-      }
-#pragma unroll
-      for (int c = 0; c < kPerLane; ++c) {
-        const int q = lane + 64 * c;
-        const int fc = (q % (WN / 16)) * 8;
-        const int64_t feat = (n0 + wn * WN) / 2 + fc;
-        const bool ok = ri[c] >= 0 && ri[c] < p.n_rows && feat < f;
-        load8g<T>(p.rows, ok ? ri[c] * f + feat : 0, e[c]);
-      }
-#pragma unroll
-      for (int c = 0; c < kPerLane; ++c) {
-        const int q = lane + 64 * c;
-        if (q >= kFeatChunks) continue;
-        const int rr = q / (WN / 16);
-        const int fc = (q % (WN / 16)) * 8;           // feature offset within the wave's WN/2
+        if (q >= kGateChunks) continue;
+        const int rr = q / kCpr;
+        const int fc = (q % kCpr) * 8;
         const int pair = fc / 32, fin = fc % 32;
+        const int row = wm * WM + i * 32 + rr;
         const int64_t m = mrow0 + rr;
-        const int64_t feat = (n0 + wn * WN) / 2 + fc;
-        if (m < p.M && feat < f && tokq[c] >= 0) {
-          float g[8], a[8];
+        const int64_t feat = wave_feat0 + fc;
+        const int64_t tok = idx_lds[row], ri = idx_lds[BM + row];
+        if (m < p.M && feat < f && tok >= 0) {
+          float g[8], a[8], e[8];
           read8(region + rr * LD + pair * 64 + fin, g);
           read8(region + rr * LD + pair * 64 + 32 + fin, a);
-          if (!(ri[c] >= 0 && ri[c] < p.n_rows)) {
+          raw_unpack8<T>(epre[i][c], e);
+          if (!(ri >= 0 && ri < p.n_rows)) {
             flag_index_error(p.err);
 #pragma unroll
-            for (int k = 0; k < 8; ++k) e[c][k] = 0.0f;
+            for (int k = 0; k < 8; ++k) e[k] = 0.0f;
           }
           float u[8], h[8];
 #pragma unroll
           for (int k = 0; k < 8; ++k) {
-            u[k] = a[k] + e[c][k];
+            u[k] = a[k] + e[k];
             h[k] = g[k] * sigmoidf_(g[k]) * u[k];
           }
-          const int64_t o = tokq[c] * f + feat;
+          const int64_t o = tok * f + feat;
           store8g<T>(p.h_out, o, h);
           if (p.g_out) store8g<T>(p.g_out, o, g);
           if (p.u_out) store8g<T>(p.u_out, o, u);
         }
       }
     } else if constexpr (EPI == kEpiGateStem) {
-      // C = g (M = tokens, N = d_ff).  The table rows of all of this lane's
-      // chunks are fetched first, then h, g, u are formed and stored.
+      // C = g (M = tokens, N = d_ff); u is the table row
       const int64_t f = p.d_ff;
-      constexpr int kPerLane = (kChunks + 63) / 64;
-      int64_t ri[kPerLane], tokq[kPerLane];
-      float e[kPerLane][8];
 #pragma unroll
-      for (int c = 0; c < kPerLane; ++c) {
+      for (int c = 0; c < kGatePer; ++c) {
         const int q = lane + 64 * c;
-        const int64_t m = mrow0 + q / (WN / 8);
-        const int64_t mm = m < p.M ? m : p.M - 1;
-        tokq[c] = p.a_rows ? static_cast<int64_t>(p.a_rows[mm]) : mm;
-        if (tokq[c] < 0 || tokq[c] >= p.a_rows_bound) tokq[c] = -1;   // flagged in the prologue
-        ri[c] = p.row_index[tokq[c] < 0 ? 0 : tokq[c]];
-      }
-#pragma unroll
-      for (int c = 0; c < kPerLane; ++c) {
-        const int q = lane + 64 * c;
-        const int64_t n = n0 + wn * WN + (q % (WN / 8)) * 8;
-        const bool ok = q < kChunks && ri[c] >= 0 && ri[c] < p.n_rows && n < f;
-        load8g<T>(p.rows, ok ? ri[c] * f + n : 0, e[c]);
-      }
-#pragma unroll
-      for (int c = 0; c < kPerLane; ++c) {
-        const int q = lane + 64 * c;
-        const int rr = q / (WN / 8), cc = (q % (WN / 8)) * 8;
+        if (q >= kGateChunks) continue;
+        const int rr = q / kCpr, cc = (q % kCpr) * 8;
+        const int row = wm * WM + i * 32 + rr;
         const int64_t m = mrow0 + rr;
-        const int64_t n = n0 + wn * WN + cc;
-        if (q < kChunks && m < p.M && n < f && tokq[c] >= 0) {
-          float g[8], h[8];
+        const int64_t n = wave_feat0 + cc;
+        const int64_t tok = idx_lds[row], ri = idx_lds[BM + row];
+        if (m < p.M && n < f && tok >= 0) {
+          float g[8], h[8], e[8];
           read8(region + rr * LD + cc, g);
-          if (!(ri[c] >= 0 && ri[c] < p.n_rows)) {
+          raw_unpack8<T>(epre[i][c], e);
+          if (!(ri >= 0 && ri < p.n_rows)) {
             flag_index_error(p.err);
 #pragma unroll
-            for (int k = 0; k < 8; ++k) e[c][k] = 0.0f;
+            for (int k = 0; k < 8; ++k) e[k] = 0.0f;
           }
 #pragma unroll
-          for (int k = 0; k < 8; ++k) h[k] = g[k] * sigmoidf_(g[k]) * e[c][k];
-          const int64_t o = tokq[c] * f + n;
+          for (int k = 0; k < 8; ++k) h[k] = g[k] * sigmoidf_(g[k]) * e[k];
+          const int64_t o = tok * f + n;
           store8g<T>(p.h_out, o, h);
           if (p.g_out) store8g<T>(p.g_out, o, g);
-          if (p.u_out) store8g<T>(p.u_out, o, e[c]);
+          if (p.u_out) store8g<T>(p.u_out, o, e);
         }
       }
     } else {  // kEpiDhAct: C = dh (M = tokens, N = d_ff)
@@ -918,7 +975,8 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(GemmArgs p) {
 template <typename T, int BM, int BN, int WGM, int WGN, bool AK, bool BK, int EPI, typename OutT,
           int RB, int NS, int PIPE = 0>
 static hipError_t run_tile(const GemmArgs& a, hipStream_t s) {
-  constexpr size_t kSmem = static_cast<size_t>(NS) * (BM + BN) * RB;
+  constexpr bool kGate = EPI == kEpiGateUp || EPI == kEpiGateStem;
+  constexpr size_t kSmem = static_cast<size_t>(NS) * (BM + BN) * RB + (kGate ? 2 * BM * sizeof(int) : 0);
   auto kern = &gemm_kernel<T, BM, BN, WGM, WGN, AK, BK, EPI, OutT, RB, NS, PIPE>;
   static const hipError_t attr = hipFuncSetAttribute(
       reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
