@@ -572,6 +572,19 @@ def run_offload_decode(torch, st, w, steps, warmup):
         st.staple_decode_step_cached(stack, ids, O["id_to_slot"], w.cache_capacity,
                                      dedup_out=dd_out, lookup_out=lk_out, workspace=step_ws)
 
+    # the same call with no compact rows: each layer's gate/up kernel reads
+    # every token's row in place (cache slot, or the pinned host table over
+    # PCIe) while its weights stream
+    stack_inplace = st.DecodeStack([{"x": lay["x"], "packed_gate_up": lay["pgu"],
+                                     "packed_down": lay["pd"], "cache_rows": O["cache_rows"][l],
+                                     "table": O["tables"][l], "y": lay["y"]}
+                                    for l, lay in enumerate(layers)],
+                                   d_model=d, d_ff=f, n_tokens=n)
+
+    def step_inplace():
+        st.staple_decode_step_cached(stack_inplace, ids, O["id_to_slot"], w.cache_capacity,
+                                     dedup_out=dd_out, lookup_out=lk_out, workspace=step_ws)
+
     def timed(step):
         for _ in range(warmup):
             step()
@@ -590,23 +603,29 @@ def run_offload_decode(torch, st, w, steps, warmup):
     torch.cuda.synchronize()
     if not all(torch.equal(a, lay["y"]) for a, lay in zip(ys, layers)):
         raise RuntimeError("the native step driver's outputs differ from the per-layer calls")
+    ms_inplace = timed(step_inplace)
+    torch.cuda.synchronize()
+    if not all(torch.equal(a, lay["y"]) for a, lay in zip(ys, layers)):
+        raise RuntimeError("the in-place row reads give other outputs than the per-layer calls")
     ms_staged = timed(step_staged)
     m = _miss_list_to_host(torch, lk_out, miss_host)
-    times = {"direct": ms_direct, "staged": ms_staged, "native": ms_native}
+    times = {"direct": ms_direct, "staged": ms_staged, "native": ms_native, "native_inplace": ms_inplace}
     method = min(times, key=times.get)
     ms = times[method]
     n_unique = int(dd_out["n_unique"].item())
     return {"workload": w.name, "ms_per_step": ms, "tokens_per_s": n / (ms * 1e-3),
             "method": method,
             "direct_ms_per_step": ms_direct, "native_ms_per_step": ms_native,
-            "staged_ms_per_step": ms_staged,
+            "native_inplace_ms_per_step": ms_inplace, "staged_ms_per_step": ms_staged,
             "n_unique": n_unique, "misses_per_layer": m, "cache_capacity": w.cache_capacity,
             "pcie_bytes_per_step": m * f * 2 * L,
             "note": "eager steps, dedup + cache probe once per step. direct: per layer one kernel "
                     "assembles R with the hits from the HBM cache and the misses read from the "
                     "pinned host table over PCIe (no host sync, one stream), then gate/up, "
                     "down. native: one staple_decode_step_cached call per step (dedup, probe, "
-                    "every layer's rows in one launch, the FFNs). staged: "
+                    "every layer's rows in one launch, the FFNs). native_inplace: the same call "
+                    "with no compact rows, each gate/up kernel reading its tokens' rows in place "
+                    "(cache slot or pinned host table). staged: "
                     "one host sync for the miss list, host pack + H2D copy per layer on a side "
                     "stream one layer ahead"}
 

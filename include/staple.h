@@ -361,12 +361,22 @@ staple_status_t staple_ffn_fwd_packed(int64_t n_tokens, int64_t d_model, int64_t
  * Table 4 caption: the 1 GB cache of frequent rows).  Enqueues on `stream`:
  *   1. staple_dedup of ids (the batch's n tokens) and staple_cache_lookup
  *      against id_to_slot;
- *   2. every layer's compact rows R_l = layers[l].rows (hits from
- *      layers[l].cache_rows, misses read straight from layers[l].table, as
- *      staple_assemble_rows_from_table), one launch for up to 32 layers, so
- *      the host reads of all layers' misses are in flight together;
+ *   2. the compact rows R_l = layers[l].rows of every layer that has them
+ *      (hits from layers[l].cache_rows, misses read straight from
+ *      layers[l].table, as staple_assemble_rows_from_table), one launch for
+ *      up to 32 layers, so the host reads of all those layers' misses are in
+ *      flight together;
  *   3. each layer's decode forward (staple_ffn_fwd_packed with rows = R_l,
- *      row_index = inv).
+ *      row_index = inv).  A layer with rows = NULL instead reads each
+ *      token's row in place inside its gate/up kernel: from cache_rows when
+ *      the row is cached, else from the table (over PCIe when it is in
+ *      pinned host memory), loaded into LDS by a wave of its own while the
+ *      weights stream (STAPLE retrieval-path table, Decode row: misses read
+ *      zero-copy from host memory).  Its y has the same bits; no R_l is
+ *      written.  This saves the assembly launch and pays off for tables in
+ *      HBM; for tables in pinned host memory every workgroup then reads
+ *      small pieces of the same miss rows over PCIe, and the one-launch
+ *      assembly of whole rows measured faster.
  * The whole step is one native call: issuing it costs one call per step
  * instead of several per layer.
  *
@@ -376,7 +386,8 @@ staple_status_t staple_ffn_fwd_packed(int64_t n_tokens, int64_t d_model, int64_t
  *     cache_rows [capacity x d_ff] bf16 device (slot s = the row of the ID
  *     with slot s in id_to_slot, e.g. from staple_cache_fill); table
  *     [vocab x d_ff] bf16, pinned host (hipHostMalloc) or device; rows
- *     [n x d_ff] bf16 device, one per layer (it holds R_l after the step);
+ *     [n x d_ff] bf16 device, one per layer (it holds R_l after the step),
+ *     or NULL (rows read in place, above);
  *     y [n x d_model] of out_dtype.
  *   1 <= n <= 64, d_model and d_ff multiples of 64 (else UNSUPPORTED).
  *   uniq, inv, sorted_pos [n], seg_start [n + 1], n_unique [1]: staple_dedup's

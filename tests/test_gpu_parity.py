@@ -913,14 +913,22 @@ def test_stem_packed_matches_oracle_and_row_major_bitwise(st, dev, n, d, f):
 
 # ---------------------------------------------------------------- native decode step driver
 @pytest.mark.parametrize("stem", [False, True])
-def test_decode_step_driver_matches_per_layer_calls(st, dev, stem):
+@pytest.mark.parametrize("rows_mode", ["assembled", "direct", "mixed", "direct_nocache"])
+def test_decode_step_driver_matches_per_layer_calls(st, dev, stem, rows_mode):
     """staple_decode_step_cached (dedup, cache probe, every layer's rows from
     the HBM cache or the pinned host table in one launch, the packed FFNs)
     gives each layer's y and rows bit for bit as the separate calls over
-    several steps, and y matches the oracle on the full table."""
+    several steps, and y matches the oracle on the full table.  Layers
+    without rows (rows_mode "direct", or every other layer in "mixed") read
+    each token's row in place inside the gate/up kernel, with the same y
+    ("direct_nocache": no HBM cache at all, every row read from the pinned
+    table, cache_rows NULL)."""
     import torch
-    L, n, d, f, vocab, cap = 3, 33, 128, 256, 500, 40
-    _log(f"decode step driver stem={stem}")
+    L, n, d, f, vocab = 3, 33, 128, 256, 500
+    cap = 0 if rows_mode == "direct_nocache" else 40
+    _log(f"decode step driver stem={stem} rows={rows_mode}")
+    keeps_rows = [rows_mode == "assembled" or (rows_mode == "mixed" and l % 2 == 1) for l in range(L)]
+    cache_refs = []
     counts = st.staple_cache_count(torch.from_numpy(S.zipf_ids(20_000, vocab, 3)).to(dev), vocab)
     i2s, s2i = st.staple_cache_build(counts, cap)
     layers, ref = [], []
@@ -929,9 +937,10 @@ def test_decode_step_driver_matches_per_layer_calls(st, dev, stem):
         x, wg, wu, wd = (to_dev(getattr(inp, k), "bf16", dev) for k in ("x", "w_gate", "w_up", "w_down"))
         host_table = torch.from_numpy(inp.table.view(np.int16)).view(torch.bfloat16).pin_memory()
         pgu, pd = st.staple_decode_pack_weights(wg, None if stem else wu, wd, d_model=d, d_ff=f)
+        cache_refs.append(st.staple_cache_fill(host_table, s2i, cap))
         layers.append({"x": x, "packed_gate_up": pgu, "packed_down": pd,
-                       "cache_rows": st.staple_cache_fill(host_table, s2i, cap), "table": host_table,
-                       "rows": torch.zeros(n, f, dtype=torch.bfloat16, device=dev),
+                       "cache_rows": None if cap == 0 else cache_refs[-1], "table": host_table,
+                       "rows": torch.zeros(n, f, dtype=torch.bfloat16, device=dev) if keeps_rows[l] else None,
                        "y": torch.zeros(n, d, dtype=torch.float32, device=dev)})
         ref.append(inp)
     stack = st.DecodeStack(layers, d_model=d, d_ff=f, n_tokens=n)
@@ -948,15 +957,16 @@ def test_decode_step_driver_matches_per_layer_calls(st, dev, stem):
         d2 = st.staple_dedup(ids, vocab)
         l2 = st.staple_cache_lookup(d2["uniq"], d2["n_unique"], i2s)
         want = []
-        for lay in layers:
-            r = st.staple_assemble_rows_from_table(lay["cache_rows"], lay["table"], d2["uniq"],
+        for l, lay in enumerate(layers):
+            r = st.staple_assemble_rows_from_table(cache_refs[l], lay["table"], d2["uniq"],
                                                    l2["code"], d2["n_unique"], capacity=cap)
             y = st.staple_ffn_fwd_packed(lay["x"], lay["packed_gate_up"], lay["packed_down"], r,
                                          d2["inv"], d_ff=f, out_dtype=torch.float32)["y"]
             want.append((r, y))
         for lay in layers:
             lay["y"].zero_()
-            lay["rows"].zero_()
+            if lay["rows"] is not None:
+                lay["rows"].zero_()
         st.staple_decode_step_cached(stack, ids, i2s, cap, dedup_out=dd, lookup_out=lk, workspace=ws)
         torch.cuda.synchronize()
         _no_device_error(st)
@@ -965,7 +975,8 @@ def test_decode_step_driver_matches_per_layer_calls(st, dev, stem):
         assert torch.equal(dd["inv"], d2["inv"]) and torch.equal(lk["code"][:u], l2["code"][:u])
         for l, lay in enumerate(layers):
             assert torch.equal(lay["y"], want[l][1]), (step, l)
-            assert torch.equal(lay["rows"][:u], want[l][0][:u]), (step, l)
+            if lay["rows"] is not None:
+                assert torch.equal(lay["rows"][:u], want[l][0][:u]), (step, l)
             g = {k: ref[l].as_f64(k) for k in ("x", "w_gate", "w_up", "w_down", "table")}
             of = O.ffn_forward(g["x"], g["w_gate"], None if stem else g["w_up"], g["w_down"],
                                g["table"], ids_np, precision=O.BF16)

@@ -399,7 +399,9 @@ class DecodeStack:
 
     def __init__(self, layers: list, *, d_model: int, d_ff: int, n_tokens: int):
         keys = ("x", "packed_gate_up", "packed_down", "cache_rows", "table", "rows", "y")
-        self.layers = [{k: lay[k] for k in keys} for lay in layers]   # keeps the tensors alive
+        # keeps the tensors alive; a layer without "rows" (or rows None) reads
+        # each token's row in place
+        self.layers = [{k: lay.get(k) for k in keys} for lay in layers]
         for lay in self.layers:
             _dev(lay["x"], lay["packed_gate_up"], lay["packed_down"], lay["cache_rows"],
                  lay["rows"], lay["y"])

@@ -31,7 +31,8 @@ hipError_t launch_split_tokens(const int32_t* inv, int64_t n, const int32_t* cod
 hipError_t launch_cache_lookup(const int32_t* uniq, const int32_t* n_unique, int64_t max_unique,
                                const int32_t* id_to_slot, int64_t vocab, int32_t* code,
                                int32_t* miss_uidx, int32_t* miss_ids, int32_t* n_miss,
-                               hipStream_t s, int* err);
+                               hipStream_t s, int* err, const int32_t* inv = nullptr,
+                               int64_t n_tokens = 0, int32_t* row_src = nullptr);
 hipError_t launch_gather_rows(const void* src, int64_t src_rows, const int32_t* index,
                               const int32_t* n_rows, int64_t max_rows, int64_t row_bytes,
                               void* dst, hipStream_t s, int* err, unsigned max_workgroups);
@@ -82,7 +83,8 @@ size_t decode_down_workspace_bytes(int64_t n, int64_t d);
 hipError_t decode_gateup(int64_t n, const int32_t* pos, int64_t n_tokens, int64_t d, int64_t f,
                          const void* x, const void* wg, const void* wu, const void* rows,
                          int64_t n_rows, const int32_t* row_index, void* h, void* g_out,
-                         void* u_out, hipStream_t s, int* err, bool packed, bool up);
+                         void* u_out, hipStream_t s, int* err, bool packed, bool up,
+                         const void* table = nullptr, int64_t vocab = 0);
 hipError_t decode_down(int64_t n, int64_t d, int64_t f, const void* h, const void* wd, void* y,
                        int out_dtype, void* ws, hipStream_t s, bool packed);
 hipError_t decode_pack(int64_t d, int64_t f, const void* wg, const void* wu, const void* wd,
@@ -558,9 +560,11 @@ staple_status_t staple_ffn_fwd_packed(int64_t n, int64_t d, int64_t f, int32_t d
 }
 
 // ------------------------------------------------------------------ decode step driver
+// workspace of the decode step driver: [dedup][per-token row sources][h][down partials]
 size_t staple_decode_step_workspace_bytes(int64_t n, int64_t d, int64_t f) {
   if (!decode_eligible(n, d, f, STAPLE_BF16) || !ffn_shape_ok(n, d, f, STAPLE_BF16)) return 0;
-  return align_up(dedup_workspace_bytes(n), 256) + staple_ffn_fwd_workspace_bytes(n, d, f, STAPLE_BF16);
+  return align_up(dedup_workspace_bytes(n), 256) + align_up(static_cast<size_t>(n) * sizeof(int32_t), 256) +
+         staple_ffn_fwd_workspace_bytes(n, d, f, STAPLE_BF16);
 }
 
 staple_status_t staple_decode_step_cached(
@@ -579,41 +583,57 @@ staple_status_t staple_decode_step_cached(
   const size_t need = staple_decode_step_workspace_bytes(n, d, f);
   if (ws_bytes < need) return STAPLE_ERR_WORKSPACE;
   REQUIRE(ws && aligned16(ws));
+  bool any_direct = false;
   for (int64_t l = 0; l < n_layers; ++l) {
     const staple_decode_layer_t& L = layers[l];
-    REQUIRE(L.x && L.packed_gate_up && L.packed_down && L.table && L.rows && L.y);
+    REQUIRE(L.x && L.packed_gate_up && L.packed_down && L.table && L.y);
     REQUIRE(capacity == 0 || L.cache_rows);
     REQUIRE(aligned16(L.x) && aligned16(L.packed_gate_up) && aligned16(L.packed_down) &&
-            aligned16(L.table) && aligned16(L.rows) && aligned16(L.y) &&
+            aligned16(L.table) && (!L.rows || aligned16(L.rows)) && aligned16(L.y) &&
             (capacity == 0 || aligned16(L.cache_rows)));
     REQUIRE(device_addressable(L.table));
+    any_direct = any_direct || !L.rows;
   }
+  REQUIRE(capacity <= 0x7fffffffll);
   GET_ERR(err);
   hipStream_t s = S(stream);
   void* dedup_ws = ws;
-  void* fwd_ws = static_cast<char*>(ws) + align_up(dedup_workspace_bytes(n), 256);
+  int32_t* row_src = reinterpret_cast<int32_t*>(static_cast<char*>(ws) + align_up(dedup_workspace_bytes(n), 256));
+  void* fwd_ws = reinterpret_cast<char*>(row_src) + align_up(static_cast<size_t>(n) * sizeof(int32_t), 256);
   void* h = fwd_ws;
   void* down_ws = static_cast<char*>(fwd_ws) + align_up(static_cast<size_t>(n) * f * 2, 256);
   HIPCALL(launch_dedup(ids, n, vocab, uniq, inv, sorted_pos, seg_start, n_unique, dedup_ws, s, err));
   HIPCALL(launch_cache_lookup(uniq, n_unique, n, id_to_slot, vocab, code, miss_uidx, nullptr, n_miss,
-                              s, err));
-  // every layer's rows in one launch per slice of layers: the misses of all
-  // layers are read from host memory together
-  for (int64_t l0 = 0; l0 < n_layers; l0 += kMaxAssembleLayers) {
-    const int cnt = static_cast<int>(std::min<int64_t>(kMaxAssembleLayers, n_layers - l0));
-    LayerRowSources src{};
-    for (int i = 0; i < cnt; ++i) {
-      src.cache_rows[i] = layers[l0 + i].cache_rows;
-      src.table[i] = layers[l0 + i].table;
-      src.rows[i] = layers[l0 + i].rows;
-    }
-    HIPCALL(launch_assemble_rows_layers(src, cnt, capacity, vocab, uniq, code, n_unique, n, f * 2, s,
-                                        err));
-  }
+                              s, err, inv, n, any_direct ? row_src : nullptr));
+  // the rows of every layer that keeps them (rows != NULL), one launch per
+  // slice of such layers: the misses of all of them are read from host
+  // memory together
+  LayerRowSources src{};
+  int cnt = 0;
   for (int64_t l = 0; l < n_layers; ++l) {
     const staple_decode_layer_t& L = layers[l];
-    HIPCALL(decode_gateup(n, nullptr, n, d, f, L.x, L.packed_gate_up, nullptr, L.rows, n, inv, h,
-                          nullptr, nullptr, s, err, true, up_proj != 0));
+    if (!L.rows) continue;
+    src.cache_rows[cnt] = L.cache_rows;
+    src.table[cnt] = L.table;
+    src.rows[cnt] = L.rows;
+    if (++cnt == kMaxAssembleLayers) {
+      HIPCALL(launch_assemble_rows_layers(src, cnt, capacity, vocab, uniq, code, n_unique, n, f * 2,
+                                          s, err));
+      cnt = 0;
+    }
+  }
+  if (cnt > 0)
+    HIPCALL(launch_assemble_rows_layers(src, cnt, capacity, vocab, uniq, code, n_unique, n, f * 2, s,
+                                        err));
+  for (int64_t l = 0; l < n_layers; ++l) {
+    const staple_decode_layer_t& L = layers[l];
+    if (L.rows)
+      HIPCALL(decode_gateup(n, nullptr, n, d, f, L.x, L.packed_gate_up, nullptr, L.rows, n, inv, h,
+                            nullptr, nullptr, s, err, true, up_proj != 0));
+    else   // each token's row read in place: its cache slot, or its row of the table
+      HIPCALL(decode_gateup(n, nullptr, n, d, f, L.x, L.packed_gate_up, nullptr, L.cache_rows,
+                            capacity, row_src, h, nullptr, nullptr, s, err, true, up_proj != 0,
+                            L.table, vocab));
     HIPCALL(decode_down(n, d, f, h, L.packed_down, L.y, out_dtype, down_ws, s, true));
   }
   return STAPLE_OK;

@@ -83,17 +83,24 @@ __device__ __forceinline__ int xblock_at(int t, int c) { return t * 128 + ((c ^ 
 
 // Roles in a decode workgroup of (G + 1) KH waves: waves 0 .. G KH - 1
 // compute (row group w % G, K part w / G); wave G KH + p loads part p's
-// activation.
+// activation.  With RW, one more wave (the last) loads the workgroup's
+// table-row slices into LDS for the epilogue (it counts as a loader for the
+// barriers and the fold).
 struct WaveRole {
   bool loader;
   int grp, part;
+  bool row;
 };
-template <int G, int KH>
+template <int G, int KH, bool RW = false>
 __device__ __forceinline__ WaveRole wave_role() {
   const int wid = threadIdx.x >> 6;
-  if (wid >= G * KH) return {true, 0, wid - G * KH};
-  return {false, wid % G, wid / G};
+  if (RW && wid == (G + 1) * KH) return {true, 0, 0, true};
+  if (wid >= G * KH) return {true, 0, wid - G * KH, false};
+  return {false, wid % G, wid / G, false};
 }
+
+// 16-byte pieces of zeros: the source of table-row pieces that do not exist.
+__device__ const uint4 g_decode_zero_rows[16] = {};
 
 // One compute wave's 16 weight rows (pa: the lane's bytes at step 0; step s
 // at pa + s * wstep and pa + s * wstep + JOFF: row-major rows have wstep 128
@@ -112,12 +119,15 @@ __device__ __forceinline__ WaveRole wave_role() {
 // wave with `active` false (a row group past the end of the matrix, pa still
 // pointing at valid memory) runs them with zeroed weights too.
 // `after_prologue` runs on compute waves once their first loads are issued.
-template <int WD, int A, int KH, int JOFF, typename RowFn, typename Hook>
+// A row wave (role.row) runs `row_issue` (loads it does not wait for here)
+// and then only joins the barriers, so its loads, however slow, hold up no
+// other wave; the caller waits for them after the stream.
+template <int WD, int A, int KH, int JOFF, typename RowFn, typename Hook, typename RowIssue>
 __device__ __forceinline__ void stream_act_ring(WaveRole role, bool active, const char* pa, int64_t wstep,
                                                 const uint16_t* act, int64_t act_ld, RowFn act_row,
                                                 int n, lds_char* xl, int64_t s0, int64_t s1,
                                                 int64_t len_max, f32x4_t (&acc)[4],
-                                                Hook&& after_prologue) {
+                                                Hook&& after_prologue, RowIssue&& row_issue) {
   constexpr int NB = 4, NS = A + 1;
   constexpr int U = NS % WD == 0 ? NS : NS * WD;   // unrolled steps: static slot and register indices
   constexpr int kSlot = KH * kXBlock;
@@ -127,11 +137,21 @@ __device__ __forceinline__ void stream_act_ring(WaveRole role, bool active, cons
   for (int k = 0; k < NB; ++k)
 #pragma unroll
     for (int i = 0; i < 4; ++i) acc[k][i] = 0.0f;
+  const int64_t ngroups = len_max > 0 ? (len_max + U - 1) / U : 0;
+  if (role.row) {
+    row_issue();
+    if (len_max > 0) {
+      lds_barrier();
+      for (int64_t it = 0; it < ngroups; ++it)
+#pragma unroll
+        for (int j = 0; j < U; ++j) lds_barrier();
+    }
+    return;
+  }
   if (len_max <= 0) {   // uniform over the workgroup
     if (!role.loader) after_prologue();
     return;
   }
-  const int64_t ngroups = (len_max + U - 1) / U;
 
   if (role.loader) {
     const char* px[8];
@@ -252,20 +272,24 @@ __device__ __forceinline__ bool fold_parts(WaveRole role, float (*stage)[16 * kS
 // With `pos`, the n tokens of the launch are pos[0 .. n) of the n_tokens rows
 // of x, h, g, u and row_index (out-of-range positions set the error word and
 // are neither read nor written).
-template <int WD, int A, int G, int KH, bool PACKED, bool UP>
-__global__ __launch_bounds__(64 * (G + 1) * KH) void decode_gateup_kernel(
+template <int WD, int A, int G, int KH, bool PACKED, bool UP, bool RW = false>
+__global__ __launch_bounds__(64 * ((G + 1) * KH + (RW ? 1 : 0))) void decode_gateup_kernel(
     int n, const int32_t* __restrict__ pos, int64_t n_tokens, int64_t d, int64_t f,
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ wg,
     const uint16_t* __restrict__ wu, const uint16_t* __restrict__ rows, int64_t n_rows,
     const int32_t* __restrict__ row_index, uint16_t* __restrict__ h, uint16_t* __restrict__ g_out,
-    uint16_t* __restrict__ u_out, int* err) {
+    uint16_t* __restrict__ u_out, int* err, const uint16_t* __restrict__ table, int64_t vocab) {
+  constexpr int FG = UP ? 8 : 16;                                   // features per row group
+  // RW: the workgroup's G FG features of each token's table row, token t at
+  // byte t kSliceBytes, loaded by the row wave
+  constexpr int kSliceBytes = G * FG * 2;
   __shared__ __attribute__((aligned(16))) char xs[(A + 1) * KH * kXBlock];
   __shared__ float stage[G][16 * kStageLd];
+  __shared__ __attribute__((aligned(16))) char erows[RW ? 64 * kSliceBytes : 16];
   const int lane = threadIdx.x & 63;
-  const WaveRole role = wave_role<G, KH>();
+  const WaveRole role = wave_role<G, KH, RW>();
   const int grp = role.grp, part = role.part;
   const int r = lane & 15, q = lane >> 4;
-  constexpr int FG = UP ? 8 : 16;                                   // features per row group
   const int64_t rb = static_cast<int64_t>(blockIdx.x) * G + grp;   // this wave's row group
   const bool active = rb < f / FG;
   const int64_t rbc = active ? rb : 0;                              // valid memory for the rest
@@ -289,19 +313,65 @@ __global__ __launch_bounds__(64 * (G + 1) * KH) void decode_gateup_kernel(
     return p < 0 ? 0 : p;
   };
   const int64_t tok = tok_of(min(lane, n - 1));
-  // the epilogue's table row (lane = token, this wave's 8 features), fetched
-  // once the stream is under way
-  int64_t ri;
-  bool erow_ok;
+  // the epilogue's table row of a token: row index v = row_index[token];
+  // with `table`, a negative v = -1 - id selects row id of the table (e.g.
+  // pinned host memory, read in place) and a non-negative one row v of
+  // `rows` (e.g. the HBM cache)
+  auto row_of = [&](int64_t v, bool& ok) -> const uint16_t* {
+    if (table && v < 0) {
+      ok = -1 - v < vocab;
+      return table + (-1 - v) * f;
+    }
+    ok = v >= 0 && v < n_rows;
+    return rows + v * f;
+  };
+  // Without RW each compute wave fetches its lane's token's row (this wave's
+  // features) once the stream is under way.  With RW the row wave loads the
+  // slices of all tokens straight into LDS (zeros for a bad index, which it
+  // flags), and no compute wave waits on those loads.
+  bool erow_ok = true;
   uint4 erow[FG / 8];
-  stream_act_ring<WD, A, KH, PACKED ? 1024 : 64>(role, active, pa, wstep, x, d, act_row, n,
-                                                  (lds_char*)(xs), s0, s1, len, acc, [&]() {
-    ri = row_index[tok < 0 ? 0 : tok];
-    erow_ok = ri >= 0 && ri < n_rows;
+  auto fetch_row = [&]() {
+    if constexpr (!RW) {
+      const uint16_t* src = row_of(row_index[tok < 0 ? 0 : tok], erow_ok);
 #pragma unroll
-    for (int c = 0; c < FG / 8; ++c)
-      erow[c] = *reinterpret_cast<const uint4*>(erow_ok ? rows + ri * f + f0 + 8 * c : x);
-  });
+      for (int c = 0; c < FG / 8; ++c)
+        erow[c] = *reinterpret_cast<const uint4*>(erow_ok ? src + f0 + 8 * c : x);
+    }
+  };
+  auto row_issue = [&]() {
+    if constexpr (RW) {
+      constexpr int kPieces = kSliceBytes / 16;          // per token; one 1 KB load per piece
+      const int64_t fbase = static_cast<int64_t>(blockIdx.x) * G * FG;
+      const int64_t p = tok_of(min(lane, n - 1));
+      bool ok = false;
+      const uint16_t* src = p < 0 ? nullptr : row_of(row_index[p], ok);
+      if (p >= 0 && !ok && lane < n) flag_index_error(err);
+      const unsigned long long base =
+          ok ? reinterpret_cast<unsigned long long>(src + fbase) : 0ull;
+#pragma unroll
+      for (int i = 0; i < kPieces; ++i) {
+        const int c = i * 64 + lane, t = c / kPieces, k = c % kPieces;
+        const unsigned long long b = __shfl(base, t, 64);
+        const bool use = t < n && b != 0ull && fbase + 8 * k < f;
+        const void* g = use ? reinterpret_cast<const void*>(b + 16ull * k)
+                            : static_cast<const void*>(g_decode_zero_rows + k);
+        __builtin_amdgcn_global_load_lds(g, static_cast<lds_void*>((lds_char*)(erows) + i * 1024), 16, 0, 0);
+      }
+    }
+  };
+  stream_act_ring<WD, A, KH, PACKED ? 1024 : 64>(role, active, pa, wstep, x, d, act_row, n,
+                                                  (lds_char*)(xs), s0, s1, len, acc, fetch_row,
+                                                  row_issue);
+  if constexpr (RW) {
+    if (role.row) wait_vmcnt<0>();   // its pieces are in LDS
+    __syncthreads();
+    if (!role.loader) {
+#pragma unroll
+      for (int c = 0; c < FG / 8; ++c)
+        erow[c] = *reinterpret_cast<const uint4*>(erows + lane * kSliceBytes + grp * FG * 2 + c * 16);
+    }
+  }
 
   // epilogue: the row group's block staged so that lane t holds its token's
   // 16 sums (UP: 8 gate then 8 up; STEM: 16 gate)
@@ -391,7 +461,8 @@ __global__ __launch_bounds__(64 * (G + 1) * KH) void decode_down_kernel(int n, i
   f32x4_t acc[4];
   stream_act_ring<WD, A, KH, PACKED ? 1024 : 64>(role, active, pa, wstep, h, f,
                                                   [](int t) -> int64_t { return t; }, n,
-                                                  (lds_char*)(xs), s0, s1, len, acc, []() {});
+                                                  (lds_char*)(xs), s0, s1, len, acc, []() {},
+                                                  []() {});
   if (!fold_parts<KH>(role, stage, acc) || !active) return;
   const float* st = stage[grp];
   const int t = lane;
@@ -511,7 +582,8 @@ static int device_cus() {
 hipError_t decode_gateup(int64_t n, const int32_t* pos, int64_t n_tokens, int64_t d, int64_t f,
                          const void* x, const void* wg, const void* wu, const void* rows,
                          int64_t n_rows, const int32_t* row_index, void* h, void* g_out,
-                         void* u_out, hipStream_t s, int* err, bool packed, bool up) {
+                         void* u_out, hipStream_t s, int* err, bool packed, bool up,
+                         const void* table, int64_t vocab) {
   // STAPLE: 4 row groups (32 features) per workgroup, on two K parts, while
   // that fits one workgroup per CU; else 6 row groups on one part (d_ff
   // 11008: 230 workgroups of 7 waves instead of 344 of 10 on 256 CUs whose
@@ -527,26 +599,35 @@ hipError_t decode_gateup(int64_t n, const int32_t* pos, int64_t n_tokens, int64_
                      : (groups <= 2 * cus ? 2 : groups <= 3 * cus ? 3 : wide ? 6 : 4);
   const unsigned grid = static_cast<unsigned>((groups + per - 1) / per);
   auto go = [&](auto kern, int threads) {
+    if (table) threads += 64;   // the row wave
     kern<<<dim3(grid), dim3(threads), 0, s>>>(
         static_cast<int>(n), pos, n_tokens, d, f, static_cast<const uint16_t*>(x),
         static_cast<const uint16_t*>(wg),
         static_cast<const uint16_t*>(wu), static_cast<const uint16_t*>(rows), n_rows, row_index,
-        static_cast<uint16_t*>(h), static_cast<uint16_t*>(g_out), static_cast<uint16_t*>(u_out), err);
+        static_cast<uint16_t*>(h), static_cast<uint16_t*>(g_out), static_cast<uint16_t*>(u_out), err,
+        static_cast<const uint16_t*>(table), vocab);
   };
-  auto pick = [&](auto packed_tag, auto up_tag) {
+  auto pick = [&](auto packed_tag, auto up_tag, auto rw_tag) {
     constexpr bool P = decltype(packed_tag)::value, U = decltype(up_tag)::value;
+    constexpr bool R = decltype(rw_tag)::value;
     constexpr int WD = kGateUpAhead, A = kGateUpActAhead, KH = kGateUpParts;
-    if (per == 6) go(decode_gateup_kernel<WD, A, 6, 1, P, U>, 64 * 7);
-    else if (per == 4) go(decode_gateup_kernel<WD, A, 4, KH, P, U>, 64 * 5 * KH);
+    if (per == 6) go(decode_gateup_kernel<WD, A, 6, 1, P, U, R>, 64 * 7);
+    else if (per == 4) go(decode_gateup_kernel<WD, A, 4, KH, P, U, R>, 64 * 5 * KH);
     else if constexpr (!U) {
-      if (per == 3) go(decode_gateup_kernel<WD, A, 3, KH, P, U>, 64 * 4 * KH);
-      else go(decode_gateup_kernel<WD, A, 2, KH, P, U>, 64 * 3 * KH);
+      if (per == 3) go(decode_gateup_kernel<WD, A, 3, KH, P, U, R>, 64 * 4 * KH);
+      else go(decode_gateup_kernel<WD, A, 2, KH, P, U, R>, 64 * 3 * KH);
     }
   };
-  if (packed && up) pick(std::true_type{}, std::true_type{});
-  else if (packed) pick(std::true_type{}, std::false_type{});
-  else if (up) pick(std::false_type{}, std::true_type{});
-  else pick(std::false_type{}, std::false_type{});
+  using T_ = std::true_type;
+  using F_ = std::false_type;
+  // rows read in place (a table given): packed weights only, with the row wave
+  if (table && !packed) return hipErrorInvalidValue;
+  if (table && up) pick(T_{}, T_{}, T_{});
+  else if (table) pick(T_{}, F_{}, T_{});
+  else if (packed && up) pick(T_{}, T_{}, F_{});
+  else if (packed) pick(T_{}, F_{}, F_{});
+  else if (up) pick(F_{}, T_{}, F_{});
+  else pick(F_{}, F_{}, F_{});
   return hipGetLastError();
 }
 

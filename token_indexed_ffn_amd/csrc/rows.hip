@@ -60,13 +60,16 @@ hipError_t launch_cache_count(const int32_t* ids, int64_t n, int64_t vocab, int6
 
 // ---------------------------------------------------------------------------
 // Cache probe + stable miss compaction (one workgroup; U is at most a batch).
+// With row_src, also each token's row source for the decode kernels' direct
+// reads: row_src[t] = the cache slot of the token's row when cached, else
+// -1 - id (the row of the table), INT32_MIN when inv or the ID is out of range.
 // ---------------------------------------------------------------------------
 constexpr int kLookupThreads = 1024;
 
 __global__ __launch_bounds__(kLookupThreads) void lookup_kernel(
     const int32_t* uniq, const int32_t* n_unique_p, int64_t max_unique, const int32_t* id_to_slot,
     int64_t vocab, int32_t* code, int32_t* miss_uidx, int32_t* miss_ids, int32_t* n_miss,
-    int* err) {
+    const int32_t* inv, int64_t n_tokens, int32_t* row_src, int* err) {
   __shared__ int wave_tmp[16];
   int64_t nu = *n_unique_p;
   if (nu < 0 || nu > max_unique) {
@@ -104,15 +107,32 @@ __global__ __launch_bounds__(kLookupThreads) void lookup_kernel(
     carry += total;
   }
   if (threadIdx.x == 0) *n_miss = carry;
+  if (!row_src) return;
+  __syncthreads();   // code[] of the whole batch written
+  for (int64_t t = threadIdx.x; t < n_tokens; t += blockDim.x) {
+    const int32_t u = inv[t];
+    int32_t src = INT32_MIN;
+    if (u < 0 || u >= nu) {
+      flag_index_error(err);
+    } else {
+      const int32_t id = uniq[u];
+      if (id >= 0 && id < vocab) {
+        const int32_t c = code[u];
+        src = c >= 0 ? c : -1 - id;
+      }
+    }
+    row_src[t] = src;
+  }
 }
 
 hipError_t launch_cache_lookup(const int32_t* uniq, const int32_t* n_unique, int64_t max_unique,
                                const int32_t* id_to_slot, int64_t vocab, int32_t* code,
                                int32_t* miss_uidx, int32_t* miss_ids, int32_t* n_miss,
-                               hipStream_t s, int* err) {
+                               hipStream_t s, int* err, const int32_t* inv, int64_t n_tokens,
+                               int32_t* row_src) {
   lookup_kernel<<<dim3(1), dim3(kLookupThreads), 0, s>>>(uniq, n_unique, max_unique, id_to_slot,
                                                          vocab, code, miss_uidx, miss_ids, n_miss,
-                                                         err);
+                                                         inv, n_tokens, row_src, err);
   return hipGetLastError();
 }
 
