@@ -23,7 +23,12 @@
 // reconstruction fused with the FFN) and stores h with 16-byte vectors.
 // The STEM layer, which has no up-projection (the table row replaces it,
 // STAPLE abstract and Table 4's STEM row), runs the same kernel on W_gate
-// alone: a wave owns the gate rows of 16 features and u = E[t].
+// alone: a wave owns the gate rows of 16 features and u = E[t].  When the
+// rows are read in place (a row index selects a cache slot or, negative, a
+// row of the table itself, e.g. in pinned host memory), one more wave per
+// workgroup loads every token's slice of its row into LDS while the weights
+// stream, so that no compute wave waits on those loads (STAPLE
+// retrieval-path table, Decode row: misses read zero-copy).
 //
 // Down: d_model is too narrow to fill 256 CUs with whole-K tiles, so the K
 // range (d_ff) is split over several workgroups per output block; each writes
