@@ -295,6 +295,40 @@ def test_gate_up_tokens_out_of_range_position_is_flagged(st, dev):
         assert torch.count_nonzero(h[n_sel:]) == 0 and torch.count_nonzero(h[1]) == 0
 
 
+@pytest.mark.parametrize("stem", [False, True])
+@pytest.mark.parametrize("n_sel", [5, 80, 300])     # decode kernel, 128 and 256 GEMM tiles
+def test_bad_table_row_index_is_flagged_and_reads_as_zero(st, dev, n_sel, stem):
+    """A row index outside the rows block (past the end, or negative) sets the
+    device error word and that token's table row counts as zeros: h, g, u equal
+    bit for bit those of the same call with the token pointed at a zero row."""
+    import torch
+    d, vocab = 128, 50
+    f = 8192 if n_sel == 300 else 256
+    _log(f"bad row index n={n_sel} stem={stem}")
+    inp = S.host_layer_inputs(n_sel, d, f, vocab, dtype="bf16", seed=11, table_std=0.5)
+    x, wg, wu, tab = (to_dev(getattr(inp, k), "bf16", dev) for k in ("x", "w_gate", "w_up", "table"))
+    wu = None if stem else wu
+    ids = torch.from_numpy(inp.ids).to(dev)
+    bad = ids.clone()
+    bad[1], bad[2] = vocab + 7, -3
+    zero_rows = torch.cat([tab, torch.zeros(1, f, dtype=torch.bfloat16, device=dev)])
+    to_zero = ids.clone()
+    to_zero[1], to_zero[2] = vocab, vocab
+
+    def run(rows, index):
+        o = {k: torch.zeros(n_sel, f, dtype=torch.bfloat16, device=dev) for k in ("h", "g", "u")}
+        st.staple_ffn_gate_up(x, wg, wu, rows, index, o["h"], o["g"], o["u"])
+        torch.cuda.synchronize()
+        return o
+
+    got = run(tab, bad)
+    assert st.staple_get_device_error() != 0      # reading it also clears it
+    ref = run(zero_rows, to_zero)
+    _no_device_error(st)
+    for k in ("h", "g", "u"):
+        assert torch.equal(got[k], ref[k]), k
+
+
 # ---------------------------------------------------------------- FFN helpers
 def _run_layer(st, dev, inp, out_f32=True, freeze_up=False, backward=True, full_table=False):
     import torch
@@ -981,6 +1015,55 @@ def test_decode_step_driver_matches_per_layer_calls(st, dev, stem, rows_mode):
             of = O.ffn_forward(g["x"], g["w_gate"], None if stem else g["w_up"], g["w_down"],
                                g["table"], ids_np, precision=O.BF16)
             assert_close(to_np(lay["y"]), of["y"], f"driver y layer {l} step {step}")
+
+
+@pytest.mark.parametrize("stem", [False, True])
+def test_decode_step_driver_in_place_bad_slot_is_flagged_and_reads_as_zero(st, dev, stem):
+    """With rows read in place, a cache slot past the capacity (a corrupt
+    id -> slot map) sets the device error word and the token's row counts as
+    zeros, as in the per-layer call on rows whose row is zero."""
+    import torch
+    L, n, d, f, vocab, cap = 2, 20, 128, 256, 60, 8
+    _log(f"decode step driver bad slot stem={stem}")
+    counts = st.staple_cache_count(torch.from_numpy(S.zipf_ids(5_000, vocab, 4)).to(dev), vocab)
+    i2s, s2i = st.staple_cache_build(counts, cap)
+    ids_np = S.zipf_ids(n, vocab, 77)
+    ids = torch.from_numpy(ids_np).to(dev)
+    corrupt = i2s.clone()
+    corrupt[int(ids_np[0])] = cap + 5                 # token 0's ID maps past the cache
+    layers = []
+    for l in range(L):
+        inp = S.host_layer_inputs(n, d, f, vocab, dtype="bf16", seed=120 + l, table_std=0.5)
+        x, wg, wu, wd = (to_dev(getattr(inp, k), "bf16", dev) for k in ("x", "w_gate", "w_up", "w_down"))
+        host_table = torch.from_numpy(inp.table.view(np.int16)).view(torch.bfloat16).pin_memory()
+        pgu, pd = st.staple_decode_pack_weights(wg, None if stem else wu, wd, d_model=d, d_ff=f)
+        layers.append({"x": x, "packed_gate_up": pgu, "packed_down": pd,
+                       "cache_rows": st.staple_cache_fill(host_table, s2i, cap), "table": host_table,
+                       "y": torch.zeros(n, d, dtype=torch.float32, device=dev)})
+    stack = st.DecodeStack(layers, d_model=d, d_ff=f, n_tokens=n)
+    i32 = dict(dtype=torch.int32, device=dev)
+    dd = {"uniq": torch.empty(n, **i32), "inv": torch.empty(n, **i32),
+          "sorted_pos": torch.empty(n, **i32), "seg_start": torch.empty(n + 1, **i32),
+          "n_unique": torch.empty(1, **i32)}
+    lk = {"code": torch.empty(n, **i32), "miss_uidx": torch.empty(n, **i32),
+          "n_miss": torch.empty(1, **i32)}
+    ws = torch.empty(st.decode_step_workspace_bytes(n, d, f), dtype=torch.uint8, device=dev)
+    st.staple_decode_step_cached(stack, ids, corrupt, cap, dedup_out=dd, lookup_out=lk, workspace=ws)
+    torch.cuda.synchronize()
+    assert st.staple_get_device_error() != 0
+    # reference: the rows from the correct map, with token 0's row zeroed
+    d2 = st.staple_dedup(ids, vocab)
+    l2 = st.staple_cache_lookup(d2["uniq"], d2["n_unique"], i2s)
+    u0 = int(d2["inv"][0].item())
+    for lay in layers:
+        r = st.staple_assemble_rows_from_table(lay["cache_rows"], lay["table"], d2["uniq"],
+                                               l2["code"], d2["n_unique"], capacity=cap)
+        r[u0].zero_()
+        want = st.staple_ffn_fwd_packed(lay["x"], lay["packed_gate_up"], lay["packed_down"], r,
+                                        d2["inv"], d_ff=f, out_dtype=torch.float32)["y"]
+        torch.cuda.synchronize()
+        assert torch.equal(lay["y"], want)
+    _no_device_error(st)
 
 
 def test_decode_step_driver_refuses_bad_arguments(st, dev):
