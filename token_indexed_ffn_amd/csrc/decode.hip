@@ -540,6 +540,9 @@ size_t decode_down_workspace_bytes(int64_t n, int64_t d) {
 // earlier layouts that split d_model (or d_ff) over the waves of a workgroup
 // and folded their partial sums in LDS all measured slower.
 constexpr int kGateUpAhead = 2;      // weight steps in flight per compute wave
+constexpr int kGateUpAheadLong = 4;  // the same for the 6-group, one-part shape (whole-d_model
+                                     // streams: 64 steps per wave at d_model 4096; 31.3 us
+                                     // against 31.5-32.6 us with 2 at 4096 x 11008)
 constexpr int kGateUpActAhead = 3;   // activation steps in flight per loader wave
 constexpr int kGateUpParts = 2;      // d_model split in two inside a 4-group gate/up workgroup
 constexpr int kDownAhead = 2;
@@ -616,7 +619,7 @@ hipError_t decode_gateup(int64_t n, const int32_t* pos, int64_t n_tokens, int64_
     constexpr bool P = decltype(packed_tag)::value, U = decltype(up_tag)::value;
     constexpr bool R = decltype(rw_tag)::value;
     constexpr int WD = kGateUpAhead, A = kGateUpActAhead, KH = kGateUpParts;
-    if (per == 6) go(decode_gateup_kernel<WD, A, 6, 1, P, U, R>, 64 * 7);
+    if (per == 6) go(decode_gateup_kernel<kGateUpAheadLong, A, 6, 1, P, U, R>, 64 * 7);
     else if (per == 4) go(decode_gateup_kernel<WD, A, 4, KH, P, U, R>, 64 * 5 * KH);
     else if constexpr (!U) {
       if (per == 3) go(decode_gateup_kernel<WD, A, 3, KH, P, U, R>, 64 * 4 * KH);
