@@ -55,6 +55,15 @@ def test_workspace_queries(lib):
     assert lib.staple_ffn_bwd_workspace_bytes(100, 64, 128, 1) == dgu + partials
     assert lib.staple_ffn_fwd_workspace_bytes(100, 64, 100, 1) == 0   # d_ff not a multiple of 64
     assert lib.staple_cache_build_workspace_bytes(100352) == 131072 * 8
+    # decode forward: [h][split-K partials, 8 splits of n x d_model fp32]
+    h = 64 * 8192 * 2
+    down = 8 * 64 * 2048 * 4
+    assert lib.staple_ffn_down_workspace_bytes(64, 2048, 8192, 1) == down
+    assert lib.staple_ffn_fwd_workspace_bytes(64, 2048, 8192, 1) == h + down
+    assert lib.staple_ffn_down_workspace_bytes(65, 2048, 8192, 1) == 0   # tiled GEMM, no partials
+    # decode step driver: [dedup (none at 64 tokens)][row sources, n int32 in 256 B][h][partials]
+    assert lib.staple_decode_step_workspace_bytes(64, 2048, 8192) == 256 + h + down
+    assert lib.staple_decode_step_workspace_bytes(65, 2048, 8192) == 0   # past a decode batch
 
 
 def test_invalid_arguments_are_rejected_before_device_work(lib):
