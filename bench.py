@@ -237,7 +237,7 @@ def run_decode(torch, st, w, steps, warmup, stem=False):
                       + (", STEM gate-only)" if stem else ")"),
             "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": achieved / HBM_PEAK_GBS,
-            "traffic": None if stem else traffic_from_profile(f"decode_gate_up/{w.name}", sha),
+            "traffic": traffic_from_profile(f"decode_gate_up/{w.name}" + ("_stem" if stem else ""), sha),
             "avg_launch_us": gu_us, "algorithmic_bytes_per_launch": gu_bytes,
         },
     }
@@ -388,8 +388,8 @@ def run_train(torch, st, w, steps, warmup, stem=False):
                        if stem else "gemm_kernel<bf16,GateUp> (staple_ffn_gate_up, training batch)"),
             "bound": "mfma", "achieved": achieved, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
             "frac": achieved / BF16_PEAK_TFLOPS,
-            "traffic": None if stem else traffic_from_profile(f"train_gate_up/{w.name}",
-                                                              source_sha("gemm.hip", "common.h")),
+            "traffic": traffic_from_profile(f"train_gate_up/{w.name}" + ("_stem" if stem else ""),
+                                            source_sha("gemm.hip", "common.h")),
             "avg_launch_us": gu_us, "algorithmic_flops_per_launch": gu_flops,
         },
         **({"adamw_table_rows": adamw} if adamw else {}),
