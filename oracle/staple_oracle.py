@@ -34,6 +34,16 @@ Two precisions:
   and input-gradient contractions).  Reading: the pages fix bf16 tables and
   weights (STAPLE Table 4 caption; Figure 4 caption) but not where
   intermediates are rounded; these are the tensors a bf16 layer stores.
+  The table-row gradient is a sum, not a contraction operand: it adds the
+  unrounded dL/du (the "fp32 accumulate" of a bf16 layer), so its only
+  rounding is that of the saved g it is computed from.
+
+Arithmetic (``accum``): ``"f64"`` (the default, the oracle proper) evaluates
+every product and sum in float64.  ``"f32"`` evaluates the same definition
+with float32 arithmetic (float32 contractions and elementwise work) and the
+same bf16 rounding points.  It is a second correct evaluation of a bf16
+layer, used only to measure how far two correct evaluations of a long batch
+sum lie apart: the floor of the weight-gradient tolerance.
 """
 from __future__ import annotations
 
@@ -69,38 +79,54 @@ def bf16_round(v) -> np.ndarray:
     return out
 
 
+def _real(a) -> np.ndarray:
+    """float32 arrays stay float32 (the ``accum="f32"`` evaluation); anything
+    else becomes float64."""
+    a = np.asarray(a)
+    return a if a.dtype == np.float32 else np.asarray(a, dtype=np.float64)
+
+
 def sigmoid(z) -> np.ndarray:
-    z = np.asarray(z, dtype=np.float64)
+    z = _real(z)
     with np.errstate(over="ignore"):
-        return 1.0 / (1.0 + np.exp(-z))
+        return 1 / (1 + np.exp(-z))
 
 
 def silu(z) -> np.ndarray:
     """SiLU(z) = z * sigmoid(z)."""
-    z = np.asarray(z, dtype=np.float64)
+    z = _real(z)
     return z * sigmoid(z)
 
 
 def silu_grad(z) -> np.ndarray:
     """d/dz [z * sigmoid(z)] = sigmoid(z) * (1 + z * (1 - sigmoid(z)))."""
-    z = np.asarray(z, dtype=np.float64)
+    z = _real(z)
     s = sigmoid(z)
-    return s * (1.0 + z * (1.0 - s))
+    return s * (1 + z * (1 - s))
 
 
 def _maybe_round(a: np.ndarray, precision: str) -> np.ndarray:
     if precision == BF16:
-        return bf16_round(a)
+        # every bf16 value is a float32 value: the f32 evaluation stays float32
+        return bf16_round(a).astype(a.dtype, copy=False)
     if precision == EXACT:
         return a
     raise ValueError(f"unknown precision {precision!r}")
 
 
-def _table_rows(table, ids: np.ndarray, cols: Optional[np.ndarray]) -> np.ndarray:
+def _ftype(accum: str):
+    if accum == "f64":
+        return np.float64
+    if accum == "f32":
+        return np.float32
+    raise ValueError(f"unknown accum {accum!r}")
+
+
+def _table_rows(table, ids: np.ndarray, cols: Optional[np.ndarray], ft=np.float64) -> np.ndarray:
     """E[t_i] for every position, restricted to the given feature columns."""
     if cols is None:
-        return np.asarray(table[ids], dtype=np.float64)
-    return np.asarray(table[np.ix_(ids, cols)], dtype=np.float64)
+        return np.asarray(table[ids], dtype=ft)
+    return np.asarray(table[np.ix_(ids, cols)], dtype=ft)
 
 
 # --------------------------------------------------------------------------
@@ -180,17 +206,12 @@ def cache_lookup(uniq: Sequence[int], id_to_slot: Sequence[int]):
     return np.asarray(code, dtype=np.int32), np.asarray(miss, dtype=np.int32)
 
 
-def assemble_rows(table, uniq: Sequence[int]) -> np.ndarray:
-    """Compact leaf block R[u] = E[uniq[u]] (AI Radio episode: the active rows,
-    materialised as an autograd leaf)."""
-    return np.asarray(table[np.asarray(uniq, dtype=np.int64)])
-
-
 # --------------------------------------------------------------------------
 # Forward
 # --------------------------------------------------------------------------
 def ffn_forward(x, w_gate, w_up, w_down, table, ids, precision: str = EXACT,
-                cols: Optional[np.ndarray] = None, with_y: bool = True) -> dict:
+                cols: Optional[np.ndarray] = None, with_y: bool = True,
+                accum: str = "f64") -> dict:
     """Forward of one augmented layer.
 
     x [N, d]; w_gate, w_up [f, d]; w_down [d, f]; table [V, f] (anything that
@@ -206,23 +227,27 @@ def ffn_forward(x, w_gate, w_up, w_down, table, ids, precision: str = EXACT,
     up-projection is replaced by the token's table row, u = E[t] (STAPLE
     abstract: STEM replaces the FFN up-projections with token-indexed
     embeddings, STAPLE keeps them and adds the embeddings as a residual).
+
+    ``accum`` selects float64 (the oracle) or float32 arithmetic (see the
+    module docstring).
     """
-    x = np.asarray(x, dtype=np.float64)
+    ft = _ftype(accum)
+    x = np.asarray(x, dtype=ft)
     ids = np.asarray(ids, dtype=np.int64)
-    wg = np.asarray(w_gate, dtype=np.float64)
-    wu = None if w_up is None else np.asarray(w_up, dtype=np.float64)
+    wg = np.asarray(w_gate, dtype=ft)
+    wu = None if w_up is None else np.asarray(w_up, dtype=ft)
     if cols is not None:
         wg = wg[cols]
         wu = None if wu is None else wu[cols]
     g = x @ wg.T
-    rows = _table_rows(table, ids, cols)
+    rows = _table_rows(table, ids, cols, ft)
     u = rows if wu is None else x @ wu.T + rows
     h = _maybe_round(silu(g) * u, precision)
     out = {"g": g, "u": u, "h": h,
            "g_saved": _maybe_round(g, precision),
            "u_saved": _maybe_round(u, precision)}
     if cols is None and with_y:
-        out["y"] = h @ np.asarray(w_down, dtype=np.float64).T
+        out["y"] = h @ np.asarray(w_down, dtype=ft).T
     return out
 
 
@@ -236,9 +261,9 @@ def table_row_grad(du: np.ndarray, ids: Sequence[int], uniq: Sequence[int]) -> n
     autograd leaf; STAPLE abstract: token-specific updates).  Reading: a plain
     sum over occurrences, no averaging by count.
     """
-    du = np.asarray(du, dtype=np.float64)
+    du = _real(du)
     index_of = {int(t): k for k, t in enumerate(uniq)}
-    out = np.zeros((len(index_of),) + du.shape[1:], dtype=np.float64)
+    out = np.zeros((len(index_of),) + du.shape[1:], dtype=du.dtype)
     for i, t in enumerate(ids):
         out[index_of[int(t)]] += du[i]
     return out
@@ -246,7 +271,9 @@ def table_row_grad(du: np.ndarray, ids: Sequence[int], uniq: Sequence[int]) -> n
 
 def ffn_backward(dy, x, w_gate, w_up, w_down, fwd: dict, ids, precision: str = EXACT,
                  freeze_up: bool = False, cols: Optional[np.ndarray] = None,
-                 uniq: Optional[Sequence[int]] = None, with_dx: bool = True) -> dict:
+                 uniq: Optional[Sequence[int]] = None, with_dx: bool = True,
+                 accum: str = "f64", recompute_h: bool = False,
+                 with_dw: bool = True) -> dict:
     """Backward of one augmented layer given the upstream gradient dy [N, d].
 
     With ``cols`` set, ``fwd`` must come from ``ffn_forward(..., cols=cols)`` and
@@ -260,33 +287,49 @@ def ffn_backward(dy, x, w_gate, w_up, w_down, fwd: dict, ids, precision: str = E
 
     ``w_up=None`` (STEM, see ffn_forward): there is no dw_up and dx has no
     up-projection term.
+
+    In the bf16 precision du and dg are rounded where they become operands of
+    the weight- and input-gradient contractions, while the table-row
+    gradient sums the unrounded dL/du (returned as ``du_sum``): a sum of
+    fp32 values accumulated in fp32 (reading of "bf16 in, fp32 accumulate").
+
+    ``recompute_h``: the backward of a caller that kept no h forms it again
+    from the saved activations, h = silu(g_saved) * u_saved (rounded as h is),
+    for dw_down; everything else is unchanged.  ``with_dw=False`` leaves the
+    weight gradients out (for callers that check only the row gradients).
     """
-    dy = np.asarray(dy, dtype=np.float64)
-    x = np.asarray(x, dtype=np.float64)
-    wd = np.asarray(w_down, dtype=np.float64)
-    wg = np.asarray(w_gate, dtype=np.float64)
-    wu = None if w_up is None else np.asarray(w_up, dtype=np.float64)
+    ft = _ftype(accum)
+    dy = np.asarray(dy, dtype=ft)
+    x = np.asarray(x, dtype=ft)
+    wd = np.asarray(w_down, dtype=ft)
+    wg = np.asarray(w_gate, dtype=ft)
+    wu = None if w_up is None else np.asarray(w_up, dtype=ft)
     if cols is not None:
         wd = wd[:, cols]
         wg = wg[cols]
         wu = None if wu is None else wu[cols]
-    g = fwd["g_saved"]
-    u = fwd["u_saved"]
-    h = fwd["h"]
+    g = np.asarray(fwd["g_saved"], dtype=ft)
+    u = np.asarray(fwd["u_saved"], dtype=ft)
+    if recompute_h:
+        h = _maybe_round(silu(g) * u, precision)
+    else:
+        h = np.asarray(fwd["h"], dtype=ft)
 
     dh = dy @ wd                                     # dL/dh = W_down^T dy
-    du = _maybe_round(dh * silu(g), precision)       # dL/du = dh * silu(g)
+    du_sum = dh * silu(g)                            # dL/du = dh * silu(g)
+    du = _maybe_round(du_sum, precision)
     dg = _maybe_round(dh * u * silu_grad(g), precision)  # dL/dg = dh * u * silu'(g)
 
     if uniq is None:
         uniq = sorted(set(int(t) for t in ids))
     out = {
-        "dh": dh, "du": du, "dg": dg,
-        "d_rows": table_row_grad(du, ids, uniq),    # dL/dE[t] summed over occurrences
-        "dw_down": dy.T @ h,                         # dL/dW_down = sum_i dy_i h_i^T
-        "dw_gate": dg.T @ x,                         # dL/dW_gate = sum_i dg_i x_i^T
+        "dh": dh, "du": du, "dg": dg, "du_sum": du_sum,
+        "d_rows": table_row_grad(du_sum, ids, uniq),  # dL/dE[t] summed over occurrences
     }
-    if not freeze_up and wu is not None:
+    if with_dw:
+        out["dw_down"] = dy.T @ h                    # dL/dW_down = sum_i dy_i h_i^T
+        out["dw_gate"] = dg.T @ x                    # dL/dW_gate = sum_i dg_i x_i^T
+    if with_dw and not freeze_up and wu is not None:
         out["dw_up"] = du.T @ x                      # dL/dW_up = sum_i du_i x_i^T
     if cols is None and with_dx:
         out["dx"] = dg @ wg                          # dL/dx = W_gate^T dg (+ W_up^T du)
@@ -338,26 +381,3 @@ def adamw_rows(table, m, v, rows: Sequence[int], grad, lr: float, weight_decay: 
         v[r] = beta2 * v[r] + (1.0 - beta2) * g[k] * g[k]
         p[r] -= lr / bc1 * m[r] / (np.sqrt(v[r]) / math.sqrt(bc2) + eps)
     return p, m, v
-
-
-# --------------------------------------------------------------------------
-# Work counts used for throughput figures
-# --------------------------------------------------------------------------
-def ffn_flops(n_tokens: int, d_model: int, d_ff: int, backward: bool,
-              freeze_up: bool = False) -> int:
-    """Multiply-add FLOPs (2 per MAC) of the layer's contractions."""
-    ndf = n_tokens * d_model * d_ff
-    fwd = 6 * ndf                        # gate, up, down
-    if not backward:
-        return fwd
-    bwd = 2 * ndf + 2 * ndf + 2 * ndf + 4 * ndf   # dh, dW_down, dW_gate, dx (two terms)
-    if not freeze_up:
-        bwd += 2 * ndf                   # dW_up
-    return fwd + bwd
-
-
-def decode_layer_bytes(n_tokens: int, d_model: int, d_ff: int, n_unique: int,
-                       elem: int = 2) -> int:
-    """Bytes a decode layer must move at least: the three weight matrices once,
-    one table row per unique token, x in and y out."""
-    return (3 * d_model * d_ff + n_unique * d_ff + 2 * n_tokens * d_model) * elem

@@ -281,7 +281,57 @@ def test_bf16_mode_rounding_points_on_a_scalar_layer():
     b = O.ffn_backward([[dy]], [[x]], [[wg]], [[wu]], [[wd]], fwd, [0], precision=O.BF16)
     assert b["du"][0, 0] == du and b["dg"][0, 0] == dg
     assert b["dw_up"][0, 0] == du * x and b["dw_gate"][0, 0] == dg * x
-    assert b["dw_down"][0, 0] == dy * h and b["d_rows"][0, 0] == du
+    assert b["dw_down"][0, 0] == dy * h
+    # the table-row gradient sums dL/du before its bf16 rounding (an fp32 sum,
+    # not a contraction operand): here the two differ
+    du_sum = dh * gs * s
+    assert bf(du_sum) != du_sum
+    assert b["d_rows"][0, 0] == du_sum and b["du_sum"][0, 0] == du_sum
+    # h recomputed from the saved (rounded) g and u for dW_down
+    br = O.ffn_backward([[dy]], [[x]], [[wg]], [[wu]], [[wd]], fwd, [0], precision=O.BF16,
+                        recompute_h=True)
+    h_rec = bf(gs * s * us)
+    assert br["dw_down"][0, 0] == dy * h_rec
+    for k in ("du", "dg", "dw_up", "dw_gate", "d_rows", "dx"):
+        assert br[k][0, 0] == b[k][0, 0], k
+
+
+def test_recomputed_h_in_bf16_is_silu_of_the_saved_activations():
+    rng = np.random.default_rng(33)
+    x, wg, wu, wd, e, ids, dy = _rand_layer(rng, 64, 16, 32, 6)
+    fwd = O.ffn_forward(x, wg, wu, wd, e, ids, precision=O.BF16)
+    b = O.ffn_backward(dy, x, wg, wu, wd, fwd, ids, precision=O.BF16, recompute_h=True)
+    g, u = fwd["g_saved"], fwd["u_saved"]
+    h_rec = torch.tensor(g / (1 + np.exp(-g)) * u).to(torch.bfloat16).double().numpy()
+    np.testing.assert_allclose(b["dw_down"], dy.T @ h_rec, rtol=1e-12, atol=1e-12)
+    assert np.any(h_rec != fwd["h"])   # the saved activations' rounding shows
+
+
+def test_recomputed_h_equals_the_forward_h_without_rounding():
+    rng = np.random.default_rng(32)
+    x, wg, wu, wd, e, ids, dy = _rand_layer(rng, 40, 8, 16, 5)
+    fwd = O.ffn_forward(x, wg, wu, wd, e, ids)
+    a = O.ffn_backward(dy, x, wg, wu, wd, fwd, ids)
+    b = O.ffn_backward(dy, x, wg, wu, wd, fwd, ids, recompute_h=True)
+    for k in ("dw_down", "dw_gate", "dw_up", "d_rows", "dx"):
+        np.testing.assert_allclose(b[k], a[k], rtol=1e-13, atol=1e-13)
+
+
+def test_bf16_table_row_gradient_sums_the_unrounded_du():
+    # d_rows = sum over occurrences of dh * silu(g_saved), with no rounding of
+    # the summands; a version that summed the rounded du would differ
+    rng = np.random.default_rng(31)
+    x, wg, wu, wd, e, _, dy = _rand_layer(rng, 200, 16, 24, 3)
+    ids = rng.integers(0, 3, size=200)
+    fwd = O.ffn_forward(x, wg, wu, wd, e, ids, precision=O.BF16)
+    b = O.ffn_backward(dy, x, wg, wu, wd, fwd, ids, precision=O.BF16)
+    dh = dy @ wd
+    want = dh * O.silu(fwd["g_saved"])
+    uniq = np.unique(ids)
+    brute = np.stack([want[ids == t].sum(axis=0) for t in uniq])
+    np.testing.assert_allclose(b["d_rows"], brute, rtol=1e-12, atol=1e-13)
+    rounded = np.stack([O.bf16_round(want)[ids == t].sum(axis=0) for t in uniq])
+    assert np.max(np.abs(rounded - brute)) > 1e-6
 
 
 # ---------------------------------------------------------------- dedup
