@@ -465,8 +465,14 @@ staple_status_t staple_cache_refresh(const void* table, int64_t vocab, int64_t d
 /* ------------------------------------------------------------------------
  * Backward of one augmented layer with the table-row gradient.
  *   dy [n_tokens x d_model] (dtype): upstream gradient of y.
- *   saved_g, saved_u, saved_h: the forward's save_g/save_u/save_h (required).
- *   sorted_pos, inv, seg_start, n_unique: staple_dedup's outputs for this batch.
+ *   saved_g, saved_u: the forward's save_g/save_u (required).
+ *   saved_h: the forward's save_h, or NULL: h is then recomputed from the
+ *     saved g and u (h = silu(g) * u, rounded to dtype) into the workspace,
+ *     so dw_down may differ from a call with the forward's h by the rounding
+ *     of g and u; every other output is the same either way.
+ *   sorted_pos, inv, seg_start, n_unique: staple_dedup's outputs for this batch;
+ *     *n_unique <= max_unique (a larger value sets the device error word and
+ *     d_rows is not written).
  * Outputs (each overwritten, not accumulated):
  *   d_rows [max_unique x d_ff] fp32: row u (< *n_unique) is the sum, over the
  *     positions holding token uniq[u], of dL/du at that position (a plain sum,
@@ -479,8 +485,13 @@ staple_status_t staple_cache_refresh(const void* table, int64_t vocab, int64_t d
  *   w_up NULL: the STEM layer (saved_u = E[t] from its forward); dx = dL/dg
  *     W_gate, d_rows as above, dw_up neither computed nor written.
  * In bf16 the backward reads bf16 g and u, forms dL/du and dL/dg in fp32 and
- * rounds them to bf16 once; every contraction accumulates in fp32; d_rows sums
- * the bf16 dL/du values in fp32.
+ * rounds them to bf16 once, as operands of the weight- and input-gradient
+ * contractions; every contraction accumulates in fp32; d_rows sums the fp32
+ * dL/du values before that rounding, in fp32 (a fixed order: the result is
+ * deterministic).
+ * Workspace (staple_ffn_bwd_workspace_bytes): [dg | du] of n_tokens x 2 d_ff
+ * (dtype), an n_tokens x d_ff fp32 block (fp32 dL/du, then the recomputed
+ * h), and the segment sum's partial rows.
  * ------------------------------------------------------------------------ */
 size_t staple_ffn_bwd_workspace_bytes(int64_t n_tokens, int64_t d_model, int64_t d_ff,
                                       int32_t dtype);

@@ -36,30 +36,50 @@ def assert_close(got, ref, name, rel_l2=REL_L2, max_abs=MAX_ABS):
     return rel, mx
 
 
-def bf16_ulp(v):
+def bf16_step(v):
     """Spacing of bfloat16 values at |v| (8 significant bits)."""
     a = np.maximum(np.abs(np.asarray(v, dtype=np.float64)), 2.0 ** -126)
     return np.ldexp(1.0, np.floor(np.log2(a)).astype(np.int64) - 7)
 
 
-def assert_close_long_sum(got, ref, name, rel_l2=REL_L2, max_abs=MAX_ABS):
-    """Bound for outputs that are sums over a whole large batch (weight
-    gradients of a 32768-token batch, |value| ~ 100): relative L2 <= rel_l2 and
-    max-abs <= max(max_abs, one bf16 ulp at the output's RMS magnitude).
-
-    Derivation: a bf16 intermediate (h, du, dg) computed in fp32 lands on the
-    neighbouring bf16 value, relative to the float64 oracle's rounding, for a
-    small fraction rho of elements (last-bit differences of fp32 accumulation
-    order).  Each such flip moves one term of an N-term sum by ~2^-8 of that
-    term, so the error has standard deviation ~ sqrt(rho) * 2^-8 * rms(output),
-    independent of the element's own magnitude.  An absolute 3e-2 is below that
-    floor once rms(output) reaches ~100; one bf16 ulp at the RMS magnitude sits
-    above it for any rho < 1."""
+def assert_close_stored_bf16(got, ref, name, rel_l2=REL_L2, max_abs=MAX_ABS):
+    """A tensor the bf16 path stores in bf16 (h, the saved g and u): relative
+    L2 <= rel_l2 and, element by element, |got - ref| <= max(max_abs, one bf16
+    step at |ref|): a value that lands on the neighbouring bf16 value of the
+    oracle's is one step away, which exceeds 3e-2 once |ref| >= 4."""
     got = np.asarray(got, dtype=np.float64)
     ref = np.asarray(ref, dtype=np.float64)
     rel, mx = errors(got, ref)
-    rms = float(np.sqrt(np.mean(ref * ref))) if ref.size else 0.0
-    bound = max(max_abs, float(bf16_ulp(rms)))
-    print(f"  {name}: rel_l2={rel:.3e} max_abs={mx:.3e} bound={bound:.3e} rms={rms:.3e}", flush=True)
-    assert rel <= rel_l2 and mx <= bound, f"{name}: rel_l2={rel:.3e}, max_abs={mx:.3e} (<= {bound:.3e})"
+    over = np.abs(got - ref) > np.maximum(max_abs, bf16_step(ref))
+    print(f"  {name}: rel_l2={rel:.3e} max_abs={mx:.3e} beyond max(3e-2, 1 bf16 step): "
+          f"{int(over.sum())}", flush=True)
+    assert rel <= rel_l2 and not over.any(), f"{name}: rel_l2={rel:.3e}, {int(over.sum())} elements out"
     return rel, mx
+
+
+# Multiple of the measured floor allowed for the GPU's max-abs error on
+# outputs that sum over a whole large batch.  The floor is how far two correct
+# evaluations (float64 and float32 arithmetic, same bf16 rounding points) lie
+# apart on the same inputs; the GPU accumulates each dot product in fp32
+# through a longer sequential chain (one MFMA k-group after another) than a
+# blocked BLAS, so its rounding flips of the bf16 intermediates are somewhat
+# more frequent than the float32 evaluation's.
+FLOOR_FACTOR = 3.0
+
+
+def assert_close_floor(got, ref, alt, name, factor=FLOOR_FACTOR, rel_l2=REL_L2, max_abs=MAX_ABS):
+    """GPU output `got` against the float64 oracle `ref`, with `alt` the
+    oracle's float32 evaluation of the same definition on the same inputs:
+    relative L2 <= rel_l2 and max-abs <= max(max_abs, factor * floor), where
+    floor = max|alt - ref| is measured here, not assumed."""
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    alt = np.asarray(alt, dtype=np.float64)
+    rel, mx = errors(got, ref)
+    floor = float(np.max(np.abs(alt - ref))) if ref.size else 0.0
+    bound = max(max_abs, factor * floor)
+    print(f"  {name}: rel_l2={rel:.3e} max_abs={mx:.3e} floor={floor:.3e} "
+          f"(x{mx / max(floor, 1e-300):.2f}) bound={bound:.3e}", flush=True)
+    assert rel <= rel_l2 and mx <= bound, \
+        f"{name}: rel_l2={rel:.3e}, max_abs={mx:.3e} (<= {bound:.3e}, floor {floor:.3e})"
+    return rel, mx, floor

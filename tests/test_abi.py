@@ -51,8 +51,10 @@ def test_workspace_queries(lib):
     assert lib.staple_dedup_workspace_bytes(32768) == 32768 * 8
     assert lib.staple_dedup_workspace_bytes(4097) == 8192 * 8
     dgu = ((100 * 256 * 2 + 255) // 256) * 256          # [dg | du] in bf16
+    aux = ((100 * 128 * 4 + 255) // 256) * 256           # fp32 du, then a recomputed h
     partials = 2 * ((100 + 31) // 32) * 128 * 4            # segment-sum chunk partials
-    assert lib.staple_ffn_bwd_workspace_bytes(100, 64, 128, 1) == dgu + partials
+    assert lib.staple_ffn_bwd_workspace_bytes(100, 64, 128, 1) == dgu + aux + partials
+    assert lib.staple_ffn_bwd_workspace_bytes(100, 64, 128, 0) == 2 * dgu + aux + partials
     assert lib.staple_ffn_fwd_workspace_bytes(100, 64, 100, 1) == 0   # d_ff not a multiple of 64
     assert lib.staple_cache_build_workspace_bytes(100352) == 131072 * 8
     # decode forward: [h][split-K partials, 8 splits of n x d_model fp32]

@@ -13,7 +13,8 @@ import pytest
 
 import staple_synth as S
 from oracle import staple_oracle as O
-from tests.helpers import assert_close, assert_close_long_sum, errors, to_dev, to_np
+from tests.helpers import (assert_close, assert_close_floor, assert_close_stored_bf16, errors,
+                           to_dev, to_np)
 
 pytestmark = pytest.mark.gpu
 
@@ -575,6 +576,36 @@ def test_freeze_up_leaves_dw_up_untouched_and_rest_identical(st, dev):
     _compare_layer(b, of, ob, u, "frozen", freeze_up=True)
 
 
+@pytest.mark.parametrize("dtype,n,d,f", [("bf16", 300, 256, 512), ("f32", 200, 128, 256)])
+def test_backward_without_saved_h_recomputes_it(st, dev, dtype, n, d, f):
+    """saved_h NULL: h is formed again from the saved g and u for dW_down; every
+    other output has the bits of the call with the forward's h, and dW_down
+    matches the oracle's backward with the recomputed h."""
+    import torch
+    _log(f"recomputed h {dtype} n={n}")
+    inp = S.host_layer_inputs(n, d, f, 90, dtype=dtype, seed=9)
+    res = _run_layer(st, dev, inp)
+    x, wg, wu, wd, dy = (to_dev(getattr(inp, k), dtype, dev)
+                         for k in ("x", "w_gate", "w_up", "w_down", "dy"))
+    fwd, dd = res["fwd"], res["dd"]
+    b = st.staple_ffn_bwd_table_grad(dy, x, wg, wu, wd, fwd["g"], fwd["u"], None,
+                                     dd["sorted_pos"], dd["seg_start"], dd["n_unique"],
+                                     inv=dd["inv"], out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    _no_device_error(st)
+    u = int(dd["n_unique"].item())
+    assert torch.equal(b["d_rows"][:u], res["bwd"]["d_rows"][:u])
+    for k in ("dx", "dw_gate", "dw_up"):
+        assert torch.equal(b[k], res["bwd"][k]), k
+    prec = O.BF16 if dtype == "bf16" else O.EXACT
+    g = {k: inp.as_f64(k) for k in ("x", "w_gate", "w_up", "w_down", "table", "dy")}
+    of = O.ffn_forward(g["x"], g["w_gate"], g["w_up"], g["w_down"], g["table"], inp.ids,
+                       precision=prec)
+    ob = O.ffn_backward(g["dy"], g["x"], g["w_gate"], g["w_up"], g["w_down"], of, inp.ids,
+                        precision=prec, recompute_h=True)
+    assert_close(to_np(b["dw_down"]), ob["dw_down"], f"recomputed-h dw_down {dtype}")
+
+
 def test_bf16_outputs_stored_in_bf16(st, dev):
     inp = S.host_layer_inputs(256, 128, 256, 100, dtype="bf16", seed=8)
     res = _run_layer(st, dev, inp, out_f32=False)
@@ -636,53 +667,153 @@ def _device_inputs(dev, w, n_tokens, seed_base=0):
     return ids, t
 
 
+def _tile_samples(total, block, rng):
+    """One index in every block of `block` consecutive indices, plus the
+    first and the last index: every tile of that size holds a sample."""
+    starts = np.arange(0, total, block)
+    idx = np.minimum(starts + rng.integers(0, block, size=len(starts)), total - 1)
+    return np.unique(np.concatenate([[0, total - 1], idx]))
+
+
+def _nan(shape, dtype, dev):
+    import torch
+    return torch.full(shape, float("nan"), dtype=dtype, device=dev)
+
+
+def _train_shape_check(st, dev, w, ids, t, rows_s, cols_s, label):
+    """One full-size training batch: forward and backward on the GPU with
+    every output NaN-poisoned first; returns the GPU and oracle y on the
+    sampled tokens.  Integer outputs are compared in full, y, h, g, u and dx
+    on the sampled tokens (every feature), d_rows and the weight gradients on
+    the sampled features (every token), the sums over the whole batch against
+    a bound measured from the oracle's float32 evaluation."""
+    import torch
+    n, d, f = w.n_tokens, w.d_model, w.d_ff
+    bf = torch.bfloat16
+    idt = torch.from_numpy(ids).to(dev)
+    dd = st.staple_dedup(idt, w.vocab)
+    rows = st.staple_gather_rows(t["table"], dd["uniq"], dd["n_unique"])
+    fout = {"y": _nan((n, d), torch.float32, dev), "g": _nan((n, f), bf, dev),
+            "u": _nan((n, f), bf, dev), "h": _nan((n, f), bf, dev)}
+    fwd = st.staple_ffn_fwd(t["x"], t["w_gate"], t["w_up"], t["w_down"], rows, dd["inv"],
+                            out=fout)
+    bout = {"d_rows": _nan((n, f), torch.float32, dev), "dx": _nan((n, d), torch.float32, dev),
+            "dw_gate": _nan((f, d), torch.float32, dev), "dw_up": _nan((f, d), torch.float32, dev),
+            "dw_down": _nan((d, f), torch.float32, dev)}
+    bwd = st.staple_ffn_bwd_table_grad(t["dy"], t["x"], t["w_gate"], t["w_up"], t["w_down"],
+                                       fwd["g"], fwd["u"], fwd["h"], dd["sorted_pos"],
+                                       dd["seg_start"], dd["n_unique"], inv=dd["inv"], out=bout)
+    torch.cuda.synchronize()
+    _no_device_error(st)
+    uniq, inv, sp, ss = O.dedup(ids)
+    u = len(uniq)
+    assert int(dd["n_unique"].item()) == u
+    np.testing.assert_array_equal(to_np(dd["uniq"])[:u], uniq)
+    np.testing.assert_array_equal(to_np(dd["inv"]), inv)
+    np.testing.assert_array_equal(to_np(dd["sorted_pos"]), sp)
+    np.testing.assert_array_equal(to_np(dd["seg_start"])[: u + 1], ss)
+    # no output element is left unwritten
+    for k, v in fwd.items():
+        assert not bool(torch.isnan(v).any()), f"{label}: {k} has unwritten elements"
+    assert not bool(torch.isnan(bwd["d_rows"][:u]).any()), f"{label}: d_rows has unwritten rows"
+    for k in ("dx", "dw_gate", "dw_up", "dw_down"):
+        assert not bool(torch.isnan(bwd[k]).any()), f"{label}: {k} has unwritten elements"
+    f64 = lambda a: a.float().cpu().numpy().astype(np.float64)
+    table = RowSubset(uniq, f64(t["table"][torch.from_numpy(uniq.astype(np.int64)).to(dev)]))
+    x, wg, wu, wdn, dy = (f64(t[k]) for k in ("x", "w_gate", "w_up", "w_down", "dy"))
+    rs = torch.from_numpy(rows_s).to(dev)
+    # forward and dx on sampled tokens (all features)
+    of_r = O.ffn_forward(x[rows_s], wg, wu, wdn, table, ids[rows_s], precision=O.BF16)
+    y_gpu = f64(fwd["y"][rs])
+    assert_close(y_gpu, of_r["y"], f"{label} y[rows]")
+    assert_close_stored_bf16(f64(fwd["h"][rs]), of_r["h"], f"{label} h[rows]")
+    assert_close_stored_bf16(f64(fwd["g"][rs]), of_r["g_saved"], f"{label} g[rows]")
+    assert_close_stored_bf16(f64(fwd["u"][rs]), of_r["u_saved"], f"{label} u[rows]")
+    ob_r = O.ffn_backward(dy[rows_s], x[rows_s], wg, wu, wdn, of_r, ids[rows_s], precision=O.BF16,
+                          with_dw=False)
+    assert_close(f64(bwd["dx"][rs]), ob_r["dx"], f"{label} dx[rows]")
+    # table-row and weight gradients on sampled features (all tokens), with the
+    # float32 evaluation giving the floor
+    ob = {}
+    for acc in ("f64", "f32"):
+        of_c = O.ffn_forward(x, wg, wu, wdn, table, ids, precision=O.BF16, cols=cols_s, accum=acc)
+        ob[acc] = O.ffn_backward(dy, x, wg, wu, wdn, of_c, ids, precision=O.BF16, cols=cols_s,
+                                 uniq=uniq, accum=acc)
+    cs = torch.from_numpy(cols_s).to(dev)
+    got = {"d_rows": f64(bwd["d_rows"][:u][:, cs]), "dw_gate": f64(bwd["dw_gate"][cs]),
+           "dw_up": f64(bwd["dw_up"][cs]), "dw_down": f64(bwd["dw_down"][:, cs])}
+    for k, v in got.items():
+        assert_close_floor(v, ob["f64"][k], ob["f32"][k], f"{label} {k}[cols]")
+    return y_gpu, of_r["y"]
+
+
+@pytest.mark.timeout(600)
 @pytest.mark.parametrize("wname", ["olmo1b", "olmo7b"])
 def test_olmo_train_shape_sampled(st, dev, wname):
     """The training batch at full size, bf16 (1B: 32768 Zipf tokens, d_model
-    2048, d_ff 8192; 7B: 16384 tokens, 4096, 11008; vocab 100352): every
-    integer output in full; y, dx on sampled tokens and d_rows, dW on sampled
-    features, each computed by the oracle over the whole batch."""
-    import torch
+    2048, d_ff 8192; 7B: 16384 tokens, 4096, 11008; vocab 100352).  The
+    sampled tokens hold one token of every 256 (an M-tile of the GEMMs), the
+    sampled features one of every 128 (an N-tile of the gate/up GEMM, whose
+    256 columns interleave 128 gate and 128 up features), so every tile of
+    every GEMM has checked outputs.  The 1B batch runs a second time with an
+    all-zero table (the dense layer the zero-initialised table starts from),
+    and the table's own contribution y(E) - y(0) is compared on its own."""
     w = {"olmo1b": S.OLMO1B_TRAIN, "olmo7b": S.OLMO7B_TRAIN}[wname]
-    n, d, f = w.n_tokens, w.d_model, w.d_ff
+    n, f = w.n_tokens, w.d_ff
     _log(f"{wname} train-shape sampled parity")
+    ids, t = _device_inputs(dev, w, n)
+    rng = np.random.default_rng(0)
+    rows_s = _tile_samples(n, 256, rng)
+    cols_s = _tile_samples(f, 128, rng)
+    y_e, ref_e = _train_shape_check(st, dev, w, ids, t, rows_s, cols_s, wname)
+    if wname == "olmo1b":
+        _log(f"{wname} train-shape sampled parity, zero table")
+        t["table"].zero_()
+        y_0, ref_0 = _train_shape_check(st, dev, w, ids, t, rows_s, cols_s, wname + " E=0")
+        assert_close(y_e - y_0, ref_e - ref_0, f"{wname} y(E) - y(0)[rows]")
+
+
+@pytest.mark.timeout(600)
+def test_olmo1b_hot_row_gradients_on_every_feature(st, dev):
+    """The table-row gradients of the ten most frequent IDs of the 32768-token
+    batch (the hottest sums ~4400 positions), on all 8192 features, against
+    the oracle's sum of the unrounded dL/du over each ID's positions."""
+    import torch
+    w = S.OLMO1B_TRAIN
+    n, f = w.n_tokens, w.d_ff
+    _log("olmo1b hot-row gradients")
     ids, t = _device_inputs(dev, w, n)
     idt = torch.from_numpy(ids).to(dev)
     dd = st.staple_dedup(idt, w.vocab)
     rows = st.staple_gather_rows(t["table"], dd["uniq"], dd["n_unique"])
-    fwd = st.staple_ffn_fwd(t["x"], t["w_gate"], t["w_up"], t["w_down"], rows, dd["inv"],
-                            out_dtype=torch.float32, save=True)
+    fwd = st.staple_ffn_fwd(t["x"], t["w_gate"], t["w_up"], t["w_down"], rows, dd["inv"], save=True)
     bwd = st.staple_ffn_bwd_table_grad(t["dy"], t["x"], t["w_gate"], t["w_up"], t["w_down"],
                                        fwd["g"], fwd["u"], fwd["h"], dd["sorted_pos"],
                                        dd["seg_start"], dd["n_unique"], inv=dd["inv"],
                                        out_dtype=torch.float32)
     torch.cuda.synchronize()
     _no_device_error(st)
-    uniq, inv, sp, ss = O.dedup(ids)
-    u = len(uniq)
-    assert int(dd["n_unique"].item()) == u
-    np.testing.assert_array_equal(to_np(dd["inv"]), inv)
-    np.testing.assert_array_equal(to_np(dd["sorted_pos"]), sp)
-    np.testing.assert_array_equal(to_np(dd["seg_start"])[: u + 1], ss)
+    uniq, counts = np.unique(ids, return_counts=True)
+    order = np.argsort(-counts, kind="stable")[:10]
+    top = uniq[order]
+    _log(f"  counts of the ten IDs: {counts[order].tolist()}")
     f64 = lambda a: a.float().cpu().numpy().astype(np.float64)
-    table = RowSubset(uniq, f64(t["table"][torch.from_numpy(uniq.astype(np.int64)).to(dev)]))
-    x, wg, wu, wdn, dy = (f64(t[k]) for k in ("x", "w_gate", "w_up", "w_down", "dy"))
-    rng = np.random.default_rng(0)
-    rows_s = np.concatenate([[0, n - 1], rng.choice(n, 30, replace=False)])
-    cols_s = np.concatenate([[0, f - 1], rng.choice(f, 14, replace=False)])
-    # forward and dx on sampled tokens (all features)
-    of_r = O.ffn_forward(x[rows_s], wg, wu, wdn, table, ids[rows_s], precision=O.BF16)
-    assert_close(f64(fwd["y"])[rows_s], of_r["y"], "y[rows]")
-    ob_r = O.ffn_backward(dy[rows_s], x[rows_s], wg, wu, wdn, of_r, ids[rows_s], precision=O.BF16)
-    assert_close(f64(bwd["dx"])[rows_s], ob_r["dx"], "dx[rows]")
-    # table-row and weight gradients on sampled features (all tokens)
-    of_c = O.ffn_forward(x, wg, wu, wdn, table, ids, precision=O.BF16, cols=cols_s)
-    ob_c = O.ffn_backward(dy, x, wg, wu, wdn, of_c, ids, precision=O.BF16, cols=cols_s, uniq=uniq)
-    cs = torch.from_numpy(cols_s).to(dev)
-    assert_close(f64(bwd["d_rows"][:u][:, cs]), ob_c["d_rows"], "d_rows[:, cols]")
-    assert_close_long_sum(f64(bwd["dw_gate"][cs]), ob_c["dw_gate"], "dw_gate[cols]")
-    assert_close_long_sum(f64(bwd["dw_up"][cs]), ob_c["dw_up"], "dw_up[cols]")
-    assert_close_long_sum(f64(bwd["dw_down"][:, cs]), ob_c["dw_down"], "dw_down[:, cols]")
+    wg, wu, wdn = (f64(t[k]) for k in ("w_gate", "w_up", "w_down"))
+    ref, alt = [], []
+    for tok in top:
+        pos = np.flatnonzero(ids == tok)
+        pt = torch.from_numpy(pos).to(dev)
+        x_p, dy_p = f64(t["x"][pt]), f64(t["dy"][pt])
+        table = RowSubset(np.array([tok]), f64(t["table"][int(tok):int(tok) + 1]))
+        for acc, dst in (("f64", ref), ("f32", alt)):
+            fw = O.ffn_forward(x_p, wg, wu, wdn, table, ids[pos], precision=O.BF16, with_y=False,
+                               accum=acc)
+            bw = O.ffn_backward(dy_p, x_p, wg, wu, wdn, fw, ids[pos], precision=O.BF16,
+                                uniq=[int(tok)], with_dx=False, with_dw=False, accum=acc)
+            dst.append(bw["d_rows"][0])
+    uidx = torch.from_numpy(np.searchsorted(uniq, top)).to(dev)
+    got = f64(bwd["d_rows"][uidx])
+    assert_close_floor(got, np.stack(ref), np.stack(alt), "hot-row d_rows (10 IDs x 8192)")
 
 
 @pytest.mark.parametrize("wname", ["olmo1b", "olmo7b"])
@@ -697,9 +828,10 @@ def test_olmo_decode_layer_full(st, dev, wname):
     ids, t = _device_inputs(dev, w, w.n_tokens)
     idt = torch.from_numpy(ids).to(dev)
     fwd = st.staple_ffn_fwd(t["x"], t["w_gate"], t["w_up"], t["w_down"], t["table"], idt,
-                            out_dtype=torch.float32)
+                            out={"y": _nan((w.n_tokens, w.d_model), torch.float32, dev)})
     torch.cuda.synchronize()
     _no_device_error(st)
+    assert not bool(torch.isnan(fwd["y"]).any())
     f64 = lambda a: a.float().cpu().numpy().astype(np.float64)
     uniq = np.unique(ids)
     table = RowSubset(uniq, f64(t["table"][torch.from_numpy(uniq.astype(np.int64)).to(dev)]))

@@ -75,3 +75,59 @@ def test_host_adamw_refuses_rows_outside_the_table():
     with pytest.raises(RuntimeError):       # step 0 has no bias correction
         st.staple_adamw_rows_host(table, m, v, torch.tensor([1, 2], dtype=torch.int32), grad,
                                   lr=1e-3, weight_decay=0.0, step=0)
+
+
+def test_host_adamw_from_several_threads_at_once_matches_serial_calls():
+    """The library's host threads are one persistent pool shared by every call:
+    calls made at the same time from several threads (each on its own table)
+    take turns and give the bits of the same calls made one after another."""
+    import threading
+    import torch
+    st = _lib()
+    rng = np.random.default_rng(12)
+    vocab, f, n = 600, 512, 400
+    jobs = []
+    for k in range(6):
+        rows = torch.from_numpy(np.sort(rng.choice(vocab, n, replace=False)).astype(np.int32))
+        grad = torch.from_numpy(rng.normal(0, 1, (n, f)).astype(np.float32))
+        p0 = torch.from_numpy(rng.normal(0, 0.05, (vocab, f)).astype(np.float32)).to(torch.bfloat16)
+        jobs.append((rows, grad, p0))
+
+    def run(rows, grad, p0):
+        t, m, v = p0.clone(), torch.zeros(vocab, f), torch.zeros(vocab, f)
+        for step in (1, 2):
+            st.staple_adamw_rows_host(t, m, v, rows, grad, lr=1e-3, weight_decay=1e-2, step=step,
+                                      n_threads=8)
+        return t, m, v
+
+    serial = [run(*j) for j in jobs]
+    out = [None] * len(jobs)
+    threads = [threading.Thread(target=lambda i=i: out.__setitem__(i, run(*jobs[i])))
+               for i in range(len(jobs))]
+    for th in threads:
+        th.start()
+    for th in threads:
+        th.join()
+    for a, b in zip(serial, out):
+        for x, y in zip(a, b):
+            assert torch.equal(x, y)
+
+
+def test_stage_misses_packs_rows_on_the_host_threads():
+    """staple_stage_misses packs host_table[ids] into the staging buffer on the
+    library's host threads (a 9.4 MB pack uses several) before it queues the
+    copy to the device; without a GPU the copy itself fails with
+    STAPLE_ERR_HIP, after the pack."""
+    import torch
+    st = _lib()
+    if torch.cuda.is_available():
+        pytest.skip("checks the host pack only on a host without a GPU")
+    rng = np.random.default_rng(13)
+    vocab, f, n = 1000, 8192, 300
+    table = rng.normal(0, 1, (vocab, f)).astype(np.float32)
+    ids = rng.choice(vocab, n, replace=False).astype(np.int32)
+    staging = np.zeros((n, f), dtype=np.float32)
+    status = st.lib().staple_stage_misses(table.ctypes.data, vocab, f, 0, ids.ctypes.data, n,
+                                          staging.ctypes.data, 16, None)
+    assert status == -4
+    np.testing.assert_array_equal(staging, table[ids])

@@ -478,7 +478,7 @@ def staple_cache_refresh(table: torch.Tensor, uniq: torch.Tensor, code: torch.Te
 def staple_ffn_bwd_table_grad(dy: torch.Tensor, x: torch.Tensor, w_gate: torch.Tensor,
                               w_up: Optional[torch.Tensor], w_down: torch.Tensor,
                               saved_g: torch.Tensor,
-                              saved_u: torch.Tensor, saved_h: torch.Tensor,
+                              saved_u: torch.Tensor, saved_h: Optional[torch.Tensor],
                               sorted_pos: torch.Tensor, seg_start: torch.Tensor,
                               n_unique: torch.Tensor, *, inv: torch.Tensor,
                               max_unique: Optional[int] = None,
@@ -487,7 +487,8 @@ def staple_ffn_bwd_table_grad(dy: torch.Tensor, x: torch.Tensor, w_gate: torch.T
                               stream=None) -> dict:
     """Backward with the table-row gradient: d_rows, dx, dw_gate, dw_up, dw_down
     (w_up None: the STEM layer, no dw_up).  sorted_pos, inv, seg_start, n_unique are
-    staple_dedup's outputs for the batch."""
+    staple_dedup's outputs for the batch; saved_h None recomputes h from saved_g,
+    saved_u."""
     _dev(dy, x, w_gate, w_up, w_down, saved_g, saved_u, saved_h, sorted_pos, inv, seg_start,
          n_unique)
     n, d = x.shape

@@ -20,7 +20,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libstaple.so")
-SOURCES = ["api.hip", "sort.hip", "rows.hip", "gemm.hip", "decode.hip", "optim.hip"]
+SOURCES = ["api.hip", "sort.hip", "rows.hip", "gemm.hip", "decode.hip", "optim.hip",
+           "host_pool.cpp"]
 ARCH = "gfx950"
 
 

@@ -9,6 +9,7 @@
 #include <vector>
 
 #include "common.h"
+#include "host_pool.h"
 
 namespace staple {
 
@@ -66,7 +67,9 @@ hipError_t down_fwd(int64_t n, int64_t d, int64_t f, const void* h, const void* 
                     int out_dtype, hipStream_t s);
 template <typename T>
 hipError_t dh_act(int64_t n, int64_t d, int64_t f, const void* dy, const void* wd, const void* g,
-                  const void* u, void* dgu, hipStream_t s);
+                  const void* u, void* dgu, float* du32, hipStream_t s);
+template <typename T>
+hipError_t recompute_h(int64_t n, int64_t f, const void* g, const void* u, void* h, hipStream_t s);
 template <typename T>
 hipError_t dx_bwd(int64_t n, int64_t d, int64_t f, const void* dgu, const void* wg,
                   const void* wu, void* dx, int out_dtype, hipStream_t s);
@@ -300,26 +303,13 @@ staple_status_t staple_stage_misses(const void* host_table, int64_t vocab, int64
   const char* src = static_cast<const char*>(host_table);
   char* dst = static_cast<char*>(host_staging);
   const size_t total = row_bytes * static_cast<size_t>(n_miss);
-  unsigned hw = std::max(1u, std::thread::hardware_concurrency());
-  unsigned nthreads = static_cast<unsigned>(std::min<size_t>(std::min(hw, 16u), total >> 21));
-  if (nthreads <= 1) {
-    for (int32_t m = 0; m < n_miss; ++m)
+  // rows packed by the library's persistent host threads (one per 2 MB)
+  auto pack = [&](int64_t lo, int64_t hi) {
+    for (int64_t m = lo; m < hi; ++m)
       std::memcpy(dst + m * row_bytes, src + static_cast<size_t>(host_miss_ids[m]) * row_bytes,
                   row_bytes);
-  } else {
-    std::vector<std::thread> pool;
-    pool.reserve(nthreads);
-    for (unsigned t = 0; t < nthreads; ++t) {
-      pool.emplace_back([=]() {
-        const int64_t lo = static_cast<int64_t>(n_miss) * t / nthreads;
-        const int64_t hi = static_cast<int64_t>(n_miss) * (t + 1) / nthreads;
-        for (int64_t m = lo; m < hi; ++m)
-          std::memcpy(dst + m * row_bytes,
-                      src + static_cast<size_t>(host_miss_ids[m]) * row_bytes, row_bytes);
-      });
-    }
-    for (auto& th : pool) th.join();
-  }
+  };
+  host_parallel_for(n_miss, host_pool_parts(static_cast<int64_t>(total), 16), pack);
   HIPCALL(hipMemcpyAsync(dev_miss_rows, host_staging, total, hipMemcpyHostToDevice, S(stream)));
   return STAPLE_OK;
 }
@@ -699,15 +689,63 @@ staple_status_t staple_cache_refresh(const void* table, int64_t vocab, int64_t d
   return STAPLE_OK;
 }
 
-// workspace of the backward: [dg | du] (n x 2f) then the segment-sum partials
+// workspace of the backward: [dg | du] (n x 2f, dtype), an n x f fp32 region
+// (bf16: du in fp32 for the segment sum, then h when it is recomputed; fp32:
+// h when it is recomputed), then the segment-sum partials
 static size_t bwd_dgu_bytes(int64_t n, int64_t f, int32_t dtype) {
   return align_up(static_cast<size_t>(n) * 2 * f * elem_bytes(dtype), 256);
+}
+static size_t bwd_aux_bytes(int64_t n, int64_t f) {
+  return align_up(static_cast<size_t>(n) * f * sizeof(float), 256);
 }
 
 size_t staple_ffn_bwd_workspace_bytes(int64_t n, int64_t d, int64_t f, int32_t dtype) {
   if (!ffn_shape_ok(n, d, f, dtype)) return 0;
-  return bwd_dgu_bytes(n, f, dtype) + align_up(segment_sum_workspace_bytes(n, f), 256);
+  return bwd_dgu_bytes(n, f, dtype) + bwd_aux_bytes(n, f) +
+         align_up(segment_sum_workspace_bytes(n, f), 256);
 }
+
+}  // extern "C"
+
+template <typename T>
+static staple_status_t bwd_impl(int64_t n, int64_t d, int64_t f, int32_t dtype, int32_t out_dtype,
+                                const void* dy, const void* x, const void* w_gate, const void* w_up,
+                                const void* w_down, const void* saved_g, const void* saved_u,
+                                const void* saved_h, const int32_t* sorted_pos, const int32_t* inv,
+                                const int32_t* seg_start, const int32_t* n_unique,
+                                int64_t max_unique, float* d_rows, void* dx, float* dw_gate,
+                                float* dw_up, float* dw_down, bool fz, void* ws, hipStream_t s,
+                                int* err) {
+  void* dgu = ws;
+  char* aux = n > 0 ? static_cast<char*>(ws) + bwd_dgu_bytes(n, f, dtype) : nullptr;
+  void* seg_ws = n > 0 ? aux + bwd_aux_bytes(n, f) : nullptr;
+  // bf16: du also goes to the fp32 region unrounded, and the segment sum adds
+  // those values; fp32: the du half of [dg | du] is already fp32
+  const bool bf = dtype == STAPLE_BF16;
+  float* du32 = bf ? reinterpret_cast<float*>(aux) : nullptr;
+  HIPCALL(dh_act<T>(n, d, f, dy, w_down, saved_g, saved_u, dgu, du32, s));
+  if (n > 0) {
+    if (bf)
+      HIPCALL(launch_segment_sum(STAPLE_F32, du32, f, 0, n, f, sorted_pos, inv, seg_start, n_unique,
+                                 max_unique, d_rows, seg_ws, s, err));
+    else
+      HIPCALL(launch_segment_sum(dtype, dgu, 2 * f, f, n, f, sorted_pos, inv, seg_start, n_unique,
+                                 max_unique, d_rows, seg_ws, s, err));
+  }
+  // h for dW_down: the forward's, or recomputed from the saved g and u into
+  // the fp32 region (after the segment sum has read it, in stream order)
+  const void* h = saved_h;
+  if (!h && n > 0) {
+    HIPCALL(recompute_h<T>(n, f, saved_g, saved_u, aux, s));
+    h = aux;
+  }
+  HIPCALL(dwdown_bwd<T>(n, d, f, dy, h, dw_down, s));
+  HIPCALL(dwgu_bwd<T>(n, d, f, dgu, x, dw_gate, dw_up, fz, s));
+  HIPCALL(dx_bwd<T>(n, d, f, dgu, w_gate, w_up, dx, out_dtype, s));
+  return STAPLE_OK;
+}
+
+extern "C" {
 
 staple_status_t staple_ffn_bwd_table_grad(
     int64_t n, int64_t d, int64_t f, int32_t dtype, int32_t out_dtype, const void* dy,
@@ -725,34 +763,21 @@ staple_status_t staple_ffn_bwd_table_grad(
   REQUIRE(aligned16(w_gate) && (!w_up || aligned16(w_up)) && aligned16(w_down) &&
           aligned16(dw_gate) && aligned16(dw_down) && (fz || aligned16(dw_up)));
   if (n > 0) {
-    REQUIRE(dy && x && saved_g && saved_u && saved_h && sorted_pos && inv && d_rows && dx);
+    REQUIRE(dy && x && saved_g && saved_u && sorted_pos && inv && d_rows && dx);
     REQUIRE(aligned16(dy) && aligned16(x) && aligned16(saved_g) && aligned16(saved_u) &&
-            aligned16(saved_h) && aligned16(dx) && aligned16(d_rows));
+            (!saved_h || aligned16(saved_h)) && aligned16(dx) && aligned16(d_rows));
     if (ws_bytes < staple_ffn_bwd_workspace_bytes(n, d, f, dtype)) return STAPLE_ERR_WORKSPACE;
     REQUIRE(ws && aligned16(ws));
   }
   GET_ERR(err);
   hipStream_t s = S(stream);
-  void* dgu = ws;
-  void* seg_ws = n > 0 ? static_cast<char*>(ws) + bwd_dgu_bytes(n, f, dtype) : nullptr;
-  if (dtype == STAPLE_BF16) {
-    HIPCALL(dh_act<bf16_t>(n, d, f, dy, w_down, saved_g, saved_u, dgu, s));
-    if (n > 0)
-      HIPCALL(launch_segment_sum(dtype, dgu, 2 * f, f, n, f, sorted_pos, inv, seg_start, n_unique,
-                                 max_unique, d_rows, seg_ws, s, err));
-    HIPCALL(dwdown_bwd<bf16_t>(n, d, f, dy, saved_h, dw_down, s));
-    HIPCALL(dwgu_bwd<bf16_t>(n, d, f, dgu, x, dw_gate, dw_up, fz, s));
-    HIPCALL(dx_bwd<bf16_t>(n, d, f, dgu, w_gate, w_up, dx, out_dtype, s));
-  } else {
-    HIPCALL(dh_act<float>(n, d, f, dy, w_down, saved_g, saved_u, dgu, s));
-    if (n > 0)
-      HIPCALL(launch_segment_sum(dtype, dgu, 2 * f, f, n, f, sorted_pos, inv, seg_start, n_unique,
-                                 max_unique, d_rows, seg_ws, s, err));
-    HIPCALL(dwdown_bwd<float>(n, d, f, dy, saved_h, dw_down, s));
-    HIPCALL(dwgu_bwd<float>(n, d, f, dgu, x, dw_gate, dw_up, fz, s));
-    HIPCALL(dx_bwd<float>(n, d, f, dgu, w_gate, w_up, dx, out_dtype, s));
-  }
-  return STAPLE_OK;
+  if (dtype == STAPLE_BF16)
+    return bwd_impl<bf16_t>(n, d, f, dtype, out_dtype, dy, x, w_gate, w_up, w_down, saved_g,
+                            saved_u, saved_h, sorted_pos, inv, seg_start, n_unique, max_unique,
+                            d_rows, dx, dw_gate, dw_up, dw_down, fz, ws, s, err);
+  return bwd_impl<float>(n, d, f, dtype, out_dtype, dy, x, w_gate, w_up, w_down, saved_g, saved_u,
+                         saved_h, sorted_pos, inv, seg_start, n_unique, max_unique, d_rows, dx,
+                         dw_gate, dw_up, dw_down, fz, ws, s, err);
 }
 
 }  // extern "C"

@@ -29,7 +29,9 @@
 //             abstract and Table 1); the epilogue reads the table row e and
 //             stores h = silu(g) * e (and g, u = e when requested).
 //   DhAct   - C is dh = dy W_down; the epilogue reads saved g, u and writes
-//             dg = dh * u * silu'(g) and du = dh * silu(g) side by side.
+//             dg = dh * u * silu'(g) and du = dh * silu(g) side by side, and
+//             (bf16 layers) du once more in fp32, unrounded, for the
+//             table-row segment sum.
 #include <type_traits>
 
 #include "common.h"
@@ -71,10 +73,11 @@ struct GemmArgs {
   void* h_out;
   void* g_out;
   void* u_out;
-  // DhAct
+  // DhAct (du32_out: optional fp32 copy of du, [M x N] row-major)
   const void* g_in;
   const void* u_in;
   void* dgu_out;
+  float* du32_out;
   int* err;
 };
 
@@ -962,6 +965,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(GemmArgs p) {
           }
           store8g<T>(p.dgu_out, m * 2 * f + n, dg);
           store8g<T>(p.dgu_out, m * 2 * f + f + n, du);
+          if (p.du32_out) store8g<float>(p.du32_out, m * f + n, du);
         }
       }
     }
@@ -1047,15 +1051,15 @@ hipError_t down_fwd(int64_t n, int64_t d, int64_t f, const void* h, const void* 
   return run<T, true, true, kEpiStore, bf16_t>(a, s);
 }
 
-// dh = dy W_down; dgu[:, :f] = dg, dgu[:, f:] = du
+// dh = dy W_down; dgu[:, :f] = dg, dgu[:, f:] = du; du32 (nullable) = du in fp32
 template <typename T>
 hipError_t dh_act(int64_t n, int64_t d, int64_t f, const void* dy, const void* wd, const void* g,
-                  const void* u, void* dgu, hipStream_t s) {
+                  const void* u, void* dgu, float* du32, hipStream_t s) {
   GemmArgs a = blank<T>();
   a.M = n; a.N = f; a.K = d;
   a.a0 = dy; a.lda = d;
   a.b0 = wd; a.ldb = f;          // B(k=j, n) = W_down[j, n]
-  a.g_in = g; a.u_in = u; a.dgu_out = dgu;
+  a.g_in = g; a.u_in = u; a.dgu_out = dgu; a.du32_out = du32;
   return run<T, true, false, kEpiDhAct, T>(a, s);
 }
 
@@ -1097,14 +1101,43 @@ hipError_t dwgu_bwd(int64_t n, int64_t d, int64_t f, const void* dgu, const void
   return run<T, false, false, kEpiStore, float>(a, s);
 }
 
+// h = silu(g) * u from the saved g and u, for a backward whose caller kept no
+// h: n * f elements (a multiple of 8), 16-byte vectors, grid-stride.
+template <typename T>
+__global__ __launch_bounds__(256) void recompute_h_kernel(const void* __restrict__ g,
+                                                          const void* __restrict__ u,
+                                                          void* __restrict__ h, int64_t n8) {
+  for (int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; i < n8;
+       i += static_cast<int64_t>(gridDim.x) * 256) {
+    float gv[8], uv[8], hv[8];
+    load8g<T>(g, i * 8, gv);
+    load8g<T>(u, i * 8, uv);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) hv[k] = gv[k] * sigmoidf_(gv[k]) * uv[k];
+    store8g<T>(h, i * 8, hv);
+  }
+}
+
+template <typename T>
+hipError_t recompute_h(int64_t n, int64_t f, const void* g, const void* u, void* h, hipStream_t s) {
+  const int64_t n8 = n * f / 8;
+  if (n8 <= 0) return hipSuccess;
+  const int64_t blocks = (n8 + 255) / 256;
+  recompute_h_kernel<T><<<dim3(static_cast<unsigned>(blocks < 8192 ? blocks : 8192)), dim3(256), 0, s>>>(
+      g, u, h, n8);
+  return hipGetLastError();
+}
+
 #define STAPLE_INST(T)                                                                          \
+  template hipError_t recompute_h<T>(int64_t, int64_t, const void*, const void*, void*,        \
+                                     hipStream_t);                                              \
   template hipError_t gateup_fwd<T>(int64_t, const int32_t*, int64_t, int64_t, int64_t,        \
                                     const void*, const void*, const void*, const void*, int64_t,\
                                     const int32_t*, void*, void*, void*, hipStream_t, int*);     \
   template hipError_t down_fwd<T>(int64_t, int64_t, int64_t, const void*, const void*, void*,  \
                                   int, hipStream_t);                                            \
   template hipError_t dh_act<T>(int64_t, int64_t, int64_t, const void*, const void*,           \
-                                const void*, const void*, void*, hipStream_t);                  \
+                                const void*, const void*, void*, float*, hipStream_t);          \
   template hipError_t dx_bwd<T>(int64_t, int64_t, int64_t, const void*, const void*,           \
                                 const void*, void*, int, hipStream_t);                          \
   template hipError_t dwdown_bwd<T>(int64_t, int64_t, int64_t, const void*, const void*,       \

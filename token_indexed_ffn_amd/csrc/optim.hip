@@ -22,6 +22,7 @@
 #include <vector>
 
 #include "common.h"
+#include "host_pool.h"
 
 namespace staple {
 
@@ -264,14 +265,7 @@ void host_adamw_rows(void* table, int dtype, float* m, float* v, int64_t d_ff, c
     else host_adamw_range(table, dtype, m, v, d_ff, rows, grad, c, lo, hi);
   };
   const int64_t nt = std::max<int64_t>(1, std::min<int64_t>(n_threads, n_rows));
-  if (nt <= 1) {
-    run(0, n_rows);
-    return;
-  }
-  std::vector<std::thread> pool;
-  pool.reserve(static_cast<size_t>(nt));
-  for (int64_t t = 0; t < nt; ++t) pool.emplace_back(run, n_rows * t / nt, n_rows * (t + 1) / nt);
-  for (auto& th : pool) th.join();
+  host_parallel_for(n_rows, static_cast<int>(std::min<int64_t>(nt, kHostPoolMax)), run);
 }
 
 // ---------------------------------------------------------------------------

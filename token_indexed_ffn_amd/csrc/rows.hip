@@ -449,14 +449,20 @@ __global__ __launch_bounds__(64 * kSegWaves) void segsum_chunk_kernel(
     const T* __restrict__ du, int64_t du_ld, int64_t du_col, int64_t n_tokens, int64_t d_ff,
     const int32_t* __restrict__ sorted_pos, const int32_t* __restrict__ inv,
     const int32_t* __restrict__ seg_start, const int32_t* __restrict__ n_unique_p,
-    float* __restrict__ d_rows, float* __restrict__ first, float* __restrict__ last, int* err) {
+    int64_t max_unique, float* __restrict__ d_rows, float* __restrict__ first,
+    float* __restrict__ last, int* err) {
   const int lane = threadIdx.x & 63;
   const int64_t c = blockIdx.y;
   const int64_t col = (static_cast<int64_t>(blockIdx.x) * kSegWaves + (threadIdx.x >> 6)) * kSegCols +
                       lane * 8;
   const int64_t p0 = c * kSegChunk;
   const int64_t p1 = min(p0 + kSegChunk, n_tokens);
+  // a unique count past the rows d_rows holds is an index error: nothing is written
   const int64_t nu = *n_unique_p;
+  if (nu > max_unique) {
+    if (threadIdx.x == 0 && blockIdx.x == 0 && blockIdx.y == 0) flag_index_error(err);
+    return;
+  }
   // whole waves past d_ff leave; inside a wave every lane stays for the row
   // exchange and only lanes with col < d_ff load and store
   if (col - lane * 8 >= d_ff || nu <= 0) return;
@@ -520,13 +526,13 @@ __global__ __launch_bounds__(64 * kSegWaves) void segsum_chunk_kernel(
 __global__ __launch_bounds__(64 * kSegWaves) void segsum_fixup_kernel(
     int64_t n_tokens, int64_t d_ff, const int32_t* __restrict__ sorted_pos,
     const int32_t* __restrict__ inv, const int32_t* __restrict__ seg_start,
-    const int32_t* __restrict__ n_unique_p, const float* __restrict__ first,
+    const int32_t* __restrict__ n_unique_p, int64_t max_unique, const float* __restrict__ first,
     const float* __restrict__ last, float* __restrict__ d_rows, int* err) {
   const int64_t c0 = blockIdx.y;
   const int64_t col = (static_cast<int64_t>(blockIdx.x) * kSegWaves + (threadIdx.x >> 6)) * kSegCols +
                       (threadIdx.x & 63) * 8;
   const int64_t nu = *n_unique_p;
-  if (col >= d_ff || nu <= 0) return;
+  if (col >= d_ff || nu <= 0 || nu > max_unique) return;   // flagged by the chunk pass
   const int64_t p0 = c0 * kSegChunk;
   const int64_t p1 = min(p0 + kSegChunk, n_tokens);
   const int64_t lo = segment_of(p1 - 1, n_tokens, nu, sorted_pos, inv, err);
@@ -572,13 +578,13 @@ hipError_t launch_segment_sum(int dtype, const void* du, int64_t du_ld, int64_t 
   if (dtype == STAPLE_BF16)
     segsum_chunk_kernel<bf16_t><<<dim3(cb, static_cast<unsigned>(chunks)), dim3(64 * kSegWaves), 0, s>>>(
         static_cast<const bf16_t*>(du), du_ld, du_col, n_tokens, d_ff, sorted_pos, inv, seg_start,
-        n_unique, d_rows, first, last, err);
+        n_unique, max_unique, d_rows, first, last, err);
   else
     segsum_chunk_kernel<float><<<dim3(cb, static_cast<unsigned>(chunks)), dim3(64 * kSegWaves), 0, s>>>(
         static_cast<const float*>(du), du_ld, du_col, n_tokens, d_ff, sorted_pos, inv, seg_start,
-        n_unique, d_rows, first, last, err);
+        n_unique, max_unique, d_rows, first, last, err);
   segsum_fixup_kernel<<<dim3(cb, static_cast<unsigned>(chunks)), dim3(64 * kSegWaves), 0, s>>>(
-      n_tokens, d_ff, sorted_pos, inv, seg_start, n_unique, first, last, d_rows, err);
+      n_tokens, d_ff, sorted_pos, inv, seg_start, n_unique, max_unique, first, last, d_rows, err);
   return hipGetLastError();
 }
 
