@@ -64,6 +64,7 @@ typedef int32_t staple_status_t;
 #define STAPLE_ERR_HIP (-4)               /* a HIP runtime call failed */
 #define STAPLE_ERR_INDEX_RANGE (-5)       /* a kernel met an out-of-range ID or index */
 #define STAPLE_ERR_HOST (-6)              /* host-side failure (thread pool, host ID check) */
+#define STAPLE_ERR_SCRATCH_LIMIT (-7)     /* larger than the allocation-free call's fixed scratch */
 
 /* Element types.  STAPLE_BF16: bfloat16 storage, fp32 accumulation.
  * STAPLE_F32: fp32 storage and accumulation. */
@@ -353,6 +354,27 @@ staple_status_t staple_ffn_fwd_packed(int64_t n_tokens, int64_t d_model, int64_t
                                       const int32_t* row_index, void* y, void* save_g,
                                       void* save_u, void* save_h, void* ws, size_t ws_bytes,
                                       void* stream);
+
+/* staple_ffn_fwd_packed_noalloc: staple_ffn_fwd_packed for callers that
+ * cannot allocate device memory or pass a workspace (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation).  Same
+ * arguments without ws/ws_bytes, same kernels and the same bits.  Its scratch
+ * (h when save_h is NULL, and the down-projection's partial sums) is a fixed
+ * 16 MiB device array inside the library, one per GPU, held until the
+ * process ends; the call allocates nothing.  A problem whose workspace
+ * (staple_ffn_fwd_workspace_bytes(n_tokens, d_model, d_ff, STAPLE_BF16))
+ * exceeds 16 MiB returns STAPLE_ERR_SCRATCH_LIMIT before any launch: 64
+ * tokens at 2048 x 8192 need 5 MiB, at 4096 x 11008 9.4 MiB.  Every call on
+ * one GPU shares that array: calls that overlap on one GPU (other streams,
+ * other threads) race and give undefined results; calls in stream order are
+ * safe (nothing in it needs to start at zero). */
+staple_status_t staple_ffn_fwd_packed_noalloc(int64_t n_tokens, int64_t d_model, int64_t d_ff,
+                                              int32_t dtype, int32_t out_dtype, const void* x,
+                                              const void* packed_gate_up, int32_t up_proj,
+                                              const void* packed_down, const void* rows,
+                                              int64_t n_rows, const int32_t* row_index, void* y,
+                                              void* save_g, void* save_u, void* save_h,
+                                              void* stream);
 
 /* ------------------------------------------------------------------------
  * One decode step over a stack of layers whose tables live in pinned host

@@ -316,6 +316,24 @@ def staple_ffn_fwd_packed(x: torch.Tensor, packed_gate_up: torch.Tensor,
     return out
 
 
+def staple_ffn_fwd_packed_noalloc(x: torch.Tensor, packed_gate_up: torch.Tensor,
+                                  packed_down: torch.Tensor, rows: torch.Tensor,
+                                  row_index: torch.Tensor, *, d_ff: int, out: dict,
+                                  stream=None) -> dict:
+    """staple_ffn_fwd_packed with its scratch in the library's fixed device array:
+    the call allocates nothing, so the caller passes every output in `out`
+    ("y", and optionally "g", "u", "h")."""
+    _dev(x, packed_gate_up, packed_down, rows, row_index, *out.values())
+    n, d = x.shape
+    f = d_ff
+    _check(lib().staple_ffn_fwd_packed_noalloc(
+        n, d, f, _dt(x), _DT[out["y"].dtype], _p(x), _p(packed_gate_up),
+        _up_proj(packed_gate_up, d, f), _p(packed_down), _p(rows), rows.shape[0], _p(row_index),
+        _p(out["y"]), _p(out.get("g")), _p(out.get("u")), _p(out.get("h")), _stream(stream)),
+        "staple_ffn_fwd_packed_noalloc")
+    return out
+
+
 def staple_ffn_gate_up_packed(x: torch.Tensor, packed_gate_up: torch.Tensor, rows: torch.Tensor,
                               row_index: torch.Tensor, h: torch.Tensor,
                               save_g: Optional[torch.Tensor] = None,

@@ -55,6 +55,9 @@ _SIGS = {
     "staple_ffn_fwd_packed": (c_i32, [c_i64, c_i64, c_i64, c_i32, c_i32, c_vp, c_vp, c_i32, c_vp,
                                       c_vp, c_i64, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_sz,
                                       c_vp]),
+    "staple_ffn_fwd_packed_noalloc": (c_i32, [c_i64, c_i64, c_i64, c_i32, c_i32, c_vp, c_vp, c_i32,
+                                              c_vp, c_vp, c_i64, c_vp, c_vp, c_vp, c_vp, c_vp,
+                                              c_vp]),
     "staple_decode_step_workspace_bytes": (c_sz, [c_i64, c_i64, c_i64]),
     "staple_decode_step_cached": (c_i32, [c_i64, c_vp, c_i64, c_i64, c_i64, c_i32, c_i32, c_vp,
                                           c_i64, c_vp, c_i64, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp,

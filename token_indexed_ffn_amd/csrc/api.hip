@@ -127,6 +127,33 @@ int* device_error_word() {
   return g_err_ptr[dev];
 }
 
+// Fixed device scratch of staple_ffn_fwd_packed_noalloc: h (when the caller
+// keeps none) and the split-K partial sums of the decode down-projection.
+// Every GPU the library runs on holds its own copy until the process ends.
+// In host code `scratch` only names the symbol: its device address comes from
+// hipGetSymbolAddress, once per device, and only that address is used.
+constexpr size_t kNoAllocScratchBytes = size_t(16) << 20;
+static __device__ __align__(256) char scratch[kNoAllocScratchBytes];
+
+static std::mutex g_scratch_mu;
+static std::vector<void*> g_scratch_ptr;  // indexed by device ordinal
+
+static void* device_scratch() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return nullptr;
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (static_cast<size_t>(dev) >= g_scratch_ptr.size()) g_scratch_ptr.resize(dev + 1, nullptr);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) {
+      (void)hipGetLastError();
+      return nullptr;
+    }
+    g_scratch_ptr[dev] = p;
+  }
+  return g_scratch_ptr[dev];
+}
+
 static inline int elem_bytes(int32_t dt) { return dt == STAPLE_BF16 ? 2 : 4; }
 static inline bool valid_dtype(int32_t dt) { return dt == STAPLE_BF16 || dt == STAPLE_F32; }
 static inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -188,6 +215,8 @@ const char* staple_status_string(staple_status_t st) {
     case STAPLE_ERR_HIP: return "HIP runtime error";
     case STAPLE_ERR_INDEX_RANGE: return "out-of-range token ID or row index met on the device";
     case STAPLE_ERR_HOST: return "host-side failure";
+    case STAPLE_ERR_SCRATCH_LIMIT:
+      return "problem larger than the fixed device scratch of the allocation-free entry point";
     default: return "unknown status";
   }
 }
@@ -539,6 +568,37 @@ staple_status_t staple_ffn_fwd_packed(int64_t n, int64_t d, int64_t f, int32_t d
           (!save_h || aligned16(save_h)));
   if (ws_bytes < staple_ffn_fwd_workspace_bytes(n, d, f, dtype)) return STAPLE_ERR_WORKSPACE;
   REQUIRE(ws && aligned16(ws));
+  void* h = save_h ? save_h : ws;
+  void* down_ws = static_cast<char*>(ws) + align_up(static_cast<size_t>(n) * f * elem_bytes(dtype), 256);
+  hipStream_t s = S(stream);
+  GET_ERR(err);
+  HIPCALL(decode_gateup(n, nullptr, n, d, f, x, packed_gate_up, nullptr, rows, n_rows, row_index, h,
+                        save_g, save_u, s, err, true, up_proj != 0));
+  HIPCALL(decode_down(n, d, f, h, packed_down, y, out_dtype, down_ws, s, true));
+  return STAPLE_OK;
+}
+
+staple_status_t staple_ffn_fwd_packed_noalloc(int64_t n, int64_t d, int64_t f, int32_t dtype,
+                                              int32_t out_dtype, const void* x,
+                                              const void* packed_gate_up, int32_t up_proj,
+                                              const void* packed_down, const void* rows,
+                                              int64_t n_rows, const int32_t* row_index, void* y,
+                                              void* save_g, void* save_u, void* save_h,
+                                              void* stream) {
+  if (dtype != STAPLE_BF16 || !valid_dtype(out_dtype)) return STAPLE_ERR_UNSUPPORTED;
+  if (!ffn_shape_ok(n, d, f, dtype)) return STAPLE_ERR_UNSUPPORTED;
+  if (n > 0 && !decode_eligible(n, d, f, dtype)) return STAPLE_ERR_UNSUPPORTED;
+  REQUIRE(packed_gate_up && packed_down && rows && n_rows >= 1);
+  REQUIRE(aligned16(packed_gate_up) && aligned16(packed_down) && aligned16(rows));
+  if (n == 0) return STAPLE_OK;
+  REQUIRE(x && row_index && y && aligned16(x) && aligned16(y));
+  REQUIRE((!save_g || aligned16(save_g)) && (!save_u || aligned16(save_u)) &&
+          (!save_h || aligned16(save_h)));
+  // the same layout as staple_ffn_fwd_packed's workspace, in the fixed scratch
+  if (staple_ffn_fwd_workspace_bytes(n, d, f, dtype) > kNoAllocScratchBytes)
+    return STAPLE_ERR_SCRATCH_LIMIT;
+  void* ws = device_scratch();
+  if (ws == nullptr) return STAPLE_ERR_HIP;
   void* h = save_h ? save_h : ws;
   void* down_ws = static_cast<char*>(ws) + align_up(static_cast<size_t>(n) * f * elem_bytes(dtype), 256);
   hipStream_t s = S(stream);
