@@ -11,13 +11,16 @@ down-projection and its sum), timed both as eager launches and as replays of
 one HIP graph; the faster is reported.
 
 Also reported: `train`, tokens/s of one OLMo-2-1B-shaped training micro-batch
-(32768 Zipf tokens) through one augmented layer (dedup, compact-row gather,
-forward, backward with the fp32 table-row segment-sum and all weight and input
-gradients, then AdamW on the touched table rows); `decode_stem`, `train_stem`,
-the same two workloads for the STEM layer (no up-projection).  With
-`--workloads`: `decode7b`, `train7b` (OLMo-2-7B shapes) and `offload` (tables in
-pinned host memory with a 5% HBM cache of the most frequent rows, decode and
-training, PCIe-inclusive).
+(32768 Zipf tokens) through one augmented layer (the timed step: dedup,
+compact-row gather, forward, backward with the fp32 table-row segment-sum and
+all weight and input gradients; the AdamW update of the touched table rows is
+timed on its own and reported beside it, `adamw_table_rows`); `decode_stem`,
+`train_stem`, the same two workloads for the STEM layer (no up-projection);
+`decode_7b`, `train_7b` (OLMo-2-7B shapes: 16 decode layers over
+100352 x 11008 tables, a 16384-token training batch); `offload_decode`,
+`offload_train` (tables in pinned host memory with a 5% HBM cache of the most
+frequent rows, PCIe-inclusive).  Every workload carries its own `roofline`
+object for its dominant kernel.  `--workloads` selects a subset.
 
 Every input is synthetic and seeded (staple_synth).  Inputs are resident in
 HBM before timing starts.  The CPU oracle is timed on a bounded sample of the
@@ -49,7 +52,7 @@ def parse_args(argv=None):
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--train-steps", type=int, default=10)
     ap.add_argument("--train-warmup", type=int, default=3)
-    ap.add_argument("--workloads", default="decode,train,stem")
+    ap.add_argument("--workloads", default="decode,train,stem,decode7b,train7b,offload")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=8.0,
                     help="target CPU time of each oracle baseline sample")
@@ -89,6 +92,25 @@ def oracle_threads() -> int:
         return int(max(n)) if n else 1
     except Exception:
         return os.cpu_count() or 1
+
+
+def host_cpu() -> dict:
+    """The host the oracle runs on: logical CPUs the process may use, all
+    logical CPUs, and the model name."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        usable = len(os.sched_getaffinity(0))
+    except AttributeError:
+        usable = os.cpu_count()
+    return {"nproc": usable, "cpus_total": os.cpu_count(), "cpu_model": model}
 
 
 # ----------------------------------------------------------------------------
@@ -196,24 +218,9 @@ def run_decode(torch, st, w, steps, warmup, stem=False):
     launch = "HIP graph replay" if graph_ms <= eager_ms else "eager launches"
     ms = min(graph_ms, eager_ms)
 
-    # dominant kernel: the fused gate/up GEMM, one launch per layer, timed with
-    # HIP events around replays of a graph holding only those launches
-    gg = torch.cuda.CUDAGraph()
-    with torch.cuda.stream(cap):
-        with torch.cuda.graph(gg, stream=cap):
-            for lay in D["layers"]:
-                st.staple_ffn_gate_up_packed(lay["x"], lay["pgu"], lay["table"], D["ids"], D["h"])
-    torch.cuda.synchronize()
-    reps = max(20, steps // 2)
-    for _ in range(5):
-        gg.replay()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(reps):
-        gg.replay()
-    e1.record()
-    torch.cuda.synchronize()
-    gu_us = e0.elapsed_time(e1) / (reps * w.n_layers) * 1e3
+    # dominant kernel: the fused gate/up kernel, one launch per layer
+    gu_us = decode_gate_up_us(torch, st, [(lay["x"], lay["pgu"], lay["table"]) for lay in D["layers"]],
+                              D["ids"], D["h"], max(20, steps // 2))
 
     n_w = 1 if stem else 2
     gu_bytes = (n_w * d * f + n * d + n_unique * f + n * f) * 2    # W_gate (+ W_up), x, rows, h
@@ -244,6 +251,34 @@ def run_decode(torch, st, w, steps, warmup, stem=False):
     return res, D
 
 
+def decode_gate_up_us(torch, st, layers, index, h, reps):
+    """Average duration of one decode gate/up launch: a HIP graph holds one
+    staple_ffn_gate_up_packed per (x, packed weights, rows) of `layers`, all on
+    the graph's capture stream, and HIP events on that stream bracket `reps`
+    replays."""
+    cap = torch.cuda.Stream()
+    cap.wait_stream(torch.cuda.current_stream())
+    gg = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(cap):
+        for x, pgu, rows in layers:        # warm the capture stream
+            st.staple_ffn_gate_up_packed(x, pgu, rows, index, h)
+        cap.synchronize()
+        with torch.cuda.graph(gg, stream=cap):
+            for x, pgu, rows in layers:
+                st.staple_ffn_gate_up_packed(x, pgu, rows, index, h)
+    torch.cuda.synchronize()
+    for _ in range(5):
+        gg.replay()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    with torch.cuda.stream(cap):
+        e0.record(cap)
+        for _ in range(reps):
+            gg.replay()
+        e1.record(cap)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / (reps * len(layers)) * 1e3
+
+
 def decode_cpu_baseline(torch, w, D, seconds):
     """Oracle forward of the decode step on the host, layer by layer, until
     `seconds` of CPU time have been spent in the oracle; tokens/s is scaled to
@@ -272,7 +307,7 @@ def decode_cpu_baseline(torch, w, D, seconds):
         l += 1
     per_layer = float(np.mean(layer_times))
     return {"value": w.n_tokens / (per_layer * w.n_layers), "unit": "tokens/s",
-            "cores": oracle_threads(), "kind": "oracle",
+            "cores": oracle_threads(), "kind": "oracle", **host_cpu(),
             "sample": f"{len(layer_times)} layer forwards of the 64-token decode batch "
                       f"(float64 numpy, bf16 rounding points), scaled to {w.n_layers} layers"}
 
@@ -449,6 +484,7 @@ def train_cpu_baseline(torch, w, T, seconds):
         elapsed += time.perf_counter() - t0
         done += s_tokens
     return {"value": done / elapsed, "unit": "tokens/s", "cores": oracle_threads(), "kind": "oracle",
+            **host_cpu(),
             "sample": f"first {done} tokens of the 32768-token batch in chunks of {s_tokens} "
                       "(dedup + forward + backward, float64 numpy, bf16 rounding points)"}
 
@@ -613,8 +649,40 @@ def run_offload_decode(torch, st, w, steps, warmup):
     method = min(times, key=times.get)
     ms = times[method]
     n_unique = int(dd_out["n_unique"].item())
+    # dominant kernel: the decode gate/up over each layer's compact rows (as
+    # the native step runs it)
+    step_native()
+    torch.cuda.synchronize()
+    h = torch.empty(n, f, dtype=torch.bfloat16, device=dev)
+    gu_us = decode_gate_up_us(torch, st, [(lay["x"], lay["pgu"], R_layers[l]) for l, lay in enumerate(layers)],
+                              dd_out["inv"], h, 20)
+    gu_bytes = (2 * d * f + n * d + n_unique * f + n * f) * 2
+    achieved = gu_bytes / (gu_us * 1e-6) / 1e9
+    # the miss rows' PCIe read: one layer's compact rows assembled from the
+    # HBM cache and the pinned host table, HIP events around repeated launches
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    reps = 20
+    e0.record()
+    for _ in range(reps):
+        st.staple_assemble_rows_from_table(O["cache_rows"][0], O["tables"][0], dd_out["uniq"],
+                                           lk_out["code"], dd_out["n_unique"], out=R,
+                                           capacity=w.cache_capacity)
+    e1.record()
+    torch.cuda.synchronize()
+    asm_us = e0.elapsed_time(e1) / reps * 1e3
     return {"workload": w.name, "ms_per_step": ms, "tokens_per_s": n / (ms * 1e-3),
             "method": method,
+            "roofline": {
+                "kernel": "decode_gateup_kernel (staple_ffn_gate_up_packed over the layer's compact rows)",
+                "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": achieved / HBM_PEAK_GBS,
+                "traffic": traffic_from_profile(f"decode_gate_up/{w.name}",
+                                                source_sha("decode.hip", "common.h")),
+                "avg_launch_us": gu_us, "algorithmic_bytes_per_launch": gu_bytes},
+            "pcie": {"kernel": "assemble_rows_table_kernel (one layer: hits from the HBM cache, "
+                               "misses from the pinned host table)",
+                     "avg_launch_us": asm_us, "pcie_bytes_per_launch": m * f * 2,
+                     "pcie_gb_s": m * f * 2 / (asm_us * 1e-6) / 1e9, "pcie_peak_gb_s": 64.0},
             "direct_ms_per_step": ms_direct, "native_ms_per_step": ms_native,
             "native_inplace_ms_per_step": ms_inplace, "staged_ms_per_step": ms_staged,
             "n_unique": n_unique, "misses_per_layer": m, "cache_capacity": w.cache_capacity,
@@ -649,8 +717,9 @@ def run_offload_train(torch, st, w, steps, warmup):
     side = torch.cuda.Stream()
     main = torch.cuda.current_stream()
     ev_copy0, ev_copy1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev_gu0, ev_gu1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     ev_ready = torch.cuda.Event()
-    stats = {"pack_s": 0.0, "copy_ms": 0.0, "hit_tokens": 0}
+    stats = {"pack_s": 0.0, "copy_ms": 0.0, "hit_tokens": 0, "gu_us": []}
 
     def step(mode):
         dd = st.staple_dedup(T["ids"], v, out=T["dd"], workspace=T["dd_ws"])
@@ -677,8 +746,10 @@ def run_offload_train(torch, st, w, steps, warmup):
         ev_ready.record(side)
         fw = T["fwd"]
         # the tokens whose rows are cached run while the miss rows are in flight
+        ev_gu0.record(main)
         st.staple_ffn_gate_up_tokens(sp["hit_pos"], n_hit, T["x"], T["w_gate"], T["w_up"],
                                      O["cache_rows"][0], sp["tok_row"], fw["h"], fw["g"], fw["u"])
+        ev_gu1.record(main)
         main.wait_event(ev_ready)
         st.staple_ffn_gate_up_tokens(sp["miss_pos"], n_miss_tok, T["x"], T["w_gate"], T["w_up"],
                                      dev_miss, sp["tok_row"], fw["h"], fw["g"], fw["u"])
@@ -702,6 +773,9 @@ def run_offload_train(torch, st, w, steps, warmup):
             m = step(mode)
             ev_copy1.synchronize()
             copy_ms.append(ev_copy0.elapsed_time(ev_copy1))
+            if mode == "direct":
+                ev_gu1.synchronize()
+                stats["gu_us"].append(ev_gu0.elapsed_time(ev_gu1) * 1e3)
         torch.cuda.synchronize()
         return ((time.perf_counter() - t0) / steps * 1e3, float(np.median(copy_ms)),
                 stats["pack_s"] / steps * 1e3, m)
@@ -711,8 +785,17 @@ def run_offload_train(torch, st, w, steps, warmup):
     mode = min(("staged", "direct"), key=lambda k: res[k][0])
     ms, _, _, m = res[mode]
     ms_res = res["resident"][0]
+    gu_us = float(np.median(stats["gu_us"]))
+    gu_flops = 4 * stats["hit_tokens"] * d * f
+    achieved = gu_flops / (gu_us * 1e-6) / 1e12
     out = {"workload": w.name, "ms_per_step": ms, "tokens_per_s": n / (ms * 1e-3),
            "method": mode, "n_unique": int(T["dd"]["n_unique"].item()), "miss_rows": m,
+           "roofline": {
+               "kernel": "gemm_kernel<bf16,GateUp> (staple_ffn_gate_up_tokens over the cached "
+                         "tokens, beside the miss-row copy)",
+               "bound": "mfma", "achieved": achieved, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+               "frac": achieved / BF16_PEAK_TFLOPS, "traffic": None,
+               "avg_launch_us": gu_us, "algorithmic_flops_per_launch": gu_flops},
            "cache_capacity": w.cache_capacity, "token_hit_rate": stats["hit_tokens"] / n,
            "resident_ms_per_step": ms_res, "pcie_bytes_per_step": m * f * 2}
     out["adamw_host"] = host_adamw
