@@ -339,6 +339,60 @@ def ffn_backward(dy, x, w_gate, w_up, w_down, fwd: dict, ids, precision: str = E
 
 
 # --------------------------------------------------------------------------
+# Low-rank table (STAPLE Table 2, row L=12, r=512: the embedding dimension r
+# is a capacity axis next to the number of augmented layers, r=512 being the
+# low-rank variant; AI Radio episode, paper summary: rank 512 shrinks the
+# token-indexed table sixteen times, i.e. d_ff / r at d_ff = 8192).
+# Reading: each layer keeps a table E_r of width r and a learned projection
+# P [d_ff x r] that maps a row to d_ff, so the up branch becomes
+# u = W_up x + P E_r[t]; the pages do not print the map, a bias-free linear
+# one is the plainest reading.
+# --------------------------------------------------------------------------
+def lowrank_rows(table_r, proj, ids, precision: str = EXACT) -> np.ndarray:
+    """Z_i = P E_r[t_i] for every position: the d_ff-wide row that the
+    low-rank table adds to the up branch.  In the bf16 precision Z is rounded
+    once, where the bf16 path stores it (the row block the gate/up reads)."""
+    ids = np.asarray(ids, dtype=np.int64)
+    e = np.asarray(table_r[ids], dtype=np.float64)
+    return _maybe_round(e @ np.asarray(proj, dtype=np.float64).T, precision)
+
+
+class LowRankTable:
+    """The low-rank layer's rows as ffn_forward reads a table: ``t[ids]`` is
+    Z_i = P E_r[t_i] for each position and ``t[np.ix_(ids, cols)]`` its
+    restriction to some features (rounded as lowrank_rows rounds)."""
+
+    def __init__(self, table_r, proj, precision: str = EXACT):
+        self.table_r = table_r
+        self.proj = np.asarray(proj, dtype=np.float64)
+        self.precision = precision
+
+    def __getitem__(self, key):
+        if isinstance(key, tuple):
+            ids, cols = key
+            ids = np.asarray(ids).reshape(-1)
+            cols = np.asarray(cols).reshape(-1)
+            return lowrank_rows(self.table_r, self.proj[cols], ids, self.precision)
+        return lowrank_rows(self.table_r, self.proj, np.asarray(key).reshape(-1), self.precision)
+
+
+def lowrank_backward(d_rows, table_r, proj, uniq, precision: str = EXACT) -> dict:
+    """Gradients of the low-rank table rows and of the projection, given
+    d_rows[u] = dL/dZ summed over the positions of uniq[u] (ffn_backward's
+    table-row gradient with the Z rows as the table):
+
+        dE_r[uniq[u]] = P^T d_rows[u]          dP = sum_u d_rows[u] E_r[uniq[u]]^T
+
+    (the sums over positions collapse to sums over unique IDs because Z_i
+    depends on t_i alone).  In the bf16 precision d_rows is rounded to bf16
+    where it becomes the operand of these two contractions."""
+    dz = _maybe_round(np.asarray(d_rows, dtype=np.float64), precision)
+    e = np.asarray(table_r[np.asarray(uniq, dtype=np.int64)], dtype=np.float64)
+    p = np.asarray(proj, dtype=np.float64)
+    return {"d_rows_r": dz @ p, "d_proj": dz.T @ e}
+
+
+# --------------------------------------------------------------------------
 # Optimizer step on the touched table rows
 # --------------------------------------------------------------------------
 ADAMW_DEFAULTS = dict(beta1=0.9, beta2=0.999, eps=1e-8)
