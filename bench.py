@@ -17,7 +17,9 @@ all weight and input gradients; the AdamW update of the touched table rows is
 timed on its own and reported beside it, `adamw_table_rows`); `decode_stem`,
 `train_stem`, the same two workloads for the STEM layer (no up-projection);
 `decode_7b`, `train_7b` (OLMo-2-7B shapes: 16 decode layers over
-100352 x 11008 tables, a 16384-token training batch); `offload_decode`,
+100352 x 11008 tables, a 16384-token training batch); `train_lowrank` (the
+1B training step with the low-rank r=512 table and its projection);
+`offload_decode`,
 `offload_train` (tables in pinned host memory with a 5% HBM cache of the most
 frequent rows, PCIe-inclusive).  Every workload carries its own `roofline`
 object for its dominant kernel.  `--workloads` selects a subset.
@@ -52,7 +54,7 @@ def parse_args(argv=None):
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--train-steps", type=int, default=10)
     ap.add_argument("--train-warmup", type=int, default=3)
-    ap.add_argument("--workloads", default="decode,train,stem,decode7b,train7b,offload")
+    ap.add_argument("--workloads", default="decode,train,stem,decode7b,train7b,offload,lowrank")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=8.0,
                     help="target CPU time of each oracle baseline sample")
@@ -429,6 +431,101 @@ def run_train(torch, st, w, steps, warmup, stem=False):
         },
         **({"adamw_table_rows": adamw} if adamw else {}),
     }, T
+
+
+def run_train_lowrank(torch, st, w, r, steps, warmup):
+    """The training step of the low-rank table layer (table E_r of width r and
+    projection P [d_ff x r]): dedup, R_r = E_r[uniq], Z = R_r P^T, the layer's
+    forward and backward over Z, then dE_r and dP (staple_lowrank_bwd)."""
+    import numpy as np
+    from staple_synth import device_normal
+    dev = torch.device("cuda:0")
+    n, d, f, v = w.n_tokens, w.d_model, w.d_ff, w.vocab
+    T = setup_train(torch, st, w)
+    s = w.layer_seeds(0)
+    del T["table"]
+    torch.cuda.empty_cache()
+    T["table_r"] = device_normal((v, r), w.table_std, s["table"], torch.bfloat16, dev)
+    T["proj"] = device_normal((f, r), w.w_std, s["w_up"] + 1000, torch.bfloat16, dev)
+    T["rows_r"] = torch.empty(n, r, dtype=torch.bfloat16, device=dev)
+    lr_out = {"d_rows_r": torch.empty(n, r, dtype=torch.float32, device=dev),
+              "d_proj": torch.empty(f, r, dtype=torch.float32, device=dev)}
+    lr_ws = torch.empty(max(st.lib().staple_lowrank_bwd_workspace_bytes(n, f, 1), 1),
+                        dtype=torch.uint8, device=dev)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+
+    def step(timed=False):
+        dd = st.staple_dedup(T["ids"], v, out=T["dd"], workspace=T["dd_ws"])
+        st.staple_gather_rows(T["table_r"], dd["uniq"], dd["n_unique"], out=T["rows_r"])
+        if timed:
+            ev[0].record()
+        st.staple_lowrank_expand(T["rows_r"], dd["n_unique"], T["proj"], out=T["rows"])
+        if timed:
+            ev[1].record()
+        fw = T["fwd"]
+        st.staple_ffn_gate_up(T["x"], T["w_gate"], T["w_up"], T["rows"], dd["inv"], fw["h"],
+                              fw["g"], fw["u"])
+        st.staple_ffn_down(fw["h"], T["w_down"], fw["y"])
+        st.staple_ffn_bwd_table_grad(T["dy"], T["x"], T["w_gate"], T["w_up"], T["w_down"], fw["g"],
+                                     fw["u"], fw["h"], dd["sorted_pos"], dd["seg_start"],
+                                     dd["n_unique"], inv=dd["inv"], out=T["bwd"],
+                                     workspace=T["bwd_ws"])
+        if timed:
+            ev[2].record()
+        st.staple_lowrank_bwd(T["bwd"]["d_rows"], T["rows_r"], dd["n_unique"], T["proj"],
+                              out=lr_out, workspace=lr_ws)
+        if timed:
+            ev[3].record()
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    if st.staple_get_device_error() != 0:
+        raise RuntimeError("device error in the low-rank training step")
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) / steps * 1e3
+    exp_us, bwd_us = [], []
+    for _ in range(3):
+        step(timed=True)
+        torch.cuda.synchronize()
+        exp_us.append(ev[0].elapsed_time(ev[1]) * 1e3)
+        bwd_us.append(ev[2].elapsed_time(ev[3]) * 1e3)
+    u = int(T["dd"]["n_unique"].item())
+    flops_total = 18 * n * d * f + 6 * u * r * f
+    # dominant kernel: the gate/up GEMM, the same launch as the full-width
+    # layer's (its rows are Z instead of E[uniq])
+    gu_us = []
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    for _ in range(3):
+        e0.record()
+        st.staple_ffn_gate_up(T["x"], T["w_gate"], T["w_up"], T["rows"], T["dd"]["inv"],
+                              T["fwd"]["h"], T["fwd"]["g"], T["fwd"]["u"])
+        e1.record()
+        torch.cuda.synchronize()
+        gu_us.append(e0.elapsed_time(e1) * 1e3)
+    gu = float(np.median(gu_us))
+    gu_flops = 4 * n * d * f
+    out = {"workload": w.name + f"_lowrank_r{r}", "tokens": n, "rank": r, "ms_per_step": ms,
+           "tokens_per_s": n / (ms * 1e-3), "n_unique": u,
+           "step_tflops": flops_total / (ms * 1e-3) / 1e12,
+           "step_mfma_frac": flops_total / (ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
+           "expand_us": float(np.median(exp_us)), "lowrank_bwd_us": float(np.median(bwd_us)),
+           "table_bytes": v * r * 2, "full_width_table_bytes": v * f * 2,
+           "roofline": {"kernel": "gemm_kernel<bf16,GateUp> (staple_ffn_gate_up over Z)",
+                        "bound": "mfma", "achieved": gu_flops / (gu * 1e-6) / 1e12,
+                        "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                        "frac": gu_flops / (gu * 1e-6) / 1e12 / BF16_PEAK_TFLOPS,
+                        "traffic": None, "avg_launch_us": gu,
+                        "algorithmic_flops_per_launch": gu_flops},
+           "note": "step: dedup, R_r = E_r[uniq] (U x r), Z = R_r P^T (staple_lowrank_expand), "
+                   "gate/up over Z, down, backward, dE_r and dP (staple_lowrank_bwd); FLOPs "
+                   "18 N d f + 6 U r f"}
+    del T, lr_out, lr_ws
+    torch.cuda.empty_cache()
+    return out
 
 
 def run_device_adamw(torch, st, T, w, reps):
@@ -943,6 +1040,9 @@ def main(argv=None) -> int:
         out["train_stem"] = dict(tr_s, workload=S.OLMO1B_TRAIN.name + "_stem")
         del T_s
         torch.cuda.empty_cache()
+    if "lowrank" in wl:
+        out["train_lowrank"] = run_train_lowrank(torch, st, S.OLMO1B_TRAIN, 512, args.train_steps,
+                                                 args.train_warmup)
     if "offload" in wl:
         out["offload_decode"] = run_offload_decode(torch, st, S.OLMO1B_OFFLOAD, 20, 3)
         torch.cuda.empty_cache()

@@ -438,6 +438,46 @@ staple_status_t staple_decode_step_cached(
     int32_t* miss_uidx, int32_t* n_miss, void* ws, size_t ws_bytes, void* stream);
 
 /* ------------------------------------------------------------------------
+ * Low-rank tables.  The embedding dimension r is a capacity axis of STAPLE
+ * next to the number of augmented layers, r = 512 being its low-rank variant
+ * (STAPLE Table 2, row L=12, r=512; AI Radio episode, paper summary: rank
+ * 512 makes the token-indexed table sixteen times smaller, d_ff / r at d_ff
+ * 8192).  Reading taken: a layer keeps a table E_r [vocab x r] and a learned
+ * projection P [d_ff x r], and the up branch adds Z = P E_r[t]:
+ *
+ *     u_i = W_up x_i + P E_r[t_i]
+ *
+ * Z depends on the token alone, so it is formed once per unique ID of the
+ * batch and the layer runs as the full-width one with Z as its compact rows:
+ *   forward : R_r = E_r[uniq] (staple_gather_rows), Z = staple_lowrank_expand,
+ *             staple_ffn_fwd(rows = Z, row_index = inv);
+ *   backward: staple_ffn_bwd_table_grad gives d_rows = dL/dZ, then
+ *             staple_lowrank_bwd gives the table-row gradient
+ *             dE_r[uniq[u]] = P^T d_rows[u] and dP = sum_u d_rows[u] R_r[u]^T.
+ *
+ * staple_lowrank_expand: z[u] = P rows_r[u] for u < *n_rows (device scalar,
+ *   <= max_rows); rows_r [max_rows x r], proj [d_ff x r], z [max_rows x d_ff],
+ *   all of `dtype` (bf16: fp32 accumulation, Z rounded to bf16 once).  Rows
+ *   of z past *n_rows are not written.
+ * staple_lowrank_bwd: d_rows [max_rows x d_ff] fp32 (rows < *n_rows read),
+ *   rows_r as above, proj [d_ff x r] (dtype).  Outputs: d_rows_r
+ *   [max_rows x r] fp32 (rows < *n_rows written), d_proj [d_ff x r] fp32
+ *   (overwritten; zeros when *n_rows is 0).  bf16: d_rows is rounded to bf16
+ *   as the operand of both contractions, which accumulate in fp32.
+ *   ws: staple_lowrank_bwd_workspace_bytes(max_rows, d_ff, dtype) bytes (the
+ *   rounded d_rows; none for fp32).
+ * r and d_ff multiples of 64; 16-byte aligned pointers.
+ * ------------------------------------------------------------------------ */
+staple_status_t staple_lowrank_expand(const void* rows_r, const int32_t* n_rows, int64_t max_rows,
+                                      int64_t r, int64_t d_ff, int32_t dtype, const void* proj,
+                                      void* z, void* stream);
+size_t staple_lowrank_bwd_workspace_bytes(int64_t max_rows, int64_t d_ff, int32_t dtype);
+staple_status_t staple_lowrank_bwd(const float* d_rows, const void* rows_r, const int32_t* n_rows,
+                                   int64_t max_rows, int64_t r, int64_t d_ff, int32_t dtype,
+                                   const void* proj, float* d_rows_r, float* d_proj, void* ws,
+                                   size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
  * AdamW step on the table rows a batch touched.  The tables are trained with
  * AdamW with fp32 moments beside the bf16 table (STAPLE Figure 4 caption:
  * bf16 tables and fp32 AdamW moments in host DRAM; Table 3: peak learning

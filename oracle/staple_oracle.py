@@ -348,13 +348,14 @@ def ffn_backward(dy, x, w_gate, w_up, w_down, fwd: dict, ids, precision: str = E
 # u = W_up x + P E_r[t]; the pages do not print the map, a bias-free linear
 # one is the plainest reading.
 # --------------------------------------------------------------------------
-def lowrank_rows(table_r, proj, ids, precision: str = EXACT) -> np.ndarray:
+def lowrank_rows(table_r, proj, ids, precision: str = EXACT, accum: str = "f64") -> np.ndarray:
     """Z_i = P E_r[t_i] for every position: the d_ff-wide row that the
     low-rank table adds to the up branch.  In the bf16 precision Z is rounded
     once, where the bf16 path stores it (the row block the gate/up reads)."""
+    ft = _ftype(accum)
     ids = np.asarray(ids, dtype=np.int64)
-    e = np.asarray(table_r[ids], dtype=np.float64)
-    return _maybe_round(e @ np.asarray(proj, dtype=np.float64).T, precision)
+    e = np.asarray(table_r[ids], dtype=ft)
+    return _maybe_round(e @ np.asarray(proj, dtype=ft).T, precision)
 
 
 class LowRankTable:
@@ -362,21 +363,24 @@ class LowRankTable:
     Z_i = P E_r[t_i] for each position and ``t[np.ix_(ids, cols)]`` its
     restriction to some features (rounded as lowrank_rows rounds)."""
 
-    def __init__(self, table_r, proj, precision: str = EXACT):
+    def __init__(self, table_r, proj, precision: str = EXACT, accum: str = "f64"):
         self.table_r = table_r
         self.proj = np.asarray(proj, dtype=np.float64)
         self.precision = precision
+        self.accum = accum
 
     def __getitem__(self, key):
         if isinstance(key, tuple):
             ids, cols = key
             ids = np.asarray(ids).reshape(-1)
             cols = np.asarray(cols).reshape(-1)
-            return lowrank_rows(self.table_r, self.proj[cols], ids, self.precision)
-        return lowrank_rows(self.table_r, self.proj, np.asarray(key).reshape(-1), self.precision)
+            return lowrank_rows(self.table_r, self.proj[cols], ids, self.precision, self.accum)
+        return lowrank_rows(self.table_r, self.proj, np.asarray(key).reshape(-1), self.precision,
+                            self.accum)
 
 
-def lowrank_backward(d_rows, table_r, proj, uniq, precision: str = EXACT) -> dict:
+def lowrank_backward(d_rows, table_r, proj, uniq, precision: str = EXACT,
+                     accum: str = "f64") -> dict:
     """Gradients of the low-rank table rows and of the projection, given
     d_rows[u] = dL/dZ summed over the positions of uniq[u] (ffn_backward's
     table-row gradient with the Z rows as the table):
@@ -386,9 +390,10 @@ def lowrank_backward(d_rows, table_r, proj, uniq, precision: str = EXACT) -> dic
     (the sums over positions collapse to sums over unique IDs because Z_i
     depends on t_i alone).  In the bf16 precision d_rows is rounded to bf16
     where it becomes the operand of these two contractions."""
-    dz = _maybe_round(np.asarray(d_rows, dtype=np.float64), precision)
-    e = np.asarray(table_r[np.asarray(uniq, dtype=np.int64)], dtype=np.float64)
-    p = np.asarray(proj, dtype=np.float64)
+    ft = _ftype(accum)
+    dz = _maybe_round(np.asarray(d_rows, dtype=ft), precision)
+    e = np.asarray(table_r[np.asarray(uniq, dtype=np.int64)], dtype=ft)
+    p = np.asarray(proj, dtype=ft)
     return {"d_rows_r": dz @ p, "d_proj": dz.T @ e}
 
 

@@ -453,6 +453,38 @@ def decode_step_workspace_bytes(n: int, d: int, f: int) -> int:
     return lib().staple_decode_step_workspace_bytes(n, d, f)
 
 
+def staple_lowrank_expand(rows_r: torch.Tensor, n_rows: torch.Tensor, proj: torch.Tensor,
+                          out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Z[u] = proj @ rows_r[u] for u < *n_rows (the low-rank table's d_ff-wide rows)."""
+    _dev(rows_r, n_rows, proj, out)
+    max_rows, r = rows_r.shape
+    f = proj.shape[0]
+    if out is None:
+        out = torch.empty(max(max_rows, 1), f, dtype=rows_r.dtype, device=rows_r.device)
+    _check(lib().staple_lowrank_expand(_p(rows_r), _p(n_rows), max_rows, r, f, _dt(rows_r),
+                                       _p(proj), _p(out), _stream(stream)), "staple_lowrank_expand")
+    return out
+
+
+def staple_lowrank_bwd(d_rows: torch.Tensor, rows_r: torch.Tensor, n_rows: torch.Tensor,
+                       proj: torch.Tensor, *, out: Optional[dict] = None,
+                       workspace: Optional[torch.Tensor] = None, stream=None) -> dict:
+    """The low-rank table-row gradient d_rows_r = d_rows @ proj and the projection's
+    gradient d_proj = d_rows^T @ rows_r over the first *n_rows rows."""
+    _dev(d_rows, rows_r, n_rows, proj)
+    max_rows, r = rows_r.shape
+    f = proj.shape[0]
+    dev = rows_r.device
+    if out is None:
+        out = {"d_rows_r": torch.empty(max(max_rows, 1), r, dtype=torch.float32, device=dev),
+               "d_proj": torch.empty(f, r, dtype=torch.float32, device=dev)}
+    ws = _ws(lib().staple_lowrank_bwd_workspace_bytes(max_rows, f, _dt(rows_r)), workspace, dev)
+    _check(lib().staple_lowrank_bwd(_p(d_rows), _p(rows_r), _p(n_rows), max_rows, r, f, _dt(rows_r),
+                                    _p(proj), _p(out["d_rows_r"]), _p(out["d_proj"]), _p(ws),
+                                    _ws_size(ws), _stream(stream)), "staple_lowrank_bwd")
+    return out
+
+
 def staple_adamw_rows(table: torch.Tensor, m: torch.Tensor, v: torch.Tensor, rows: torch.Tensor,
                       grad: torch.Tensor, *, lr: float, weight_decay: float, step: int,
                       n_rows: Optional[torch.Tensor] = None, beta1: float = 0.9,

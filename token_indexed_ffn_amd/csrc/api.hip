@@ -71,6 +71,13 @@ hipError_t dh_act(int64_t n, int64_t d, int64_t f, const void* dy, const void* w
 template <typename T>
 hipError_t recompute_h(int64_t n, int64_t f, const void* g, const void* u, void* h, hipStream_t s);
 template <typename T>
+hipError_t lowrank_expand(int64_t max_rows, const int32_t* n_dev, int64_t r, int64_t f,
+                          const void* rows_r, const void* proj, void* z, hipStream_t s);
+template <typename T>
+hipError_t lowrank_bwd(int64_t max_rows, const int32_t* n_dev, int64_t r, int64_t f,
+                       const float* dz, const void* rows_r, const void* proj, float* d_rows_r,
+                       float* d_proj, void* ws, hipStream_t s);
+template <typename T>
 hipError_t dx_bwd(int64_t n, int64_t d, int64_t f, const void* dgu, const void* wg,
                   const void* wu, void* dx, int out_dtype, hipStream_t s);
 template <typename T>
@@ -686,6 +693,54 @@ staple_status_t staple_decode_step_cached(
                             L.table, vocab));
     HIPCALL(decode_down(n, d, f, h, L.packed_down, L.y, out_dtype, down_ws, s, true));
   }
+  return STAPLE_OK;
+}
+
+// ------------------------------------------------------------------ low-rank table
+static bool lowrank_shape_ok(int64_t max_rows, int64_t r, int64_t f, int32_t dtype) {
+  return valid_dtype(dtype) && max_rows >= 0 && max_rows <= 0x7fffffffll && r > 0 && f > 0 &&
+         r % 64 == 0 && f % 64 == 0 && r <= (1ll << 20) && f <= (1ll << 20);
+}
+
+staple_status_t staple_lowrank_expand(const void* rows_r, const int32_t* n_rows, int64_t max_rows,
+                                      int64_t r, int64_t d_ff, int32_t dtype, const void* proj,
+                                      void* z, void* stream) {
+  if (!lowrank_shape_ok(max_rows, r, d_ff, dtype)) return STAPLE_ERR_UNSUPPORTED;
+  REQUIRE(n_rows && proj && aligned16(proj));
+  if (max_rows == 0) return STAPLE_OK;
+  REQUIRE(rows_r && z && aligned16(rows_r) && aligned16(z));
+  if (dtype == STAPLE_BF16)
+    HIPCALL(lowrank_expand<bf16_t>(max_rows, n_rows, r, d_ff, rows_r, proj, z, S(stream)));
+  else
+    HIPCALL(lowrank_expand<float>(max_rows, n_rows, r, d_ff, rows_r, proj, z, S(stream)));
+  return STAPLE_OK;
+}
+
+size_t staple_lowrank_bwd_workspace_bytes(int64_t max_rows, int64_t d_ff, int32_t dtype) {
+  if (max_rows < 0 || d_ff <= 0 || !valid_dtype(dtype)) return 0;
+  return dtype == STAPLE_BF16 ? align_up(static_cast<size_t>(max_rows) * d_ff * 2, 256) : 0;
+}
+
+staple_status_t staple_lowrank_bwd(const float* d_rows, const void* rows_r, const int32_t* n_rows,
+                                   int64_t max_rows, int64_t r, int64_t d_ff, int32_t dtype,
+                                   const void* proj, float* d_rows_r, float* d_proj, void* ws,
+                                   size_t ws_bytes, void* stream) {
+  if (!lowrank_shape_ok(max_rows, r, d_ff, dtype)) return STAPLE_ERR_UNSUPPORTED;
+  REQUIRE(n_rows && proj && d_proj && aligned16(proj) && aligned16(d_proj));
+  if (max_rows > 0) {
+    REQUIRE(d_rows && rows_r && d_rows_r);
+    REQUIRE(aligned16(d_rows) && aligned16(rows_r) && aligned16(d_rows_r));
+    const size_t need = staple_lowrank_bwd_workspace_bytes(max_rows, d_ff, dtype);
+    if (ws_bytes < need) return STAPLE_ERR_WORKSPACE;
+    REQUIRE(need == 0 || (ws && aligned16(ws)));
+  }
+  // max_rows == 0 still writes dP (all zeros: the K range is empty)
+  if (dtype == STAPLE_BF16)
+    HIPCALL(lowrank_bwd<bf16_t>(max_rows, n_rows, r, d_ff, d_rows, rows_r, proj, d_rows_r, d_proj,
+                                ws, S(stream)));
+  else
+    HIPCALL(lowrank_bwd<float>(max_rows, n_rows, r, d_ff, d_rows, rows_r, proj, d_rows_r, d_proj,
+                               ws, S(stream)));
   return STAPLE_OK;
 }
 

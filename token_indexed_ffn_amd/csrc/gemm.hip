@@ -79,6 +79,12 @@ struct GemmArgs {
   void* dgu_out;
   float* du32_out;
   int* err;
+  // Optional device-side limits (counts known only on the device, e.g. the
+  // batch's unique IDs): M and K become min(M, *m_dev) and min(K, *k_dev);
+  // the grid is sized for the host M and the tiles past the device M leave.
+  // k_dev is only used with MN-major operands (rows past K read zeros).
+  const int32_t* m_dev;
+  const int32_t* k_dev;
 };
 
 constexpr int kRowBytes = 128;  // bytes of k per LDS tile row and stage
@@ -586,8 +592,20 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(GemmArgs p) {
   char* Bs0 = smem + BM * RB;
   constexpr int kStage = (BM + BN) * RB;
 
+  // A device-side M shrinks the tile grid: the first tiles_m x tiles_n
+  // workgroups take the live tiles (spread over every XCD by tile_coords),
+  // the rest leave at once (the same decision for the whole workgroup).
+  if (p.m_dev) {
+    const int64_t md = *p.m_dev;
+    p.M = md < p.M ? (md > 0 ? md : 0) : p.M;
+    if (static_cast<int64_t>(blockIdx.x) >= ((p.M + BM - 1) / BM) * ((p.N + BN - 1) / BN)) return;
+  }
   int64_t mt, nt;
   tile_coords((p.M + BM - 1) / BM, (p.N + BN - 1) / BN, mt, nt);
+  if (p.k_dev) {
+    const int64_t kd = *p.k_dev;
+    p.K = kd < p.K ? (kd > 0 ? kd : 0) : p.K;
+  }
   const int64_t m0 = mt * BM;
   const int64_t n0 = nt * BN;
   const int lane = threadIdx.x & 63;
@@ -1128,7 +1146,76 @@ hipError_t recompute_h(int64_t n, int64_t f, const void* g, const void* u, void*
   return hipGetLastError();
 }
 
+// ---------------------------------------------------------------------------
+// Low-rank table: Z = R_r P^T for the first *n of max_rows compact rows, and
+// the gradients dE_r = dZ P, dP = dZ^T R_r from dZ (the layer's fp32
+// table-row gradient, rounded to T as the operand of both contractions).
+// ---------------------------------------------------------------------------
+template <typename T>
+hipError_t lowrank_expand(int64_t max_rows, const int32_t* n_dev, int64_t r, int64_t f,
+                          const void* rows_r, const void* proj, void* z, hipStream_t s) {
+  GemmArgs a = blank<T>();
+  a.M = max_rows; a.N = f; a.K = r;
+  a.a0 = rows_r; a.lda = r;        // A(u, k) = R_r[u, k]
+  a.b0 = proj; a.ldb = r;          // B(k, j) = P[j, k] (K-major rows of P)
+  a.c0 = z; a.ldc = f;
+  a.m_dev = n_dev;
+  return run<T, true, true, kEpiStore, T>(a, s);
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void round_rows_kernel(const float* __restrict__ src,
+                                                         void* __restrict__ dst, int64_t max_rows,
+                                                         const int32_t* __restrict__ n_dev,
+                                                         int64_t cols) {
+  const int64_t nd = *n_dev;
+  const int64_t n8 = (nd < max_rows ? (nd > 0 ? nd : 0) : max_rows) * cols / 8;
+  for (int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; i < n8;
+       i += static_cast<int64_t>(gridDim.x) * 256) {
+    float v[8];
+    read8(src + i * 8, v);
+    store8g<T>(dst, i * 8, v);
+  }
+}
+
+// dZ (fp32 [max_rows x f]) -> dE_r [max_rows x r] fp32, dP [f x r] fp32;
+// bf16: dZ rounded into ws ([max_rows x f] bf16) first.
+template <typename T>
+hipError_t lowrank_bwd(int64_t max_rows, const int32_t* n_dev, int64_t r, int64_t f,
+                       const float* dz, const void* rows_r, const void* proj, float* d_rows_r,
+                       float* d_proj, void* ws, hipStream_t s) {
+  const void* dzo = dz;
+  if constexpr (sizeof(T) == 2) {
+    const int64_t blocks = (max_rows * f / 8 + 255) / 256;
+    if (blocks > 0)
+      round_rows_kernel<T><<<dim3(static_cast<unsigned>(blocks < 4096 ? blocks : 4096)), dim3(256), 0,
+                           s>>>(dz, ws, max_rows, n_dev, f);
+    dzo = ws;
+  }
+  GemmArgs a = blank<T>();         // dE_r = dZ P: M = rows, N = r, K = f
+  a.M = max_rows; a.N = r; a.K = f;
+  a.a0 = dzo; a.lda = f;           // A(u, j) = dZ[u, j]
+  a.b0 = proj; a.ldb = r;          // B(j, n) = P[j, n] (MN-major)
+  a.c0 = d_rows_r; a.ldc = r;
+  a.m_dev = n_dev;
+  // r is narrow (2 tiles of 256 at r = 512): 128 x 128 tiles keep every CU busy
+  hipError_t e = run_tile<T, 128, 128, 2, 2, true, false, kEpiStore, float, kRowBytes, 2>(a, s);
+  if (e != hipSuccess) return e;
+  GemmArgs b = blank<T>();         // dP = dZ^T R_r: M = f, N = r, K = rows
+  b.M = f; b.N = r; b.K = max_rows;
+  b.a0 = dzo; b.lda = f;           // A(j, u) = dZ[u, j] (MN-major)
+  b.b0 = rows_r; b.ldb = r;        // B(u, n) = R_r[u, n] (MN-major)
+  b.c0 = d_proj; b.ldc = r;
+  b.k_dev = n_dev;
+  return run<T, false, false, kEpiStore, float>(b, s);
+}
+
 #define STAPLE_INST(T)                                                                          \
+  template hipError_t lowrank_expand<T>(int64_t, const int32_t*, int64_t, int64_t, const void*,\
+                                        const void*, void*, hipStream_t);                       \
+  template hipError_t lowrank_bwd<T>(int64_t, const int32_t*, int64_t, int64_t, const float*,  \
+                                     const void*, const void*, float*, float*, void*,           \
+                                     hipStream_t);                                              \
   template hipError_t recompute_h<T>(int64_t, int64_t, const void*, const void*, void*,        \
                                      hipStream_t);                                              \
   template hipError_t gateup_fwd<T>(int64_t, const int32_t*, int64_t, int64_t, int64_t,        \
