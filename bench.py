@@ -718,6 +718,27 @@ def run_offload_decode(torch, st, w, steps, warmup):
         st.staple_decode_step_cached(stack_inplace, ids, O["id_to_slot"], w.cache_capacity,
                                      dedup_out=dd_out, lookup_out=lk_out, workspace=step_ws)
 
+    # groups of layers: the first group's rows assembled before layer 0, each
+    # later group's rows copied by the gate/up launches of the group before
+    # it; groups of two over the separate tables, and groups of four over
+    # tables interleaved token-major by fours in host memory (one contiguous
+    # read per miss per group)
+    def step_carried():
+        st.staple_decode_step_cached(stack, ids, O["id_to_slot"], w.cache_capacity,
+                                     dedup_out=dd_out, lookup_out=lk_out, workspace=step_ws, group=2)
+
+    grouped = [st.staple_group_tables_host(O["tables"][g:g + 4]) for g in range(0, L, 4)]
+    stack_grouped = st.DecodeStack(
+        [{"x": lay["x"], "packed_gate_up": lay["pgu"], "packed_down": lay["pd"],
+          "cache_rows": O["cache_rows"][l],
+          "table": (grouped[l // 4], (l % 4) * f, min(4, L - (l // 4) * 4) * f),
+          "rows": R_layers[l], "y": lay["y"]} for l, lay in enumerate(layers)],
+        d_model=d, d_ff=f, n_tokens=n)
+
+    def step_grouped():
+        st.staple_decode_step_cached(stack_grouped, ids, O["id_to_slot"], w.cache_capacity,
+                                     dedup_out=dd_out, lookup_out=lk_out, workspace=step_ws, group=4)
+
     def timed(step):
         for _ in range(warmup):
             step()
@@ -740,9 +761,18 @@ def run_offload_decode(torch, st, w, steps, warmup):
     torch.cuda.synchronize()
     if not all(torch.equal(a, lay["y"]) for a, lay in zip(ys, layers)):
         raise RuntimeError("the in-place row reads give other outputs than the per-layer calls")
+    ms_carried = timed(step_carried)
+    torch.cuda.synchronize()
+    if not all(torch.equal(a, lay["y"]) for a, lay in zip(ys, layers)):
+        raise RuntimeError("the carried row copies give other outputs than the per-layer calls")
+    ms_grouped = timed(step_grouped)
+    torch.cuda.synchronize()
+    if not all(torch.equal(a, lay["y"]) for a, lay in zip(ys, layers)):
+        raise RuntimeError("the grouped host tables give other outputs than the per-layer calls")
     ms_staged = timed(step_staged)
     m = _miss_list_to_host(torch, lk_out, miss_host)
-    times = {"direct": ms_direct, "staged": ms_staged, "native": ms_native, "native_inplace": ms_inplace}
+    times = {"direct": ms_direct, "staged": ms_staged, "native": ms_native, "native_inplace": ms_inplace,
+             "native_carried": ms_carried, "native_grouped": ms_grouped}
     method = min(times, key=times.get)
     ms = times[method]
     n_unique = int(dd_out["n_unique"].item())
@@ -781,7 +811,8 @@ def run_offload_decode(torch, st, w, steps, warmup):
                      "avg_launch_us": asm_us, "pcie_bytes_per_launch": m * f * 2,
                      "pcie_gb_s": m * f * 2 / (asm_us * 1e-6) / 1e9, "pcie_peak_gb_s": 64.0},
             "direct_ms_per_step": ms_direct, "native_ms_per_step": ms_native,
-            "native_inplace_ms_per_step": ms_inplace, "staged_ms_per_step": ms_staged,
+            "native_inplace_ms_per_step": ms_inplace, "native_carried_ms_per_step": ms_carried,
+            "native_grouped_ms_per_step": ms_grouped, "staged_ms_per_step": ms_staged,
             "n_unique": n_unique, "misses_per_layer": m, "cache_capacity": w.cache_capacity,
             "pcie_bytes_per_step": m * f * 2 * L,
             "note": "eager steps, dedup + cache probe once per step. direct: per layer one kernel "
@@ -790,7 +821,11 @@ def run_offload_decode(torch, st, w, steps, warmup):
                     "down. native: one staple_decode_step_cached call per step (dedup, probe, "
                     "every layer's rows in one launch, the FFNs). native_inplace: the same call "
                     "with no compact rows, each gate/up kernel reading its tokens' rows in place "
-                    "(cache slot or pinned host table). staged: "
+                    "(cache slot or pinned host table). native_carried: the same call with groups "
+                    "of two layers, the first group's rows assembled first and every later "
+                    "group's rows copied by the copy waves of the gate/up launches of the group "
+                    "before it. native_grouped: native_carried over host tables interleaved "
+                    "token-major by groups of four. staged: "
                     "one host sync for the miss list, host pack + H2D copy per layer on a side "
                     "stream one layer ahead"}
 

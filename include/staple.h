@@ -382,7 +382,7 @@ staple_status_t staple_ffn_fwd_packed_noalloc(int64_t n_tokens, int64_t d_model,
  * table, Decode row: one dedup and cache probe per step, then the layers;
  * Table 4 caption: the 1 GB cache of frequent rows).  Enqueues on `stream`:
  *   1. staple_dedup of ids (the batch's n tokens) and staple_cache_lookup
- *      against id_to_slot;
+ *      against id_to_slot (one launch: a decode batch fits one wave);
  *   2. the compact rows R_l = layers[l].rows of every layer that has them
  *      (hits from layers[l].cache_rows, misses read straight from
  *      layers[l].table, as staple_assemble_rows_from_table), one launch for
@@ -402,12 +402,32 @@ staple_status_t staple_ffn_fwd_packed_noalloc(int64_t n_tokens, int64_t d_model,
  * The whole step is one native call: issuing it costs one call per step
  * instead of several per layer.
  *
+ * group (0 .. 4): how the compact rows of the layers reach the device.
+ *   0: every layer's rows are assembled before the first layer (step 2).
+ *   G > 0: the layers form groups of G consecutive layers (the pages keep
+ *     every four adjacent tables together and synchronise a group's lookups
+ *     only where the group is first used: STAPLE retrieval-path table, Decode
+ *     row).  Group 0's rows are assembled before the first layer; the rows of
+ *     group k + 1 are copied while group k runs, by a copy wave in each
+ *     workgroup of group k's gate/up launches (launch j of the group carries
+ *     part j of the next group's unique rows, for all of its layers), so the
+ *     PCIe reads of the misses hide under those launches' weight streams.
+ *     Stream order makes group k + 1's rows complete before its first layer.
+ *     Every layer needs `rows`.  A group whose part would not fit one
+ *     launch's copy waves is assembled before the first layer instead.
+ *   Every choice gives the same bits.
+ *
  *   layers: host array of n_layers descriptors:
  *     x [n x d_model] bf16; packed_gate_up, packed_down from
  *     staple_decode_pack_weights (up_proj as for staple_ffn_fwd_packed);
  *     cache_rows [capacity x d_ff] bf16 device (slot s = the row of the ID
  *     with slot s in id_to_slot, e.g. from staple_cache_fill); table
- *     [vocab x d_ff] bf16, pinned host (hipHostMalloc) or device; rows
+ *     [vocab x d_ff] bf16, pinned host (hipHostMalloc) or device, whose
+ *     token rows lie table_stride elements apart (0: d_ff; more when several
+ *     layers' tables are interleaved token-major, as staple_group_tables_host
+ *     makes them: layer j of a group then has table = group base + j d_ff and
+ *     table_stride = (tables in the group) d_ff, so one miss of the group is
+ *     one contiguous read of all its layers' rows); rows
  *     [n x d_ff] bf16 device, one per layer (it holds R_l after the step),
  *     or NULL (rows read in place, above);
  *     y [n x d_model] of out_dtype.
@@ -427,15 +447,30 @@ typedef struct staple_decode_layer {
   const void* table;
   void* rows;
   void* y;
+  int64_t table_stride;
 } staple_decode_layer_t;
 
 size_t staple_decode_step_workspace_bytes(int64_t n_tokens, int64_t d_model, int64_t d_ff);
 staple_status_t staple_decode_step_cached(
     int64_t n_layers, const staple_decode_layer_t* layers, int64_t n_tokens, int64_t d_model,
     int64_t d_ff, int32_t up_proj, int32_t out_dtype, const int32_t* ids, int64_t vocab,
-    const int32_t* id_to_slot, int64_t capacity, int32_t* uniq, int32_t* inv,
+    const int32_t* id_to_slot, int64_t capacity, int32_t group, int32_t* uniq, int32_t* inv,
     int32_t* sorted_pos, int32_t* seg_start, int32_t* n_unique, int32_t* code,
     int32_t* miss_uidx, int32_t* n_miss, void* ws, size_t ws_bytes, void* stream);
+
+/* Host-side layout of offloaded tables: every n_tables adjacent layers' tables
+ * stored token-major in one block (STAPLE retrieval-path table, Decode row:
+ * every four adjacent tables in a token-major CPU layout), so that the rows of
+ * one token for all of those layers are one contiguous read:
+ *   grouped[t * n_tables * d_ff + j * d_ff + c] = tables[j][t * d_ff + c].
+ * tables: host array of n_tables host pointers, each [vocab x d_ff] of dtype;
+ * grouped: host memory of vocab * n_tables * d_ff elements (pinned
+ * (hipHostMalloc) when kernels are to read it), not overlapping the sources.
+ * Runs on the calling thread with the library's host threads; synchronous.
+ * 1 <= n_tables <= 64. */
+staple_status_t staple_group_tables_host(const void* const* tables, int64_t n_tables,
+                                         int64_t vocab, int64_t d_ff, int32_t dtype,
+                                         void* grouped);
 
 /* ------------------------------------------------------------------------
  * Low-rank tables.  The embedding dimension r is a capacity axis of STAPLE

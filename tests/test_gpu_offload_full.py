@@ -125,6 +125,28 @@ def test_offloaded_decode_step_full_size(st, dev):
                                      lookup_out=lk, workspace=ws)
     torch.cuda.synchronize()
     assert st.staple_get_device_error() == 0
+    # groups of four layers with carried row copies, over separate tables and
+    # over tables interleaved token-major by groups of four
+    grouped = [st.staple_group_tables_host(tables[g:g + 4]) for g in range(0, L, 4)]
+    ys_c = [nan() for _ in range(L)]
+    ys_g = [nan() for _ in range(L)]
+    R_c = [torch.empty(n, f, dtype=torch.bfloat16, device=dev) for _ in range(L)]
+    R_g = [torch.empty(n, f, dtype=torch.bfloat16, device=dev) for _ in range(L)]
+    carried = st.DecodeStack([dict(common(l), rows=R_c[l], y=ys_c[l]) for l in range(L)],
+                             d_model=d, d_ff=f, n_tokens=n)
+    grouped_stack = st.DecodeStack(
+        [dict(common(l), table=(grouped[l // 4], (l % 4) * f, 4 * f), rows=R_g[l], y=ys_g[l])
+         for l in range(L)], d_model=d, d_ff=f, n_tokens=n)
+    for stack in (carried, grouped_stack):
+        st.staple_decode_step_cached(stack, ids, id_to_slot, w.cache_capacity, dedup_out=dd,
+                                     lookup_out=lk, workspace=ws, group=4)
+    torch.cuda.synchronize()
+    assert st.staple_get_device_error() == 0
+    nu = int(dd["n_unique"].item())
+    for l in range(L):
+        assert torch.equal(ys_c[l], ys_a[l]) and torch.equal(ys_g[l], ys_a[l]), f"layer {l}"
+        assert torch.equal(R_c[l][:nu], R[l][:nu]) and torch.equal(R_g[l][:nu], R[l][:nu]), \
+            f"layer {l} rows"
     uniq = np.unique(ids_np)
     u = len(uniq)
     assert int(dd["n_unique"].item()) == u

@@ -1149,6 +1149,107 @@ def test_decode_step_driver_matches_per_layer_calls(st, dev, stem, rows_mode):
             assert_close(to_np(lay["y"]), of["y"], f"driver y layer {l} step {step}")
 
 
+@pytest.mark.parametrize("stem,n,f,cap", [(False, 64, 256, 40), (True, 33, 256, 40),
+                                          (False, 64, 256, 0), (True, 64, 16448, 40)])
+def test_decode_step_driver_carried_rows_and_grouped_tables(st, dev, stem, n, f, cap):
+    """The decode step with the rows of each group of layers copied by the
+    gate/up launches of the group before (group 1, 2, 3, 4; seven layers, so
+    the last group is partial) and with the tables interleaved token-major by
+    groups of four (staple_group_tables_host: one contiguous host read per
+    miss per group) gives every layer's y and compact rows bit for bit as the
+    step that assembles every row first from separate tables.  cap 0: no HBM
+    cache, every row from the pinned tables.  STEM at d_ff 16448: six row
+    groups per workgroup, whose copy waves cannot carry a part, so those
+    groups are assembled first instead."""
+    import torch
+    L, d, vocab = 7, 64, 300
+    _log(f"carried rows stem={stem} n={n} f={f} cap={cap}")
+    counts = st.staple_cache_count(torch.from_numpy(S.zipf_ids(20_000, vocab, 3)).to(dev), vocab)
+    i2s, s2i = st.staple_cache_build(counts, cap)
+    base, tables, caches = [], [], []
+    for l in range(L):
+        inp = S.host_layer_inputs(n, d, f, vocab, dtype="bf16", seed=120 + l, table_std=0.5)
+        x, wg, wu, wd = (to_dev(getattr(inp, k), "bf16", dev) for k in ("x", "w_gate", "w_up", "w_down"))
+        tab = torch.from_numpy(inp.table.view(np.int16)).view(torch.bfloat16).pin_memory()
+        pgu, pd = st.staple_decode_pack_weights(wg, None if stem else wu, wd, d_model=d, d_ff=f)
+        tables.append(tab)
+        caches.append(st.staple_cache_fill(tab, s2i, cap))
+        base.append({"x": x, "packed_gate_up": pgu, "packed_down": pd,
+                     "cache_rows": None if cap == 0 else caches[-1]})
+    grouped = [st.staple_group_tables_host(tables[g:g + 4]) for g in range(0, L, 4)]
+    torch.testing.assert_close(grouped[0][:, 2], tables[2], rtol=0, atol=0)
+
+    def stack(layout):
+        lays = []
+        for l in range(L):
+            gsz = min(4, L - (l // 4) * 4)
+            tab = tables[l] if layout == "separate" else (grouped[l // 4], (l % 4) * f, gsz * f)
+            lays.append(dict(base[l], table=tab,
+                             rows=torch.zeros(n, f, dtype=torch.bfloat16, device=dev),
+                             y=torch.zeros(n, d, dtype=torch.float32, device=dev)))
+        return lays, st.DecodeStack(lays, d_model=d, d_ff=f, n_tokens=n)
+
+    i32 = dict(dtype=torch.int32, device=dev)
+    dd = {"uniq": torch.empty(n, **i32), "inv": torch.empty(n, **i32),
+          "sorted_pos": torch.empty(n, **i32), "seg_start": torch.empty(n + 1, **i32),
+          "n_unique": torch.empty(1, **i32)}
+    lk = {"code": torch.empty(n, **i32), "miss_uidx": torch.empty(n, **i32),
+          "n_miss": torch.empty(1, **i32)}
+    ws = torch.empty(st.decode_step_workspace_bytes(n, d, f), dtype=torch.uint8, device=dev)
+    ref_lays, ref_stack = stack("separate")
+    for step in range(2):
+        ids = torch.from_numpy(S.zipf_ids(n, vocab, 700 + step)).to(dev)
+        st.staple_decode_step_cached(ref_stack, ids, i2s, cap, dedup_out=dd, lookup_out=lk,
+                                     workspace=ws, group=0)
+        torch.cuda.synchronize()
+        _no_device_error(st)
+        u = int(dd["n_unique"].item())
+        for layout in ("separate", "grouped"):
+            for group in (1, 2, 3, 4):
+                lays, stk = stack(layout)
+                st.staple_decode_step_cached(stk, ids, i2s, cap, dedup_out=dd, lookup_out=lk,
+                                             workspace=ws, group=group)
+                torch.cuda.synchronize()
+                _no_device_error(st)
+                for l in range(L):
+                    assert torch.equal(lays[l]["y"], ref_lays[l]["y"]), (layout, group, step, l)
+                    assert torch.equal(lays[l]["rows"][:u], ref_lays[l]["rows"][:u]), \
+                        (layout, group, step, l)
+    # the oracle on the last step
+    ids_np = S.zipf_ids(n, vocab, 701)
+    uniq = np.unique(ids_np)
+    for l in (0, L - 1):
+        inp = S.host_layer_inputs(n, d, f, vocab, dtype="bf16", seed=120 + l, table_std=0.5)
+        g = {k: inp.as_f64(k) for k in ("x", "w_gate", "w_up", "w_down", "table")}
+        of = O.ffn_forward(g["x"], g["w_gate"], None if stem else g["w_up"], g["w_down"],
+                           g["table"], ids_np, precision=O.BF16)
+        assert_close(to_np(ref_lays[l]["y"]), of["y"], f"carried y layer {l}")
+
+
+def test_decode_step_driver_refuses_carried_rows_without_compact_rows(st, dev):
+    import torch
+    d, f, n, vocab = 64, 64, 8, 16
+    wg = torch.zeros(f, d, dtype=torch.bfloat16, device=dev)
+    pgu, pd = st.staple_decode_pack_weights(wg, wg, wg.t().contiguous(), d_model=d, d_ff=f)
+    tab = torch.zeros(vocab, f, dtype=torch.bfloat16, device=dev)
+    lay = {"x": torch.zeros(n, d, dtype=torch.bfloat16, device=dev), "packed_gate_up": pgu,
+           "packed_down": pd, "cache_rows": None, "table": tab,
+           "y": torch.zeros(n, d, dtype=torch.bfloat16, device=dev)}
+    stk = st.DecodeStack([lay], d_model=d, d_ff=f, n_tokens=n)
+    i32 = dict(dtype=torch.int32, device=dev)
+    dd = {k: torch.empty(n + 1, **i32) for k in ("uniq", "inv", "sorted_pos", "seg_start")}
+    dd["n_unique"] = torch.empty(1, **i32)
+    lk = {k: torch.empty(n, **i32) for k in ("code", "miss_uidx")}
+    lk["n_miss"] = torch.empty(1, **i32)
+    ws = torch.empty(max(st.decode_step_workspace_bytes(n, d, f), 1), dtype=torch.uint8, device=dev)
+    ids = torch.zeros(n, dtype=torch.int32, device=dev)
+    i2s = torch.full((vocab,), -1, dtype=torch.int32, device=dev)
+    for group in (2, 5):
+        with pytest.raises(RuntimeError, match="invalid argument"):
+            st.staple_decode_step_cached(stk, ids, i2s, 0, dedup_out=dd, lookup_out=lk,
+                                         workspace=ws, group=group)
+
+
 @pytest.mark.parametrize("stem", [False, True])
 def test_decode_step_driver_in_place_bad_slot_is_flagged_and_reads_as_zero(st, dev, stem):
     """With rows read in place, a cache slot past the capacity (a corrupt

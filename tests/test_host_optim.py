@@ -131,3 +131,17 @@ def test_stage_misses_packs_rows_on_the_host_threads():
                                           staging.ctypes.data, 16, None)
     assert status == -4
     np.testing.assert_array_equal(staging, table[ids])
+
+
+def test_group_tables_host_interleaves_token_major():
+    """staple_group_tables_host: grouped[t, j] = tables[j][t] (host threads)."""
+    import torch
+    st = _lib()
+    rng = np.random.default_rng(14)
+    vocab, f = 3000, 128
+    tabs = [torch.from_numpy(rng.normal(0, 1, (vocab, f)).astype(np.float32)).to(torch.bfloat16)
+            for _ in range(3)]
+    out = torch.empty(vocab, 3, f, dtype=torch.bfloat16)
+    st.staple_group_tables_host(tabs, out=out)
+    for j in range(3):
+        assert torch.equal(out[:, j], tabs[j])

@@ -408,7 +408,8 @@ def staple_ffn_down(h: torch.Tensor, w_down: torch.Tensor, y: torch.Tensor,
 
 class _DecodeLayer(ctypes.Structure):
     _fields_ = [(k, ctypes.c_void_p) for k in
-                ("x", "packed_gate_up", "packed_down", "cache_rows", "table", "rows", "y")]
+                ("x", "packed_gate_up", "packed_down", "cache_rows", "table", "rows", "y")] + \
+               [("table_stride", ctypes.c_int64)]
 
 
 class DecodeStack:
@@ -418,35 +419,60 @@ class DecodeStack:
     def __init__(self, layers: list, *, d_model: int, d_ff: int, n_tokens: int):
         keys = ("x", "packed_gate_up", "packed_down", "cache_rows", "table", "rows", "y")
         # keeps the tensors alive; a layer without "rows" (or rows None) reads
-        # each token's row in place
+        # each token's row in place.  "table" is a [vocab x d_ff] tensor, or a
+        # (tensor, element offset, row stride) triple for a layer whose table
+        # is interleaved with others' (staple_group_tables_host).
         self.layers = [{k: lay.get(k) for k in keys} for lay in layers]
+        ptrs = []
         for lay in self.layers:
             _dev(lay["x"], lay["packed_gate_up"], lay["packed_down"], lay["cache_rows"],
                  lay["rows"], lay["y"])
-            if not (lay["table"].is_cuda or lay["table"].is_pinned()):
+            tab, off, stride = (lay["table"] if isinstance(lay["table"], tuple)
+                                else (lay["table"], 0, 0))
+            if not (tab.is_cuda or tab.is_pinned()):
                 raise ValueError("table must be a device or pinned host tensor")
+            ptrs.append((tab.data_ptr() + off * tab.element_size(), stride))
         self.n_layers = len(layers)
         self.d_model, self.d_ff, self.n_tokens = d_model, d_ff, n_tokens
         self.up_proj = _up_proj(self.layers[0]["packed_gate_up"], d_model, d_ff)
         self.out_dtype = _DT[self.layers[0]["y"].dtype]
         self.desc = (_DecodeLayer * self.n_layers)(
-            *[_DecodeLayer(*[_p(lay[k]) for k in keys]) for lay in self.layers])
+            *[_DecodeLayer(*[(_p(lay[k]) if k != "table" else tp) for k in keys], stride)
+              for lay, (tp, stride) in zip(self.layers, ptrs)])
 
 
 def staple_decode_step_cached(stack: DecodeStack, ids: torch.Tensor, id_to_slot: torch.Tensor,
                               capacity: int, *, dedup_out: dict, lookup_out: dict,
-                              workspace: torch.Tensor, stream=None) -> None:
-    """One decode step over the stack: dedup + cache probe, every layer's rows (one
-    launch), each layer's packed FFN."""
+                              workspace: torch.Tensor, group: int = 0, stream=None) -> None:
+    """One decode step over the stack: dedup + cache probe, the layers' compact rows
+    (group 0: all before the first layer; group G: the first G layers' before, the
+    others carried by the gate/up launches of the group before), each layer's
+    packed FFN."""
     n = ids.numel()
     vocab = id_to_slot.numel()
     dd, lk = dedup_out, lookup_out
     _check(lib().staple_decode_step_cached(
         stack.n_layers, ctypes.cast(stack.desc, ctypes.c_void_p), n, stack.d_model, stack.d_ff,
-        stack.up_proj, stack.out_dtype, _p(ids), vocab, _p(id_to_slot), int(capacity),
+        stack.up_proj, stack.out_dtype, _p(ids), vocab, _p(id_to_slot), int(capacity), int(group),
         _p(dd["uniq"]), _p(dd["inv"]), _p(dd["sorted_pos"]), _p(dd["seg_start"]),
         _p(dd["n_unique"]), _p(lk["code"]), _p(lk["miss_uidx"]), _p(lk["n_miss"]), _p(workspace),
         _ws_size(workspace), _stream(stream)), "staple_decode_step_cached")
+
+
+def staple_group_tables_host(tables: list, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """The tables' rows interleaved token-major: out[t, j] = tables[j][t] (host tensors;
+    out pinned when none is given)."""
+    for t in tables:
+        if t.is_cuda or not t.is_contiguous():
+            raise ValueError("expected contiguous host tensors")
+    vocab, d_ff = tables[0].shape
+    if out is None:
+        out = torch.empty(vocab, len(tables), d_ff, dtype=tables[0].dtype, pin_memory=True)
+    arr = (ctypes.c_void_p * len(tables))(*[t.data_ptr() for t in tables])
+    _check(lib().staple_group_tables_host(ctypes.cast(arr, ctypes.c_void_p), len(tables), vocab,
+                                          d_ff, _dt(tables[0]), out.data_ptr()),
+           "staple_group_tables_host")
+    return out
 
 
 def decode_step_workspace_bytes(n: int, d: int, f: int) -> int:

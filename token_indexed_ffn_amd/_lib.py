@@ -60,8 +60,9 @@ _SIGS = {
                                               c_vp]),
     "staple_decode_step_workspace_bytes": (c_sz, [c_i64, c_i64, c_i64]),
     "staple_decode_step_cached": (c_i32, [c_i64, c_vp, c_i64, c_i64, c_i64, c_i32, c_i32, c_vp,
-                                          c_i64, c_vp, c_i64, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp,
-                                          c_vp, c_vp, c_vp, c_sz, c_vp]),
+                                          c_i64, c_vp, c_i64, c_i32, c_vp, c_vp, c_vp, c_vp, c_vp,
+                                          c_vp, c_vp, c_vp, c_vp, c_sz, c_vp]),
+    "staple_group_tables_host": (c_i32, [c_vp, c_i64, c_i64, c_i64, c_i32, c_vp]),
     "staple_lowrank_expand": (c_i32, [c_vp, c_vp, c_i64, c_i64, c_i64, c_i32, c_vp, c_vp, c_vp]),
     "staple_lowrank_bwd_workspace_bytes": (c_sz, [c_i64, c_i64, c_i32]),
     "staple_lowrank_bwd": (c_i32, [c_vp, c_vp, c_vp, c_i64, c_i64, c_i64, c_i32, c_vp, c_vp, c_vp,

@@ -18,6 +18,11 @@ size_t dedup_workspace_bytes(int64_t n);
 hipError_t launch_dedup(const int32_t* ids, int64_t n, int64_t vocab, int32_t* uniq, int32_t* inv,
                         int32_t* sorted_pos, int32_t* seg_start, int32_t* n_unique, void* ws,
                         hipStream_t s, int* err);
+hipError_t launch_dedup_lookup_wave(const int32_t* ids, int64_t n, int64_t vocab,
+                                    const int32_t* id_to_slot, int32_t* uniq, int32_t* inv,
+                                    int32_t* sorted_pos, int32_t* seg_start, int32_t* n_unique,
+                                    int32_t* code, int32_t* miss_uidx, int32_t* n_miss,
+                                    int32_t* row_src, hipStream_t s, int* err);
 size_t cache_build_workspace_bytes(int64_t vocab);
 hipError_t launch_cache_build(const int64_t* counts, int64_t vocab, int64_t capacity,
                               int32_t* id_to_slot, int32_t* slot_to_id, void* ws, hipStream_t s,
@@ -94,7 +99,9 @@ hipError_t decode_gateup(int64_t n, const int32_t* pos, int64_t n_tokens, int64_
                          const void* x, const void* wg, const void* wu, const void* rows,
                          int64_t n_rows, const int32_t* row_index, void* h, void* g_out,
                          void* u_out, hipStream_t s, int* err, bool packed, bool up,
-                         const void* table = nullptr, int64_t vocab = 0);
+                         const void* table = nullptr, int64_t vocab = 0, int64_t table_ld = 0,
+                         const RowCopyJob* job = nullptr);
+bool decode_copy_plan(int64_t rows, int64_t f, bool up, int* per, int* seg);
 hipError_t decode_down(int64_t n, int64_t d, int64_t f, const void* h, const void* wd, void* y,
                        int out_dtype, void* ws, hipStream_t s, bool packed);
 hipError_t decode_pack(int64_t d, int64_t f, const void* wg, const void* wu, const void* wd,
@@ -627,14 +634,15 @@ size_t staple_decode_step_workspace_bytes(int64_t n, int64_t d, int64_t f) {
 staple_status_t staple_decode_step_cached(
     int64_t n_layers, const staple_decode_layer_t* layers, int64_t n, int64_t d, int64_t f,
     int32_t up_proj, int32_t out_dtype, const int32_t* ids, int64_t vocab,
-    const int32_t* id_to_slot, int64_t capacity, int32_t* uniq, int32_t* inv, int32_t* sorted_pos,
-    int32_t* seg_start, int32_t* n_unique, int32_t* code, int32_t* miss_uidx, int32_t* n_miss,
-    void* ws, size_t ws_bytes, void* stream) {
+    const int32_t* id_to_slot, int64_t capacity, int32_t group, int32_t* uniq, int32_t* inv,
+    int32_t* sorted_pos, int32_t* seg_start, int32_t* n_unique, int32_t* code, int32_t* miss_uidx,
+    int32_t* n_miss, void* ws, size_t ws_bytes, void* stream) {
   if (!valid_dtype(out_dtype) || !ffn_shape_ok(n, d, f, STAPLE_BF16) ||
       !decode_eligible(n, d, f, STAPLE_BF16))
     return STAPLE_ERR_UNSUPPORTED;
   REQUIRE(n_layers >= 1 && n_layers <= 4096 && layers);
   REQUIRE(vocab >= 1 && vocab <= 0x7fffffffll && capacity >= 0);
+  REQUIRE(group >= 0 && group <= kCopyJobLayers);
   REQUIRE(ids && id_to_slot && uniq && inv && sorted_pos && seg_start && n_unique && code &&
           miss_uidx && n_miss);
   const size_t need = staple_decode_step_workspace_bytes(n, d, f);
@@ -648,51 +656,118 @@ staple_status_t staple_decode_step_cached(
     REQUIRE(aligned16(L.x) && aligned16(L.packed_gate_up) && aligned16(L.packed_down) &&
             aligned16(L.table) && (!L.rows || aligned16(L.rows)) && aligned16(L.y) &&
             (capacity == 0 || aligned16(L.cache_rows)));
+    REQUIRE(L.table_stride == 0 || (L.table_stride >= f && L.table_stride % 8 == 0));
     REQUIRE(device_addressable(L.table));
+    REQUIRE(group == 0 || L.rows);   // carried copies fill compact rows
     any_direct = any_direct || !L.rows;
   }
   REQUIRE(capacity <= 0x7fffffffll);
   GET_ERR(err);
   hipStream_t s = S(stream);
+  const int64_t row_bytes = f * 2;
+  auto table_ld = [&](const staple_decode_layer_t& L) -> int64_t {
+    return (L.table_stride ? L.table_stride : f) * 2;
+  };
   void* dedup_ws = ws;
   int32_t* row_src = reinterpret_cast<int32_t*>(static_cast<char*>(ws) + align_up(dedup_workspace_bytes(n), 256));
   void* fwd_ws = reinterpret_cast<char*>(row_src) + align_up(static_cast<size_t>(n) * sizeof(int32_t), 256);
   void* h = fwd_ws;
   void* down_ws = static_cast<char*>(fwd_ws) + align_up(static_cast<size_t>(n) * f * 2, 256);
-  HIPCALL(launch_dedup(ids, n, vocab, uniq, inv, sorted_pos, seg_start, n_unique, dedup_ws, s, err));
-  HIPCALL(launch_cache_lookup(uniq, n_unique, n, id_to_slot, vocab, code, miss_uidx, nullptr, n_miss,
-                              s, err, inv, n, any_direct ? row_src : nullptr));
-  // the rows of every layer that keeps them (rows != NULL), one launch per
-  // slice of such layers: the misses of all of them are read from host
-  // memory together
+  // a decode batch (at most 64 tokens): dedup and cache probe in one wave
+  (void)dedup_ws;
+  HIPCALL(launch_dedup_lookup_wave(ids, n, vocab, id_to_slot, uniq, inv, sorted_pos, seg_start,
+                                   n_unique, code, miss_uidx, n_miss,
+                                   any_direct ? row_src : nullptr, s, err));
+  // Which layers' rows are copied by the gate/up launches of the group before
+  // (group > 0): group k + 1's rows, split in `group` parts over group k's
+  // launches, when a part fits the copy waves of one launch.  The others
+  // (group 0, and all of them when group == 0) are assembled here, before the
+  // first layer, one launch per slice of layers.
+  const int64_t G = group;
+  const int64_t n_groups = G > 0 ? (n_layers + G - 1) / G : 0;
+  // a part of group g's rows: unique rows part, part + G, ... (at most
+  // ceil(n / G) of them) of each of its layers
+  auto plan = [&](int64_t g, int* per, int* seg) -> bool {
+    const int64_t layers_in = std::min<int64_t>(G, n_layers - g * G);
+    return decode_copy_plan((n + G - 1) / G * layers_in, f, up_proj != 0, per, seg);
+  };
+  auto carried = [&](int64_t g) -> bool {   // group g's rows ride group g - 1's launches
+    int per = 0, seg = 0;
+    return G > 0 && g > 0 && g < n_groups && plan(g, &per, &seg);
+  };
   LayerRowSources src{};
   int cnt = 0;
   for (int64_t l = 0; l < n_layers; ++l) {
     const staple_decode_layer_t& L = layers[l];
-    if (!L.rows) continue;
+    if (!L.rows || (G > 0 && carried(l / G))) continue;
     src.cache_rows[cnt] = L.cache_rows;
     src.table[cnt] = L.table;
+    src.table_ld[cnt] = table_ld(L);
     src.rows[cnt] = L.rows;
     if (++cnt == kMaxAssembleLayers) {
-      HIPCALL(launch_assemble_rows_layers(src, cnt, capacity, vocab, uniq, code, n_unique, n, f * 2,
-                                          s, err));
+      HIPCALL(launch_assemble_rows_layers(src, cnt, capacity, vocab, uniq, code, n_unique, n,
+                                          row_bytes, s, err));
       cnt = 0;
     }
   }
   if (cnt > 0)
-    HIPCALL(launch_assemble_rows_layers(src, cnt, capacity, vocab, uniq, code, n_unique, n, f * 2, s,
-                                        err));
+    HIPCALL(launch_assemble_rows_layers(src, cnt, capacity, vocab, uniq, code, n_unique, n,
+                                        row_bytes, s, err));
   for (int64_t l = 0; l < n_layers; ++l) {
     const staple_decode_layer_t& L = layers[l];
+    RowCopyJob job{};
+    bool with_job = false;
+    if (G > 0 && carried(l / G + 1)) {
+      const int64_t first = (l / G + 1) * G;
+      job.n_layers = static_cast<int>(std::min<int64_t>(G, n_layers - first));
+      for (int j = 0; j < job.n_layers; ++j) {
+        const staple_decode_layer_t& M = layers[first + j];
+        job.cache_rows[j] = M.cache_rows;
+        job.table[j] = M.table;
+        job.table_ld[j] = table_ld(M);
+        job.rows[j] = M.rows;
+      }
+      job.uniq = uniq;
+      job.code = code;
+      job.n_unique = n_unique;
+      job.max_unique = n;
+      job.capacity = capacity;
+      job.vocab = vocab;
+      job.row_bytes = row_bytes;
+      job.part = static_cast<int>(l % G);
+      job.parts = static_cast<int>(G);
+      job.rows_max = static_cast<int>((n + G - 1) / G * job.n_layers);
+      plan(l / G + 1, &job.per, &job.seg);
+      with_job = true;
+    }
     if (L.rows)
       HIPCALL(decode_gateup(n, nullptr, n, d, f, L.x, L.packed_gate_up, nullptr, L.rows, n, inv, h,
-                            nullptr, nullptr, s, err, true, up_proj != 0));
+                            nullptr, nullptr, s, err, true, up_proj != 0, nullptr, 0, 0,
+                            with_job ? &job : nullptr));
     else   // each token's row read in place: its cache slot, or its row of the table
       HIPCALL(decode_gateup(n, nullptr, n, d, f, L.x, L.packed_gate_up, nullptr, L.cache_rows,
                             capacity, row_src, h, nullptr, nullptr, s, err, true, up_proj != 0,
-                            L.table, vocab));
+                            L.table, vocab, L.table_stride ? L.table_stride : f));
     HIPCALL(decode_down(n, d, f, h, L.packed_down, L.y, out_dtype, down_ws, s, true));
   }
+  return STAPLE_OK;
+}
+
+staple_status_t staple_group_tables_host(const void* const* tables, int64_t n_tables,
+                                         int64_t vocab, int64_t d_ff, int32_t dtype,
+                                         void* grouped) {
+  REQUIRE(valid_dtype(dtype) && n_tables >= 1 && n_tables <= 64 && vocab >= 1 && d_ff > 0);
+  REQUIRE(tables && grouped);
+  for (int64_t j = 0; j < n_tables; ++j) REQUIRE(tables[j]);
+  const size_t row = static_cast<size_t>(d_ff) * elem_bytes(dtype);
+  char* dst = static_cast<char*>(grouped);
+  auto body = [&](int64_t lo, int64_t hi) {
+    for (int64_t t = lo; t < hi; ++t)
+      for (int64_t j = 0; j < n_tables; ++j)
+        std::memcpy(dst + (t * n_tables + j) * row,
+                    static_cast<const char*>(tables[j]) + t * row, row);
+  };
+  host_parallel_for(vocab, host_pool_parts(static_cast<int64_t>(vocab * n_tables * row), 16), body);
   return STAPLE_OK;
 }
 

@@ -137,7 +137,29 @@ constexpr unsigned kLayerRowWorkgroups = 512;
 struct LayerRowSources {
   const void* cache_rows[kMaxAssembleLayers];
   const void* table[kMaxAssembleLayers];
+  int64_t table_ld[kMaxAssembleLayers];   // bytes between consecutive token rows of the table
   void* rows[kMaxAssembleLayers];
+};
+
+// Compact-row copies carried by a decode gate/up launch (a copy wave per
+// workgroup, see decode.hip): for each of n_layers layers j and the unique
+// rows u = part, part + parts, ... below U = *n_unique,
+// rows[j][u] = code[u] >= 0 ? cache_rows[j][code[u]] : table[j][uniq[u]].
+constexpr int kCopyJobLayers = 4;
+struct RowCopyJob {
+  const void* cache_rows[kCopyJobLayers];
+  const void* table[kCopyJobLayers];
+  int64_t table_ld[kCopyJobLayers];       // bytes between consecutive token rows of table j
+  void* rows[kCopyJobLayers];
+  const int32_t* uniq;
+  const int32_t* code;
+  const int32_t* n_unique;
+  int64_t max_unique, capacity, vocab, row_bytes;
+  int n_layers, part, parts;
+  // this launch's rows: unique rows u = part + parts i (i = 0, 1, ...) below
+  // *n_unique, each for the n_layers layers; rows_max of them at most, each
+  // cut into `per` segments of at most `seg` 16-byte pieces
+  int rows_max, per, seg;
 };
 }  // namespace staple
 

@@ -124,9 +124,10 @@ __device__ const uint4 g_decode_zero_rows[16] = {};
 // wave with `active` false (a row group past the end of the matrix, pa still
 // pointing at valid memory) runs them with zeroed weights too.
 // `after_prologue` runs on compute waves once their first loads are issued.
-// A row wave (role.row) runs `row_issue` (loads it does not wait for here)
-// and then only joins the barriers, so its loads, however slow, hold up no
-// other wave; the caller waits for them after the stream.
+// A row wave (role.row) runs `row_issue` (loads it does not wait for here),
+// in two phases around the first barrier, and then only joins the barriers,
+// so its loads, however slow, hold up no other wave; the caller waits for
+// them after the stream.
 template <int WD, int A, int KH, int JOFF, typename RowFn, typename Hook, typename RowIssue>
 __device__ __forceinline__ void stream_act_ring(WaveRole role, bool active, const char* pa, int64_t wstep,
                                                 const uint16_t* act, int64_t act_ld, RowFn act_row,
@@ -144,12 +145,18 @@ __device__ __forceinline__ void stream_act_ring(WaveRole role, bool active, cons
     for (int i = 0; i < 4; ++i) acc[k][i] = 0.0f;
   const int64_t ngroups = len_max > 0 ? (len_max + U - 1) / U : 0;
   if (role.row) {
-    row_issue();
+    // row_issue(0) before the first barrier, row_issue(1) right after it, so
+    // that work which must wait for loads of its own (row indices) is done
+    // while the first step computes instead of before it starts
+    row_issue(0);
     if (len_max > 0) {
       lds_barrier();
+      row_issue(1);
       for (int64_t it = 0; it < ngroups; ++it)
 #pragma unroll
         for (int j = 0; j < U; ++j) lds_barrier();
+    } else {
+      row_issue(1);
     }
     return;
   }
@@ -277,13 +284,24 @@ __device__ __forceinline__ bool fold_parts(WaveRole role, float (*stage)[16 * kS
 // With `pos`, the n tokens of the launch are pos[0 .. n) of the n_tokens rows
 // of x, h, g, u and row_index (out-of-range positions set the error word and
 // are neither read nor written).
-template <int WD, int A, int G, int KH, bool PACKED, bool UP, bool RW = false>
-__global__ __launch_bounds__(64 * ((G + 1) * KH + (RW ? 1 : 0))) void decode_gateup_kernel(
+// 16-byte pieces one copy-wave lane carries (RowCopyJob): the launcher sizes
+// each job to fit grid x 64 x kCopyVecs pieces.
+constexpr int kCopyVecs = 8;
+
+template <typename P>
+__device__ __forceinline__ P pick4(const P (&a)[kCopyJobLayers], int j) {
+  return j == 0 ? a[0] : j == 1 ? a[1] : j == 2 ? a[2] : a[3];
+}
+
+template <int WD, int A, int G, int KH, bool PACKED, bool UP, bool RW = false, bool CW = false>
+__global__ __launch_bounds__(64 * ((G + 1) * KH + (RW || CW ? 1 : 0))) void decode_gateup_kernel(
     int n, const int32_t* __restrict__ pos, int64_t n_tokens, int64_t d, int64_t f,
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ wg,
     const uint16_t* __restrict__ wu, const uint16_t* __restrict__ rows, int64_t n_rows,
     const int32_t* __restrict__ row_index, uint16_t* __restrict__ h, uint16_t* __restrict__ g_out,
-    uint16_t* __restrict__ u_out, int* err, const uint16_t* __restrict__ table, int64_t vocab) {
+    uint16_t* __restrict__ u_out, int* err, const uint16_t* __restrict__ table, int64_t vocab,
+    int64_t table_ld, RowCopyJob job) {
+  static_assert(!(RW && CW), "one extra wave");
   constexpr int FG = UP ? 8 : 16;                                   // features per row group
   // RW: the workgroup's G FG features of each token's table row, token t at
   // byte t kSliceBytes, loaded by the row wave
@@ -291,8 +309,9 @@ __global__ __launch_bounds__(64 * ((G + 1) * KH + (RW ? 1 : 0))) void decode_gat
   __shared__ __attribute__((aligned(16))) char xs[(A + 1) * KH * kXBlock];
   __shared__ float stage[G][16 * kStageLd];
   __shared__ __attribute__((aligned(16))) char erows[RW ? 64 * kSliceBytes : 16];
+  __shared__ __attribute__((aligned(16))) char cbuf[CW ? kCopyVecs * 1024 : 16];
   const int lane = threadIdx.x & 63;
-  const WaveRole role = wave_role<G, KH, RW>();
+  const WaveRole role = wave_role<G, KH, RW || CW>();
   const int grp = role.grp, part = role.part;
   const int r = lane & 15, q = lane >> 4;
   const int64_t rb = static_cast<int64_t>(blockIdx.x) * G + grp;   // this wave's row group
@@ -325,7 +344,7 @@ __global__ __launch_bounds__(64 * ((G + 1) * KH + (RW ? 1 : 0))) void decode_gat
   auto row_of = [&](int64_t v, bool& ok) -> const uint16_t* {
     if (table && v < 0) {
       ok = -1 - v < vocab;
-      return table + (-1 - v) * f;
+      return table + (-1 - v) * table_ld;
     }
     ok = v >= 0 && v < n_rows;
     return rows + v * f;
@@ -344,8 +363,9 @@ __global__ __launch_bounds__(64 * ((G + 1) * KH + (RW ? 1 : 0))) void decode_gat
         erow[c] = *reinterpret_cast<const uint4*>(erow_ok ? src + f0 + 8 * c : x);
     }
   };
-  auto row_issue = [&]() {
+  auto row_issue = [&](int phase) {
     if constexpr (RW) {
+      if (phase != 0) return;
       constexpr int kPieces = kSliceBytes / 16;          // per token; one 1 KB load per piece
       const int64_t fbase = static_cast<int64_t>(blockIdx.x) * G * FG;
       const int64_t p = tok_of(min(lane, n - 1));
@@ -365,9 +385,89 @@ __global__ __launch_bounds__(64 * ((G + 1) * KH + (RW ? 1 : 0))) void decode_gat
       }
     }
   };
+  // CW: the extra wave carries compact-row copies of other layers (job).
+  // Before the stream it fetches the row indices of its pieces (one wait),
+  // then loads every piece straight into LDS (global-to-LDS, over PCIe for
+  // rows of a pinned host table) with no wait in between; it joins the
+  // stream's barriers without waiting for them, and after the stream waits
+  // once and writes the pieces to their compact rows.  So the copies hide
+  // under the weight stream and hold up no compute wave, and no piece is
+  // held in registers across the stream.
+  // The job's rows (unique row u, layer j) of this launch, token-major (the
+  // rows of one token over the job's layers side by side: one contiguous
+  // read when the tables are interleaved token-major), are cut into job.per
+  // segments each; workgroup b copies segment b % per of row b / per, lane l
+  // its 16-byte pieces l, l + 64, ... (the launcher sizes job.seg to fit the
+  // wave).  The row's unique index does not depend on the device count, so
+  // the count, the cache code and the ID are loaded together and waited for
+  // once; this runs right after the stream's first barrier, beside the first
+  // step's MFMAs, and the pieces' loads are then never waited for before the
+  // stream ends.
+  uint32_t cmask = 0;            // pieces this lane loaded
+  int64_t c_dst = 0;             // byte offset of the segment in its compact-row block
+  int c_j = 0;                   // its layer in the job
+  auto copy_issue = [&](int phase) {
+    if constexpr (CW) {
+      if (phase != 1) return;
+      const uint32_t per = static_cast<uint32_t>(job.per);
+      const uint32_t r = blockIdx.x / per, sg = blockIdx.x - r * per;
+      if (r >= static_cast<uint32_t>(job.rows_max)) return;
+      const uint32_t nl = static_cast<uint32_t>(job.n_layers);
+      const uint32_t i = r / nl;
+      c_j = static_cast<int>(r - i * nl);
+      const int64_t u = job.part + static_cast<int64_t>(job.parts) * i;
+      const int64_t u_ld = u < job.max_unique ? u : job.max_unique - 1;
+      const int64_t nu = *job.n_unique;
+      const int32_t code = job.code[u_ld];
+      const int32_t id = job.uniq[u_ld];
+      if (u >= nu || u >= job.max_unique) return;
+      const char* src;
+      if (code >= 0) {
+        if (code >= job.capacity) {
+          if (lane == 0) flag_index_error(err);
+          return;
+        }
+        src = static_cast<const char*>(pick4(job.cache_rows, c_j)) + code * job.row_bytes;
+      } else {
+        if (id < 0 || id >= job.vocab) {
+          if (lane == 0) flag_index_error(err);
+          return;
+        }
+        src = static_cast<const char*>(pick4(job.table, c_j)) + id * pick4(job.table_ld, c_j);
+      }
+      const uint32_t vecs = static_cast<uint32_t>(job.row_bytes / 16);
+      const uint32_t c0 = sg * static_cast<uint32_t>(job.seg);
+      const uint32_t c1 = min(c0 + static_cast<uint32_t>(job.seg), vecs);
+      c_dst = u * job.row_bytes + static_cast<int64_t>(c0) * 16;
+      src += static_cast<int64_t>(c0) * 16;
+#pragma unroll
+      for (int k = 0; k < kCopyVecs; ++k) {
+        const uint32_t c = static_cast<uint32_t>(k) * 64u + lane;
+        if (c0 + c < c1) {
+          __builtin_amdgcn_global_load_lds(src + c * 16u,
+                                           static_cast<lds_void*>((lds_char*)(cbuf) + k * 1024), 16, 0, 0);
+          cmask |= 1u << k;
+        }
+      }
+    } else {
+      row_issue(phase);
+    }
+  };
   stream_act_ring<WD, A, KH, PACKED ? 1024 : 64>(role, active, pa, wstep, x, d, act_row, n,
                                                   (lds_char*)(xs), s0, s1, len, acc, fetch_row,
-                                                  row_issue);
+                                                  copy_issue);
+  if constexpr (CW) {
+    if (role.row && cmask) {
+      wait_vmcnt<0>();
+      char* dst = static_cast<char*>(pick4(job.rows, c_j)) + c_dst;
+#pragma unroll
+      for (int k = 0; k < kCopyVecs; ++k) {
+        if ((cmask >> k) & 1u)
+          *reinterpret_cast<uint4*>(dst + (k * 64 + lane) * 16) =
+              *reinterpret_cast<const uint4*>(cbuf + k * 1024 + lane * 16);
+      }
+    }
+  }
   if constexpr (RW) {
     if (role.row) wait_vmcnt<0>();   // its pieces are in LDS
     __syncthreads();
@@ -467,7 +567,7 @@ __global__ __launch_bounds__(64 * (G + 1) * KH) void decode_down_kernel(int n, i
   stream_act_ring<WD, A, KH, PACKED ? 1024 : 64>(role, active, pa, wstep, h, f,
                                                   [](int t) -> int64_t { return t; }, n,
                                                   (lds_char*)(xs), s0, s1, len, acc, []() {},
-                                                  []() {});
+                                                  [](int) {});
   if (!fold_parts<KH>(role, stage, acc) || !active) return;
   const float* st = stage[grp];
   const int t = lane;
@@ -587,11 +687,37 @@ static int device_cus() {
 
 // `up`: the weights hold W_up (the STAPLE layer; row-major: wu, packed: the
 // interleaved blocks) or not (the STEM layer: W_gate alone, u = E[t]).
+int decode_gateup_grid(int64_t f, bool up) {
+  const int64_t groups = up ? f / 8 : f / 16;
+  const int64_t cus = device_cus();
+  const bool wide = groups > 4 * cus;
+  const int per = up ? (wide ? 6 : 4)
+                     : (groups <= 2 * cus ? 2 : groups <= 3 * cus ? 3 : wide ? 6 : 4);
+  return static_cast<int>((groups + per - 1) / per);
+}
+
+// The segments of a gate/up launch's copy job of at most `rows` compact rows
+// of d_ff f: every row gets gridDim / rows workgroups; false when a
+// workgroup's segment would not fit its copy wave (64 lanes x kCopyVecs
+// pieces of 16 bytes).
+bool decode_copy_plan(int64_t rows, int64_t f, bool up, int* per, int* seg) {
+  const int64_t grid = decode_gateup_grid(f, up);
+  if (rows <= 0 || rows > grid) return false;
+  const int64_t p = grid / rows, vecs = f * 2 / 16, sz = (vecs + p - 1) / p;
+  if (sz > 64 * kCopyVecs) return false;
+  *per = static_cast<int>(p);
+  *seg = static_cast<int>(sz);
+  return true;
+}
+
 hipError_t decode_gateup(int64_t n, const int32_t* pos, int64_t n_tokens, int64_t d, int64_t f,
                          const void* x, const void* wg, const void* wu, const void* rows,
                          int64_t n_rows, const int32_t* row_index, void* h, void* g_out,
                          void* u_out, hipStream_t s, int* err, bool packed, bool up,
-                         const void* table, int64_t vocab) {
+                         const void* table, int64_t vocab, int64_t table_ld,
+                         const RowCopyJob* job) {
+  if (table_ld <= 0) table_ld = f;
+  if (job && (table || !packed)) return hipErrorInvalidValue;   // copies ride the packed kernel only
   // STAPLE: 4 row groups (32 features) per workgroup, on two K parts, while
   // that fits one workgroup per CU; else 6 row groups on one part (d_ff
   // 11008: 230 workgroups of 7 waves instead of 344 of 10 on 256 CUs whose
@@ -606,36 +732,39 @@ hipError_t decode_gateup(int64_t n, const int32_t* pos, int64_t n_tokens, int64_
   const int per = up ? (wide ? 6 : 4)
                      : (groups <= 2 * cus ? 2 : groups <= 3 * cus ? 3 : wide ? 6 : 4);
   const unsigned grid = static_cast<unsigned>((groups + per - 1) / per);
+  const RowCopyJob no_job{};
   auto go = [&](auto kern, int threads) {
-    if (table) threads += 64;   // the row wave
+    if (table || job) threads += 64;   // the row wave or the copy wave
     kern<<<dim3(grid), dim3(threads), 0, s>>>(
         static_cast<int>(n), pos, n_tokens, d, f, static_cast<const uint16_t*>(x),
         static_cast<const uint16_t*>(wg),
         static_cast<const uint16_t*>(wu), static_cast<const uint16_t*>(rows), n_rows, row_index,
         static_cast<uint16_t*>(h), static_cast<uint16_t*>(g_out), static_cast<uint16_t*>(u_out), err,
-        static_cast<const uint16_t*>(table), vocab);
+        static_cast<const uint16_t*>(table), vocab, table_ld, job ? *job : no_job);
   };
-  auto pick = [&](auto packed_tag, auto up_tag, auto rw_tag) {
+  auto pick = [&](auto packed_tag, auto up_tag, auto rw_tag, auto cw_tag) {
     constexpr bool P = decltype(packed_tag)::value, U = decltype(up_tag)::value;
-    constexpr bool R = decltype(rw_tag)::value;
+    constexpr bool R = decltype(rw_tag)::value, C = decltype(cw_tag)::value;
     constexpr int WD = kGateUpAhead, A = kGateUpActAhead, KH = kGateUpParts;
-    if (per == 6) go(decode_gateup_kernel<kGateUpAheadLong, A, 6, 1, P, U, R>, 64 * 7);
-    else if (per == 4) go(decode_gateup_kernel<WD, A, 4, KH, P, U, R>, 64 * 5 * KH);
+    if (per == 6) go(decode_gateup_kernel<kGateUpAheadLong, A, 6, 1, P, U, R, C>, 64 * 7);
+    else if (per == 4) go(decode_gateup_kernel<WD, A, 4, KH, P, U, R, C>, 64 * 5 * KH);
     else if constexpr (!U) {
-      if (per == 3) go(decode_gateup_kernel<WD, A, 3, KH, P, U, R>, 64 * 4 * KH);
-      else go(decode_gateup_kernel<WD, A, 2, KH, P, U, R>, 64 * 3 * KH);
+      if (per == 3) go(decode_gateup_kernel<WD, A, 3, KH, P, U, R, C>, 64 * 4 * KH);
+      else go(decode_gateup_kernel<WD, A, 2, KH, P, U, R, C>, 64 * 3 * KH);
     }
   };
   using T_ = std::true_type;
   using F_ = std::false_type;
   // rows read in place (a table given): packed weights only, with the row wave
   if (table && !packed) return hipErrorInvalidValue;
-  if (table && up) pick(T_{}, T_{}, T_{});
-  else if (table) pick(T_{}, F_{}, T_{});
-  else if (packed && up) pick(T_{}, T_{}, F_{});
-  else if (packed) pick(T_{}, F_{}, F_{});
-  else if (up) pick(F_{}, T_{}, F_{});
-  else pick(F_{}, F_{}, F_{});
+  if (table && up) pick(T_{}, T_{}, T_{}, F_{});
+  else if (table) pick(T_{}, F_{}, T_{}, F_{});
+  else if (job && up) pick(T_{}, T_{}, F_{}, T_{});
+  else if (job) pick(T_{}, F_{}, F_{}, T_{});
+  else if (packed && up) pick(T_{}, T_{}, F_{}, F_{});
+  else if (packed) pick(T_{}, F_{}, F_{}, F_{});
+  else if (up) pick(F_{}, T_{}, F_{}, F_{});
+  else pick(F_{}, F_{}, F_{}, F_{});
   return hipGetLastError();
 }
 

@@ -329,7 +329,9 @@ hipError_t launch_assemble_rows_table(const void* cache_rows, int64_t capacity, 
 // The same assembly for several layers at once (the tables of a layer stack
 // share one cache map): work item k = (layer k / max_unique, unique row
 // k % max_unique), one row per workgroup, so the PCIe reads of every layer's
-// misses are in flight together.
+// misses are in flight together.  Table l's token rows are table_ld[l] bytes
+// apart (row_bytes for a table of its own, more when several layers' tables
+// are interleaved token-major).
 __global__ __launch_bounds__(kRowThreads) void assemble_rows_layers_kernel(
     LayerRowSources src, int n_layers, int64_t capacity, int64_t vocab, const int32_t* uniq,
     const int32_t* code, const int32_t* n_unique_p, int64_t max_unique, int64_t row_bytes,
@@ -354,7 +356,7 @@ __global__ __launch_bounds__(kRowThreads) void assemble_rows_layers_kernel(
         if (threadIdx.x == 0) flag_index_error(err);
         continue;
       }
-      from = static_cast<const char*>(src.table[l]) + id * row_bytes;
+      from = static_cast<const char*>(src.table[l]) + id * src.table_ld[l];
     }
     copy_row16(reinterpret_cast<const uint4*>(from),
                reinterpret_cast<uint4*>(static_cast<char*>(src.rows[l]) + u * row_bytes),

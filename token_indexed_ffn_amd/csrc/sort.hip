@@ -298,6 +298,75 @@ __global__ __launch_bounds__(64) void dedup_wave_kernel(const int32_t* ids, int6
   }
 }
 
+// Dedup and cache probe of a decode batch (at most 64 tokens) in one wave:
+// the one-wave dedup above, then every unique ID's cache slot (code[u] = slot
+// on a hit, -1 - m on the m-th miss in ascending u), the miss list and, with
+// row_src, each token's row source (its slot, or -1 - id for a row of the
+// table; INT32_MIN for an ID outside the table).  The same outputs as
+// staple_dedup followed by staple_cache_lookup, in one launch.
+__global__ __launch_bounds__(64) void dedup_lookup_wave_kernel(
+    const int32_t* ids, int64_t n, int64_t vocab, const int32_t* id_to_slot, int32_t* uniq,
+    int32_t* inv, int32_t* sorted_pos, int32_t* seg_start, int32_t* n_unique, int32_t* code,
+    int32_t* miss_uidx, int32_t* n_miss, int32_t* row_src, int* err) {
+  const int lane = threadIdx.x;
+  uint64_t key = dedup_key(ids, lane, n, vocab, err);
+#pragma unroll
+  for (int k = 2; k <= 64; k <<= 1) {
+#pragma unroll
+    for (int j = k >> 1; j >= 1; j >>= 1) {
+      const uint64_t other = shfl_xor_u64(key, j);
+      const bool asc = (lane & k) == 0;
+      const bool lower = (lane & j) == 0;
+      key = (lower == asc) ? (key < other ? key : other) : (key < other ? other : key);
+    }
+  }
+  const bool valid = lane < n;
+  const int32_t id = static_cast<int32_t>(key >> 32);
+  const int32_t prev = __shfl_up(id, 1, 64);
+  const bool first = valid && (lane == 0 || prev != id);
+  const uint64_t starts = __ballot(first);
+  const int seg = __popcll(starts & ((2ull << lane) - 1)) - 1;
+  const bool in_table = id >= 0 && id < vocab;
+  const int32_t slot = valid && in_table ? id_to_slot[id] : -1;
+  const bool miss = first && slot < 0;
+  const uint64_t misses = __ballot(miss);
+  if (valid) {
+    const int32_t pos = static_cast<int32_t>(key & 0xffffffffu);
+    if (first) {
+      uniq[seg] = id;
+      seg_start[seg] = lane;
+      if (miss) {
+        const int m = __popcll(misses & ((1ull << lane) - 1));
+        code[seg] = -1 - m;
+        miss_uidx[m] = seg;
+      } else {
+        code[seg] = slot;
+      }
+    }
+    sorted_pos[lane] = pos;
+    inv[pos] = seg;
+    if (row_src) row_src[pos] = in_table ? (slot >= 0 ? slot : -1 - id) : INT32_MIN;
+  }
+  if (lane == 0) {
+    const int total = __popcll(starts);
+    *n_unique = total;
+    seg_start[total] = static_cast<int32_t>(n);
+    *n_miss = __popcll(misses);
+  }
+}
+
+hipError_t launch_dedup_lookup_wave(const int32_t* ids, int64_t n, int64_t vocab,
+                                    const int32_t* id_to_slot, int32_t* uniq, int32_t* inv,
+                                    int32_t* sorted_pos, int32_t* seg_start, int32_t* n_unique,
+                                    int32_t* code, int32_t* miss_uidx, int32_t* n_miss,
+                                    int32_t* row_src, hipStream_t s, int* err) {
+  if (n < 1 || n > 64) return hipErrorInvalidValue;
+  dedup_lookup_wave_kernel<<<dim3(1), dim3(64), 0, s>>>(ids, n, vocab, id_to_slot, uniq, inv,
+                                                        sorted_pos, seg_start, n_unique, code,
+                                                        miss_uidx, n_miss, row_src, err);
+  return hipGetLastError();
+}
+
 size_t dedup_workspace_bytes(int64_t n) {
   if (n <= kTile) return 0;
   return static_cast<size_t>(next_pow2(n)) * sizeof(uint64_t);
