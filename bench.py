@@ -853,15 +853,22 @@ def run_offload_train(torch, st, w, steps, warmup):
     ev_ready = torch.cuda.Event()
     stats = {"pack_s": 0.0, "copy_ms": 0.0, "hit_tokens": 0, "gu_us": []}
 
-    def step(mode):
-        dd = st.staple_dedup(T["ids"], v, out=T["dd"], workspace=T["dd_ws"])
-        lk = st.staple_cache_lookup(dd["uniq"], dd["n_unique"], O["id_to_slot"], out=lk_out)
+    def step(mode, B=None, before_rows=None, rows_event=None):
+        """B: the step's own dedup, probe and row-gradient buffers (default:
+        the shared ones); before_rows: called once the miss list is known and
+        before anything reads the table's rows (the optimizer's finish)."""
+        dd = st.staple_dedup(T["ids"], v, out=T["dd"] if B is None else B["dd"],
+                             workspace=T["dd_ws"])
+        lk = st.staple_cache_lookup(dd["uniq"], dd["n_unique"], O["id_to_slot"],
+                                    out=lk_out if B is None else B["lk"])
         sp = st.staple_split_tokens(dd["inv"], lk["code"], dd["n_unique"], out=sp_out)
         counts_host.copy_(sp["counts"], non_blocking=True)
         m = _miss_list_to_host(torch, lk, miss_host)        # one host sync for both
         n_hit, n_miss_tok = int(counts_host[0]), int(counts_host[1])
         stats["hit_tokens"] = n_hit
         side.wait_stream(main)
+        if before_rows is not None:
+            before_rows()
         t0 = time.perf_counter()
         with torch.cuda.stream(side):
             ev_copy0.record(side)
@@ -888,8 +895,9 @@ def run_offload_train(torch, st, w, steps, warmup):
         st.staple_ffn_down(fw["h"], T["w_down"], fw["y"])
         st.staple_ffn_bwd_table_grad(T["dy"], T["x"], T["w_gate"], T["w_up"], T["w_down"], fw["g"],
                                      fw["u"], fw["h"], dd["sorted_pos"], dd["seg_start"],
-                                     dd["n_unique"], inv=dd["inv"], out=T["bwd"],
-                                     workspace=T["bwd_ws"])
+                                     dd["n_unique"], inv=dd["inv"],
+                                     out=T["bwd"] if B is None else B["bwd"],
+                                     workspace=T["bwd_ws"], rows_event=rows_event)
         return m
 
     def timed(mode):
@@ -915,12 +923,18 @@ def run_offload_train(torch, st, w, steps, warmup):
     res = {k: timed(k) for k in ("staged", "direct", "resident")}
     host_adamw = run_host_adamw(torch, st, O, T, lk_out)
     mode = min(("staged", "direct"), key=lambda k: res[k][0])
-    ms, _, _, m = res[mode]
+    ms_free, _, _, m = res[mode]
     ms_res = res["resident"][0]
+    opt = run_offload_train_optimizer(torch, st, O, T, lk_out, step, mode, steps, warmup)
+    ms = opt["overlapped_ms_per_step"]
+    opt["ratio_to_optimizer_free_step"] = ms / ms_free
+    opt["serial_ratio_to_optimizer_free_step"] = opt["serial_ms_per_step"] / ms_free
     gu_us = float(np.median(stats["gu_us"]))
     gu_flops = 4 * stats["hit_tokens"] * d * f
     achieved = gu_flops / (gu_us * 1e-6) / 1e12
     out = {"workload": w.name, "ms_per_step": ms, "tokens_per_s": n / (ms * 1e-3),
+           "optimizer_free_ms_per_step": ms_free,
+           "optimizer_free_tokens_per_s": n / (ms_free * 1e-3), "optimizer": opt,
            "method": mode, "n_unique": int(T["dd"]["n_unique"].item()), "miss_rows": m,
            "roofline": {
                "kernel": "gemm_kernel<bf16,GateUp> (staple_ffn_gate_up_tokens over the cached "
@@ -942,9 +956,94 @@ def run_offload_train(torch, st, w, steps, warmup):
                    "pack into pinned staging + one H2D copy; direct: a kernel reads them from the "
                    "pinned host table) while the gate/up GEMM of the cached tokens runs (rows "
                    "from the cache slots); then the missed tokens' gate/up, down, backward. "
-                   "resident: the same step with the miss rows already in HBM, for the hidden "
-                   "fraction = 1 - (t - t_resident) / (host pack + copy time)")
+                   "ms_per_step and tokens_per_s include the table rows' AdamW update on the host "
+                   "overlapped with the GPU (optimizer.overlapped); optimizer_free_*: the same "
+                   "step without it. resident: the step with the miss rows already in HBM, for "
+                   "the hidden fraction = 1 - (t - t_resident) / (host pack + copy time)")
     return out
+
+
+def run_offload_train_optimizer(torch, st, O, T, lk_out, step, mode, steps, warmup):
+    """The offloaded training step with the AdamW update of the table rows on
+    the host (bf16 table, fp32 moments in host memory; STAPLE Figure 4
+    caption), in two schedules:
+      serial: after the step, the row gradients come to the host, host threads
+        update the rows, the cached copies are refreshed; then the next step.
+      overlapped (staple_host_adamw_*): the row gradients leave in chunks on a
+        copy stream as soon as the backward's segment sum has formed them, a
+        host worker updates each chunk as it lands and refreshes its cached
+        copies, all while the GPU runs the rest of the backward and the next
+        step's dedup and probe; the next step waits for the update only
+        before it reads table rows (miss copy, cached tokens' gate/up).
+    Each step's dedup, probe and row gradients live in one of two buffer sets
+    (alternating), so the update of one step reads buffers the next step does
+    not write."""
+    import numpy as np
+    table, cache = O["tables"][0], O["cache_rows"][0]
+    vocab, f = table.shape
+    n = T["ids"].numel()
+    m = torch.zeros(vocab, f, dtype=torch.float32)
+    v = torch.zeros(vocab, f, dtype=torch.float32)
+    hp = dict(lr=3e-4, weight_decay=1e-4)
+    sets = [{"dd": {k: torch.empty_like(t) for k, t in T["dd"].items()},
+             "lk": {k: torch.empty_like(t) for k, t in lk_out.items()},
+             "bwd": dict(T["bwd"], d_rows=torch.empty_like(T["bwd"]["d_rows"]))}
+            for _ in range(2)]
+    main = torch.cuda.current_stream()
+    copy_s = torch.cuda.Stream()
+    grad_h = torch.empty(n, f, dtype=torch.float32, pin_memory=True)
+    uniq_h = torch.empty(n, dtype=torch.int32, pin_memory=True)
+    t_step = [0]
+
+    def serial(k):
+        B = sets[k % 2]
+        step(mode, B)
+        dd = B["dd"]
+        u = int(dd["n_unique"].item())                 # synchronizes
+        grad_h[:u].copy_(B["bwd"]["d_rows"][:u])
+        uniq_h[:u].copy_(dd["uniq"][:u])
+        t_step[0] += 1
+        st.staple_adamw_rows_host(table, m, v, uniq_h[:u], grad_h[:u], step=t_step[0], **hp)
+        st.staple_cache_refresh(table, dd["uniq"], B["lk"]["code"], dd["n_unique"], cache)
+
+    ha = st.HostAdamW(n, f)
+    pending = [False]
+
+    def finish():
+        if pending[0]:
+            ha.finish(main)
+            pending[0] = False
+
+    def overlapped(k):
+        B = sets[k % 2]
+        step(mode, B, before_rows=finish, rows_event=ha.event)
+        t_step[0] += 1
+        ha.start(table, m, v, B["dd"]["uniq"], B["dd"]["n_unique"], B["bwd"]["d_rows"],
+                 step=t_step[0], copy_stream=copy_s, code=B["lk"]["code"], cache_rows=cache, **hp)
+        pending[0] = True
+
+    def timed(fn):
+        for k in range(warmup):
+            fn(k)
+        finish()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for k in range(steps):
+            fn(k)
+        finish()
+        torch.cuda.synchronize()
+        if st.staple_get_device_error() != 0:
+            raise RuntimeError("device error in offload train with the optimizer")
+        return (time.perf_counter() - t0) / steps * 1e3
+
+    ms_serial = timed(serial)
+    ms_ovl = timed(overlapped)
+    ha.close()
+    return {"serial_ms_per_step": ms_serial, "overlapped_ms_per_step": ms_ovl,
+            "rows_per_step": int(sets[0]["dd"]["n_unique"].item()),
+            "note": "AdamW of the batch's unique table rows on the host (bf16 table, fp32 moments "
+                    "in host memory) and the refresh of their cached copies, once per step: "
+                    "serial after the step, or overlapped with it (staple_host_adamw_*)"}
 
 
 def run_host_adamw(torch, st, O, T, lk, reps=3):

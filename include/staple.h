@@ -559,6 +559,51 @@ staple_status_t staple_cache_refresh(const void* table, int64_t vocab, int64_t d
                                      const int32_t* n_unique, int64_t max_unique, void* cache_rows,
                                      int64_t capacity, void* stream);
 
+/* The host update overlapped with the GPU step (the pages' placement keeps
+ * the tables and their AdamW moments in host DRAM and still trains within 3%
+ * of dense: STAPLE Figure 4 caption; abstract).  A handle owns pinned staging
+ * for the gradient rows, a "rows ready" event and a worker thread:
+ *   staple_host_adamw_create: once, for up to max_rows rows of width d_ff
+ *     (allocates pinned memory and events; not on a hot path).
+ *   staple_host_adamw_event: the handle's rows-ready event (a hipEvent_t);
+ *     pass it to staple_ffn_bwd_table_grad as rows_event, which records it
+ *     right after d_rows is complete, before the weight-gradient GEMMs.
+ *   staple_host_adamw_start: after that backward call, on the same thread:
+ *     enqueues on copy_stream a wait for the event and the copies of
+ *     *n_unique and uniq to the host, then returns; the worker then copies the
+ *     gradient rows to the host in chunks on copy_stream and applies the
+ *     update of staple_adamw_rows_host (same arguments; table, m, v host
+ *     memory) to each chunk as it lands, while the GPU goes on.  grad, uniq,
+ *     n_unique: device memory (d_rows and staple_dedup's uniq, n_unique),
+ *     unchanged until the update finishes; uniq holds at least max_rows
+ *     entries (all max_rows are copied) and grad at least *n_unique rows of
+ *     d_ff floats.  code, cache_rows, capacity: the batch's cache probe
+ *     (staple_cache_lookup's code) and the HBM cache; when code is not NULL
+ *     and capacity > 0 the worker also refreshes the cached copies of each
+ *     updated chunk (staple_cache_refresh's operation, on a stream of the
+ *     handle; the table must then be pinned).  A second start before finish
+ *     returns STAPLE_ERR_INVALID_ARGUMENT.
+ *   staple_host_adamw_finish: waits for the host update and returns its
+ *     status (STAPLE_ERR_HOST for an ID outside the table,
+ *     STAPLE_ERR_INDEX_RANGE for a row count past max_rows: nothing
+ *     updated); on success `stream` (NULL: the null stream) is made to wait
+ *     for the refreshes.  Read the host table, and the cache on another
+ *     stream, only after it.
+ *   staple_host_adamw_destroy: waits for a running update, then frees all.
+ * The rows are updated by the same routine as staple_adamw_rows_host, each
+ * once and independently: the same bits as the serial update. */
+typedef struct staple_host_adamw staple_host_adamw_t;
+staple_status_t staple_host_adamw_create(int64_t max_rows, int64_t d_ff, staple_host_adamw_t** out);
+void* staple_host_adamw_event(staple_host_adamw_t* h);
+staple_status_t staple_host_adamw_start(staple_host_adamw_t* h, void* table, float* m, float* v,
+                                        int64_t vocab, int32_t dtype, const int32_t* uniq,
+                                        const int32_t* n_unique, const float* grad, float lr,
+                                        float beta1, float beta2, float eps, float weight_decay,
+                                        int64_t step, int32_t n_threads, const int32_t* code,
+                                        void* cache_rows, int64_t capacity, void* copy_stream);
+staple_status_t staple_host_adamw_finish(staple_host_adamw_t* h, void* stream);
+void staple_host_adamw_destroy(staple_host_adamw_t* h);
+
 /* ------------------------------------------------------------------------
  * Backward of one augmented layer with the table-row gradient.
  *   dy [n_tokens x d_model] (dtype): upstream gradient of y.
@@ -581,6 +626,10 @@ staple_status_t staple_cache_refresh(const void* table, int64_t vocab, int64_t d
  *     NULL) while the gradient still flows through W_up into dx and d_rows.
  *   w_up NULL: the STEM layer (saved_u = E[t] from its forward); dx = dL/dg
  *     W_gate, d_rows as above, dw_up neither computed nor written.
+ *   rows_event: a hipEvent_t or NULL; when given it is recorded on `stream`
+ *     right after d_rows is complete (before the weight- and input-gradient
+ *     GEMMs), e.g. staple_host_adamw_event's, so the rows can leave for the
+ *     host while the rest of the backward runs.
  * In bf16 the backward reads bf16 g and u, forms dL/du and dL/dg in fp32 and
  * rounds them to bf16 once, as operands of the weight- and input-gradient
  * contractions; every contraction accumulates in fp32; d_rows sums the fp32
@@ -604,7 +653,7 @@ staple_status_t staple_ffn_bwd_table_grad(int64_t n_tokens, int64_t d_model, int
                                           float* d_rows, void* dx,
                                           float* dw_gate, float* dw_up, float* dw_down,
                                           int32_t freeze_up, void* ws, size_t ws_bytes,
-                                          void* stream);
+                                          void* rows_event, void* stream);
 
 #ifdef __cplusplus
 }

@@ -539,6 +539,66 @@ def staple_adamw_rows_host(table: torch.Tensor, m: torch.Tensor, v: torch.Tensor
                                         weight_decay, step, n_threads), "staple_adamw_rows_host")
 
 
+class HostAdamW:
+    """The host AdamW update overlapped with the GPU (staple_host_adamw_*): the
+    gradient rows leave for the host right after the backward's segment sum
+    (pass `event` to staple_ffn_bwd_table_grad as rows_event), a worker
+    updates them as they land and, given the batch's cache probe, refreshes
+    their cached copies; finish() waits for the host update and orders
+    `stream` after the refreshes."""
+
+    def __init__(self, max_rows: int, d_ff: int):
+        h = ctypes.c_void_p()
+        _check(lib().staple_host_adamw_create(int(max_rows), int(d_ff), ctypes.byref(h)),
+               "staple_host_adamw_create")
+        self._h = h
+        self.max_rows, self.d_ff = int(max_rows), int(d_ff)
+        self.event = lib().staple_host_adamw_event(h)
+
+    def start(self, table: torch.Tensor, m: torch.Tensor, v: torch.Tensor, uniq: torch.Tensor,
+              n_unique: torch.Tensor, grad: torch.Tensor, *, lr: float, weight_decay: float,
+              step: int, copy_stream, code: Optional[torch.Tensor] = None,
+              cache_rows: Optional[torch.Tensor] = None, beta1: float = 0.9,
+              beta2: float = 0.999, eps: float = 1e-8, n_threads: int = 0) -> None:
+        for t in (table, m, v):
+            if t.is_cuda or not t.is_contiguous():
+                raise ValueError("table and moments are contiguous host tensors")
+        _dev(uniq, n_unique, grad)
+        if uniq.numel() < self.max_rows or grad.dim() != 2 or grad.shape[1] != self.d_ff \
+                or grad.shape[0] < self.max_rows or table.shape[1] != self.d_ff:
+            raise ValueError("uniq and grad must hold max_rows rows of the handle's width")
+        if (code is None) != (cache_rows is None):
+            raise ValueError("code and cache_rows go together")
+        if code is not None:
+            _dev(code, cache_rows)
+            if code.numel() < self.max_rows or cache_rows.shape[-1] != self.d_ff \
+                    or not table.is_pinned():
+                raise ValueError("a refresh needs the batch's code, the cache of the table's "
+                                 "width and a pinned table")
+        vocab = table.shape[0]
+        cap = 0 if cache_rows is None else cache_rows.shape[0]
+        _check(lib().staple_host_adamw_start(self._h, _p(table), _p(m), _p(v), vocab, _dt(table),
+                                             _p(uniq), _p(n_unique), _p(grad), lr, beta1, beta2,
+                                             eps, weight_decay, step, n_threads, _p(code),
+                                             _p(cache_rows), cap, _stream(copy_stream)),
+               "staple_host_adamw_start")
+
+    def finish(self, stream=None) -> None:
+        _check(lib().staple_host_adamw_finish(self._h, _stream(stream)),
+               "staple_host_adamw_finish")
+
+    def close(self) -> None:
+        if self._h:
+            lib().staple_host_adamw_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
 def staple_cache_refresh(table: torch.Tensor, uniq: torch.Tensor, code: torch.Tensor,
                          n_unique: torch.Tensor, cache_rows: torch.Tensor, stream=None) -> None:
     """cache_rows[code[u]] = table[uniq[u]] for the cached rows among uniq[:n_unique]."""
@@ -560,7 +620,7 @@ def staple_ffn_bwd_table_grad(dy: torch.Tensor, x: torch.Tensor, w_gate: torch.T
                               max_unique: Optional[int] = None,
                               freeze_up: bool = False, out_dtype: Optional[torch.dtype] = None,
                               out: Optional[dict] = None, workspace: Optional[torch.Tensor] = None,
-                              stream=None) -> dict:
+                              rows_event: Optional[int] = None, stream=None) -> dict:
     """Backward with the table-row gradient: d_rows, dx, dw_gate, dw_up, dw_down
     (w_up None: the STEM layer, no dw_up).  sorted_pos, inv, seg_start, n_unique are
     staple_dedup's outputs for the batch; saved_h None recomputes h from saved_g,
@@ -587,8 +647,8 @@ def staple_ffn_bwd_table_grad(dy: torch.Tensor, x: torch.Tensor, w_gate: torch.T
         _p(saved_g), _p(saved_u), _p(saved_h), _p(sorted_pos), _p(inv), _p(seg_start),
         _p(n_unique), mu,
         _p(out["d_rows"]), _p(out["dx"]), _p(out["dw_gate"]), _p(out.get("dw_up")),
-        _p(out["dw_down"]), int(bool(freeze_up)), _p(ws), _ws_size(ws), _stream(stream)),
-        "staple_ffn_bwd_table_grad")
+        _p(out["dw_down"]), int(bool(freeze_up)), _p(ws), _ws_size(ws), rows_event,
+        _stream(stream)), "staple_ffn_bwd_table_grad")
     return out
 
 

@@ -77,7 +77,14 @@ _SIGS = {
     "staple_ffn_bwd_table_grad": (c_i32, [c_i64, c_i64, c_i64, c_i32, c_i32, c_vp, c_vp, c_vp,
                                           c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp,
                                           c_i64, c_vp, c_vp, c_vp, c_vp, c_vp, c_i32, c_vp, c_sz,
-                                          c_vp]),
+                                          c_vp, c_vp]),
+    "staple_host_adamw_create": (c_i32, [c_i64, c_i64, c_vp]),
+    "staple_host_adamw_event": (c_vp, [c_vp]),
+    "staple_host_adamw_start": (c_i32, [c_vp, c_vp, c_vp, c_vp, c_i64, c_i32, c_vp, c_vp, c_vp,
+                                        c_f32, c_f32, c_f32, c_f32, c_f32, c_i64, c_i32, c_vp,
+                                        c_vp, c_i64, c_vp]),
+    "staple_host_adamw_finish": (c_i32, [c_vp, c_vp]),
+    "staple_host_adamw_destroy": (None, [c_vp]),
 }
 
 EXPORTED = tuple(_SIGS)

@@ -904,8 +904,8 @@ static staple_status_t bwd_impl(int64_t n, int64_t d, int64_t f, int32_t dtype, 
                                 const void* saved_h, const int32_t* sorted_pos, const int32_t* inv,
                                 const int32_t* seg_start, const int32_t* n_unique,
                                 int64_t max_unique, float* d_rows, void* dx, float* dw_gate,
-                                float* dw_up, float* dw_down, bool fz, void* ws, hipStream_t s,
-                                int* err) {
+                                float* dw_up, float* dw_down, bool fz, void* ws,
+                                hipEvent_t rows_event, hipStream_t s, int* err) {
   void* dgu = ws;
   char* aux = n > 0 ? static_cast<char*>(ws) + bwd_dgu_bytes(n, f, dtype) : nullptr;
   void* seg_ws = n > 0 ? aux + bwd_aux_bytes(n, f) : nullptr;
@@ -922,6 +922,7 @@ static staple_status_t bwd_impl(int64_t n, int64_t d, int64_t f, int32_t dtype, 
       HIPCALL(launch_segment_sum(dtype, dgu, 2 * f, f, n, f, sorted_pos, inv, seg_start, n_unique,
                                  max_unique, d_rows, seg_ws, s, err));
   }
+  if (rows_event) HIPCALL(hipEventRecord(rows_event, s));   // d_rows complete
   // h for dW_down: the forward's, or recomputed from the saved g and u into
   // the fp32 region (after the segment sum has read it, in stream order)
   const void* h = saved_h;
@@ -943,7 +944,8 @@ staple_status_t staple_ffn_bwd_table_grad(
     const void* saved_u, const void* saved_h, const int32_t* sorted_pos, const int32_t* inv,
     const int32_t* seg_start,
     const int32_t* n_unique, int64_t max_unique, float* d_rows, void* dx, float* dw_gate,
-    float* dw_up, float* dw_down, int32_t freeze_up, void* ws, size_t ws_bytes, void* stream) {
+    float* dw_up, float* dw_down, int32_t freeze_up, void* ws, size_t ws_bytes, void* rows_event,
+    void* stream) {
   if (!valid_dtype(dtype) || !valid_dtype(out_dtype)) return STAPLE_ERR_UNSUPPORTED;
   if (!ffn_shape_ok(n, d, f, dtype)) return STAPLE_ERR_UNSUPPORTED;
   // w_up null: the STEM layer (no up-projection, so no dw_up either)
@@ -964,10 +966,12 @@ staple_status_t staple_ffn_bwd_table_grad(
   if (dtype == STAPLE_BF16)
     return bwd_impl<bf16_t>(n, d, f, dtype, out_dtype, dy, x, w_gate, w_up, w_down, saved_g,
                             saved_u, saved_h, sorted_pos, inv, seg_start, n_unique, max_unique,
-                            d_rows, dx, dw_gate, dw_up, dw_down, fz, ws, s, err);
+                            d_rows, dx, dw_gate, dw_up, dw_down, fz, ws,
+                            static_cast<hipEvent_t>(rows_event), s, err);
   return bwd_impl<float>(n, d, f, dtype, out_dtype, dy, x, w_gate, w_up, w_down, saved_g, saved_u,
                          saved_h, sorted_pos, inv, seg_start, n_unique, max_unique, d_rows, dx,
-                         dw_gate, dw_up, dw_down, fz, ws, s, err);
+                         dw_gate, dw_up, dw_down, fz, ws, static_cast<hipEvent_t>(rows_event), s,
+                         err);
 }
 
 }  // extern "C"

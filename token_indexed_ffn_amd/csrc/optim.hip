@@ -304,3 +304,236 @@ hipError_t launch_cache_refresh(const void* table, int64_t vocab, const int32_t*
 }
 
 }  // namespace staple
+
+// ---------------------------------------------------------------------------
+// Host update overlapped with the GPU: the gradient rows come to the host in
+// chunks on a copy stream as soon as the backward has formed them (an event
+// recorded right after the table-row segment sum), and a worker thread of
+// the update updates each chunk with the library's host threads as it lands,
+// while the GPU goes on with the rest of the backward.  The rows are updated
+// by the same routine as staple_adamw_rows_host, each row once and
+// independently, so the result is the same bits as the serial update.
+// ---------------------------------------------------------------------------
+#include <condition_variable>
+#include <mutex>
+#include <new>
+
+struct staple_host_adamw {
+  static constexpr int kChunks = 8;
+  // workgroups of one refresh launch: the rows come over PCIe, so a few
+  // dozen workgroups keep enough reads in flight
+  static constexpr unsigned kRefreshWorkgroups = 64;
+  int device = 0;
+  int64_t max_rows = 0, d_ff = 0;
+  float* grad_host = nullptr;      // pinned [max_rows x d_ff]
+  int32_t* meta_host = nullptr;    // pinned [1 + max_rows]: the row count, then the row IDs
+  hipEvent_t ev_rows = nullptr, ev_meta = nullptr, ev_done = nullptr;
+  hipEvent_t ev_chunk[kChunks] = {};
+  hipStream_t refresh = nullptr;   // the cache refreshes, beside the copies
+  std::thread worker;
+  std::mutex mu;
+  std::condition_variable cv;
+  bool job = false, busy = false, quit = false;
+  staple_status_t result = STAPLE_OK;
+  // the current job
+  void* table = nullptr;
+  float* m = nullptr;
+  float* v = nullptr;
+  int64_t vocab = 0;
+  int dtype = STAPLE_BF16;
+  const float* grad_dev = nullptr;
+  const int32_t* uniq_dev = nullptr;
+  const int32_t* n_unique_dev = nullptr;
+  const int32_t* code = nullptr;   // NULL: no cache refresh
+  void* cache_rows = nullptr;
+  int64_t capacity = 0;
+  int* err = nullptr;
+  hipStream_t copy = nullptr;
+  staple::AdamWConsts c{};
+  int n_threads = 0;
+
+  staple_status_t run_job() {
+    if (hipSetDevice(device) != hipSuccess) return STAPLE_ERR_HIP;
+    if (hipEventSynchronize(ev_meta) != hipSuccess) return STAPLE_ERR_HIP;
+    const int64_t n = meta_host[0];
+    if (n < 0 || n > max_rows) return STAPLE_ERR_INDEX_RANGE;
+    if (n == 0) return hipEventRecord(ev_done, refresh) == hipSuccess ? STAPLE_OK : STAPLE_ERR_HIP;
+    const int32_t* ids = meta_host + 1;
+    for (int64_t k = 0; k < n; ++k)
+      if (ids[k] < 0 || ids[k] >= vocab) return STAPLE_ERR_HOST;
+    const int parts = static_cast<int>(std::min<int64_t>(kChunks, n));
+    for (int p = 0; p < parts; ++p) {
+      const int64_t lo = n * p / parts, hi = n * (p + 1) / parts;
+      const size_t bytes = static_cast<size_t>(hi - lo) * d_ff * sizeof(float);
+      if (hipMemcpyAsync(grad_host + lo * d_ff, grad_dev + lo * d_ff, bytes, hipMemcpyDeviceToHost,
+                         copy) != hipSuccess ||
+          hipEventRecord(ev_chunk[p], copy) != hipSuccess)
+        return STAPLE_ERR_HIP;
+    }
+    for (int p = 0; p < parts; ++p) {
+      const int64_t lo = n * p / parts, hi = n * (p + 1) / parts;
+      if (hipEventSynchronize(ev_chunk[p]) != hipSuccess) return STAPLE_ERR_HIP;
+      staple::host_adamw_rows(table, dtype, m, v, d_ff, ids + lo, hi - lo, grad_host + lo * d_ff, c,
+                              n_threads);
+      // the cached copies of this chunk's rows, read from the updated host
+      // table while the next chunk is updated (*n_unique >= hi, so the
+      // launch's row count is hi - lo)
+      if (code && capacity > 0 &&
+          staple::launch_cache_refresh(table, vocab, uniq_dev + lo, code + lo, n_unique_dev, hi - lo,
+                                       d_ff * (dtype == STAPLE_BF16 ? 2 : 4), cache_rows, capacity,
+                                       refresh, err, kRefreshWorkgroups) != hipSuccess)
+        return STAPLE_ERR_HIP;
+    }
+    return hipEventRecord(ev_done, refresh) == hipSuccess ? STAPLE_OK : STAPLE_ERR_HIP;
+  }
+
+  void loop() {
+    std::unique_lock<std::mutex> lk(mu);
+    for (;;) {
+      cv.wait(lk, [&] { return job || quit; });
+      if (quit) return;
+      job = false;
+      lk.unlock();
+      const staple_status_t r = run_job();
+      lk.lock();
+      result = r;
+      busy = false;
+      cv.notify_all();
+    }
+  }
+};
+
+using namespace staple;
+
+extern "C" {
+
+staple_status_t staple_host_adamw_create(int64_t max_rows, int64_t d_ff, staple_host_adamw_t** out) {
+  if (!out || max_rows < 1 || max_rows > 0x7fffffffll || d_ff <= 0) return STAPLE_ERR_INVALID_ARGUMENT;
+  *out = nullptr;
+  staple_host_adamw_t* h = new (std::nothrow) staple_host_adamw_t();
+  if (!h) return STAPLE_ERR_HOST;
+  h->max_rows = max_rows;
+  h->d_ff = d_ff;
+  bool ok = hipGetDevice(&h->device) == hipSuccess &&
+            hipHostMalloc(reinterpret_cast<void**>(&h->grad_host),
+                          static_cast<size_t>(max_rows) * d_ff * sizeof(float), hipHostMallocDefault) == hipSuccess &&
+            hipHostMalloc(reinterpret_cast<void**>(&h->meta_host),
+                          static_cast<size_t>(max_rows + 1) * sizeof(int32_t), hipHostMallocDefault) == hipSuccess &&
+            hipEventCreateWithFlags(&h->ev_rows, hipEventDisableTiming) == hipSuccess &&
+            hipEventCreateWithFlags(&h->ev_meta, hipEventDisableTiming) == hipSuccess &&
+            hipEventCreateWithFlags(&h->ev_done, hipEventDisableTiming) == hipSuccess &&
+            hipStreamCreateWithFlags(&h->refresh, hipStreamNonBlocking) == hipSuccess;
+  for (int p = 0; ok && p < staple_host_adamw_t::kChunks; ++p)
+    ok = hipEventCreateWithFlags(&h->ev_chunk[p], hipEventDisableTiming) == hipSuccess;
+  if (ok) {
+    try {
+      h->worker = std::thread(&staple_host_adamw_t::loop, h);
+    } catch (...) {
+      ok = false;
+    }
+  }
+  if (!ok) {
+    staple_host_adamw_destroy(h);
+    return STAPLE_ERR_HIP;
+  }
+  *out = h;
+  return STAPLE_OK;
+}
+
+void* staple_host_adamw_event(staple_host_adamw_t* h) { return h ? h->ev_rows : nullptr; }
+
+staple_status_t staple_host_adamw_start(staple_host_adamw_t* h, void* table, float* m, float* v,
+                                        int64_t vocab, int32_t dtype, const int32_t* uniq,
+                                        const int32_t* n_unique, const float* grad, float lr,
+                                        float beta1, float beta2, float eps, float weight_decay,
+                                        int64_t step, int32_t n_threads, const int32_t* code,
+                                        void* cache_rows, int64_t capacity, void* copy_stream) {
+  if (!h || !table || !m || !v || !uniq || !n_unique || !grad || vocab < 1 || capacity < 0 ||
+      (dtype != STAPLE_BF16 && dtype != STAPLE_F32))
+    return STAPLE_ERR_INVALID_ARGUMENT;
+  const int64_t row_bytes = h->d_ff * (dtype == STAPLE_BF16 ? 2 : 4);
+  int* err = nullptr;
+  if (code && capacity > 0) {
+    // the refresh kernels read the host table: it must be pinned
+    hipPointerAttribute_t attr{};
+    if (!cache_rows || row_bytes % 16 != 0 || reinterpret_cast<uintptr_t>(table) % 16 != 0 ||
+        reinterpret_cast<uintptr_t>(cache_rows) % 16 != 0)
+      return STAPLE_ERR_INVALID_ARGUMENT;
+    if (hipPointerGetAttributes(&attr, table) != hipSuccess) {
+      (void)hipGetLastError();
+      return STAPLE_ERR_INVALID_ARGUMENT;
+    }
+    if (attr.type != hipMemoryTypeHost) return STAPLE_ERR_INVALID_ARGUMENT;
+    err = device_error_word();
+    if (!err) return STAPLE_ERR_HIP;
+  }
+  if (!(step >= 1 && std::isfinite(lr) && lr >= 0.0f && beta1 >= 0.0f && beta1 < 1.0f &&
+        beta2 >= 0.0f && beta2 < 1.0f && std::isfinite(eps) && eps >= 0.0f &&
+        std::isfinite(weight_decay) && weight_decay >= 0.0f))
+    return STAPLE_ERR_INVALID_ARGUMENT;
+  std::unique_lock<std::mutex> lk(h->mu);
+  if (h->busy) return STAPLE_ERR_INVALID_ARGUMENT;   // the previous update was not finished
+  hipStream_t cs = static_cast<hipStream_t>(copy_stream);
+  if (hipStreamWaitEvent(cs, h->ev_rows, 0) != hipSuccess ||
+      hipStreamWaitEvent(h->refresh, h->ev_rows, 0) != hipSuccess ||
+      hipMemcpyAsync(h->meta_host, n_unique, sizeof(int32_t), hipMemcpyDeviceToHost, cs) != hipSuccess ||
+      hipMemcpyAsync(h->meta_host + 1, uniq, static_cast<size_t>(h->max_rows) * sizeof(int32_t),
+                     hipMemcpyDeviceToHost, cs) != hipSuccess ||
+      hipEventRecord(h->ev_meta, cs) != hipSuccess)
+    return STAPLE_ERR_HIP;
+  h->table = table;
+  h->m = m;
+  h->v = v;
+  h->vocab = vocab;
+  h->dtype = dtype;
+  h->grad_dev = grad;
+  h->uniq_dev = uniq;
+  h->n_unique_dev = n_unique;
+  h->code = capacity > 0 ? code : nullptr;
+  h->cache_rows = cache_rows;
+  h->capacity = capacity;
+  h->err = err;
+  h->copy = cs;
+  h->c = adamw_consts(lr, beta1, beta2, eps, weight_decay, step);
+  const int hw = static_cast<int>(std::max(1u, std::thread::hardware_concurrency()));
+  h->n_threads = n_threads > 0 ? n_threads : std::min(hw, 16);
+  h->result = STAPLE_OK;
+  h->busy = true;
+  h->job = true;
+  h->cv.notify_all();
+  return STAPLE_OK;
+}
+
+staple_status_t staple_host_adamw_finish(staple_host_adamw_t* h, void* stream) {
+  if (!h) return STAPLE_ERR_INVALID_ARGUMENT;
+  std::unique_lock<std::mutex> lk(h->mu);
+  h->cv.wait(lk, [&] { return !h->busy; });
+  if (h->result == STAPLE_OK &&
+      hipStreamWaitEvent(static_cast<hipStream_t>(stream), h->ev_done, 0) != hipSuccess)
+    return STAPLE_ERR_HIP;
+  return h->result;
+}
+
+void staple_host_adamw_destroy(staple_host_adamw_t* h) {
+  if (!h) return;
+  if (h->worker.joinable()) {
+    {
+      std::unique_lock<std::mutex> lk(h->mu);
+      h->cv.wait(lk, [&] { return !h->busy; });
+      h->quit = true;
+      h->cv.notify_all();
+    }
+    h->worker.join();
+  }
+  for (int p = 0; p < staple_host_adamw_t::kChunks; ++p)
+    if (h->ev_chunk[p]) (void)hipEventDestroy(h->ev_chunk[p]);
+  if (h->ev_meta) (void)hipEventDestroy(h->ev_meta);
+  if (h->ev_done) (void)hipEventDestroy(h->ev_done);
+  if (h->refresh) (void)hipStreamDestroy(h->refresh);
+  if (h->ev_rows) (void)hipEventDestroy(h->ev_rows);
+  if (h->meta_host) (void)hipHostFree(h->meta_host);
+  if (h->grad_host) (void)hipHostFree(h->grad_host);
+  delete h;
+}
+
+}  // extern "C"
