@@ -47,16 +47,22 @@ def test_status_strings(lib):
 
 
 def test_workspace_queries(lib):
+    # radix sort: two buffers of 8-byte (key, value) pairs, digit histograms
+    # (256 bins x 64 workgroups) and 64 per-workgroup run counts; up to 4096
+    # positions the whole dedup runs in one workgroup's LDS
+    pairs = lambda n: (n * 8 + 255) // 256 * 256
+    radix = lambda n: 2 * pairs(n) + 256 * 64 * 4 + 64 * 4
     assert lib.staple_dedup_workspace_bytes(64) == 0
-    assert lib.staple_dedup_workspace_bytes(32768) == 32768 * 8
-    assert lib.staple_dedup_workspace_bytes(4097) == 8192 * 8
+    assert lib.staple_dedup_workspace_bytes(4096) == 0
+    assert lib.staple_dedup_workspace_bytes(32768) == radix(32768)
+    assert lib.staple_dedup_workspace_bytes(4097) == radix(4097)
     dgu = ((100 * 256 * 2 + 255) // 256) * 256          # [dg | du] in bf16
     aux = ((100 * 128 * 4 + 255) // 256) * 256           # fp32 du, then a recomputed h
     partials = 2 * ((100 + 31) // 32) * 128 * 4            # segment-sum chunk partials
     assert lib.staple_ffn_bwd_workspace_bytes(100, 64, 128, 1) == dgu + aux + partials
     assert lib.staple_ffn_bwd_workspace_bytes(100, 64, 128, 0) == 2 * dgu + aux + partials
     assert lib.staple_ffn_fwd_workspace_bytes(100, 64, 100, 1) == 0   # d_ff not a multiple of 64
-    assert lib.staple_cache_build_workspace_bytes(100352) == 131072 * 8
+    assert lib.staple_cache_build_workspace_bytes(100352) == radix(100352)
     # decode forward: [h][split-K partials, 8 splits of n x d_model fp32]
     h = 64 * 8192 * 2
     down = 8 * 64 * 2048 * 4

@@ -56,6 +56,15 @@ DEDUP_CASES = [
     ("train32k", 32768, 100352, None),
     ("all_equal", 5000, 100352, "equal"),
     ("all_distinct", 6000, 100352, "distinct"),
+    # radix-sort paths: one-wave (1-bit passes), one workgroup (LDS), and the
+    # multi-workgroup passes with several 4096-pair steps per workgroup
+    ("wave_ragged", 37, 100352, None),
+    ("small_65", 65, 100352, None),
+    ("vocab1", 700, 1, "zero"),
+    ("wave_31bit", 64, 2**31 - 1, "wide"),
+    ("group_31bit", 3000, 2**31 - 1, "wide"),
+    ("multi_31bit", 20000, 2**31 - 1, "wide"),
+    ("multi_step", 300_000, 100352, None),
 ]
 
 
@@ -65,6 +74,12 @@ def test_dedup_bit_exact(st, dev, name, n, vocab, kind):
     _log(f"dedup case {name} n={n} vocab={vocab}")
     if kind == "equal":
         ids = np.full(n, 77, dtype=np.int32)
+    elif kind == "zero":
+        ids = np.zeros(n, dtype=np.int32)
+    elif kind == "wide":   # IDs over 31 bits, a third of them repeated
+        rng = np.random.default_rng(n)
+        base = rng.integers(0, vocab, n, dtype=np.int64).astype(np.int32)
+        ids = np.where(rng.random(n) < 0.33, base[rng.integers(0, max(n // 8, 1), n)], base)
     elif kind == "distinct":
         ids = np.random.default_rng(3).permutation(vocab)[:n].astype(np.int32)
     else:
@@ -91,7 +106,8 @@ def test_dedup_flags_out_of_range_ids(st, dev):
 
 # ---------------------------------------------------------------- cache
 @pytest.mark.parametrize("vocab,capacity,n_cal", [(4096, 205, 50_000), (100352, 5018, 1 << 20),
-                                                  (1000, 0, 5000), (1000, 1000, 5000)])
+                                                  (1000, 0, 5000), (1000, 1000, 5000),
+                                                  (300_000, 15000, 1 << 20), (1, 1, 10)])
 def test_cache_count_build_lookup_bit_exact(st, dev, vocab, capacity, n_cal):
     import torch
     _log(f"cache vocab={vocab} capacity={capacity}")
