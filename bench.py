@@ -1102,6 +1102,11 @@ def copy_probe(torch):
                       "copy_bytes_written_per_launch": b.numel() * 2}))
 
 
+def _progress(msg: str) -> None:
+    """One line per finished workload on stderr (the JSON line goes to stdout)."""
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
 def main(argv=None) -> int:
     args = parse_args(argv)
     if args.gpus != 1:
@@ -1138,6 +1143,7 @@ def main(argv=None) -> int:
             out["cpu_baseline"] = decode_cpu_baseline(torch, w, D, args.cpu_seconds)
         del D
         torch.cuda.empty_cache()
+        _progress(f"decode: {out['value']:.0f} tokens/s")
     if "train" in wl:
         wt = S.OLMO1B_TRAIN
         tr, T = run_train(torch, st, wt, args.train_steps, args.train_warmup)
@@ -1151,38 +1157,46 @@ def main(argv=None) -> int:
             out["config"] = {"workload": wt.name}
         del T
         torch.cuda.empty_cache()
+        _progress(f"train: {tr['tokens_per_s']:.0f} tokens/s")
     if "decode7b" in wl:
         w7 = S.OLMO7B_DECODE
         dec7, D7 = run_decode(torch, st, w7, max(20, args.steps // 2), args.warmup)
         out["decode_7b"] = dict(dec7, workload=w7.name)
         del D7
         torch.cuda.empty_cache()
+        _progress(f"decode7b: {dec7['tokens_per_s']:.0f} tokens/s")
     if "train7b" in wl:
         w7 = S.OLMO7B_TRAIN
         tr7, T7 = run_train(torch, st, w7, args.train_steps, args.train_warmup)
         out["train_7b"] = tr7
         del T7
         torch.cuda.empty_cache()
+        _progress(f"train7b: {tr7['tokens_per_s']:.0f} tokens/s")
     if "stem" in wl:
         # the STEM layer STAPLE is compared against (no up-projection), same workloads
         dec_s, D_s = run_decode(torch, st, w, args.steps, args.warmup, stem=True)
         out["decode_stem"] = dict(dec_s, workload=w.name + "_stem")
         del D_s
         torch.cuda.empty_cache()
+        _progress(f"decode stem: {dec_s['tokens_per_s']:.0f} tokens/s")
         tr_s, T_s = run_train(torch, st, S.OLMO1B_TRAIN, args.train_steps, args.train_warmup,
                               stem=True)
         out["train_stem"] = dict(tr_s, workload=S.OLMO1B_TRAIN.name + "_stem")
         del T_s
         torch.cuda.empty_cache()
+        _progress(f"train stem: {tr_s['tokens_per_s']:.0f} tokens/s")
     if "lowrank" in wl:
         out["train_lowrank"] = run_train_lowrank(torch, st, S.OLMO1B_TRAIN, 512, args.train_steps,
                                                  args.train_warmup)
+        _progress(f"lowrank: {out['train_lowrank']['tokens_per_s']:.0f} tokens/s")
     if "offload" in wl:
         out["offload_decode"] = run_offload_decode(torch, st, S.OLMO1B_OFFLOAD, 20, 3)
         torch.cuda.empty_cache()
+        _progress(f"offload decode: {out['offload_decode']['tokens_per_s']:.0f} tokens/s")
         out["offload_train"] = run_offload_train(torch, st, S.OLMO1B_OFFLOAD_TRAIN,
                                                  args.train_steps, args.train_warmup)
         torch.cuda.empty_cache()
+        _progress(f"offload train: {out['offload_train']['tokens_per_s']:.0f} tokens/s")
     print(json.dumps(out), flush=True)
     return 0
 

@@ -59,7 +59,9 @@ def test_workspace_queries(lib):
     dgu = ((100 * 256 * 2 + 255) // 256) * 256          # [dg | du] in bf16
     aux = ((100 * 128 * 4 + 255) // 256) * 256           # fp32 du, then a recomputed h
     partials = 2 * ((100 + 31) // 32) * 128 * 4            # segment-sum chunk partials
-    assert lib.staple_ffn_bwd_workspace_bytes(100, 64, 128, 1) == dgu + aux + partials
+    # bf16: K-major copies W_down^T [f x d], [W_gate^T | W_up^T] [d x 2f], dy^T [d x 128]
+    kt = 128 * 64 * 2 + 64 * 256 * 2 + 64 * 128 * 2
+    assert lib.staple_ffn_bwd_workspace_bytes(100, 64, 128, 1) == dgu + aux + partials + kt
     assert lib.staple_ffn_bwd_workspace_bytes(100, 64, 128, 0) == 2 * dgu + aux + partials
     assert lib.staple_ffn_fwd_workspace_bytes(100, 64, 100, 1) == 0   # d_ff not a multiple of 64
     assert lib.staple_cache_build_workspace_bytes(100352) == radix(100352)

@@ -91,6 +91,14 @@ hipError_t dwdown_bwd(int64_t n, int64_t d, int64_t f, const void* dy, const voi
 template <typename T>
 hipError_t dwgu_bwd(int64_t n, int64_t d, int64_t f, const void* dgu, const void* x, float* dwg,
                     float* dwu, bool freeze_up, hipStream_t s);
+hipError_t transpose_bf16(const void* src, int64_t rows, int64_t cols, int64_t ld_src, void* dst,
+                          int64_t dst_cols, int64_t ld_dst, hipStream_t s);
+hipError_t dh_act_kt(int64_t n, int64_t d, int64_t f, const void* dy, const void* wd_t,
+                     const void* g, const void* u, void* dgu, float* du32, hipStream_t s);
+hipError_t dx_bwd_kt(int64_t n, int64_t d, int64_t k, const void* dgu, int64_t ld_dgu,
+                     const void* w_t, void* dx, int out_dtype, hipStream_t s);
+hipError_t dwdown_bwd_kt(int64_t n, int64_t d, int64_t f, const void* dy_t, int64_t ld_t,
+                         const void* h, float* dwd, hipStream_t s);
 
 // kernels (decode.hip)
 bool decode_eligible(int64_t n, int64_t d, int64_t f, int dtype);
@@ -888,11 +896,19 @@ static size_t bwd_dgu_bytes(int64_t n, int64_t f, int32_t dtype) {
 static size_t bwd_aux_bytes(int64_t n, int64_t f) {
   return align_up(static_cast<size_t>(n) * f * sizeof(float), 256);
 }
+// bf16: the K-major copies W_down^T [f x d], [W_gate^T | W_up^T] [d x 2f] and
+// dy^T [d x n64] (n64 = n rounded up to whole 64-token k stages, zero-padded)
+static int64_t round64(int64_t v) { return (v + 63) / 64 * 64; }
+static size_t bwd_kt_bytes(int64_t n, int64_t d, int64_t f, int32_t dtype) {
+  if (dtype != STAPLE_BF16 || n == 0) return 0;
+  return align_up(static_cast<size_t>(f) * d * 2, 256) + align_up(static_cast<size_t>(d) * 2 * f * 2, 256) +
+         align_up(static_cast<size_t>(d) * round64(n) * 2, 256);
+}
 
 size_t staple_ffn_bwd_workspace_bytes(int64_t n, int64_t d, int64_t f, int32_t dtype) {
   if (!ffn_shape_ok(n, d, f, dtype)) return 0;
   return bwd_dgu_bytes(n, f, dtype) + bwd_aux_bytes(n, f) +
-         align_up(segment_sum_workspace_bytes(n, f), 256);
+         align_up(segment_sum_workspace_bytes(n, f), 256) + bwd_kt_bytes(n, d, f, dtype);
 }
 
 }  // extern "C"
@@ -908,12 +924,28 @@ static staple_status_t bwd_impl(int64_t n, int64_t d, int64_t f, int32_t dtype, 
                                 hipEvent_t rows_event, hipStream_t s, int* err) {
   void* dgu = ws;
   char* aux = n > 0 ? static_cast<char*>(ws) + bwd_dgu_bytes(n, f, dtype) : nullptr;
-  void* seg_ws = n > 0 ? aux + bwd_aux_bytes(n, f) : nullptr;
+  char* seg_ws = n > 0 ? aux + bwd_aux_bytes(n, f) : nullptr;
   // bf16: du also goes to the fp32 region unrounded, and the segment sum adds
   // those values; fp32: the du half of [dg | du] is already fp32
   const bool bf = dtype == STAPLE_BF16;
   float* du32 = bf ? reinterpret_cast<float*>(aux) : nullptr;
-  HIPCALL(dh_act<T>(n, d, f, dy, w_down, saved_g, saved_u, dgu, du32, s));
+  // bf16: K-major copies of W_down, [W_gate; W_up] and dy, so that dh, dx
+  // and dW_down read every operand K-major (the same products in the same
+  // order: the outputs are the same bits as with the MN-major operands)
+  const bool kt = bf && n > 0;
+  char* wd_t = kt ? seg_ws + align_up(segment_sum_workspace_bytes(n, f), 256) : nullptr;
+  char* w_t = kt ? wd_t + align_up(static_cast<size_t>(f) * d * 2, 256) : nullptr;
+  char* dy_t = kt ? w_t + align_up(static_cast<size_t>(d) * 2 * f * 2, 256) : nullptr;
+  const int64_t k_dx = w_up ? 2 * f : f;    // dx contracts over [dg | du], or dg alone (STEM)
+  if (kt) {
+    HIPCALL(transpose_bf16(w_down, d, f, f, wd_t, d, d, s));
+    HIPCALL(transpose_bf16(w_gate, f, d, d, w_t, f, k_dx, s));
+    if (w_up) HIPCALL(transpose_bf16(w_up, f, d, d, w_t + f * 2, f, k_dx, s));
+    HIPCALL(transpose_bf16(dy, n, d, d, dy_t, round64(n), round64(n), s));
+    HIPCALL(dh_act_kt(n, d, f, dy, wd_t, saved_g, saved_u, dgu, du32, s));
+  } else {
+    HIPCALL(dh_act<T>(n, d, f, dy, w_down, saved_g, saved_u, dgu, du32, s));
+  }
   if (n > 0) {
     if (bf)
       HIPCALL(launch_segment_sum(STAPLE_F32, du32, f, 0, n, f, sorted_pos, inv, seg_start, n_unique,
@@ -930,9 +962,11 @@ static staple_status_t bwd_impl(int64_t n, int64_t d, int64_t f, int32_t dtype, 
     HIPCALL(recompute_h<T>(n, f, saved_g, saved_u, aux, s));
     h = aux;
   }
-  HIPCALL(dwdown_bwd<T>(n, d, f, dy, h, dw_down, s));
+  if (kt) HIPCALL(dwdown_bwd_kt(n, d, f, dy_t, round64(n), h, dw_down, s));
+  else HIPCALL(dwdown_bwd<T>(n, d, f, dy, h, dw_down, s));
   HIPCALL(dwgu_bwd<T>(n, d, f, dgu, x, dw_gate, dw_up, fz, s));
-  HIPCALL(dx_bwd<T>(n, d, f, dgu, w_gate, w_up, dx, out_dtype, s));
+  if (kt) HIPCALL(dx_bwd_kt(n, d, k_dx, dgu, 2 * f, w_t, dx, out_dtype, s));
+  else HIPCALL(dx_bwd<T>(n, d, f, dgu, w_gate, w_up, dx, out_dtype, s));
   return STAPLE_OK;
 }
 

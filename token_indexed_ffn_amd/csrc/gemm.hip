@@ -1119,6 +1119,101 @@ hipError_t dwgu_bwd(int64_t n, int64_t d, int64_t f, const void* dgu, const void
   return run<T, false, false, kEpiStore, float>(a, s);
 }
 
+// ---------------------------------------------------------------------------
+// K-major copies for the backward (bf16).  The GEMM reads a K-major operand
+// with one 16-byte LDS read per fragment and an MN-major one with two
+// transposing reads; at the 1B training shapes the K-major form of dx, dh and
+// dW_down is 7-20% faster than the MN-major one, for a copy that costs a few
+// percent of that GEMM.
+// ---------------------------------------------------------------------------
+// dst[c * ld_dst + r] = src[r * ld_src + c] for r < rows, c < cols, through a
+// 64 x 64 tile in LDS (16-byte loads along src rows, 16-byte stores along dst
+// rows); dst entries r in [rows, dst_cols) are zeros, so a K-major operand
+// can be padded to whole 64-element k stages.  cols, dst_cols, ld_src and
+// ld_dst are multiples of 8.
+constexpr int kTrTile = 64;
+__global__ __launch_bounds__(256) void transpose_bf16_kernel(const uint16_t* __restrict__ src,
+                                                             int64_t rows, int64_t cols,
+                                                             int64_t ld_src,
+                                                             uint16_t* __restrict__ dst,
+                                                             int64_t dst_cols, int64_t ld_dst) {
+  __shared__ uint16_t t[kTrTile][kTrTile + 2];
+  const int64_t c0 = static_cast<int64_t>(blockIdx.x) * kTrTile;
+  const int64_t r0 = static_cast<int64_t>(blockIdx.y) * kTrTile;
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int rr = static_cast<int>(threadIdx.x) / 8 + 32 * i, vc = (threadIdx.x % 8) * 8;
+    const int64_t r = r0 + rr, c = c0 + vc;
+    uint4 v = make_uint4(0, 0, 0, 0);
+    if (r < rows && c < cols) v = *reinterpret_cast<const uint4*>(src + r * ld_src + c);
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      t[rr][vc + 2 * j] = static_cast<uint16_t>(w[j] & 0xffffu);
+      t[rr][vc + 2 * j + 1] = static_cast<uint16_t>(w[j] >> 16);
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int cc = static_cast<int>(threadIdx.x) / 8 + 32 * i, vr = (threadIdx.x % 8) * 8;
+    const int64_t c = c0 + cc, r = r0 + vr;
+    if (c >= cols || r >= dst_cols) continue;
+    uint32_t w[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      w[j] = static_cast<uint32_t>(t[vr + 2 * j][cc]) | (static_cast<uint32_t>(t[vr + 2 * j + 1][cc]) << 16);
+    *reinterpret_cast<uint4*>(dst + c * ld_dst + r) = make_uint4(w[0], w[1], w[2], w[3]);
+  }
+}
+
+hipError_t transpose_bf16(const void* src, int64_t rows, int64_t cols, int64_t ld_src, void* dst,
+                          int64_t dst_cols, int64_t ld_dst, hipStream_t s) {
+  if (rows <= 0 || cols <= 0 || dst_cols <= 0) return hipSuccess;
+  if (cols % 8 || dst_cols % 8 || ld_src % 8 || ld_dst % 8 || dst_cols < rows || ld_dst < dst_cols)
+    return hipErrorInvalidValue;
+  const dim3 grid(static_cast<unsigned>((cols + kTrTile - 1) / kTrTile),
+                  static_cast<unsigned>((dst_cols + kTrTile - 1) / kTrTile));
+  transpose_bf16_kernel<<<grid, dim3(256), 0, s>>>(static_cast<const uint16_t*>(src), rows, cols,
+                                                   ld_src, static_cast<uint16_t*>(dst), dst_cols,
+                                                   ld_dst);
+  return hipGetLastError();
+}
+
+// dh with B = W_down^T [f x d] K-major (wd_t: B(k, n) = wd_t[n d + k])
+hipError_t dh_act_kt(int64_t n, int64_t d, int64_t f, const void* dy, const void* wd_t,
+                     const void* g, const void* u, void* dgu, float* du32, hipStream_t s) {
+  GemmArgs a = blank<bf16_t>();
+  a.M = n; a.N = f; a.K = d;
+  a.a0 = dy; a.lda = d;
+  a.b0 = wd_t; a.ldb = d;
+  a.g_in = g; a.u_in = u; a.dgu_out = dgu; a.du32_out = du32;
+  return run<bf16_t, true, true, kEpiDhAct, bf16_t>(a, s);
+}
+
+// dx with B = [W_gate^T | W_up^T] [d x k] K-major (k = 2f, or f for the STEM layer)
+hipError_t dx_bwd_kt(int64_t n, int64_t d, int64_t k, const void* dgu, int64_t ld_dgu,
+                     const void* w_t, void* dx, int out_dtype, hipStream_t s) {
+  GemmArgs a = blank<bf16_t>();
+  a.M = n; a.N = d; a.K = k;
+  a.a0 = dgu; a.lda = ld_dgu;
+  a.b0 = w_t; a.ldb = k;
+  a.c0 = dx; a.ldc = d;
+  if (out_dtype == STAPLE_F32) return run<bf16_t, true, true, kEpiStore, float>(a, s);
+  return run<bf16_t, true, true, kEpiStore, bf16_t>(a, s);
+}
+
+// dW_down with A = dy^T [d x ld_t] K-major (zero past the n tokens)
+hipError_t dwdown_bwd_kt(int64_t n, int64_t d, int64_t f, const void* dy_t, int64_t ld_t,
+                         const void* h, float* dwd, hipStream_t s) {
+  GemmArgs a = blank<bf16_t>();
+  a.M = d; a.N = f; a.K = n;
+  a.a0 = dy_t; a.lda = ld_t;
+  a.b0 = h; a.ldb = f;
+  a.c0 = dwd; a.ldc = f;
+  return run<bf16_t, true, false, kEpiStore, float>(a, s);
+}
+
 // h = silu(g) * u from the saved g and u, for a backward whose caller kept no
 // h: n * f elements (a multiple of 8), 16-byte vectors, grid-stride.
 template <typename T>
