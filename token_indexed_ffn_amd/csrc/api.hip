@@ -99,6 +99,8 @@ hipError_t dx_bwd_kt(int64_t n, int64_t d, int64_t k, const void* dgu, int64_t l
                      const void* w_t, void* dx, int out_dtype, hipStream_t s);
 hipError_t dwdown_bwd_kt(int64_t n, int64_t d, int64_t f, const void* dy_t, int64_t ld_t,
                          const void* h, float* dwd, hipStream_t s);
+hipError_t dwgu_bwd_kt(int64_t n, int64_t d, int64_t f, const void* x_t, int64_t ld_t,
+                       const void* dgu, float* dwg, float* dwu, bool freeze_up, hipStream_t s);
 
 // kernels (decode.hip)
 bool decode_eligible(int64_t n, int64_t d, int64_t f, int dtype);
@@ -929,9 +931,10 @@ static staple_status_t bwd_impl(int64_t n, int64_t d, int64_t f, int32_t dtype, 
   // those values; fp32: the du half of [dg | du] is already fp32
   const bool bf = dtype == STAPLE_BF16;
   float* du32 = bf ? reinterpret_cast<float*>(aux) : nullptr;
-  // bf16: K-major copies of W_down, [W_gate; W_up] and dy, so that dh, dx
-  // and dW_down read every operand K-major (the same products in the same
-  // order: the outputs are the same bits as with the MN-major operands)
+  // bf16: K-major copies of W_down, [W_gate; W_up], dy and x, so that dh and
+  // dx read both operands K-major and the weight gradients one (the same
+  // products in the same order: the outputs are the same bits as with
+  // MN-major operands)
   const bool kt = bf && n > 0;
   char* wd_t = kt ? seg_ws + align_up(segment_sum_workspace_bytes(n, f), 256) : nullptr;
   char* w_t = kt ? wd_t + align_up(static_cast<size_t>(f) * d * 2, 256) : nullptr;
@@ -962,9 +965,16 @@ static staple_status_t bwd_impl(int64_t n, int64_t d, int64_t f, int32_t dtype, 
     HIPCALL(recompute_h<T>(n, f, saved_g, saved_u, aux, s));
     h = aux;
   }
-  if (kt) HIPCALL(dwdown_bwd_kt(n, d, f, dy_t, round64(n), h, dw_down, s));
-  else HIPCALL(dwdown_bwd<T>(n, d, f, dy, h, dw_down, s));
-  HIPCALL(dwgu_bwd<T>(n, d, f, dgu, x, dw_gate, dw_up, fz, s));
+  if (kt) {
+    HIPCALL(dwdown_bwd_kt(n, d, f, dy_t, round64(n), h, dw_down, s));
+    // x^T into dy^T's buffer (dW_down has read it, in stream order); the
+    // weight gradients come out of x^T [dg | du] transposed
+    HIPCALL(transpose_bf16(x, n, d, d, dy_t, round64(n), round64(n), s));
+    HIPCALL(dwgu_bwd_kt(n, d, f, dy_t, round64(n), dgu, dw_gate, dw_up, fz, s));
+  } else {
+    HIPCALL(dwdown_bwd<T>(n, d, f, dy, h, dw_down, s));
+    HIPCALL(dwgu_bwd<T>(n, d, f, dgu, x, dw_gate, dw_up, fz, s));
+  }
   if (kt) HIPCALL(dx_bwd_kt(n, d, k_dx, dgu, 2 * f, w_t, dx, out_dtype, s));
   else HIPCALL(dx_bwd<T>(n, d, f, dgu, w_gate, w_up, dx, out_dtype, s));
   return STAPLE_OK;

@@ -18,6 +18,8 @@
 // Epilogues stage each wave's accumulators through LDS, 32 rows at a time,
 // so every global access of the epilogue is a 16-byte vector along a row:
 //   Store   - C to fp32 or bf16 (optionally split by rows into two buffers).
+//   StoreT  - C^T: element (m, n) to row n, column m (optionally split by
+//             columns n into two buffers), 8 consecutive m per store.
 //   GateUp  - the B rows interleave W_gate and W_up in 32-row groups, so one
 //             wave holds g and a = W_up x for the same (token, feature); the
 //             epilogue reads the token's table row, forms u = a + E[t] and
@@ -38,7 +40,7 @@
 
 namespace staple {
 
-enum EpiKind { kEpiStore = 0, kEpiGateUp = 1, kEpiDhAct = 2, kEpiGateStem = 3 };
+enum EpiKind { kEpiStore = 0, kEpiGateUp = 1, kEpiDhAct = 2, kEpiGateStem = 3, kEpiStoreT = 4 };
 
 struct GemmArgs {
   int64_t M, N, K;
@@ -61,6 +63,7 @@ struct GemmArgs {
   int64_t ldb;
   int64_t b_split;
   // Store: C(m,n) -> (m < c_split ? c0 + m*ldc : c1 + (m-c_split)*ldc)[n]
+  // StoreT: C(m,n) -> (n < c_split ? c0 + n*ldc : c1 + (n-c_split)*ldc)[m]  (M a multiple of 8)
   void* c0;
   void* c1;
   int64_t ldc;
@@ -885,6 +888,22 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(GemmArgs p) {
           store8g<OutT>(cb, mm * p.ldc + n, v);
         }
       }
+    } else if constexpr (EPI == kEpiStoreT) {
+      // lane q % WN owns column n, 8 rows from (q / WN) 8 per store
+#pragma unroll
+      for (int q = lane; q < WN * 4; q += 64) {
+        const int cc = q % WN, rg = (q / WN) * 8;
+        const int64_t m = mrow0 + rg;
+        const int64_t n = n0 + wn * WN + cc;
+        if (m < p.M && n < p.N) {
+          float v[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) v[e] = region[(rg + e) * LD + cc];
+          void* cb = n < p.c_split ? p.c0 : p.c1;
+          const int64_t nn = n < p.c_split ? n : n - p.c_split;
+          store8g<OutT>(cb, nn * p.ldc + m, v);
+        }
+      }
     } else if constexpr (EPI == kEpiGateUp) {
       // h, g, u from the staged [gate | up] pairs and the prefetched rows
       const int64_t f = p.d_ff;
@@ -1201,6 +1220,19 @@ hipError_t dx_bwd_kt(int64_t n, int64_t d, int64_t k, const void* dgu, int64_t l
   a.c0 = dx; a.ldc = d;
   if (out_dtype == STAPLE_F32) return run<bf16_t, true, true, kEpiStore, float>(a, s);
   return run<bf16_t, true, true, kEpiStore, bf16_t>(a, s);
+}
+
+// [dW_gate; dW_up] with A = x^T [d x ld_t] K-major (zero past the n tokens):
+// C = x^T [dg | du] is [dW_gate; dW_up]^T, stored transposed (M = d, N = 2f,
+// or f when the up-projection is frozen)
+hipError_t dwgu_bwd_kt(int64_t n, int64_t d, int64_t f, const void* x_t, int64_t ld_t,
+                       const void* dgu, float* dwg, float* dwu, bool freeze_up, hipStream_t s) {
+  GemmArgs a = blank<bf16_t>();
+  a.M = d; a.N = freeze_up ? f : 2 * f; a.K = n;
+  a.a0 = x_t; a.lda = ld_t;
+  a.b0 = dgu; a.ldb = 2 * f;
+  a.c0 = dwg; a.c1 = dwu; a.ldc = d; a.c_split = f;
+  return run<bf16_t, true, false, kEpiStoreT, float>(a, s);
 }
 
 // dW_down with A = dy^T [d x ld_t] K-major (zero past the n tokens)
