@@ -614,12 +614,19 @@ def setup_offload(torch, st, w, n_layers):
             "cache_rows": cache_rows}
 
 
-def _miss_list_to_host(torch, lk, host_buf):
-    """Copies n_miss and the miss IDs to pinned host memory (one sync)."""
+def _miss_list_to_host(torch, lk, host_buf, blocking=False):
+    """Copies n_miss and the miss IDs to pinned host memory (one sync;
+    blocking: the thread sleeps in the wait instead of spinning, leaving its
+    core to host threads that work meanwhile)."""
     n = torch.empty(1, dtype=torch.int32, pin_memory=True)
     n.copy_(lk["n_miss"], non_blocking=True)
     host_buf[: lk["miss_ids"].numel()].copy_(lk["miss_ids"], non_blocking=True)
-    torch.cuda.current_stream().synchronize()
+    if blocking:
+        ev = torch.cuda.Event(blocking=True)
+        ev.record()
+        ev.synchronize()
+    else:
+        torch.cuda.current_stream().synchronize()
     return int(n.item())
 
 
@@ -853,7 +860,7 @@ def run_offload_train(torch, st, w, steps, warmup):
     ev_ready = torch.cuda.Event()
     stats = {"pack_s": 0.0, "copy_ms": 0.0, "hit_tokens": 0, "gu_us": []}
 
-    def step(mode, B=None, before_rows=None, rows_event=None):
+    def step(mode, B=None, before_rows=None, rows_event=None, blocking=False):
         """B: the step's own dedup, probe and row-gradient buffers (default:
         the shared ones); before_rows: called once the miss list is known and
         before anything reads the table's rows (the optimizer's finish)."""
@@ -863,7 +870,7 @@ def run_offload_train(torch, st, w, steps, warmup):
                                     out=lk_out if B is None else B["lk"])
         sp = st.staple_split_tokens(dd["inv"], lk["code"], dd["n_unique"], out=sp_out)
         counts_host.copy_(sp["counts"], non_blocking=True)
-        m = _miss_list_to_host(torch, lk, miss_host)        # one host sync for both
+        m = _miss_list_to_host(torch, lk, miss_host, blocking)   # one host sync for both
         n_hit, n_miss_tok = int(counts_host[0]), int(counts_host[1])
         stats["hit_tokens"] = n_hit
         side.wait_stream(main)
@@ -1016,7 +1023,7 @@ def run_offload_train_optimizer(torch, st, O, T, lk_out, step, mode, steps, warm
 
     def overlapped(k):
         B = sets[k % 2]
-        step(mode, B, before_rows=finish, rows_event=ha.event)
+        step(mode, B, before_rows=finish, rows_event=ha.event, blocking=True)
         t_step[0] += 1
         ha.start(table, m, v, B["dd"]["uniq"], B["dd"]["n_unique"], B["bwd"]["d_rows"],
                  step=t_step[0], copy_stream=copy_s, code=B["lk"]["code"], cache_rows=cache, **hp)

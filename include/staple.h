@@ -573,7 +573,8 @@ staple_status_t staple_cache_refresh(const void* table, int64_t vocab, int64_t d
  *     *n_unique and uniq to the host, then returns; the worker then copies the
  *     gradient rows to the host in chunks on copy_stream and applies the
  *     update of staple_adamw_rows_host (same arguments; table, m, v host
- *     memory) to each chunk as it lands, while the GPU goes on.  grad, uniq,
+ *     memory; n_threads <= 0: up to 14, leaving the caller's thread and the
+ *     runtime a core) to each chunk as it lands, while the GPU goes on.  grad, uniq,
  *     n_unique: device memory (d_rows and staple_dedup's uniq, n_unique),
  *     unchanged until the update finishes; uniq holds at least max_rows
  *     entries (all max_rows are copied) and grad at least *n_unique rows of

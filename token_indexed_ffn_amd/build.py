@@ -57,7 +57,8 @@ def build(jobs: int = 4, verbose: bool = False) -> str:
     with ThreadPoolExecutor(max_workers=max(1, jobs)) as ex:
         objs = list(ex.map(_compile, SOURCES))
     tmp = LIB + ".tmp"
-    cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp] + objs
+    cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp] + objs + \
+        ["-L/opt/rocm/lib", "-lhsa-runtime64"]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"linking libstaple.so failed:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")

@@ -293,6 +293,24 @@ __device__ __forceinline__ P pick4(const P (&a)[kCopyJobLayers], int j) {
   return j == 0 ? a[0] : j == 1 ? a[1] : j == 2 ? a[2] : a[3];
 }
 
+// Source of a token's table row for the gate/up epilogue: row index v =
+// row_index[token]; with `table`, a negative v = -1 - id selects row id of
+// the table (e.g. pinned host memory, read in place) and a non-negative one
+// row v of `rows` (e.g. the HBM cache).  (A free function of plain values:
+// as a lambda over captured variables the compiler selected between the
+// addresses of the two row strides and kept both in scratch memory.)
+__device__ __forceinline__ const uint16_t* decode_row_src(const uint16_t* table, int64_t vocab,
+                                                          int64_t table_ld, const uint16_t* rows,
+                                                          int64_t n_rows, int64_t f, int64_t v,
+                                                          bool& ok) {
+  if (table && v < 0) {
+    ok = -1 - v < vocab;
+    return table + (-1 - v) * table_ld;
+  }
+  ok = v >= 0 && v < n_rows;
+  return rows + v * f;
+}
+
 template <int WD, int A, int G, int KH, bool PACKED, bool UP, bool RW = false, bool CW = false>
 __global__ __launch_bounds__(64 * ((G + 1) * KH + (RW || CW ? 1 : 0))) void decode_gateup_kernel(
     int n, const int32_t* __restrict__ pos, int64_t n_tokens, int64_t d, int64_t f,
@@ -337,17 +355,9 @@ __global__ __launch_bounds__(64 * ((G + 1) * KH + (RW || CW ? 1 : 0))) void deco
     return p < 0 ? 0 : p;
   };
   const int64_t tok = tok_of(min(lane, n - 1));
-  // the epilogue's table row of a token: row index v = row_index[token];
-  // with `table`, a negative v = -1 - id selects row id of the table (e.g.
-  // pinned host memory, read in place) and a non-negative one row v of
-  // `rows` (e.g. the HBM cache)
+  // the epilogue's table row of a token (row index v = row_index[token])
   auto row_of = [&](int64_t v, bool& ok) -> const uint16_t* {
-    if (table && v < 0) {
-      ok = -1 - v < vocab;
-      return table + (-1 - v) * table_ld;
-    }
-    ok = v >= 0 && v < n_rows;
-    return rows + v * f;
+    return decode_row_src(table, vocab, table_ld, rows, n_rows, f, v, ok);
   };
   // Without RW each compute wave fetches its lane's token's row (this wave's
   // features) once the stream is under way.  With RW the row wave loads the

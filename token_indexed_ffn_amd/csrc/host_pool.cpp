@@ -77,17 +77,20 @@ int host_pool_parts(int64_t work_bytes, int cap) {
   return static_cast<int>(std::max<int64_t>(1, std::min<int64_t>(lim, by_work)));
 }
 
-void host_pool_run(int64_t n, int parts, void (*body)(void*, int64_t, int64_t), void* ctx) {
-  parts = std::max(1, std::min(parts, kHostPoolMax));
+void host_pool_run(int64_t n, int threads, void (*body)(void*, int64_t, int64_t), void* ctx) {
+  threads = std::max(1, std::min(threads, kHostPoolMax));
   if (n <= 0) return;
-  if (parts == 1 || n == 1) {
+  if (threads == 1 || n == 1) {
     body(ctx, 0, n);
     return;
   }
+  // several parts per thread, taken in turn: a thread the OS holds back
+  // (other work on the host's cores) delays only the part it is on
+  const int parts = static_cast<int>(std::min<int64_t>(n, static_cast<int64_t>(threads) * kPartsPerThread));
   Pool& P = pool();
   std::lock_guard<std::mutex> run_lk(P.run_mu);
   std::unique_lock<std::mutex> lk(P.mu);
-  P.ensure_workers(parts);
+  P.ensure_workers(threads);
   P.body = body;
   P.ctx = ctx;
   P.n = n;

@@ -9,19 +9,22 @@
 
 namespace staple {
 
-// Runs body(ctx, lo, hi) over [0, n) cut into `parts` contiguous ranges
-// (parts <= kHostPoolMax), the calling thread taking part as well; returns
-// when every range is done.  Calls from several threads take turns.
+// Runs body(ctx, lo, hi) over [0, n) on `threads` threads (at most
+// kHostPoolMax, the calling thread one of them): [0, n) is cut into up to
+// kPartsPerThread contiguous ranges per thread, which the threads take in
+// turn; returns when every range is done.  Calls from several threads take
+// turns.
 constexpr int kHostPoolMax = 16;
-void host_pool_run(int64_t n, int parts, void (*body)(void*, int64_t, int64_t), void* ctx);
+constexpr int kPartsPerThread = 4;
+void host_pool_run(int64_t n, int threads, void (*body)(void*, int64_t, int64_t), void* ctx);
 
 // Threads a host loop of `work` bytes should use: one per 2 MB of work, at
-// most `cap` (<= kHostPoolMax), at least one.
+// most `cap` (<= kHostPoolMax) and the host's hardware threads, at least one.
 int host_pool_parts(int64_t work_bytes, int cap);
 
 template <typename F>
-void host_parallel_for(int64_t n, int parts, F& f) {
-  host_pool_run(n, parts,
+void host_parallel_for(int64_t n, int threads, F& f) {
+  host_pool_run(n, threads,
                 [](void* c, int64_t lo, int64_t hi) { (*static_cast<F*>(c))(lo, hi); }, &f);
 }
 

@@ -314,15 +314,102 @@ hipError_t launch_cache_refresh(const void* table, int64_t vocab, const int32_t*
 // by the same routine as staple_adamw_rows_host, each row once and
 // independently, so the result is the same bits as the serial update.
 // ---------------------------------------------------------------------------
+#include <hsa/hsa.h>
+#include <hsa/hsa_ext_amd.h>
+
 #include <condition_variable>
 #include <mutex>
 #include <new>
 
+namespace {
+
+// Device-to-host copies on the GPU's DMA (SDMA) engines through the HSA
+// runtime.  A hipMemcpyAsync to pinned host memory may be carried out by a
+// copy kernel; while the backward's weight-gradient GEMMs run (a few hundred
+// long workgroups, one per CU at a time) such a kernel's workgroups hold CU
+// slots and the GEMM's last workgroups start late.  The DMA engines use no
+// compute unit.
+struct SdmaCopier {
+  bool ready = false;
+  hsa_agent_t gpu{}, cpu{};
+  static constexpr int kMaxSignals = 16;
+  hsa_signal_t sig[kMaxSignals] = {};
+  int n_sig = 0;
+
+  struct Find {
+    uint32_t bdf = 0;        // bus << 8 | device << 3 of the GPU to find
+    hsa_agent_t gpu{}, cpu{};
+    bool got_gpu = false, got_cpu = false;
+  };
+  static hsa_status_t visit(hsa_agent_t a, void* data) {
+    Find* f = static_cast<Find*>(data);
+    hsa_device_type_t t;
+    if (hsa_agent_get_info(a, HSA_AGENT_INFO_DEVICE, &t) != HSA_STATUS_SUCCESS) return HSA_STATUS_SUCCESS;
+    if (t == HSA_DEVICE_TYPE_CPU && !f->got_cpu) {
+      f->cpu = a;
+      f->got_cpu = true;
+    } else if (t == HSA_DEVICE_TYPE_GPU && !f->got_gpu) {
+      uint32_t bdf = 0;
+      if (hsa_agent_get_info(a, static_cast<hsa_agent_info_t>(HSA_AMD_AGENT_INFO_BDFID), &bdf) ==
+              HSA_STATUS_SUCCESS && (bdf & ~7u) == f->bdf) {
+        f->gpu = a;
+        f->got_gpu = true;
+      }
+    }
+    return HSA_STATUS_SUCCESS;
+  }
+
+  // For HIP device `device`, with `n` completion signals; on any failure the
+  // copier stays unready and the caller copies with hipMemcpyAsync.
+  void init(int device, int n) {
+    if (n > kMaxSignals) return;
+    int bus = -1, dev = -1;
+    if (hipDeviceGetAttribute(&bus, hipDeviceAttributePciBusId, device) != hipSuccess ||
+        hipDeviceGetAttribute(&dev, hipDeviceAttributePciDeviceId, device) != hipSuccess)
+      return;
+    if (hsa_init() != HSA_STATUS_SUCCESS) return;
+    Find f;
+    f.bdf = (static_cast<uint32_t>(bus) << 8) | (static_cast<uint32_t>(dev) << 3);
+    if (hsa_iterate_agents(&SdmaCopier::visit, &f) != HSA_STATUS_SUCCESS || !f.got_gpu || !f.got_cpu) {
+      (void)hsa_shut_down();
+      return;
+    }
+    gpu = f.gpu;
+    cpu = f.cpu;
+    for (n_sig = 0; n_sig < n; ++n_sig)
+      if (hsa_signal_create(0, 0, nullptr, &sig[n_sig]) != HSA_STATUS_SUCCESS) break;
+    ready = n_sig == n;
+    if (!ready) release();
+  }
+  void release() {
+    for (int i = 0; i < n_sig; ++i) (void)hsa_signal_destroy(sig[i]);
+    if (n_sig > 0 || ready) (void)hsa_shut_down();
+    n_sig = 0;
+    ready = false;
+  }
+  // Starts copy i (device src -> pinned host dst).
+  bool start(int i, void* dst, const void* src, size_t bytes) {
+    hsa_signal_store_screlease(sig[i], 1);
+    return hsa_amd_memory_async_copy(dst, cpu, src, gpu, bytes, 0, nullptr, sig[i]) == HSA_STATUS_SUCCESS;
+  }
+  // Waits for copy i; false when the engine reported an error.
+  bool wait(int i) {
+    hsa_signal_value_t v;
+    do {
+      v = hsa_signal_wait_scacquire(sig[i], HSA_SIGNAL_CONDITION_LT, 1, UINT64_MAX, HSA_WAIT_STATE_BLOCKED);
+    } while (v >= 1);
+    return v == 0;
+  }
+};
+
+}  // namespace
+
 struct staple_host_adamw {
   static constexpr int kChunks = 8;
-  // workgroups of one refresh launch: the rows come over PCIe, so a few
-  // dozen workgroups keep enough reads in flight
-  static constexpr unsigned kRefreshWorkgroups = 64;
+  // workgroups of one refresh launch: the rows come over PCIe, and 16
+  // workgroups keep enough reads in flight while leaving nearly every CU to
+  // the backward's GEMMs running beside them
+  static constexpr unsigned kRefreshWorkgroups = 16;
   int device = 0;
   int64_t max_rows = 0, d_ff = 0;
   float* grad_host = nullptr;      // pinned [max_rows x d_ff]
@@ -330,6 +417,7 @@ struct staple_host_adamw {
   hipEvent_t ev_rows = nullptr, ev_meta = nullptr, ev_done = nullptr;
   hipEvent_t ev_chunk[kChunks] = {};
   hipStream_t refresh = nullptr;   // the cache refreshes, beside the copies
+  SdmaCopier sdma;                 // the gradient chunks' copies, when available
   std::thread worker;
   std::mutex mu;
   std::condition_variable cv;
@@ -354,7 +442,19 @@ struct staple_host_adamw {
 
   staple_status_t run_job() {
     if (hipSetDevice(device) != hipSuccess) return STAPLE_ERR_HIP;
-    if (hipEventSynchronize(ev_meta) != hipSuccess) return STAPLE_ERR_HIP;
+    if (sdma.ready) {
+      // the row count and IDs on the DMA engines as soon as the rows are
+      // complete (a copy kernel could wait behind the GEMMs for a CU)
+      if (hipEventSynchronize(ev_rows) != hipSuccess) return STAPLE_ERR_HIP;
+      const bool a = sdma.start(kChunks, meta_host, n_unique_dev, sizeof(int32_t));
+      const bool b = a && sdma.start(kChunks + 1, meta_host + 1, uniq_dev,
+                                     static_cast<size_t>(max_rows) * sizeof(int32_t));
+      const bool wa = a && sdma.wait(kChunks);
+      const bool wb = b && sdma.wait(kChunks + 1);
+      if (!(wa && wb)) return STAPLE_ERR_HIP;
+    } else if (hipEventSynchronize(ev_meta) != hipSuccess) {
+      return STAPLE_ERR_HIP;
+    }
     const int64_t n = meta_host[0];
     if (n < 0 || n > max_rows) return STAPLE_ERR_INDEX_RANGE;
     if (n == 0) return hipEventRecord(ev_done, refresh) == hipSuccess ? STAPLE_OK : STAPLE_ERR_HIP;
@@ -362,17 +462,31 @@ struct staple_host_adamw {
     for (int64_t k = 0; k < n; ++k)
       if (ids[k] < 0 || ids[k] >= vocab) return STAPLE_ERR_HOST;
     const int parts = static_cast<int>(std::min<int64_t>(kChunks, n));
+    // the rows are complete (ev_rows, or ev_meta after it on the copy stream)
     for (int p = 0; p < parts; ++p) {
       const int64_t lo = n * p / parts, hi = n * (p + 1) / parts;
       const size_t bytes = static_cast<size_t>(hi - lo) * d_ff * sizeof(float);
-      if (hipMemcpyAsync(grad_host + lo * d_ff, grad_dev + lo * d_ff, bytes, hipMemcpyDeviceToHost,
-                         copy) != hipSuccess ||
-          hipEventRecord(ev_chunk[p], copy) != hipSuccess)
+      if (sdma.ready) {
+        if (!sdma.start(p, grad_host + lo * d_ff, grad_dev + lo * d_ff, bytes)) {
+          for (int q = 0; q < p; ++q) (void)sdma.wait(q);   // none left writing the staging
+          return STAPLE_ERR_HIP;
+        }
+      } else if (hipMemcpyAsync(grad_host + lo * d_ff, grad_dev + lo * d_ff, bytes,
+                                hipMemcpyDeviceToHost, copy) != hipSuccess ||
+                 hipEventRecord(ev_chunk[p], copy) != hipSuccess) {
+        (void)hipStreamSynchronize(copy);
         return STAPLE_ERR_HIP;
+      }
     }
     for (int p = 0; p < parts; ++p) {
       const int64_t lo = n * p / parts, hi = n * (p + 1) / parts;
-      if (hipEventSynchronize(ev_chunk[p]) != hipSuccess) return STAPLE_ERR_HIP;
+      if (sdma.ready ? !sdma.wait(p) : hipEventSynchronize(ev_chunk[p]) != hipSuccess) {
+        for (int q = p + 1; q < parts; ++q) {
+          if (sdma.ready) (void)sdma.wait(q);
+          else (void)hipEventSynchronize(ev_chunk[q]);
+        }
+        return STAPLE_ERR_HIP;
+      }
       staple::host_adamw_rows(table, dtype, m, v, d_ff, ids + lo, hi - lo, grad_host + lo * d_ff, c,
                               n_threads);
       // the cached copies of this chunk's rows, read from the updated host
@@ -405,6 +519,10 @@ struct staple_host_adamw {
 
 using namespace staple;
 
+// The worker sleeps while it waits for a copy (blocking-sync events) rather
+// than spinning on a core the update's threads could use.
+constexpr unsigned kWaitFlags = hipEventDisableTiming | hipEventBlockingSync;
+
 extern "C" {
 
 staple_status_t staple_host_adamw_create(int64_t max_rows, int64_t d_ff, staple_host_adamw_t** out) {
@@ -419,12 +537,13 @@ staple_status_t staple_host_adamw_create(int64_t max_rows, int64_t d_ff, staple_
                           static_cast<size_t>(max_rows) * d_ff * sizeof(float), hipHostMallocDefault) == hipSuccess &&
             hipHostMalloc(reinterpret_cast<void**>(&h->meta_host),
                           static_cast<size_t>(max_rows + 1) * sizeof(int32_t), hipHostMallocDefault) == hipSuccess &&
-            hipEventCreateWithFlags(&h->ev_rows, hipEventDisableTiming) == hipSuccess &&
-            hipEventCreateWithFlags(&h->ev_meta, hipEventDisableTiming) == hipSuccess &&
+            hipEventCreateWithFlags(&h->ev_rows, kWaitFlags) == hipSuccess &&
+            hipEventCreateWithFlags(&h->ev_meta, kWaitFlags) == hipSuccess &&
             hipEventCreateWithFlags(&h->ev_done, hipEventDisableTiming) == hipSuccess &&
             hipStreamCreateWithFlags(&h->refresh, hipStreamNonBlocking) == hipSuccess;
   for (int p = 0; ok && p < staple_host_adamw_t::kChunks; ++p)
-    ok = hipEventCreateWithFlags(&h->ev_chunk[p], hipEventDisableTiming) == hipSuccess;
+    ok = hipEventCreateWithFlags(&h->ev_chunk[p], kWaitFlags) == hipSuccess;
+  if (ok) h->sdma.init(h->device, staple_host_adamw_t::kChunks + 2);   // chunks, count, IDs
   if (ok) {
     try {
       h->worker = std::thread(&staple_host_adamw_t::loop, h);
@@ -474,12 +593,13 @@ staple_status_t staple_host_adamw_start(staple_host_adamw_t* h, void* table, flo
   std::unique_lock<std::mutex> lk(h->mu);
   if (h->busy) return STAPLE_ERR_INVALID_ARGUMENT;   // the previous update was not finished
   hipStream_t cs = static_cast<hipStream_t>(copy_stream);
-  if (hipStreamWaitEvent(cs, h->ev_rows, 0) != hipSuccess ||
-      hipStreamWaitEvent(h->refresh, h->ev_rows, 0) != hipSuccess ||
-      hipMemcpyAsync(h->meta_host, n_unique, sizeof(int32_t), hipMemcpyDeviceToHost, cs) != hipSuccess ||
-      hipMemcpyAsync(h->meta_host + 1, uniq, static_cast<size_t>(h->max_rows) * sizeof(int32_t),
-                     hipMemcpyDeviceToHost, cs) != hipSuccess ||
-      hipEventRecord(h->ev_meta, cs) != hipSuccess)
+  if (hipStreamWaitEvent(h->refresh, h->ev_rows, 0) != hipSuccess) return STAPLE_ERR_HIP;
+  if (!h->sdma.ready &&
+      (hipStreamWaitEvent(cs, h->ev_rows, 0) != hipSuccess ||
+       hipMemcpyAsync(h->meta_host, n_unique, sizeof(int32_t), hipMemcpyDeviceToHost, cs) != hipSuccess ||
+       hipMemcpyAsync(h->meta_host + 1, uniq, static_cast<size_t>(h->max_rows) * sizeof(int32_t),
+                      hipMemcpyDeviceToHost, cs) != hipSuccess ||
+       hipEventRecord(h->ev_meta, cs) != hipSuccess))
     return STAPLE_ERR_HIP;
   h->table = table;
   h->m = m;
@@ -495,8 +615,10 @@ staple_status_t staple_host_adamw_start(staple_host_adamw_t* h, void* table, flo
   h->err = err;
   h->copy = cs;
   h->c = adamw_consts(lr, beta1, beta2, eps, weight_decay, step);
+  // by default two threads fewer than the pool's maximum: the caller's
+  // thread keeps feeding the GPU meanwhile
   const int hw = static_cast<int>(std::max(1u, std::thread::hardware_concurrency()));
-  h->n_threads = n_threads > 0 ? n_threads : std::min(hw, 16);
+  h->n_threads = n_threads > 0 ? n_threads : std::max(1, std::min(hw, kHostPoolMax) - 2);
   h->result = STAPLE_OK;
   h->busy = true;
   h->job = true;
@@ -527,6 +649,7 @@ void staple_host_adamw_destroy(staple_host_adamw_t* h) {
   }
   for (int p = 0; p < staple_host_adamw_t::kChunks; ++p)
     if (h->ev_chunk[p]) (void)hipEventDestroy(h->ev_chunk[p]);
+  h->sdma.release();
   if (h->ev_meta) (void)hipEventDestroy(h->ev_meta);
   if (h->ev_done) (void)hipEventDestroy(h->ev_done);
   if (h->refresh) (void)hipStreamDestroy(h->refresh);
