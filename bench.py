@@ -734,6 +734,10 @@ def run_offload_decode(torch, st, w, steps, warmup):
         st.staple_decode_step_cached(stack, ids, O["id_to_slot"], w.cache_capacity,
                                      dedup_out=dd_out, lookup_out=lk_out, workspace=step_ws, group=2)
 
+    def step_carried1():
+        st.staple_decode_step_cached(stack, ids, O["id_to_slot"], w.cache_capacity,
+                                     dedup_out=dd_out, lookup_out=lk_out, workspace=step_ws, group=1)
+
     grouped = [st.staple_group_tables_host(O["tables"][g:g + 4]) for g in range(0, L, 4)]
     stack_grouped = st.DecodeStack(
         [{"x": lay["x"], "packed_gate_up": lay["pgu"], "packed_down": lay["pd"],
@@ -776,10 +780,15 @@ def run_offload_decode(torch, st, w, steps, warmup):
     torch.cuda.synchronize()
     if not all(torch.equal(a, lay["y"]) for a, lay in zip(ys, layers)):
         raise RuntimeError("the grouped host tables give other outputs than the per-layer calls")
+    ms_carried1 = timed(step_carried1)
+    torch.cuda.synchronize()
+    if not all(torch.equal(a, lay["y"]) for a, lay in zip(ys, layers)):
+        raise RuntimeError("the carried row copies give other outputs than the per-layer calls")
     ms_staged = timed(step_staged)
     m = _miss_list_to_host(torch, lk_out, miss_host)
     times = {"direct": ms_direct, "staged": ms_staged, "native": ms_native, "native_inplace": ms_inplace,
-             "native_carried": ms_carried, "native_grouped": ms_grouped}
+             "native_carried": ms_carried, "native_carried1": ms_carried1,
+             "native_grouped": ms_grouped}
     method = min(times, key=times.get)
     ms = times[method]
     n_unique = int(dd_out["n_unique"].item())
@@ -819,6 +828,7 @@ def run_offload_decode(torch, st, w, steps, warmup):
                      "pcie_gb_s": m * f * 2 / (asm_us * 1e-6) / 1e9, "pcie_peak_gb_s": 64.0},
             "direct_ms_per_step": ms_direct, "native_ms_per_step": ms_native,
             "native_inplace_ms_per_step": ms_inplace, "native_carried_ms_per_step": ms_carried,
+            "native_carried1_ms_per_step": ms_carried1,
             "native_grouped_ms_per_step": ms_grouped, "staged_ms_per_step": ms_staged,
             "n_unique": n_unique, "misses_per_layer": m, "cache_capacity": w.cache_capacity,
             "pcie_bytes_per_step": m * f * 2 * L,
@@ -831,7 +841,9 @@ def run_offload_decode(torch, st, w, steps, warmup):
                     "(cache slot or pinned host table). native_carried: the same call with groups "
                     "of two layers, the first group's rows assembled first and every later "
                     "group's rows copied by the copy waves of the gate/up launches of the group "
-                    "before it. native_grouped: native_carried over host tables interleaved "
+                    "before it (native_carried1: groups of one layer, each layer's rows copied "
+                    "during the previous layer's gate/up). native_grouped: native_carried over "
+                    "host tables interleaved "
                     "token-major by groups of four. staged: "
                     "one host sync for the miss list, host pack + H2D copy per layer on a side "
                     "stream one layer ahead"}
