@@ -568,10 +568,11 @@ staple_status_t staple_cache_refresh(const void* table, int64_t vocab, int64_t d
  *   staple_host_adamw_event: the handle's rows-ready event (a hipEvent_t);
  *     pass it to staple_ffn_bwd_table_grad as rows_event, which records it
  *     right after d_rows is complete, before the weight-gradient GEMMs.
- *   staple_host_adamw_start: after that backward call, on the same thread:
- *     enqueues on copy_stream a wait for the event and the copies of
- *     *n_unique and uniq to the host, then returns; the worker then copies the
- *     gradient rows to the host in chunks on copy_stream and applies the
+ *   staple_host_adamw_start: after that backward call, on the same thread;
+ *     returns at once.  The worker waits for the event, copies *n_unique,
+ *     uniq and then the gradient rows (in chunks) to the host on the GPU's
+ *     DMA engines (no compute unit is used; copy_stream carries these
+ *     copies instead when the DMA engines cannot be reached) and applies the
  *     update of staple_adamw_rows_host (same arguments; table, m, v host
  *     memory; n_threads <= 0: up to 14, leaving the caller's thread and the
  *     runtime a core) to each chunk as it lands, while the GPU goes on.  grad, uniq,

@@ -56,6 +56,15 @@ hipError_t launch_assemble_rows_layers(const LayerRowSources& src, int n_layers,
                                        const int32_t* n_unique, int64_t max_unique,
                                        int64_t row_bytes, hipStream_t s, int* err);
 size_t segment_sum_workspace_bytes(int64_t n_tokens, int64_t d_ff);
+hipError_t launch_segment_sum_fixup(int64_t n_tokens, int64_t d_ff, const int32_t* sorted_pos,
+                                    const int32_t* inv, const int32_t* seg_start,
+                                    const int32_t* n_unique, int64_t max_unique, float* d_rows,
+                                    void* ws, hipStream_t s, int* err);
+hipError_t dh_seg_kt(int64_t n, int64_t d, int64_t f, const void* dy, const void* wd_t,
+                     const void* g, const void* u, void* dgu, const int32_t* sorted_pos,
+                     const int32_t* inv, const int32_t* seg_start, const int32_t* n_unique,
+                     int64_t max_unique, float* d_rows, float* first, float* last, hipStream_t s,
+                     int* err);
 hipError_t launch_segment_sum(int dtype, const void* du, int64_t du_ld, int64_t du_col,
                               int64_t n_tokens, int64_t d_ff, const int32_t* sorted_pos,
                               const int32_t* inv, const int32_t* seg_start,
@@ -890,8 +899,8 @@ staple_status_t staple_cache_refresh(const void* table, int64_t vocab, int64_t d
 }
 
 // workspace of the backward: [dg | du] (n x 2f, dtype), an n x f fp32 region
-// (bf16: du in fp32 for the segment sum, then h when it is recomputed; fp32:
-// h when it is recomputed), then the segment-sum partials
+// (h when it is recomputed), the segment-sum partials, then (bf16) the
+// K-major copies
 static size_t bwd_dgu_bytes(int64_t n, int64_t f, int32_t dtype) {
   return align_up(static_cast<size_t>(n) * 2 * f * elem_bytes(dtype), 256);
 }
@@ -927,15 +936,13 @@ static staple_status_t bwd_impl(int64_t n, int64_t d, int64_t f, int32_t dtype, 
   void* dgu = ws;
   char* aux = n > 0 ? static_cast<char*>(ws) + bwd_dgu_bytes(n, f, dtype) : nullptr;
   char* seg_ws = n > 0 ? aux + bwd_aux_bytes(n, f) : nullptr;
-  // bf16: du also goes to the fp32 region unrounded, and the segment sum adds
-  // those values; fp32: the du half of [dg | du] is already fp32
-  const bool bf = dtype == STAPLE_BF16;
-  float* du32 = bf ? reinterpret_cast<float*>(aux) : nullptr;
   // bf16: K-major copies of W_down, [W_gate; W_up], dy and x, so that dh and
   // dx read both operands K-major and the weight gradients one (the same
   // products in the same order: the outputs are the same bits as with
-  // MN-major operands)
-  const bool kt = bf && n > 0;
+  // MN-major operands); dh runs over the tokens in sorted order and its
+  // epilogue does the table-row segment sum's chunk pass on the fp32 du.
+  // fp32: the du half of [dg | du] is fp32 and the segment sum reads it.
+  const bool kt = dtype == STAPLE_BF16 && n > 0;
   char* wd_t = kt ? seg_ws + align_up(segment_sum_workspace_bytes(n, f), 256) : nullptr;
   char* w_t = kt ? wd_t + align_up(static_cast<size_t>(f) * d * 2, 256) : nullptr;
   char* dy_t = kt ? w_t + align_up(static_cast<size_t>(d) * 2 * f * 2, 256) : nullptr;
@@ -945,21 +952,25 @@ static staple_status_t bwd_impl(int64_t n, int64_t d, int64_t f, int32_t dtype, 
     HIPCALL(transpose_bf16(w_gate, f, d, d, w_t, f, k_dx, s));
     if (w_up) HIPCALL(transpose_bf16(w_up, f, d, d, w_t + f * 2, f, k_dx, s));
     HIPCALL(transpose_bf16(dy, n, d, d, dy_t, round64(n), round64(n), s));
-    HIPCALL(dh_act_kt(n, d, f, dy, wd_t, saved_g, saved_u, dgu, du32, s));
+    if (max_unique > 0) {
+      const int64_t chunks = (n + kSegChunk - 1) / kSegChunk;
+      float* first = reinterpret_cast<float*>(seg_ws);
+      HIPCALL(dh_seg_kt(n, d, f, dy, wd_t, saved_g, saved_u, dgu, sorted_pos, inv, seg_start,
+                        n_unique, max_unique, d_rows, first, first + chunks * f, s, err));
+      HIPCALL(launch_segment_sum_fixup(n, f, sorted_pos, inv, seg_start, n_unique, max_unique,
+                                       d_rows, seg_ws, s, err));
+    } else {
+      HIPCALL(dh_act_kt(n, d, f, dy, wd_t, saved_g, saved_u, dgu, nullptr, s));
+    }
   } else {
-    HIPCALL(dh_act<T>(n, d, f, dy, w_down, saved_g, saved_u, dgu, du32, s));
-  }
-  if (n > 0) {
-    if (bf)
-      HIPCALL(launch_segment_sum(STAPLE_F32, du32, f, 0, n, f, sorted_pos, inv, seg_start, n_unique,
-                                 max_unique, d_rows, seg_ws, s, err));
-    else
+    HIPCALL(dh_act<T>(n, d, f, dy, w_down, saved_g, saved_u, dgu, nullptr, s));
+    if (n > 0)
       HIPCALL(launch_segment_sum(dtype, dgu, 2 * f, f, n, f, sorted_pos, inv, seg_start, n_unique,
                                  max_unique, d_rows, seg_ws, s, err));
   }
   if (rows_event) HIPCALL(hipEventRecord(rows_event, s));   // d_rows complete
   // h for dW_down: the forward's, or recomputed from the saved g and u into
-  // the fp32 region (after the segment sum has read it, in stream order)
+  // the n x f fp32 region of the workspace
   const void* h = saved_h;
   if (!h && n > 0) {
     HIPCALL(recompute_h<T>(n, f, saved_g, saved_u, aux, s));

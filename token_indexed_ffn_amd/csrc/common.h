@@ -102,6 +102,10 @@ int* device_error_word();
 
 inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
+// Sorted positions per chunk of the table-row gradient's segment sum (its
+// chunk pass and the dh GEMM epilogue that can do that pass share it).
+constexpr int kSegChunk = 32;
+
 // Bump allocator over a caller-provided workspace.
 struct Workspace {
   char* base;

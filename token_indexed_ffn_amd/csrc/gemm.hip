@@ -32,15 +32,24 @@
 //             stores h = silu(g) * e (and g, u = e when requested).
 //   DhAct   - C is dh = dy W_down; the epilogue reads saved g, u and writes
 //             dg = dh * u * silu'(g) and du = dh * silu(g) side by side, and
-//             (bf16 layers) du once more in fp32, unrounded, for the
-//             table-row segment sum.
+//             optionally du once more in fp32, unrounded, for the table-row
+//             segment sum.
+//   DhSeg   - DhAct over the tokens in sorted order (row p of the tile is
+//             sorted position p, token sorted_pos[p]): g, u and [dg | du]
+//             are addressed by token, and the epilogue also sums the fp32 du
+//             over each run of equal IDs inside every 32-position chunk, in
+//             position order, writing a segment whole to its table-row
+//             gradient and a segment that crosses a chunk boundary to the
+//             chunk's first / last partial (the segment sum's chunk pass,
+//             done without the fp32 du ever leaving the CU).
 #include <type_traits>
 
 #include "common.h"
 
 namespace staple {
 
-enum EpiKind { kEpiStore = 0, kEpiGateUp = 1, kEpiDhAct = 2, kEpiGateStem = 3, kEpiStoreT = 4 };
+enum EpiKind { kEpiStore = 0, kEpiGateUp = 1, kEpiDhAct = 2, kEpiGateStem = 3, kEpiStoreT = 4,
+               kEpiDhSeg = 5 };
 
 struct GemmArgs {
   int64_t M, N, K;
@@ -88,6 +97,17 @@ struct GemmArgs {
   // k_dev is only used with MN-major operands (rows past K read zeros).
   const int32_t* m_dev;
   const int32_t* k_dev;
+  // DhSeg: sorted positions (also the A operand's rows), the inverse map,
+  // the segment offsets [U + 1], the device unique count and the row buffer
+  // bound, the table-row gradient [max_unique x N] and the chunk partials
+  // first / last [chunks of 32 positions x N]
+  const int32_t* seg_inv;
+  const int32_t* seg_start;
+  const int32_t* seg_nu;
+  int64_t seg_max_unique;
+  float* seg_rows;
+  float* seg_first;
+  float* seg_last;
 };
 
 constexpr int kRowBytes = 128;  // bytes of k per LDS tile row and stage
@@ -684,11 +704,17 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(GemmArgs p) {
   // epilogue can issue all of its table-row gathers at once.  They are
   // written to LDS after the first stage's loads are issued, whose wait
   // covers them.
+  // DhSeg keeps each row's token and segment (-1 when invalid) the same way.
   constexpr bool kGate = EPI == kEpiGateUp || EPI == kEpiGateStem;
+  constexpr bool kSeg = EPI == kEpiDhSeg;
+  static_assert(!kSeg || WN == 64, "the segment pass gives each lane one column");
   int* idx_lds = reinterpret_cast<int*>(smem + NS * kStage);
   constexpr int kIdxPer = (BM + NT - 1) / NT;
-  int pro_tok[kGate ? kIdxPer : 1], pro_ri[kGate ? kIdxPer : 1];
-  if constexpr (kGate) {
+  int pro_tok[kGate || kSeg ? kIdxPer : 1], pro_ri[kGate || kSeg ? kIdxPer : 1];
+  // DhSeg: the batch's unique count; past the row buffer nothing is written
+  const int64_t seg_nu = kSeg ? static_cast<int64_t>(*p.seg_nu) : 0;
+  const bool seg_ok = !kSeg || (seg_nu >= 0 && seg_nu <= p.seg_max_unique);
+  if constexpr (kGate || kSeg) {
 #pragma unroll
     for (int j = 0; j < kIdxPer; ++j) {
       const int t = static_cast<int>(threadIdx.x) + j * NT;
@@ -697,11 +723,20 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(GemmArgs p) {
       int64_t tok = p.a_rows ? static_cast<int64_t>(p.a_rows[m]) : m;
       if (tok < 0 || tok >= p.a_rows_bound) tok = -1;   // flagged with the A operand's rows
       pro_tok[j] = static_cast<int>(tok);
-      pro_ri[j] = tok < 0 ? -1 : p.row_index[tok];
+      if constexpr (kGate) {
+        pro_ri[j] = tok < 0 ? -1 : p.row_index[tok];
+      } else {
+        int64_t sg = tok < 0 ? -1 : p.seg_inv[tok];
+        if (sg < 0 || sg >= seg_nu) {
+          if (tok >= 0 && seg_ok) flag_index_error(p.err);
+          sg = -1;
+        }
+        pro_ri[j] = static_cast<int>(sg);
+      }
     }
   }
   auto stash_idx = [&]() {
-    if constexpr (kGate) {
+    if constexpr (kGate || kSeg) {
 #pragma unroll
       for (int j = 0; j < kIdxPer; ++j) {
         const int t = static_cast<int>(threadIdx.x) + j * NT;
@@ -969,6 +1004,104 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(GemmArgs p) {
           if (p.u_out) store8g<T>(p.u_out, o, e);
         }
       }
+    } else if constexpr (EPI == kEpiDhSeg) {
+      // rows are sorted positions; g, u and [dg | du] live at the row's token
+      const int64_t f = p.N;
+      constexpr int kPerLane = (kChunks + 63) / 64;
+      float gv[kPerLane][8], uv[kPerLane][8];
+#pragma unroll
+      for (int c = 0; c < kPerLane; ++c) {
+        const int q = lane + 64 * c;
+        const int rr = q / (WN / 8), cc = (q % (WN / 8)) * 8;
+        const int64_t m = mrow0 + rr;
+        const int64_t n = n0 + wn * WN + cc;
+        const int64_t tok = idx_lds[wm * WM + i * 32 + rr];
+        const bool ok = q < kChunks && m < p.M && n < f && tok >= 0;
+        load8g<T>(p.g_in, ok ? tok * f + n : 0, gv[c]);
+        load8g<T>(p.u_in, ok ? tok * f + n : 0, uv[c]);
+      }
+#pragma unroll
+      for (int c = 0; c < kPerLane; ++c) {
+        const int q = lane + 64 * c;
+        const int rr = q / (WN / 8), cc = (q % (WN / 8)) * 8;
+        const int64_t m = mrow0 + rr;
+        const int64_t n = n0 + wn * WN + cc;
+        const int64_t tok = idx_lds[wm * WM + i * 32 + rr];
+        if (q < kChunks && m < p.M) {
+          float du[8];
+          if (n < f && tok >= 0) {
+            float dh[8], dg[8];
+            read8(region + rr * LD + cc, dh);
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {
+              const float s = sigmoidf_(gv[c][k]);
+              du[k] = dh[k] * gv[c][k] * s;
+              dg[k] = dh[k] * uv[c][k] * s * (1.0f + gv[c][k] * (1.0f - s));
+            }
+            store8g<T>(p.dgu_out, tok * 2 * f + n, dg);
+            store8g<T>(p.dgu_out, tok * 2 * f + f + n, du);
+          } else {
+#pragma unroll
+            for (int k = 0; k < 8; ++k) du[k] = 0.0f;   // a flagged row adds nothing
+          }
+          // the fp32 du stays in this wave's staging rows for the segment pass
+          *reinterpret_cast<float4*>(region + rr * LD + cc) = make_float4(du[0], du[1], du[2], du[3]);
+          *reinterpret_cast<float4*>(region + rr * LD + cc + 4) = make_float4(du[4], du[5], du[6], du[7]);
+        }
+      }
+      __syncthreads();
+      // lane l walks column l of the block's 32 positions in order; a run of
+      // one segment ends at a change of segment or at the block's end.  A
+      // run that starts the block belongs to a segment begun in an earlier
+      // chunk when position p0 - 1 has the same segment; one that ends the
+      // block continues past it when position p1 has the same segment
+      // (segments are contiguous in sorted order): so no segment offset is
+      // loaded inside the walk.
+      static_assert(kSegChunk == 32, "one chunk of the segment sum per 32-row block");
+      const int64_t p0 = mrow0;
+      const int64_t p1 = p0 + kSegChunk < p.M ? p0 + kSegChunk : p.M;
+      if (seg_ok && p0 < p.M) {
+        const int64_t chunk = p0 / kSegChunk;
+        const int row0 = wm * WM + i * 32;
+        const int len = static_cast<int>(p1 - p0);
+        // segments of the positions just before and after the block (-2: none)
+        auto seg_at = [&](int64_t pos) -> int {
+          if (pos < 0 || pos >= p.M) return -2;
+          if (pos >= m0 && pos < m0 + BM) return idx_lds[BM + (pos - m0)];
+          const int64_t t = p.a_rows[pos];
+          if (t < 0 || t >= p.a_rows_bound) return -1;
+          const int64_t sg = p.seg_inv[t];
+          return sg >= 0 && sg < seg_nu ? static_cast<int>(sg) : -1;
+        };
+        const int prev_sg = seg_at(p0 - 1), next_sg = seg_at(p1);
+        // lane r: the segment of row r, and whether row r ends a run
+        const int my_sg = lane < len ? idx_lds[BM + row0 + lane] : -3;
+        const int nx_sg = lane + 1 < len ? idx_lds[BM + row0 + lane + 1] : -4;
+        const uint64_t ends = __ballot(lane < len && (lane == len - 1 || nx_sg != my_sg));
+        const int64_t col = n0 + wn * WN + lane;
+        float a = 0.0f;
+        int run0 = 0;
+#pragma unroll
+        for (int r = 0; r < kSegChunk; ++r) {
+          if (r < len) {
+            a += region[r * LD + lane];
+            if ((ends >> r) & 1ull) {
+              const int sg = __builtin_amdgcn_readlane(my_sg, r);
+              if (sg >= 0 && col < f) {
+                const bool before = run0 == 0 && prev_sg == sg;
+                const bool after = r == len - 1 && next_sg == sg;
+                float* dst = before ? p.seg_first + chunk * f + col         // began in an earlier chunk
+                             : after ? p.seg_last + chunk * f + col          // continues past p1
+                                     : p.seg_rows + sg * f + col;           // whole segment here
+                *dst = a;
+              }
+              a = 0.0f;
+              run0 = r + 1;
+            }
+          }
+        }
+      }
+      if (!seg_ok && blockIdx.x == 0 && threadIdx.x == 0 && i == 0) flag_index_error(p.err);
     } else {  // kEpiDhAct: C = dh (M = tokens, N = d_ff)
       // g and u of all of this lane's chunks are loaded first, then dg, du
       // are formed and stored
@@ -1016,8 +1149,8 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(GemmArgs p) {
 template <typename T, int BM, int BN, int WGM, int WGN, bool AK, bool BK, int EPI, typename OutT,
           int RB, int NS, int PIPE = 0>
 static hipError_t run_tile(const GemmArgs& a, hipStream_t s) {
-  constexpr bool kGate = EPI == kEpiGateUp || EPI == kEpiGateStem;
-  constexpr size_t kSmem = static_cast<size_t>(NS) * (BM + BN) * RB + (kGate ? 2 * BM * sizeof(int) : 0);
+  constexpr bool kIdx = EPI == kEpiGateUp || EPI == kEpiGateStem || EPI == kEpiDhSeg;
+  constexpr size_t kSmem = static_cast<size_t>(NS) * (BM + BN) * RB + (kIdx ? 2 * BM * sizeof(int) : 0);
   auto kern = &gemm_kernel<T, BM, BN, WGM, WGN, AK, BK, EPI, OutT, RB, NS, PIPE>;
   static const hipError_t attr = hipFuncSetAttribute(
       reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
@@ -1208,6 +1341,27 @@ hipError_t dh_act_kt(int64_t n, int64_t d, int64_t f, const void* dy, const void
   a.b0 = wd_t; a.ldb = d;
   a.g_in = g; a.u_in = u; a.dgu_out = dgu; a.du32_out = du32;
   return run<bf16_t, true, true, kEpiDhAct, bf16_t>(a, s);
+}
+
+// dh over the tokens in sorted order with B = W_down^T K-major, [dg | du] at
+// each token's row, and the table-row gradient's chunk pass in the epilogue:
+// d_rows for segments inside a 32-position chunk, first / last partials for
+// the others (completed by the segment sum's fixup pass)
+hipError_t dh_seg_kt(int64_t n, int64_t d, int64_t f, const void* dy, const void* wd_t,
+                     const void* g, const void* u, void* dgu, const int32_t* sorted_pos,
+                     const int32_t* inv, const int32_t* seg_start, const int32_t* n_unique,
+                     int64_t max_unique, float* d_rows, float* first, float* last, hipStream_t s,
+                     int* err) {
+  GemmArgs a = blank<bf16_t>();
+  a.M = n; a.N = f; a.K = d;
+  a.a0 = dy; a.lda = d;
+  a.a_rows = sorted_pos; a.a_rows_bound = n;
+  a.b0 = wd_t; a.ldb = d;
+  a.g_in = g; a.u_in = u; a.dgu_out = dgu;
+  a.seg_inv = inv; a.seg_start = seg_start; a.seg_nu = n_unique; a.seg_max_unique = max_unique;
+  a.seg_rows = d_rows; a.seg_first = first; a.seg_last = last;
+  a.err = err;
+  return run<bf16_t, true, true, kEpiDhSeg, bf16_t>(a, s);
 }
 
 // dx with B = [W_gate^T | W_up^T] [d x k] K-major (k = 2f, or f for the STEM layer)

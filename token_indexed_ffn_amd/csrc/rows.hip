@@ -395,7 +395,6 @@ hipError_t launch_assemble_rows_layers(const LayerRowSources& src, int n_layers,
 // du lives at column offset du_col of rows with stride du_ld (elements);
 // each lane owns 8 consecutive columns (one 16-byte bf16 load, two for fp32).
 // ---------------------------------------------------------------------------
-constexpr int kSegChunk = 32;
 constexpr int kSegCols = 512;   // 64 lanes x 8 columns
 constexpr int kSegAhead = 8;    // du rows in flight per lane (chunk pass)
 constexpr int kFixAhead = 8;    // partials in flight per lane (fixup pass)
@@ -585,6 +584,22 @@ hipError_t launch_segment_sum(int dtype, const void* du, int64_t du_ld, int64_t 
     segsum_chunk_kernel<float><<<dim3(cb, static_cast<unsigned>(chunks)), dim3(64 * kSegWaves), 0, s>>>(
         static_cast<const float*>(du), du_ld, du_col, n_tokens, d_ff, sorted_pos, inv, seg_start,
         n_unique, max_unique, d_rows, first, last, err);
+  segsum_fixup_kernel<<<dim3(cb, static_cast<unsigned>(chunks)), dim3(64 * kSegWaves), 0, s>>>(
+      n_tokens, d_ff, sorted_pos, inv, seg_start, n_unique, max_unique, first, last, d_rows, err);
+  return hipGetLastError();
+}
+
+// The fixup pass alone, after a chunk pass done elsewhere (the dh GEMM's
+// epilogue over sorted positions) into d_rows and the partials at ws.
+hipError_t launch_segment_sum_fixup(int64_t n_tokens, int64_t d_ff, const int32_t* sorted_pos,
+                                    const int32_t* inv, const int32_t* seg_start,
+                                    const int32_t* n_unique, int64_t max_unique, float* d_rows,
+                                    void* ws, hipStream_t s, int* err) {
+  if (max_unique == 0 || n_tokens == 0) return hipSuccess;
+  const int64_t chunks = (n_tokens + kSegChunk - 1) / kSegChunk;
+  float* first = static_cast<float*>(ws);
+  float* last = first + chunks * d_ff;
+  const unsigned cb = static_cast<unsigned>((d_ff + kSegCols * kSegWaves - 1) / (kSegCols * kSegWaves));
   segsum_fixup_kernel<<<dim3(cb, static_cast<unsigned>(chunks)), dim3(64 * kSegWaves), 0, s>>>(
       n_tokens, d_ff, sorted_pos, inv, seg_start, n_unique, max_unique, first, last, d_rows, err);
   return hipGetLastError();
