@@ -588,9 +588,10 @@ staple_status_t staple_cache_refresh(const void* table, int64_t vocab, int64_t d
  *   staple_host_adamw_finish: waits for the host update and returns its
  *     status (STAPLE_ERR_HOST for an ID outside the table,
  *     STAPLE_ERR_INDEX_RANGE for a row count past max_rows: nothing
- *     updated); on success `stream` (NULL: the null stream) is made to wait
- *     for the refreshes.  Read the host table, and the cache on another
- *     stream, only after it.
+ *     updated; for a failure part way, rows of earlier chunks may be
+ *     updated); `stream` (NULL: the null stream) is made to wait for every
+ *     refresh the update launched, whatever the status.  Read the host
+ *     table, and the cache on another stream, only after it.
  *   staple_host_adamw_destroy: waits for a running update, then frees all.
  * The rows are updated by the same routine as staple_adamw_rows_host, each
  * once and independently: the same bits as the serial update. */

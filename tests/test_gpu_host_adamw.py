@@ -119,3 +119,54 @@ def test_overlapped_host_adamw_matches_the_serial_schedule(st, cap, in_worker):
     got = ovl[0].float().numpy().astype(np.float64)
     step = np.ldexp(1.0, np.floor(np.log2(np.maximum(np.abs(p), 1e-30))).astype(np.int64) - 7)
     assert np.mean(np.abs(got - p) <= step * 1.01) > 0.999
+
+
+def test_overlapped_host_adamw_reports_an_id_outside_the_table(st):
+    """A row ID past the table's end: finish() raises STAPLE_ERR_HOST, nothing
+    is updated, and the same handle then runs a normal update."""
+    import torch
+    dev = torch.device("cuda:0")
+    n, d, f, vocab = 300, 128, 256, 2000
+    _log("overlapped host AdamW with an ID outside the table")
+    inp = S.host_layer_inputs(n, d, f, vocab, dtype="bf16", seed=83)
+    x, wg, wu, wd, dy = (to_dev(getattr(inp, k), "bf16", dev)
+                         for k in ("x", "w_gate", "w_up", "w_down", "dy"))
+    table = torch.from_numpy(inp.table.view(np.int16)).view(torch.bfloat16).pin_memory()
+    ids = S.zipf_ids(n, vocab, 910)
+    ids[0] = vocab - 1                                # above the short table's end
+    ids_dev = torch.from_numpy(ids).to(dev)
+    dd = st.staple_dedup(ids_dev, vocab)
+    rows = st.staple_gather_rows(table, dd["uniq"], dd["n_unique"])
+    fwd = st.staple_ffn_fwd(x, wg, wu, wd, rows, dd["inv"], out_dtype=torch.float32, save=True)
+    ha = st.HostAdamW(n, f)
+    bwd = st.staple_ffn_bwd_table_grad(dy, x, wg, wu, wd, fwd["g"], fwd["u"], fwd["h"],
+                                       dd["sorted_pos"], dd["seg_start"], dd["n_unique"],
+                                       inv=dd["inv"], rows_event=ha.event)
+    side = torch.cuda.Stream()
+    short = table[: vocab // 2]                       # a pinned view of the first rows
+    m = torch.zeros(vocab, f, dtype=torch.float32)
+    v = torch.zeros(vocab, f, dtype=torch.float32)
+    before = short.clone()
+    ha.start(short, m[: vocab // 2], v[: vocab // 2], dd["uniq"], dd["n_unique"], bwd["d_rows"],
+             lr=1e-2, weight_decay=1e-2, step=1, copy_stream=side)
+    with pytest.raises(st.StapleError) as e:
+        ha.finish()
+    assert e.value.status == -6                       # STAPLE_ERR_HOST
+    assert torch.equal(short, before)
+    assert not m.any() and not v.any()
+    # the handle is usable again: a full-size table, compared with the serial update
+    bwd = st.staple_ffn_bwd_table_grad(dy, x, wg, wu, wd, fwd["g"], fwd["u"], fwd["h"],
+                                       dd["sorted_pos"], dd["seg_start"], dd["n_unique"],
+                                       inv=dd["inv"], rows_event=ha.event)
+    ref_t, ref_m, ref_v = table.clone(), m.clone(), v.clone()
+    ha.start(table, m, v, dd["uniq"], dd["n_unique"], bwd["d_rows"], lr=1e-2, weight_decay=1e-2,
+             step=1, copy_stream=side)
+    ha.finish()
+    ha.close()
+    torch.cuda.synchronize()
+    u = int(dd["n_unique"].item())
+    st.staple_adamw_rows_host(ref_t, ref_m, ref_v, dd["uniq"][:u].cpu().contiguous(),
+                              bwd["d_rows"][:u].cpu().contiguous(), step=1, lr=1e-2,
+                              weight_decay=1e-2)
+    assert torch.equal(table, ref_t) and torch.equal(m, ref_m) and torch.equal(v, ref_v)
+    assert st.staple_get_device_error() == 0

@@ -440,8 +440,17 @@ struct staple_host_adamw {
   staple::AdamWConsts c{};
   int n_threads = 0;
 
+  // ev_done is recorded on the refresh stream whatever the outcome, so that
+  // finish orders the caller's stream after every refresh launched, also
+  // when the job stopped part way.
   staple_status_t run_job() {
     if (hipSetDevice(device) != hipSuccess) return STAPLE_ERR_HIP;
+    const staple_status_t r = run_job_steps();
+    const bool rec = hipEventRecord(ev_done, refresh) == hipSuccess;
+    return r == STAPLE_OK && !rec ? STAPLE_ERR_HIP : r;
+  }
+
+  staple_status_t run_job_steps() {
     if (sdma.ready) {
       // the row count and IDs on the DMA engines as soon as the rows are
       // complete (a copy kernel could wait behind the GEMMs for a CU)
@@ -457,7 +466,7 @@ struct staple_host_adamw {
     }
     const int64_t n = meta_host[0];
     if (n < 0 || n > max_rows) return STAPLE_ERR_INDEX_RANGE;
-    if (n == 0) return hipEventRecord(ev_done, refresh) == hipSuccess ? STAPLE_OK : STAPLE_ERR_HIP;
+    if (n == 0) return STAPLE_OK;
     const int32_t* ids = meta_host + 1;
     for (int64_t k = 0; k < n; ++k)
       if (ids[k] < 0 || ids[k] >= vocab) return STAPLE_ERR_HOST;
@@ -498,7 +507,7 @@ struct staple_host_adamw {
                                        refresh, err, kRefreshWorkgroups) != hipSuccess)
         return STAPLE_ERR_HIP;
     }
-    return hipEventRecord(ev_done, refresh) == hipSuccess ? STAPLE_OK : STAPLE_ERR_HIP;
+    return STAPLE_OK;
   }
 
   void loop() {
@@ -630,8 +639,9 @@ staple_status_t staple_host_adamw_finish(staple_host_adamw_t* h, void* stream) {
   if (!h) return STAPLE_ERR_INVALID_ARGUMENT;
   std::unique_lock<std::mutex> lk(h->mu);
   h->cv.wait(lk, [&] { return !h->busy; });
-  if (h->result == STAPLE_OK &&
-      hipStreamWaitEvent(static_cast<hipStream_t>(stream), h->ev_done, 0) != hipSuccess)
+  // also after a failed job: its refreshes may still be running
+  if (hipStreamWaitEvent(static_cast<hipStream_t>(stream), h->ev_done, 0) != hipSuccess &&
+      h->result == STAPLE_OK)
     return STAPLE_ERR_HIP;
   return h->result;
 }
