@@ -19,9 +19,11 @@ timed on its own and reported beside it, `adamw_table_rows`); `decode_stem`,
 `decode_7b`, `train_7b` (OLMo-2-7B shapes: 16 decode layers over
 100352 x 11008 tables, a 16384-token training batch); `train_lowrank` (the
 1B training step with the low-rank r=512 table and its projection);
-`offload_decode`,
-`offload_train` (tables in pinned host memory with a 5% HBM cache of the most
-frequent rows, PCIe-inclusive).  Every workload carries its own `roofline`
+`offload_decode`, `offload_prefill` (64 prompts of 256 tokens through the 12
+layers in chunks of 4096 tokens, the next chunk's rows assembled on a side
+stream while the current chunk's layers run), `offload_train` (tables in
+pinned host memory with a 5% HBM cache of the most frequent rows,
+PCIe-inclusive).  Every workload carries its own `roofline`
 object for its dominant kernel.  `--workloads` selects a subset.
 
 Every input is synthetic and seeded (staple_synth).  Inputs are resident in
@@ -630,11 +632,12 @@ def _miss_list_to_host(torch, lk, host_buf, blocking=False):
     return int(n.item())
 
 
-def run_offload_decode(torch, st, w, steps, warmup):
+def run_offload_decode(torch, st, w, steps, warmup, O=None):
     from staple_synth import device_normal
     dev = torch.device("cuda:0")
     n, d, f, v, L = w.n_tokens, w.d_model, w.d_ff, w.vocab, w.n_layers
-    O = setup_offload(torch, st, w, L)
+    if O is None:
+        O = setup_offload(torch, st, w, L)
     ids = torch.from_numpy(w.ids()).to(dev)
     layers = []
     for l in range(L):
@@ -784,11 +787,26 @@ def run_offload_decode(torch, st, w, steps, warmup):
     torch.cuda.synchronize()
     if not all(torch.equal(a, lay["y"]) for a, lay in zip(ys, layers)):
         raise RuntimeError("the carried row copies give other outputs than the per-layer calls")
+    # the carried step captured once in a HIP graph, replayed
+    cap_s = torch.cuda.Stream()
+    cap_s.wait_stream(main)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(cap_s):
+        step_carried()
+        cap_s.synchronize()
+        with torch.cuda.graph(graph, stream=cap_s):
+            step_carried()
+    torch.cuda.synchronize()
+    ms_graph = timed(graph.replay)
+    torch.cuda.synchronize()
+    if not all(torch.equal(a, lay["y"]) for a, lay in zip(ys, layers)):
+        raise RuntimeError("the graph-replayed step gives other outputs than the per-layer calls")
+    del graph
     ms_staged = timed(step_staged)
     m = _miss_list_to_host(torch, lk_out, miss_host)
     times = {"direct": ms_direct, "staged": ms_staged, "native": ms_native, "native_inplace": ms_inplace,
              "native_carried": ms_carried, "native_carried1": ms_carried1,
-             "native_grouped": ms_grouped}
+             "native_grouped": ms_grouped, "native_carried_graph": ms_graph}
     method = min(times, key=times.get)
     ms = times[method]
     n_unique = int(dd_out["n_unique"].item())
@@ -830,6 +848,7 @@ def run_offload_decode(torch, st, w, steps, warmup):
             "native_inplace_ms_per_step": ms_inplace, "native_carried_ms_per_step": ms_carried,
             "native_carried1_ms_per_step": ms_carried1,
             "native_grouped_ms_per_step": ms_grouped, "staged_ms_per_step": ms_staged,
+            "native_carried_graph_ms_per_step": ms_graph,
             "n_unique": n_unique, "misses_per_layer": m, "cache_capacity": w.cache_capacity,
             "pcie_bytes_per_step": m * f * 2 * L,
             "note": "eager steps, dedup + cache probe once per step. direct: per layer one kernel "
@@ -844,9 +863,192 @@ def run_offload_decode(torch, st, w, steps, warmup):
                     "before it (native_carried1: groups of one layer, each layer's rows copied "
                     "during the previous layer's gate/up). native_grouped: native_carried over "
                     "host tables interleaved "
-                    "token-major by groups of four. staged: "
+                    "token-major by groups of four. native_carried_graph: native_carried "
+                    "captured once in a HIP graph and replayed. staged: "
                     "one host sync for the miss list, host pack + H2D copy per layer on a side "
                     "stream one layer ahead"}
+
+
+def run_offload_prefill(torch, st, w, O, steps, warmup, chunk=4096, workgroups=(16, 32, 64)):
+    """Prefill of w.n_tokens tokens through w.n_layers layers whose tables are in
+    pinned host memory (top-5% rows cached in HBM), in chunks of `chunk` tokens.
+    Each chunk's rows come from one staple_prefill_rows_cached call (dedup, cache
+    probe, all layers' compact rows with the misses read over PCIe), then the
+    layers' FFNs (staple_ffn_fwd: gate/up GEMM with the row epilogue, down GEMM).
+    compute_only: every chunk's rows assembled beforehand (the FFNs alone).
+    serial: each chunk's rows, then its FFNs, on one stream.  pipelined: chunk
+    c + 1's rows on a side stream, on at most `workgroups` workgroups, while
+    chunk c's FFNs run; in the first chunk, layer 0's rows come first (full
+    grid) and each later layer's rows while the layer before it runs; two sets
+    of row buffers, each reused only after the chunk that read it."""
+    from staple_synth import device_normal
+    dev = torch.device("cuda:0")
+    n, d, f, v, L = w.n_tokens, w.d_model, w.d_ff, w.vocab, w.n_layers
+    C = chunk
+    nc = n // C
+    cap = w.cache_capacity
+    ids = torch.from_numpy(w.ids()).to(dev)
+    layers = []
+    for l in range(L):
+        s = w.layer_seeds(l)
+        layers.append({k: device_normal(shape, std, s[k], torch.bfloat16, dev) for k, shape, std in (
+            ("x", (n, d), w.x_std), ("w_gate", (f, d), w.w_std), ("w_up", (f, d), w.w_std),
+            ("w_down", (d, f), w.w_std))})
+        layers[-1]["y"] = torch.empty(n, d, dtype=torch.bfloat16, device=dev)
+    i32 = dict(dtype=torch.int32, device=dev)
+    ws_bytes = st.prefill_rows_workspace_bytes(C)
+
+    def buffers():
+        B = {"dd": {"uniq": torch.empty(C, **i32), "inv": torch.empty(C, **i32),
+                    "sorted_pos": torch.empty(C, **i32), "seg_start": torch.empty(C + 1, **i32),
+                    "n_unique": torch.empty(1, **i32)},
+             "lk": {"code": torch.empty(C, **i32), "miss_uidx": torch.empty(C, **i32),
+                    "n_miss": torch.empty(1, **i32)},
+             "rows": [torch.empty(C, f, dtype=torch.bfloat16, device=dev) for _ in range(L)],
+             "ws": torch.empty(ws_bytes, dtype=torch.uint8, device=dev) if ws_bytes else None}
+        srcs = [{"table": O["tables"][l], "cache_rows": O["cache_rows"][l], "rows": B["rows"][l]}
+                for l in range(L)]
+        B["rs"] = st.RowSources(srcs, d_ff=f)
+        B["rs_layer"] = [st.RowSources([src], d_ff=f) for src in srcs]
+        return B
+
+    bufs = [buffers() for _ in range(2)]
+    pre = [buffers() for _ in range(nc)]
+    fwd_ws = torch.empty(st.lib().staple_ffn_fwd_workspace_bytes(C, d, f, 1), dtype=torch.uint8,
+                         device=dev)
+    main, side = torch.cuda.current_stream(), torch.cuda.Stream()
+    ready = [torch.cuda.Event() for _ in range(nc)]
+    done = [torch.cuda.Event() for _ in range(nc)]
+    layer_ready = [torch.cuda.Event() for _ in range(L)]
+
+    def rows(B, c, stream, wg, rs=None, lookup=True):
+        st.staple_prefill_rows_cached(B["rs"] if rs is None else rs, ids[c * C:(c + 1) * C],
+                                      O["id_to_slot"], cap, dedup_out=B["dd"], lookup_out=B["lk"],
+                                      workspace=B["ws"], max_workgroups=wg, lookup=lookup,
+                                      stream=stream)
+
+    def ffns(B, c, per_layer=None):
+        for l, lay in enumerate(layers):
+            if per_layer is not None:
+                main.wait_event(per_layer[l])
+            st.staple_ffn_fwd(lay["x"][c * C:(c + 1) * C], lay["w_gate"], lay["w_up"],
+                              lay["w_down"], B["rows"][l], B["dd"]["inv"],
+                              out={"y": lay["y"][c * C:(c + 1) * C]}, workspace=fwd_ws,
+                              stream=main)
+
+    def compute_only():
+        for c in range(nc):
+            ffns(pre[c], c)
+
+    def serial():
+        for c in range(nc):
+            rows(bufs[0], c, main, 0)
+            ffns(bufs[0], c)
+
+    def pipelined(wg):
+        side.wait_stream(main)          # the previous prefill has finished with the buffers
+
+        def issue(c):
+            if c >= 2:
+                side.wait_event(done[c - 2])
+            rows(bufs[c % 2], c, side, wg)
+            ready[c].record(side)
+
+        # the first chunk: layer 0's rows (with the dedup and the probe) on the
+        # full grid, nothing else running yet; then each later layer's rows,
+        # one call each, so that layer l + 1's rows arrive during layer l
+        B0 = bufs[0]
+        rows(B0, 0, side, 0, rs=B0["rs_layer"][0])
+        layer_ready[0].record(side)
+        for l in range(1, L):
+            rows(B0, 0, side, wg, rs=B0["rs_layer"][l], lookup=False)
+            layer_ready[l].record(side)
+        for c in range(nc):
+            if c + 1 < nc:
+                issue(c + 1)
+            if c == 0:
+                ffns(B0, 0, per_layer=layer_ready)
+            else:
+                main.wait_event(ready[c])
+                ffns(bufs[c % 2], c)
+            done[c].record(main)
+
+    def timed(fn):
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        if st.staple_get_device_error() != 0:
+            raise RuntimeError("device error in offload prefill")
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            fn()
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) / steps * 1e3
+
+    for c in range(nc):
+        rows(pre[c], c, main, 0)
+    torch.cuda.synchronize()
+    misses = sum(int(B["lk"]["n_miss"].item()) for B in pre)
+    uniques = sum(int(B["dd"]["n_unique"].item()) for B in pre)
+    ms_compute = timed(compute_only)
+    ref = [layers[0]["y"].clone(), layers[-1]["y"].clone()]
+    ms_serial = timed(serial)
+    same = lambda: torch.equal(ref[0], layers[0]["y"]) and torch.equal(ref[1], layers[-1]["y"])
+    if not same():
+        raise RuntimeError("serial prefill outputs differ from the precomputed-rows run")
+    ms_pipe = {}
+    for wg in workgroups:
+        ms_pipe[wg] = timed(lambda: pipelined(wg))
+        torch.cuda.synchronize()
+        if not same():
+            raise RuntimeError("pipelined prefill outputs differ from the serial run")
+    best_wg = min(ms_pipe, key=ms_pipe.get)
+    ms = ms_pipe[best_wg]
+    # the rows of one chunk alone (all layers, full grid): what the pipeline hides
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for c in range(nc):
+        rows(bufs[0], c, main, 0)
+    e1.record()
+    torch.cuda.synchronize()
+    rows_ms = e0.elapsed_time(e1)
+    # dominant kernel: the gate/up GEMM of one chunk (events around each launch)
+    h = torch.empty(C, f, dtype=torch.bfloat16, device=dev)
+    durs = []
+    for rep in range(max(3, steps)):
+        lay, B = layers[rep % L], pre[rep % nc]
+        c = rep % nc
+        ev = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+        ev[0].record()
+        st.staple_ffn_gate_up(lay["x"][c * C:(c + 1) * C], lay["w_gate"], lay["w_up"],
+                              B["rows"][rep % L], B["dd"]["inv"], h)
+        ev[1].record()
+        torch.cuda.synchronize()
+        durs.append(ev[0].elapsed_time(ev[1]) * 1e3)
+    gu_us = sum(durs) / len(durs)
+    gu_flops = 4 * C * d * f
+    achieved = gu_flops / (gu_us * 1e-6) / 1e12
+    flops = 6 * n * d * f * L
+    pcie = misses * L * f * 2
+    return {"workload": w.name, "tokens": n, "chunk_tokens": C, "chunks": nc, "layers": L,
+            "ms_per_prefill": ms, "tokens_per_s": n / (ms * 1e-3),
+            "tflops": flops / (ms * 1e-3) / 1e12,
+            "mfma_frac": flops / (ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
+            "pipelined_ms": {str(k): t for k, t in ms_pipe.items()}, "max_workgroups": best_wg,
+            "serial_ms": ms_serial, "compute_only_ms": ms_compute,
+            "ratio_to_compute_only": ms / ms_compute,
+            "rows_alone_ms": rows_ms,
+            "hidden_fraction_of_rows": 1.0 - (ms - ms_compute) / rows_ms,
+            "unique_rows_per_chunk": uniques / nc, "miss_rows_per_chunk": misses / nc,
+            "pcie_bytes_per_prefill": pcie, "cache_capacity": cap,
+            "roofline": {
+                "kernel": "gemm_kernel<bf16,GateUp> (staple_ffn_gate_up, one 4096-token chunk)",
+                "bound": "mfma", "achieved": achieved, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": achieved / BF16_PEAK_TFLOPS, "traffic": None,
+                "avg_launch_us": gu_us, "algorithmic_flops_per_launch": gu_flops},
+            "note": "forward only (prefill), eager launches; FLOPs 6 N d f per layer. "
+                    "rows_alone_ms: every chunk's rows on the full grid with nothing beside them; "
+                    "hidden_fraction_of_rows = 1 - (pipelined - compute_only) / rows_alone_ms"}
 
 
 def run_offload_train(torch, st, w, steps, warmup):
@@ -1209,9 +1411,15 @@ def main(argv=None) -> int:
                                                  args.train_warmup)
         _progress(f"lowrank: {out['train_lowrank']['tokens_per_s']:.0f} tokens/s")
     if "offload" in wl:
-        out["offload_decode"] = run_offload_decode(torch, st, S.OLMO1B_OFFLOAD, 20, 3)
+        O12 = setup_offload(torch, st, S.OLMO1B_OFFLOAD, S.OLMO1B_OFFLOAD.n_layers)
+        out["offload_decode"] = run_offload_decode(torch, st, S.OLMO1B_OFFLOAD, 20, 3, O=O12)
         torch.cuda.empty_cache()
         _progress(f"offload decode: {out['offload_decode']['tokens_per_s']:.0f} tokens/s")
+        out["offload_prefill"] = run_offload_prefill(torch, st, S.OLMO1B_OFFLOAD_PREFILL, O12,
+                                                     max(3, args.train_steps), 1)
+        del O12
+        torch.cuda.empty_cache()
+        _progress(f"offload prefill: {out['offload_prefill']['tokens_per_s']:.0f} tokens/s")
         out["offload_train"] = run_offload_train(torch, st, S.OLMO1B_OFFLOAD_TRAIN,
                                                  args.train_steps, args.train_warmup)
         torch.cuda.empty_cache()

@@ -473,6 +473,60 @@ staple_status_t staple_group_tables_host(const void* const* tables, int64_t n_ta
                                          void* grouped);
 
 /* ------------------------------------------------------------------------
+ * Rows of one prefill chunk for a stack of layers with host-offloaded tables
+ * (STAPLE retrieval-path table, Prefill row: the prompt's tokens are
+ * deduplicated once, the HBM cache is probed, one inverse map serves every
+ * layer, later layers' rows are fetched while earlier layers run and
+ * successive chunks are pipelined).  One call per chunk:
+ *   1. (lookup = 1) staple_dedup of ids[0 .. n) (outputs uniq, inv,
+ *      sorted_pos, seg_start, n_unique, as staple_dedup);
+ *   2. (lookup = 1) staple_cache_lookup of the unique IDs (outputs code,
+ *      miss_uidx, n_miss, as staple_cache_lookup; no miss-ID list);
+ *   3. every layer's compact rows: layers[l].rows[u] = cache_rows_l[code[u]]
+ *      on a hit, the table's row uniq[u] on a miss, for u < *n_unique, in one
+ *      launch for up to 32 layers (a longer stack in slices of 32).
+ * lookup = 0 skips steps 1 and 2 and reads uniq, code and n_unique as an
+ * earlier call on the same chunk left them (nothing else is read or
+ * written): the rows of some layers can then be fetched first (the first
+ * layer's, say) and the others while those layers run.
+ * With a pinned host table the misses cross PCIe inside that launch.  It
+ * runs on at most max_workgroups workgroups (0: up to 512, enough to fill
+ * the GPU); a small count (16-64) lets the assembly of the next chunk, issued
+ * on a second stream, run beside the current chunk's GEMMs while holding
+ * only that many compute units.  The caller orders the streams with events:
+ * the next chunk's FFNs after this call, and this call after the FFNs that
+ * still read the `rows` it overwrites.
+ *   layers: host array of n_layers descriptors; cache_rows [capacity x d_ff]
+ *     device (may be NULL when capacity is 0); table [vocab x d_ff], pinned
+ *     host (hipHostMalloc) or device, token rows table_stride elements apart
+ *     (0: d_ff; larger for tables interleaved by staple_group_tables_host);
+ *     rows [n x d_ff] device.  All 16-byte aligned.
+ *   ids [n] device, 1 <= n < 2^31; id_to_slot [vocab] from staple_cache_build.
+ *   uniq, inv, sorted_pos, code, miss_uidx [n], seg_start [n + 1], n_unique,
+ *     n_miss [1]: device outputs.
+ *   ws: staple_prefill_rows_workspace_bytes(n) bytes (0 up to 4096 tokens;
+ *     then ws may be NULL).
+ * The same bits as the three separate calls (and as
+ * staple_assemble_rows_from_table per layer), whatever max_workgroups.
+ * Argument errors return before anything is enqueued; IDs out of range are
+ * reported through the device error word.
+ * ------------------------------------------------------------------------ */
+typedef struct staple_row_source {
+  const void* cache_rows;
+  const void* table;
+  int64_t table_stride;
+  void* rows;
+} staple_row_source_t;
+
+size_t staple_prefill_rows_workspace_bytes(int64_t n_tokens);
+staple_status_t staple_prefill_rows_cached(
+    int64_t n_layers, const staple_row_source_t* layers, int64_t n_tokens, int64_t d_ff,
+    int32_t dtype, const int32_t* ids, int64_t vocab, const int32_t* id_to_slot,
+    int64_t capacity, int32_t lookup, int32_t max_workgroups, int32_t* uniq, int32_t* inv,
+    int32_t* sorted_pos, int32_t* seg_start, int32_t* n_unique, int32_t* code, int32_t* miss_uidx,
+    int32_t* n_miss, void* ws, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
  * Low-rank tables.  The embedding dimension r is a capacity axis of STAPLE
  * next to the number of augmented layers, r = 512 being its low-rank variant
  * (STAPLE Table 2, row L=12, r=512; AI Radio episode, paper summary: rank

@@ -200,8 +200,15 @@ OLMO1B_OFFLOAD_TRAIN = Workload(
     notes="training batch of 32768 tokens through one layer whose table is in "
           "pinned host memory with the top-5% rows cached in HBM")
 
+OLMO1B_OFFLOAD_PREFILL = Workload(
+    name="olmo2_1b_offload_cache5_prefill_16k", d_model=2048, d_ff=8192, vocab=100352,
+    n_tokens=64 * 256, n_layers=12, cache_fraction=0.05, ids_seed=1007,
+    notes="prefill of 64 prompts of 256 tokens (16384 tokens) through the 12 "
+          "layers of the offloaded stack (the same tables and cache), in chunks")
+
 WORKLOADS = {w.name: w for w in (TINY_F32, OLMO1B_DECODE, OLMO1B_TRAIN, OLMO1B_OFFLOAD,
-                                 OLMO1B_OFFLOAD_TRAIN, OLMO7B_TRAIN, OLMO7B_DECODE)}
+                                 OLMO1B_OFFLOAD_TRAIN, OLMO7B_TRAIN, OLMO7B_DECODE,
+                                 OLMO1B_OFFLOAD_PREFILL)}
 
 
 @dataclass

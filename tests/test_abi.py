@@ -56,6 +56,9 @@ def test_workspace_queries(lib):
     assert lib.staple_dedup_workspace_bytes(4096) == 0
     assert lib.staple_dedup_workspace_bytes(32768) == radix(32768)
     assert lib.staple_dedup_workspace_bytes(4097) == radix(4097)
+    # the prefill chunk rows: the dedup's workspace
+    assert lib.staple_prefill_rows_workspace_bytes(4096) == 0
+    assert lib.staple_prefill_rows_workspace_bytes(8192) == radix(8192)
     dgu = ((100 * 256 * 2 + 255) // 256) * 256          # [dg | du] in bf16
     aux = ((100 * 128 * 4 + 255) // 256) * 256           # fp32 du, then a recomputed h
     partials = 2 * ((100 + 31) // 32) * 128 * 4            # segment-sum chunk partials
@@ -98,3 +101,21 @@ def test_invalid_arguments_are_rejected_before_device_work(lib):
                                  stage.ctypes.data, 1, null)
     assert st == -6
     assert np.all(stage == 0)
+
+
+def test_prefill_rows_rejects_bad_arguments_before_device_work(lib):
+    null, p = None, 16   # any non-null address: nothing is dereferenced before the checks
+    outs = [p] * 8
+
+    def call(n_layers, layers, n, d_ff, dtype=0, vocab=100, cap=0, wgs=0, ws_bytes=0, lookup=1):
+        return lib.staple_prefill_rows_cached(n_layers, layers, n, d_ff, dtype, p, vocab, p, cap,
+                                              lookup, wgs, *outs, null, ws_bytes, null)
+    assert call(1, p, 0, 256) == -1            # no tokens
+    assert call(0, p, 64, 256) == -1           # no layers
+    assert call(1, null, 64, 256) == -1        # no descriptors
+    assert call(1, p, 64, 256, dtype=7) == -1  # dtype
+    assert call(1, p, 64, 4, dtype=1) == -1    # a bf16 row that is not whole 16-byte vectors
+    assert call(1, p, 64, 256, wgs=-1) == -1   # workgroup cap
+    assert call(1, p, 64, 256, cap=-1) == -1   # capacity
+    assert call(1, p, 64, 256, lookup=2) == -1 # lookup is 0 or 1
+    assert call(1, p, 8192, 256) == -3         # no workspace for the multi-workgroup dedup

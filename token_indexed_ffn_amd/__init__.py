@@ -459,6 +459,61 @@ def staple_decode_step_cached(stack: DecodeStack, ids: torch.Tensor, id_to_slot:
         _ws_size(workspace), _stream(stream)), "staple_decode_step_cached")
 
 
+class _RowSource(ctypes.Structure):
+    _fields_ = [("cache_rows", ctypes.c_void_p), ("table", ctypes.c_void_p),
+                ("table_stride", ctypes.c_int64), ("rows", ctypes.c_void_p)]
+
+
+class RowSources:
+    """The per-layer row sources of staple_prefill_rows_cached, marshalled once:
+    dicts with "table" (a [vocab x d_ff] device or pinned host tensor, or a
+    (tensor, element offset, row stride) triple for tables interleaved by
+    staple_group_tables_host), "cache_rows" (device, or None without a cache)
+    and "rows" (device [n x d_ff], the layer's compact rows)."""
+
+    def __init__(self, layers: list, *, d_ff: int):
+        self.layers = [{k: lay.get(k) for k in ("cache_rows", "table", "rows")} for lay in layers]
+        descs = []
+        for lay in self.layers:
+            _dev(lay["cache_rows"], lay["rows"])
+            if lay["rows"] is None:
+                raise ValueError("every layer needs its rows")
+            tab, off, stride = (lay["table"] if isinstance(lay["table"], tuple)
+                                else (lay["table"], 0, 0))
+            if not (tab.is_cuda or tab.is_pinned()):
+                raise ValueError("table must be a device or pinned host tensor")
+            descs.append(_RowSource(_p(lay["cache_rows"]), tab.data_ptr() + off * tab.element_size(),
+                                    stride, _p(lay["rows"])))
+        self.n_layers, self.d_ff = len(layers), d_ff
+        self.dtype = _dt(self.layers[0]["rows"])
+        self.desc = (_RowSource * self.n_layers)(*descs)
+
+
+def prefill_rows_workspace_bytes(n_tokens: int) -> int:
+    return int(lib().staple_prefill_rows_workspace_bytes(n_tokens))
+
+
+def staple_prefill_rows_cached(sources: RowSources, ids: torch.Tensor, id_to_slot: torch.Tensor,
+                               capacity: int, *, dedup_out: dict, lookup_out: dict,
+                               workspace: Optional[torch.Tensor], max_workgroups: int = 0,
+                               lookup: bool = True, stream=None) -> None:
+    """The rows of one prefill chunk for every layer: dedup of `ids`, cache probe,
+    then each layer's compact rows (hits from its cache, misses from its table) in
+    one launch of at most max_workgroups workgroups (0: enough to fill the GPU).
+    lookup False: no dedup or probe; the rows from the uniq, code and n_unique an
+    earlier call on the same chunk left in dedup_out / lookup_out."""
+    _dev(ids, id_to_slot, workspace)
+    n, vocab = ids.numel(), id_to_slot.numel()
+    dd, lk = dedup_out, lookup_out
+    _check(lib().staple_prefill_rows_cached(
+        sources.n_layers, ctypes.cast(sources.desc, ctypes.c_void_p), n, sources.d_ff,
+        sources.dtype, _p(ids), vocab, _p(id_to_slot), int(capacity), int(bool(lookup)),
+        int(max_workgroups),
+        _p(dd["uniq"]), _p(dd["inv"]), _p(dd["sorted_pos"]), _p(dd["seg_start"]),
+        _p(dd["n_unique"]), _p(lk["code"]), _p(lk["miss_uidx"]), _p(lk["n_miss"]), _p(workspace),
+        _ws_size(workspace), _stream(stream)), "staple_prefill_rows_cached")
+
+
 def staple_group_tables_host(tables: list, out: Optional[torch.Tensor] = None) -> torch.Tensor:
     """The tables' rows interleaved token-major: out[t, j] = tables[j][t] (host tensors;
     out pinned when none is given)."""

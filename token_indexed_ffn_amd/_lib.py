@@ -63,6 +63,10 @@ _SIGS = {
                                           c_i64, c_vp, c_i64, c_i32, c_vp, c_vp, c_vp, c_vp, c_vp,
                                           c_vp, c_vp, c_vp, c_vp, c_sz, c_vp]),
     "staple_group_tables_host": (c_i32, [c_vp, c_i64, c_i64, c_i64, c_i32, c_vp]),
+    "staple_prefill_rows_workspace_bytes": (c_sz, [c_i64]),
+    "staple_prefill_rows_cached": (c_i32, [c_i64, c_vp, c_i64, c_i64, c_i32, c_vp, c_i64, c_vp,
+                                           c_i64, c_i32, c_i32, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp,
+                                           c_vp, c_vp, c_vp, c_sz, c_vp]),
     "staple_lowrank_expand": (c_i32, [c_vp, c_vp, c_i64, c_i64, c_i64, c_i32, c_vp, c_vp, c_vp]),
     "staple_lowrank_bwd_workspace_bytes": (c_sz, [c_i64, c_i64, c_i32]),
     "staple_lowrank_bwd": (c_i32, [c_vp, c_vp, c_vp, c_i64, c_i64, c_i64, c_i32, c_vp, c_vp, c_vp,

@@ -54,7 +54,8 @@ hipError_t launch_assemble_rows_table(const void* cache_rows, int64_t capacity, 
 hipError_t launch_assemble_rows_layers(const LayerRowSources& src, int n_layers, int64_t capacity,
                                        int64_t vocab, const int32_t* uniq, const int32_t* code,
                                        const int32_t* n_unique, int64_t max_unique,
-                                       int64_t row_bytes, hipStream_t s, int* err);
+                                       int64_t row_bytes, hipStream_t s, int* err,
+                                       unsigned max_workgroups = kLayerRowWorkgroups);
 size_t segment_sum_workspace_bytes(int64_t n_tokens, int64_t d_ff);
 hipError_t launch_segment_sum_fixup(int64_t n_tokens, int64_t d_ff, const int32_t* sorted_pos,
                                     const int32_t* inv, const int32_t* seg_start,
@@ -768,6 +769,61 @@ staple_status_t staple_decode_step_cached(
                             capacity, row_src, h, nullptr, nullptr, s, err, true, up_proj != 0,
                             L.table, vocab, L.table_stride ? L.table_stride : f));
     HIPCALL(decode_down(n, d, f, h, L.packed_down, L.y, out_dtype, down_ws, s, true));
+  }
+  return STAPLE_OK;
+}
+
+// ------------------------------------------------------------------ prefill chunk rows
+size_t staple_prefill_rows_workspace_bytes(int64_t n) {
+  return n < 1 || n > 0x7fffffffll ? 0 : align_up(dedup_workspace_bytes(n), 256);
+}
+
+staple_status_t staple_prefill_rows_cached(
+    int64_t n_layers, const staple_row_source_t* layers, int64_t n, int64_t d_ff, int32_t dtype,
+    const int32_t* ids, int64_t vocab, const int32_t* id_to_slot, int64_t capacity,
+    int32_t lookup, int32_t max_workgroups, int32_t* uniq, int32_t* inv, int32_t* sorted_pos,
+    int32_t* seg_start, int32_t* n_unique, int32_t* code, int32_t* miss_uidx, int32_t* n_miss,
+    void* ws, size_t ws_bytes, void* stream) {
+  REQUIRE(valid_dtype(dtype) && d_ff > 0 && (d_ff * elem_bytes(dtype)) % 16 == 0);
+  REQUIRE(n >= 1 && n <= 0x7fffffffll && vocab >= 1 && vocab <= 0x7fffffffll);
+  REQUIRE(capacity >= 0 && capacity <= 0x7fffffffll && max_workgroups >= 0);
+  REQUIRE(lookup == 0 || lookup == 1);
+  REQUIRE(n_layers >= 1 && n_layers <= 4096 && layers);
+  REQUIRE(ids && id_to_slot && uniq && inv && sorted_pos && seg_start && n_unique && code &&
+          miss_uidx && n_miss);
+  const size_t need = staple_prefill_rows_workspace_bytes(n);
+  if (ws_bytes < need) return STAPLE_ERR_WORKSPACE;
+  REQUIRE(need == 0 || (ws && aligned16(ws)));
+  for (int64_t l = 0; l < n_layers; ++l) {
+    const staple_row_source_t& L = layers[l];
+    REQUIRE(L.table && L.rows && (capacity == 0 || L.cache_rows));
+    REQUIRE(aligned16(L.table) && aligned16(L.rows) && (capacity == 0 || aligned16(L.cache_rows)));
+    REQUIRE(L.table_stride == 0 ||
+            (L.table_stride >= d_ff && (L.table_stride * elem_bytes(dtype)) % 16 == 0));
+    REQUIRE(device_addressable(L.table) && device_addressable(L.rows));
+  }
+  GET_ERR(err);
+  hipStream_t s = S(stream);
+  const int64_t row_bytes = d_ff * elem_bytes(dtype);
+  if (lookup) {
+    HIPCALL(launch_dedup(ids, n, vocab, uniq, inv, sorted_pos, seg_start, n_unique, ws, s, err));
+    HIPCALL(launch_cache_lookup(uniq, n_unique, n, id_to_slot, vocab, code, miss_uidx, nullptr,
+                                n_miss, s, err));
+  }
+  const unsigned wgs = max_workgroups > 0 ? static_cast<unsigned>(max_workgroups) : kLayerRowWorkgroups;
+  LayerRowSources src{};
+  int cnt = 0;
+  for (int64_t l = 0; l < n_layers; ++l) {
+    const staple_row_source_t& L = layers[l];
+    src.cache_rows[cnt] = L.cache_rows;
+    src.table[cnt] = L.table;
+    src.table_ld[cnt] = (L.table_stride ? L.table_stride : d_ff) * elem_bytes(dtype);
+    src.rows[cnt] = L.rows;
+    if (++cnt == kMaxAssembleLayers || l + 1 == n_layers) {
+      HIPCALL(launch_assemble_rows_layers(src, cnt, capacity, vocab, uniq, code, n_unique, n,
+                                          row_bytes, s, err, wgs));
+      cnt = 0;
+    }
   }
   return STAPLE_OK;
 }

@@ -328,48 +328,115 @@ hipError_t launch_assemble_rows_table(const void* cache_rows, int64_t capacity, 
 
 // The same assembly for several layers at once (the tables of a layer stack
 // share one cache map): work item k = (layer k / max_unique, unique row
-// k % max_unique), one row per workgroup, so the PCIe reads of every layer's
-// misses are in flight together.  Table l's token rows are table_ld[l] bytes
-// apart (row_bytes for a table of its own, more when several layers' tables
-// are interleaved token-major).
+// k % max_unique).  A workgroup takes kLayerRowsInFlight consecutive work
+// items and loads all of their rows before storing any, so that many rows'
+// PCIe reads are in flight per workgroup and a capped grid (running beside
+// another kernel on a few CUs) still keeps the link busy.  Table l's token
+// rows are table_ld[l] bytes apart (row_bytes for a table of its own, more
+// when several layers' tables are interleaved token-major).
+constexpr int kLayerRowsInFlight = 4;
+
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+typedef const __attribute__((address_space(1))) u32x4_t* grow_src_t;
+typedef __attribute__((address_space(1))) u32x4_t* grow_dst_t;
+
+// Source and destination of work item k of a multi-layer assembly, or false
+// when it has nothing to copy (past the unique rows, or a bad slot or ID,
+// which it flags).  Global-address-space pointers: device memory or pinned
+// host memory mapped for the device.
+__device__ __forceinline__ bool layer_row_ends(const LayerRowSources& src, int64_t k, int64_t total,
+                                               int64_t n, int64_t max_unique, int64_t capacity,
+                                               int64_t vocab, const int32_t* uniq,
+                                               const int32_t* code, int64_t row_bytes, int* err,
+                                               grow_src_t& from, grow_dst_t& to) {
+  if (k >= total) return false;
+  const int l = static_cast<int>(k / max_unique);
+  const int64_t u = k - static_cast<int64_t>(l) * max_unique;
+  if (u >= n) return false;
+  const int32_t c = code[u];
+  const char* f;
+  if (c >= 0) {
+    if (c >= capacity) {
+      if (threadIdx.x == 0) flag_index_error(err);
+      return false;
+    }
+    f = static_cast<const char*>(src.cache_rows[l]) + c * row_bytes;
+  } else {
+    const int32_t id = uniq[u];
+    if (id < 0 || id >= vocab) {
+      if (threadIdx.x == 0) flag_index_error(err);
+      return false;
+    }
+    f = static_cast<const char*>(src.table[l]) + id * src.table_ld[l];
+  }
+  from = (grow_src_t)(f);
+  to = (grow_dst_t)(static_cast<char*>(src.rows[l]) + u * row_bytes);
+  return true;
+}
+
 __global__ __launch_bounds__(kRowThreads) void assemble_rows_layers_kernel(
     LayerRowSources src, int n_layers, int64_t capacity, int64_t vocab, const int32_t* uniq,
     const int32_t* code, const int32_t* n_unique_p, int64_t max_unique, int64_t row_bytes,
     int* err) {
   const int64_t n = min(static_cast<int64_t>(*n_unique_p), max_unique);
   const int64_t total = static_cast<int64_t>(n_layers) * max_unique;
-  for (int64_t k = blockIdx.x; k < total; k += gridDim.x) {
-    const int l = static_cast<int>(k / max_unique);
-    const int64_t u = k - static_cast<int64_t>(l) * max_unique;
-    if (u >= n) continue;
-    const int32_t c = code[u];
-    const char* from;
-    if (c >= 0) {
-      if (c >= capacity) {
-        if (threadIdx.x == 0) flag_index_error(err);
-        continue;
+  const int64_t vecs = row_bytes / 16;
+  for (int64_t k0 = static_cast<int64_t>(blockIdx.x) * kLayerRowsInFlight; k0 < total;
+       k0 += static_cast<int64_t>(gridDim.x) * kLayerRowsInFlight) {
+    grow_src_t f[kLayerRowsInFlight] = {};
+    grow_dst_t d[kLayerRowsInFlight] = {};
+    bool ok[kLayerRowsInFlight];
+#pragma unroll
+    for (int j = 0; j < kLayerRowsInFlight; ++j)
+      ok[j] = layer_row_ends(src, k0 + j, total, n, max_unique, capacity, vocab, uniq, code,
+                             row_bytes, err, f[j], d[j]);
+    // a group with nothing to copy is skipped; an empty place of a group
+    // repeats its first row (the same bytes to the same place, by the same
+    // thread), so the copy below needs no per-row predicate
+    int first = -1;
+#pragma unroll
+    for (int j = kLayerRowsInFlight - 1; j >= 0; --j)
+      if (ok[j]) first = j;
+    if (first < 0) continue;
+#pragma unroll
+    for (int j = 0; j < kLayerRowsInFlight; ++j) {
+      if (!ok[j]) {
+        f[j] = f[first];
+        d[j] = d[first];
       }
-      from = static_cast<const char*>(src.cache_rows[l]) + c * row_bytes;
-    } else {
-      const int32_t id = uniq[u];
-      if (id < 0 || id >= vocab) {
-        if (threadIdx.x == 0) flag_index_error(err);
-        continue;
-      }
-      from = static_cast<const char*>(src.table[l]) + id * src.table_ld[l];
     }
-    copy_row16(reinterpret_cast<const uint4*>(from),
-               reinterpret_cast<uint4*>(static_cast<char*>(src.rows[l]) + u * row_bytes),
-               row_bytes / 16);
+    // whole passes of 4 pieces per thread: every row's pieces loaded, then stored
+    int64_t v0 = 0;
+    for (; v0 + 4 * kRowThreads <= vecs; v0 += 4 * kRowThreads) {
+      u32x4_t t[kLayerRowsInFlight][4];
+#pragma unroll
+      for (int j = 0; j < kLayerRowsInFlight; ++j)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) t[j][i] = f[j][v0 + threadIdx.x + i * kRowThreads];
+#pragma unroll
+      for (int j = 0; j < kLayerRowsInFlight; ++j)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) d[j][v0 + threadIdx.x + i * kRowThreads] = t[j][i];
+    }
+    for (int64_t v = v0 + threadIdx.x; v < vecs; v += kRowThreads) {
+      u32x4_t t[kLayerRowsInFlight];
+#pragma unroll
+      for (int j = 0; j < kLayerRowsInFlight; ++j) t[j] = f[j][v];
+#pragma unroll
+      for (int j = 0; j < kLayerRowsInFlight; ++j) d[j][v] = t[j];
+    }
   }
 }
 
 hipError_t launch_assemble_rows_layers(const LayerRowSources& src, int n_layers, int64_t capacity,
                                        int64_t vocab, const int32_t* uniq, const int32_t* code,
                                        const int32_t* n_unique, int64_t max_unique,
-                                       int64_t row_bytes, hipStream_t s, int* err) {
+                                       int64_t row_bytes, hipStream_t s, int* err,
+                                       unsigned max_workgroups) {
   if (max_unique == 0 || n_layers == 0) return hipSuccess;
-  assemble_rows_layers_kernel<<<dim3(row_grid(n_layers * max_unique, kLayerRowWorkgroups)),
+  const int64_t groups = (static_cast<int64_t>(n_layers) * max_unique + kLayerRowsInFlight - 1) /
+                        kLayerRowsInFlight;
+  assemble_rows_layers_kernel<<<dim3(row_grid(groups, max_workgroups)),
                                 dim3(kRowThreads), 0, s>>>(src, n_layers, capacity, vocab, uniq,
                                                             code, n_unique, max_unique, row_bytes,
                                                             err);
