@@ -328,13 +328,17 @@ hipError_t launch_assemble_rows_table(const void* cache_rows, int64_t capacity, 
 
 // The same assembly for several layers at once (the tables of a layer stack
 // share one cache map): work item k = (layer k / max_unique, unique row
-// k % max_unique).  A workgroup takes kLayerRowsInFlight consecutive work
-// items and loads all of their rows before storing any, so that many rows'
-// PCIe reads are in flight per workgroup and a capped grid (running beside
-// another kernel on a few CUs) still keeps the link busy.  Table l's token
-// rows are table_ld[l] bytes apart (row_bytes for a table of its own, more
-// when several layers' tables are interleaved token-major).
-constexpr int kLayerRowsInFlight = 4;
+// k % max_unique).  A workgroup takes R consecutive work items and loads all
+// of their rows before storing any.  R = 4 when the grid is capped to run
+// beside another kernel on a few CUs, or when there are enough items for
+// four per workgroup to fill the grid: many rows' PCIe reads are then in
+// flight per workgroup.  R = 1 otherwise (a decode step's few rows spread
+// over as many workgroups as possible).  Table l's token rows are
+// table_ld[l] bytes apart (row_bytes for a table of its own, more when
+// several layers' tables are interleaved token-major).
+
+// a grid capped below this many workgroups shares the GPU with another kernel
+constexpr unsigned kRowDeepCap = 256;
 
 typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 typedef const __attribute__((address_space(1))) u32x4_t* grow_src_t;
@@ -374,6 +378,7 @@ __device__ __forceinline__ bool layer_row_ends(const LayerRowSources& src, int64
   return true;
 }
 
+template <int R>
 __global__ __launch_bounds__(kRowThreads) void assemble_rows_layers_kernel(
     LayerRowSources src, int n_layers, int64_t capacity, int64_t vocab, const int32_t* uniq,
     const int32_t* code, const int32_t* n_unique_p, int64_t max_unique, int64_t row_bytes,
@@ -381,13 +386,13 @@ __global__ __launch_bounds__(kRowThreads) void assemble_rows_layers_kernel(
   const int64_t n = min(static_cast<int64_t>(*n_unique_p), max_unique);
   const int64_t total = static_cast<int64_t>(n_layers) * max_unique;
   const int64_t vecs = row_bytes / 16;
-  for (int64_t k0 = static_cast<int64_t>(blockIdx.x) * kLayerRowsInFlight; k0 < total;
-       k0 += static_cast<int64_t>(gridDim.x) * kLayerRowsInFlight) {
-    grow_src_t f[kLayerRowsInFlight] = {};
-    grow_dst_t d[kLayerRowsInFlight] = {};
-    bool ok[kLayerRowsInFlight];
+  for (int64_t k0 = static_cast<int64_t>(blockIdx.x) * R; k0 < total;
+       k0 += static_cast<int64_t>(gridDim.x) * R) {
+    grow_src_t f[R] = {};
+    grow_dst_t d[R] = {};
+    bool ok[R];
 #pragma unroll
-    for (int j = 0; j < kLayerRowsInFlight; ++j)
+    for (int j = 0; j < R; ++j)
       ok[j] = layer_row_ends(src, k0 + j, total, n, max_unique, capacity, vocab, uniq, code,
                              row_bytes, err, f[j], d[j]);
     // a group with nothing to copy is skipped; an empty place of a group
@@ -395,11 +400,11 @@ __global__ __launch_bounds__(kRowThreads) void assemble_rows_layers_kernel(
     // thread), so the copy below needs no per-row predicate
     int first = -1;
 #pragma unroll
-    for (int j = kLayerRowsInFlight - 1; j >= 0; --j)
+    for (int j = R - 1; j >= 0; --j)
       if (ok[j]) first = j;
     if (first < 0) continue;
 #pragma unroll
-    for (int j = 0; j < kLayerRowsInFlight; ++j) {
+    for (int j = 0; j < R; ++j) {
       if (!ok[j]) {
         f[j] = f[first];
         d[j] = d[first];
@@ -408,22 +413,22 @@ __global__ __launch_bounds__(kRowThreads) void assemble_rows_layers_kernel(
     // whole passes of 4 pieces per thread: every row's pieces loaded, then stored
     int64_t v0 = 0;
     for (; v0 + 4 * kRowThreads <= vecs; v0 += 4 * kRowThreads) {
-      u32x4_t t[kLayerRowsInFlight][4];
+      u32x4_t t[R][4];
 #pragma unroll
-      for (int j = 0; j < kLayerRowsInFlight; ++j)
+      for (int j = 0; j < R; ++j)
 #pragma unroll
         for (int i = 0; i < 4; ++i) t[j][i] = f[j][v0 + threadIdx.x + i * kRowThreads];
 #pragma unroll
-      for (int j = 0; j < kLayerRowsInFlight; ++j)
+      for (int j = 0; j < R; ++j)
 #pragma unroll
         for (int i = 0; i < 4; ++i) d[j][v0 + threadIdx.x + i * kRowThreads] = t[j][i];
     }
     for (int64_t v = v0 + threadIdx.x; v < vecs; v += kRowThreads) {
-      u32x4_t t[kLayerRowsInFlight];
+      u32x4_t t[R];
 #pragma unroll
-      for (int j = 0; j < kLayerRowsInFlight; ++j) t[j] = f[j][v];
+      for (int j = 0; j < R; ++j) t[j] = f[j][v];
 #pragma unroll
-      for (int j = 0; j < kLayerRowsInFlight; ++j) d[j][v] = t[j];
+      for (int j = 0; j < R; ++j) d[j][v] = t[j];
     }
   }
 }
@@ -434,12 +439,16 @@ hipError_t launch_assemble_rows_layers(const LayerRowSources& src, int n_layers,
                                        int64_t row_bytes, hipStream_t s, int* err,
                                        unsigned max_workgroups) {
   if (max_unique == 0 || n_layers == 0) return hipSuccess;
-  const int64_t groups = (static_cast<int64_t>(n_layers) * max_unique + kLayerRowsInFlight - 1) /
-                        kLayerRowsInFlight;
-  assemble_rows_layers_kernel<<<dim3(row_grid(groups, max_workgroups)),
-                                dim3(kRowThreads), 0, s>>>(src, n_layers, capacity, vocab, uniq,
-                                                            code, n_unique, max_unique, row_bytes,
-                                                            err);
+  const int64_t items = static_cast<int64_t>(n_layers) * max_unique;
+  const int64_t groups4 = (items + 3) / 4;
+  if (max_workgroups < kRowDeepCap || groups4 >= max_workgroups)
+    assemble_rows_layers_kernel<4><<<dim3(row_grid(groups4, max_workgroups)), dim3(kRowThreads), 0,
+                                     s>>>(src, n_layers, capacity, vocab, uniq, code, n_unique,
+                                          max_unique, row_bytes, err);
+  else
+    assemble_rows_layers_kernel<1><<<dim3(row_grid(items, max_workgroups)), dim3(kRowThreads), 0,
+                                     s>>>(src, n_layers, capacity, vocab, uniq, code, n_unique,
+                                          max_unique, row_bytes, err);
   return hipGetLastError();
 }
 
