@@ -50,6 +50,9 @@ BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, published
 PROFILES = os.path.join(ROOT, "profiles")
 
 
+WORKLOADS = ("decode", "train", "stem", "decode7b", "train7b", "offload", "prefill", "lowrank")
+
+
 def parse_args(argv=None):
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -57,13 +60,18 @@ def parse_args(argv=None):
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--train-steps", type=int, default=10)
     ap.add_argument("--train-warmup", type=int, default=3)
-    ap.add_argument("--workloads", default="decode,train,stem,decode7b,train7b,offload,prefill,lowrank")
+    ap.add_argument("--workloads", default=",".join(WORKLOADS),
+                    help="comma-separated subset of %(default)s")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=8.0,
                     help="target CPU time of each oracle baseline sample")
     ap.add_argument("--mode", default="bench", choices=["bench", "copy"],
                     help="copy: run a plain 1 GiB device copy (counter calibration)")
-    return ap.parse_args(argv)
+    args = ap.parse_args(argv)
+    unknown = sorted(set(args.workloads.split(",")) - set(WORKLOADS))
+    if unknown:
+        ap.error(f"unknown workloads {', '.join(unknown)}; choose from {', '.join(WORKLOADS)}")
+    return args
 
 
 def source_sha(*names) -> str:
