@@ -1323,8 +1323,9 @@ def test_decode_step_driver_refuses_bad_arguments(st, dev):
     d, f, vocab = 64, 64, 10
     t = lambda *sh, **kw: torch.zeros(*sh, dtype=kw.get("dtype", torch.bfloat16), device=dev)
     host_table = torch.zeros(vocab, f, dtype=torch.bfloat16).pin_memory()
-    lay = {"x": t(64, d), "packed_gate_up": t(2 * f * d), "packed_down": t(f * d),
-           "cache_rows": t(1, f), "table": host_table, "rows": t(64, f), "y": t(64, d)}
+    # buffers for 65 tokens, so that the library's own check of the batch is reached
+    lay = {"x": t(65, d), "packed_gate_up": t(2 * f * d), "packed_down": t(f * d),
+           "cache_rows": t(1, f), "table": host_table, "rows": t(65, f), "y": t(65, d)}
     stack = st.DecodeStack([lay], d_model=d, d_ff=f, n_tokens=64)
     i32 = dict(dtype=torch.int32)
     dd = {k: t(66, **i32) for k in ("uniq", "inv", "sorted_pos", "seg_start", "n_unique")}

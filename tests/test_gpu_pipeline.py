@@ -306,3 +306,39 @@ def test_decode_step_graph_replays_match_eager(st, dev, group, in_place):
     of = O.ffn_forward(g["x"], g["w_gate"], g["w_up"], g["w_down"], g["table"], ids_np,
                        precision=O.BF16)
     assert_close(to_np(g_lays[L - 1]["y"]), of["y"], "graph-replayed decode y")
+
+
+def test_prefill_rows_refuses_short_outputs_and_mixed_dtypes(st, dev):
+    """Outputs or rows shorter than the chunk, a cache shorter than the
+    capacity, and tables of another dtype are refused on the host; nothing is
+    written."""
+    import torch
+    n, f, vocab, cap = 100, 64, 50, 4
+    table = torch.zeros(vocab, f, dtype=torch.bfloat16).pin_memory()
+    cache = torch.zeros(cap, f, dtype=torch.bfloat16, device=dev)
+    rows = torch.zeros(n, f, dtype=torch.bfloat16, device=dev)
+    i2s = torch.full((vocab,), -1, dtype=torch.int32, device=dev)
+    ids = torch.zeros(n, dtype=torch.int32, device=dev)
+    rs = st.RowSources([{"table": table, "cache_rows": cache, "rows": rows}], d_ff=f)
+    dd, lk = _outputs(torch, n, dev)
+    kw = dict(dedup_out=dd, lookup_out=lk, workspace=None)
+    short = dict(dd, uniq=dd["uniq"][: n - 1])
+    with pytest.raises(ValueError, match="uniq"):
+        st.staple_prefill_rows_cached(rs, ids, i2s, cap, **dict(kw, dedup_out=short))
+    with pytest.raises(ValueError, match="seg_start"):
+        st.staple_prefill_rows_cached(rs, ids, i2s, cap,
+                                      **dict(kw, dedup_out=dict(dd, seg_start=dd["seg_start"][:n])))
+    with pytest.raises(ValueError, match="cache_rows"):
+        st.staple_prefill_rows_cached(rs, ids, i2s, cap + 1, **kw)
+    with pytest.raises(ValueError, match="ids"):
+        st.staple_prefill_rows_cached(rs, ids.to(torch.int64), i2s, cap, **kw)
+    with pytest.raises(ValueError, match="rows"):
+        st.staple_prefill_rows_cached(rs, torch.zeros(n + 1, dtype=torch.int32, device=dev), i2s,
+                                      cap, **dict(kw, **{k: v for k, v in
+                                                        zip(("dedup_out", "lookup_out"),
+                                                            _outputs(torch, n + 1, dev))}))
+    with pytest.raises(ValueError, match="dtype"):
+        st.RowSources([{"table": table.float().pin_memory(), "cache_rows": cache, "rows": rows}],
+                      d_ff=f)
+    torch.cuda.synchronize()
+    assert not rows.any()

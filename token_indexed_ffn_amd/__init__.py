@@ -75,6 +75,23 @@ def _ws_size(w: Optional[torch.Tensor]) -> int:
     return 0 if w is None else w.numel() * w.element_size()
 
 
+def _need(t: torch.Tensor, n: int, what: str, dtype=torch.int32) -> None:
+    """A caller-provided output or index array: dtype and at least n elements (the
+    kernels write up to that many; a shorter buffer would be written past its end)."""
+    if t.dtype != dtype or t.numel() < n:
+        raise ValueError(f"{what}: needs {n} {dtype} elements, got {t.numel()} {t.dtype}")
+
+
+def _step_outputs(dd: dict, lk: dict, n: int) -> None:
+    for k in ("uniq", "inv", "sorted_pos"):
+        _need(dd[k], n, k)
+    _need(dd["seg_start"], n + 1, "seg_start")
+    _need(dd["n_unique"], 1, "n_unique")
+    for k in ("code", "miss_uidx"):
+        _need(lk[k], n, k)
+    _need(lk["n_miss"], 1, "n_miss")
+
+
 # ----------------------------------------------------------------------------
 def staple_get_device_error(stream=None) -> int:
     """Synchronises the stream and returns (and clears) the device error status."""
@@ -451,6 +468,20 @@ def staple_decode_step_cached(stack: DecodeStack, ids: torch.Tensor, id_to_slot:
     n = ids.numel()
     vocab = id_to_slot.numel()
     dd, lk = dedup_out, lookup_out
+    _dev(ids, id_to_slot, workspace)
+    _need(ids, n, "ids")
+    _need(id_to_slot, vocab, "id_to_slot")
+    _step_outputs(dd, lk, n)
+    for lay in stack.layers:
+        if lay["x"].numel() < n * stack.d_model:
+            raise ValueError(f"each layer's x needs {n} rows")
+        if lay["rows"] is not None and lay["rows"].numel() < n * stack.d_ff:
+            raise ValueError(f"each layer's rows need {n} rows")
+        if lay["y"].numel() < n * stack.d_model:
+            raise ValueError(f"each layer's y needs {n} rows")
+        if capacity > 0 and (lay["cache_rows"] is None
+                             or lay["cache_rows"].numel() < capacity * stack.d_ff):
+            raise ValueError("each layer's cache_rows need `capacity` rows")
     _check(lib().staple_decode_step_cached(
         stack.n_layers, ctypes.cast(stack.desc, ctypes.c_void_p), n, stack.d_model, stack.d_ff,
         stack.up_proj, stack.out_dtype, _p(ids), vocab, _p(id_to_slot), int(capacity), int(group),
@@ -473,6 +504,9 @@ class RowSources:
 
     def __init__(self, layers: list, *, d_ff: int):
         self.layers = [{k: lay.get(k) for k in ("cache_rows", "table", "rows")} for lay in layers]
+        if not self.layers or self.layers[0]["rows"] is None:
+            raise ValueError("every layer needs its rows")
+        dt = self.layers[0]["rows"].dtype
         descs = []
         for lay in self.layers:
             _dev(lay["cache_rows"], lay["rows"])
@@ -482,6 +516,14 @@ class RowSources:
                                 else (lay["table"], 0, 0))
             if not (tab.is_cuda or tab.is_pinned()):
                 raise ValueError("table must be a device or pinned host tensor")
+            for t in (lay["rows"], lay["cache_rows"], tab):
+                if t is not None and t.dtype != dt:
+                    raise ValueError("tables, caches and rows must share one dtype")
+            for t in (lay["rows"], lay["cache_rows"]):
+                if t is not None and (t.dim() != 2 or t.shape[1] != d_ff):
+                    raise ValueError("rows and cache_rows are [rows x d_ff]")
+            if not isinstance(lay["table"], tuple) and (tab.dim() != 2 or tab.shape[1] != d_ff):
+                raise ValueError("table is [vocab x d_ff]")
             descs.append(_RowSource(_p(lay["cache_rows"]), tab.data_ptr() + off * tab.element_size(),
                                     stride, _p(lay["rows"])))
         self.n_layers, self.d_ff = len(layers), d_ff
@@ -505,6 +547,16 @@ def staple_prefill_rows_cached(sources: RowSources, ids: torch.Tensor, id_to_slo
     _dev(ids, id_to_slot, workspace)
     n, vocab = ids.numel(), id_to_slot.numel()
     dd, lk = dedup_out, lookup_out
+    _need(ids, n, "ids")
+    _need(id_to_slot, vocab, "id_to_slot")
+    _step_outputs(dd, lk, n)
+    for lay in sources.layers:
+        if lay["rows"].shape[0] < n:
+            raise ValueError(f"each layer's rows need {n} rows")
+        if capacity > 0 and (lay["cache_rows"] is None or lay["cache_rows"].shape[0] < capacity):
+            raise ValueError("each layer's cache_rows need `capacity` rows")
+        if not isinstance(lay["table"], tuple) and lay["table"].shape[0] < vocab:
+            raise ValueError("each layer's table needs id_to_slot's vocabulary")
     _check(lib().staple_prefill_rows_cached(
         sources.n_layers, ctypes.cast(sources.desc, ctypes.c_void_p), n, sources.d_ff,
         sources.dtype, _p(ids), vocab, _p(id_to_slot), int(capacity), int(bool(lookup)),
