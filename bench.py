@@ -1053,7 +1053,9 @@ def run_offload_prefill(torch, st, w, O, steps, warmup, chunk=4096, workgroups=(
             "roofline": {
                 "kernel": "gemm_kernel<bf16,GateUp> (staple_ffn_gate_up, one 4096-token chunk)",
                 "bound": "mfma", "achieved": achieved, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                "frac": achieved / BF16_PEAK_TFLOPS, "traffic": None,
+                "frac": achieved / BF16_PEAK_TFLOPS,
+                "traffic": traffic_from_profile(f"prefill_gate_up/{w.name}",
+                                                source_sha("gemm.hip", "common.h")),
                 "avg_launch_us": gu_us, "algorithmic_flops_per_launch": gu_flops},
             "note": "forward only (prefill), eager launches; FLOPs 6 N d f per layer. "
                     "rows_alone_ms: every chunk's rows on the full grid with nothing beside them; "
