@@ -342,3 +342,36 @@ def test_prefill_rows_refuses_short_outputs_and_mixed_dtypes(st, dev):
                       d_ff=f)
     torch.cuda.synchronize()
     assert not rows.any()
+
+
+def test_prefill_rows_of_a_stack_longer_than_one_launch(st, dev):
+    """Forty layers: the rows are assembled in launches of at most 32 layers;
+    every layer's rows are its own table's rows (some layers cached, the
+    tables in pinned host memory and on the device)."""
+    import torch
+    L, n, f, vocab, cap = 40, 300, 64, 200, 10
+    _log(f"prefill rows over {L} layers")
+    counts = st.staple_cache_count(torch.from_numpy(S.zipf_ids(5000, vocab, 8)).to(dev), vocab)
+    i2s, s2i = st.staple_cache_build(counts, cap)
+    rng = np.random.default_rng(5)
+    hosts = [rng.integers(0, 1 << 16, size=(vocab, f), dtype=np.uint16) for _ in range(L)]
+    srcs = []
+    for l, tb in enumerate(hosts):
+        t = torch.from_numpy(tb.view(np.int16)).view(torch.bfloat16)
+        tab = t.pin_memory() if l % 2 == 0 else t.to(dev)
+        srcs.append({"table": tab, "cache_rows": st.staple_cache_fill(tab, s2i, cap),
+                     "rows": torch.zeros(n, f, dtype=torch.bfloat16, device=dev)})
+    rs = st.RowSources(srcs, d_ff=f)
+    ids_np = S.zipf_ids(n, vocab, 41)
+    dd, lk = _outputs(torch, n, dev)
+    st.staple_prefill_rows_cached(rs, torch.from_numpy(ids_np).to(dev), i2s, cap, dedup_out=dd,
+                                  lookup_out=lk, workspace=_workspace(torch, st, n, dev),
+                                  max_workgroups=5)
+    torch.cuda.synchronize()
+    _no_device_error(st)
+    uniq = np.unique(ids_np)
+    u = len(uniq)
+    assert int(dd["n_unique"].item()) == u
+    for l in range(L):
+        got = srcs[l]["rows"][:u].view(torch.int16).cpu().numpy().view(np.uint16)
+        assert np.array_equal(got, hosts[l][uniq]), f"layer {l}"
