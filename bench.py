@@ -601,6 +601,15 @@ def train_cpu_baseline(torch, w, T, seconds):
 # ----------------------------------------------------------------------------
 # Host-offloaded tables with the HBM row cache (decode batch and training batch)
 # ----------------------------------------------------------------------------
+def _stream_pair(torch, k=2):
+    """k streams for work that must overlap: consecutive streams of torch's pool.
+    Streams share the process's few hardware queues (four on this machine);
+    the default stream and a stream taken from the pool can land on the same
+    queue, depending on how many streams the process has asked for before,
+    and then run one after the other."""
+    return tuple(torch.cuda.Stream() for _ in range(k))
+
+
 def setup_offload(torch, st, w, n_layers):
     """Pinned host tables (one per layer), the calibration-ranked HBM cache and
     per-layer cached rows."""
@@ -879,6 +888,14 @@ def run_offload_decode(torch, st, w, steps, warmup, O=None):
 
 
 def run_offload_prefill(torch, st, w, O, steps, warmup, chunk=4096, workgroups=(16, 32, 64)):
+    main, side = _stream_pair(torch)
+    with torch.cuda.stream(main):
+        out = _run_offload_prefill(torch, st, w, O, steps, warmup, chunk, workgroups, main, side)
+    torch.cuda.synchronize()
+    return out
+
+
+def _run_offload_prefill(torch, st, w, O, steps, warmup, chunk, workgroups, main, side):
     """Prefill of w.n_tokens tokens through w.n_layers layers whose tables are in
     pinned host memory (top-5% rows cached in HBM), in chunks of `chunk` tokens.
     Each chunk's rows come from one staple_prefill_rows_cached call (dedup, cache
@@ -925,7 +942,6 @@ def run_offload_prefill(torch, st, w, O, steps, warmup, chunk=4096, workgroups=(
     pre = [buffers() for _ in range(nc)]
     fwd_ws = torch.empty(st.lib().staple_ffn_fwd_workspace_bytes(C, d, f, 1), dtype=torch.uint8,
                          device=dev)
-    main, side = torch.cuda.current_stream(), torch.cuda.Stream()
     ready = [torch.cuda.Event() for _ in range(nc)]
     done = [torch.cuda.Event() for _ in range(nc)]
     layer_ready = [torch.cuda.Event() for _ in range(L)]
@@ -1063,6 +1079,15 @@ def run_offload_prefill(torch, st, w, O, steps, warmup, chunk=4096, workgroups=(
 
 
 def run_offload_train(torch, st, w, steps, warmup):
+    # the step, the miss-row copy, the host update's refreshes
+    main, side, copy = _stream_pair(torch, 3)
+    with torch.cuda.stream(main):
+        out = _run_offload_train(torch, st, w, steps, warmup, main, side, copy)
+    torch.cuda.synchronize()
+    return out
+
+
+def _run_offload_train(torch, st, w, steps, warmup, main, side, copy):
     import numpy as np
     from staple_synth import device_normal
     dev = torch.device("cuda:0")
@@ -1078,8 +1103,6 @@ def run_offload_train(torch, st, w, steps, warmup):
     sp_out["counts"] = torch.empty(2, **i32)
     staging = torch.empty(n, f, dtype=torch.bfloat16, pin_memory=True)
     dev_miss = torch.empty(n, f, dtype=torch.bfloat16, device=dev)
-    side = torch.cuda.Stream()
-    main = torch.cuda.current_stream()
     ev_copy0, ev_copy1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     ev_gu0, ev_gu1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     ev_ready = torch.cuda.Event()
@@ -1157,7 +1180,7 @@ def run_offload_train(torch, st, w, steps, warmup):
     mode = min(("staged", "direct"), key=lambda k: res[k][0])
     ms_free, _, _, m = res[mode]
     ms_res = res["resident"][0]
-    opt = run_offload_train_optimizer(torch, st, O, T, lk_out, step, mode, steps, warmup)
+    opt = run_offload_train_optimizer(torch, st, O, T, lk_out, step, mode, steps, warmup, copy)
     ms = opt["overlapped_ms_per_step"]
     opt["ratio_to_optimizer_free_step"] = ms / ms_free
     opt["serial_ratio_to_optimizer_free_step"] = opt["serial_ms_per_step"] / ms_free
@@ -1195,7 +1218,7 @@ def run_offload_train(torch, st, w, steps, warmup):
     return out
 
 
-def run_offload_train_optimizer(torch, st, O, T, lk_out, step, mode, steps, warmup):
+def run_offload_train_optimizer(torch, st, O, T, lk_out, step, mode, steps, warmup, copy_s):
     """The offloaded training step with the AdamW update of the table rows on
     the host (bf16 table, fp32 moments in host memory; STAPLE Figure 4
     caption), in two schedules:
@@ -1222,7 +1245,6 @@ def run_offload_train_optimizer(torch, st, O, T, lk_out, step, mode, steps, warm
              "bwd": dict(T["bwd"], d_rows=torch.empty_like(T["bwd"]["d_rows"]))}
             for _ in range(2)]
     main = torch.cuda.current_stream()
-    copy_s = torch.cuda.Stream()
     grad_h = torch.empty(n, f, dtype=torch.float32, pin_memory=True)
     uniq_h = torch.empty(n, dtype=torch.int32, pin_memory=True)
     t_step = [0]

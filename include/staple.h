@@ -636,9 +636,13 @@ staple_status_t staple_cache_refresh(const void* table, int64_t vocab, int64_t d
  *     d_ff floats.  code, cache_rows, capacity: the batch's cache probe
  *     (staple_cache_lookup's code) and the HBM cache; when code is not NULL
  *     and capacity > 0 the worker also refreshes the cached copies of each
- *     updated chunk (staple_cache_refresh's operation, on a stream of the
- *     handle; the table must then be pinned).  A second start before finish
- *     returns STAPLE_ERR_INVALID_ARGUMENT.
+ *     updated chunk (staple_cache_refresh's operation, launched on
+ *     copy_stream; the table must then be pinned).  copy_stream is made to
+ *     wait for the rows-ready event first; give it a stream that does not
+ *     carry the training step, so that the refreshes run beside the step
+ *     (streams share a few hardware queues: two streams taken one after the
+ *     other from a pool usually land on different ones).  A second start
+ *     before finish returns STAPLE_ERR_INVALID_ARGUMENT.
  *   staple_host_adamw_finish: waits for the host update and returns its
  *     status (STAPLE_ERR_HOST for an ID outside the table,
  *     STAPLE_ERR_INDEX_RANGE for a row count past max_rows: nothing

@@ -416,7 +416,6 @@ struct staple_host_adamw {
   int32_t* meta_host = nullptr;    // pinned [1 + max_rows]: the row count, then the row IDs
   hipEvent_t ev_rows = nullptr, ev_meta = nullptr, ev_done = nullptr;
   hipEvent_t ev_chunk[kChunks] = {};
-  hipStream_t refresh = nullptr;   // the cache refreshes, beside the copies
   SdmaCopier sdma;                 // the gradient chunks' copies, when available
   std::thread worker;
   std::mutex mu;
@@ -440,13 +439,13 @@ struct staple_host_adamw {
   staple::AdamWConsts c{};
   int n_threads = 0;
 
-  // ev_done is recorded on the refresh stream whatever the outcome, so that
+  // ev_done is recorded on the copy stream whatever the outcome, so that
   // finish orders the caller's stream after every refresh launched, also
   // when the job stopped part way.
   staple_status_t run_job() {
     if (hipSetDevice(device) != hipSuccess) return STAPLE_ERR_HIP;
     const staple_status_t r = run_job_steps();
-    const bool rec = hipEventRecord(ev_done, refresh) == hipSuccess;
+    const bool rec = hipEventRecord(ev_done, copy) == hipSuccess;
     return r == STAPLE_OK && !rec ? STAPLE_ERR_HIP : r;
   }
 
@@ -504,7 +503,7 @@ struct staple_host_adamw {
       if (code && capacity > 0 &&
           staple::launch_cache_refresh(table, vocab, uniq_dev + lo, code + lo, n_unique_dev, hi - lo,
                                        d_ff * (dtype == STAPLE_BF16 ? 2 : 4), cache_rows, capacity,
-                                       refresh, err, kRefreshWorkgroups) != hipSuccess)
+                                       copy, err, kRefreshWorkgroups) != hipSuccess)
         return STAPLE_ERR_HIP;
     }
     return STAPLE_OK;
@@ -548,8 +547,7 @@ staple_status_t staple_host_adamw_create(int64_t max_rows, int64_t d_ff, staple_
                           static_cast<size_t>(max_rows + 1) * sizeof(int32_t), hipHostMallocDefault) == hipSuccess &&
             hipEventCreateWithFlags(&h->ev_rows, kWaitFlags) == hipSuccess &&
             hipEventCreateWithFlags(&h->ev_meta, kWaitFlags) == hipSuccess &&
-            hipEventCreateWithFlags(&h->ev_done, hipEventDisableTiming) == hipSuccess &&
-            hipStreamCreateWithFlags(&h->refresh, hipStreamNonBlocking) == hipSuccess;
+            hipEventCreateWithFlags(&h->ev_done, hipEventDisableTiming) == hipSuccess;
   for (int p = 0; ok && p < staple_host_adamw_t::kChunks; ++p)
     ok = hipEventCreateWithFlags(&h->ev_chunk[p], kWaitFlags) == hipSuccess;
   if (ok) h->sdma.init(h->device, staple_host_adamw_t::kChunks + 2);   // chunks, count, IDs
@@ -602,10 +600,11 @@ staple_status_t staple_host_adamw_start(staple_host_adamw_t* h, void* table, flo
   std::unique_lock<std::mutex> lk(h->mu);
   if (h->busy) return STAPLE_ERR_INVALID_ARGUMENT;   // the previous update was not finished
   hipStream_t cs = static_cast<hipStream_t>(copy_stream);
-  if (hipStreamWaitEvent(h->refresh, h->ev_rows, 0) != hipSuccess) return STAPLE_ERR_HIP;
+  // the copy stream carries the refreshes (and, without the DMA engines, the
+  // copies): nothing on it before the rows are complete
+  if (hipStreamWaitEvent(cs, h->ev_rows, 0) != hipSuccess) return STAPLE_ERR_HIP;
   if (!h->sdma.ready &&
-      (hipStreamWaitEvent(cs, h->ev_rows, 0) != hipSuccess ||
-       hipMemcpyAsync(h->meta_host, n_unique, sizeof(int32_t), hipMemcpyDeviceToHost, cs) != hipSuccess ||
+      (hipMemcpyAsync(h->meta_host, n_unique, sizeof(int32_t), hipMemcpyDeviceToHost, cs) != hipSuccess ||
        hipMemcpyAsync(h->meta_host + 1, uniq, static_cast<size_t>(h->max_rows) * sizeof(int32_t),
                       hipMemcpyDeviceToHost, cs) != hipSuccess ||
        hipEventRecord(h->ev_meta, cs) != hipSuccess))
@@ -662,7 +661,6 @@ void staple_host_adamw_destroy(staple_host_adamw_t* h) {
   h->sdma.release();
   if (h->ev_meta) (void)hipEventDestroy(h->ev_meta);
   if (h->ev_done) (void)hipEventDestroy(h->ev_done);
-  if (h->refresh) (void)hipStreamDestroy(h->refresh);
   if (h->ev_rows) (void)hipEventDestroy(h->ev_rows);
   if (h->meta_host) (void)hipHostFree(h->meta_host);
   if (h->grad_host) (void)hipHostFree(h->grad_host);
