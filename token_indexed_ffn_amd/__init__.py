@@ -651,8 +651,9 @@ class HostAdamW:
     gradient rows leave for the host right after the backward's segment sum
     (pass `event` to staple_ffn_bwd_table_grad as rows_event), a worker
     updates them as they land and, given the batch's cache probe, refreshes
-    their cached copies; finish() waits for the host update and orders
-    `stream` after the refreshes."""
+    their cached copies on `copy_stream` (a stream that does not carry the
+    step); finish() waits for the host update and orders `stream` after the
+    refreshes."""
 
     def __init__(self, max_rows: int, d_ff: int):
         h = ctypes.c_void_p()
