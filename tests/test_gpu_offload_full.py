@@ -10,6 +10,9 @@ bf16 tables in pinned host memory, the 5018 most frequent rows of each
   and copied over PCIe; h, g, u have the bits of the whole-batch gate/up over
   the rows gathered from the host table, and h matches the oracle on sampled
   features.
+* The 16384-token prefill in chunks of 4096 over two layers, the next
+  chunk's rows assembled on a second stream: y has the bits of the whole
+  batch in one pass and matches the oracle on sampled tokens.
 """
 import sys
 
@@ -224,3 +227,92 @@ def test_offloaded_training_split_full_size(st, dev):
     cs = torch.from_numpy(cols).to(dev)
     assert_close_stored_bf16(f64(h[:, cs]), of["h"], "split h[:, cols]")
     assert_close_stored_bf16(f64(u[:, cs]), of["u_saved"], "split u[:, cols]")
+
+
+@pytest.mark.timeout(900)
+def test_offloaded_prefill_pipeline_full_size(st, dev):
+    """The prefill of 64 prompts x 256 tokens over two layers of pinned
+    100352 x 8192 tables with the 5018-row cache, in chunks of 4096 tokens:
+    chunk c + 1's rows assembled on a second stream on 16 workgroups while
+    chunk c's layers run.  Every layer's y has the bits of the whole batch in
+    one pass, and matches the oracle on one token of every 256."""
+    import torch
+    from staple_synth import device_normal
+    w = S.OLMO1B_OFFLOAD_PREFILL
+    n, d, f, L, C = w.n_tokens, w.d_model, w.d_ff, 2, 4096
+    nc = n // C
+    cap = w.cache_capacity
+    _log(f"offloaded prefill, {n} tokens in chunks of {C}, {L} pinned tables, cache {cap}")
+    id_to_slot, tables, cache_rows = _host_tables(torch, st, w, L, dev)
+    ids_np = w.ids()
+    ids = torch.from_numpy(ids_np).to(dev)
+    layers = []
+    for l in range(L):
+        s = w.layer_seeds(l)
+        layers.append({k: device_normal(shape, std, s[k], torch.bfloat16, dev) for k, shape, std in (
+            ("x", (n, d), w.x_std), ("w_gate", (f, d), w.w_std), ("w_up", (f, d), w.w_std),
+            ("w_down", (d, f), w.w_std))})
+    # the whole batch in one pass
+    dd = st.staple_dedup(ids, w.vocab)
+    lk = st.staple_cache_lookup(dd["uniq"], dd["n_unique"], id_to_slot)
+    y_ref = []
+    for l, lay in enumerate(layers):
+        R = st.staple_assemble_rows_from_table(cache_rows[l], tables[l], dd["uniq"], lk["code"],
+                                               dd["n_unique"], capacity=cap)
+        y_ref.append(st.staple_ffn_fwd(lay["x"], lay["w_gate"], lay["w_up"], lay["w_down"], R,
+                                       dd["inv"], out_dtype=torch.float32)["y"])
+    torch.cuda.synchronize()
+    # the pipelined chunks
+    i32 = dict(dtype=torch.int32, device=dev)
+    main, side = torch.cuda.Stream(), torch.cuda.Stream()
+    bufs = []
+    for _ in range(2):
+        B = {"dd": {"uniq": torch.empty(C, **i32), "inv": torch.empty(C, **i32),
+                    "sorted_pos": torch.empty(C, **i32), "seg_start": torch.empty(C + 1, **i32),
+                    "n_unique": torch.empty(1, **i32)},
+             "lk": {"code": torch.empty(C, **i32), "miss_uidx": torch.empty(C, **i32),
+                    "n_miss": torch.empty(1, **i32)},
+             "rows": [torch.empty(C, f, dtype=torch.bfloat16, device=dev) for _ in range(L)]}
+        B["rs"] = st.RowSources([{"table": tables[l], "cache_rows": cache_rows[l],
+                                  "rows": B["rows"][l]} for l in range(L)], d_ff=f)
+        bufs.append(B)
+    y = [torch.full((n, d), float("nan"), dtype=torch.float32, device=dev) for _ in range(L)]
+    ready = [torch.cuda.Event() for _ in range(nc)]
+    done = [torch.cuda.Event() for _ in range(nc)]
+    main.wait_stream(torch.cuda.current_stream())
+    side.wait_stream(torch.cuda.current_stream())
+
+    def issue(c):
+        if c >= 2:
+            side.wait_event(done[c - 2])
+        B = bufs[c % 2]
+        st.staple_prefill_rows_cached(B["rs"], ids[c * C:(c + 1) * C], id_to_slot, cap,
+                                      dedup_out=B["dd"], lookup_out=B["lk"], workspace=None,
+                                      max_workgroups=16 if c > 0 else 0, stream=side)
+        ready[c].record(side)
+
+    issue(0)
+    with torch.cuda.stream(main):
+        for c in range(nc):
+            if c + 1 < nc:
+                issue(c + 1)
+            main.wait_event(ready[c])
+            B = bufs[c % 2]
+            for l, lay in enumerate(layers):
+                st.staple_ffn_fwd(lay["x"][c * C:(c + 1) * C], lay["w_gate"], lay["w_up"],
+                                  lay["w_down"], B["rows"][l], B["dd"]["inv"],
+                                  out={"y": y[l][c * C:(c + 1) * C]}, stream=main)
+            done[c].record(main)
+    torch.cuda.synchronize()
+    assert st.staple_get_device_error() == 0
+    toks = np.arange(0, n, 256)
+    f64 = lambda a: a.float().cpu().numpy().astype(np.float64)
+    for l, lay in enumerate(layers):
+        assert not bool(torch.isnan(y[l]).any()), f"layer {l}: a chunk was not written"
+        assert torch.equal(y[l], y_ref[l]), f"layer {l}: pipelined prefill differs"
+        sel = np.unique(ids_np[toks])
+        rows = f64(tables[l][torch.from_numpy(sel.astype(np.int64))])
+        tk = torch.from_numpy(toks).to(dev)
+        of = O.ffn_forward(f64(lay["x"][tk]), f64(lay["w_gate"]), f64(lay["w_up"]),
+                           f64(lay["w_down"]), _Rows(sel, rows), ids_np[toks], precision=O.BF16)
+        assert_close(f64(y[l][tk]), of["y"], f"prefill layer {l} y (sampled tokens)")
