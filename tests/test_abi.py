@@ -119,3 +119,21 @@ def test_prefill_rows_rejects_bad_arguments_before_device_work(lib):
     assert call(1, p, 64, 256, cap=-1) == -1   # capacity
     assert call(1, p, 64, 256, lookup=2) == -1 # lookup is 0 or 1
     assert call(1, p, 8192, 256) == -3         # no workspace for the multi-workgroup dedup
+
+
+def test_header_compiles_as_c99_and_cpp(tmp_path):
+    """The boundary is a C ABI: the header alone compiles as strict C99 and as C++."""
+    import shutil
+    import subprocess
+    inc = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include")
+    src = tmp_path / "use.c"
+    src.write_text('#include "staple.h"\n'
+                   "int main(void) { staple_row_source_t r = {0}; (void)r;\n"
+                   "  return (int)staple_dedup_workspace_bytes(0); }\n")
+    for cc, args in (("gcc", ["-std=c99", "-pedantic", "-Werror"]),
+                     ("g++", ["-std=c++17", "-Werror", "-x", "c++"])):
+        if shutil.which(cc) is None:
+            pytest.skip(f"{cc} not found")
+        r = subprocess.run([cc, *args, "-Wall", "-I", inc, "-fsyntax-only", str(src)],
+                           capture_output=True, text=True, timeout=60)
+        assert r.returncode == 0, r.stderr
