@@ -529,7 +529,9 @@ def run_train_lowrank(torch, st, w, r, steps, warmup):
                         "bound": "mfma", "achieved": gu_flops / (gu * 1e-6) / 1e12,
                         "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                         "frac": gu_flops / (gu * 1e-6) / 1e12 / BF16_PEAK_TFLOPS,
-                        "traffic": None, "avg_launch_us": gu,
+                        "traffic": traffic_from_profile(f"train_gate_up/{w.name}_lowrank_r{r}",
+                                                        source_sha("gemm.hip", "common.h")),
+                        "avg_launch_us": gu,
                         "algorithmic_flops_per_launch": gu_flops},
            "note": "step: dedup, R_r = E_r[uniq] (U x r), Z = R_r P^T (staple_lowrank_expand), "
                    "gate/up over Z, down, backward, dE_r and dP (staple_lowrank_bwd); FLOPs "
@@ -1195,7 +1197,9 @@ def _run_offload_train(torch, st, w, steps, warmup, main, side, copy):
                "kernel": "gemm_kernel<bf16,GateUp> (staple_ffn_gate_up_tokens over the cached "
                          "tokens, beside the miss-row copy)",
                "bound": "mfma", "achieved": achieved, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-               "frac": achieved / BF16_PEAK_TFLOPS, "traffic": None,
+               "frac": achieved / BF16_PEAK_TFLOPS,
+               "traffic": traffic_from_profile(f"offload_gate_up/{w.name}",
+                                               source_sha("gemm.hip", "common.h")),
                "avg_launch_us": gu_us, "algorithmic_flops_per_launch": gu_flops},
            "cache_capacity": w.cache_capacity, "token_hit_rate": stats["hit_tokens"] / n,
            "resident_ms_per_step": ms_res, "pcie_bytes_per_step": m * f * 2}
