@@ -437,6 +437,49 @@ def test_bf16_layer_matches_oracle(st, dev, n, d, f, v, seed):
     _compare_layer(res, of, ob, u, f"bf16 n={n}")
 
 
+@pytest.mark.parametrize("n,d,f,seed", [(4096, 2048, 256, 5), (2600, 1984, 512, 6),
+                                        (2048, 2048, 256, 7), (4608, 2048, 128, 8)])
+def test_plain_gemm_tile_shapes_match_oracle(st, dev, n, d, f, seed):
+    """Token counts at which the down projection and dx (plain stores of two
+    K-major operands) change tile shape on a 256-CU device: 256 x 256 tiles
+    that would fill at most half of the compute units give way to 256 x 128
+    tiles (4096 x 2048, and 2600 x 1984 with ragged tails in both
+    dimensions); with fewer tiles still, 128 x 128 (2048 x 2048); with more,
+    256 x 256 (4608 x 2048).  y and dx on every token against the oracle,
+    every element written (NaN-poisoned first)."""
+    import torch
+    _log(f"plain GEMM tile shapes n={n} d={d} f={f}")
+    inp = S.host_layer_inputs(n, d, f, 3000, dtype="bf16", seed=seed)
+    x, wg, wu, wd, tab, dy = (to_dev(getattr(inp, k), "bf16", dev)
+                              for k in ("x", "w_gate", "w_up", "w_down", "table", "dy"))
+    ids = torch.from_numpy(inp.ids).to(dev)
+    dd = st.staple_dedup(ids, tab.shape[0])
+    rows = st.staple_gather_rows(tab, dd["uniq"], dd["n_unique"])
+    bf = torch.bfloat16
+    fwd = st.staple_ffn_fwd(x, wg, wu, wd, rows, dd["inv"],
+                            out={"y": _nan((n, d), torch.float32, dev), "g": _nan((n, f), bf, dev),
+                                 "u": _nan((n, f), bf, dev), "h": _nan((n, f), bf, dev)})
+    bwd = st.staple_ffn_bwd_table_grad(dy, x, wg, wu, wd, fwd["g"], fwd["u"], fwd["h"],
+                                       dd["sorted_pos"], dd["seg_start"], dd["n_unique"],
+                                       inv=dd["inv"], out_dtype=torch.float32,
+                                       out={"d_rows": torch.empty(n, f, dtype=torch.float32, device=dev),
+                                            "dx": _nan((n, d), torch.float32, dev),
+                                            "dw_gate": torch.empty(f, d, dtype=torch.float32, device=dev),
+                                            "dw_up": torch.empty(f, d, dtype=torch.float32, device=dev),
+                                            "dw_down": torch.empty(d, f, dtype=torch.float32, device=dev)})
+    torch.cuda.synchronize()
+    _no_device_error(st)
+    for k, t in (("y", fwd["y"]), ("dx", bwd["dx"])):
+        assert not bool(torch.isnan(t).any()), f"{k} has unwritten elements"
+    g = {k: inp.as_f64(k) for k in ("x", "w_gate", "w_up", "w_down", "table", "dy")}
+    of = O.ffn_forward(g["x"], g["w_gate"], g["w_up"], g["w_down"], g["table"], inp.ids,
+                       precision=O.BF16)
+    ob = O.ffn_backward(g["dy"], g["x"], g["w_gate"], g["w_up"], g["w_down"], of, inp.ids,
+                        precision=O.BF16, with_dw=False)
+    assert_close(to_np(fwd["y"]), of["y"], f"n={n} y")
+    assert_close(to_np(bwd["dx"]), ob["dx"], f"n={n} dx")
+
+
 @pytest.mark.parametrize("n", [1, 17, 33, 63, 64, 65])
 def test_decode_path_boundary(st, dev, n):
     """Batches of at most 64 bf16 tokens take the decode kernels, 65 the tiled

@@ -34,7 +34,6 @@
 // range (d_ff) is split over several workgroups per output block; each writes
 // an fp32 partial and a second small kernel sums the partials in split order
 // (deterministic) and stores y.
-#include <atomic>
 #include <type_traits>
 
 #include "common.h"
@@ -678,21 +677,6 @@ hipError_t decode_pack(int64_t d, int64_t f, const void* wg, const void* wu, con
   }
   if (packed_down) go(d / 16, f, false, wd, nullptr, packed_down);
   return hipGetLastError();
-}
-
-// Compute units of the current device, looked up once per device.
-static int device_cus() {
-  constexpr int kMaxDevices = 64;
-  static std::atomic<int> cache[kMaxDevices];
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 256;
-  int v = cache[dev].load(std::memory_order_relaxed);
-  if (v <= 0) {
-    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0)
-      v = 256;
-    cache[dev].store(v, std::memory_order_relaxed);
-  }
-  return v;
 }
 
 // `up`: the weights hold W_up (the STAPLE layer; row-major: wu, packed: the

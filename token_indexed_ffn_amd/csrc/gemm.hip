@@ -1172,7 +1172,21 @@ static hipError_t run(const GemmArgs& a, hipStream_t s) {
     // with either pipeline, three to five 32 KB stages (loads three or four
     // stages ahead: the kernels are not waiting on global-load latency), and
     // 256x128 or 128x256 tiles on 4 waves with two workgroups per CU.
-    if (a.M >= 256 && a.N >= 256 && ((a.M + 255) / 256) * ((a.N + 255) / 256) >= 128)
+    const int64_t tiles256 = ((a.M + 255) / 256) * ((a.N + 255) / 256);
+    // Plain stores of two K-major operands with 256 x 256 tiles for at most
+    // half the compute units: 256 x 128 tiles on 4 x 2 waves of 64 x 64
+    // (direct-to-LDS pipeline) when they fill more than half and at most all
+    // of them, one round.  Measured for N = 2048, K = 8192: M 2560-4096
+    // 134-149 us against 139-158 us on 128 x 128 tiles and (M 4096) 192 us
+    // on 256 x 256 ones; from M 4608 (a second round of 256 x 128 tiles) the
+    // 256 x 256 tiles are faster again, 190 against 248 us.
+    if constexpr (EPI == kEpiStore && AK && BK) {
+      const int64_t cus = device_cus();
+      const int64_t tiles_rect = ((a.M + 255) / 256) * ((a.N + 127) / 128);
+      if (a.M >= 256 && 2 * tiles256 <= cus && 2 * tiles_rect > cus && tiles_rect <= cus)
+        return run_tile<T, 256, 128, 4, 2, AK, BK, EPI, OutT, kRowBytes, 2>(a, s);
+    }
+    if (a.M >= 256 && a.N >= 256 && tiles256 >= 128)
       return run_tile<T, 256, 256, 2, 4, AK, BK, EPI, OutT, kRowBytes, 2, 2>(a, s);
   }
   return run_tile<T, 128, 128, 2, 2, AK, BK, EPI, OutT, kRowBytes, 2>(a, s);
