@@ -187,6 +187,37 @@ staple_status_t staple_stage_misses(const void* host_table, int64_t vocab, int64
                                     int32_t dtype, const int32_t* host_miss_ids, int32_t n_miss,
                                     void* host_staging, void* dev_miss_rows, void* stream);
 
+/* Miss staging of a stack of layers on the GPU's DMA engines (STAPLE
+ * retrieval-path table, Prefill row: miss rows packed into pinned host
+ * buffers and sent with bulk asynchronous host-to-device copies).  For each
+ * layer l < n_layers the rows host_tables[l][host_miss_ids[m]], m < n_miss,
+ * are packed by the library's host threads into the block
+ * host_staging + l * n_miss * d_ff elements, and that block is copied to
+ * dev_miss_rows[l] by a DMA engine of the current device, which uses no
+ * compute unit (layer l + 1 is packed while layer l's block is copied).
+ * Runs on the calling thread and returns when every copy has completed; the
+ * caller then enqueues what reads dev_miss_rows (staple_assemble_rows), and
+ * must have seen earlier readers of dev_miss_rows finish (an event
+ * synchronised on the host) before the call.
+ *   host_tables: host array of n_layers host pointers, each [vocab x d_ff]
+ *     with rows table_stride elements apart (0: d_ff; larger for tables
+ *     interleaved by staple_group_tables_host), read by the host only;
+ *   host_miss_ids: host int32[n_miss], each in [0, vocab) (checked first:
+ *     STAPLE_ERR_HOST and nothing copied);
+ *   host_staging: pinned host memory (hipHostMalloc) of
+ *     n_layers * n_miss * d_ff elements;
+ *   dev_miss_rows: host array of n_layers pointers to device memory, each
+ *     [>= n_miss x d_ff].
+ * STAPLE_ERR_UNSUPPORTED when the device's DMA engines cannot be reached
+ * through the HSA runtime (nothing is copied; staple_stage_misses does the
+ * same work with a stream copy); STAPLE_ERR_HIP when an engine reports a
+ * failed copy.  Calls on one device take turns. */
+staple_status_t staple_stage_misses_dma(int64_t n_layers, const void* const* host_tables,
+                                        int64_t table_stride, int64_t vocab, int64_t d_ff,
+                                        int32_t dtype, const int32_t* host_miss_ids,
+                                        int32_t n_miss, void* host_staging,
+                                        void* const* dev_miss_rows);
+
 /* Compact leaf block assembly (AI Radio episode: only the active U x d_ff rows
  * are materialised on the GPU).
  * rows[u] = code[u] >= 0 ? cache_rows[code[u]] : miss_rows[-1-code[u]]

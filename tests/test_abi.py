@@ -103,6 +103,29 @@ def test_invalid_arguments_are_rejected_before_device_work(lib):
     assert np.all(stage == 0)
 
 
+def test_stage_misses_dma_rejects_before_any_copy(lib):
+    import numpy as np
+    table = np.zeros((4, 8), dtype=np.float32)
+    ids = np.array([1, 9], dtype=np.int32)
+    stage = np.zeros((2, 8), dtype=np.float32)
+    tabs = (ctypes.c_void_p * 1)(table.ctypes.data)
+    dst = (ctypes.c_void_p * 1)(16)   # never dereferenced: every case fails (or ends) first
+
+    def call(n_layers=1, stride=0, vocab=4, d_ff=8, dtype=0, n_miss=2, t=tabs, d=dst):
+        return lib.staple_stage_misses_dma(n_layers, ctypes.cast(t, ctypes.c_void_p) if t else None,
+                                           stride, vocab, d_ff, dtype, ids.ctypes.data, n_miss,
+                                           stage.ctypes.data,
+                                           ctypes.cast(d, ctypes.c_void_p) if d else None)
+    assert call(n_layers=0) == -1   # no layers
+    assert call(stride=4) == -1     # a row stride shorter than a row
+    assert call(dtype=7) == -1      # dtype
+    assert call(t=None) == -1       # no tables
+    assert call(d=None) == -1       # no destinations
+    assert call(n_miss=0) == 0      # nothing to copy
+    assert call() == -6             # ID 9 outside the vocabulary of 4: refused on the host
+    assert np.all(stage == 0)
+
+
 def test_prefill_rows_rejects_bad_arguments_before_device_work(lib):
     null, p = None, 16   # any non-null address: nothing is dereferenced before the checks
     outs = [p] * 8

@@ -375,3 +375,43 @@ def test_prefill_rows_of_a_stack_longer_than_one_launch(st, dev):
     for l in range(L):
         got = srcs[l]["rows"][:u].view(torch.int16).cpu().numpy().view(np.uint16)
         assert np.array_equal(got, hosts[l][uniq]), f"layer {l}"
+
+
+@pytest.mark.parametrize("grouped", [False, True])
+def test_stage_misses_dma_rows_reach_the_device(st, dev, grouped):
+    """staple_stage_misses_dma: every layer's miss rows land in its device block
+    as the host tables' bytes (separate tables, and tables interleaved by fours);
+    over several calls into the same blocks, each after a kernel has read the
+    previous contents, a kernel reading the blocks (the compact-row assembly)
+    sees the new rows."""
+    import torch
+    L, v, f = 4, 3000, 2048
+    _log(f"stage misses dma grouped={grouped}")
+    gen = torch.Generator().manual_seed(41)
+    tables = [torch.randn(v, f, generator=gen).to(torch.bfloat16) for _ in range(L)]
+    if grouped:
+        inter = st.staple_group_tables_host(tables)
+        srcs = [(inter, l * f, L * f) for l in range(L)]
+    else:
+        srcs = tables
+    n_max = 700
+    staging = torch.empty(L * n_max * f, dtype=torch.bfloat16, pin_memory=True)
+    blocks = [torch.full((n_max, f), float("nan"), dtype=torch.bfloat16, device=dev)
+              for _ in range(L)]
+    cache = torch.zeros(4, f, dtype=torch.bfloat16, device=dev)
+    rng = np.random.default_rng(7)
+    for call, n in enumerate((n_max, 333, 1, 610)):
+        ids = rng.choice(v, size=n, replace=False).astype(np.int32)
+        st.staple_stage_misses_dma(srcs, torch.from_numpy(ids), n, staging, blocks)
+        code = torch.from_numpy(-1 - np.arange(n, dtype=np.int32)).to(dev)
+        nu = torch.tensor([n], dtype=torch.int32, device=dev)
+        for l in range(L):
+            got = st.staple_assemble_rows(cache, blocks[l], code, nu)
+            torch.cuda.synchronize()
+            want = tables[l][torch.from_numpy(ids.astype(np.int64))]
+            assert torch.equal(got.cpu().view(torch.int16), want.view(torch.int16)), \
+                f"call {call} layer {l}: rows differ"
+        _no_device_error(st)
+    with pytest.raises(st.StapleError):
+        bad = np.array([1, v], dtype=np.int32)
+        st.staple_stage_misses_dma(srcs, torch.from_numpy(bad), 2, staging, blocks)

@@ -200,6 +200,47 @@ def staple_stage_misses(host_table: torch.Tensor, host_miss_ids: torch.Tensor, n
                                      _stream(stream)), "staple_stage_misses")
 
 
+def staple_stage_misses_dma(host_tables: list, host_miss_ids: torch.Tensor, n_miss: int,
+                            host_staging: torch.Tensor, dev_miss_rows: list) -> None:
+    """Every layer's miss rows host_tables[l][host_miss_ids[:n_miss]] packed into pinned
+    staging and copied to dev_miss_rows[l] on the GPU's DMA engines; returns when the
+    copies have completed.  host_tables: [vocab x d_ff] host tensors, or (tensor,
+    element offset, row stride) triples for tables interleaved by
+    staple_group_tables_host (one stride for all)."""
+    if not host_tables or len(host_tables) != len(dev_miss_rows):
+        raise ValueError("one device block per table")
+    trip = [t if isinstance(t, tuple) else (t, 0, 0) for t in host_tables]
+    strides = {s for _, _, s in trip}
+    if len(strides) != 1:
+        raise ValueError("the tables share one row stride")
+    stride = strides.pop()
+    dt = trip[0][0].dtype
+    d_ff = dev_miss_rows[0].shape[1]
+    vocab = None
+    for tab, off, s in trip:
+        if tab.is_cuda or tab.dtype != dt:
+            raise ValueError("tables are host tensors of one dtype")
+        v = tab.shape[0] if s == 0 else tab.numel() // s
+        vocab = v if vocab is None else min(vocab, v)
+        if s == 0 and (tab.dim() != 2 or tab.shape[1] != d_ff or not tab.is_contiguous()):
+            raise ValueError("table is a contiguous [vocab x d_ff] tensor")
+    for r in dev_miss_rows:
+        if not r.is_cuda or r.dtype != dt or r.dim() != 2 or r.shape[1] != d_ff or r.shape[0] < n_miss:
+            raise ValueError(f"each device block is [>= {n_miss} x {d_ff}] of the tables' dtype")
+    if host_miss_ids.is_cuda or host_miss_ids.dtype != torch.int32:
+        raise ValueError("host_miss_ids is a host int32 tensor")
+    _need(host_miss_ids, n_miss, "host_miss_ids")
+    if host_staging.is_cuda or not host_staging.is_pinned() or host_staging.dtype != dt:
+        raise ValueError("host_staging is pinned host memory of the tables' dtype")
+    _need(host_staging, len(trip) * n_miss * d_ff, "host_staging", dtype=dt)
+    tabs = (ctypes.c_void_p * len(trip))(*[t.data_ptr() + off * t.element_size() for t, off, _ in trip])
+    dst = (ctypes.c_void_p * len(trip))(*[r.data_ptr() for r in dev_miss_rows])
+    _check(lib().staple_stage_misses_dma(len(trip), ctypes.cast(tabs, ctypes.c_void_p), stride, vocab,
+                                         d_ff, _DT[dt], _p(host_miss_ids), int(n_miss),
+                                         _p(host_staging), ctypes.cast(dst, ctypes.c_void_p)),
+           "staple_stage_misses_dma")
+
+
 def staple_assemble_rows(cache_rows: torch.Tensor, miss_rows: torch.Tensor, code: torch.Tensor,
                          n_unique: torch.Tensor, out: Optional[torch.Tensor] = None,
                          stream=None) -> torch.Tensor:

@@ -32,6 +32,8 @@ _SIGS = {
     "staple_cache_lookup": (c_i32, [c_vp, c_vp, c_i64, c_vp, c_i64, c_vp, c_vp, c_vp, c_vp, c_vp]),
     "staple_split_tokens": (c_i32, [c_vp, c_i64, c_vp, c_vp, c_i64, c_vp, c_vp, c_vp, c_vp, c_vp]),
     "staple_stage_misses": (c_i32, [c_vp, c_i64, c_i64, c_i32, c_vp, c_i32, c_vp, c_vp, c_vp]),
+    "staple_stage_misses_dma": (c_i32, [c_i64, c_vp, c_i64, c_i64, c_i64, c_i32, c_vp, c_i32, c_vp,
+                                        c_vp]),
     "staple_assemble_rows": (c_i32, [c_vp, c_i64, c_vp, c_i64, c_vp, c_vp, c_i64, c_i64, c_i32,
                                      c_vp, c_vp]),
     "staple_assemble_rows_from_table": (c_i32, [c_vp, c_i64, c_vp, c_i64, c_vp, c_vp, c_vp, c_i64,

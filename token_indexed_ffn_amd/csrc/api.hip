@@ -9,6 +9,7 @@
 #include <vector>
 
 #include "common.h"
+#include "dma.h"
 #include "host_pool.h"
 
 namespace staple {
@@ -375,6 +376,68 @@ staple_status_t staple_stage_misses(const void* host_table, int64_t vocab, int64
   host_parallel_for(n_miss, host_pool_parts(static_cast<int64_t>(total), 16), pack);
   HIPCALL(hipMemcpyAsync(dev_miss_rows, host_staging, total, hipMemcpyHostToDevice, S(stream)));
   return STAPLE_OK;
+}
+
+// One DMA copier per device for the staging below, set up on first use and
+// kept until the process ends; calls on one device take turns.
+namespace {
+struct DmaStaging {
+  std::mutex mu;
+  bool tried = false;
+  SdmaCopier copier;
+};
+constexpr int kDmaDevices = 64;
+DmaStaging g_dma[kDmaDevices];
+}  // namespace
+
+staple_status_t staple_stage_misses_dma(int64_t n_layers, const void* const* host_tables,
+                                        int64_t table_stride, int64_t vocab, int64_t d_ff,
+                                        int32_t dtype, const int32_t* host_miss_ids,
+                                        int32_t n_miss, void* host_staging,
+                                        void* const* dev_miss_rows) {
+  REQUIRE(valid_dtype(dtype) && vocab >= 1 && d_ff > 0 && n_miss >= 0);
+  REQUIRE(n_layers >= 1 && n_layers <= 4096 && (table_stride == 0 || table_stride >= d_ff));
+  if (n_miss == 0) return STAPLE_OK;
+  REQUIRE(host_tables && host_miss_ids && host_staging && dev_miss_rows);
+  for (int64_t l = 0; l < n_layers; ++l) REQUIRE(host_tables[l] && dev_miss_rows[l]);
+  for (int32_t m = 0; m < n_miss; ++m)
+    if (host_miss_ids[m] < 0 || host_miss_ids[m] >= vocab) return STAPLE_ERR_HOST;
+  REQUIRE(host_memory(host_staging));
+  for (int64_t l = 0; l < n_layers; ++l) REQUIRE(device_addressable(dev_miss_rows[l]));
+  int device = 0;
+  if (hipGetDevice(&device) != hipSuccess || device < 0 || device >= kDmaDevices) return STAPLE_ERR_HIP;
+  DmaStaging& ds = g_dma[device];
+  std::lock_guard<std::mutex> lock(ds.mu);
+  if (!ds.tried) {
+    ds.tried = true;
+    ds.copier.init(device, SdmaCopier::kMaxSignals);
+  }
+  if (!ds.copier.ready) return STAPLE_ERR_UNSUPPORTED;
+  const size_t row_bytes = static_cast<size_t>(d_ff) * elem_bytes(dtype);
+  const size_t src_stride = static_cast<size_t>(table_stride ? table_stride : d_ff) * elem_bytes(dtype);
+  const size_t block = row_bytes * static_cast<size_t>(n_miss);
+  constexpr int kSig = SdmaCopier::kMaxSignals;
+  char* staging = static_cast<char*>(host_staging);
+  // layer l's rows are packed while layer l - 1's block is on the DMA engine
+  bool ok = true;
+  int64_t started = 0;
+  for (int64_t l = 0; l < n_layers && ok; ++l) {
+    const char* src = static_cast<const char*>(host_tables[l]);
+    char* dst = staging + static_cast<size_t>(l) * block;
+    auto pack = [&](int64_t lo, int64_t hi) {
+      for (int64_t m = lo; m < hi; ++m)
+        std::memcpy(dst + m * row_bytes, src + static_cast<size_t>(host_miss_ids[m]) * src_stride,
+                    row_bytes);
+    };
+    host_parallel_for(n_miss, host_pool_parts(static_cast<int64_t>(block), 16), pack);
+    const int sig = static_cast<int>(l % kSig);
+    if (l >= kSig) ok = ds.copier.wait(sig);     // the copy that last used this signal
+    ok = ok && ds.copier.start_h2d(sig, dev_miss_rows[l], dst, block);
+    if (ok) started = l + 1;
+  }
+  for (int64_t l = std::max<int64_t>(0, started - kSig); l < started; ++l)
+    ok = ds.copier.wait(static_cast<int>(l % kSig)) && ok;
+  return ok ? STAPLE_OK : STAPLE_ERR_HIP;
 }
 
 staple_status_t staple_assemble_rows(const void* cache_rows, int64_t capacity,

@@ -314,95 +314,13 @@ hipError_t launch_cache_refresh(const void* table, int64_t vocab, const int32_t*
 // by the same routine as staple_adamw_rows_host, each row once and
 // independently, so the result is the same bits as the serial update.
 // ---------------------------------------------------------------------------
-#include <hsa/hsa.h>
-#include <hsa/hsa_ext_amd.h>
-
 #include <condition_variable>
 #include <mutex>
 #include <new>
 
-namespace {
+#include "dma.h"
 
-// Device-to-host copies on the GPU's DMA (SDMA) engines through the HSA
-// runtime.  A hipMemcpyAsync to pinned host memory may be carried out by a
-// copy kernel; while the backward's weight-gradient GEMMs run (a few hundred
-// long workgroups, one per CU at a time) such a kernel's workgroups hold CU
-// slots and the GEMM's last workgroups start late.  The DMA engines use no
-// compute unit.
-struct SdmaCopier {
-  bool ready = false;
-  hsa_agent_t gpu{}, cpu{};
-  static constexpr int kMaxSignals = 16;
-  hsa_signal_t sig[kMaxSignals] = {};
-  int n_sig = 0;
-
-  struct Find {
-    uint32_t bdf = 0;        // bus << 8 | device << 3 of the GPU to find
-    hsa_agent_t gpu{}, cpu{};
-    bool got_gpu = false, got_cpu = false;
-  };
-  static hsa_status_t visit(hsa_agent_t a, void* data) {
-    Find* f = static_cast<Find*>(data);
-    hsa_device_type_t t;
-    if (hsa_agent_get_info(a, HSA_AGENT_INFO_DEVICE, &t) != HSA_STATUS_SUCCESS) return HSA_STATUS_SUCCESS;
-    if (t == HSA_DEVICE_TYPE_CPU && !f->got_cpu) {
-      f->cpu = a;
-      f->got_cpu = true;
-    } else if (t == HSA_DEVICE_TYPE_GPU && !f->got_gpu) {
-      uint32_t bdf = 0;
-      if (hsa_agent_get_info(a, static_cast<hsa_agent_info_t>(HSA_AMD_AGENT_INFO_BDFID), &bdf) ==
-              HSA_STATUS_SUCCESS && (bdf & ~7u) == f->bdf) {
-        f->gpu = a;
-        f->got_gpu = true;
-      }
-    }
-    return HSA_STATUS_SUCCESS;
-  }
-
-  // For HIP device `device`, with `n` completion signals; on any failure the
-  // copier stays unready and the caller copies with hipMemcpyAsync.
-  void init(int device, int n) {
-    if (n > kMaxSignals) return;
-    int bus = -1, dev = -1;
-    if (hipDeviceGetAttribute(&bus, hipDeviceAttributePciBusId, device) != hipSuccess ||
-        hipDeviceGetAttribute(&dev, hipDeviceAttributePciDeviceId, device) != hipSuccess)
-      return;
-    if (hsa_init() != HSA_STATUS_SUCCESS) return;
-    Find f;
-    f.bdf = (static_cast<uint32_t>(bus) << 8) | (static_cast<uint32_t>(dev) << 3);
-    if (hsa_iterate_agents(&SdmaCopier::visit, &f) != HSA_STATUS_SUCCESS || !f.got_gpu || !f.got_cpu) {
-      (void)hsa_shut_down();
-      return;
-    }
-    gpu = f.gpu;
-    cpu = f.cpu;
-    for (n_sig = 0; n_sig < n; ++n_sig)
-      if (hsa_signal_create(0, 0, nullptr, &sig[n_sig]) != HSA_STATUS_SUCCESS) break;
-    ready = n_sig == n;
-    if (!ready) release();
-  }
-  void release() {
-    for (int i = 0; i < n_sig; ++i) (void)hsa_signal_destroy(sig[i]);
-    if (n_sig > 0 || ready) (void)hsa_shut_down();
-    n_sig = 0;
-    ready = false;
-  }
-  // Starts copy i (device src -> pinned host dst).
-  bool start(int i, void* dst, const void* src, size_t bytes) {
-    hsa_signal_store_screlease(sig[i], 1);
-    return hsa_amd_memory_async_copy(dst, cpu, src, gpu, bytes, 0, nullptr, sig[i]) == HSA_STATUS_SUCCESS;
-  }
-  // Waits for copy i; false when the engine reported an error.
-  bool wait(int i) {
-    hsa_signal_value_t v;
-    do {
-      v = hsa_signal_wait_scacquire(sig[i], HSA_SIGNAL_CONDITION_LT, 1, UINT64_MAX, HSA_WAIT_STATE_BLOCKED);
-    } while (v >= 1);
-    return v == 0;
-  }
-};
-
-}  // namespace
+using staple::SdmaCopier;
 
 struct staple_host_adamw {
   static constexpr int kChunks = 8;
@@ -454,8 +372,8 @@ struct staple_host_adamw {
       // the row count and IDs on the DMA engines as soon as the rows are
       // complete (a copy kernel could wait behind the GEMMs for a CU)
       if (hipEventSynchronize(ev_rows) != hipSuccess) return STAPLE_ERR_HIP;
-      const bool a = sdma.start(kChunks, meta_host, n_unique_dev, sizeof(int32_t));
-      const bool b = a && sdma.start(kChunks + 1, meta_host + 1, uniq_dev,
+      const bool a = sdma.start_d2h(kChunks, meta_host, n_unique_dev, sizeof(int32_t));
+      const bool b = a && sdma.start_d2h(kChunks + 1, meta_host + 1, uniq_dev,
                                      static_cast<size_t>(max_rows) * sizeof(int32_t));
       const bool wa = a && sdma.wait(kChunks);
       const bool wb = b && sdma.wait(kChunks + 1);
@@ -475,7 +393,7 @@ struct staple_host_adamw {
       const int64_t lo = n * p / parts, hi = n * (p + 1) / parts;
       const size_t bytes = static_cast<size_t>(hi - lo) * d_ff * sizeof(float);
       if (sdma.ready) {
-        if (!sdma.start(p, grad_host + lo * d_ff, grad_dev + lo * d_ff, bytes)) {
+        if (!sdma.start_d2h(p, grad_host + lo * d_ff, grad_dev + lo * d_ff, bytes)) {
           for (int q = 0; q < p; ++q) (void)sdma.wait(q);   // none left writing the staging
           return STAPLE_ERR_HIP;
         }
