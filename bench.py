@@ -1192,7 +1192,7 @@ def _run_offload_train(torch, st, w, steps, warmup, main, side, copy):
     ev_copy0, ev_copy1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     ev_gu0, ev_gu1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     ev_ready = torch.cuda.Event()
-    stats = {"pack_s": 0.0, "copy_ms": 0.0, "hit_tokens": 0, "gu_us": []}
+    stats = {"pack_s": 0.0, "copy_ms": 0.0, "hit_tokens": 0, "gu_us": {}, "dma_ms": 0.0}
 
     def step(mode, B=None, before_rows=None, rows_event=None, blocking=False):
         """B: the step's own dedup, probe and row-gradient buffers (default:
@@ -1210,27 +1210,42 @@ def _run_offload_train(torch, st, w, steps, warmup, main, side, copy):
         side.wait_stream(main)
         if before_rows is not None:
             before_rows()
-        t0 = time.perf_counter()
-        with torch.cuda.stream(side):
-            ev_copy0.record(side)
-        if mode == "staged":      # host pack into pinned staging, one H2D copy
-            st.staple_stage_misses(O["tables"][0], miss_host, m, staging, dev_miss, stream=side)
-        elif mode == "direct":    # a kernel reads the rows from the pinned host table
-            with torch.cuda.stream(side):
-                st.staple_gather_rows(O["tables"][0], lk["miss_ids"], lk["n_miss"], out=dev_miss,
-                                      stream=side)
-        # mode "resident": the miss rows are already in HBM (no copy; reference)
-        with torch.cuda.stream(side):
-            ev_copy1.record(side)
-        stats["pack_s"] += time.perf_counter() - t0
-        ev_ready.record(side)
         fw = T["fwd"]
-        # the tokens whose rows are cached run while the miss rows are in flight
-        ev_gu0.record(main)
-        st.staple_ffn_gate_up_tokens(sp["hit_pos"], n_hit, T["x"], T["w_gate"], T["w_up"],
-                                     O["cache_rows"][0], sp["tok_row"], fw["h"], fw["g"], fw["u"])
-        ev_gu1.record(main)
-        main.wait_event(ev_ready)
+
+        def gate_up_cached():
+            # the tokens whose rows are cached run while the miss rows are in flight
+            ev_gu0.record(main)
+            st.staple_ffn_gate_up_tokens(sp["hit_pos"], n_hit, T["x"], T["w_gate"], T["w_up"],
+                                         O["cache_rows"][0], sp["tok_row"], fw["h"], fw["g"],
+                                         fw["u"])
+            ev_gu1.record(main)
+
+        if mode == "dma":
+            # the cached tokens' gate/up first; meanwhile the host packs the miss
+            # rows and the DMA engines copy them (no compute unit); the missed
+            # tokens' gate/up is enqueued once the copy is done.  The previous
+            # step's readers of dev_miss finished before the miss-list sync.
+            gate_up_cached()
+            t0 = time.perf_counter()
+            st.staple_stage_misses_dma([O["tables"][0]], miss_host, m, staging, [dev_miss])
+            stats["dma_ms"] = (time.perf_counter() - t0) * 1e3
+        else:
+            t0 = time.perf_counter()
+            with torch.cuda.stream(side):
+                ev_copy0.record(side)
+            if mode == "staged":      # host pack into pinned staging, one H2D copy
+                st.staple_stage_misses(O["tables"][0], miss_host, m, staging, dev_miss, stream=side)
+            elif mode == "direct":    # a kernel reads the rows from the pinned host table
+                with torch.cuda.stream(side):
+                    st.staple_gather_rows(O["tables"][0], lk["miss_ids"], lk["n_miss"],
+                                          out=dev_miss, stream=side)
+            # mode "resident": the miss rows are already in HBM (no copy; reference)
+            with torch.cuda.stream(side):
+                ev_copy1.record(side)
+            stats["pack_s"] += time.perf_counter() - t0
+            ev_ready.record(side)
+            gate_up_cached()
+            main.wait_event(ev_ready)
         st.staple_ffn_gate_up_tokens(sp["miss_pos"], n_miss_tok, T["x"], T["w_gate"], T["w_up"],
                                      dev_miss, sp["tok_row"], fw["h"], fw["g"], fw["u"])
         st.staple_ffn_down(fw["h"], T["w_down"], fw["y"])
@@ -1252,25 +1267,28 @@ def _run_offload_train(torch, st, w, steps, warmup, main, side, copy):
         t0 = time.perf_counter()
         for _ in range(steps):
             m = step(mode)
-            ev_copy1.synchronize()
-            copy_ms.append(ev_copy0.elapsed_time(ev_copy1))
-            if mode == "direct":
+            if mode == "dma":
+                copy_ms.append(stats["dma_ms"])   # host pack and DMA copy, timed on the host
+            else:
+                ev_copy1.synchronize()
+                copy_ms.append(ev_copy0.elapsed_time(ev_copy1))
+            if mode in ("direct", "dma"):
                 ev_gu1.synchronize()
-                stats["gu_us"].append(ev_gu0.elapsed_time(ev_gu1) * 1e3)
+                stats["gu_us"].setdefault(mode, []).append(ev_gu0.elapsed_time(ev_gu1) * 1e3)
         torch.cuda.synchronize()
         return ((time.perf_counter() - t0) / steps * 1e3, float(np.median(copy_ms)),
                 stats["pack_s"] / steps * 1e3, m)
 
-    res = {k: timed(k) for k in ("staged", "direct", "resident")}
+    res = {k: timed(k) for k in ("staged", "direct", "dma", "resident")}
     host_adamw = run_host_adamw(torch, st, O, T, lk_out)
-    mode = min(("staged", "direct"), key=lambda k: res[k][0])
+    mode = min(("staged", "direct", "dma"), key=lambda k: res[k][0])
     ms_free, _, _, m = res[mode]
     ms_res = res["resident"][0]
     opt = run_offload_train_optimizer(torch, st, O, T, lk_out, step, mode, steps, warmup, copy)
     ms = opt["overlapped_ms_per_step"]
     opt["ratio_to_optimizer_free_step"] = ms / ms_free
     opt["serial_ratio_to_optimizer_free_step"] = opt["serial_ms_per_step"] / ms_free
-    gu_us = float(np.median(stats["gu_us"]))
+    gu_us = float(np.median(stats["gu_us"]["dma" if mode == "dma" else "direct"]))
     gu_flops = 4 * stats["hit_tokens"] * d * f
     achieved = gu_flops / (gu_us * 1e-6) / 1e12
     out = {"workload": w.name, "ms_per_step": ms, "tokens_per_s": n / (ms * 1e-3),
@@ -1288,17 +1306,19 @@ def _run_offload_train(torch, st, w, steps, warmup, main, side, copy):
            "cache_capacity": w.cache_capacity, "token_hit_rate": stats["hit_tokens"] / n,
            "resident_ms_per_step": ms_res, "pcie_bytes_per_step": m * f * 2}
     out["adamw_host"] = host_adamw
-    for k in ("staged", "direct"):
+    for k in ("staged", "direct", "dma"):
         ms_k, copy_k, pack_k, _ = res[k]
         out[k] = {"ms_per_step": ms_k, "copy_ms": copy_k, "host_pack_ms": pack_k,
                   "pcie_gb_s": m * f * 2 / (copy_k * 1e-3) / 1e9,
                   "hidden_fraction_of_copy": max(0.0, min(1.0, 1.0 - max(0.0, ms_k - ms_res) /
                                                           max(copy_k + pack_k, 1e-9)))}
     out["note"] = ("eager step: dedup + cache probe + token split, one host sync for the miss "
-                   "list and the split counts; the miss rows move on a side stream (staged: host "
-                   "pack into pinned staging + one H2D copy; direct: a kernel reads them from the "
-                   "pinned host table) while the gate/up GEMM of the cached tokens runs (rows "
-                   "from the cache slots); then the missed tokens' gate/up, down, backward. "
+                   "list and the split counts; the miss rows move while the gate/up GEMM of the "
+                   "cached tokens runs (rows from the cache slots): staged, host pack into pinned "
+                   "staging + one H2D copy on a side stream; direct, a kernel on a side stream "
+                   "reads them from the pinned host table; dma, host pack + a copy on the DMA "
+                   "engines (staple_stage_misses_dma), its copy_ms the pack and copy timed on "
+                   "the host; then the missed tokens' gate/up, down, backward. "
                    "ms_per_step and tokens_per_s include the table rows' AdamW update on the host "
                    "overlapped with the GPU (optimizer.overlapped); optimizer_free_*: the same "
                    "step without it. resident: the step with the miss rows already in HBM, for "
