@@ -1279,12 +1279,24 @@ def _run_offload_train(torch, st, w, steps, warmup, main, side, copy):
         return ((time.perf_counter() - t0) / steps * 1e3, float(np.median(copy_ms)),
                 stats["pack_s"] / steps * 1e3, m)
 
-    res = {k: timed(k) for k in ("staged", "direct", "dma", "resident")}
+    # "resident" reuses the miss rows the step before it copied
+    res, outs = {}, {}
+    for k in ("staged", "resident", "direct", "dma"):
+        res[k] = timed(k)
+        outs[k] = (T["fwd"]["y"].clone(), T["bwd"]["d_rows"].clone())
+        if not all(torch.equal(a, b) for a, b in zip(outs[k], outs["staged"])):
+            raise RuntimeError(f"offloaded training step ({k}) differs from the staged one")
+    del outs
     host_adamw = run_host_adamw(torch, st, O, T, lk_out)
-    mode = min(("staged", "direct", "dma"), key=lambda k: res[k][0])
+    # the optimizer overlapped with each of the two faster row paths (their
+    # optimizer-free times are within run-to-run noise); the faster counts
+    opts = {k: run_offload_train_optimizer(torch, st, O, T, lk_out, step, k, steps, warmup, copy)
+            for k in ("direct", "dma")}
+    mode = min(opts, key=lambda k: opts[k]["overlapped_ms_per_step"])
+    opt = opts[mode]
+    opt["overlapped_ms_per_step_by_method"] = {k: o["overlapped_ms_per_step"] for k, o in opts.items()}
     ms_free, _, _, m = res[mode]
     ms_res = res["resident"][0]
-    opt = run_offload_train_optimizer(torch, st, O, T, lk_out, step, mode, steps, warmup, copy)
     ms = opt["overlapped_ms_per_step"]
     opt["ratio_to_optimizer_free_step"] = ms / ms_free
     opt["serial_ratio_to_optimizer_free_step"] = opt["serial_ms_per_step"] / ms_free
