@@ -135,6 +135,19 @@ def test_prefill_rows_match_the_separate_calls(st, dev, n, vocab, cap, wgs, layo
         assert torch.equal(srcs[l]["rows"][:u], kept[l]), f"layer {l}, lookup off"
     for k, t in kept_dd.items():
         assert torch.equal(dd[k], t), k
+    # the misses staged by the DMA engines instead, then assembled with the
+    # cached rows: the same compact rows
+    miss_h = rl["miss_ids"][:max(m, 1)].cpu().contiguous()
+    staging = torch.empty(L * max(m, 1) * f, dtype=torch.bfloat16, pin_memory=True)
+    blocks = [torch.empty(max(m, 1), f, dtype=torch.bfloat16, device=dev) for _ in range(L)]
+    st.staple_stage_misses_dma([src["table"] for src in srcs], miss_h, m, staging, blocks)
+    for l in range(L):
+        cache = caches[l] if caches[l] is not None else torch.zeros(1, f, dtype=torch.bfloat16,
+                                                                   device=dev)
+        staged = st.staple_assemble_rows(cache, blocks[l], rl["code"], rd["n_unique"])
+        torch.cuda.synchronize()
+        assert torch.equal(staged[:u], kept[l]), f"layer {l}, DMA-staged misses"
+    _no_device_error(st)
 
 
 def test_chunked_prefill_pipeline_matches_the_whole_batch(st, dev):
