@@ -610,7 +610,9 @@ def _stream_pair(torch, k=2):
     on the order the process created them (measured: every sixteenth pair of
     consecutive pool streams did).  So each stream taken from the pool is
     checked against the ones already chosen: a four-workgroup GEMM on each
-    (about 0.6 ms alone) must run side by side, else the stream is skipped."""
+    (about 0.6 ms alone) must run side by side, else the stream is skipped.
+    Where no stream does (a profiler that serialises the kernels), the first
+    k candidates are returned."""
     import token_indexed_ffn_amd as st
     from staple_synth import device_normal
     dev = torch.device("cuda:0")
@@ -633,14 +635,17 @@ def _stream_pair(torch, k=2):
         t2 = time.perf_counter()
         return (t2 - t1) < 1.5 * (t1 - t0)
 
-    chosen = []
-    for _ in range(64):
+    chosen, seen = [], []
+    for _ in range(16):
         s = torch.cuda.Stream()
+        seen.append(s)
         if all(side_by_side(c, s) for c in chosen):
             chosen.append(s)
             if len(chosen) == k:
                 return tuple(chosen)
-    raise RuntimeError(f"no {k} streams of torch's pool run side by side")
+    print(f"[bench] no {k} streams ran side by side (kernels serialised?); using the first {k}",
+          file=sys.stderr, flush=True)
+    return tuple(seen[:k])
 
 
 def setup_offload(torch, st, w, n_layers):
