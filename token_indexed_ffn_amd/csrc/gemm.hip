@@ -1161,7 +1161,9 @@ static hipError_t run_tile(const GemmArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-// 256x256 tiles for large bf16 problems, 128x128 tiles on 4 waves otherwise.
+// 256x256 tiles for large bf16 problems, 256x128 tiles for plain GEMMs that
+// 256x256 tiles would leave half the GPU idle on, 128x128 tiles on 4 waves
+// otherwise.
 template <typename T, bool AK, bool BK, int EPI, typename OutT>
 static hipError_t run(const GemmArgs& a, hipStream_t s) {
   if (a.M <= 0 || a.N <= 0) return hipSuccess;
@@ -1171,7 +1173,8 @@ static hipError_t run(const GemmArgs& a, hipStream_t s) {
     // Measured slower: 2x2 waves of 128x128 (half the LDS reads per MFMA)
     // with either pipeline, three to five 32 KB stages (loads three or four
     // stages ahead: the kernels are not waiting on global-load latency), and
-    // 256x128 or 128x256 tiles on 4 waves with two workgroups per CU.
+    // (on the training shapes) 256x128 or 128x256 tiles on 4 waves with two
+    // workgroups per CU.
     const int64_t tiles256 = ((a.M + 255) / 256) * ((a.N + 255) / 256);
     // Plain stores of two K-major operands with 256 x 256 tiles for at most
     // half the compute units: 256 x 128 tiles on 4 x 2 waves of 64 x 64
